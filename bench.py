@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X selective scan: one JSON line on stdout.
+
+Headline workload (a "step"): one selective scan of the Mamba-1.4B-layer
+shape B=4, L=4096, D=4096, N=16, bf16 inputs/outputs, fp32 state,
+z-gated, with the inputs already resident in HBM.  metric = state updates
+per second (B*L*D*N per step).
+
+Also reported in the same line:
+  roofline      -- the scan kernel against its binding roofline (VALU issue
+                   slots; the HBM fraction is given beside it), from HIP events
+                   around every timed launch;
+  cpu_baseline  -- the fp64 C oracle on this same input, on the host cores;
+  secondary     -- the decode state update (1024 steps of h[256,4096,16]) and
+                   the million-token chunked scan (B1 L1048576 D1024 N16).
+
+Options: --gpus N (only 1 is supported), --steps K, --warmup W,
+--no-cpu-baseline, --no-secondary, --profile-run (short run for rocprofv3),
+--copy-calibration MiB (also run a plain torch copy of that size, for
+counter calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# VALU issue slots per second with packed FP32 off: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic VALU slots per state update: mul (delta*A), v_exp_f32 (2 slots: it issues at
+# half the FMA rate on gfx950), mul (delta*x*B), fma (state), fma (readout)
+SLOTS_PER_UPDATE = 6.0
+# per (b, t, d): delta*x, D*x fma, gate: mul, exp (2), add, rcp (2), mul, mul
+SLOTS_PER_TOKEN_CHANNEL_GATED = 10.0
+SLOTS_PER_TOKEN_CHANNEL = 2.0
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("ssm_kernels.hip", "ssm_host.cpp", "ssm_host.h"):
+        with open(os.path.join(ROOT, "selective_state_space_50_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, src_hash):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
+    only while the kernel sources are unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def scan_bytes(B, L, D, N, esz, gated):
+    tok = B * L * D * esz
+    return tok * (3 + (1 if gated else 0)) + 2 * B * L * N * esz + D * N * 4 + D * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="few steps, no CPU baseline, no secondary (for rocprofv3)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    ap.add_argument("--secondary-only", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "requested_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if args.profile_run:
+        args.no_cpu_baseline = True
+        args.no_secondary = True
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_50_amd as ssm
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    ssm.lib()
+    src_hash = kernel_source_hash()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration} MiB copied 3 times")
+
+    result = {}
+    cfg = synth.CONFIGS[2]
+    B, L, D, N = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    updates = B * L * D * N
+    if not args.secondary_only:
+        t0 = time.time()
+        inp = synth.config_inputs(2)
+        log(f"generated {cfg['name']} inputs in {time.time() - t0:.1f}s")
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        x, dl, z, Bm, Cm = (up(inp[k]) for k in ("x", "delta", "z", "B", "C"))
+        A = torch.from_numpy(inp["A"]).to(dev)
+        Dk = torch.from_numpy(inp["Dskip"]).to(dev)
+        y = torch.empty_like(x)
+        plan = ssm.scan_plan(B, L, D, N, "bf16")
+        ws = None
+        if plan["workspace_bytes"]:
+            ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+
+        def step():
+            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        steps = args.steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            step()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        kms = [s.elapsed_time(e) for s, e in ev]
+        k_avg = sum(kms) / len(kms)
+        k_min = min(kms)
+        ms_per_step = elapsed * 1e3 / steps
+        value = updates * steps / elapsed
+        alg_bytes = scan_bytes(B, L, D, N, 2, True)
+        alg_slots = updates * SLOTS_PER_UPDATE + B * L * D * SLOTS_PER_TOKEN_CHANNEL_GATED
+        hbm_gbs = alg_bytes / (k_avg * 1e-3) / 1e9
+        alu_tslots = alg_slots / (k_avg * 1e-3) / 1e12
+        traffic = load_traffic("scan_cfg2", src_hash)
+        roofline = {"bound": "alu", "achieved": round(alu_tslots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                    "unit": "Tslot/s", "frac": round(alu_tslots / VALU_PEAK_TSLOTS, 4),
+                    "traffic": traffic,
+                    "kernel": "scan_kernel<bf16, G=%d, TB=%d, gated>" % (plan["states_per_lane"], plan["time_block"]),
+                    "kernel_ms_avg": round(k_avg, 5), "kernel_ms_min": round(k_min, 5),
+                    "alg_slots_per_launch": alg_slots, "alg_bytes_per_launch": alg_bytes,
+                    "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}}
+        log(f"scan: {k_avg * 1e3:.1f} us/launch avg ({k_min * 1e3:.1f} min), {value:.3e} updates/s, "
+            f"HBM {hbm_gbs:.0f} GB/s ({hbm_gbs / HBM_PEAK_GBS:.1%}), VALU {alu_tslots / VALU_PEAK_TSLOTS:.1%}")
+        result.update({
+            "metric": "state-updates/s (B*L*D*N), scan B4 L4096 D4096 N16",
+            "value": value, "unit": "state-updates/s", "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded generator: x,z,B,C ~ N(0,1), delta log-uniform [1e-3,1e-1], "
+                    "A=-(n+1), D ~ N(1,0.1))",
+            "config": {"workload": cfg["name"], "batch": B, "seqlen": L, "dim": D, "dstate": N,
+                       "io_dtype": "bf16", "state_dtype": "f32", "gate": True, "plan": plan},
+            "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+            "roofline": roofline,
+            "source_hash": src_hash,
+        })
+        del x, dl, z, Bm, Cm, y
+
+        if not args.no_cpu_baseline:
+            import oracle
+            cores = oracle.default_threads()
+            w = lambda a: synth.to_f64(a, "bf16")
+            t0 = time.time()
+            ch_b = np.repeat(np.arange(B), D)
+            ch_d = np.tile(np.arange(D), B)
+            xs = w(inp["x"]).transpose(0, 2, 1).reshape(B * D, L)
+            ds = w(inp["delta"]).transpose(0, 2, 1).reshape(B * D, L)
+            zs = w(inp["z"]).transpose(0, 2, 1).reshape(B * D, L)
+            Bw, Cw = w(inp["B"]), w(inp["C"])
+            log(f"oracle inputs widened in {time.time() - t0:.1f}s; timing the oracle on {cores} threads")
+            t0 = time.perf_counter()
+            oracle.scan_f64(xs, ds, inp["A"], Bw, Cw, inp["Dskip"], zs, None, False, ch_b, ch_d,
+                            nthreads=cores)
+            t_cpu = time.perf_counter() - t0
+            result["cpu_baseline"] = {
+                "value": updates / t_cpu, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+                "sample": f"the whole headline input (all {B * D} channels x {L} steps, "
+                          f"{updates:.3e} updates), fp64 C oracle, {t_cpu:.2f} s wall",
+                "cpu": platform.processor() or platform.machine()}
+            log(f"oracle: {t_cpu:.2f}s on {cores} threads -> {updates / t_cpu:.3e} updates/s")
+            del xs, ds, zs
+
+    if not args.no_secondary:
+        result["secondary"] = secondary(torch, ssm, synth, dev, log, src_hash)
+
+    print(json.dumps(result), flush=True)
+
+
+def _randn(shape, gen, dev, dtype):
+    import torch
+    return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(dtype)
+
+
+def _delta(shape, gen, dev, dtype):
+    import math
+    import torch
+    u = torch.rand(shape, generator=gen, device=dev, dtype=torch.float32)
+    lo, hi = math.log(1e-3), math.log(1e-1)
+    return torch.exp(lo + (hi - lo) * u).to(dtype)
+
+
+def secondary(torch, ssm, synth, dev, log, src_hash):
+    """Decode (1024 steps) and the million-token chunked scan.  Inputs drawn on the
+    GPU with torch's seeded generator, same distributions as the headline input."""
+    out = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    bf = torch.bfloat16
+    # --- decode: h[256, 4096, 16] fp32, 1024 gated steps from zero ---
+    c = synth.CONFIGS[4]
+    Bsz, D, N, S = c["batch"], c["dim"], c["dstate"], c["seqlen"]
+    A = torch.from_numpy(synth.make_A(4, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(4, D, "normal")).to(dev)
+    xs = _randn((S, Bsz, D), gen, dev, bf)
+    ds = _delta((S, Bsz, D), gen, dev, bf)
+    zs = _randn((S, Bsz, D), gen, dev, bf)
+    Bs = _randn((S, Bsz, N), gen, dev, bf)
+    Cs = _randn((S, Bsz, N), gen, dev, bf)
+    h = torch.zeros((Bsz, D, N), device=dev)
+    y = torch.empty((Bsz, D), dtype=bf, device=dev)
+
+    def run_decode():
+        h.zero_()
+        for s in range(S):
+            ssm.state_update(h, xs[s], ds[s], A, Bs[s], Cs[s], Dk, zs[s], out=y)
+
+    run_decode()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    h.zero_()
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(S):
+        kev[s][0].record()
+        ssm.state_update(h, xs[s], ds[s], A, Bs[s], Cs[s], Dk, zs[s], out=y)
+        kev[s][1].record()
+    e1.record()
+    torch.cuda.synchronize()
+    tot_ms = e0.elapsed_time(e1)
+    k_avg = sum(a.elapsed_time(b) for a, b in kev) / S
+    step_bytes = Bsz * D * N * 8 + Bsz * D * 2 * 4 + 2 * Bsz * N * 2 + D * N * 4 + D * 4
+    out["decode"] = {
+        "workload": c["name"], "tokens_per_s": Bsz * S / (tot_ms * 1e-3),
+        "state_updates_per_s": Bsz * D * N * S / (tot_ms * 1e-3), "ms_total": tot_ms,
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (k_avg * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_bytes / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("state_update_cfg4", src_hash),
+                     "kernel_us_avg": round(k_avg * 1e3, 2), "alg_bytes_per_launch": step_bytes},
+        "note": "h (67 MB) fits the 256 MB Infinity Cache, so steps after the first can beat HBM",
+    }
+    log(f"decode: {tot_ms:.2f} ms for {S} steps, kernel {k_avg * 1e3:.1f} us avg")
+    del xs, ds, zs, Bs, Cs, h
+    torch.cuda.empty_cache()
+    # --- million-token scan (chunk carries) ---
+    c = synth.CONFIGS[3]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    x = _randn((Bsz, L, D), gen, dev, bf)
+    dl = _delta((Bsz, L, D), gen, dev, bf)
+    Bm = _randn((Bsz, L, N), gen, dev, bf)
+    Cm = _randn((Bsz, L, N), gen, dev, bf)
+    A = torch.from_numpy(synth.make_A(3, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(3, D, "normal")).to(dev)
+    plan = ssm.scan_plan(Bsz, L, D, N, "bf16")
+    ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    reps = 5
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, out=y, workspace=ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    upd = Bsz * L * D * N
+    byts = scan_bytes(Bsz, L, D, N, 2, False)
+    slots = upd * SLOTS_PER_UPDATE + Bsz * L * D * SLOTS_PER_TOKEN_CHANNEL
+    out["long_sequence"] = {
+        "workload": c["name"], "state_updates_per_s": upd / (ms * 1e-3), "ms_per_call": ms,
+        "plan": plan, "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "alu_frac_single_pass_work": round(slots / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+        "note": "all launches of one call (carry pass, combine, rescan) inside the events",
+    }
+    log(f"long sequence: {ms:.2f} ms/call, {upd / (ms * 1e-3):.3e} updates/s, plan {plan}")
+    return out
+
+
+if __name__ == "__main__":
+    main()

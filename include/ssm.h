@@ -1,0 +1,168 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective-scan library (libssm.so).
+ *
+ * The library computes the Mamba (S6) selective scan and its single-token
+ * recurrent state update.  For every batch row b, channel d and state n:
+ *
+ *     dA      = exp(delta[b,t,d] * A[d,n])                  (discretised A)
+ *     h[n]    = dA * h[n] + delta[b,t,d] * B[b,t,n] * x[b,t,d]
+ *     y[b,t,d] = sum_n C[b,t,n] * h[n] + Dskip[d] * x[b,t,d]
+ *     y[b,t,d] = y[b,t,d] * z * sigmoid(z),  z = z[b,t,d]   (optional gate)
+ *
+ * Sources: the "selective_scan(x, delta, A, B, C, D)" listing and the
+ * MambaBlock listing (gate y * silu(z)) on managen.ai, "Mamba: State Space
+ * Models Challenge Transformers"; the MambaBlock._selective_scan listing on the
+ * "State Space Models Mamba" skill page (A_bar = exp(delta A), B_bar = delta
+ * B, readout after the update, skip term D u); the inference-mode update on
+ * brentwoodlivery, "State-space models (Mamba, S4)", section "Training vs
+ * Inference Modes".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers (HIP global memory) on the
+ *   current device, contiguous and row-major, 16-byte aligned.
+ * - Layouts: x, delta, z, y are [batch, seqlen, dim] with dim fastest;
+ *   B and C are [batch, seqlen, dstate] with dstate fastest; A is [dim, dstate];
+ *   Dskip is [dim]; every state (h0, h_last, h) is [batch, dim, dstate] fp32.
+ * - `dtype` applies to x, delta, z, B, C and y.  A, Dskip and all states are fp32.
+ *   bf16 outputs are rounded to nearest-even from the fp32 accumulator.
+ * - The caller owns and allocates all memory, including the scan workspace
+ *   (size from ssm_scan_workspace_bytes).  The library never allocates,
+ *   frees or synchronises.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *   Argument checks run on the host before any launch; a rejected call
+ *   launches nothing and writes nothing.  Faults inside a kernel surface at
+ *   the caller's next synchronisation.
+ * - Return value: an ssm_status.  On anything but SSM_OK a one-line reason is
+ *   available from ssm_last_error() (per thread).  Nothing aborts, throws
+ *   across the ABI or prints.
+ * - Thread safety: the library holds no global state beyond the per-thread
+ *   error text; concurrent calls on different streams are independent.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_DSTATE 16
+
+typedef enum ssm_dtype {
+    SSM_DTYPE_F32 = 0,
+    SSM_DTYPE_BF16 = 1
+} ssm_dtype;
+
+typedef enum ssm_status {
+    SSM_OK = 0,
+    SSM_EINVAL = 1,        /* bad shape, null or misaligned pointer, overlapping output */
+    SSM_EUNSUPPORTED = 2,  /* valid request this build does not implement (dstate > 16) */
+    SSM_EWORKSPACE = 3,    /* workspace missing or smaller than ssm_scan_workspace_bytes() */
+    SSM_EHIP = 4           /* the HIP runtime refused a launch */
+} ssm_status;
+
+/* Optional tuning of ssm_scan_fwd.  A NULL pointer or a zero field means
+ * "choose automatically".  None of these change the result beyond fp32
+ * rounding order. */
+typedef struct ssm_scan_opts {
+    int64_t chunk_len;     /* length of the sequence chunks scanned in parallel (>= 1) */
+    int32_t states_per_lane; /* 1, 2, 4, 8 or 16 states of one channel per GPU lane */
+    int32_t time_block;    /* time steps staged per block: 8, 16 or 32 */
+} ssm_scan_opts;
+
+/* What ssm_scan_fwd will launch for a given shape (host-only query). */
+typedef struct ssm_scan_plan {
+    int64_t chunk_len;
+    int64_t n_chunks;        /* 1 = single pass; > 1 = chunk carries + combine + rescan */
+    int32_t states_per_lane;
+    int32_t waves_per_block;
+    int32_t time_block;
+    int32_t reserved;
+    uint64_t workspace_bytes;
+    uint64_t blocks;         /* workgroups of the main scan launch */
+} ssm_scan_plan;
+
+/* ABI version of the loaded library (SSM_ABI_VERSION at build time). */
+int ssm_abi_version(void);
+
+/* Static text for a status code ("ok", "invalid argument", ...). */
+const char *ssm_status_str(int status);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *ssm_last_error(void);
+
+/* Host-only: fill *plan for this shape.  Returns SSM_OK, or the status the
+ * same shape would get from ssm_scan_fwd's shape checks. */
+int ssm_scan_plan_get(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                      const ssm_scan_opts *opts, ssm_scan_plan *plan);
+
+/* Host-only: bytes of device workspace ssm_scan_fwd needs for this shape and
+ * these options (0 when the scan runs in one pass, or the shape is invalid). */
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int dtype, const ssm_scan_opts *opts);
+
+/*
+ * Selective scan over a whole sequence (training / prefill form).
+ *
+ * Defines y[b,t,d] for t in [0, seqlen) by the recurrence above, starting
+ * from h = h0[b,d,:] (or zeros when h0 is NULL), and stores the final state
+ * in h_last (when not NULL).  The sequence is cut into chunks scanned in
+ * parallel; chunk carries (product of dA over the chunk, end state from
+ * zero) are combined with the associative operator
+ *     (P1, H1) o (P2, H2) = (P2 * P1, P2 * H1 + H2)
+ * (the parallel associative scan of the skill page's "Hardware-Efficient
+ * Scan" section, with the operator derived from its recurrence).
+ *
+ *   x, delta  [batch, seqlen, dim]   dtype   required
+ *   A         [dim, dstate]          fp32    required; finite, usually <= 0
+ *   B, C      [batch, seqlen, dstate] dtype  required
+ *   Dskip     [dim]                  fp32    NULL = no skip term
+ *   z         [batch, seqlen, dim]   dtype   NULL = no output gate
+ *   h0        [batch, dim, dstate]   fp32    NULL = zero start state
+ *   h_last    [batch, dim, dstate]   fp32    NULL = not stored; must not overlap h0
+ *   y         [batch, seqlen, dim]   dtype   output; must not overlap any input
+ *   delta_softplus  0: delta is the step size;  1: step size = log(1 + exp(delta))
+ *   opts      NULL or tuning (see ssm_scan_opts)
+ *   workspace device memory of ssm_scan_workspace_bytes() bytes (NULL if 0)
+ *
+ * batch, seqlen or dim == 0 is a valid no-op (with seqlen == 0, h_last
+ * receives h0 or zeros).  1 <= dstate <= 16, else SSM_EINVAL (< 1) or
+ * SSM_EUNSUPPORTED (> 16).
+ */
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                 const void *x, const void *delta, const float *A, const void *B,
+                 const void *C, const float *Dskip, const void *z, const float *h0,
+                 float *h_last, void *y, int delta_softplus, const ssm_scan_opts *opts,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Single-token recurrent state update (generation form): one step of the
+ * recurrence for every (b, d), with the state kept in HBM between calls.
+ * brentwoodlivery, "Training vs Inference Modes": keep h_{k-1}, receive x_k,
+ * update h_k, emit y_k, constant work per token.
+ *
+ *   h         [batch, dim, dstate]   fp32    read and overwritten in place
+ *   x, delta  [batch, dim]           dtype   required
+ *   A         [dim, dstate]          fp32    required
+ *   B, C      [batch, dstate]        dtype   required
+ *   Dskip     [dim]                  fp32    NULL = no skip term
+ *   z         [batch, dim]           dtype   NULL = no output gate
+ *   y         [batch, dim]           dtype   output; must not overlap any input or h
+ *
+ * L consecutive calls give the same y and final h as one ssm_scan_fwd over
+ * those L tokens (up to fp32 rounding order).
+ */
+int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, float *h,
+                     const void *x, const void *delta, const float *A, const void *B,
+                     const void *C, const float *Dskip, const void *z, void *y,
+                     int delta_softplus, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,228 @@
+"""MI355X (gfx950) selective scan: thin Python binding of libssm.so.
+
+The binding only marshals arguments: it checks tensor dtypes, devices and
+contiguity, allocates outputs and the workspace with torch, and passes raw
+device pointers plus torch's current HIP stream to the C ABI declared in
+``include/ssm.h``.  Every step of the computation runs in the HIP kernels.
+There is no CPU fallback: if the library is missing or fails to load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = ["scan_fwd", "state_update", "scan_plan", "scan_workspace_bytes", "lib", "SSMError",
+           "LIB_PATH", "HEADER_PATH", "exported_api"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
+
+SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func} failed with status {status} ({_status_name(status)}): {detail}")
+
+
+class ScanOpts(ctypes.Structure):
+    _fields_ = [("chunk_len", ctypes.c_int64), ("states_per_lane", ctypes.c_int32),
+                ("time_block", ctypes.c_int32)]
+
+
+class ScanPlan(ctypes.Structure):
+    _fields_ = [("chunk_len", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
+                ("states_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+                ("time_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64), ("blocks", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libssm.so (built in-tree by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libssm.so not found at {LIB_PATH}: build it first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    I64, I32, P, SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.ssm_abi_version.restype = I32
+    L.ssm_abi_version.argtypes = []
+    L.ssm_status_str.restype = ctypes.c_char_p
+    L.ssm_status_str.argtypes = [I32]
+    L.ssm_last_error.restype = ctypes.c_char_p
+    L.ssm_last_error.argtypes = []
+    L.ssm_scan_plan_get.restype = I32
+    L.ssm_scan_plan_get.argtypes = [I64, I64, I64, I64, I32, ctypes.POINTER(ScanOpts),
+                                    ctypes.POINTER(ScanPlan)]
+    L.ssm_scan_workspace_bytes.restype = SZ
+    L.ssm_scan_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, ctypes.POINTER(ScanOpts)]
+    L.ssm_scan_fwd.restype = I32
+    L.ssm_scan_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, P, I32,
+                               ctypes.POINTER(ScanOpts), P, SZ, P]
+    L.ssm_state_update.restype = I32
+    L.ssm_state_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, I32, P]
+    if L.ssm_abi_version() != 1:
+        raise ImportError(f"libssm ABI version {L.ssm_abi_version()} != 1")
+    _lib = L
+    return L
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().ssm_status_str(status).decode()
+    except Exception:  # pragma: no cover - used while building an error message
+        return "?"
+
+
+def _check(status: int, func: str):
+    if status != SSM_OK:
+        raise SSMError(status, func, lib().ssm_last_error().decode())
+
+
+def exported_api():
+    """Function names declared in include/ssm.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
+
+
+def _opts(chunk_len=0, states_per_lane=0, time_block=0):
+    if not (chunk_len or states_per_lane or time_block):
+        return None
+    return ScanOpts(int(chunk_len), int(states_per_lane), int(time_block))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def scan_plan(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0, states_per_lane=0,
+              time_block=0) -> dict:
+    """What ssm_scan_fwd will launch for this shape (host-only)."""
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    p = ScanPlan()
+    o = _opts(chunk_len, states_per_lane, time_block)
+    _check(lib().ssm_scan_plan_get(batch, seqlen, dim, dstate, code,
+                                   ctypes.byref(o) if o else None, ctypes.byref(p)),
+           "ssm_scan_plan_get")
+    return {k: getattr(p, k) for k, _ in ScanPlan._fields_ if k != "reserved"}
+
+
+def scan_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0,
+                         states_per_lane=0, time_block=0) -> int:
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    o = _opts(chunk_len, states_per_lane, time_block)
+    return int(lib().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, code,
+                                              ctypes.byref(o) if o else None))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
+             return_last_state=False, out=None, h_last=None, workspace=None, chunk_len=0,
+             states_per_lane=0, time_block=0, stream=None):
+    """Selective scan y = S6(x, delta, A, B, C, D) [* silu(z)] on the GPU.
+
+    x, delta, z: [B, L, D];  B, C: [B, L, N];  A: [D, N] fp32;  D: [D] fp32;
+    h0: [B, D, N] fp32.  x/delta/z/B/C share one dtype (bfloat16 or float32).
+    Returns y (same dtype as x), or (y, h_last) when return_last_state.
+    """
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, dim] and A [dim, dstate]")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd runs on the GPU only; tensors must be on a cuda device")
+    _need(x, "x", (Bsz, L, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, L, Dm), dt, dev)
+    _need(z, "z", (Bsz, L, Dm), dt, dev)
+    _need(B, "B", (Bsz, L, N), dt, dev)
+    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _need(h0, "h0", (Bsz, Dm, N), torch.float32, dev)
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, L, Dm), dt, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
+    _need(h_last, "h_last", (Bsz, Dm, N), torch.float32, dev)
+    o = _opts(chunk_len, states_per_lane, time_block)
+    ws_bytes = int(lib().ssm_scan_workspace_bytes(Bsz, L, Dm, N, code, ctypes.byref(o) if o else None))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_scan_fwd(Bsz, L, Dm, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(z), _ptr(h0), _ptr(h_last), _ptr(out),
+                            int(bool(delta_softplus)), ctypes.byref(o) if o else None,
+                            _ptr(workspace) if ws_bytes else None, ws_bytes,
+                            ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_scan_fwd")
+    return (out, h_last) if return_last_state else out
+
+
+def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False, out=None,
+                 stream=None):
+    """One recurrent step: updates h [B, D, N] fp32 in place and returns y [B, D].
+
+    x, delta, z: [B, D];  B, C: [B, N];  A: [D, N] fp32;  D: [D] fp32.
+    """
+    import torch
+    if h.dim() != 3:
+        raise ValueError("h must be [batch, dim, dstate]")
+    Bsz, Dm, N = h.shape
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("state_update runs on the GPU only; tensors must be on a cuda device")
+    _need(h, "h", (Bsz, Dm, N), torch.float32, dev)
+    _need(x, "x", (Bsz, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, Dm), dt, dev)
+    _need(z, "z", (Bsz, Dm), dt, dev)
+    _need(B, "B", (Bsz, N), dt, dev)
+    _need(C, "C", (Bsz, N), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, Dm), dt, dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_state_update(Bsz, Dm, N, code, _ptr(h), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                _ptr(C), _ptr(D), _ptr(z), _ptr(out), int(bool(delta_softplus)),
+                                ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_state_update")
+    return out

@@ -1,0 +1,324 @@
+// Host-side argument checks, launch planning and error text for libssm.
+#include "ssm_host.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+namespace ssm {
+
+namespace {
+thread_local char g_err[512] = {0};
+
+constexpr int64_t kMaxElems = int64_t(1) << 50;  // keeps every byte offset far from int64 overflow
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char *name, const void *p, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_dims(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+    if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16) {
+        set_error("dtype %d is neither SSM_DTYPE_F32 (0) nor SSM_DTYPE_BF16 (1)", dtype);
+        return SSM_EINVAL;
+    }
+    if (batch < 0 || seqlen < 0 || dim < 0) {
+        set_error("negative size (batch=%lld seqlen=%lld dim=%lld)", (long long)batch,
+                  (long long)seqlen, (long long)dim);
+        return SSM_EINVAL;
+    }
+    if (dstate < 1) {
+        set_error("dstate=%lld: need at least one state", (long long)dstate);
+        return SSM_EINVAL;
+    }
+    if (dstate > SSM_MAX_DSTATE) {
+        set_error("dstate=%lld exceeds the supported maximum %d", (long long)dstate, SSM_MAX_DSTATE);
+        return SSM_EUNSUPPORTED;
+    }
+    // overflow-safe product checks
+    if (batch > 0 && seqlen > 0 && dim > 0) {
+        if (seqlen > kMaxElems / batch || dim > kMaxElems / (batch * seqlen) ||
+            dstate > kMaxElems / (batch * seqlen)) {
+            set_error("tensor of %lld x %lld x %lld elements is too large", (long long)batch,
+                      (long long)seqlen, (long long)dim);
+            return SSM_EINVAL;
+        }
+    }
+    if (batch > 0 && dim > 0 && dim > kMaxElems / (batch * dstate)) {
+        set_error("state of %lld x %lld x %lld elements is too large", (long long)batch,
+                  (long long)dim, (long long)dstate);
+        return SSM_EINVAL;
+    }
+    return SSM_OK;
+}
+
+int check_no_overlap(const Range *outs, int n_out, const Range *all, int n_all) {
+    for (int i = 0; i < n_out; ++i)
+        for (int j = 0; j < n_all; ++j) {
+            if (outs[i].lo == all[j].lo && outs[i].hi == all[j].hi &&
+                std::strcmp(outs[i].name, all[j].name) == 0)
+                continue;  // itself
+            if (overlaps(outs[i], all[j])) {
+                set_error("output %s overlaps %s", outs[i].name, all[j].name);
+                return SSM_EINVAL;
+            }
+        }
+    return SSM_OK;
+}
+
+int check_aligned(const Range *all, int n) {
+    for (int i = 0; i < n; ++i)
+        if (all[i].lo && !aligned16(reinterpret_cast<const void *>(all[i].lo))) {
+            set_error("pointer %s is not 16-byte aligned", all[i].name);
+            return SSM_EINVAL;
+        }
+    return SSM_OK;
+}
+}  // namespace
+
+void set_error(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+              const ssm_scan_opts *opts, ScanPlan *plan) {
+    int st = check_dims(batch, seqlen, dim, dstate, dtype);
+    if (st != SSM_OK) return st;
+    ssm_scan_opts o{0, 0, 0};
+    if (opts) o = *opts;
+    if (o.chunk_len < 0) {
+        set_error("opts.chunk_len=%lld is negative", (long long)o.chunk_len);
+        return SSM_EINVAL;
+    }
+    if (!(o.states_per_lane == 0 || o.states_per_lane == 1 || o.states_per_lane == 2 ||
+          o.states_per_lane == 4 || o.states_per_lane == 8 || o.states_per_lane == 16)) {
+        set_error("opts.states_per_lane=%d is not 0, 1, 2, 4, 8 or 16", o.states_per_lane);
+        return SSM_EINVAL;
+    }
+    if (!(o.time_block == 0 || o.time_block == 8 || o.time_block == 16 || o.time_block == 32)) {
+        set_error("opts.time_block=%d is not 0, 8, 16 or 32", o.time_block);
+        return SSM_EINVAL;
+    }
+    ScanPlan p;
+    // states per lane: default 4 (a quarter of the N=16 state in each of four waves)
+    int G = o.states_per_lane;
+    if (G == 0) {
+        G = 1;
+        while (G < dstate && G < 4) G *= 2;
+    }
+    p.G = G;
+    p.NW = static_cast<int>(ceil_div(dstate, G));
+    // time block: each thread stages ceil(TB / NW) <= 8 rows, and the
+    // workgroup's LDS (step sizes, B/C rows, per-wave y shares) stays <= 64 KiB
+    auto rows_ok = [&](int tb) { return (tb + p.NW - 1) / p.NW <= 8; };
+    auto lds_ok = [&](int tb) {
+        const int64_t np = static_cast<int64_t>(p.NW) * p.G;
+        return 4 * (tb * 64 * 2 + 2 * tb * np + static_cast<int64_t>(p.NW) * tb * 64) <= 65536;
+    };
+    if (o.time_block) {
+        if (!rows_ok(o.time_block) || !lds_ok(o.time_block)) {
+            set_error("opts.time_block=%d does not fit %d waves of %d states", o.time_block, p.NW, p.G);
+            return SSM_EINVAL;
+        }
+        p.TB = o.time_block;
+    } else {
+        p.TB = 8;
+        for (int tb : {32, 16}) {
+            if (rows_ok(tb) && lds_ok(tb)) {
+                p.TB = tb;
+                break;
+            }
+        }
+    }
+    const int64_t dblocks = ceil_div(dim, kChannelsPerBlock);
+    // sequence chunks: split only when one pass leaves most SIMDs idle
+    int64_t n_chunks = 1;
+    if (seqlen > 0) {
+        if (o.chunk_len > 0) {
+            n_chunks = ceil_div(seqlen, o.chunk_len);
+        } else {
+            const int64_t waves = batch * dblocks * p.NW;
+            const int64_t kSimds = 1024;      // 256 CUs x 4 SIMDs
+            const int64_t kMinChunk = 2048;   // keeps the carry pass's share small
+            if (waves > 0 && waves * 2 <= kSimds) {
+                int64_t want = ceil_div(2 * kSimds, waves);
+                int64_t cap = ceil_div(seqlen, kMinChunk);
+                n_chunks = want < cap ? want : cap;
+                if (n_chunks < 1) n_chunks = 1;
+            }
+        }
+    }
+    p.chunk_len = seqlen > 0 ? ceil_div(seqlen, n_chunks) : 0;
+    p.n_chunks = seqlen > 0 ? ceil_div(seqlen, p.chunk_len > 0 ? p.chunk_len : 1) : 1;
+    if (p.n_chunks > 1) {
+        const size_t carries = static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks - 1) *
+                               static_cast<size_t>(dim);
+        p.ws_S_off = 0;
+        p.ws_H_off = align_up(carries * sizeof(float), kWsAlign);
+        p.ws_bytes = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float),
+                              kWsAlign);
+    }
+    // grid: x = 64-channel blocks, y = batch rows, z = chunks (hardware limit 65535 on y and z)
+    if (batch > 65535 || p.n_chunks > 65535 || dblocks > 0x7fffffff) {
+        set_error("grid too large (batch=%lld, chunks=%lld): at most 65535 of each",
+                  (long long)batch, (long long)p.n_chunks);
+        return SSM_EUNSUPPORTED;
+    }
+    p.blocks = static_cast<uint64_t>(dblocks) * static_cast<uint64_t>(batch) *
+               static_cast<uint64_t>(p.n_chunks);
+    *plan = p;
+    return SSM_OK;
+}
+
+int check_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+               const void *x, const void *delta, const float *A, const void *B, const void *C,
+               const float *Dskip, const void *z, const float *h0, const float *h_last,
+               const void *y, int delta_softplus, const ssm_scan_opts *opts,
+               const void *workspace, size_t workspace_bytes, ScanPlan *plan) {
+    int st = plan_scan(batch, seqlen, dim, dstate, dtype, opts, plan);
+    if (st != SSM_OK) return st;
+    if (delta_softplus != 0 && delta_softplus != 1) {
+        set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
+        return SSM_EINVAL;
+    }
+    if (batch == 0 || dim == 0) return SSM_OK;  // nothing to compute or store
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    const int64_t tok = batch * seqlen * dim * es;
+    const int64_t bc = batch * seqlen * dstate * es;
+    const int64_t st_bytes = batch * dim * dstate * 4;
+    if (seqlen > 0) {
+        const char *missing = !x ? "x" : !delta ? "delta" : !A ? "A" : !B ? "B" : !C ? "C" : !y ? "y" : nullptr;
+        if (missing) {
+            set_error("required pointer %s is NULL", missing);
+            return SSM_EINVAL;
+        }
+    }
+    Range all[] = {
+        range("x", x, tok),           range("delta", delta, tok),
+        range("z", z, tok),           range("B", B, bc),
+        range("C", C, bc),            range("A", A, dim * dstate * 4),
+        range("Dskip", Dskip, dim * 4), range("h0", h0, st_bytes),
+        range("h_last", h_last, st_bytes), range("y", y, seqlen > 0 ? tok : 0),
+        range("workspace", workspace, static_cast<int64_t>(plan->ws_bytes)),
+    };
+    const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
+    st = check_aligned(all, n_all);
+    if (st != SSM_OK) return st;
+    Range outs[] = {all[9], all[8], all[10]};  // y, h_last, workspace
+    st = check_no_overlap(outs, 3, all, n_all);
+    if (st != SSM_OK) return st;
+    if (plan->ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan->ws_bytes) {
+            set_error("workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                      plan->ws_bytes);
+            return SSM_EWORKSPACE;
+        }
+    }
+    return SSM_OK;
+}
+
+int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, const float *h,
+                       const void *x, const void *delta, const float *A, const void *B,
+                       const void *C, const float *Dskip, const void *z, const void *y,
+                       int delta_softplus) {
+    int st = check_dims(batch, 1, dim, dstate, dtype);
+    if (st != SSM_OK) return st;
+    if (delta_softplus != 0 && delta_softplus != 1) {
+        set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
+        return SSM_EINVAL;
+    }
+    if (batch == 0 || dim == 0) return SSM_OK;
+    if (batch * dim > (int64_t(1) << 34)) {   // 16 lanes per channel at most, 256-thread blocks
+        set_error("batch*dim=%lld is too large for one launch", (long long)(batch * dim));
+        return SSM_EUNSUPPORTED;
+    }
+    const char *missing = !h ? "h" : !x ? "x" : !delta ? "delta" : !A ? "A" : !B ? "B" : !C ? "C" : !y ? "y" : nullptr;
+    if (missing) {
+        set_error("required pointer %s is NULL", missing);
+        return SSM_EINVAL;
+    }
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    Range all[] = {
+        range("h", h, batch * dim * dstate * 4), range("x", x, batch * dim * es),
+        range("delta", delta, batch * dim * es), range("z", z, batch * dim * es),
+        range("B", B, batch * dstate * es),     range("C", C, batch * dstate * es),
+        range("A", A, dim * dstate * 4),        range("Dskip", Dskip, dim * 4),
+        range("y", y, batch * dim * es),
+    };
+    const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
+    st = check_aligned(all, n_all);
+    if (st != SSM_OK) return st;
+    Range outs[] = {all[8], all[0]};  // y, h
+    return check_no_overlap(outs, 2, all, n_all);
+}
+
+}  // namespace ssm
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char *ssm_status_str(int status) {
+    switch (status) {
+        case SSM_OK: return "ok";
+        case SSM_EINVAL: return "invalid argument";
+        case SSM_EUNSUPPORTED: return "unsupported";
+        case SSM_EWORKSPACE: return "workspace too small";
+        case SSM_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *ssm_last_error(void) { return ssm::g_err; }
+
+int ssm_scan_plan_get(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                      const ssm_scan_opts *opts, ssm_scan_plan *out) {
+    ssm::clear_error();
+    if (!out) {
+        ssm::set_error("plan pointer is NULL");
+        return SSM_EINVAL;
+    }
+    ssm::ScanPlan p;
+    int st = ssm::plan_scan(batch, seqlen, dim, dstate, dtype, opts, &p);
+    if (st != SSM_OK) return st;
+    std::memset(out, 0, sizeof(*out));
+    out->chunk_len = p.chunk_len;
+    out->n_chunks = p.n_chunks;
+    out->states_per_lane = p.G;
+    out->waves_per_block = p.NW;
+    out->time_block = p.TB;
+    out->workspace_bytes = p.ws_bytes;
+    out->blocks = p.blocks;
+    return SSM_OK;
+}
+
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                int dtype, const ssm_scan_opts *opts) {
+    ssm::ScanPlan p;
+    if (ssm::plan_scan(batch, seqlen, dim, dstate, dtype, opts, &p) != SSM_OK) return 0;
+    return p.ws_bytes;
+}
+
+}  // extern "C"

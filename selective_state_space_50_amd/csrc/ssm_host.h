@@ -1,0 +1,53 @@
+// Host-side argument checks and launch planning for libssm (no HIP here, so
+// the same code builds with g++ under sanitizers for CPU tests).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ssm.h"
+
+namespace ssm {
+
+constexpr int kWave = 64;            // lanes per wavefront on gfx950
+constexpr int kChannelsPerBlock = 64; // one channel per lane of a wave
+constexpr int kMaxWavesPerBlock = 16;
+constexpr size_t kWsAlign = 256;
+
+struct ScanPlan {
+    int G = 4;            // states of one channel held by one lane
+    int NW = 4;           // waves per workgroup = ceil(N / G)
+    int TB = 32;          // time steps staged per block
+    int64_t chunk_len = 0;
+    int64_t n_chunks = 1;
+    size_t ws_bytes = 0;  // workspace for chunk carries (0 when n_chunks == 1)
+    size_t ws_S_off = 0;  // byte offset of the per-chunk delta sums [B][C-1][D]
+    size_t ws_H_off = 0;  // byte offset of the per-chunk end states [B][C-1][D][N]
+    uint64_t blocks = 0;  // workgroups of the main scan launch
+};
+
+// Per-thread error text (ssm_last_error).
+void set_error(const char *fmt, ...);
+void clear_error();
+
+// Shape and option checks + plan.  Returns an ssm_status.
+int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+              const ssm_scan_opts *opts, ScanPlan *plan);
+
+// Full argument check of ssm_scan_fwd (shape, pointers, alignment, overlap,
+// workspace).  Returns an ssm_status; fills *plan on success.
+int check_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+               const void *x, const void *delta, const float *A, const void *B, const void *C,
+               const float *Dskip, const void *z, const float *h0, const float *h_last,
+               const void *y, int delta_softplus, const ssm_scan_opts *opts,
+               const void *workspace, size_t workspace_bytes, ScanPlan *plan);
+
+// Full argument check of ssm_state_update.
+int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, const float *h,
+                       const void *x, const void *delta, const float *A, const void *B,
+                       const void *C, const float *Dskip, const void *z, const void *y,
+                       int delta_softplus);
+
+inline size_t dtype_size(int dtype) { return dtype == SSM_DTYPE_BF16 ? 2 : 4; }
+
+}  // namespace ssm

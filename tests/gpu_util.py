@@ -1,0 +1,71 @@
+"""Helpers shared by the GPU parity tests (device upload, the tolerance rule)."""
+from __future__ import annotations
+
+import numpy as np
+
+# Parity rule per element: |gpu - oracle| <= max(RTOL * |oracle|, ATOL).
+# bf16 inputs with an fp32 state: 1e-2 relative with a 1e-3 absolute floor.
+# fp32 inputs (and every fp32 state): 1e-4 relative with a 1e-5 absolute floor.
+TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-4, 1e-5)}
+
+
+def to_dev(a, dtype):
+    import torch
+    if a is None:
+        return None
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def to_host(t):
+    import torch
+    return t.float().cpu().numpy().astype(np.float64) if t.dtype != torch.float64 else t.cpu().numpy()
+
+
+def device_inputs(inp):
+    import torch
+    dt = inp["dtype"]
+    out = {k: to_dev(inp[k], dt) for k in ("x", "delta", "z", "B", "C")}
+    out["A"] = torch.from_numpy(inp["A"]).cuda()
+    out["D"] = torch.from_numpy(inp["Dskip"]).cuda()
+    out["h0"] = None if inp.get("h0") is None else torch.from_numpy(inp["h0"]).cuda()
+    return out
+
+
+def compare(g, r, dtype, what="y"):
+    """Returns a stats dict; 'bad' counts elements outside the rule (NaN must match NaN)."""
+    rtol, atol = TOL[dtype]
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    nan_g, nan_r = np.isnan(g), np.isnan(r)
+    both = nan_g & nan_r
+    err = np.where(both, 0.0, np.abs(g - r))
+    lim = np.maximum(rtol * np.abs(np.where(nan_r, 0, r)), atol)
+    ratio = np.where(both, 0.0, err / lim)
+    ratio = np.where(nan_g ^ nan_r, np.inf, ratio)
+    bad = int((ratio > 1.0).sum())
+    nz = np.abs(r) > 0
+    unfloored = float(np.max(np.where(nz & ~both, err / np.where(nz, np.abs(r), 1), 0))) if g.size else 0.0
+    norm = float(np.linalg.norm(np.where(both, 0, g - r)) / max(np.linalg.norm(np.where(nan_r, 0, r)), 1e-300)) if g.size else 0.0
+    return {"what": what, "bad": bad, "n": int(g.size),
+            "max_abs": float(err.max()) if g.size else 0.0,
+            "worst_ratio": float(ratio.max()) if g.size else 0.0,
+            "max_rel_unfloored": unfloored, "normwise": norm}
+
+
+def assert_close(g, r, dtype, what="y"):
+    st = compare(g, r, dtype, what)
+    assert st["bad"] == 0, f"{what}: {st['bad']}/{st['n']} elements out of tolerance; {st}"
+    return st
+
+
+def sample_channels(batch, dim, n):
+    """n distinct (b, d) channels spread over the batch and the channel axis (first and last included)."""
+    ch = {(0, 0), (batch - 1, dim - 1)}
+    i = 0
+    while len(ch) < min(n, batch * dim):
+        ch.add((i % batch, (i * 977 + 13) % dim))
+        i += 1
+    return sorted(ch)

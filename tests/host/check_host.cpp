@@ -1,0 +1,88 @@
+// Drives every argument-check path of libssm's host layer (built with g++
+// under AddressSanitizer + UndefinedBehaviorSanitizer; no GPU, no HIP).
+#include <cstdio>
+#include <cstdint>
+#include <cstring>
+#include <initializer_list>
+
+#include "ssm.h"
+#include "ssm_host.h"
+
+static int fails = 0;
+#define EXPECT(cond)                                                      \
+    do {                                                                  \
+        if (!(cond)) {                                                    \
+            std::printf("FAIL line %d: %s (%s)\n", __LINE__, #cond, ssm_last_error()); \
+            ++fails;                                                      \
+        }                                                                 \
+    } while (0)
+
+static void *P(uintptr_t a) { return reinterpret_cast<void *>(a); }
+
+int main() {
+    using namespace ssm;
+    ScanPlan p;
+    // fake, well-separated, 16-byte aligned device addresses (never dereferenced)
+    const uintptr_t base = uintptr_t(1) << 40, gap = uintptr_t(1) << 32;
+    void *x = P(base), *dl = P(base + gap), *z = P(base + 2 * gap), *B = P(base + 3 * gap),
+         *C = P(base + 4 * gap), *y = P(base + 5 * gap), *ws = P(base + 9 * gap);
+    float *A = static_cast<float *>(P(base + 6 * gap)), *Dk = static_cast<float *>(P(base + 7 * gap));
+    float *h0 = static_cast<float *>(P(base + 8 * gap)), *hl = static_cast<float *>(P(base + 10 * gap));
+    auto scan = [&](int64_t b, int64_t l, int64_t d, int64_t n, int dt, const void *x_, const void *y_,
+                    const ssm_scan_opts *o, const void *w, size_t wb, const float *h0_, const float *hl_) {
+        return check_scan(b, l, d, n, dt, x_, dl, A, B, C, Dk, z, h0_, hl_, y_, 0, o, w, wb, &p);
+    };
+    EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_OK);
+    EXPECT(p.n_chunks == 1 && p.G == 4 && p.NW == 4 && p.TB == 32 && p.ws_bytes == 0);
+    EXPECT(scan(4, 4096, 4096, 16, 2, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 17, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EUNSUPPORTED);
+    EXPECT(scan(4, 4096, 4096, 0, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(-1, 4096, 4096, 16, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, nullptr, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, P(base + 2), y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, x, P(base + 64), nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(std::strstr(ssm_last_error(), "overlaps") != nullptr);
+    EXPECT(scan(4, 4096, 4096, 16, 1, x, y, nullptr, nullptr, 0, h0, h0) == SSM_EINVAL);
+    EXPECT(scan(int64_t(1) << 30, int64_t(1) << 30, 4096, 16, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    // empty problems are valid no-ops, even with null data pointers
+    EXPECT(scan(0, 4096, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr) == SSM_OK);
+    EXPECT(scan(4, 0, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, 0, h0, hl) == SSM_OK);
+    // chunked plan needs a workspace
+    ssm_scan_opts o{1024, 0, 0};
+    EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
+    EXPECT(p.n_chunks == 8 && p.ws_bytes > 0);
+    const size_t need = p.ws_bytes;
+    EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, ws, need - 1, h0, hl) == SSM_EWORKSPACE);
+    EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, ws, need, h0, hl) == SSM_OK);
+    EXPECT(ssm_scan_workspace_bytes(1, 8192, 1024, 16, 1, &o) == need);
+    ssm_scan_opts bad1{-5, 0, 0}, bad2{0, 3, 0}, bad3{0, 0, 24}, bad4{0, 1, 32};
+    EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad1, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad2, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad3, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad4, nullptr, 0, h0, hl) == SSM_EINVAL);
+    // automatic chunking for a long, narrow sequence
+    EXPECT(scan(1, int64_t(1) << 20, 1024, 16, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
+    EXPECT(p.n_chunks > 1);
+    // every plan keeps the staging and LDS limits the kernel relies on
+    for (int n = 1; n <= 16; ++n)
+        for (int g : {0, 1, 2, 4, 8, 16}) {
+            ssm_scan_opts og{0, g, 0};
+            if (plan_scan(3, 1000, 100, n, 1, &og, &p) != SSM_OK) { EXPECT(false); continue; }
+            const int rows = (p.TB + p.NW - 1) / p.NW;
+            EXPECT(rows <= 8);
+            EXPECT(p.NW * p.G >= n && p.NW * p.G <= 16 && p.NW * 64 <= 1024);
+            EXPECT(4 * (p.TB * 128 + 2 * p.TB * p.NW * p.G + p.NW * p.TB * 64) <= 65536);
+        }
+    // state update
+    float *h = h0;
+    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 0) == SSM_OK);
+    EXPECT(check_state_update(256, 4096, 16, 1, nullptr, x, dl, A, B, C, Dk, z, y, 0) == SSM_EINVAL);
+    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, x, 0) == SSM_EINVAL);
+    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 2) == SSM_EINVAL);
+    EXPECT(check_state_update(256, 4096, 32, 1, h, x, dl, A, B, C, Dk, z, y, 0) == SSM_EUNSUPPORTED);
+    EXPECT(check_state_update(0, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, 0) == SSM_OK);
+    EXPECT(std::strcmp(ssm_status_str(SSM_EWORKSPACE), "workspace too small") == 0);
+    std::printf("%s: %d failure(s)\n", fails ? "FAILED" : "ok", fails);
+    return fails ? 1 : 0;
+}

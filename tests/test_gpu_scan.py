@@ -1,0 +1,230 @@
+"""GPU parity of ssm_scan_fwd against the fp64 oracle (MI355X only)."""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import assert_close, compare, device_inputs, sample_channels, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_50_amd as m
+    m.lib()
+    return m
+
+
+def _run_dev(ssm, inp, **kw):
+    import torch
+    t = device_inputs(inp)
+    y, hl = ssm.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                         delta_softplus=inp["delta_softplus"], return_last_state=True, **kw)
+    torch.cuda.synchronize()
+    return y, hl
+
+
+def _run(ssm, inp, **kw):
+    y, hl = _run_dev(ssm, inp, **kw)
+    return to_host(y), to_host(hl)
+
+
+def _log(name, st):
+    print(f"[parity] {name}: {json.dumps(st)}", flush=True)
+
+
+def test_worked_example(ssm):
+    """Pages' 2-D example in selective form (fp32 storage): h1=(0.47,0.45), y1=0.245."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_2d.json")) as f:
+        g = json.load(f)
+    inp = {
+        "x": np.array([[[g["x1"]]]], np.float32), "delta": np.ones((1, 1, 1), np.float32),
+        "z": None, "B": np.array(g["B_bar"], np.float32).reshape(1, 1, 2),
+        "C": np.array(g["C"], np.float32).reshape(1, 1, 2),
+        "A": np.log(np.array(g["A_bar_diag"])).astype(np.float32).reshape(1, 2),
+        "Dskip": np.zeros(1, np.float32), "h0": np.array(g["h0"], np.float32).reshape(1, 1, 2),
+        "dtype": "f32", "delta_softplus": False,
+    }
+    y, h = _run(ssm, inp)
+    assert abs(y[0, 0, 0] - g["expected_y1"]) < 1e-6
+    assert np.allclose(h[0, 0], g["expected_h1"], atol=1e-6)
+    yr, hr = oracle.scan(inp)
+    assert_close(y, yr, "f32")
+    assert_close(h, hr, "f32", "h_last")
+
+
+SMALL = [
+    # B, L, D, N, dtype, gate, h0, softplus, a_kind
+    (1, 1, 1, 1, "f32", False, False, False, "mamba"),
+    (1, 7, 3, 2, "f32", True, True, False, "random"),
+    (2, 33, 65, 16, "f32", True, True, False, "random"),
+    (3, 100, 130, 16, "bf16", True, True, False, "mamba"),
+    (2, 257, 64, 3, "bf16", False, True, True, "random"),
+    (1, 300, 200, 15, "bf16", True, False, False, "random"),
+    (2, 64, 96, 5, "f32", False, False, True, "mamba"),
+    (1, 95, 17, 9, "bf16", True, True, False, "random"),
+    (2, 40, 128, 12, "f32", True, False, False, "mamba"),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,N,dt,gate,h0,sp,ak", SMALL)
+def test_parity_small_shapes(ssm, Bsz, L, D, N, dt, gate, h0, sp, ak):
+    inp = synth.scan_inputs(Bsz, L, D, N, dt, seed=100 + L + D + N, gate=gate, d_kind="normal",
+                            a_kind=ak, softplus_input=sp, h0=h0)
+    y, h = _run(ssm, inp)
+    yr, hr = oracle.scan(inp)
+    _log(f"small {Bsz}x{L}x{D}x{N} {dt}", assert_close(y, yr, dt))
+    assert_close(h, hr, "f32", "h_last")
+
+
+@pytest.mark.parametrize("G,TB", [(1, 8), (2, 16), (4, 32), (4, 16), (8, 16), (16, 8)])
+def test_states_per_lane_variants(ssm, G, TB):
+    inp = synth.scan_inputs(2, 150, 130, 16, "f32", seed=5, gate=True, d_kind="normal",
+                            a_kind="random", h0=True)
+    y, h = _run(ssm, inp, states_per_lane=G, time_block=TB)
+    yr, hr = oracle.scan(inp)
+    assert_close(y, yr, "f32")
+    assert_close(h, hr, "f32", "h_last")
+
+
+@pytest.mark.parametrize("chunk", [64, 1000, 4096, 0])
+def test_split_invariance(ssm, chunk):
+    """Forced sequence chunks (carry pass + combine + rescan) match the oracle, and
+    the unchunked scan within 1e-5 (fp32)."""
+    inp = synth.scan_inputs(2, 8192, 128, 16, "f32", seed=21, gate=False, d_kind="normal",
+                            a_kind="random", h0=True)
+    plan = ssm.scan_plan(2, 8192, 128, 16, "f32", chunk_len=chunk)
+    y, h = _run(ssm, inp, chunk_len=chunk)
+    yr, hr = oracle.scan(inp)
+    _log(f"split chunk={chunk} plan={plan}", assert_close(y, yr, "f32"))
+    assert_close(h, hr, "f32", "h_last")
+    y1, h1 = _run(ssm, inp, chunk_len=8192)
+    assert np.max(np.abs(y - y1)) <= 1e-5 * max(1.0, np.max(np.abs(y1)))
+
+
+def test_determinism(ssm):
+    inp = synth.scan_inputs(2, 3000, 256, 16, "bf16", seed=9, gate=True, d_kind="normal", h0=True)
+    outs = [_run(ssm, inp, chunk_len=700) for _ in range(3)]
+    for y, h in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(h, outs[0][1])
+
+
+def test_empty_and_degenerate(ssm):
+    import torch
+    dev = "cuda"
+    A = torch.full((8, 4), -1.0, device=dev)
+    for (Bsz, L, D) in [(0, 5, 8), (2, 0, 8), (2, 5, 0)]:
+        x = torch.zeros((Bsz, L, D), dtype=torch.bfloat16, device=dev)
+        Bm = torch.zeros((Bsz, L, 4), dtype=torch.bfloat16, device=dev)
+        Am = A[:D] if D else torch.zeros((0, 4), device=dev)
+        h0 = torch.randn((Bsz, D, 4), device=dev)
+        y, hl = ssm.scan_fwd(x, x, Am.contiguous(), Bm, Bm, None, None, h0 if Bsz * D else None,
+                             return_last_state=True)
+        torch.cuda.synchronize()
+        assert y.shape == (Bsz, L, D)
+        if L == 0 and Bsz * D:
+            assert torch.equal(hl, h0)
+    # L == 0 without h0: zeros
+    hl = torch.full((2, 8, 4), 7.0, device=dev)
+    x = torch.zeros((2, 0, 8), dtype=torch.bfloat16, device=dev)
+    Bm = torch.zeros((2, 0, 4), dtype=torch.bfloat16, device=dev)
+    ssm.scan_fwd(x, x, A, Bm, Bm, h_last=hl, return_last_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(hl).item() == 0
+
+
+def test_errors_launch_nothing(ssm):
+    import torch
+    x = torch.zeros((1, 4, 8), dtype=torch.bfloat16, device="cuda")
+    Bm = torch.zeros((1, 4, 20), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((8, 20), device="cuda")
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.scan_fwd(x, x, A, Bm, Bm)
+    assert e.value.status == 2  # dstate > 16 is unsupported
+    y = torch.zeros((1, 4, 8), dtype=torch.bfloat16, device="cuda")
+    Bm = torch.zeros((1, 4, 4), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ssm.SSMError) as e:   # y overlapping x
+        ssm.scan_fwd(x, x, torch.zeros((8, 4), device="cuda"), Bm, Bm, out=x)
+    assert e.value.status == 1
+
+
+def test_nan_propagates_forward_only(ssm):
+    inp = synth.scan_inputs(1, 50, 64, 16, "f32", seed=3, d_kind="normal")
+    inp["x"] = inp["x"].copy()
+    inp["x"][0, 20, 5] = np.nan
+    y, h = _run(ssm, inp)
+    assert np.isnan(y[0, 20:, 5]).all() and not np.isnan(y[0, :20, 5]).any()
+    mask = np.ones(y.shape, bool)
+    mask[0, 20:, 5] = False
+    assert not np.isnan(y[mask]).any()
+    assert np.isnan(h[0, 5]).all() and np.isfinite(np.delete(h[0], 5, axis=0)).all()
+
+
+def test_softplus_mode_matches_plain(ssm):
+    inp = synth.scan_inputs(2, 200, 96, 16, "f32", seed=11, gate=True, d_kind="normal",
+                            softplus_input=True, h0=True)
+    y, h = _run(ssm, inp)
+    yr, hr = oracle.scan(inp)
+    assert_close(y, yr, "f32")
+    assert_close(h, hr, "f32", "h_last")
+
+
+# ---- the five workloads at full size -------------------------------------
+
+def _config_parity(ssm, k, sample=None, seed=None, **kw):
+    import torch
+    c = synth.CONFIGS[k]
+    inp = synth.config_inputs(k, seed=seed)
+    print(f"[parity] config {k} ({c['name']}) seed={seed if seed is not None else k} generated", flush=True)
+    dt = c["dtype"]
+    if sample is None:
+        y, h = _run(ssm, inp, **kw)
+        yr, hr = oracle.scan(inp)
+        st = assert_close(y, yr, dt)
+        assert_close(h, hr, "f32", "h_last")
+    else:
+        yd, hd = _run_dev(ssm, inp, **kw)
+        assert bool(torch.isfinite(yd.float()).all())
+        ch = sample_channels(c["batch"], c["dim"], sample)
+        cb = torch.tensor([b for b, _ in ch], device=yd.device)
+        cd = torch.tensor([d for _, d in ch], device=yd.device)
+        yg = to_host(yd[cb, :, cd])
+        hg = to_host(hd[cb, cd])
+        del yd
+        yr, hr = oracle.scan(inp, channels=ch)
+        st = assert_close(yg, yr, dt)
+        assert_close(hg, hr, "f32", "h_last")
+    _log(f"config {k}", st)
+    return st
+
+
+def test_parity_config0(ssm):
+    _config_parity(ssm, 0)
+    _config_parity(ssm, 0, seed=100)
+
+
+@pytest.mark.timeout(900)
+def test_parity_config1(ssm):
+    _config_parity(ssm, 1)
+
+
+@pytest.mark.timeout(900)
+def test_parity_config2(ssm):
+    _config_parity(ssm, 2)
+
+
+@pytest.mark.timeout(900)
+def test_parity_config3(ssm):
+    """Million-token scan: sampled channels over the whole length (chunk carries path)."""
+    plan = ssm.scan_plan(1, 1 << 20, 1024, 16, "bf16")
+    assert plan["n_chunks"] > 1
+    _config_parity(ssm, 3, sample=48)
