@@ -45,9 +45,11 @@ SLOTS_PER_TOKEN_CHANNEL = 2.0
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("ssm_kernels.hip", "ssm_host.cpp", "ssm_host.h"):
-        with open(os.path.join(ROOT, "selective_state_space_50_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "selective_state_space_50_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -81,7 +81,7 @@ typedef struct ssm_scan_plan {
     int32_t states_per_lane;
     int32_t waves_per_block;
     int32_t time_block;
-    int32_t reserved;
+    int32_t specialised;     /* 1: the dstate == 16, dim % 64 == 0 kernel runs; 0: the generic one */
     uint64_t workspace_bytes;
     uint64_t blocks;         /* workgroups of the main scan launch */
 } ssm_scan_plan;

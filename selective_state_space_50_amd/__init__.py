@@ -38,7 +38,7 @@ class ScanOpts(ctypes.Structure):
 class ScanPlan(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("states_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
-                ("time_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("time_block", ctypes.c_int32), ("specialised", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("blocks", ctypes.c_uint64)]
 
 
@@ -121,7 +121,7 @@ def scan_plan(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0, states_per_
     _check(lib().ssm_scan_plan_get(batch, seqlen, dim, dstate, code,
                                    ctypes.byref(o) if o else None, ctypes.byref(p)),
            "ssm_scan_plan_get")
-    return {k: getattr(p, k) for k, _ in ScanPlan._fields_ if k != "reserved"}
+    return {k: getattr(p, k) for k, _ in ScanPlan._fields_}
 
 
 def scan_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0,

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
-SOURCES = [os.path.join(CSRC, "ssm_kernels.hip"), os.path.join(CSRC, "ssm_host.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("ssm_api.hip", "scan_fast.hip", "scan_generic.hip", "decode.hip", "ssm_host.cpp")]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
@@ -20,18 +21,37 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(proc, what):
+    _, err = proc.communicate()
+    err = "\n".join(l for l in err.splitlines() if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{err}")
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel, then link libssm.so."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        procs.append((src, _run([hipcc, *compile_flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj], verbose)))
+    warnings = [_finish(p, src) for src, p in procs]
+    tmp = LIB + ".tmp"
+    link = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    warnings.append(_finish(link, "link"))
+    if verbose and any(w.strip() for w in warnings):
+        print("\n".join(w for w in warnings if w.strip()), file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,131 @@
+// C-ABI entry points of libssm, the chunk-carry combine and the empty-sequence fill.
+//
+// Long sequences are cut into chunks: a carry pass stores, per chunk, the sum
+// of delta and the end state from h = 0; the combine folds them in order with
+// (P1, H1) o (P2, H2) = (P2 P1, P2 H1 + H2), P = exp(A sum delta) (skill page
+// "State Space Models Mamba", section "Hardware-Efficient Scan": the
+// recurrence is linear, so it admits an associative scan); a second scan pass
+// then starts every chunk from its carried-in state.
+#include "ssm_device.h"
+
+namespace ssm {
+namespace {
+
+// Fold chunk carries in sequence order, one thread per (b, d, n):
+//   h_in(0) = h0,  h_in(c+1) = exp(A * S_c) * h_in(c) + H_c
+// and overwrite slot c with h_in(c+1), the state chunk c+1 starts from.
+__global__ void __launch_bounds__(256) combine_kernel(ScanArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t D = a.D, N = a.N;
+    if (i >= a.B * D * N) return;
+    const int64_t n = i % N;
+    const int64_t d = (i / N) % D;
+    const int64_t b = i / (N * D);
+    const float al = a.A[d * N + n] * kLog2e;
+    float h = a.h0 ? a.h0[i] : 0.0f;
+    const int64_t C1 = a.n_chunks - 1;
+    for (int64_t c = 0; c < C1; ++c) {
+        const int64_t slot = b * C1 + c;
+        const float P = __builtin_amdgcn_exp2f(al * a.ws_S[slot * D + d]);
+        float *Hp = a.ws_H + (slot * D + d) * N + n;
+        h = __builtin_fmaf(P, h, *Hp);
+        *Hp = h;
+    }
+}
+
+// h_last = h0 (or zeros) for an empty sequence.
+__global__ void __launch_bounds__(256) fill_state_kernel(float *h_last, const float *h0, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) h_last[i] = h0 ? h0[i] : 0.0f;
+}
+
+
+int hip_fail(const char *what, hipError_t e) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return SSM_EHIP;
+}
+
+hipError_t launch_scan_any(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z,
+                           bool carry, hipStream_t s) {
+    if (p.fast) return launch_scan_fast(a, grid, p, bf16, has_z, carry, s);
+    return launch_scan_generic(a, grid, p, bf16, has_z, carry, s);
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                            const void *x, const void *delta, const float *A, const void *B,
+                            const void *C, const float *Dskip, const void *z, const float *h0,
+                            float *h_last, void *y, int delta_softplus, const ssm_scan_opts *opts,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    using namespace ssm;
+    clear_error();
+    ScanPlan p;
+    int st = check_scan(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last,
+                        y, delta_softplus, opts, workspace, workspace_bytes, &p);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_last) return SSM_OK;
+        const int64_t n = batch * dim * dstate;
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                           0, s, h_last, h0, n);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
+    }
+    ScanArgs a;
+    a.B = batch; a.L = seqlen; a.D = dim; a.N = dstate;
+    a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;
+    a.A = A; a.Dskip = Dskip; a.h0 = h0; a.h_last = h_last; a.y = y;
+    a.softplus = delta_softplus;
+    a.NW = p.NW;
+    a.chunk_len = p.chunk_len;
+    a.n_chunks = p.n_chunks;
+    a.ws_S = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_S_off) : nullptr;
+    a.ws_H = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_H_off) : nullptr;
+    const unsigned dblocks = static_cast<unsigned>((dim + kChannelsPerBlock - 1) / kChannelsPerBlock);
+    const bool bf16 = dtype == SSM_DTYPE_BF16;
+    const bool has_z = z != nullptr;
+    hipError_t e;
+    if (p.n_chunks > 1) {
+        // 1) carries of every chunk but the last
+        dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks - 1));
+        e = launch_scan_any(a, g1, p, bf16, false, true, s);
+        if (e != hipSuccess) return hip_fail("scan carry launch", e);
+        // 2) fold the carries in order
+        const int64_t n = batch * dim * dstate;
+        hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail("carry combine launch", e);
+    }
+    // 3) every chunk from its carried-in state, producing y
+    dim3 g3(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks));
+    e = launch_scan_any(a, g3, p, bf16, has_z, false, s);
+    if (e != hipSuccess) return hip_fail("scan launch", e);
+    return SSM_OK;
+}
+
+extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, float *h,
+                                const void *x, const void *delta, const float *A, const void *B,
+                                const void *C, const float *Dskip, const void *z, void *y,
+                                int delta_softplus, void *stream) {
+    using namespace ssm;
+    clear_error();
+    int st = check_state_update(batch, dim, dstate, dtype, h, x, delta, A, B, C, Dskip, z, y,
+                                delta_softplus);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    UpdArgs a;
+    a.B = batch; a.D = dim; a.N = dstate; a.h = h;
+    a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C; a.A = A; a.Dskip = Dskip; a.y = y;
+    a.softplus = delta_softplus;
+    const int G = (dstate % 4 == 0) ? 4 : 1;
+    int lpc = 1;
+    while (lpc * G < dstate) lpc *= 2;
+    a.lpc = lpc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_state_update(a, dtype == SSM_DTYPE_BF16, z != nullptr, s);
+    return e == hipSuccess ? SSM_OK : hip_fail("state update launch", e);
+}

@@ -186,6 +186,8 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
                   (long long)batch, (long long)p.n_chunks);
         return SSM_EUNSUPPORTED;
     }
+    p.fast = dstate == 16 && dim % 64 == 0 && dim < (int64_t(1) << 24) &&
+             ((p.G == 2 && p.TB == 16) || (p.G == 4 && (p.TB == 16 || p.TB == 32)));
     p.blocks = static_cast<uint64_t>(dblocks) * static_cast<uint64_t>(batch) *
                static_cast<uint64_t>(p.n_chunks);
     *plan = p;
@@ -309,6 +311,7 @@ int ssm_scan_plan_get(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
     out->states_per_lane = p.G;
     out->waves_per_block = p.NW;
     out->time_block = p.TB;
+    out->specialised = p.fast ? 1 : 0;
     out->workspace_bytes = p.ws_bytes;
     out->blocks = p.blocks;
     return SSM_OK;

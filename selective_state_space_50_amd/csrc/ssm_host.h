@@ -24,6 +24,7 @@ struct ScanPlan {
     size_t ws_S_off = 0;  // byte offset of the per-chunk delta sums [B][C-1][D]
     size_t ws_H_off = 0;  // byte offset of the per-chunk end states [B][C-1][D][N]
     uint64_t blocks = 0;  // workgroups of the main scan launch
+    bool fast = false;    // dstate == 16 and dim % 64 == 0: the specialised kernel runs
 };
 
 // Per-thread error text (ssm_last_error).

@@ -37,7 +37,9 @@ def test_version_and_status_text(lib):
 def test_plans(lib):
     p2 = ssm.scan_plan(4, 4096, 4096, 16, "bf16")
     assert p2["n_chunks"] == 1 and p2["states_per_lane"] == 4 and p2["waves_per_block"] == 4
-    assert p2["blocks"] == 4 * 64
+    assert p2["blocks"] == 4 * 64 and p2["specialised"] == 1
+    assert ssm.scan_plan(2, 100, 130, 16, "bf16")["specialised"] == 0
+    assert ssm.scan_plan(2, 100, 128, 12, "bf16")["specialised"] == 0
     p3 = ssm.scan_plan(1, 1 << 20, 1024, 16, "bf16")
     assert p3["n_chunks"] > 1 and p3["workspace_bytes"] > 0
     assert ssm.scan_workspace_bytes(1, 1 << 20, 1024, 16, "bf16") == p3["workspace_bytes"]

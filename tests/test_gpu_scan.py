@@ -88,11 +88,41 @@ def test_parity_small_shapes(ssm, Bsz, L, D, N, dt, gate, h0, sp, ak):
 
 @pytest.mark.parametrize("G,TB", [(1, 8), (2, 16), (4, 32), (4, 16), (8, 16), (16, 8)])
 def test_states_per_lane_variants(ssm, G, TB):
+    """Generic kernel (dim not a multiple of 64) with every lane width."""
+    assert ssm.scan_plan(2, 150, 130, 16, "f32", states_per_lane=G, time_block=TB)["specialised"] == 0
     inp = synth.scan_inputs(2, 150, 130, 16, "f32", seed=5, gate=True, d_kind="normal",
                             a_kind="random", h0=True)
     y, h = _run(ssm, inp, states_per_lane=G, time_block=TB)
     yr, hr = oracle.scan(inp)
     assert_close(y, yr, "f32")
+    assert_close(h, hr, "f32", "h_last")
+
+
+FAST = [
+    # B, L, D, dtype, gate, h0, softplus, G, TB, chunk
+    (2, 1, 64, "f32", False, False, False, 4, 32, 0),
+    (2, 17, 64, "f32", True, True, False, 4, 32, 0),
+    (3, 333, 192, "f32", True, True, False, 4, 16, 0),
+    (2, 100, 128, "f32", True, False, True, 2, 16, 0),
+    (1, 257, 64, "bf16", True, True, False, 2, 16, 0),
+    (2, 700, 128, "bf16", True, True, False, 4, 32, 0),
+    (2, 700, 128, "f32", False, True, False, 4, 32, 50),
+    (1, 999, 64, "f32", True, True, False, 2, 16, 100),
+    (2, 640, 64, "bf16", True, False, True, 4, 16, 64),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,dt,gate,h0,sp,G,TB,chunk", FAST)
+def test_parity_specialised_kernel(ssm, Bsz, L, D, dt, gate, h0, sp, G, TB, chunk):
+    """dstate == 16, dim % 64 == 0: the specialised kernel (both lane widths, both time
+    blocks, ragged lengths, the chunk-carry mode)."""
+    plan = ssm.scan_plan(Bsz, L, D, 16, dt, chunk_len=chunk, states_per_lane=G, time_block=TB)
+    assert plan["specialised"] == 1
+    inp = synth.scan_inputs(Bsz, L, D, 16, dt, seed=300 + L + G, gate=gate, d_kind="normal",
+                            a_kind="random", softplus_input=sp, h0=h0)
+    y, h = _run(ssm, inp, chunk_len=chunk, states_per_lane=G, time_block=TB)
+    yr, hr = oracle.scan(inp)
+    _log(f"specialised {Bsz}x{L}x{D} {dt} G={G} TB={TB} chunk={chunk}", assert_close(y, yr, dt))
     assert_close(h, hr, "f32", "h_last")
 
 
