@@ -72,6 +72,8 @@ typedef struct ssm_scan_opts {
     int64_t chunk_len;     /* length of the sequence chunks scanned in parallel (>= 1) */
     int32_t states_per_lane; /* 1, 2, 4, 8 or 16 states of one channel per GPU lane */
     int32_t time_block;    /* time steps staged per block: 8, 16 or 32 */
+    int32_t one_block_per_cu; /* 0: automatic; 1: reserve LDS so each CU runs one workgroup; -1: never */
+    int32_t reserved;      /* must be 0 */
 } ssm_scan_opts;
 
 /* What ssm_scan_fwd will launch for a given shape (host-only query). */
@@ -84,6 +86,7 @@ typedef struct ssm_scan_plan {
     int32_t specialised;     /* 1: the dstate == 16, dim % 64 == 0 kernel runs; 0: the generic one */
     uint64_t workspace_bytes;
     uint64_t blocks;         /* workgroups of the main scan launch */
+    uint64_t lds_reserve;    /* extra LDS bytes per workgroup that keep one workgroup per CU (0 = none) */
 } ssm_scan_plan;
 
 /* ABI version of the loaded library (SSM_ABI_VERSION at build time). */

@@ -32,14 +32,16 @@ class SSMError(RuntimeError):
 
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("states_per_lane", ctypes.c_int32),
-                ("time_block", ctypes.c_int32)]
+                ("time_block", ctypes.c_int32), ("one_block_per_cu", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class ScanPlan(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("states_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
                 ("time_block", ctypes.c_int32), ("specialised", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64), ("blocks", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("blocks", ctypes.c_uint64),
+                ("lds_reserve", ctypes.c_uint64)]
 
 
 _lib = None
@@ -97,10 +99,10 @@ def exported_api():
     return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
 
 
-def _opts(chunk_len=0, states_per_lane=0, time_block=0):
-    if not (chunk_len or states_per_lane or time_block):
+def _opts(chunk_len=0, states_per_lane=0, time_block=0, one_block_per_cu=0):
+    if not (chunk_len or states_per_lane or time_block or one_block_per_cu):
         return None
-    return ScanOpts(int(chunk_len), int(states_per_lane), int(time_block))
+    return ScanOpts(int(chunk_len), int(states_per_lane), int(time_block), int(one_block_per_cu), 0)
 
 
 def _dtype_code(t):
@@ -113,11 +115,11 @@ def _dtype_code(t):
 
 
 def scan_plan(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0, states_per_lane=0,
-              time_block=0) -> dict:
+              time_block=0, one_block_per_cu=0) -> dict:
     """What ssm_scan_fwd will launch for this shape (host-only)."""
     code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
     p = ScanPlan()
-    o = _opts(chunk_len, states_per_lane, time_block)
+    o = _opts(chunk_len, states_per_lane, time_block, one_block_per_cu)
     _check(lib().ssm_scan_plan_get(batch, seqlen, dim, dstate, code,
                                    ctypes.byref(o) if o else None, ctypes.byref(p)),
            "ssm_scan_plan_get")
@@ -125,9 +127,9 @@ def scan_plan(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0, states_per_
 
 
 def scan_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16", chunk_len=0,
-                         states_per_lane=0, time_block=0) -> int:
+                         states_per_lane=0, time_block=0, one_block_per_cu=0) -> int:
     code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
-    o = _opts(chunk_len, states_per_lane, time_block)
+    o = _opts(chunk_len, states_per_lane, time_block, one_block_per_cu)
     return int(lib().ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, code,
                                               ctypes.byref(o) if o else None))
 
@@ -151,7 +153,7 @@ def _need(t, name, shape, dtype, device):
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
              return_last_state=False, out=None, h_last=None, workspace=None, chunk_len=0,
-             states_per_lane=0, time_block=0, stream=None):
+             states_per_lane=0, time_block=0, one_block_per_cu=0, stream=None):
     """Selective scan y = S6(x, delta, A, B, C, D) [* silu(z)] on the GPU.
 
     x, delta, z: [B, L, D];  B, C: [B, L, N];  A: [D, N] fp32;  D: [D] fp32;
@@ -181,7 +183,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False
     if return_last_state and h_last is None:
         h_last = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
     _need(h_last, "h_last", (Bsz, Dm, N), torch.float32, dev)
-    o = _opts(chunk_len, states_per_lane, time_block)
+    o = _opts(chunk_len, states_per_lane, time_block, one_block_per_cu)
     ws_bytes = int(lib().ssm_scan_workspace_bytes(Bsz, L, Dm, N, code, ctypes.byref(o) if o else None))
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

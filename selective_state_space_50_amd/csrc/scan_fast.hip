@@ -1,22 +1,38 @@
 // Selective-scan kernel specialised for dstate == 16 and dim % 64 == 0 (the
 // shapes of Mamba layers: N = 16, d_inner a multiple of 64).
 //
-// Same work mapping as the generic kernel -- lane = channel, wave = a group of
-// G states, per-wave shares of y reduced through LDS -- with every layout
-// fixed at compile time so that the inner loop is pure VALU work on operands
-// read with immediate LDS offsets:
-//   * staging and epilogue threads each own CPT adjacent channels of one time
-//     row: x / delta / z are fetched as one vector per row (2 or 4 bf16), the
-//     step sizes and delta*x are written to LDS as float4 pairs, the partial
-//     sums of y are read back as vectors and y is stored as packed bf16;
-//   * row addresses are a uniform 64-bit base plus a 32-bit lane offset;
-//   * the LDS operands of step i+1 are read while step i computes.
+// Work mapping as in the generic kernel -- lane = channel, wave = a group of G
+// states held in VGPRs, per-wave shares of y reduced through LDS -- but the
+// waves of a workgroup are split by role:
+//   * NC = 16 / G compute waves only scan: per step they read (delta,
+//     delta*x) and the B/C values of their states from LDS, update G states,
+//     and write their share of y to LDS.  They never touch global memory
+//     inside the sequence loop;
+//   * 4 helper waves (one per SIMD) do all streaming: they prefetch x, delta,
+//     z and the B/C rows one block ahead as vectors of adjacent channels,
+//     convert them into the LDS staging buffer, and finish every output row
+//     (sum of the NC shares, D*x, gate, packed bf16 store).
+// Staging and y-share buffers are double-buffered, so block k is scanned
+// while block k-1 is finished and block k+1 is staged; one barrier per block.
+// B_t and C_t are the same for every channel of a token, so they do not go
+// through LDS: a pre-pass packs them once per call to fp32, grouped by the
+// states of one compute wave, and each compute wave reads two steps of them
+// with one scalar load into SGPRs, which the VALU takes as scalar operands.
 #include "ssm_device.h"
+
+#include <type_traits>
 
 namespace ssm {
 namespace {
 
 constexpr int kN = 16;
+constexpr int kTB = 16;          // time steps per block
+constexpr int kHT = 256;         // helper threads (4 waves, one per SIMD)
+
+template <int P>
+using Par = std::integral_constant<int, P>;
+using Full = std::true_type;     // every row of the block is inside the chunk
+using Part = std::false_type;
 
 // CPT consecutive elements of T loaded as one vector and unpacked to float.
 template <typename T, int CPT>
@@ -24,301 +40,347 @@ struct Vec;
 template <>
 struct Vec<uint16_t, 2> {
     uint32_t r;
-    __device__ void load(const uint16_t *p) { r = *reinterpret_cast<const uint32_t *>(p); }
     __device__ void zero() { r = 0; }
     __device__ float get(int i) const { return i == 0 ? bf_lo(r) : bf_hi(r); }
 };
 template <>
-struct Vec<uint16_t, 4> {
-    uint2 r;
-    __device__ void load(const uint16_t *p) { r = *reinterpret_cast<const uint2 *>(p); }
-    __device__ void zero() { r = make_uint2(0, 0); }
-    __device__ float get(int i) const {
-        const uint32_t v = (i < 2) ? r.x : r.y;
-        return (i & 1) ? bf_hi(v) : bf_lo(v);
-    }
-};
-template <>
 struct Vec<float, 2> {
     float2 r;
-    __device__ void load(const float *p) { r = *reinterpret_cast<const float2 *>(p); }
     __device__ void zero() { r = make_float2(0.f, 0.f); }
     __device__ float get(int i) const { return i == 0 ? r.x : r.y; }
 };
-template <>
-struct Vec<float, 4> {
-    float4 r;
-    __device__ void load(const float *p) { r = *reinterpret_cast<const float4 *>(p); }
-    __device__ void zero() { r = make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ float get(int i) const { return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w; }
-};
 
-template <int CPT>
-__device__ __forceinline__ void store_out(uint16_t *p, const float (&v)[CPT]) {
-    if constexpr (CPT == 2) {
-        *reinterpret_cast<uint32_t *>(p) = pack_bf16(v[0], v[1]);
-    } else {
-        *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-    }
+// Loads/stores at a wave-uniform base plus a 32-bit unsigned byte offset, so the
+// address is formed by the memory unit (SGPR base + VGPR offset), not by VALU.
+template <typename V>
+__device__ __forceinline__ V ld_at(const void *base, uint32_t byte_off) {
+    return *reinterpret_cast<const V *>(static_cast<const char *>(base) + byte_off);
 }
-template <int CPT>
-__device__ __forceinline__ void store_out(float *p, const float (&v)[CPT]) {
-    if constexpr (CPT == 2) {
-        *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
-    } else {
-        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    }
+template <typename V>
+__device__ __forceinline__ void st_at(void *base, uint32_t byte_off, V v) {
+    *reinterpret_cast<V *>(static_cast<char *>(base) + byte_off) = v;
 }
 
-template <int G>
-__device__ __forceinline__ void lds_g(const float *p, float (&v)[G]) {
-    if constexpr (G == 4) {
-        const float4 q = *reinterpret_cast<const float4 *>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    } else {
-        const float2 q = *reinterpret_cast<const float2 *>(p);
-        v[0] = q.x; v[1] = q.y;
+// Read-only for the whole launch (written by the pre-pass launch): the constant
+// address space lets wave-uniform reads become scalar loads into SGPRs.
+typedef const float __attribute__((address_space(4))) cfloat;
+
+// Pre-pass: ws_BC[b][w][c][tl][g][0/1] = B, C [b, c*chunk_len + tl, w*G + g], zero past
+// the chunk (or the sequence) so the last block of a chunk reads zeros.
+template <typename T, int G>
+__global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b, c, tl, n)
+    const int64_t lp = a.bc_lpad;
+    const int64_t total = a.B * a.n_chunks * lp * kN;
+    if (i >= total) return;
+    const int n = static_cast<int>(i % kN);
+    const int64_t tl = (i / kN) % lp;
+    const int64_t c = (i / (kN * lp)) % a.n_chunks;
+    const int64_t b = i / (kN * lp * a.n_chunks);
+    const int64_t t = c * a.chunk_len + tl;
+    float bv = 0.0f, cv = 0.0f;
+    if (tl < a.chunk_len && t < a.L) {
+        bv = widen(static_cast<const T *>(a.Bm), (b * a.L + t) * kN + n);
+        cv = widen(static_cast<const T *>(a.Cm), (b * a.L + t) * kN + n);
     }
+    const int w = n / G, g = n % G;
+    float2 *o = reinterpret_cast<float2 *>(a.ws_BC);
+    o[(((b * (kN / G) + w) * a.n_chunks + c) * lp + tl) * G + g] = make_float2(bv, cv);
 }
 
-template <typename T, int G, int TB, bool HAS_Z, bool CARRY>
-__global__ void __launch_bounds__(64 * (kN / G)) scan_fast_kernel(ScanArgs a) {
-    constexpr int NW = kN / G;          // waves per workgroup
-    constexpr int NT = NW * 64;         // threads
-    constexpr int CPT = NT >= 512 ? 2 : 4;  // channels per staging/epilogue thread
-    constexpr int TPR = 64 / CPT;       // threads per time row
-    constexpr int RPP = NT / TPR;       // rows per staging pass
-    constexpr int PASSES = TB / RPP;
-    constexpr int BCT = TB * kN / 4;    // threads staging 4 B/C values each
-    static_assert(TB % RPP == 0 && PASSES >= 1, "time block must be a multiple of the rows per pass");
-    static_assert(BCT <= NT, "B/C staging needs TB*16/4 threads");
+template <typename T, int G, bool HAS_Z, bool CARRY>
+__global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a) {
+    constexpr int NC = kN / G;          // compute waves
+    // Helper thread hid owns time rows 2*rp, 2*rp+1 and channels cp, cp+1 of every block.
+    static_assert((kTB / 2) * 32 == kHT, "helpers cover the block in row pairs x channel pairs");
 
-    __shared__ float4 sDU4[TB * 32];                    // float2 (delta, delta*x) [TB][64]
-    __shared__ float4 sB4[TB * kN / 4];                 // [TB][16]
-    __shared__ float4 sC4[CARRY ? 1 : TB * kN / 4];     // [TB][16]
-    __shared__ float4 sY4[CARRY ? 1 : NW * TB * 16];    // [NW][TB][64]
-    float2 *sDU = reinterpret_cast<float2 *>(sDU4);
-    float *sB = reinterpret_cast<float *>(sB4);
-    float *sC = reinterpret_cast<float *>(sC4);
-    float *sY = reinterpret_cast<float *>(sY4);
+    // Step-pair interleaved layouts so one LDS instruction moves two steps:
+    //   sDU [P][i/2][lane] float4 = (delta_i, delta_i*x_i, delta_i+1, delta_i+1*x_i+1)
+    //   sY  [P][w][i/2][lane] float2 = (share of y_i, share of y_i+1)
+    __shared__ float4 sDU[2][kTB / 2 * 64];
+    __shared__ float2 sY[2][CARRY ? 1 : NC * kTB / 2 * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool helper = w >= NC;        // wave-uniform role
     const int64_t D = a.D, L = a.L;
     const int64_t b = blockIdx.y;
     const int64_t c = blockIdx.z;
     const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
     const int64_t t0 = c * a.chunk_len;
     const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
-    const int n0 = w * G;
-    const int sr = tid / TPR;           // staging row within a pass
-    const int sc = (tid % TPR) * CPT;   // staging channel offset within the 64
-    const int32_t lane_off = sr * static_cast<int32_t>(D) + sc;   // D < 2^24 (checked by the plan)
+    const int64_t nblk = (t1 - t0 + kTB - 1) / kTB;
 
+    // ---- compute-wave state: G states of channel d0 + lane, A scaled by log2(e)
+    const int n0 = (helper ? 0 : w) * G;
+    const int64_t d = d0 + lane;
+    float Al[G], h[G];
+    float dsum = 0.0f;
+    // packed B/C of this wave's states for this chunk: [step][g][B, C]
+    // (global and constant address spaces share 64-bit addresses on gfx950)
+    cfloat *bcw = reinterpret_cast<cfloat *>(reinterpret_cast<uintptr_t>(
+        a.ws_BC + ((b * NC + (helper ? 0 : w)) * a.n_chunks + c) * a.bc_lpad * (2 * G)));
+
+    // ---- helper role
+    const int hid = tid - NC * 64;
+    const int rp = hid >> 5;            // row pair
+    const int cp = (hid & 31) * 2;      // channel pair
+    const int r0 = 2 * rp;
+    const int32_t D32 = static_cast<int32_t>(D);                // D < 2^24 (checked by the plan)
     const T *X = static_cast<const T *>(a.x) + b * L * D + d0;
     const T *DL = static_cast<const T *>(a.delta) + b * L * D + d0;
     const T *Z = HAS_Z ? static_cast<const T *>(a.z) + b * L * D + d0 : nullptr;
-    const T *Bb = static_cast<const T *>(a.Bm) + b * L * kN;
-    const T *Cb = static_cast<const T *>(a.Cm) + b * L * kN;
+    T *Yb = static_cast<T *>(a.y) + b * L * D + d0;
+    constexpr uint32_t ES = sizeof(T);
+    const uint32_t off0 = static_cast<uint32_t>(r0 * D32 + cp) * ES;    // row r0
+    const uint32_t off1 = off0 + static_cast<uint32_t>(D32) * ES;       // row r0 + 1
+    float dsk[2];
+    // raw prefetch registers, two sets by block parity (block j lives in set j & 1)
+    Vec<T, 2> rx[2][2], rd[2][2], rz[2][2];   // [set][row of the pair]
+    float ex[2][2][2], ez[2][2][2];     // [block parity][row][channel]
 
-    // per-lane state: G states of channel d0 + lane, A pre-scaled by log2(e)
-    const int64_t d = d0 + lane;
-    float Al[G], h[G];
+    auto load_block = [&](int64_t tb0, auto set, auto full) {   // helpers: raw rows at tb0
+        constexpr int S = decltype(set)::value;
+        const T *xb = X + tb0 * D;      // uniform row bases
+        const T *db = DL + tb0 * D;
+        const T *zb = HAS_Z ? Z + tb0 * D : nullptr;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        Al[g] = a.A[d * kN + n0 + g] * kLog2e;
-        float hv = 0.0f;
-        if (!CARRY) {
-            if (c == 0) {
-                if (a.h0) hv = a.h0[(b * D + d) * kN + n0 + g];
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t off = q ? off1 : off0;
+            if (decltype(full)::value || tb0 + r0 + q < t1) {
+                rx[S][q].r = ld_at<decltype(rx[S][q].r)>(xb, off);
+                rd[S][q].r = ld_at<decltype(rd[S][q].r)>(db, off);
+                if constexpr (HAS_Z && !CARRY) rz[S][q].r = ld_at<decltype(rz[S][q].r)>(zb, off);
             } else {
-                hv = a.ws_H[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + n0 + g];
-            }
-        }
-        h[g] = hv;
-    }
-    float dsk[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) dsk[j] = (!CARRY && a.Dskip) ? a.Dskip[d0 + sc + j] : 0.0f;
-    float dsum = 0.0f;
-
-    Vec<T, CPT> rx[PASSES], rd[PASSES], rz[PASSES];
-    Vec<T, 4> rbv, rcv;
-    float ex[PASSES][CPT], ez[PASSES][CPT];
-
-    auto load_block = [&](int64_t tb0) {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int64_t row0 = tb0 + p * RPP;             // uniform
-            if (row0 + sr < t1) {
-                const int64_t base = row0 * D;
-                rx[p].load(X + base + lane_off);
-                rd[p].load(DL + base + lane_off);
-                if constexpr (HAS_Z && !CARRY) rz[p].load(Z + base + lane_off);
-            } else {
-                rx[p].zero();
-                rd[p].zero();
-                if constexpr (HAS_Z && !CARRY) rz[p].zero();
-            }
-        }
-        if (tid < BCT) {
-            const int e = tid * 4;
-            const int64_t t = tb0 + e / kN;
-            if (t < t1) {
-                rbv.load(Bb + tb0 * kN + e);
-                if constexpr (!CARRY) rcv.load(Cb + tb0 * kN + e);
-            } else {
-                rbv.zero();
-                if constexpr (!CARRY) rcv.zero();
+                rx[S][q].zero();
+                rd[S][q].zero();
+                if constexpr (HAS_Z && !CARRY) rz[S][q].zero();
             }
         }
     };
 
-    auto stage_block = [&](int64_t tb0) {
+    auto stage_block = [&](int64_t tb0, auto par, auto full, auto softplus) {   // helpers
+        constexpr int P = decltype(par)::value;   // block parity = LDS buffer = register set
+        float dv[2][2], uv[2][2];
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int i = p * RPP + sr;
-            const bool live = tb0 + i < t1;
-            float du[2 * CPT];
+        for (int q = 0; q < 2; ++q) {
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                float dv = rd[p].get(j);
-                float xv = rx[p].get(j);
-                if (a.softplus) dv = softplus_f(dv);
-                if (!live) { dv = 0.0f; xv = 0.0f; }   // padded steps leave h unchanged
-                du[2 * j] = dv;
-                du[2 * j + 1] = dv * xv;
-                ex[p][j] = xv;
-                ez[p][j] = (HAS_Z && !CARRY) ? rz[p].get(j) : 0.0f;
+            for (int j = 0; j < 2; ++j) {
+                float dl = rd[P][q].get(j);
+                float xv = rx[P][q].get(j);
+                if constexpr (decltype(softplus)::value) dl = softplus_f(dl);
+                if constexpr (!decltype(full)::value) {
+                    if (tb0 + r0 + q >= t1) { dl = 0.0f; xv = 0.0f; }   // padded steps leave h unchanged
+                }
+                dv[q][j] = dl;
+                uv[q][j] = dl * xv;
+                ex[P][q][j] = xv;
+                ez[P][q][j] = (HAS_Z && !CARRY) ? rz[P][q].get(j) : 0.0f;
             }
-            float4 *dst = reinterpret_cast<float4 *>(sDU + i * 64 + sc);
-#pragma unroll
-            for (int q = 0; q < CPT / 2; ++q)
-                dst[q] = make_float4(du[4 * q], du[4 * q + 1], du[4 * q + 2], du[4 * q + 3]);
         }
-        if (tid < BCT) {
-            sB4[tid] = make_float4(rbv.get(0), rbv.get(1), rbv.get(2), rbv.get(3));
-            if constexpr (!CARRY) sC4[tid] = make_float4(rcv.get(0), rcv.get(1), rcv.get(2), rcv.get(3));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
+    };
+
+    auto epilogue = [&](int64_t tb0, auto par, auto full) {   // helpers: finish rows r0, r0+1
+        constexpr int P = decltype(par)::value;
+        // (y_r0 ch cp, y_r0+1 ch cp, y_r0 ch cp+1, y_r0+1 ch cp+1)
+        float4 acc = *reinterpret_cast<const float4 *>(&sY[P][rp * 64 + cp]);
+#pragma unroll
+        for (int ww = 1; ww < NC; ++ww) {
+            const float4 v = *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp) * 64 + cp]);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        const float ys[2][2] = {{acc.x, acc.z}, {acc.y, acc.w}};
+        T *yb = Yb + tb0 * D;           // uniform row base
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (decltype(full)::value || tb0 + r0 + q < t1) {
+                float o[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float yv = __builtin_fmaf(dsk[j], ex[P][q][j], ys[q][j]);
+                    if (HAS_Z) yv *= silu_f(ez[P][q][j]);
+                    o[j] = yv;
+                }
+                const uint32_t off = q ? off1 : off0;
+                if constexpr (sizeof(T) == 2) st_at<uint32_t>(yb, off, pack_bf16(o[0], o[1]));
+                else st_at<float2>(yb, off, make_float2(o[0], o[1]));
+            }
         }
     };
 
-    const int64_t nblk = (t1 - t0 + TB - 1) / TB;
-    // the start state, A and D loads must not queue behind the block prefetch
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if (nblk > 0) {
-        load_block(t0);
-        stage_block(t0);
-        if (nblk > 1) load_block(t0 + TB);
-    }
-    for (int64_t k = 0; k < nblk; ++k) {
-        const int64_t tb0 = t0 + k * TB;
-        __syncthreads();   // stage of block k visible; y shares of block k-1 consumed
-        float2 du_n = sDU[lane];
-        float bv_n[G], cv_n[G];
-        lds_g<G>(sB + n0, bv_n);
-        if constexpr (!CARRY) lds_g<G>(sC + n0, cv_n);
+    auto compute_block = [&](int64_t k, auto par) {   // compute waves: 16 steps of G states
+        constexpr int P = decltype(par)::value;
+        cfloat *bck = bcw + k * kTB * (2 * G);        // uniform: scalar loads
+        // operands of step pair i+2 are fetched while pair i computes
+        float4 du_n = sDU[P][lane];
+        float bc_n[4 * G];
 #pragma unroll
-        for (int i = 0; i < TB; ++i) {
-            const float2 du = du_n;
-            float bv[G], cv[G];
+        for (int j = 0; j < 4 * G; ++j) bc_n[j] = bck[j];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                bv[g] = bv_n[g];
-                if constexpr (!CARRY) cv[g] = cv_n[g];
+        for (int i = 0; i < kTB; i += 2) {
+            const float4 du = du_n;
+            float bc[4 * G];
+#pragma unroll
+            for (int j = 0; j < 4 * G; ++j) bc[j] = bc_n[j];
+            if (i + 2 < kTB) {
+                du_n = sDU[P][(i / 2 + 1) * 64 + lane];
+#pragma unroll
+                for (int j = 0; j < 4 * G; ++j) bc_n[j] = bck[(i + 2) * 2 * G + j];
             }
-            if (i + 1 < TB) {
-                du_n = sDU[(i + 1) * 64 + lane];
-                lds_g<G>(sB + (i + 1) * kN + n0, bv_n);
-                if constexpr (!CARRY) lds_g<G>(sC + (i + 1) * kN + n0, cv_n);
-            }
+            // bc = [step i: g0 B, g0 C, g1 B, g1 C, ...][step i+1: ...]
             if constexpr (CARRY) {
                 dsum += du.x;
+                dsum += du.z;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float dA = __builtin_amdgcn_exp2f(du.x * Al[g]);
-                    h[g] = __builtin_fmaf(dA, h[g], du.y * bv[g]);
+                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
+                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
                 }
             } else {
-                float yp;
+                float y0, y1;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float dA = __builtin_amdgcn_exp2f(du.x * Al[g]);
-                    h[g] = __builtin_fmaf(dA, h[g], du.y * bv[g]);
-                    yp = g == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[g], h[g], yp);
+                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
+                    y0 = g == 0 ? bc[1] * h[0] : __builtin_fmaf(bc[2 * g + 1], h[g], y0);
+                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
+                    y1 = g == 0 ? bc[2 * G + 1] * h[0] : __builtin_fmaf(bc[2 * G + 2 * g + 1], h[g], y1);
                 }
-                sY[(w * TB + i) * 64 + lane] = yp;
+                sY[P][(w * kTB / 2 + i / 2) * 64 + lane] = make_float2(y0, y1);
             }
         }
-        __syncthreads();   // y shares complete; staging buffers free
-        if constexpr (!CARRY) {
-            T *Y = static_cast<T *>(a.y) + b * L * D + d0;
-#pragma unroll
-            for (int p = 0; p < PASSES; ++p) {
-                const int i = p * RPP + sr;
-                const int64_t row0 = tb0 + p * RPP;
-                if (row0 + sr < t1) {
-                    float ys[CPT];
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j) ys[j] = 0.0f;
-#pragma unroll
-                    for (int ww = 0; ww < NW; ++ww) {
-                        const float *src = sY + (ww * TB + i) * 64 + sc;
-                        if constexpr (CPT == 4) {
-                            const float4 v = *reinterpret_cast<const float4 *>(src);
-                            ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
-                        } else {
-                            const float2 v = *reinterpret_cast<const float2 *>(src);
-                            ys[0] += v.x; ys[1] += v.y;
-                        }
-                    }
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j) {
-                        float yv = __builtin_fmaf(dsk[j], ex[p][j], ys[j]);
-                        if (HAS_Z) yv *= silu_f(ez[p][j]);
-                        ys[j] = yv;
-                    }
-                    store_out<CPT>(Y + row0 * D + lane_off, ys);
-                }
+    };
+
+    auto stage_any = [&](int64_t tb0, auto par) {
+        const bool full = tb0 + kTB <= t1;
+        if (a.softplus) {
+            if (full) stage_block(tb0, par, Full{}, std::true_type{});
+            else stage_block(tb0, par, Part{}, std::true_type{});
+        } else {
+            if (full) stage_block(tb0, par, Full{}, std::false_type{});
+            else stage_block(tb0, par, Part{}, std::false_type{});
+        }
+    };
+    auto load_any = [&](int64_t tb0, auto set) {
+        if (tb0 + kTB <= t1) load_block(tb0, set, Full{});
+        else load_block(tb0, set, Part{});
+    };
+    auto epilogue_any = [&](int64_t tb0, auto par) {
+        if (tb0 + kTB <= t1) epilogue(tb0, par, Full{});
+        else epilogue(tb0, par, Part{});
+    };
+
+    // block k: compute waves scan buffer k&1; helpers finish block k-1, stage block k+1
+    // and prefetch block k+2
+    auto iteration = [&](int64_t k, auto par) {
+        constexpr int P = decltype(par)::value;
+        const int64_t tb0 = t0 + k * kTB;
+        if (!helper) {
+            compute_block(k, par);
+        } else {
+            if constexpr (!CARRY) {
+                if (k >= 1) epilogue_any(tb0 - kTB, Par<1 - P>{});
+            }
+            if (k + 1 < nblk) {
+                stage_any(tb0 + kTB, Par<1 - P>{});
+                if (k + 2 < nblk) load_any(tb0 + 2 * kTB, Par<P>{});
             }
         }
-        if (k + 1 < nblk) {
-            stage_block(tb0 + TB);
-            if (k + 2 < nblk) load_block(tb0 + 2 * TB);
+        __syncthreads();
+    };
+
+    if (!helper) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            Al[g] = a.A[d * kN + n0 + g] * kLog2e;
+            float hv = 0.0f;
+            if (!CARRY) {
+                if (c == 0) {
+                    if (a.h0) hv = a.h0[(b * D + d) * kN + n0 + g];
+                } else {
+                    hv = a.ws_H[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + n0 + g];
+                }
+            }
+            h[g] = hv;
+        }
+    } else {
+        // producer waves are served first, so their block is ready at each barrier
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dsk[j] = (!CARRY && a.Dskip) ? a.Dskip[d0 + cp + j] : 0.0f;
+        // keep the D loads out of the in-order queue of the block prefetch
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        if (nblk > 0) {
+            load_any(t0, Par<0>{});
+            stage_any(t0, Par<0>{});
+            if (nblk > 1) load_any(t0 + kTB, Par<1>{});
+        }
+    }
+    __syncthreads();
+    int64_t k = 0;
+    for (; k + 1 < nblk; k += 2) {
+        iteration(k, Par<0>{});
+        iteration(k + 1, Par<1>{});
+    }
+    if (k < nblk) iteration(k, Par<0>{});
+    if constexpr (!CARRY) {
+        if (helper && nblk > 0) {
+            const int64_t last = t0 + (nblk - 1) * kTB;
+            if ((nblk - 1) & 1) epilogue_any(last, Par<1>{});
+            else epilogue_any(last, Par<0>{});
         }
     }
 
-    if constexpr (CARRY) {
-        const int64_t slot = b * (a.n_chunks - 1) + c;
-        if (w == 0) a.ws_S[slot * D + d] = dsum;
+    if (!helper) {
+        if constexpr (CARRY) {
+            const int64_t slot = b * (a.n_chunks - 1) + c;
+            if (w == 0) a.ws_S[slot * D + d] = dsum;
 #pragma unroll
-        for (int g = 0; g < G; ++g) a.ws_H[(slot * D + d) * kN + n0 + g] = h[g];
-    } else {
-        if (a.h_last && c == a.n_chunks - 1) {
+            for (int g = 0; g < G; ++g) a.ws_H[(slot * D + d) * kN + n0 + g] = h[g];
+        } else {
+            if (a.h_last && c == a.n_chunks - 1) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + n0 + g] = h[g];
+                for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + n0 + g] = h[g];
+            }
         }
     }
 }
 
-template <typename T, int G, int TB>
-hipError_t launch_t(const ScanArgs &a, dim3 grid, bool has_z, bool carry, hipStream_t s) {
-    const dim3 block(64 * (kN / G));
-    if (carry) hipLaunchKernelGGL((scan_fast_kernel<T, G, TB, false, true>), grid, block, 0, s, a);
-    else if (has_z) hipLaunchKernelGGL((scan_fast_kernel<T, G, TB, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((scan_fast_kernel<T, G, TB, false, false>), grid, block, 0, s, a);
+// lds_reserve: unused dynamic LDS that keeps the residency at one workgroup per CU
+template <typename T, int G>
+hipError_t launch_t(const ScanArgs &a, dim3 grid, bool has_z, bool carry, size_t lds_reserve,
+                    hipStream_t s) {
+    const dim3 block(64 * (kN / G + 4));
+    if (carry) hipLaunchKernelGGL((scan_fast_kernel<T, G, false, true>), grid, block, 0, s, a);
+    else if (has_z) hipLaunchKernelGGL((scan_fast_kernel<T, G, true, false>), grid, block, lds_reserve, s, a);
+    else hipLaunchKernelGGL((scan_fast_kernel<T, G, false, false>), grid, block, lds_reserve, s, a);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_dt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool has_z, bool carry,
                      hipStream_t s) {
-    if (p.G == 2) return launch_t<T, 2, 16>(a, grid, has_z, carry, s);
-    if (p.TB == 16) return launch_t<T, 4, 16>(a, grid, has_z, carry, s);
-    return launch_t<T, 4, 32>(a, grid, has_z, carry, s);
+    if (p.G == 2) return launch_t<T, 2>(a, grid, has_z, carry, p.lds_reserve, s);
+    return launch_t<T, 4>(a, grid, has_z, carry, p.lds_reserve, s);
 }
 
 }  // namespace
+
+hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s) {
+    const int64_t total = a.B * a.n_chunks * a.bc_lpad * kN;
+    const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+    if (bf16) {
+        if (p.G == 2) hipLaunchKernelGGL((bc_pack_kernel<uint16_t, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((bc_pack_kernel<uint16_t, 4>), grid, dim3(256), 0, s, a);
+    } else {
+        if (p.G == 2) hipLaunchKernelGGL((bc_pack_kernel<float, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((bc_pack_kernel<float, 4>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_scan_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z,
                             bool carry, hipStream_t s) {

@@ -85,10 +85,17 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.n_chunks = p.n_chunks;
     a.ws_S = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_S_off) : nullptr;
     a.ws_H = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_H_off) : nullptr;
+    a.ws_BC = p.fast ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_BC_off) : nullptr;
+    a.bc_lpad = p.bc_lpad;
     const unsigned dblocks = static_cast<unsigned>((dim + kChannelsPerBlock - 1) / kChannelsPerBlock);
     const bool bf16 = dtype == SSM_DTYPE_BF16;
     const bool has_z = z != nullptr;
     hipError_t e;
+    if (p.fast) {
+        // 0) B/C rows of every chunk to fp32, interleaved per state group, zero-padded
+        e = launch_bc_pack(a, p, bf16, s);
+        if (e != hipSuccess) return hip_fail("B/C pack launch", e);
+    }
     if (p.n_chunks > 1) {
         // 1) carries of every chunk but the last
         dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks - 1));

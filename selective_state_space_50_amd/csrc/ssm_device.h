@@ -30,6 +30,8 @@ struct ScanArgs {
     int64_t chunk_len, n_chunks;
     float *ws_S;          // [B][n_chunks-1][D]     sum of delta over a chunk
     float *ws_H;          // [B][n_chunks-1][D][N]  chunk end state, then carried-in state
+    float *ws_BC;         // specialised kernel: [B][16/G][n_chunks][bc_lpad][G][2] fp32 (B, C)
+    int64_t bc_lpad;
 };
 
 struct UpdArgs {
@@ -55,8 +57,12 @@ __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 
 __device__ __forceinline__ uint16_t to_bf16(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return static_cast<uint32_t>(to_bf16(lo)) | (static_cast<uint32_t>(to_bf16(hi)) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ void put(uint16_t *p, int64_t i, float v) { p[i] = to_bf16(v); }
@@ -78,6 +84,8 @@ hipError_t launch_scan_generic(const ScanArgs &a, dim3 grid, const ScanPlan &p, 
 // Specialised path (plan.fast): dstate == 16, dim % 64 == 0, states_per_lane 2 or 4.
 hipError_t launch_scan_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16,
                             bool has_z, bool carry, hipStream_t s);
+// Specialised path pre-pass: pack B/C rows into ws_BC.
+hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s);
 
 }  // namespace ssm

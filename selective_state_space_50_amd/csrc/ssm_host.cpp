@@ -106,8 +106,12 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
               const ssm_scan_opts *opts, ScanPlan *plan) {
     int st = check_dims(batch, seqlen, dim, dstate, dtype);
     if (st != SSM_OK) return st;
-    ssm_scan_opts o{0, 0, 0};
+    ssm_scan_opts o{0, 0, 0, 0, 0};
     if (opts) o = *opts;
+    if (o.one_block_per_cu < -1 || o.one_block_per_cu > 1 || o.reserved != 0) {
+        set_error("opts.one_block_per_cu=%d must be -1, 0 or 1 and opts.reserved 0", o.one_block_per_cu);
+        return SSM_EINVAL;
+    }
     if (o.chunk_len < 0) {
         set_error("opts.chunk_len=%lld is negative", (long long)o.chunk_len);
         return SSM_EINVAL;
@@ -172,24 +176,53 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     }
     p.chunk_len = seqlen > 0 ? ceil_div(seqlen, n_chunks) : 0;
     p.n_chunks = seqlen > 0 ? ceil_div(seqlen, p.chunk_len > 0 ? p.chunk_len : 1) : 1;
-    if (p.n_chunks > 1) {
-        const size_t carries = static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks - 1) *
-                               static_cast<size_t>(dim);
-        p.ws_S_off = 0;
-        p.ws_H_off = align_up(carries * sizeof(float), kWsAlign);
-        p.ws_bytes = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float),
-                              kWsAlign);
-    }
     // grid: x = 64-channel blocks, y = batch rows, z = chunks (hardware limit 65535 on y and z)
     if (batch > 65535 || p.n_chunks > 65535 || dblocks > 0x7fffffff) {
         set_error("grid too large (batch=%lld, chunks=%lld): at most 65535 of each",
                   (long long)batch, (long long)p.n_chunks);
         return SSM_EUNSUPPORTED;
     }
-    p.fast = dstate == 16 && dim % 64 == 0 && dim < (int64_t(1) << 24) &&
-             ((p.G == 2 && p.TB == 16) || (p.G == 4 && (p.TB == 16 || p.TB == 32)));
+    // specialised kernel: 16 / G compute waves (G = 2 or 4 states per lane) + 4 helper
+    // waves, 16-step blocks, double-buffered LDS, B/C rows packed to fp32 by a pre-pass
+    p.fast = dstate == 16 && dim % 64 == 0 && dim < (int64_t(1) << 24) && (p.G == 2 || p.G == 4) &&
+             (o.time_block == 0 || o.time_block == 16);
+    if (p.fast) {
+        // With G = 4 a grid of at most one compute wave per SIMD leaves each compute wave
+        // alone on its SIMD, where it cannot hide the scalar-load latency of B/C; G = 2
+        // puts two compute waves on every SIMD instead.
+        const int64_t cw4 = batch * dblocks * p.n_chunks * 4;
+        if (o.states_per_lane == 0) p.G = cw4 <= kCUs * 4 ? 2 : 4;
+        p.TB = 16;
+        p.NW = 16 / p.G + 4;
+    }
+    size_t ws = 0;
+    if (p.n_chunks > 1) {
+        const size_t carries = static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks - 1) *
+                               static_cast<size_t>(dim);
+        p.ws_S_off = 0;
+        p.ws_H_off = align_up(carries * sizeof(float), kWsAlign);
+        ws = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
+    }
+    if (p.fast && seqlen > 0 && batch > 0 && dim > 0) {
+        // [batch][16/G][chunks][bc_lpad][G][B, C] fp32, zero past each chunk's end
+        p.bc_lpad = ceil_div(p.chunk_len, 16) * 16;
+        p.ws_BC_off = ws;
+        ws = align_up(ws + static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks) *
+                               static_cast<size_t>(p.bc_lpad) * 16 * 2 * sizeof(float),
+                      kWsAlign);
+    }
+    p.ws_bytes = ws;
     p.blocks = static_cast<uint64_t>(dblocks) * static_cast<uint64_t>(batch) *
                static_cast<uint64_t>(p.n_chunks);
+    // With no more workgroups than CUs, the dispatcher may still stack two on one
+    // CU and leave another idle; reserving over half of a CU's LDS prevents that.
+    const bool one = o.one_block_per_cu == 1 ||
+                     (o.one_block_per_cu == 0 && p.fast && p.blocks <= static_cast<uint64_t>(kCUs));
+    if (one && p.fast) {
+        // static LDS of the specialised kernel's y pass: staging 16 KiB + y shares 2 x NC x 4 KiB
+        const size_t used = 16384 + 2 * static_cast<size_t>(16 / p.G) * 4096;
+        if (used <= kLdsPerCU / 2) p.lds_reserve = kLdsPerCU / 2 + 1024 - used;
+    }
     *plan = p;
     return SSM_OK;
 }
@@ -313,6 +346,7 @@ int ssm_scan_plan_get(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
     out->time_block = p.TB;
     out->specialised = p.fast ? 1 : 0;
     out->workspace_bytes = p.ws_bytes;
+    out->lds_reserve = p.lds_reserve;
     out->blocks = p.blocks;
     return SSM_OK;
 }

@@ -13,6 +13,8 @@ constexpr int kWave = 64;            // lanes per wavefront on gfx950
 constexpr int kChannelsPerBlock = 64; // one channel per lane of a wave
 constexpr int kMaxWavesPerBlock = 16;
 constexpr size_t kWsAlign = 256;
+constexpr int64_t kCUs = 256;          // MI355X compute units
+constexpr size_t kLdsPerCU = 160 * 1024;
 
 struct ScanPlan {
     int G = 4;            // states of one channel held by one lane
@@ -23,8 +25,11 @@ struct ScanPlan {
     size_t ws_bytes = 0;  // workspace for chunk carries (0 when n_chunks == 1)
     size_t ws_S_off = 0;  // byte offset of the per-chunk delta sums [B][C-1][D]
     size_t ws_H_off = 0;  // byte offset of the per-chunk end states [B][C-1][D][N]
+    size_t ws_BC_off = 0; // specialised kernel: byte offset of the packed fp32 B/C rows
+    int64_t bc_lpad = 0;  // specialised kernel: steps per chunk in the packed B/C rows (multiple of 16)
     uint64_t blocks = 0;  // workgroups of the main scan launch
     bool fast = false;    // dstate == 16 and dim % 64 == 0: the specialised kernel runs
+    size_t lds_reserve = 0;  // dynamic LDS that caps residency at one workgroup per CU
 };
 
 // Per-thread error text (ssm_last_error).

@@ -32,42 +32,51 @@ int main() {
                     const ssm_scan_opts *o, const void *w, size_t wb, const float *h0_, const float *hl_) {
         return check_scan(b, l, d, n, dt, x_, dl, A, B, C, Dk, z, h0_, hl_, y_, 0, o, w, wb, &p);
     };
-    EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_OK);
-    EXPECT(p.n_chunks == 1 && p.G == 4 && p.NW == 4 && p.TB == 32 && p.ws_bytes == 0);
-    EXPECT(scan(4, 4096, 4096, 16, 2, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
-    EXPECT(scan(4, 4096, 4096, 17, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EUNSUPPORTED);
-    EXPECT(scan(4, 4096, 4096, 0, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
-    EXPECT(scan(-1, 4096, 4096, 16, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
-    EXPECT(scan(4, 4096, 4096, 16, 1, nullptr, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
-    EXPECT(scan(4, 4096, 4096, 16, 1, P(base + 2), y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
-    EXPECT(scan(4, 4096, 4096, 16, 1, x, P(base + 64), nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
+    // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
+    EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
+    EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
+    EXPECT(p.n_chunks == 1 && p.G == 2 && p.NW == 12 && p.TB == 16 && p.fast);
+    EXPECT(p.ws_bytes == size_t(4) * 4096 * 16 * 2 * 4 && p.bc_lpad == 4096);
+    EXPECT(p.lds_reserve + 16384 + 2 * (16 / p.G) * 4096 > 80 * 1024 && p.lds_reserve + 16384 + 2 * (16 / p.G) * 4096 <= 160 * 1024);
+    EXPECT(scan(4, 4096, 4096, 16, 2, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 17, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EUNSUPPORTED);
+    EXPECT(scan(4, 4096, 4096, 0, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(-1, 4096, 4096, 16, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, nullptr, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, P(base + 2), y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, x, P(base + 64), nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
     EXPECT(std::strstr(ssm_last_error(), "overlaps") != nullptr);
-    EXPECT(scan(4, 4096, 4096, 16, 1, x, y, nullptr, nullptr, 0, h0, h0) == SSM_EINVAL);
+    EXPECT(scan(4, 4096, 4096, 16, 1, x, y, nullptr, ws, size_t(1) << 30, h0, h0) == SSM_EINVAL);
     EXPECT(scan(int64_t(1) << 30, int64_t(1) << 30, 4096, 16, 1, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EINVAL);
     // empty problems are valid no-ops, even with null data pointers
     EXPECT(scan(0, 4096, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr) == SSM_OK);
     EXPECT(scan(4, 0, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, 0, h0, hl) == SSM_OK);
     // chunked plan needs a workspace
-    ssm_scan_opts o{1024, 0, 0};
+    ssm_scan_opts o{1024, 0, 0, 0, 0};
     EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
-    EXPECT(p.n_chunks == 8 && p.ws_bytes > 0);
+    EXPECT(p.n_chunks == 8 && p.ws_bytes > 0 && p.ws_BC_off > p.ws_H_off && p.bc_lpad == 1024);
     const size_t need = p.ws_bytes;
     EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, ws, need - 1, h0, hl) == SSM_EWORKSPACE);
     EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, ws, need, h0, hl) == SSM_OK);
     EXPECT(ssm_scan_workspace_bytes(1, 8192, 1024, 16, 1, &o) == need);
-    ssm_scan_opts bad1{-5, 0, 0}, bad2{0, 3, 0}, bad3{0, 0, 24}, bad4{0, 1, 32};
+    ssm_scan_opts bad1{-5, 0, 0, 0, 0}, bad2{0, 3, 0, 0, 0}, bad3{0, 0, 24, 0, 0}, bad4{0, 1, 32, 0, 0}, bad5{0, 0, 0, 2, 0};
     EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad1, nullptr, 0, h0, hl) == SSM_EINVAL);
     EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad2, nullptr, 0, h0, hl) == SSM_EINVAL);
     EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad3, nullptr, 0, h0, hl) == SSM_EINVAL);
     EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad4, nullptr, 0, h0, hl) == SSM_EINVAL);
+    EXPECT(scan(1, 100, 64, 16, 1, x, y, &bad5, nullptr, 0, h0, hl) == SSM_EINVAL);
     // automatic chunking for a long, narrow sequence
     EXPECT(scan(1, int64_t(1) << 20, 1024, 16, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
     EXPECT(p.n_chunks > 1);
     // every plan keeps the staging and LDS limits the kernel relies on
     for (int n = 1; n <= 16; ++n)
         for (int g : {0, 1, 2, 4, 8, 16}) {
-            ssm_scan_opts og{0, g, 0};
-            if (plan_scan(3, 1000, 100, n, 1, &og, &p) != SSM_OK) { EXPECT(false); continue; }
+            ssm_scan_opts og{0, g, 0, 0, 0};
+            if (plan_scan(3, 1000, n == 16 ? 128 : 100, n, 1, &og, &p) != SSM_OK) { EXPECT(false); continue; }
+            if (p.fast) {   // 16/G compute waves + 4 helpers, double-buffered staging and y shares
+                EXPECT(n == 16 && p.NW == 16 / p.G + 4 && (p.G == 2 || p.G == 4) && p.TB == 16);
+                continue;
+            }
             const int rows = (p.TB + p.NW - 1) / p.NW;
             EXPECT(rows <= 8);
             EXPECT(p.NW * p.G >= n && p.NW * p.G <= 16 && p.NW * 64 <= 1024);

@@ -36,10 +36,14 @@ def test_version_and_status_text(lib):
 
 def test_plans(lib):
     p2 = ssm.scan_plan(4, 4096, 4096, 16, "bf16")
-    assert p2["n_chunks"] == 1 and p2["states_per_lane"] == 4 and p2["waves_per_block"] == 4
+    # one 64-channel block per CU: two compute waves per SIMD with 2 states per lane
+    assert p2["n_chunks"] == 1 and p2["states_per_lane"] == 2 and p2["waves_per_block"] == 12
+    p8 = ssm.scan_plan(8, 4096, 4096, 16, "bf16")
+    assert p8["states_per_lane"] == 4 and p8["waves_per_block"] == 8
     assert p2["blocks"] == 4 * 64 and p2["specialised"] == 1
     assert ssm.scan_plan(2, 100, 130, 16, "bf16")["specialised"] == 0
     assert ssm.scan_plan(2, 100, 128, 12, "bf16")["specialised"] == 0
+    assert p2["workspace_bytes"] == 4 * 4096 * 16 * 2 * 4   # packed B/C rows
     p3 = ssm.scan_plan(1, 1 << 20, 1024, 16, "bf16")
     assert p3["n_chunks"] > 1 and p3["workspace_bytes"] > 0
     assert ssm.scan_workspace_bytes(1, 1 << 20, 1024, 16, "bf16") == p3["workspace_bytes"]
@@ -71,8 +75,10 @@ def test_validation_rejects_before_launch(lib):
     assert _scan_status(lib, y=G4 + 16) == 1
     assert b"overlaps" in lib.ssm_last_error()
     assert _scan_status(lib, softplus=3) == 1
-    assert _scan_status(lib, L=4096, opts=ssm.ScanOpts(128, 0, 0)) == 3
-    assert _scan_status(lib, opts=ssm.ScanOpts(0, 3, 0)) == 1
+    assert _scan_status(lib, L=4096, opts=ssm.ScanOpts(128, 0, 0, 0, 0)) == 3
+    assert _scan_status(lib, L=16, D=64) == 3        # packed B/C rows need a workspace
+    assert _scan_status(lib, opts=ssm.ScanOpts(0, 3, 0, 0, 0)) == 1
+    assert _scan_status(lib, opts=ssm.ScanOpts(0, 0, 0, 0, 7)) == 1
     V = ctypes.c_void_p
     assert lib.ssm_state_update(4, 64, 16, 1, None, V(1 << 40), V(1 << 41), V(1 << 42), V(1 << 43),
                                 V(1 << 44), None, None, V(1 << 45), 0, None) == 1

@@ -26,6 +26,8 @@ def _step_dev(step, dt):
 @pytest.mark.parametrize("Bsz,D,N,dt,gate,sp", [
     (1, 1, 1, "f32", False, False), (3, 70, 16, "f32", True, False), (2, 65, 5, "bf16", True, True),
     (4, 128, 12, "bf16", False, False), (2, 33, 3, "f32", True, False), (5, 256, 16, "bf16", True, False),
+    (3, 512, 16, "f32", True, True), (2, 256, 16, "f32", False, False), (1, 768, 16, "bf16", False, False),
+    (2, 64, 16, "bf16", True, False), (3, 192, 16, "f32", True, False),
 ])
 def test_decode_steps_small(ssm, Bsz, D, N, dt, gate, sp):
     import torch
@@ -95,3 +97,50 @@ def test_parity_config4_decode_1024_steps(ssm):
     hg = to_host(h)[cb, cd]
     st = assert_close(hg, h_ref, "f32", "h after 1024 steps")
     print(f"[parity] decode 1024 steps ok: y worst ratio {worst:.3f}, h {st}", flush=True)
+
+
+def test_decode_graph_replays_match_eager(ssm):
+    """The decode loop captured in a HIP graph: every replay (with eager work and
+    synchronisations between replays) reproduces the eager result bit for bit."""
+    import torch
+    Bsz, D, N, S = 8, 512, 16, 12
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    bf = torch.bfloat16
+    xs = torch.randn((S, Bsz, D), generator=g, device="cuda").to(bf)
+    ds = (torch.rand((S, Bsz, D), generator=g, device="cuda") * 0.1 + 1e-3).to(bf)
+    zs = torch.randn((S, Bsz, D), generator=g, device="cuda").to(bf)
+    Bs = torch.randn((S, Bsz, N), generator=g, device="cuda").to(bf)
+    Cs = torch.randn((S, Bsz, N), generator=g, device="cuda").to(bf)
+    A = torch.from_numpy(synth.make_A(0, D, N, "random")).cuda()
+    Dk = torch.from_numpy(synth.make_D(0, D, "normal")).cuda()
+    h = torch.zeros((Bsz, D, N), device="cuda")
+    ys = torch.empty((S, Bsz, D), dtype=bf, device="cuda")
+
+    def run():
+        for s in range(S):
+            ssm.state_update(h, xs[s], ds[s], A, Bs[s], Cs[s], Dk, zs[s], out=ys[s])
+
+    h.zero_()
+    run()
+    torch.cuda.synchronize()
+    y_eager, h_eager = ys.clone(), h.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        h.zero_()
+        run()          # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        h.zero_()
+        ys.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, y_eager), f"replay {rep}: y differs"
+        assert torch.equal(h, h_eager), f"replay {rep}: h differs"
+        _ = (xs.float().sum() + 1).item()   # unrelated eager work between replays

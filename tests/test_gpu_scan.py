@@ -99,16 +99,22 @@ def test_states_per_lane_variants(ssm, G, TB):
 
 
 FAST = [
-    # B, L, D, dtype, gate, h0, softplus, G, TB, chunk
-    (2, 1, 64, "f32", False, False, False, 4, 32, 0),
-    (2, 17, 64, "f32", True, True, False, 4, 32, 0),
+    # B, L, D, dtype, gate, h0, softplus, G, TB, chunk   (TB 0 = automatic)
+    (2, 1, 64, "f32", False, False, False, 4, 0, 0),
+    (2, 17, 64, "f32", True, True, False, 4, 0, 0),
     (3, 333, 192, "f32", True, True, False, 4, 16, 0),
-    (2, 100, 128, "f32", True, False, True, 2, 16, 0),
-    (1, 257, 64, "bf16", True, True, False, 2, 16, 0),
-    (2, 700, 128, "bf16", True, True, False, 4, 32, 0),
-    (2, 700, 128, "f32", False, True, False, 4, 32, 50),
-    (1, 999, 64, "f32", True, True, False, 2, 16, 100),
+    (2, 100, 128, "f32", True, False, True, 4, 0, 0),
+    (1, 257, 64, "bf16", True, True, False, 4, 0, 0),
+    (2, 700, 128, "bf16", True, True, False, 4, 16, 0),
+    (2, 700, 128, "f32", False, True, False, 4, 0, 50),
+    (1, 999, 64, "f32", True, True, False, 4, 0, 100),
     (2, 640, 64, "bf16", True, False, True, 4, 16, 64),
+    (1, 33, 64, "bf16", True, True, False, 4, 16, 16),
+    (1, 2, 64, "bf16", True, True, False, 4, 0, 1),
+    (2, 333, 128, "f32", True, True, False, 2, 0, 0),
+    (1, 700, 64, "bf16", True, True, True, 2, 16, 0),
+    (2, 500, 64, "f32", False, True, False, 2, 0, 70),
+    (1, 17, 192, "bf16", True, False, False, 2, 0, 0),
 ]
 
 
