@@ -83,6 +83,8 @@ def main():
                     help="few steps, no CPU baseline, no secondary (for rocprofv3)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--secondary-only", action="store_true")
+    ap.add_argument("--profile-decode", type=int, default=0, metavar="STEPS",
+                    help="only run this many decode steps of h[256,4096,16] (for rocprofv3)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +119,11 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy calibration: {args.copy_calibration} MiB copied 3 times")
+
+    if args.profile_decode:
+        profile_decode(torch, ssm, synth, dev, args.profile_decode)
+        log(f"decode profile run: {args.profile_decode} steps")
+        return
 
     result = {}
     cfg = synth.CONFIGS[2]
@@ -232,6 +239,24 @@ def _delta(shape, gen, dev, dtype):
     u = torch.rand(shape, generator=gen, device=dev, dtype=torch.float32)
     lo, hi = math.log(1e-3), math.log(1e-1)
     return torch.exp(lo + (hi - lo) * u).to(dtype)
+
+
+def profile_decode(torch, ssm, synth, dev, steps):
+    """A few decode steps on the decode workload's state (h [256, 4096, 16] fp32)."""
+    c = synth.CONFIGS[4]
+    Bsz, D, N = c["batch"], c["dim"], c["dstate"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    bf = torch.bfloat16
+    A = torch.from_numpy(synth.make_A(4, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(4, D, "normal")).to(dev)
+    h = torch.zeros((Bsz, D, N), device=dev)
+    y = torch.empty((Bsz, D), dtype=bf, device=dev)
+    for s in range(steps):
+        x, dl, z = _randn((Bsz, D), gen, dev, bf), _delta((Bsz, D), gen, dev, bf), _randn((Bsz, D), gen, dev, bf)
+        Bm, Cm = _randn((Bsz, N), gen, dev, bf), _randn((Bsz, N), gen, dev, bf)
+        ssm.state_update(h, x, dl, A, Bm, Cm, Dk, z, out=y)
+    torch.cuda.synchronize()
 
 
 def secondary(torch, ssm, synth, dev, log, src_hash):

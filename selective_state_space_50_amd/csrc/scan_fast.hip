@@ -212,44 +212,74 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
         }
     };
 
+    // Compute waves work in sub-blocks of SUB steps (16 floats of B/C, held in SGPRs).
+    // While a sub-block computes, the operands of the next one are requested: its
+    // (delta, delta*x) pairs from LDS and its B/C from the packed rows (scalar loads).
+    // Scalar loads return out of order, so each sub-block ends in one lgkmcnt(0) wait
+    // rather than one per step.  The B/C of the first sub-block of block k+1 are
+    // requested during the last sub-block of block k (they do not depend on the helpers).
+    constexpr int SUB = 8 / G;
+    constexpr int NSUB = kTB / SUB;
+    constexpr int NBC = SUB * 2 * G;    // 16 floats of B/C per sub-block
+    float bc_nx[NBC];                   // B/C of the next sub-block (maybe of the next block)
+
+    auto load_bc = [&](int64_t k, int sb) {
+        cfloat *src = bcw + (k * kTB + sb * SUB) * (2 * G);   // uniform: scalar loads
+#pragma unroll
+        for (int j = 0; j < NBC; ++j) bc_nx[j] = src[j];
+    };
+
     auto compute_block = [&](int64_t k, auto par) {   // compute waves: 16 steps of G states
         constexpr int P = decltype(par)::value;
-        cfloat *bck = bcw + k * kTB * (2 * G);        // uniform: scalar loads
-        // operands of step pair i+2 are fetched while pair i computes
-        float4 du_n = sDU[P][lane];
-        float bc_n[4 * G];
+        float4 du_c[SUB / 2], du_n[SUB / 2];
+        float bc_c[NBC];
 #pragma unroll
-        for (int j = 0; j < 4 * G; ++j) bc_n[j] = bck[j];
+        for (int q = 0; q < SUB / 2; ++q) du_c[q] = sDU[P][q * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < kTB; i += 2) {
-            const float4 du = du_n;
-            float bc[4 * G];
+        for (int j = 0; j < NBC; ++j) bc_c[j] = bc_nx[j];
+        // sub-block 0's operands land before the next prefetch is queued behind them
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4 * G; ++j) bc[j] = bc_n[j];
-            if (i + 2 < kTB) {
-                du_n = sDU[P][(i / 2 + 1) * 64 + lane];
+        for (int sb = 0; sb < NSUB; ++sb) {
+            if (sb + 1 < NSUB) {
 #pragma unroll
-                for (int j = 0; j < 4 * G; ++j) bc_n[j] = bck[(i + 2) * 2 * G + j];
+                for (int q = 0; q < SUB / 2; ++q) du_n[q] = sDU[P][((sb + 1) * SUB / 2 + q) * 64 + lane];
+                load_bc(k, sb + 1);
+            } else if (k + 1 < nblk) {
+                load_bc(k + 1, 0);
             }
-            // bc = [step i: g0 B, g0 C, g1 B, g1 C, ...][step i+1: ...]
-            if constexpr (CARRY) {
-                dsum += du.x;
-                dsum += du.z;
+            // keep those loads here: the scheduler would otherwise sink them to their use
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
-                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
-                }
-            } else {
-                float y0, y1;
+            for (int q = 0; q < SUB / 2; ++q) {
+                const float4 du = du_c[q];
+                const float *bc = bc_c + q * 4 * G;   // [step 2q: g B, g C ...][step 2q+1: ...]
+                if constexpr (CARRY) {
+                    dsum += du.x;
+                    dsum += du.z;
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
-                    y0 = g == 0 ? bc[1] * h[0] : __builtin_fmaf(bc[2 * g + 1], h[g], y0);
-                    h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
-                    y1 = g == 0 ? bc[2 * G + 1] * h[0] : __builtin_fmaf(bc[2 * G + 2 * g + 1], h[g], y1);
+                    for (int g = 0; g < G; ++g) {
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
+                    }
+                } else {
+                    float y0, y1;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
+                        y0 = g == 0 ? bc[1] * h[0] : __builtin_fmaf(bc[2 * g + 1], h[g], y0);
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
+                        y1 = g == 0 ? bc[2 * G + 1] * h[0] : __builtin_fmaf(bc[2 * G + 2 * g + 1], h[g], y1);
+                    }
+                    sY[P][(w * kTB / 2 + sb * SUB / 2 + q) * 64 + lane] = make_float2(y0, y1);
                 }
-                sY[P][(w * kTB / 2 + i / 2) * 64 + lane] = make_float2(y0, y1);
+            }
+            if (sb + 1 < NSUB) {
+#pragma unroll
+                for (int q = 0; q < SUB / 2; ++q) du_c[q] = du_n[q];
+#pragma unroll
+                for (int j = 0; j < NBC; ++j) bc_c[j] = bc_nx[j];
             }
         }
     };
@@ -293,6 +323,7 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
     };
 
     if (!helper) {
+        if (nblk > 0) load_bc(0, 0);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             Al[g] = a.A[d * kN + n0 + g] * kLog2e;
