@@ -172,7 +172,7 @@ def main():
         alg_slots = updates * SLOTS_PER_UPDATE + B * L * D * SLOTS_PER_TOKEN_CHANNEL_GATED
         hbm_gbs = alg_bytes / (k_avg * 1e-3) / 1e9
         alu_tslots = alg_slots / (k_avg * 1e-3) / 1e12
-        traffic = load_traffic("scan_cfg2", src_hash)
+        traffic = load_traffic("scan_B4_L4096_D4096_N16_bf16_gated", src_hash)
         roofline = {"bound": "alu", "achieved": round(alu_tslots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                     "unit": "Tslot/s", "frac": round(alu_tslots / VALU_PEAK_TSLOTS, 4),
                     "traffic": traffic,
@@ -306,7 +306,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / (k_avg * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_bytes / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic("state_update_cfg4", src_hash),
+                     "traffic": load_traffic("state_update_B256_D4096_N16_bf16_gated", src_hash),
                      "kernel_us_avg": round(k_avg * 1e3, 2), "alg_bytes_per_launch": step_bytes},
         "note": "h (67 MB) fits the 256 MB Infinity Cache, so steps after the first can beat HBM",
     }
