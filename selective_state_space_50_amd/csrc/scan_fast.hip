@@ -27,7 +27,16 @@ namespace {
 
 constexpr int kN = 16;
 constexpr int kTB = 16;          // time steps per block
-constexpr int kHT = 256;         // helper threads (4 waves, one per SIMD)
+// Helper register sets: the loads of block k are issued kRS - 1 blocks before block k is
+// staged (fewer sets for fp32 inputs, whose raw rows take twice the registers).
+template <typename T>
+constexpr int reg_sets() { return sizeof(T) == 2 ? 4 : 2; }
+// Helper waves: one per SIMD.  A helper thread owns RPT = 8 / HW rows and two adjacent
+// channels of every block.
+template <int G>
+constexpr int helper_waves() { return 4; }
+template <int G>
+constexpr int waves_per_block() { return kN / G + helper_waves<G>(); }
 
 template <int P>
 using Par = std::integral_constant<int, P>;
@@ -65,8 +74,11 @@ __device__ __forceinline__ void st_at(void *base, uint32_t byte_off, V v) {
 // address space lets wave-uniform reads become scalar loads into SGPRs.
 typedef const float __attribute__((address_space(4))) cfloat;
 
-// Pre-pass: ws_BC[b][w][c][tl][g][0/1] = B, C [b, c*chunk_len + tl, w*G + g], zero past
-// the chunk (or the sequence) so the last block of a chunk reads zeros.
+// Pre-pass: ws_BC[b][c][tl/16][w][tl%16][g][0/1] = B, C [b, c*chunk_len + tl, w*G + g],
+// zero past the chunk (or the sequence) so the last block of a chunk reads zeros.  The
+// rows of the 16/G compute waves are interleaved per 16-step block: the lines that the
+// waves of a workgroup read at the same time are adjacent instead of one chunk apart
+// (a stride that maps them all to the same sets of the scalar cache).
 template <typename T, int G>
 __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b, c, tl, n)
@@ -85,20 +97,30 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
     }
     const int w = n / G, g = n % G;
     float2 *o = reinterpret_cast<float2 *>(a.ws_BC);
-    o[(((b * (kN / G) + w) * a.n_chunks + c) * lp + tl) * G + g] = make_float2(bv, cv);
+    const int64_t blk = (b * a.n_chunks + c) * (lp / kTB) + tl / kTB;
+    o[((blk * (kN / G) + w) * kTB + tl % kTB) * G + g] = make_float2(bv, cv);
 }
 
 template <typename T, int G, bool HAS_Z, bool CARRY>
-__global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a) {
+__global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
     constexpr int NC = kN / G;          // compute waves
-    // Helper thread hid owns time rows 2*rp, 2*rp+1 and channels cp, cp+1 of every block.
-    static_assert((kTB / 2) * 32 == kHT, "helpers cover the block in row pairs x channel pairs");
+    constexpr int HW = helper_waves<G>();
+    constexpr int RPT = kTB * 32 / (HW * 64);   // rows per helper thread
+    static_assert(RPT == 1 || RPT == 2, "helpers cover the block in rows x channel pairs");
 
     // Step-pair interleaved layouts so one LDS instruction moves two steps:
     //   sDU [P][i/2][lane] float4 = (delta_i, delta_i*x_i, delta_i+1, delta_i+1*x_i+1)
     //   sY  [P][w][i/2][lane] float2 = (share of y_i, share of y_i+1)
-    __shared__ float4 sDU[2][kTB / 2 * 64];
-    __shared__ float2 sY[2][CARRY ? 1 : NC * kTB / 2 * 64];
+    // one object, staging first: every staging address stays below 64 KiB, in reach of
+    // the 16-bit immediate offset of the LDS instructions
+    struct Smem {
+        float4 du[2][kTB / 2 * 64];
+        float2 y[2][CARRY ? 1 : NC * kTB / 2 * 64];
+    };
+    __shared__ Smem smem;
+    auto &sDU = smem.du;
+    auto &sY = smem.y;
+    constexpr int kRS = reg_sets<T>();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -117,16 +139,18 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
     const int64_t d = d0 + lane;
     float Al[G], h[G];
     float dsum = 0.0f;
-    // packed B/C of this wave's states for this chunk: [step][g][B, C]
+    // packed B/C of this wave's states in block 0 of this chunk: [step][g][B, C]; the
+    // rows of the NC waves alternate every kTB steps
     // (global and constant address spaces share 64-bit addresses on gfx950)
     cfloat *bcw = reinterpret_cast<cfloat *>(reinterpret_cast<uintptr_t>(
-        a.ws_BC + ((b * NC + (helper ? 0 : w)) * a.n_chunks + c) * a.bc_lpad * (2 * G)));
+        a.ws_BC + ((b * a.n_chunks + c) * (a.bc_lpad / kTB) * NC + (helper ? 0 : w)) * kTB * (2 * G)));
 
     // ---- helper role
     const int hid = tid - NC * 64;
-    const int rp = hid >> 5;            // row pair
+    const int r0 = (hid >> 5) * RPT;    // first row of this thread
+    const int rp = r0 >> 1;             // its row pair in the step-pair layouts
+    const int rh = r0 & 1;              // RPT == 1: which row of the pair
     const int cp = (hid & 31) * 2;      // channel pair
-    const int r0 = 2 * rp;
     const int32_t D32 = static_cast<int32_t>(D);                // D < 2^24 (checked by the plan)
     const T *X = static_cast<const T *>(a.x) + b * L * D + d0;
     const T *DL = static_cast<const T *>(a.delta) + b * L * D + d0;
@@ -136,39 +160,42 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
     const uint32_t off0 = static_cast<uint32_t>(r0 * D32 + cp) * ES;    // row r0
     const uint32_t off1 = off0 + static_cast<uint32_t>(D32) * ES;       // row r0 + 1
     float dsk[2];
-    // raw prefetch registers, two sets by block parity (block j lives in set j & 1)
-    Vec<T, 2> rx[2][2], rd[2][2], rz[2][2];   // [set][row of the pair]
-    float ex[2][2][2], ez[2][2][2];     // [block parity][row][channel]
+    // raw prefetch registers, a ring of kRS sets (block j lives in set j % kRS), so the
+    // loads of a block are issued kRS - 1 blocks before they are staged
+    Vec<T, 2> rx[kRS][RPT], rd[kRS][RPT], rz[kRS][RPT];   // [set][row]
+    float ex[2][RPT][2], ez[2][RPT][2];     // [block parity][row][channel]
 
-    auto load_block = [&](int64_t tb0, auto set, auto full) {   // helpers: raw rows at tb0
+    // helpers: raw rows of block kb into register set S.  Branch-free, so that every call
+    // issues the same loads and the compiler can count exactly which of them are still in
+    // flight when a block is staged: a block past the last one reloads the last block, and
+    // rows past the end of the chunk reload its last row (staging zeroes those rows).
+    auto load_block = [&](int64_t kb, auto set) __attribute__((always_inline)) {
         constexpr int S = decltype(set)::value;
+        const int64_t tb0 = t0 + (kb < nblk ? kb : nblk - 1) * kTB;
+        const int32_t last = static_cast<int32_t>(t1 - 1 - tb0);   // last row of the block
         const T *xb = X + tb0 * D;      // uniform row bases
         const T *db = DL + tb0 * D;
         const T *zb = HAS_Z ? Z + tb0 * D : nullptr;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint32_t off = q ? off1 : off0;
-            if (decltype(full)::value || tb0 + r0 + q < t1) {
-                rx[S][q].r = ld_at<decltype(rx[S][q].r)>(xb, off);
-                rd[S][q].r = ld_at<decltype(rd[S][q].r)>(db, off);
-                if constexpr (HAS_Z && !CARRY) rz[S][q].r = ld_at<decltype(rz[S][q].r)>(zb, off);
-            } else {
-                rx[S][q].zero();
-                rd[S][q].zero();
-                if constexpr (HAS_Z && !CARRY) rz[S][q].zero();
-            }
+        for (int q = 0; q < RPT; ++q) {
+            const int32_t row = r0 + q < last ? r0 + q : last;
+            const uint32_t off = static_cast<uint32_t>(row * D32 + cp) * ES;
+            rx[S][q].r = ld_at<decltype(rx[S][q].r)>(xb, off);
+            rd[S][q].r = ld_at<decltype(rd[S][q].r)>(db, off);
+            if constexpr (HAS_Z && !CARRY) rz[S][q].r = ld_at<decltype(rz[S][q].r)>(zb, off);
         }
     };
 
-    auto stage_block = [&](int64_t tb0, auto par, auto full, auto softplus) {   // helpers
-        constexpr int P = decltype(par)::value;   // block parity = LDS buffer = register set
-        float dv[2][2], uv[2][2];
+    auto stage_block = [&](int64_t tb0, auto par, auto set, auto full, auto softplus) __attribute__((always_inline)) {   // helpers
+        constexpr int P = decltype(par)::value;   // block parity = LDS buffer
+        constexpr int S = decltype(set)::value;   // register set of the block
+        float dv[RPT][2], uv[RPT][2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < RPT; ++q) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                float dl = rd[P][q].get(j);
-                float xv = rx[P][q].get(j);
+                float dl = rd[S][q].get(j);
+                float xv = rx[S][q].get(j);
                 if constexpr (decltype(softplus)::value) dl = softplus_f(dl);
                 if constexpr (!decltype(full)::value) {
                     if (tb0 + r0 + q >= t1) { dl = 0.0f; xv = 0.0f; }   // padded steps leave h unchanged
@@ -176,27 +203,48 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
                 dv[q][j] = dl;
                 uv[q][j] = dl * xv;
                 ex[P][q][j] = xv;
-                ez[P][q][j] = (HAS_Z && !CARRY) ? rz[P][q].get(j) : 0.0f;
+                ez[P][q][j] = (HAS_Z && !CARRY) ? rz[S][q].get(j) : 0.0f;
             }
         }
+        if constexpr (RPT == 2) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
+            for (int j = 0; j < 2; ++j)
+                sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
+        } else {
+            // this row's half (.xy or .zw) of two adjacent entries
+            float2 *e = reinterpret_cast<float2 *>(&sDU[P][rp * 64 + cp]) + rh;
+            e[0] = make_float2(dv[0][0], uv[0][0]);
+            e[2] = make_float2(dv[0][1], uv[0][1]);
+        }
     };
 
-    auto epilogue = [&](int64_t tb0, auto par, auto full) {   // helpers: finish rows r0, r0+1
+    auto epilogue = [&](int64_t tb0, auto par, auto full) __attribute__((always_inline)) {   // helpers: finish rows r0, r0+1
         constexpr int P = decltype(par)::value;
-        // (y_r0 ch cp, y_r0+1 ch cp, y_r0 ch cp+1, y_r0+1 ch cp+1)
-        float4 acc = *reinterpret_cast<const float4 *>(&sY[P][rp * 64 + cp]);
+        float ys[RPT][2];               // [row][channel]
+        if constexpr (RPT == 2) {
+            // (y_r0 ch cp, y_r0+1 ch cp, y_r0 ch cp+1, y_r0+1 ch cp+1)
+            float4 acc = *reinterpret_cast<const float4 *>(&sY[P][rp * 64 + cp]);
 #pragma unroll
-        for (int ww = 1; ww < NC; ++ww) {
-            const float4 v = *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp) * 64 + cp]);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            for (int ww = 1; ww < NC; ++ww) {
+                const float4 v = *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp) * 64 + cp]);
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            ys[0][0] = acc.x; ys[0][1] = acc.z;
+            ys[RPT - 1][0] = acc.y; ys[RPT - 1][1] = acc.w;
+        } else {
+            // this row's component of the entries of channels cp and cp + 1
+            const float *e = reinterpret_cast<const float *>(&sY[P][rp * 64 + cp]) + rh;
+            float a0 = e[0], a1 = e[2];
+#pragma unroll
+            for (int ww = 1; ww < NC; ++ww) {
+                a0 += e[ww * kTB / 2 * 64 * 2];
+                a1 += e[ww * kTB / 2 * 64 * 2 + 2];
+            }
+            ys[0][0] = a0; ys[0][1] = a1;
         }
-        const float ys[2][2] = {{acc.x, acc.z}, {acc.y, acc.w}};
         T *yb = Yb + tb0 * D;           // uniform row base
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < RPT; ++q) {
             if (decltype(full)::value || tb0 + r0 + q < t1) {
                 float o[2];
 #pragma unroll
@@ -223,13 +271,13 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
     constexpr int NBC = SUB * 2 * G;    // 16 floats of B/C per sub-block
     float bc_nx[NBC];                   // B/C of the next sub-block (maybe of the next block)
 
-    auto load_bc = [&](int64_t k, int sb) {
-        cfloat *src = bcw + (k * kTB + sb * SUB) * (2 * G);   // uniform: scalar loads
+    auto load_bc = [&](int64_t k, int sb) __attribute__((always_inline)) {
+        cfloat *src = bcw + (k * NC * kTB + sb * SUB) * (2 * G);   // uniform: scalar loads
 #pragma unroll
         for (int j = 0; j < NBC; ++j) bc_nx[j] = src[j];
     };
 
-    auto compute_block = [&](int64_t k, auto par) {   // compute waves: 16 steps of G states
+    auto compute_block = [&](int64_t k, auto par) __attribute__((always_inline)) {   // compute waves: 16 steps of G states
         constexpr int P = decltype(par)::value;
         float4 du_c[SUB / 2], du_n[SUB / 2];
         float bc_c[NBC];
@@ -284,44 +332,25 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
         }
     };
 
-    auto stage_any = [&](int64_t tb0, auto par) {
+    auto stage_any = [&](int64_t tb0, auto par, auto set) __attribute__((always_inline)) {
         const bool full = tb0 + kTB <= t1;
         if (a.softplus) {
-            if (full) stage_block(tb0, par, Full{}, std::true_type{});
-            else stage_block(tb0, par, Part{}, std::true_type{});
+            if (full) stage_block(tb0, par, set, Full{}, std::true_type{});
+            else stage_block(tb0, par, set, Part{}, std::true_type{});
         } else {
-            if (full) stage_block(tb0, par, Full{}, std::false_type{});
-            else stage_block(tb0, par, Part{}, std::false_type{});
+            if (full) stage_block(tb0, par, set, Full{}, std::false_type{});
+            else stage_block(tb0, par, set, Part{}, std::false_type{});
         }
     };
-    auto load_any = [&](int64_t tb0, auto set) {
-        if (tb0 + kTB <= t1) load_block(tb0, set, Full{});
-        else load_block(tb0, set, Part{});
-    };
-    auto epilogue_any = [&](int64_t tb0, auto par) {
+    auto epilogue_any = [&](int64_t tb0, auto par) __attribute__((always_inline)) {
         if (tb0 + kTB <= t1) epilogue(tb0, par, Full{});
         else epilogue(tb0, par, Part{});
     };
 
-    // block k: compute waves scan buffer k&1; helpers finish block k-1, stage block k+1
-    // and prefetch block k+2
-    auto iteration = [&](int64_t k, auto par) {
-        constexpr int P = decltype(par)::value;
-        const int64_t tb0 = t0 + k * kTB;
-        if (!helper) {
-            compute_block(k, par);
-        } else {
-            if constexpr (!CARRY) {
-                if (k >= 1) epilogue_any(tb0 - kTB, Par<1 - P>{});
-            }
-            if (k + 1 < nblk) {
-                stage_any(tb0 + kTB, Par<1 - P>{});
-                if (k + 2 < nblk) load_any(tb0 + 2 * kTB, Par<P>{});
-            }
-        }
-        __syncthreads();
-    };
-
+    // The two roles run separate loops with one barrier per block each (and one after the
+    // prologue).  At block k the compute waves scan LDS buffer k & 1 while the helpers finish
+    // block k-1 (its y shares, buffer (k-1) & 1), stage block k+1 into buffer (k+1) & 1 and
+    // request block k+kRS into the register set that block k used.
     if (!helper) {
         if (nblk > 0) load_bc(0, 0);
 #pragma unroll
@@ -337,35 +366,18 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
             }
             h[g] = hv;
         }
-    } else {
-        // producer waves are served first, so their block is ready at each barrier
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dsk[j] = (!CARRY && a.Dskip) ? a.Dskip[d0 + cp + j] : 0.0f;
-        // keep the D loads out of the in-order queue of the block prefetch
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        if (nblk > 0) {
-            load_any(t0, Par<0>{});
-            stage_any(t0, Par<0>{});
-            if (nblk > 1) load_any(t0 + kTB, Par<1>{});
+        __syncthreads();
+        int64_t k = 0;
+        for (; k + 1 < nblk; k += 2) {
+            compute_block(k, Par<0>{});
+            __syncthreads();
+            compute_block(k + 1, Par<1>{});
+            __syncthreads();
         }
-    }
-    __syncthreads();
-    int64_t k = 0;
-    for (; k + 1 < nblk; k += 2) {
-        iteration(k, Par<0>{});
-        iteration(k + 1, Par<1>{});
-    }
-    if (k < nblk) iteration(k, Par<0>{});
-    if constexpr (!CARRY) {
-        if (helper && nblk > 0) {
-            const int64_t last = t0 + (nblk - 1) * kTB;
-            if ((nblk - 1) & 1) epilogue_any(last, Par<1>{});
-            else epilogue_any(last, Par<0>{});
+        if (k < nblk) {
+            compute_block(k, Par<0>{});
+            __syncthreads();
         }
-    }
-
-    if (!helper) {
         if constexpr (CARRY) {
             const int64_t slot = b * (a.n_chunks - 1) + c;
             if (w == 0) a.ws_S[slot * D + d] = dsum;
@@ -377,6 +389,56 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
                 for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + n0 + g] = h[g];
             }
         }
+    } else {
+        // producer waves are served first, so their block is ready at each barrier
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dsk[j] = (!CARRY && a.Dskip) ? a.Dskip[d0 + cp + j] : 0.0f;
+        // keep the D loads out of the in-order queue of the block prefetch
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        static_assert(kRS == 2 || kRS == 4, "the loop below is unrolled by four");
+        if (nblk > 0) {
+            load_block(0, Par<0>{});
+            load_block(1, Par<1>{});
+            if constexpr (kRS == 4) {
+                load_block(2, Par<2>{});
+                load_block(3, Par<3>{});
+            }
+            stage_any(t0, Par<0>{}, Par<0>{});
+        }
+        __syncthreads();
+        // block k >= 1, k % 4 == S: every block before the last is full
+        auto step = [&](int64_t k, auto set) __attribute__((always_inline)) {
+            constexpr int S = decltype(set)::value;
+            constexpr int P = S & 1;
+            const int64_t tb0 = t0 + k * kTB;
+            if constexpr (!CARRY) epilogue(tb0 - kTB, Par<1 - P>{}, Full{});
+            if (k + 1 < nblk) stage_any(tb0 + kTB, Par<1 - P>{}, Par<(S + 1) % kRS>{});
+            load_block(k + kRS, Par<S % kRS>{});
+            __syncthreads();
+        };
+        if (nblk > 0) {   // block 0: nothing to finish yet
+            if (nblk > 1) stage_any(t0 + kTB, Par<1>{}, Par<1>{});
+            load_block(kRS, Par<0>{});
+            __syncthreads();
+        }
+        int64_t k = 1;
+        for (; k + 3 < nblk; k += 4) {
+            step(k, Par<1>{});
+            step(k + 1, Par<2>{});
+            step(k + 2, Par<3>{});
+            step(k + 3, Par<0>{});
+        }
+        if (k < nblk) step(k, Par<1>{});
+        if (k + 1 < nblk) step(k + 1, Par<2>{});
+        if (k + 2 < nblk) step(k + 2, Par<3>{});
+        if constexpr (!CARRY) {
+            if (nblk > 0) {
+                const int64_t last = t0 + (nblk - 1) * kTB;
+                if ((nblk - 1) & 1) epilogue_any(last, Par<1>{});
+                else epilogue_any(last, Par<0>{});
+            }
+        }
     }
 }
 
@@ -384,7 +446,7 @@ __global__ void __launch_bounds__(64 * (kN / G + 4)) scan_fast_kernel(ScanArgs a
 template <typename T, int G>
 hipError_t launch_t(const ScanArgs &a, dim3 grid, bool has_z, bool carry, size_t lds_reserve,
                     hipStream_t s) {
-    const dim3 block(64 * (kN / G + 4));
+    const dim3 block(64 * waves_per_block<G>());
     if (carry) hipLaunchKernelGGL((scan_fast_kernel<T, G, false, true>), grid, block, 0, s, a);
     else if (has_z) hipLaunchKernelGGL((scan_fast_kernel<T, G, true, false>), grid, block, lds_reserve, s, a);
     else hipLaunchKernelGGL((scan_fast_kernel<T, G, false, false>), grid, block, lds_reserve, s, a);

@@ -193,7 +193,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         const int64_t cw4 = batch * dblocks * p.n_chunks * 4;
         if (o.states_per_lane == 0) p.G = cw4 <= kCUs * 4 ? 2 : 4;
         p.TB = 16;
-        p.NW = 16 / p.G + 4;
+        p.NW = 16 / p.G + 4;                        // compute waves + helper waves
     }
     size_t ws = 0;
     if (p.n_chunks > 1) {
@@ -204,7 +204,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         ws = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
     }
     if (p.fast && seqlen > 0 && batch > 0 && dim > 0) {
-        // [batch][16/G][chunks][bc_lpad][G][B, C] fp32, zero past each chunk's end
+        // [batch][chunks][bc_lpad/16][16/G][16][G][B, C] fp32, zero past each chunk's end
         p.bc_lpad = ceil_div(p.chunk_len, 16) * 16;
         p.ws_BC_off = ws;
         ws = align_up(ws + static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks) *
