@@ -35,8 +35,15 @@ constexpr int reg_sets() { return sizeof(T) == 2 ? 4 : 2; }
 // channels of every block.
 template <int G>
 constexpr int helper_waves() { return 4; }
+// With G = 2 (one workgroup per CU) a last wave only prefetches: at block k it reads one
+// word of every 64-byte line of the packed B/C of block k + kPD, so that the compute waves'
+// scalar loads of that block hit the scalar cache instead of going to L2 or beyond.  (With
+// G = 4 two workgroups share a CU and a ninth wave would not fit beside them.)
 template <int G>
-constexpr int waves_per_block() { return kN / G + helper_waves<G>(); }
+constexpr bool has_prefetch_wave() { return G == 2; }
+constexpr int kPD = 2;
+template <int G>
+constexpr int waves_per_block() { return kN / G + helper_waves<G>() + (has_prefetch_wave<G>() ? 1 : 0); }
 
 template <int P>
 using Par = std::integral_constant<int, P>;
@@ -125,7 +132,8 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool helper = w >= NC;        // wave-uniform role
+    const bool helper = w >= NC;        // wave-uniform role: not a compute wave
+    const bool pfw = has_prefetch_wave<G>() && w >= NC + helper_waves<G>();
     const int64_t D = a.D, L = a.L;
     const int64_t b = blockIdx.y;
     const int64_t c = blockIdx.z;
@@ -388,6 +396,29 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
 #pragma unroll
                 for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + n0 + g] = h[g];
             }
+        }
+    } else if (pfw) {
+        // one request per line, all issued before the one wait for them (a use per load
+        // would wait on each in turn); the wait falls before the barrier, well within a block
+        auto touch = [&](int64_t k) __attribute__((always_inline)) {
+            constexpr int NL = NC * kTB * 2 * G / 16;
+            cfloat *p = bcw + k * (NC * kTB * 2 * G);
+            float v[NL];
+#pragma unroll
+            for (int j = 0; j < NL; ++j) v[j] = p[j * 16];
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t acc = 0;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) acc ^= __float_as_uint(v[j]);
+            __asm__ volatile("" ::"s"(acc));   // keeps the loads
+        };
+#pragma unroll
+        for (int j = 1; j < kPD; ++j)
+            if (j < nblk) touch(j);
+        __syncthreads();
+        for (int64_t k = 0; k < nblk; ++k) {
+            if (k + kPD < nblk) touch(k + kPD);
+            __syncthreads();
         }
     } else {
         // producer waves are served first, so their block is ready at each barrier

@@ -193,7 +193,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         const int64_t cw4 = batch * dblocks * p.n_chunks * 4;
         if (o.states_per_lane == 0) p.G = cw4 <= kCUs * 4 ? 2 : 4;
         p.TB = 16;
-        p.NW = 16 / p.G + 4;                        // compute waves + helper waves
+        p.NW = 16 / p.G + 4 + (p.G == 2 ? 1 : 0);   // compute, helper and prefetch waves
     }
     size_t ws = 0;
     if (p.n_chunks > 1) {

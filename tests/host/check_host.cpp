@@ -35,7 +35,7 @@ int main() {
     // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
-    EXPECT(p.n_chunks == 1 && p.G == 2 && p.NW == 12 && p.TB == 16 && p.fast);
+    EXPECT(p.n_chunks == 1 && p.G == 2 && p.NW == 13 && p.TB == 16 && p.fast);
     EXPECT(p.ws_bytes == size_t(4) * 4096 * 16 * 2 * 4 && p.bc_lpad == 4096);
     EXPECT(p.lds_reserve + 16384 + 2 * (16 / p.G) * 4096 > 80 * 1024 && p.lds_reserve + 16384 + 2 * (16 / p.G) * 4096 <= 160 * 1024);
     EXPECT(scan(4, 4096, 4096, 16, 2, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
@@ -74,7 +74,7 @@ int main() {
             ssm_scan_opts og{0, g, 0, 0, 0};
             if (plan_scan(3, 1000, n == 16 ? 128 : 100, n, 1, &og, &p) != SSM_OK) { EXPECT(false); continue; }
             if (p.fast) {   // 16/G compute waves + 4 helpers, double-buffered staging and y shares
-                EXPECT(n == 16 && p.NW == 16 / p.G + 4 && (p.G == 2 || p.G == 4) && p.TB == 16);
+                EXPECT(n == 16 && p.NW == 16 / p.G + 4 + (p.G == 2) && (p.G == 2 || p.G == 4) && p.TB == 16);
                 continue;
             }
             const int rows = (p.TB + p.NW - 1) / p.NW;

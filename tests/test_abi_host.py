@@ -37,7 +37,7 @@ def test_version_and_status_text(lib):
 def test_plans(lib):
     p2 = ssm.scan_plan(4, 4096, 4096, 16, "bf16")
     # one 64-channel block per CU: two compute waves per SIMD with 2 states per lane
-    assert p2["n_chunks"] == 1 and p2["states_per_lane"] == 2 and p2["waves_per_block"] == 12
+    assert p2["n_chunks"] == 1 and p2["states_per_lane"] == 2 and p2["waves_per_block"] == 13
     p8 = ssm.scan_plan(8, 4096, 4096, 16, "bf16")
     assert p8["states_per_lane"] == 4 and p8["waves_per_block"] == 8
     assert p2["blocks"] == 4 * 64 and p2["specialised"] == 1
