@@ -298,6 +298,12 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
+            // The two compute waves of a SIMD take turns at the higher priority every half
+            // block.  Left to the age-ordered issue, the older one would run ahead, reach the
+            // barrier first and leave the younger one to finish alone at the issue rate of a
+            // single wave.
+            if ((((sb * 2) / NSUB + (w >> 2)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
             if (sb + 1 < NSUB) {
 #pragma unroll
                 for (int q = 0; q < SUB / 2; ++q) du_n[q] = sDU[P][((sb + 1) * SUB / 2 + q) * 64 + lane];
@@ -421,8 +427,9 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             __syncthreads();
         }
     } else {
-        // producer waves are served first, so their block is ready at each barrier
-        __builtin_amdgcn_s_setprio(1);
+        // producer waves are served first (above both compute priorities), so their block
+        // is ready at each barrier
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int j = 0; j < 2; ++j) dsk[j] = (!CARRY && a.Dskip) ? a.Dskip[d0 + cp + j] : 0.0f;
         // keep the D loads out of the in-order queue of the block prefetch
