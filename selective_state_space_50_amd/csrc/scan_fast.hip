@@ -5,18 +5,20 @@
 // states held in VGPRs, per-wave shares of y reduced through LDS -- but the
 // waves of a workgroup are split by role:
 //   * NC = 16 / G compute waves only scan: per step they read (delta,
-//     delta*x) and the B/C values of their states from LDS, update G states,
-//     and write their share of y to LDS.  They never touch global memory
-//     inside the sequence loop;
-//   * 4 helper waves (one per SIMD) do all streaming: they prefetch x, delta,
-//     z and the B/C rows one block ahead as vectors of adjacent channels,
-//     convert them into the LDS staging buffer, and finish every output row
-//     (sum of the NC shares, D*x, gate, packed bf16 store).
+//     delta*x) from LDS, take the B/C values of their states as scalar
+//     operands, update G states and write their share of y to LDS.  Their only
+//     memory traffic inside the sequence loop is those scalar loads;
+//   * 4 helper waves (one per SIMD) do all streaming: they prefetch x, delta
+//     and z three blocks ahead as vectors of adjacent channels, convert them
+//     into the LDS staging buffer, and finish every output row (sum of the NC
+//     shares, D*x, gate, packed bf16 store);
+//   * with G = 2, one prefetch wave pulls the packed B/C lines of block k+2
+//     into the scalar cache.
 // Staging and y-share buffers are double-buffered, so block k is scanned
 // while block k-1 is finished and block k+1 is staged; one barrier per block.
 // B_t and C_t are the same for every channel of a token, so they do not go
 // through LDS: a pre-pass packs them once per call to fp32, grouped by the
-// states of one compute wave, and each compute wave reads two steps of them
+// states of one compute wave, and each compute wave reads four steps of them
 // with one scalar load into SGPRs, which the VALU takes as scalar operands.
 #include "ssm_device.h"
 
