@@ -286,19 +286,40 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
 
     run_decode()
     torch.cuda.synchronize()
+    # Eager launches from Python are host-bound here (the binding's checks take longer
+    # than a step), so the step is timed from a HIP graph of the whole 1024-step loop,
+    # the way a serving loop would replay it.  The eager time is reported beside it.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
     h.zero_()
     torch.cuda.synchronize()
     e0.record()
-    for s in range(S):
-        kev[s][0].record()
-        ssm.state_update(h, xs[s], ds[s], A, Bs[s], Cs[s], Dk, zs[s], out=y)
-        kev[s][1].record()
+    run_decode_steps = lambda: [ssm.state_update(h, xs[s], ds[s], A, Bs[s], Cs[s], Dk, zs[s], out=y)
+                                for s in range(S)]
+    run_decode_steps()
     e1.record()
     torch.cuda.synchronize()
-    tot_ms = e0.elapsed_time(e1)
-    k_avg = sum(a.elapsed_time(b) for a, b in kev) / S
+    eager_ms = e0.elapsed_time(e1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ssm.state_update(h, xs[0], ds[0], A, Bs[0], Cs[0], Dk, zs[0], out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_decode_steps()
+    reps = []
+    for _ in range(3):
+        h.zero_()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1))
+    tot_ms = min(reps)
+    k_avg = tot_ms / S
+    del graph
     step_bytes = Bsz * D * N * 8 + Bsz * D * 2 * 4 + 2 * Bsz * N * 2 + D * N * 4 + D * 4
     out["decode"] = {
         "workload": c["name"], "tokens_per_s": Bsz * S / (tot_ms * 1e-3),
@@ -308,9 +329,12 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
                      "frac": round(step_bytes / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("state_update_B256_D4096_N16_bf16_gated", src_hash),
                      "kernel_us_avg": round(k_avg * 1e3, 2), "alg_bytes_per_launch": step_bytes},
+        "timing": "HIP graph of the 1024-step loop, best of 3 replays; per-step = replay / 1024",
+        "eager_ms_total": round(eager_ms, 2),
         "note": "h (67 MB) fits the 256 MB Infinity Cache, so steps after the first can beat HBM",
     }
-    log(f"decode: {tot_ms:.2f} ms for {S} steps, kernel {k_avg * 1e3:.1f} us avg")
+    log(f"decode: {tot_ms:.2f} ms for {S} steps from a graph ({k_avg * 1e3:.1f} us/step); "
+        f"eager from Python {eager_ms:.2f} ms")
     del xs, ds, zs, Bs, Cs, h
     torch.cuda.empty_cache()
     # --- million-token scan (chunk carries) ---

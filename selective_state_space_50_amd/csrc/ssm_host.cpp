@@ -157,11 +157,25 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         }
     }
     const int64_t dblocks = ceil_div(dim, kChannelsPerBlock);
+    const bool fast_ok = dstate == 16 && dim % 64 == 0 && dim < (int64_t(1) << 24) &&
+                         (o.states_per_lane == 0 || o.states_per_lane == 2 || o.states_per_lane == 4) &&
+                         (o.time_block == 0 || o.time_block == 16);
     // sequence chunks: split only when one pass leaves most SIMDs idle
     int64_t n_chunks = 1;
     if (seqlen > 0) {
         if (o.chunk_len > 0) {
             n_chunks = ceil_div(seqlen, o.chunk_len);
+        } else if (fast_ok) {
+            // specialised kernel: aim at one workgroup per CU (G = 2, two compute waves
+            // per SIMD), the configuration with the highest update rate per CU
+            const int64_t bd = batch * dblocks;
+            const int64_t kMinChunk = 2048;   // keeps the carry pass's share small
+            if (bd > 0 && bd < kCUs) {
+                const int64_t want = ceil_div(kCUs, bd);
+                const int64_t cap = ceil_div(seqlen, kMinChunk);
+                n_chunks = want < cap ? want : cap;
+                if (n_chunks < 1) n_chunks = 1;
+            }
         } else {
             const int64_t waves = batch * dblocks * p.NW;
             const int64_t kSimds = 1024;      // 256 CUs x 4 SIMDs
@@ -184,8 +198,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     }
     // specialised kernel: 16 / G compute waves (G = 2 or 4 states per lane) + 4 helper
     // waves, 16-step blocks, double-buffered LDS, B/C rows packed to fp32 by a pre-pass
-    p.fast = dstate == 16 && dim % 64 == 0 && dim < (int64_t(1) << 24) && (p.G == 2 || p.G == 4) &&
-             (o.time_block == 0 || o.time_block == 16);
+    p.fast = fast_ok && (p.G == 2 || p.G == 4);
     if (p.fast) {
         // With G = 4 a grid of at most one compute wave per SIMD leaves each compute wave
         // alone on its SIMD, where it cannot hide the scalar-load latency of B/C; G = 2
