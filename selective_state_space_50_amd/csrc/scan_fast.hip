@@ -28,11 +28,16 @@ namespace ssm {
 namespace {
 
 constexpr int kN = 16;
-constexpr int kTB = 16;          // time steps per block
+// Time steps per block.  (32 steps for the G = 2 y pass fits the LDS exactly but measured
+// no faster: the barriers are not what limits the kernel.)
+template <int G, bool CARRY>
+constexpr int time_block() { return 16; }
+// The packed B/C are laid out in 16-step blocks whatever the kernel's time block.
+constexpr int kLB = 16;
 // Helper register sets: the loads of block k are issued kRS - 1 blocks before block k is
 // staged (fewer sets for fp32 inputs, whose raw rows take twice the registers).
-template <typename T>
-constexpr int reg_sets() { return sizeof(T) == 2 ? 4 : 2; }
+template <typename T, int RPT>
+constexpr int reg_sets() { return (sizeof(T) == 2 && RPT <= 2) ? 4 : 2; }
 // Helper waves: one per SIMD.  A helper thread owns RPT = 8 / HW rows and two adjacent
 // channels of every block.
 template <int G>
@@ -83,11 +88,14 @@ __device__ __forceinline__ void st_at(void *base, uint32_t byte_off, V v) {
 // address space lets wave-uniform reads become scalar loads into SGPRs.
 typedef const float __attribute__((address_space(4))) cfloat;
 
-// Pre-pass: ws_BC[b][c][tl/16][w][tl%16][g][0/1] = B, C [b, c*chunk_len + tl, w*G + g],
-// zero past the chunk (or the sequence) so the last block of a chunk reads zeros.  The
-// rows of the 16/G compute waves are interleaved per 16-step block: the lines that the
-// waves of a workgroup read at the same time are adjacent instead of one chunk apart
-// (a stride that maps them all to the same sets of the scalar cache).
+// Pre-pass: the B and C values of token t = c*chunk_len + tl, state n = w*G + g, go to
+//   ws_BC[b][c][tl / 16][w][(tl % 16) / SUB][B or C][tl % SUB][g],   SUB = 8 / G,
+// fp32, zero past the chunk (or the sequence) so the last block of a chunk reads zeros.
+// A compute wave's sub-block of SUB steps is one 64-byte line: SUB*G values of B, then
+// SUB*G of C (so a pass that only needs B reads the first half as one 32-byte load).
+// The lines of the NC compute waves are interleaved per block: those that the waves of a
+// workgroup read at the same time are adjacent instead of one chunk apart (a stride that
+// maps them all to the same sets of the scalar cache).
 template <typename T, int G>
 __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b, c, tl, n)
@@ -104,18 +112,22 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
         bv = widen(static_cast<const T *>(a.Bm), (b * a.L + t) * kN + n);
         cv = widen(static_cast<const T *>(a.Cm), (b * a.L + t) * kN + n);
     }
+    constexpr int SUB = 8 / G;
     const int w = n / G, g = n % G;
-    float2 *o = reinterpret_cast<float2 *>(a.ws_BC);
-    const int64_t blk = (b * a.n_chunks + c) * (lp / kTB) + tl / kTB;
-    o[((blk * (kN / G) + w) * kTB + tl % kTB) * G + g] = make_float2(bv, cv);
+    const int tb = static_cast<int>(tl % kLB);
+    const int64_t blk = (b * a.n_chunks + c) * (lp / kLB) + tl / kLB;
+    float *o = a.ws_BC + ((blk * (kN / G) + w) * (kLB / SUB) + tb / SUB) * (2 * SUB * G) + (tb % SUB) * G + g;
+    o[0] = bv;
+    o[SUB * G] = cv;
 }
 
 template <typename T, int G, bool HAS_Z, bool CARRY>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
     constexpr int NC = kN / G;          // compute waves
+    constexpr int kTB = time_block<G, CARRY>();
     constexpr int HW = helper_waves<G>();
     constexpr int RPT = kTB * 32 / (HW * 64);   // rows per helper thread
-    static_assert(RPT == 1 || RPT == 2, "helpers cover the block in rows x channel pairs");
+    static_assert(RPT == 1 || RPT == 2 || RPT == 4, "helpers cover the block in rows x channel pairs");
 
     // Step-pair interleaved layouts so one LDS instruction moves two steps:
     //   sDU [P][i/2][lane] float4 = (delta_i, delta_i*x_i, delta_i+1, delta_i+1*x_i+1)
@@ -129,7 +141,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     __shared__ Smem smem;
     auto &sDU = smem.du;
     auto &sY = smem.y;
-    constexpr int kRS = reg_sets<T>();
+    constexpr int kRS = reg_sets<T, RPT>();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -150,10 +162,10 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     float Al[G], h[G];
     float dsum = 0.0f;
     // packed B/C of this wave's states in block 0 of this chunk: [step][g][B, C]; the
-    // rows of the NC waves alternate every kTB steps
+    // rows of the NC waves alternate every kLB steps
     // (global and constant address spaces share 64-bit addresses on gfx950)
     cfloat *bcw = reinterpret_cast<cfloat *>(reinterpret_cast<uintptr_t>(
-        a.ws_BC + ((b * a.n_chunks + c) * (a.bc_lpad / kTB) * NC + (helper ? 0 : w)) * kTB * (2 * G)));
+        a.ws_BC + ((b * a.n_chunks + c) * (a.bc_lpad / kLB) * NC + (helper ? 0 : w)) * kLB * (2 * G)));
 
     // ---- helper role
     const int hid = tid - NC * 64;
@@ -168,12 +180,11 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     T *Yb = static_cast<T *>(a.y) + b * L * D + d0;
     constexpr uint32_t ES = sizeof(T);
     const uint32_t off0 = static_cast<uint32_t>(r0 * D32 + cp) * ES;    // row r0
-    const uint32_t off1 = off0 + static_cast<uint32_t>(D32) * ES;       // row r0 + 1
     float dsk[2];
     // raw prefetch registers, a ring of kRS sets (block j lives in set j % kRS), so the
     // loads of a block are issued kRS - 1 blocks before they are staged
     Vec<T, 2> rx[kRS][RPT], rd[kRS][RPT], rz[kRS][RPT];   // [set][row]
-    float ex[2][RPT][2], ez[2][RPT][2];     // [block parity][row][channel]
+    Vec<T, 2> ex[2][RPT], ez[2][RPT];   // raw x, z kept for the epilogue [block parity][row]
 
     // helpers: raw rows of block kb into register set S.  Branch-free, so that every call
     // issues the same loads and the compiler can count exactly which of them are still in
@@ -212,14 +223,17 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 }
                 dv[q][j] = dl;
                 uv[q][j] = dl * xv;
-                ex[P][q][j] = xv;
-                ez[P][q][j] = (HAS_Z && !CARRY) ? rz[S][q].get(j) : 0.0f;
             }
+            ex[P][q] = rx[S][q];
+            if constexpr (HAS_Z && !CARRY) ez[P][q] = rz[S][q];
         }
-        if constexpr (RPT == 2) {
+        if constexpr (RPT >= 2) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
+            for (int qp = 0; qp < RPT / 2; ++qp)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    sDU[P][(rp + qp) * 64 + cp + j] =
+                        make_float4(dv[2 * qp][j], uv[2 * qp][j], dv[2 * qp + 1][j], uv[2 * qp + 1][j]);
         } else {
             // this row's half (.xy or .zw) of two adjacent entries
             float2 *e = reinterpret_cast<float2 *>(&sDU[P][rp * 64 + cp]) + rh;
@@ -231,16 +245,20 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     auto epilogue = [&](int64_t tb0, auto par, auto full) __attribute__((always_inline)) {   // helpers: finish rows r0, r0+1
         constexpr int P = decltype(par)::value;
         float ys[RPT][2];               // [row][channel]
-        if constexpr (RPT == 2) {
-            // (y_r0 ch cp, y_r0+1 ch cp, y_r0 ch cp+1, y_r0+1 ch cp+1)
-            float4 acc = *reinterpret_cast<const float4 *>(&sY[P][rp * 64 + cp]);
+        if constexpr (RPT >= 2) {
 #pragma unroll
-            for (int ww = 1; ww < NC; ++ww) {
-                const float4 v = *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp) * 64 + cp]);
-                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            for (int qp = 0; qp < RPT / 2; ++qp) {
+                // (y_2qp ch cp, y_2qp+1 ch cp, y_2qp ch cp+1, y_2qp+1 ch cp+1) of this row pair
+                float4 acc = *reinterpret_cast<const float4 *>(&sY[P][(rp + qp) * 64 + cp]);
+#pragma unroll
+                for (int ww = 1; ww < NC; ++ww) {
+                    const float4 v =
+                        *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp + qp) * 64 + cp]);
+                    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+                }
+                ys[2 * qp][0] = acc.x; ys[2 * qp][1] = acc.z;
+                ys[2 * qp + 1][0] = acc.y; ys[2 * qp + 1][1] = acc.w;
             }
-            ys[0][0] = acc.x; ys[0][1] = acc.z;
-            ys[RPT - 1][0] = acc.y; ys[RPT - 1][1] = acc.w;
         } else {
             // this row's component of the entries of channels cp and cp + 1
             const float *e = reinterpret_cast<const float *>(&sY[P][rp * 64 + cp]) + rh;
@@ -259,11 +277,11 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 float o[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    float yv = __builtin_fmaf(dsk[j], ex[P][q][j], ys[q][j]);
-                    if (HAS_Z) yv *= silu_f(ez[P][q][j]);
+                    float yv = __builtin_fmaf(dsk[j], ex[P][q].get(j), ys[q][j]);
+                    if constexpr (HAS_Z) yv *= silu_f(ez[P][q].get(j));
                     o[j] = yv;
                 }
-                const uint32_t off = q ? off1 : off0;
+                const uint32_t off = off0 + static_cast<uint32_t>(q * D32) * ES;
                 if constexpr (sizeof(T) == 2) st_at<uint32_t>(yb, off, pack_bf16(o[0], o[1]));
                 else st_at<float2>(yb, off, make_float2(o[0], o[1]));
             }
@@ -278,11 +296,13 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     // requested during the last sub-block of block k (they do not depend on the helpers).
     constexpr int SUB = 8 / G;
     constexpr int NSUB = kTB / SUB;
-    constexpr int NBC = SUB * 2 * G;    // 16 floats of B/C per sub-block
+    constexpr int NBC = SUB * 2 * G;    // 16 floats per sub-block: [step][g] of B, then of C
     float bc_nx[NBC];                   // B/C of the next sub-block (maybe of the next block)
 
     auto load_bc = [&](int64_t k, int sb) __attribute__((always_inline)) {
-        cfloat *src = bcw + (k * NC * kTB + sb * SUB) * (2 * G);   // uniform: scalar loads
+        // sub-block sb of block k: layout block k * kTB / kLB + sb * SUB / kLB (uniform: scalar loads)
+        const int64_t lb = k * (kTB / kLB) + (sb * SUB) / kLB;
+        cfloat *src = bcw + (lb * NC * kLB + (sb * SUB) % kLB) * (2 * G);
 #pragma unroll
         for (int j = 0; j < NBC; ++j) bc_nx[j] = src[j];
     };
@@ -318,23 +338,24 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
 #pragma unroll
             for (int q = 0; q < SUB / 2; ++q) {
                 const float4 du = du_c[q];
-                const float *bc = bc_c + q * 4 * G;   // [step 2q: g B, g C ...][step 2q+1: ...]
+                const float *bB = bc_c + 2 * q * G;             // B of steps 2q, 2q+1: [step][g]
+                const float *bC = bc_c + SUB * G + 2 * q * G;   // C of the same steps
                 if constexpr (CARRY) {
                     dsum += du.x;
                     dsum += du.z;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
-                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bB[g]);
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bB[G + g]);
                     }
                 } else {
                     float y0, y1;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bc[2 * g]);
-                        y0 = g == 0 ? bc[1] * h[0] : __builtin_fmaf(bc[2 * g + 1], h[g], y0);
-                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bc[2 * G + 2 * g]);
-                        y1 = g == 0 ? bc[2 * G + 1] * h[0] : __builtin_fmaf(bc[2 * G + 2 * g + 1], h[g], y1);
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.x * Al[g]), h[g], du.y * bB[g]);
+                        y0 = g == 0 ? bC[0] * h[0] : __builtin_fmaf(bC[g], h[g], y0);
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(du.z * Al[g]), h[g], du.w * bB[G + g]);
+                        y1 = g == 0 ? bC[G] * h[0] : __builtin_fmaf(bC[G + g], h[g], y1);
                     }
                     sY[P][(w * kTB / 2 + sb * SUB / 2 + q) * 64 + lane] = make_float2(y0, y1);
                 }
@@ -409,16 +430,20 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         // one request per line, all issued before the one wait for them (a use per load
         // would wait on each in turn); the wait falls before the barrier, well within a block
         auto touch = [&](int64_t k) __attribute__((always_inline)) {
-            constexpr int NL = NC * kTB * 2 * G / 16;
-            cfloat *p = bcw + k * (NC * kTB * 2 * G);
-            float v[NL];
+            constexpr int NL = NC * kTB * 2 * G / 16;   // lines per block
+            constexpr int NB = NL < 32 ? NL : 32;        // lines per batch of requests
+            cfloat *p = bcw + k * (NC * kTB * 2 * G);   // kTB / kLB adjacent layout blocks
 #pragma unroll
-            for (int j = 0; j < NL; ++j) v[j] = p[j * 16];
-            __builtin_amdgcn_sched_barrier(0);
-            uint32_t acc = 0;
+            for (int j0 = 0; j0 < NL; j0 += NB) {
+                float v[NB];
 #pragma unroll
-            for (int j = 0; j < NL; ++j) acc ^= __float_as_uint(v[j]);
-            __asm__ volatile("" ::"s"(acc));   // keeps the loads
+                for (int j = 0; j < NB; ++j) v[j] = p[(j0 + j) * 16];
+                __builtin_amdgcn_sched_barrier(0);
+                uint32_t acc = 0;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc ^= __float_as_uint(v[j]);
+                __asm__ volatile("" ::"s"(acc));   // keeps the loads
+            }
         };
 #pragma unroll
         for (int j = 1; j < kPD; ++j)

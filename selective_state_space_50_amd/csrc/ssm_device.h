@@ -30,7 +30,7 @@ struct ScanArgs {
     int64_t chunk_len, n_chunks;
     float *ws_S;          // [B][n_chunks-1][D]     sum of delta over a chunk
     float *ws_H;          // [B][n_chunks-1][D][N]  chunk end state, then carried-in state
-    float *ws_BC;         // specialised kernel: [B][n_chunks][bc_lpad/16][16/G][16][G][2] fp32 (B, C)
+    float *ws_BC;         // specialised kernel: packed fp32 B/C, 64-byte line per wave and sub-block
     int64_t bc_lpad;
 };
 

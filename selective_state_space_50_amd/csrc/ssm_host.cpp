@@ -217,7 +217,8 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         ws = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
     }
     if (p.fast && seqlen > 0 && batch > 0 && dim > 0) {
-        // [batch][chunks][bc_lpad/16][16/G][16][G][B, C] fp32, zero past each chunk's end
+        // [batch][chunks][bc_lpad/16][16/G][16/SUB][B, C][SUB][G] fp32 (SUB = 8/G), zero past
+        // each chunk's end
         p.bc_lpad = ceil_div(p.chunk_len, 16) * 16;
         p.ws_BC_off = ws;
         ws = align_up(ws + static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks) *
@@ -232,8 +233,8 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     const bool one = o.one_block_per_cu == 1 ||
                      (o.one_block_per_cu == 0 && p.fast && p.blocks <= static_cast<uint64_t>(kCUs));
     if (one && p.fast) {
-        // static LDS of the specialised kernel's y pass: staging 16 KiB + y shares 2 x NC x 4 KiB
-        const size_t used = 16384 + 2 * static_cast<size_t>(16 / p.G) * 4096;
+        // static LDS of the specialised kernel's y pass: double-buffered staging (TB/2 float4 per lane) and y shares (16/G waves)
+        const size_t used = static_cast<size_t>(p.TB) * 1024 + static_cast<size_t>(16 / p.G) * p.TB * 512;
         if (used <= kLdsPerCU / 2) p.lds_reserve = kLdsPerCU / 2 + 1024 - used;
     }
     *plan = p;
