@@ -115,6 +115,13 @@ FAST = [
     (1, 700, 64, "bf16", True, True, True, 2, 16, 0),
     (2, 500, 64, "f32", False, True, False, 2, 0, 70),
     (1, 17, 192, "bf16", True, False, False, 2, 0, 0),
+    (1, 16, 64, "bf16", True, True, False, 2, 0, 0),
+    (2, 4100, 64, "f32", True, True, True, 2, 0, 2048),
+    (3, 1500, 256, "f32", True, False, False, 2, 16, 0),
+    # planner's own choice: few channel blocks, so the sequence is cut into ragged chunks
+    # (1667 steps each here) to fill the CUs
+    (1, 5000, 128, "bf16", True, True, False, 0, 0, 0),
+    (2, 2049, 64, "bf16", True, True, True, 0, 0, 0),
 ]
 
 
