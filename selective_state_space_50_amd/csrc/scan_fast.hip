@@ -28,18 +28,15 @@ namespace ssm {
 namespace {
 
 constexpr int kN = 16;
-// Time steps per block.  (32 steps for the G = 2 y pass fits the LDS exactly but measured
-// no faster: the barriers are not what limits the kernel.)
-template <int G, bool CARRY>
-constexpr int time_block() { return 16; }
-// The packed B/C are laid out in 16-step blocks whatever the kernel's time block.
-constexpr int kLB = 16;
+// Time steps per block.  (32 steps for the G = 2 kernel would fill the LDS exactly but
+// measured no faster: the barriers are not what limits the kernel.)
+constexpr int kTB = 16;
 // Helper register sets: the loads of block k are issued kRS - 1 blocks before block k is
 // staged (fewer sets for fp32 inputs, whose raw rows take twice the registers).
-template <typename T, int RPT>
-constexpr int reg_sets() { return (sizeof(T) == 2 && RPT <= 2) ? 4 : 2; }
-// Helper waves: one per SIMD.  A helper thread owns RPT = 8 / HW rows and two adjacent
-// channels of every block.
+template <typename T>
+constexpr int reg_sets() { return sizeof(T) == 2 ? 4 : 2; }
+// Helper waves: one per SIMD.  A helper thread owns two rows (a step pair) and two
+// adjacent channels of every block.
 template <int G>
 constexpr int helper_waves() { return 4; }
 // With G = 2 (one workgroup per CU) a last wave only prefetches: at block k it reads one
@@ -114,9 +111,9 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
     }
     constexpr int SUB = 8 / G;
     const int w = n / G, g = n % G;
-    const int tb = static_cast<int>(tl % kLB);
-    const int64_t blk = (b * a.n_chunks + c) * (lp / kLB) + tl / kLB;
-    float *o = a.ws_BC + ((blk * (kN / G) + w) * (kLB / SUB) + tb / SUB) * (2 * SUB * G) + (tb % SUB) * G + g;
+    const int tb = static_cast<int>(tl % kTB);
+    const int64_t blk = (b * a.n_chunks + c) * (lp / kTB) + tl / kTB;
+    float *o = a.ws_BC + ((blk * (kN / G) + w) * (kTB / SUB) + tb / SUB) * (2 * SUB * G) + (tb % SUB) * G + g;
     o[0] = bv;
     o[SUB * G] = cv;
 }
@@ -124,10 +121,8 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
 template <typename T, int G, bool HAS_Z, bool CARRY>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
     constexpr int NC = kN / G;          // compute waves
-    constexpr int kTB = time_block<G, CARRY>();
-    constexpr int HW = helper_waves<G>();
-    constexpr int RPT = kTB * 32 / (HW * 64);   // rows per helper thread
-    static_assert(RPT == 1 || RPT == 2 || RPT == 4, "helpers cover the block in rows x channel pairs");
+    constexpr int RPT = 2;              // rows per helper thread
+    static_assert(kTB / RPT * 32 == helper_waves<G>() * 64, "helpers cover the block in row pairs x channel pairs");
 
     // Step-pair interleaved layouts so one LDS instruction moves two steps:
     //   sDU [P][i/2][lane] float4 = (delta_i, delta_i*x_i, delta_i+1, delta_i+1*x_i+1)
@@ -141,7 +136,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     __shared__ Smem smem;
     auto &sDU = smem.du;
     auto &sY = smem.y;
-    constexpr int kRS = reg_sets<T, RPT>();
+    constexpr int kRS = reg_sets<T>();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -162,16 +157,15 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     float Al[G], h[G];
     float dsum = 0.0f;
     // packed B/C of this wave's states in block 0 of this chunk: [step][g][B, C]; the
-    // rows of the NC waves alternate every kLB steps
+    // rows of the NC waves alternate every kTB steps
     // (global and constant address spaces share 64-bit addresses on gfx950)
     cfloat *bcw = reinterpret_cast<cfloat *>(reinterpret_cast<uintptr_t>(
-        a.ws_BC + ((b * a.n_chunks + c) * (a.bc_lpad / kLB) * NC + (helper ? 0 : w)) * kLB * (2 * G)));
+        a.ws_BC + ((b * a.n_chunks + c) * (a.bc_lpad / kTB) * NC + (helper ? 0 : w)) * kTB * (2 * G)));
 
     // ---- helper role
     const int hid = tid - NC * 64;
     const int r0 = (hid >> 5) * RPT;    // first row of this thread
     const int rp = r0 >> 1;             // its row pair in the step-pair layouts
-    const int rh = r0 & 1;              // RPT == 1: which row of the pair
     const int cp = (hid & 31) * 2;      // channel pair
     const int32_t D32 = static_cast<int32_t>(D);                // D < 2^24 (checked by the plan)
     const T *X = static_cast<const T *>(a.x) + b * L * D + d0;
@@ -227,49 +221,21 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             ex[P][q] = rx[S][q];
             if constexpr (HAS_Z && !CARRY) ez[P][q] = rz[S][q];
         }
-        if constexpr (RPT >= 2) {
 #pragma unroll
-            for (int qp = 0; qp < RPT / 2; ++qp)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    sDU[P][(rp + qp) * 64 + cp + j] =
-                        make_float4(dv[2 * qp][j], uv[2 * qp][j], dv[2 * qp + 1][j], uv[2 * qp + 1][j]);
-        } else {
-            // this row's half (.xy or .zw) of two adjacent entries
-            float2 *e = reinterpret_cast<float2 *>(&sDU[P][rp * 64 + cp]) + rh;
-            e[0] = make_float2(dv[0][0], uv[0][0]);
-            e[2] = make_float2(dv[0][1], uv[0][1]);
-        }
+        for (int j = 0; j < 2; ++j)
+            sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
     };
 
     auto epilogue = [&](int64_t tb0, auto par, auto full) __attribute__((always_inline)) {   // helpers: finish rows r0, r0+1
         constexpr int P = decltype(par)::value;
-        float ys[RPT][2];               // [row][channel]
-        if constexpr (RPT >= 2) {
+        // (y_r0 ch cp, y_r0+1 ch cp, y_r0 ch cp+1, y_r0+1 ch cp+1)
+        float4 acc = *reinterpret_cast<const float4 *>(&sY[P][rp * 64 + cp]);
 #pragma unroll
-            for (int qp = 0; qp < RPT / 2; ++qp) {
-                // (y_2qp ch cp, y_2qp+1 ch cp, y_2qp ch cp+1, y_2qp+1 ch cp+1) of this row pair
-                float4 acc = *reinterpret_cast<const float4 *>(&sY[P][(rp + qp) * 64 + cp]);
-#pragma unroll
-                for (int ww = 1; ww < NC; ++ww) {
-                    const float4 v =
-                        *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp + qp) * 64 + cp]);
-                    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-                }
-                ys[2 * qp][0] = acc.x; ys[2 * qp][1] = acc.z;
-                ys[2 * qp + 1][0] = acc.y; ys[2 * qp + 1][1] = acc.w;
-            }
-        } else {
-            // this row's component of the entries of channels cp and cp + 1
-            const float *e = reinterpret_cast<const float *>(&sY[P][rp * 64 + cp]) + rh;
-            float a0 = e[0], a1 = e[2];
-#pragma unroll
-            for (int ww = 1; ww < NC; ++ww) {
-                a0 += e[ww * kTB / 2 * 64 * 2];
-                a1 += e[ww * kTB / 2 * 64 * 2 + 2];
-            }
-            ys[0][0] = a0; ys[0][1] = a1;
+        for (int ww = 1; ww < NC; ++ww) {
+            const float4 v = *reinterpret_cast<const float4 *>(&sY[P][(ww * kTB / 2 + rp) * 64 + cp]);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
+        const float ys[RPT][2] = {{acc.x, acc.z}, {acc.y, acc.w}};   // [row][channel]
         T *yb = Yb + tb0 * D;           // uniform row base
 #pragma unroll
         for (int q = 0; q < RPT; ++q) {
@@ -300,9 +266,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     float bc_nx[NBC];                   // B/C of the next sub-block (maybe of the next block)
 
     auto load_bc = [&](int64_t k, int sb) __attribute__((always_inline)) {
-        // sub-block sb of block k: layout block k * kTB / kLB + sb * SUB / kLB (uniform: scalar loads)
-        const int64_t lb = k * (kTB / kLB) + (sb * SUB) / kLB;
-        cfloat *src = bcw + (lb * NC * kLB + (sb * SUB) % kLB) * (2 * G);
+        cfloat *src = bcw + (k * NC * kTB + sb * SUB) * (2 * G);   // uniform: scalar loads
 #pragma unroll
         for (int j = 0; j < NBC; ++j) bc_nx[j] = src[j];
     };
@@ -432,7 +396,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         auto touch = [&](int64_t k) __attribute__((always_inline)) {
             constexpr int NL = NC * kTB * 2 * G / 16;   // lines per block
             constexpr int NB = NL < 32 ? NL : 32;        // lines per batch of requests
-            cfloat *p = bcw + k * (NC * kTB * 2 * G);   // kTB / kLB adjacent layout blocks
+            cfloat *p = bcw + k * (NC * kTB * 2 * G);
 #pragma unroll
             for (int j0 = 0; j0 < NL; j0 += NB) {
                 float v[NB];
