@@ -196,6 +196,40 @@ def main():
             "roofline": roofline,
             "source_hash": src_hash,
         })
+        if not args.profile_run:
+            # Cold-cache launches: each preceded by an untimed 1 GiB write that evicts the L2s
+            # and the 256 MB Infinity Cache.  And a plain device copy for the HBM bandwidth
+            # this box reaches.
+            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            cold = []
+            for _ in range(10):
+                flush.fill_(1)
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                step()
+                b_.record()
+                torch.cuda.synchronize()
+                cold.append(a_.elapsed_time(b_))
+            cold.sort()
+            dst = torch.empty_like(flush)
+            cp = []
+            for _ in range(5):
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                dst.copy_(flush)
+                b_.record()
+                torch.cuda.synchronize()
+                cp.append(a_.elapsed_time(b_))
+            copy_gbs = 2 * (1 << 30) / (min(cp) * 1e-3) / 1e9
+            result_extra = {
+                "cold_cache": {"kernel_ms_median": round(cold[len(cold) // 2], 5), "kernel_ms_min": round(cold[0], 5),
+                               "note": "each launch after an untimed 1 GiB write (L2 and Infinity Cache evicted)"},
+                "copy_probe": {"GB/s": round(copy_gbs, 1), "note": "1 GiB device-to-device copy, read + write bytes"}}
+            log(f"cold cache: {cold[len(cold) // 2] * 1e3:.1f} us median; copy probe {copy_gbs:.0f} GB/s")
+            del flush, dst
+        else:
+            result_extra = {}
+        result.update(result_extra)
         del x, dl, z, Bm, Cm, y
 
         if not args.no_cpu_baseline:

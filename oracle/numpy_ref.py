@@ -50,3 +50,67 @@ def scan_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fal
             yt = yt * _silu(np.asarray(z, dtype=np.float64)[:, t, :])
         y[:, t, :] = yt
     return y, h
+
+
+def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=False,
+                gy=None, g_last=None):
+    """Reverse-mode derivative of ``scan_np`` for the loss <gy, y> + <g_last, h_last>.
+
+    Written as the chain rule through the discretised operands: with
+    lam_t = dLoss/dh_t (after step t), the step h_t = A_bar_t h_{t-1} + B_bar_t x_t gives
+        dLoss/dA_bar_t = lam_t * h_{t-1},   dLoss/dB_bar_t = lam_t * x_t,
+        dLoss/dh_{t-1} = A_bar_t * lam_t (+ the readout of step t-1),
+    and A_bar = exp(dt A), B_bar = dt B carry those on to dt, A, B.  All float64;
+    shapes as ``scan_np`` plus gy [B, L, D] and g_last [B, D, N] (either may be None
+    = zero).  Returns a dict dx, ddelta, dz, dB, dC, dA, dD, dh0 (dz None without a
+    gate; ddelta with respect to the raw input in softplus mode)."""
+    x = np.asarray(x, dtype=np.float64)
+    Bsz, L, D = x.shape
+    A = np.asarray(A, dtype=np.float64)
+    N = A.shape[1]
+    Bm = np.asarray(Bm, dtype=np.float64)
+    Cm = np.asarray(Cm, dtype=np.float64)
+    raw = np.asarray(delta, dtype=np.float64)
+    dl = _softplus(raw) if delta_softplus else raw
+    gy = np.zeros((Bsz, L, D)) if gy is None else np.asarray(gy, dtype=np.float64)
+    zz = None if z is None else np.asarray(z, dtype=np.float64)
+    # forward slabs: h_{t-1} for every t, and the ungated output
+    hs = np.empty((L + 1, Bsz, D, N))
+    hs[0] = 0.0 if h0 is None else np.asarray(h0, dtype=np.float64)
+    y0 = np.empty((Bsz, L, D))
+    for t in range(L):
+        a_bar = np.exp(dl[:, t, :, None] * A[None])
+        b_bar = dl[:, t, :, None] * Bm[:, t, None, :]
+        hs[t + 1] = a_bar * hs[t] + b_bar * x[:, t, :, None]
+        y0[:, t, :] = np.einsum("bdn,bn->bd", hs[t + 1], Cm[:, t, :])
+        if Dskip is not None:
+            y0[:, t, :] += np.asarray(Dskip, dtype=np.float64)[None, :] * x[:, t, :]
+    out = {"dx": np.zeros((Bsz, L, D)), "ddelta": np.zeros((Bsz, L, D)),
+           "dz": None if zz is None else np.zeros((Bsz, L, D)),
+           "dB": np.zeros((Bsz, L, N)), "dC": np.zeros((Bsz, L, N)),
+           "dA": np.zeros((D, N)), "dD": np.zeros(D)}
+    lam = np.zeros((Bsz, D, N)) if g_last is None else np.array(g_last, dtype=np.float64)
+    for t in range(L - 1, -1, -1):
+        if zz is not None:
+            sg = 1.0 / (1.0 + np.exp(-zz[:, t, :]))
+            gy0 = gy[:, t, :] * zz[:, t, :] * sg
+            out["dz"][:, t, :] = gy[:, t, :] * y0[:, t, :] * sg * (1.0 + zz[:, t, :] * (1.0 - sg))
+        else:
+            gy0 = gy[:, t, :]
+        if Dskip is not None:
+            out["dD"] += (gy0 * x[:, t, :]).sum(axis=0)
+            out["dx"][:, t, :] += np.asarray(Dskip, dtype=np.float64)[None, :] * gy0
+        # readout y0 = <h_t, C_t>: into C and into the state adjoint
+        out["dC"][:, t, :] += np.einsum("bd,bdn->bn", gy0, hs[t + 1])
+        lam = lam + gy0[:, :, None] * Cm[:, t, None, :]
+        a_bar = np.exp(dl[:, t, :, None] * A[None])
+        g_abar = lam * hs[t]                       # dLoss/dA_bar_t
+        g_bbar = lam * x[:, t, :, None]            # dLoss/dB_bar_t
+        out["dx"][:, t, :] += np.einsum("bdn,bdn->bd", lam, dl[:, t, :, None] * Bm[:, t, None, :])
+        g_dt = np.einsum("bdn,bdn->bd", g_abar, a_bar * A[None]) + np.einsum("bdn,bn->bd", g_bbar, Bm[:, t, :])
+        out["ddelta"][:, t, :] = g_dt / (1.0 + np.exp(-raw[:, t, :])) if delta_softplus else g_dt
+        out["dA"] += np.einsum("bdn,bdn->dn", g_abar, a_bar * dl[:, t, :, None])
+        out["dB"][:, t, :] += np.einsum("bdn,bd->bn", g_bbar, dl[:, t, :])
+        lam = a_bar * lam
+    out["dh0"] = lam
+    return out

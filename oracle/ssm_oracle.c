@@ -152,4 +152,175 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
     return 0;
 }
 
-int oracle_abi_version(void) { return 1; }
+/*
+ * Backward (adjoint) of the same scan, for a loss whose gradients with respect
+ * to the outputs are given: gy[t] = dLoss/dy[t] for every channel, and
+ * g_last[n] = dLoss/dh_last[n] (or 0).  Plain reverse-mode differentiation of
+ * the definition above, one channel at a time, no reordering:
+ *
+ *   forward, kept for the reverse sweep:  h_{t-1}[n], a_t[n] = exp(dt_t A[d,n]),
+ *                                         y0[t] = sum_n C[t,n] h_t[n] + D x[t]
+ *   lam[n] = g_last[n]                    (dLoss/dh_t[n] arriving from step t+1)
+ *   for t = L-1 .. 0:
+ *       gy0      = gy[t] * silu(z[t])     (gy[t] without a gate)
+ *       dz[t]    = gy[t] * y0[t] * silu'(z[t]),  silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *       dD      += gy0 * x[t]
+ *       dx[t]    = D gy0
+ *       for n:  lam[n]    += C[t,n] gy0                          (now dLoss/dh_t[n])
+ *               dC[t,n]   += gy0 h_t[n]
+ *               dB[t,n]   += lam[n] dt_t x[t]
+ *               dx[t]     += lam[n] dt_t B[t,n]
+ *               ddt       += lam[n] (A[d,n] a_t[n] h_{t-1}[n] + B[t,n] x[t])
+ *               dA[d,n]   += lam[n] dt_t a_t[n] h_{t-1}[n]
+ *               lam[n]     = a_t[n] lam[n]                       (dLoss/dh_{t-1}[n])
+ *       ddelta[t] = ddt (times sigmoid(delta[t]) in softplus mode, the derivative of
+ *                   softplus at the raw input)
+ *   dh0[n] = lam[n]
+ *
+ * The per-channel contributions to the shared tensors are returned separately
+ * (dB, dC per channel [nchan][L][N]; dA, dD per channel), and the caller sums
+ * them over the channels that share a batch row (dB, dC) or a dim index (dA, dD).
+ * Layouts: gy, dx, ddelta, dz [nchan][L]; g_last, dh0, dA_c [nchan][N]; dD_c [nchan].
+ */
+typedef struct {
+    int64_t L, N, nchan;
+    const int64_t *ch_b, *ch_d;
+    const double *x, *delta, *z;
+    int delta_softplus;
+    const double *Bm, *Cm, *A, *Dskip, *h0, *gy, *g_last;
+    double *dx, *ddelta, *dz, *dB_c, *dC_c, *dA_c, *dD_c, *dh0;
+    int64_t next;
+    pthread_mutex_t lock;
+} bjob_t;
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+static void one_channel_bwd(const bjob_t *J, int64_t c)
+{
+    const int64_t L = J->L, N = J->N;
+    const int64_t b = J->ch_b[c], d = J->ch_d[c];
+    const int64_t NN = N > 0 ? N : 1;
+    double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * NN));   /* h_{t-1} at row t */
+    double *y0 = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double *lam = (double *)malloc(sizeof(double) * (size_t)NN);
+
+    for (int64_t n = 0; n < N; ++n)
+        hs[n] = J->h0 ? J->h0[c * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        double dt = J->delta[c * L + t];
+        if (J->delta_softplus)
+            dt = softplus(dt);
+        const double xt = J->x[c * L + t];
+        const double *Bt = J->Bm + (b * L + t) * N;
+        const double *Ct = J->Cm + (b * L + t) * N;
+        double y = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double h = exp(dt * J->A[d * N + n]) * hs[t * N + n] + dt * Bt[n] * xt;
+            hs[(t + 1) * N + n] = h;
+            y += Ct[n] * h;
+        }
+        if (J->Dskip)
+            y += J->Dskip[d] * xt;
+        y0[t] = y;
+    }
+
+    for (int64_t n = 0; n < N; ++n) {
+        lam[n] = J->g_last ? J->g_last[c * N + n] : 0.0;
+        J->dA_c[c * N + n] = 0.0;
+    }
+    double dD = 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+        const double raw = J->delta[c * L + t];
+        const double dt = J->delta_softplus ? softplus(raw) : raw;
+        const double xt = J->x[c * L + t];
+        const double *Bt = J->Bm + (b * L + t) * N;
+        const double *Ct = J->Cm + (b * L + t) * N;
+        const double gy = J->gy[c * L + t];
+        double gy0 = gy;
+        if (J->z) {
+            const double zt = J->z[c * L + t];
+            const double s = sigmoid(zt);
+            gy0 = gy * (zt * s);
+            J->dz[c * L + t] = gy * y0[t] * (s * (1.0 + zt * (1.0 - s)));
+        }
+        dD += gy0 * xt;
+        double gx = J->Dskip ? J->Dskip[d] * gy0 : 0.0;
+        double gdt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double a = exp(dt * J->A[d * N + n]);
+            const double hprev = hs[t * N + n];
+            lam[n] += Ct[n] * gy0;
+            J->dC_c[(c * L + t) * N + n] = gy0 * hs[(t + 1) * N + n];
+            J->dB_c[(c * L + t) * N + n] = lam[n] * dt * xt;
+            gx += lam[n] * dt * Bt[n];
+            gdt += lam[n] * (J->A[d * N + n] * a * hprev + Bt[n] * xt);
+            J->dA_c[c * N + n] += lam[n] * dt * a * hprev;
+            lam[n] = a * lam[n];
+        }
+        J->dx[c * L + t] = gx;
+        J->ddelta[c * L + t] = J->delta_softplus ? gdt * sigmoid(raw) : gdt;
+    }
+    J->dD_c[c] = dD;
+    for (int64_t n = 0; n < N; ++n)
+        J->dh0[c * N + n] = lam[n];
+    free(hs);
+    free(y0);
+    free(lam);
+}
+
+static void *worker_bwd(void *arg)
+{
+    bjob_t *J = (bjob_t *)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        const int64_t c = J->next++;
+        pthread_mutex_unlock(&J->lock);
+        if (c >= J->nchan)
+            break;
+        one_channel_bwd(J, c);
+    }
+    return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments.  z may be NULL (no gate; dz is then
+ * not written), Dskip, h0 and g_last may be NULL. */
+int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const int64_t *ch_d,
+                    const double *x, const double *delta, const double *z, int delta_softplus,
+                    const double *Bm, const double *Cm, const double *A, const double *Dskip,
+                    const double *h0, const double *gy, const double *g_last,
+                    double *dx, double *ddelta, double *dz, double *dB_c, double *dC_c,
+                    double *dA_c, double *dD_c, double *dh0, int nthreads)
+{
+    if (L < 0 || N < 0 || nchan < 0)
+        return -1;
+    if (nchan > 0 && (!ch_b || !ch_d || !dD_c || !dh0 || (N > 0 && (!A || !dA_c)) ||
+                      (L > 0 && (!x || !delta || !Bm || !Cm || !gy || !dx || !ddelta || !dB_c || !dC_c)) ||
+                      (z && !dz)))
+        return -1;
+    bjob_t J;
+    memset(&J, 0, sizeof(J));
+    J.L = L; J.N = N; J.nchan = nchan; J.ch_b = ch_b; J.ch_d = ch_d;
+    J.x = x; J.delta = delta; J.z = z; J.delta_softplus = delta_softplus;
+    J.Bm = Bm; J.Cm = Cm; J.A = A; J.Dskip = Dskip; J.h0 = h0; J.gy = gy; J.g_last = g_last;
+    J.dx = dx; J.ddelta = ddelta; J.dz = dz; J.dB_c = dB_c; J.dC_c = dC_c; J.dA_c = dA_c;
+    J.dD_c = dD_c; J.dh0 = dh0; J.next = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if ((int64_t)nthreads > nchan)
+        nthreads = (int)(nchan > 0 ? nchan : 1);
+    pthread_t tid[256];
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&tid[started], NULL, worker_bwd, &J) == 0)
+            ++started;
+    worker_bwd(&J);
+    for (int i = 0; i < started; ++i)
+        pthread_join(tid[i], NULL);
+    pthread_mutex_destroy(&J.lock);
+    return 0;
+}
+
+int oracle_abi_version(void) { return 2; }

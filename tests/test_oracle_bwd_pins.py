@@ -1,0 +1,204 @@
+"""Pins of the backward (adjoint) oracle, against things other than itself.
+
+* Central finite differences of the forward oracle (already pinned by
+  tests/test_oracle_pins.py) for every input element of small problems: the
+  adjoint must equal the derivative of the forward definition.
+* The LTI special case: with constant step size, B and C, no gate and h0 = 0 the
+  scan is a causal convolution y = K * x + D x, so dLoss/dx is the correlation of
+  dLoss/dy with the same kernel K_k = sum_n C_n exp(dt A_n)^k dt B_n (brentwoodlivery
+  "State-space models (Mamba, S4)", section "The Convolution View"), written out by
+  brute force.
+* Linearity in the incoming gradient, and the two fp64 implementations (C and
+  numpy) agreeing.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.numpy_ref import scan_bwd_np, scan_np
+
+
+def _problem(seed, Bsz=2, L=6, D=3, N=3, gate=True, h0=True, dskip=True):
+    r = np.random.default_rng(seed)
+    p = {
+        "x": r.standard_normal((Bsz, L, D)),
+        "delta": np.exp(r.uniform(np.log(0.05), np.log(0.5), (Bsz, L, D))),
+        "z": r.standard_normal((Bsz, L, D)) if gate else None,
+        "B": r.standard_normal((Bsz, L, N)),
+        "C": r.standard_normal((Bsz, L, N)),
+        "A": -np.exp(r.standard_normal((D, N)) * 0.5),
+        "D": r.standard_normal(D) if dskip else None,
+        "h0": r.standard_normal((Bsz, D, N)) if h0 else None,
+    }
+    gy = r.standard_normal((Bsz, L, D))
+    gl = r.standard_normal((Bsz, D, N))
+    return p, gy, gl
+
+
+def _loss(p, gy, gl, sp):
+    y, h = scan_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp)
+    return float((y * gy).sum() + (h * gl).sum())
+
+
+def _c_bwd(p, gy, gl, sp):
+    """Backward through the C oracle on float64 arrays (channels in (b, d) order)."""
+    Bsz, L, D = p["x"].shape
+    N = p["A"].shape[1]
+    cb, cd = np.meshgrid(np.arange(Bsz), np.arange(D), indexing="ij")
+    cb, cd = cb.reshape(-1), cd.reshape(-1)
+    ser = lambda a: None if a is None else a[cb, :, cd]
+    r = oracle.scan_bwd_f64(ser(p["x"]), ser(p["delta"]), p["A"], p["B"], p["C"], p["D"], ser(p["z"]),
+                            None if p["h0"] is None else p["h0"][cb, cd, :], ser(gy),
+                            gl[cb, cd, :], sp, cb, cd, nthreads=2)
+    back = lambda a: a.reshape(Bsz, D, L).transpose(0, 2, 1)
+    return {"x": back(r["dx"]), "delta": back(r["ddelta"]),
+            "z": None if r["dz"] is None else back(r["dz"]),
+            "B": r["dB_c"].reshape(Bsz, D, L, N).sum(axis=1),
+            "C": r["dC_c"].reshape(Bsz, D, L, N).sum(axis=1),
+            "A": r["dA_c"].reshape(Bsz, D, N).sum(axis=0),
+            "D": r["dD_c"].reshape(Bsz, D).sum(axis=0),
+            "h0": r["dh0"].reshape(Bsz, D, N)}
+
+
+@pytest.mark.parametrize("seed,sp,gate,h0,dskip", [
+    (0, False, True, True, True), (1, True, True, True, True), (2, False, False, False, True),
+    (3, True, False, True, False),
+])
+def test_adjoint_equals_finite_differences(seed, sp, gate, h0, dskip):
+    p, gy, gl = _problem(seed, gate=gate, h0=h0, dskip=dskip)
+    if sp:
+        p["delta"] = np.log(np.expm1(p["delta"]))      # raw input u, dt = softplus(u)
+    g = _c_bwd(p, gy, gl, sp)
+    worst = 0.0
+    for name, arr in p.items():
+        if arr is None:
+            assert g[name] is None or name in ("D", "h0")
+            continue
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            v = arr[idx]
+            eps = 1e-6 * max(1.0, abs(v))
+            arr[idx] = v + eps
+            lp = _loss(p, gy, gl, sp)
+            arr[idx] = v - eps
+            lm = _loss(p, gy, gl, sp)
+            arr[idx] = v
+            fd = (lp - lm) / (2 * eps)
+            err = abs(fd - g[name][idx]) / max(1.0, abs(fd))
+            worst = max(worst, err)
+            assert err < 1e-6, (name, idx, fd, g[name][idx])
+    print(f"[pin] finite differences: worst {worst:.2e}")
+
+
+def test_lti_input_gradient_is_kernel_correlation():
+    r = np.random.default_rng(7)
+    Bsz, L, D, N = 1, 40, 2, 4
+    dt = np.array([0.3, 0.07])
+    A = -np.exp(r.standard_normal((D, N)) * 0.5)
+    Bv, Cv = r.standard_normal(N), r.standard_normal(N)
+    Dk = r.standard_normal(D)
+    p = {"x": r.standard_normal((Bsz, L, D)), "delta": np.broadcast_to(dt, (Bsz, L, D)).copy(),
+         "z": None, "B": np.broadcast_to(Bv, (Bsz, L, N)).copy(), "C": np.broadcast_to(Cv, (Bsz, L, N)).copy(),
+         "A": A, "D": Dk, "h0": None}
+    gy = r.standard_normal((Bsz, L, D))
+    g = _c_bwd(p, gy, np.zeros((Bsz, D, N)), False)
+    for d in range(D):
+        K = np.array([np.sum(Cv * np.exp(dt[d] * A[d]) ** k * dt[d] * Bv) for k in range(L)])
+        want = np.array([sum(K[t - s] * gy[0, t, d] for t in range(s, L)) + Dk[d] * gy[0, s, d]
+                         for s in range(L)])
+        np.testing.assert_allclose(g["x"][0, :, d], want, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_in_incoming_gradient():
+    p, gy, gl = _problem(11, L=20, D=4, N=5)
+    _, gy2, gl2 = _problem(12, L=20, D=4, N=5)
+    a, b = 0.7, -1.3
+    g1, g2 = _c_bwd(p, gy, gl, False), _c_bwd(p, gy2, gl2, False)
+    g12 = _c_bwd(p, a * gy + b * gy2, a * gl + b * gl2, False)
+    for k in g12:
+        np.testing.assert_allclose(g12[k], a * g1[k] + b * g2[k], rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("sp", [False, True])
+def test_c_and_numpy_backward_agree(sp):
+    p, gy, gl = _problem(21, Bsz=3, L=50, D=6, N=7)
+    if sp:
+        p["delta"] = np.log(np.expm1(p["delta"]))
+    g = _c_bwd(p, gy, gl, sp)
+    n = scan_bwd_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl)
+    names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0"}
+    for k, nk in names.items():
+        np.testing.assert_allclose(g[k], n[nk], rtol=1e-11, atol=1e-11)
+
+
+def test_storage_wrapper_matches_core():
+    import synth
+    inp = synth.scan_inputs(2, 33, 5, 16, "bf16", seed=5, gate=True, d_kind="normal", a_kind="random", h0=True)
+    r = np.random.default_rng(3)
+    gy = r.standard_normal((2, 33, 5))
+    out = oracle.scan_bwd(inp, gy)
+    w = lambda a: synth.to_f64(a, "bf16")
+    n = scan_bwd_np(w(inp["x"]), w(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["Dskip"],
+                    w(inp["z"]), inp["h0"], False, gy, None)
+    for k in n:
+        np.testing.assert_allclose(out[k], n[k], rtol=1e-11, atol=1e-11)
+
+
+# Planted mistakes in a copy of the numpy backward: each must fail the finite-difference
+# pin (so the pin would catch that mistake in the oracle).
+_MUTANTS = {
+    "silu_prime_dropped": ("sg * (1.0 + zz[:, t, :] * (1.0 - sg))", "sg"),
+    "readout_dropped": ("lam = lam + gy0[:, :, None] * Cm[:, t, None, :]", "lam = lam"),
+    "dA_without_dt": ("a_bar * dl[:, t, :, None])", "a_bar)"),
+    "dx_without_dt": ("dl[:, t, :, None] * Bm[:, t, None, :])", "Bm[:, t, None, :])"),
+    "ddelta_without_A": ("a_bar * A[None])", "a_bar)"),
+    "dh0_not_decayed": ("        lam = a_bar * lam\n", "        lam = lam\n"),
+    "dB_with_wrong_input": ("g_bbar = lam * x[:, t, :, None]", "g_bbar = lam * hs[t]"),
+    "softplus_chain_dropped": ("g_dt / (1.0 + np.exp(-raw[:, t, :]))", "g_dt"),
+    "dC_with_old_state": ("gy0, hs[t + 1])", "gy0, hs[t])"),
+}
+
+
+def _mutated_bwd(kind):
+    import inspect
+    from oracle import numpy_ref
+    src = inspect.getsource(numpy_ref.scan_bwd_np)
+    old, new = _MUTANTS[kind]
+    assert old in src, kind
+    ns = dict(vars(numpy_ref))
+    exec(src.replace(old, new), ns)
+    return ns["scan_bwd_np"]
+
+
+def _fd_worst(fn, seed, sp):
+    p, gy, gl = _problem(seed)
+    if sp:
+        p["delta"] = np.log(np.expm1(p["delta"]))
+    g = fn(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl)
+    names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0"}
+    worst = 0.0
+    for name, arr in p.items():
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            v = arr[idx]
+            eps = 1e-6 * max(1.0, abs(v))
+            arr[idx] = v + eps
+            lp = _loss(p, gy, gl, sp)
+            arr[idx] = v - eps
+            lm = _loss(p, gy, gl, sp)
+            arr[idx] = v
+            fd = (lp - lm) / (2 * eps)
+            worst = max(worst, abs(fd - g[names[name]][idx]) / max(1.0, abs(fd)))
+    return worst
+
+
+@pytest.mark.parametrize("kind", sorted(_MUTANTS))
+def test_planted_backward_mistake_is_caught(kind):
+    fn = _mutated_bwd(kind)
+    assert max(_fd_worst(fn, 30, False), _fd_worst(fn, 31, True)) > 1e-3, f"mutant {kind} passes the pin"
+
+
+def test_unmutated_backward_copy_passes():
+    assert max(_fd_worst(scan_bwd_np, 30, False), _fd_worst(scan_bwd_np, 31, True)) < 1e-6
