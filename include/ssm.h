@@ -164,6 +164,49 @@ int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, floa
                      const void *C, const float *Dskip, const void *z, void *y,
                      int delta_softplus, void *stream);
 
+/* Host-only: bytes of device workspace ssm_scan_bwd needs for this shape (0 when
+ * nothing is computed, or the shape is invalid or unsupported). */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    int dtype);
+
+/*
+ * Backward pass of ssm_scan_fwd: gradients of a loss with respect to every input,
+ * given dy = dLoss/dy and (optionally) dh_last = dLoss/dh_last.  Reverse-mode
+ * derivative of the recurrence above (the skill page's Verification Checklist asks
+ * for gradients through the step size; the step is the managen.ai page's "Selective
+ * Scan Algorithm"): with lam = dLoss/dh after step t, running t backwards,
+ *     lam += C_t gy0,  gy0 = dy_t * silu(z_t) (dy_t without a gate)
+ *     dC_t += gy0 h_t,   dB_t += lam dt x_t,   dA += lam dt exp(dt A) h_{t-1}
+ *     dx_t = D gy0 + dt sum_n lam B_t,  ddelta_t = sum_n lam (A exp(dt A) h_{t-1} + B_t x_t)
+ *     lam = exp(dt A) lam,   dh0 = lam after t = 0
+ * (ddelta_t is multiplied by sigmoid(delta_t) in softplus mode: the derivative with
+ * respect to the raw input).
+ *
+ * Inputs as ssm_scan_fwd (same layouts and dtypes), plus
+ *   dy        [batch, seqlen, dim]   dtype   required
+ *   dh_last   [batch, dim, dstate]   fp32    NULL = zero
+ * Outputs (device memory owned by the caller; none may overlap an input or another
+ * output; each is fully overwritten):
+ *   dx, ddelta [batch, seqlen, dim]  dtype   required
+ *   dz        [batch, seqlen, dim]   dtype   required when z is given, else ignored
+ *   dB, dC    [batch, seqlen, dstate] dtype  required (sums over dim)
+ *   dA        [dim, dstate]          fp32    required (sum over batch and time)
+ *   dD        [dim]                  fp32    required when Dskip is given, else ignored
+ *   dh0       [batch, dim, dstate]   fp32    NULL = not stored
+ *   workspace device memory of ssm_scan_bwd_workspace_bytes() bytes (state
+ *             checkpoints every 8 steps, packed B/C, partial sums)
+ *
+ * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  batch or dim
+ * == 0 is a no-op; seqlen == 0 sets dh0 = dh_last (or zeros) and dA, dD to zero.
+ * Deterministic: every reduction runs in a fixed order.
+ */
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                 const void *x, const void *delta, const float *A, const void *B,
+                 const void *C, const float *Dskip, const void *z, const float *h0,
+                 const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
+                 void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

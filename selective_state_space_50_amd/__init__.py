@@ -13,8 +13,9 @@ import ctypes
 import os
 import re
 
-__all__ = ["scan_fwd", "state_update", "scan_plan", "scan_workspace_bytes", "lib", "SSMError",
-           "LIB_PATH", "HEADER_PATH", "exported_api"]
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "scan_plan", "scan_workspace_bytes",
+           "scan_bwd_workspace_bytes", "selective_scan", "lib", "SSMError", "LIB_PATH",
+           "HEADER_PATH", "exported_api"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
@@ -73,6 +74,10 @@ def lib():
                                ctypes.POINTER(ScanOpts), P, SZ, P]
     L.ssm_state_update.restype = I32
     L.ssm_state_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, I32, P]
+    L.ssm_scan_bwd_workspace_bytes.restype = SZ
+    L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
+    L.ssm_scan_bwd.restype = I32
+    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, P, SZ, P]
     if L.ssm_abi_version() != 1:
         raise ImportError(f"libssm ABI version {L.ssm_abi_version()} != 1")
     _lib = L
@@ -228,3 +233,76 @@ def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False, 
                                 ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_state_update")
     return out
+
+
+def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    return int(lib().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, code))
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, *,
+             delta_softplus=False, need_dh0=True, workspace=None, stream=None):
+    """Gradients of a loss through scan_fwd, given dy = dLoss/dy [B, L, D] (same dtype as
+    x) and optionally dh_last = dLoss/dh_last [B, D, N] fp32.
+
+    Returns a dict: dx, ddelta, dz (None without z) in x's dtype [B, L, D]; dB, dC in
+    x's dtype [B, L, N]; dA [D, N], dD [D] (None without D) and dh0 [B, D, N] in fp32
+    (dh0 None when need_dh0 is false).
+    """
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, dim] and A [dim, dstate]")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("scan_bwd runs on the GPU only; tensors must be on a cuda device")
+    if dy is None:
+        raise ValueError("dy is required")
+    for t, name, shape, tdt in ((x, "x", (Bsz, L, Dm), dt), (delta, "delta", (Bsz, L, Dm), dt),
+                                (z, "z", (Bsz, L, Dm), dt), (B, "B", (Bsz, L, N), dt),
+                                (C, "C", (Bsz, L, N), dt), (A, "A", (Dm, N), torch.float32),
+                                (D, "D", (Dm,), torch.float32), (h0, "h0", (Bsz, Dm, N), torch.float32),
+                                (dy, "dy", (Bsz, L, Dm), dt), (dh_last, "dh_last", (Bsz, Dm, N), torch.float32)):
+        _need(t, name, shape, tdt, dev)
+    code = _dtype_code(x)
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+           "dz": torch.empty_like(x) if z is not None else None,
+           "dB": torch.empty((Bsz, L, N), dtype=dt, device=dev),
+           "dC": torch.empty((Bsz, L, N), dtype=dt, device=dev),
+           "dA": torch.empty((Dm, N), dtype=torch.float32, device=dev),
+           "dD": torch.empty((Dm,), dtype=torch.float32, device=dev) if D is not None else None,
+           "dh0": torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if need_dh0 else None}
+    ws_bytes = int(lib().ssm_scan_bwd_workspace_bytes(Bsz, L, Dm, N, code))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_scan_bwd(Bsz, L, Dm, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["dx"]),
+                            _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                            _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]), int(bool(delta_softplus)),
+                            _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_scan_bwd")
+    return out
+
+
+def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=False):
+    """Differentiable selective scan: y = scan_fwd(...) with a torch autograd backward
+    through scan_bwd (gradients for every tensor argument)."""
+    import torch
+
+    class _Scan(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, delta, A, B, C, D, z, h0):
+            y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus)
+            ctx.save_for_backward(x, delta, A, B, C, D, z, h0)
+            return y
+
+        @staticmethod
+        def backward(ctx, gy):
+            x, delta, A, B, C, D, z, h0 = ctx.saved_tensors
+            g = scan_bwd(x, delta, A, B, C, D, z, h0, gy.contiguous(), delta_softplus=delta_softplus,
+                         need_dh0=h0 is not None and ctx.needs_input_grad[7])
+            return g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"]
+
+    return _Scan.apply(x, delta, A, B, C, D, z, h0)

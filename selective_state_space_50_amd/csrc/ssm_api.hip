@@ -136,3 +136,71 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int 
     hipError_t e = launch_state_update(a, dtype == SSM_DTYPE_BF16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("state update launch", e);
 }
+
+extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                            const void *x, const void *delta, const float *A, const void *B,
+                            const void *C, const float *Dskip, const void *z, const float *h0,
+                            const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
+                            void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    using namespace ssm;
+    clear_error();
+    BwdPlan p;
+    int st = check_scan_bwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy,
+                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, workspace,
+                            workspace_bytes, &p);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (seqlen == 0) {
+        // no steps: dh0 = dh_last, and the reductions over steps are zero
+        if (dh0) {
+            const int64_t n = batch * dim * dstate;
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                               0, s, dh0, dh_last, n);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        }
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim * dstate + 255) / 256)),
+                           dim3(256), 0, s, dA, static_cast<const float *>(nullptr), dim * dstate);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        if (Dskip && dD) {
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
+                               0, s, dD, static_cast<const float *>(nullptr), dim);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        }
+        return SSM_OK;
+    }
+    char *ws = static_cast<char *>(workspace);
+    // packed B/C: the forward pre-pass with 4 states per wave, one chunk
+    ScanArgs pa;
+    pa.B = batch; pa.L = seqlen; pa.D = dim; pa.N = dstate;
+    pa.Bm = B; pa.Cm = C;
+    pa.chunk_len = seqlen; pa.n_chunks = 1;
+    pa.ws_BC = reinterpret_cast<float *>(ws + p.bc_off);
+    pa.bc_lpad = p.bc_lpad;
+    ScanPlan pp;
+    pp.G = 4;
+    const bool bf16 = dtype == SSM_DTYPE_BF16;
+    e = launch_bc_pack(pa, pp, bf16, s);
+    if (e != hipSuccess) return hip_fail("B/C pack launch", e);
+    BwdArgs a;
+    a.B = batch; a.L = seqlen; a.D = dim;
+    a.x = x; a.delta = delta; a.z = z; a.dy = dy;
+    a.A = A; a.Dskip = Dskip; a.h0 = h0; a.dh_last = dh_last;
+    a.dx = dx; a.ddelta = ddelta; a.dz = dz; a.dB = dB; a.dC = dC;
+    a.dA = dA; a.dD = Dskip ? dD : nullptr; a.dh0 = dh0;
+    a.softplus = delta_softplus;
+    a.nblk = p.nblk;
+    a.bc_lpad = p.bc_lpad;
+    a.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
+    a.ws_BC = pa.ws_BC;
+    a.partBC = reinterpret_cast<float *>(ws + p.partBC_off);
+    a.partA = reinterpret_cast<float *>(ws + p.partA_off);
+    a.partD = reinterpret_cast<float *>(ws + p.partD_off);
+    e = launch_scan_bwd(a, bf16, z != nullptr, s);
+    return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
+}

@@ -323,9 +323,97 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
     return check_no_overlap(outs, 2, all, n_all);
 }
 
+int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                  BwdPlan *plan) {
+    int st = check_dims(batch, seqlen, dim, dstate, dtype);
+    if (st != SSM_OK) return st;
+    if (dstate != 16 || dim % 64 != 0 || dim >= (int64_t(1) << 24)) {
+        set_error("ssm_scan_bwd supports dstate == 16 and dim a multiple of 64 (got dstate=%lld, dim=%lld)",
+                  (long long)dstate, (long long)dim);
+        return SSM_EUNSUPPORTED;
+    }
+    if (batch > 65535) {
+        set_error("batch=%lld: at most 65535 rows", (long long)batch);
+        return SSM_EUNSUPPORTED;
+    }
+    BwdPlan p;
+    p.nblk = ceil_div(seqlen, 8);
+    p.bc_lpad = ceil_div(seqlen, 16) * 16;
+    const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen), D = static_cast<size_t>(dim);
+    size_t ws = 0;
+    p.ckpt_off = ws;
+    ws = align_up(ws + B * static_cast<size_t>(p.nblk) * D * 16 * sizeof(float), kWsAlign);
+    p.bc_off = ws;
+    ws = align_up(ws + B * static_cast<size_t>(p.bc_lpad) * 16 * 2 * sizeof(float), kWsAlign);
+    p.partBC_off = ws;
+    ws = align_up(ws + 2 * B * (D / 64) * L * 16 * sizeof(float), kWsAlign);
+    p.partA_off = ws;
+    ws = align_up(ws + B * D * 16 * sizeof(float), kWsAlign);
+    p.partD_off = ws;
+    ws = align_up(ws + B * 4 * D * sizeof(float), kWsAlign);
+    p.ws_bytes = (batch == 0 || seqlen == 0 || dim == 0) ? 0 : ws;
+    *plan = p;
+    return SSM_OK;
+}
+
+int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                   const void *x, const void *delta, const float *A, const void *B, const void *C,
+                   const float *Dskip, const void *z, const float *h0, const void *dy,
+                   const float *dh_last, const void *dx, const void *ddelta, const float *dA,
+                   const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
+                   int delta_softplus, const void *workspace, size_t workspace_bytes, BwdPlan *plan) {
+    int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
+    if (st != SSM_OK) return st;
+    if (delta_softplus != 0 && delta_softplus != 1) {
+        set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
+        return SSM_EINVAL;
+    }
+    if (batch == 0 || dim == 0) return SSM_OK;
+    const char *missing = !A ? "A" : !dA ? "dA" : (z && !dz) ? "dz (z is given)" : (Dskip && !dD) ? "dD (Dskip is given)" : nullptr;
+    if (!missing && seqlen > 0)
+        missing = !x ? "x" : !delta ? "delta" : !B ? "B" : !C ? "C" : !dy ? "dy" : !dx ? "dx" :
+                  !ddelta ? "ddelta" : !dB ? "dB" : !dC ? "dC" : nullptr;
+    if (missing) {
+        set_error("required pointer %s is NULL", missing);
+        return SSM_EINVAL;
+    }
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    const int64_t tok = batch * seqlen * dim * es;
+    const int64_t bc = batch * seqlen * dstate * es;
+    const int64_t stb = batch * dim * dstate * 4;
+    Range all[] = {
+        range("x", x, tok), range("delta", delta, tok), range("z", z, tok), range("B", B, bc),
+        range("C", C, bc), range("A", A, dim * dstate * 4), range("Dskip", Dskip, dim * 4),
+        range("h0", h0, stb), range("dy", dy, tok), range("dh_last", dh_last, stb),
+        // outputs from here on
+        range("dx", dx, tok), range("ddelta", ddelta, tok), range("dA", dA, dim * dstate * 4),
+        range("dB", dB, bc), range("dC", dC, bc), range("dD", Dskip ? dD : nullptr, dim * 4),
+        range("dz", z ? dz : nullptr, tok), range("dh0", dh0, stb),
+        range("workspace", workspace, static_cast<int64_t>(plan->ws_bytes)),
+    };
+    const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
+    st = check_aligned(all, n_all);
+    if (st != SSM_OK) return st;
+    st = check_no_overlap(all + 10, n_all - 10, all, n_all);
+    if (st != SSM_OK) return st;
+    if (plan->ws_bytes > 0 && (!workspace || workspace_bytes < plan->ws_bytes)) {
+        set_error("workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                  plan->ws_bytes);
+        return SSM_EWORKSPACE;
+    }
+    return SSM_OK;
+}
+
 }  // namespace ssm
 
 extern "C" {
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+    ssm::clear_error();
+    ssm::BwdPlan p;
+    if (ssm::plan_scan_bwd(batch, seqlen, dim, dstate, dtype, &p) != SSM_OK) return 0;
+    return p.ws_bytes;
+}
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 

@@ -54,6 +54,26 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
                        const void *C, const float *Dskip, const void *z, const void *y,
                        int delta_softplus);
 
+// Workspace of ssm_scan_bwd: state checkpoints, packed B/C, per-workgroup shares of
+// dB/dC, per-batch-row shares of dA/dD.
+struct BwdPlan {
+    int64_t nblk = 0;       // 8-step blocks of the reverse sweep
+    int64_t bc_lpad = 0;    // steps in the packed B/C rows (multiple of 16)
+    size_t ckpt_off = 0, bc_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0;
+    size_t ws_bytes = 0;
+};
+
+int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                  BwdPlan *plan);
+
+// Full argument check of ssm_scan_bwd.
+int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                   const void *x, const void *delta, const float *A, const void *B, const void *C,
+                   const float *Dskip, const void *z, const float *h0, const void *dy,
+                   const float *dh_last, const void *dx, const void *ddelta, const float *dA,
+                   const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
+                   int delta_softplus, const void *workspace, size_t workspace_bytes, BwdPlan *plan);
+
 inline size_t dtype_size(int dtype) { return dtype == SSM_DTYPE_BF16 ? 2 : 4; }
 
 }  // namespace ssm

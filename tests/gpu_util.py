@@ -28,7 +28,7 @@ def device_inputs(inp):
     dt = inp["dtype"]
     out = {k: to_dev(inp[k], dt) for k in ("x", "delta", "z", "B", "C")}
     out["A"] = torch.from_numpy(inp["A"]).cuda()
-    out["D"] = torch.from_numpy(inp["Dskip"]).cuda()
+    out["D"] = None if inp.get("Dskip") is None else torch.from_numpy(inp["Dskip"]).cuda()
     out["h0"] = None if inp.get("h0") is None else torch.from_numpy(inp["h0"]).cuda()
     return out
 
@@ -69,3 +69,30 @@ def sample_channels(batch, dim, n):
         ch.add((i % batch, (i * 977 + 13) % dim))
         i += 1
     return sorted(ch)
+
+
+# Backward parity rule per gradient tensor G (the pages state no tolerance for the
+# backward; derived from the arithmetic): |gpu - oracle| <= max(RTOL * |oracle|,
+# FLOOR * max|oracle over G|).  The floor is relative to the tensor's own scale because
+# gradients are sums whose terms cancel (ddelta = sum of terms of both signs; dB, dC sum
+# over channels; dA over batch and time): an fp32 sum of K terms of size s carries an
+# error of about K * 6e-8 * s that no relative bound on a small result can cover.
+# bf16 outputs: RTOL 1e-2 (a bf16 rounding is 2^-8), FLOOR 2e-3.  fp32 outputs: RTOL 1e-3,
+# FLOOR 1e-4 (the adjoint runs through L fp32 decays and exps).
+BWD_TOL = {"bf16": (1e-2, 2e-3), "f32": (1e-3, 1e-4)}
+
+
+def assert_close_grad(g, r, dtype, what):
+    rtol, floor = BWD_TOL[dtype]
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite gradient"
+    scale = float(np.max(np.abs(r))) if r.size else 0.0
+    # an all-zero result (e.g. dA with h0 = 0 and one step) keeps a tiny absolute floor
+    lim = np.maximum(np.maximum(rtol * np.abs(r), floor * scale), 1e-7)
+    err = np.abs(g - r)
+    ratio = float(np.max(err / np.where(lim > 0, lim, 1.0))) if r.size else 0.0
+    bad = int((err > lim).sum())
+    assert bad == 0, f"{what}: {bad}/{r.size} out of tolerance, worst ratio {ratio:.3f}, scale {scale:.3g}"
+    return ratio

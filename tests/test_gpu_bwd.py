@@ -1,0 +1,125 @@
+"""GPU parity of ssm_scan_bwd (the backward pass) against the fp64 backward oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import assert_close_grad, device_inputs, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_50_amd as m
+    m.lib()
+    return m
+
+
+def _case(Bsz, L, D, dt, gate, h0, dhl, sp, dskip, seed):
+    inp = synth.scan_inputs(Bsz, L, D, 16, dt, seed=seed, gate=gate, d_kind="normal",
+                            a_kind="random", softplus_input=sp, h0=h0)
+    if not dskip:
+        inp["Dskip"] = None
+    r = np.random.default_rng(seed + 1000)
+    gy = synth.store(r.standard_normal((Bsz, L, D)).astype(np.float32), dt)
+    gl = r.standard_normal((Bsz, D, 16)).astype(np.float32) if dhl else None
+    return inp, gy, gl
+
+
+def _run(ssm, inp, gy, gl):
+    import torch
+    dt = inp["dtype"]
+    t = device_inputs(inp)
+    Dt = t["D"]
+    g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], Dt, t["z"], t["h0"], to_dev(gy, dt),
+                     None if gl is None else torch.from_numpy(gl).cuda(),
+                     delta_softplus=inp["delta_softplus"])
+    torch.cuda.synchronize()
+    return {k: (None if v is None else to_host(v)) for k, v in g.items()}
+
+
+def _check(g, r, dt, label):
+    worst = {}
+    for k in ("dx", "ddelta", "dz", "dB", "dC"):
+        if r[k] is None:
+            assert g[k] is None, k
+            continue
+        worst[k] = assert_close_grad(g[k], r[k], dt, f"{label} {k}")
+    for k in ("dA", "dD", "dh0"):
+        if g[k] is None:
+            continue
+        worst[k] = assert_close_grad(g[k], r[k], "f32", f"{label} {k}")   # fp32 outputs
+    print(f"[parity] backward {label}: worst ratios " + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()), flush=True)
+
+
+CASES = [
+    # B, L, D, dtype, gate, h0, dh_last, softplus, Dskip
+    (1, 1, 64, "f32", False, False, False, False, True),
+    (2, 17, 64, "f32", True, True, True, False, True),
+    (1, 8, 128, "f32", True, False, True, True, True),
+    (1, 9, 64, "bf16", True, True, False, False, True),
+    (2, 100, 128, "bf16", True, True, True, False, True),
+    (3, 333, 192, "f32", False, True, False, True, True),
+    (2, 64, 64, "bf16", False, False, True, False, False),
+    (1, 1000, 256, "bf16", True, True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,dt,gate,h0,dhl,sp,dskip", CASES)
+def test_backward_parity(ssm, Bsz, L, D, dt, gate, h0, dhl, sp, dskip):
+    inp, gy, gl = _case(Bsz, L, D, dt, gate, h0, dhl, sp, dskip, seed=40 + L)
+    g = _run(ssm, inp, gy, gl)
+    gy64 = synth.to_f64(gy, dt)
+    r = oracle.scan_bwd(inp, gy64, gl)
+    if not gate:
+        r["dz"] = None
+    if not dskip:
+        assert g["dD"] is None
+        r["dD"] = None
+    _check(g, r, dt, f"{Bsz}x{L}x{D} {dt} gate={gate} h0={h0} dh_last={dhl} softplus={sp} D={dskip}")
+
+
+def test_backward_deterministic(ssm):
+    inp, gy, gl = _case(2, 200, 128, "bf16", True, True, True, False, True, seed=7)
+    a = _run(ssm, inp, gy, gl)
+    b = _run(ssm, inp, gy, gl)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_empty_and_unsupported(ssm):
+    import torch
+    A = torch.zeros((64, 16), device="cuda")
+    Dk = torch.ones(64, device="cuda")
+    x = torch.zeros((2, 0, 64), device="cuda")
+    hl = torch.randn((2, 64, 16), device="cuda")
+    g = ssm.scan_bwd(x, x, A, torch.zeros((2, 0, 16), device="cuda"), torch.zeros((2, 0, 16), device="cuda"),
+                     Dk, None, None, x, hl)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], hl) and float(g["dA"].abs().sum()) == 0.0 and float(g["dD"].abs().sum()) == 0.0
+    xs = torch.zeros((1, 4, 96), device="cuda")
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.scan_bwd(xs, xs, torch.zeros((96, 16), device="cuda"), torch.zeros((1, 4, 16), device="cuda"),
+                     torch.zeros((1, 4, 16), device="cuda"), None, None, None, xs)
+    assert e.value.status == ssm.SSM_EUNSUPPORTED
+
+
+def test_autograd_matches_oracle(ssm):
+    """selective_scan's torch autograd backward is scan_bwd: gradients of <w, y> for
+    every input against the oracle."""
+    import torch
+    inp, gy, _ = _case(2, 50, 64, "f32", True, True, False, True, True, seed=3)
+    t = device_inputs(inp)
+    leaves = {k: t[k].clone().requires_grad_(True) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    y = ssm.selective_scan(leaves["x"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"], leaves["D"],
+                           leaves["z"], leaves["h0"], delta_softplus=True)
+    (y * to_dev(gy, "f32")).sum().backward()
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"))
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    for k, rk in names.items():
+        assert_close_grad(to_host(leaves[k].grad), r[rk], "f32", f"autograd {k}")
