@@ -371,6 +371,39 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         f"eager from Python {eager_ms:.2f} ms")
     del xs, ds, zs, Bs, Cs, h
     torch.cuda.empty_cache()
+    # --- backward pass at the headline shape ---
+    c = synth.CONFIGS[2]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    x, dl, z, gy = (_randn((Bsz, L, D), gen, dev, bf) if k != "dl" else _delta((Bsz, L, D), gen, dev, bf)
+                    for k in ("x", "dl", "z", "gy"))
+    Bm = _randn((Bsz, L, N), gen, dev, bf)
+    Cm = _randn((Bsz, L, N), gen, dev, bf)
+    A = torch.from_numpy(synth.make_A(2, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(2, D, "normal")).to(dev)
+    ws = torch.empty(ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16"), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
+    torch.cuda.synchronize()
+    bt = []
+    for _ in range(5):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
+        b_.record()
+        torch.cuda.synchronize()
+        bt.append(a_.elapsed_time(b_))
+    bt.sort()
+    ms = bt[len(bt) // 2]
+    upd = Bsz * L * D * N
+    out["backward"] = {
+        "workload": c["name"] + " backward (dx, ddelta, dz, dB, dC, dA, dD)",
+        "ms_median": round(ms, 4), "ms_min": round(bt[0], 4),
+        "state_updates_per_s": upd / (ms * 1e-3),
+        "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
+    }
+    log(f"backward: {ms:.3f} ms median ({upd / (ms * 1e-3):.3e} state-updates/s)")
+    del x, dl, z, gy, Bm, Cm, ws
+    torch.cuda.empty_cache()
     # --- million-token scan (chunk carries) ---
     c = synth.CONFIGS[3]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]

@@ -194,7 +194,7 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   dD        [dim]                  fp32    required when Dskip is given, else ignored
  *   dh0       [batch, dim, dstate]   fp32    NULL = not stored
  *   workspace device memory of ssm_scan_bwd_workspace_bytes() bytes (state
- *             checkpoints every 8 steps, packed B/C, partial sums)
+ *             checkpoints every 8 steps, partial sums)
  *
  * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  batch or dim
  * == 0 is a no-op; seqlen == 0 sets dh0 = dh_last (or zeros) and dA, dD to zero.

@@ -15,41 +15,48 @@
 // section "Selective Scan Algorithm"; the need for gradients through the step size is in
 // the skill page "State Space Models Mamba", Verification Checklist).
 //
-// Mapping: a workgroup = 64 channels (lanes) of one batch row; 4 waves, wave w holding
-// states 4w..4w+3 of every channel.  Two sweeps over the sequence:
+// Mapping: a workgroup = 64 channels (lanes) of one batch row; 8 waves, wave w holding
+// states 2w, 2w+1 of every channel (two waves per SIMD, so one can issue while the other
+// waits).  Two sweeps over the sequence:
 //   1. forward, storing the state at the start of every 8-step block (checkpoints);
 //   2. blocks in reverse: reload the block's checkpoint, recompute its 8 states and
 //      decays in registers, run the adjoint backwards through the block, then reduce
-//      through LDS: per (step, channel) the four waves' partial sums give dx, ddelta, dz;
+//      through LDS: per (step, channel) the eight waves' partial sums give dx, ddelta, dz;
 //      per (step, state) the 64 channels' terms give this workgroup's share of dB, dC.
-// A finishing kernel sums the shares of dB, dC over channel blocks and dA, dD over
-// batch rows.  The packed fp32 B/C rows of the forward's pre-pass (4 states per wave)
-// supply B_t, C_t as scalar operands.
+// The per-lane input rows (x, delta, dy, z) of the next block are loaded while the current
+// one is processed; the block's B_t, C_t rows go through LDS.  A finishing kernel sums the
+// shares of dB, dC over channel blocks and dA, dD over batch rows.
 #include "ssm_device.h"
+
+#include <type_traits>
 
 namespace ssm {
 namespace {
 
 constexpr int kN = 16;
-constexpr int kG = 4;       // states per lane
-constexpr int kW = 4;       // waves
-constexpr int kTB = 8;      // steps per block of the reverse sweep
-
-typedef const float __attribute__((address_space(4))) cfloat;
+constexpr int kG = 2;       // states per lane
+constexpr int kW = 8;       // waves
+constexpr int kTB = 8;      // steps per block
+constexpr int kThreads = kW * 64;
 
 __device__ __forceinline__ float sigmoid_f(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
+template <int P>
+using Set = std::integral_constant<int, P>;
+
 template <typename T, bool HAS_Z>
-__global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
-    // per wave, step, lane: partial sums over the wave's 4 states of
-    // (lam*A*a*h_prev, lam*B, C*h)
+__global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
+    // per wave, step, lane: partial sums over the wave's states of (lam*A*a*h_prev, lam*B, C*h)
     __shared__ float sS[kW][kTB][3][64];
     // per wave, step, (dB term, dC term), state, lane
     __shared__ float sG[kW][kTB][2][kG][64];
     // per step, lane: (dt, x, gy, z, raw delta) of the block, written by wave 0
     __shared__ float sV[kTB][5][64];
+    // the block's B_t, C_t: [step][state][B, C]; sweep 1 double-buffers B alone
+    __shared__ float sBC[kTB][kN][2];
+    __shared__ float sB1[2][kTB][kN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -60,10 +67,13 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
     const int64_t d = d0 + lane;
     const int n0 = w * kG;
     const int64_t nblk = a.nblk;
-    const T *X = static_cast<const T *>(a.x) + b * L * D + d;
-    const T *DL = static_cast<const T *>(a.delta) + b * L * D + d;
-    const T *Z = HAS_Z ? static_cast<const T *>(a.z) + b * L * D + d : nullptr;
-    const T *GY = static_cast<const T *>(a.dy) + b * L * D + d;
+    const int64_t base = b * L * D + d;
+    const T *X = static_cast<const T *>(a.x) + base;
+    const T *DL = static_cast<const T *>(a.delta) + base;
+    const T *Z = HAS_Z ? static_cast<const T *>(a.z) + base : nullptr;
+    const T *GY = static_cast<const T *>(a.dy) + base;
+    const T *Bm = static_cast<const T *>(a.Bm) + b * L * kN;
+    const T *Cm = static_cast<const T *>(a.Cm) + b * L * kN;
 
     float Av[kG], Al[kG];
 #pragma unroll
@@ -72,89 +82,134 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
         Al[g] = Av[g] * kLog2e;
     }
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
-    // packed B/C of this wave: [16-step block][2-step line][B: 2 x 4 | C: 2 x 4]
-    cfloat *bcw = reinterpret_cast<cfloat *>(reinterpret_cast<uintptr_t>(
-        a.ws_BC + (b * (a.bc_lpad / 16) * kW + w) * 128));
-    auto line = [&](int64_t t) { return bcw + (t >> 4) * (kW * 128) + ((t & 15) >> 1) * 16; };
-    auto delta_at = [&](int64_t t, float &raw) {
-        raw = widen(DL, t * D);
-        return a.softplus ? softplus_f(raw) : raw;
-    };
     float *ck = a.ckpt + ((b * nblk) * D + d) * kN + n0;   // block k at + k * D * kN
+    auto dt_of = [&](float raw) { return a.softplus ? softplus_f(raw) : raw; };
+    // rows of block k, clamped into the sequence (rows past its end are never used)
+    auto row = [&](int64_t k, int i) {
+        const int64_t t = k * kTB + i;
+        return (t < L ? t : L - 1) * D;
+    };
+    // element e of the block's B (e < 128) or C (e >= 128) rows, clamped likewise
+    const int e_i = (tid & 127) >> 4, e_n = tid & 15;
+    auto bc_elem = [&](int64_t k, const T *src) {
+        const int64_t t = k * kTB + e_i;
+        return widen(src, (t < L ? t : L - 1) * kN + e_n);
+    };
 
     // ---- sweep 1: forward, checkpoint at the start of every block
     float h[kG];
     {
-        float4 h4 = a.h0 ? *reinterpret_cast<const float4 *>(a.h0 + (b * D + d) * kN + n0)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        h[0] = h4.x; h[1] = h4.y; h[2] = h4.z; h[3] = h4.w;
+        float2 h2 = a.h0 ? *reinterpret_cast<const float2 *>(a.h0 + (b * D + d) * kN + n0) : make_float2(0.f, 0.f);
+        h[0] = h2.x; h[1] = h2.y;
     }
-    for (int64_t k = 0; k < nblk; ++k) {
-        *reinterpret_cast<float4 *>(ck + k * D * kN) = make_float4(h[0], h[1], h[2], h[3]);
-        const int64_t t0 = k * kTB;
-        const int nb = static_cast<int>(L - t0 < kTB ? L - t0 : kTB);
-        for (int i = 0; i < nb; ++i) {
-            const int64_t t = t0 + i;
-            float raw;
-            const float dt = delta_at(t, raw);
-            const float u = dt * widen(X, t * D);
-            cfloat *ln = line(t);
-            const int o = static_cast<int>(t & 1) * kG;
+    {
+        T rd1[2][kTB], rx1[2][kTB];   // [set][row]
+        float bnext = 0.0f;
+        auto load1 = [&](int64_t k, auto set) __attribute__((always_inline)) {
+            constexpr int S = decltype(set)::value;
 #pragma unroll
-            for (int g = 0; g < kG; ++g)
-                h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * Al[g]), h[g], u * ln[o + g]);
+            for (int i = 0; i < kTB; ++i) {
+                rd1[S][i] = DL[row(k, i)];
+                rx1[S][i] = X[row(k, i)];
+            }
+        };
+        auto block1 = [&](int64_t k, auto set) __attribute__((always_inline)) {
+            constexpr int S = decltype(set)::value;   // register set of block k = LDS buffer of its B
+            // B of block k+1 into the other buffer; request block k+2's
+            if (tid < 128) sB1[1 - S][e_i][e_n] = bnext;
+            if (tid < 128 && k + 2 < nblk) bnext = bc_elem(k + 2, Bm);
+            if (k + 1 < nblk) load1(k + 1, Set<1 - S>{});
+            *reinterpret_cast<float2 *>(ck + k * D * kN) = make_float2(h[0], h[1]);
+            const int nb = static_cast<int>(L - k * kTB < kTB ? L - k * kTB : kTB);
+#pragma unroll
+            for (int i = 0; i < kTB; ++i) {
+                if (i < nb) {
+                    const float dt = dt_of(widen_v(rd1[S][i]));
+                    const float u = dt * widen_v(rx1[S][i]);
+#pragma unroll
+                    for (int g = 0; g < kG; ++g)
+                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * Al[g]), h[g], u * sB1[S][i][n0 + g]);
+                }
+            }
+            __syncthreads();
+        };
+        if (nblk > 0) {
+            if (tid < 128) sB1[0][e_i][e_n] = bc_elem(0, Bm);
+            if (tid < 128 && nblk > 1) bnext = bc_elem(1, Bm);
+            load1(0, Set<0>{});
         }
+        __syncthreads();
+        int64_t k = 0;
+        for (; k + 1 < nblk; k += 2) {
+            block1(k, Set<0>{});
+            block1(k + 1, Set<1>{});
+        }
+        if (k < nblk) block1(k, Set<0>{});
     }
 
     // ---- sweep 2: blocks in reverse
     float lam[kG], gA[kG];
     {
-        float4 l4 = a.dh_last ? *reinterpret_cast<const float4 *>(a.dh_last + (b * D + d) * kN + n0)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-        lam[0] = l4.x; lam[1] = l4.y; lam[2] = l4.z; lam[3] = l4.w;
+        float2 l2 = a.dh_last ? *reinterpret_cast<const float2 *>(a.dh_last + (b * D + d) * kN + n0)
+                              : make_float2(0.f, 0.f);
+        lam[0] = l2.x; lam[1] = l2.y;
     }
-#pragma unroll
-    for (int g = 0; g < kG; ++g) gA[g] = 0.0f;
-    float gDp = 0.0f;   // this thread's share of sum_t gy0 x for its channel
-    const int rs_i = tid >> 5;            // dB/dC reduction: step,
-    const int rs_which = (tid >> 4) & 1;  // term (0: dB, 1: dC),
-    const int rs_n = tid & 15;            // state
+    gA[0] = gA[1] = 0.0f;
+    float gDp = 0.0f;   // sum of gy0 x over this thread's steps (step w of every block)
     const int64_t ndb = D / 64;
-
-    for (int64_t k = nblk - 1; k >= 0; --k) {
+    T rd[2][kTB], rx[2][kTB], rg[2][kTB], rz[2][kTB];   // [set][row]
+    float bcn = 0.0f;                                    // next block's B or C element (tid < 256)
+    auto load2 = [&](int64_t k, auto set) __attribute__((always_inline)) {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int i = 0; i < kTB; ++i) {
+            const int64_t r = row(k, i);
+            rd[S][i] = DL[r];
+            rx[S][i] = X[r];
+            rg[S][i] = GY[r];
+            if constexpr (HAS_Z) rz[S][i] = Z[r];
+        }
+        if (tid < 256) bcn = bc_elem(k, tid < 128 ? Bm : Cm);
+    };
+    auto block2 = [&](int64_t k, auto set) __attribute__((always_inline)) {
+        constexpr int S = decltype(set)::value;
         const int64_t t0 = k * kTB;
         const int nb = static_cast<int>(L - t0 < kTB ? L - t0 : kTB);
+        if (tid < 256) sBC[e_i][e_n][tid >> 7] = bcn;
+        if (k > 0) load2(k - 1, Set<1 - S>{});
+        __syncthreads();
         float hs[kTB][kG], as[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
         {
-            const float4 c4 = *reinterpret_cast<const float4 *>(ck + k * D * kN);
-            h[0] = c4.x; h[1] = c4.y; h[2] = c4.z; h[3] = c4.w;
+            const float2 c2 = *reinterpret_cast<const float2 *>(ck + k * D * kN);
+            h[0] = c2.x; h[1] = c2.y;
         }
-#pragma unroll
-        for (int g = 0; g < kG; ++g) h_in[g] = h[g];   // the state before the block
+        h_in[0] = h[0];
+        h_in[1] = h[1];
         // recompute the block forward; keep states, decays and per-step scalars
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
             if (i < nb) {
-                const int64_t t = t0 + i;
-                float raw;
-                const float dt = delta_at(t, raw);
-                const float xv = widen(X, t * D);
+                const float raw = widen_v(rd[S][i]);
+                const float dt = dt_of(raw);
+                const float xv = widen_v(rx[S][i]);
                 const float u = dt * xv;
-                const float gy = widen(GY, t * D);
-                const float zv = HAS_Z ? widen(Z, t * D) : 0.0f;
+                const float gy = widen_v(rg[S][i]);
+                const float zv = HAS_Z ? widen_v(rz[S][i]) : 0.0f;
                 dts[i] = dt;
                 us[i] = u;
                 g0s[i] = HAS_Z ? gy * silu_f(zv) : gy;
-                cfloat *ln = line(t);
-                const int o = static_cast<int>(t & 1) * kG;
+                const float4 bc = *reinterpret_cast<const float4 *>(&sBC[i][n0][0]);   // B0 C0 B1 C1
                 float y0p = 0.0f;
-#pragma unroll
-                for (int g = 0; g < kG; ++g) {
-                    const float dA = __builtin_amdgcn_exp2f(dt * Al[g]);
-                    h[g] = __builtin_fmaf(dA, h[g], u * ln[o + g]);
-                    hs[i][g] = h[g];
-                    as[i][g] = dA;
-                    y0p = __builtin_fmaf(ln[2 * kG + o + g], h[g], y0p);
+                {
+                    const float dA0 = __builtin_amdgcn_exp2f(dt * Al[0]);
+                    h[0] = __builtin_fmaf(dA0, h[0], u * bc.x);
+                    hs[i][0] = h[0];
+                    as[i][0] = dA0;
+                    const float dA1 = __builtin_amdgcn_exp2f(dt * Al[1]);
+                    h[1] = __builtin_fmaf(dA1, h[1], u * bc.z);
+                    hs[i][1] = h[1];
+                    as[i][1] = dA1;
+                    y0p = __builtin_fmaf(bc.y, h[0], bc.w * h[1]);
                 }
                 sS[w][i][2][lane] = y0p;
                 if (w == 0) {
@@ -170,17 +225,15 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = kTB - 1; i >= 0; --i) {
             if (i < nb) {
-                const int64_t t = t0 + i;
-                cfloat *ln = line(t);
-                const int o = static_cast<int>(t & 1) * kG;
+                const float4 bc = *reinterpret_cast<const float4 *>(&sBC[i][n0][0]);
+                const float Bv[kG] = {bc.x, bc.z}, Cv[kG] = {bc.y, bc.w};
                 float S1 = 0.0f, S3 = 0.0f;
 #pragma unroll
                 for (int g = 0; g < kG; ++g) {
-                    const float Bv = ln[o + g], Cv = ln[2 * kG + o + g];
-                    lam[g] = __builtin_fmaf(Cv, g0s[i], lam[g]);
+                    lam[g] = __builtin_fmaf(Cv[g], g0s[i], lam[g]);
                     sG[w][i][1][g][lane] = g0s[i] * hs[i][g];
                     sG[w][i][0][g][lane] = lam[g] * us[i];
-                    S3 = __builtin_fmaf(lam[g], Bv, S3);
+                    S3 = __builtin_fmaf(lam[g], Bv[g], S3);
                     const float ah = as[i][g] * (i > 0 ? hs[i > 0 ? i - 1 : 0][g] : h_in[g]);   // a_t h_{t-1}
                     S1 = __builtin_fmaf(lam[g] * Av[g], ah, S1);
                     gA[g] = __builtin_fmaf(lam[g] * dts[i], ah, gA[g]);
@@ -191,10 +244,9 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
-        // per (step, channel): thread (w, lane) finishes steps w and w + 4 of its channel
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int i = w + 4 * j;
+        // per (step, channel): thread (w, lane) finishes step w of its channel
+        {
+            const int i = w;
             if (i < nb) {
                 const int64_t t = t0 + i;
                 float S1 = 0.0f, S3 = 0.0f, y0 = 0.0f;
@@ -209,10 +261,10 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
                 y0 = __builtin_fmaf(dsk, xv, y0);
                 float g0 = gy;
                 if constexpr (HAS_Z) {
-                    const float s = sigmoid_f(zv);
-                    g0 = gy * (zv * s);
+                    const float sg = sigmoid_f(zv);
+                    g0 = gy * (zv * sg);
                     put(static_cast<T *>(a.dz) + b * L * D, t * D + d,
-                        gy * y0 * (s * __builtin_fmaf(zv, 1.0f - s, 1.0f)));
+                        gy * y0 * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f)));
                 }
                 gDp = __builtin_fmaf(g0, xv, gDp);
                 float gdt = __builtin_fmaf(xv, S3, S1);
@@ -221,23 +273,34 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
                 put(static_cast<T *>(a.dx) + b * L * D, t * D + d, __builtin_fmaf(dt, S3, dsk * g0));
             }
         }
-        // per (step, state, term): sum over the 64 channels of this workgroup
-        if (rs_i < nb) {
-            const float *row = &sG[rs_n >> 2][rs_i][rs_which][rs_n & 3][0];
-            float s = 0.0f;
+        // per (step, state, term): sum over the 64 channels, two threads per sum
+        {
+            const int q = tid >> 1, half = tid & 1;
+            const int ri = q >> 5, which = (q >> 4) & 1, n = q & 15;
+            const float *rowp = &sG[n >> 1][ri][which][n & 1][half * 32];
+            float sacc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {   // staggered 16-byte chunks: fewer bank conflicts
-                const int c = ((j + tid) & 15) * 4;
-                const float4 v = *reinterpret_cast<const float4 *>(row + c);
-                s += (v.x + v.y) + (v.z + v.w);
+            for (int j = 0; j < 8; ++j) {   // staggered 16-byte chunks: fewer bank conflicts
+                const int c = ((j + q) & 7) * 4;
+                const float4 v = *reinterpret_cast<const float4 *>(rowp + c);
+                sacc += (v.x + v.y) + (v.z + v.w);
             }
-            a.partBC[(((static_cast<int64_t>(rs_which) * a.B + b) * ndb + blockIdx.x) * L + t0 + rs_i) * kN + rs_n] = s;
+            sacc += __shfl_xor(sacc, 1);
+            if (half == 0 && ri < nb)
+                a.partBC[(((static_cast<int64_t>(which) * a.B + b) * ndb + blockIdx.x) * L + t0 + ri) * kN + n] = sacc;
         }
         __syncthreads();
+    };
+    if (nblk > 0) load2(nblk - 1, Set<(1) & 1>{});
+    // block k uses register set (nblk - 1 - k) & 1 ^ 1, alternating from set 1
+    int64_t k = nblk - 1;
+    for (; k >= 1; k -= 2) {
+        block2(k, Set<1>{});
+        block2(k - 1, Set<0>{});
     }
-    if (a.dh0)
-        *reinterpret_cast<float4 *>(a.dh0 + (b * D + d) * kN + n0) = make_float4(lam[0], lam[1], lam[2], lam[3]);
-    *reinterpret_cast<float4 *>(a.partA + (b * D + d) * kN + n0) = make_float4(gA[0], gA[1], gA[2], gA[3]);
+    if (k == 0) block2(0, Set<1>{});
+    if (a.dh0) *reinterpret_cast<float2 *>(a.dh0 + (b * D + d) * kN + n0) = make_float2(lam[0], lam[1]);
+    *reinterpret_cast<float2 *>(a.partA + (b * D + d) * kN + n0) = make_float2(gA[0], gA[1]);
     a.partD[(b * kW + w) * D + d] = gDp;
 }
 
@@ -278,8 +341,8 @@ __global__ void __launch_bounds__(256) bwd_finish_ad_kernel(BwdArgs a) {
 template <typename T>
 hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B));
-    if (has_z) hipLaunchKernelGGL((scan_bwd_kernel<T, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<T, false>), grid, dim3(256), 0, s, a);
+    if (has_z) hipLaunchKernelGGL((scan_bwd_kernel<T, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<T, false>), grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nbc = 2 * a.B * a.L * kN;

@@ -175,29 +175,16 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         return SSM_OK;
     }
     char *ws = static_cast<char *>(workspace);
-    // packed B/C: the forward pre-pass with 4 states per wave, one chunk
-    ScanArgs pa;
-    pa.B = batch; pa.L = seqlen; pa.D = dim; pa.N = dstate;
-    pa.Bm = B; pa.Cm = C;
-    pa.chunk_len = seqlen; pa.n_chunks = 1;
-    pa.ws_BC = reinterpret_cast<float *>(ws + p.bc_off);
-    pa.bc_lpad = p.bc_lpad;
-    ScanPlan pp;
-    pp.G = 4;
     const bool bf16 = dtype == SSM_DTYPE_BF16;
-    e = launch_bc_pack(pa, pp, bf16, s);
-    if (e != hipSuccess) return hip_fail("B/C pack launch", e);
     BwdArgs a;
     a.B = batch; a.L = seqlen; a.D = dim;
-    a.x = x; a.delta = delta; a.z = z; a.dy = dy;
+    a.x = x; a.delta = delta; a.z = z; a.dy = dy; a.Bm = B; a.Cm = C;
     a.A = A; a.Dskip = Dskip; a.h0 = h0; a.dh_last = dh_last;
     a.dx = dx; a.ddelta = ddelta; a.dz = dz; a.dB = dB; a.dC = dC;
     a.dA = dA; a.dD = Dskip ? dD : nullptr; a.dh0 = dh0;
     a.softplus = delta_softplus;
     a.nblk = p.nblk;
-    a.bc_lpad = p.bc_lpad;
     a.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
-    a.ws_BC = pa.ws_BC;
     a.partBC = reinterpret_cast<float *>(ws + p.partBC_off);
     a.partA = reinterpret_cast<float *>(ws + p.partA_off);
     a.partD = reinterpret_cast<float *>(ws + p.partD_off);

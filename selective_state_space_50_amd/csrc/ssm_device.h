@@ -46,18 +46,16 @@ struct UpdArgs {
 
 struct BwdArgs {
     int64_t B, L, D;
-    const void *x, *delta, *z, *dy;
+    const void *x, *delta, *z, *dy, *Bm, *Cm;
     const float *A, *Dskip, *h0, *dh_last;
     void *dx, *ddelta, *dz, *dB, *dC;
     float *dA, *dD, *dh0;
     int softplus;
     int64_t nblk;         // 8-step blocks of the reverse sweep
-    int64_t bc_lpad;      // steps in the packed B/C rows
     float *ckpt;          // [B][nblk][D][16] state at the start of every block
-    float *ws_BC;         // packed fp32 B/C, 4 states per wave (the forward pre-pass layout)
     float *partBC;        // [2][B][D/64][L][16] per-workgroup shares of dB, dC
     float *partA;         // [B][D][16] per-batch-row shares of dA
-    float *partD;         // [B][4][D] per-(row, wave) shares of dD
+    float *partD;         // [B][8][D] per-(row, wave) shares of dD
 };
 
 __device__ __forceinline__ float widen(const uint16_t *p, int64_t i) {
@@ -103,7 +101,7 @@ hipError_t launch_scan_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, boo
 // Specialised path pre-pass: pack B/C rows into ws_BC.
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s);
-// Backward pass (dstate == 16, dim % 64 == 0); ws_BC must hold the packed B/C (G = 4).
+// Backward pass (dstate == 16, dim % 64 == 0).
 hipError_t launch_scan_bwd(const BwdArgs &a, bool bf16, bool has_z, hipStream_t s);
 
 }  // namespace ssm

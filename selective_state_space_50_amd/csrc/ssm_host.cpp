@@ -338,19 +338,16 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
     }
     BwdPlan p;
     p.nblk = ceil_div(seqlen, 8);
-    p.bc_lpad = ceil_div(seqlen, 16) * 16;
     const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen), D = static_cast<size_t>(dim);
     size_t ws = 0;
     p.ckpt_off = ws;
     ws = align_up(ws + B * static_cast<size_t>(p.nblk) * D * 16 * sizeof(float), kWsAlign);
-    p.bc_off = ws;
-    ws = align_up(ws + B * static_cast<size_t>(p.bc_lpad) * 16 * 2 * sizeof(float), kWsAlign);
     p.partBC_off = ws;
     ws = align_up(ws + 2 * B * (D / 64) * L * 16 * sizeof(float), kWsAlign);
     p.partA_off = ws;
     ws = align_up(ws + B * D * 16 * sizeof(float), kWsAlign);
     p.partD_off = ws;
-    ws = align_up(ws + B * 4 * D * sizeof(float), kWsAlign);
+    ws = align_up(ws + B * 8 * D * sizeof(float), kWsAlign);
     p.ws_bytes = (batch == 0 || seqlen == 0 || dim == 0) ? 0 : ws;
     *plan = p;
     return SSM_OK;

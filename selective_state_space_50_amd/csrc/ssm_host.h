@@ -54,12 +54,11 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
                        const void *C, const float *Dskip, const void *z, const void *y,
                        int delta_softplus);
 
-// Workspace of ssm_scan_bwd: state checkpoints, packed B/C, per-workgroup shares of
-// dB/dC, per-batch-row shares of dA/dD.
+// Workspace of ssm_scan_bwd: state checkpoints, per-workgroup shares of dB/dC,
+// per-batch-row shares of dA/dD.
 struct BwdPlan {
     int64_t nblk = 0;       // 8-step blocks of the reverse sweep
-    int64_t bc_lpad = 0;    // steps in the packed B/C rows (multiple of 16)
-    size_t ckpt_off = 0, bc_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0;
+    size_t ckpt_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0;
     size_t ws_bytes = 0;
 };
 
