@@ -18,7 +18,8 @@
 // Mapping: a workgroup = 64 channels (lanes) of one batch row; 8 waves, wave w holding
 // states 2w, 2w+1 of every channel (two waves per SIMD, so one can issue while the other
 // waits).  Two sweeps over the sequence:
-//   1. forward, storing the state at the start of every 8-step block (checkpoints);
+//   1. forward, storing the state at the start of every 8-step block (checkpoints): the
+//      specialised forward kernel in its checkpoint mode, launched before this kernel;
 //   2. blocks in reverse: reload the block's checkpoint, recompute its 8 states and
 //      decays in registers, run the adjoint backwards through the block, then reduce
 //      through LDS: per (step, channel) the eight waves' partial sums give dx, ddelta, dz;
@@ -43,9 +44,6 @@ __device__ __forceinline__ float sigmoid_f(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
-template <int P>
-using Set = std::integral_constant<int, P>;
-
 template <typename T, bool HAS_Z>
 __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     // per wave, step, lane: partial sums over the wave's states of (lam*A*a*h_prev, lam*B, C*h)
@@ -54,9 +52,8 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     __shared__ float sG[kW][kTB][2][kG][64];
     // per step, lane: (dt, x, gy, z, raw delta) of the block, written by wave 0
     __shared__ float sV[kTB][5][64];
-    // the block's B_t, C_t: [step][state][B, C]; sweep 1 double-buffers B alone
+    // the block's B_t, C_t: [step][state][B, C]
     __shared__ float sBC[kTB][kN][2];
-    __shared__ float sB1[2][kTB][kN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -96,58 +93,9 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         return widen(src, (t < L ? t : L - 1) * kN + e_n);
     };
 
-    // ---- sweep 1: forward, checkpoint at the start of every block
     float h[kG];
-    {
-        float2 h2 = a.h0 ? *reinterpret_cast<const float2 *>(a.h0 + (b * D + d) * kN + n0) : make_float2(0.f, 0.f);
-        h[0] = h2.x; h[1] = h2.y;
-    }
-    {
-        T rd1[2][kTB], rx1[2][kTB];   // [set][row]
-        float bnext = 0.0f;
-        auto load1 = [&](int64_t k, auto set) __attribute__((always_inline)) {
-            constexpr int S = decltype(set)::value;
-#pragma unroll
-            for (int i = 0; i < kTB; ++i) {
-                rd1[S][i] = DL[row(k, i)];
-                rx1[S][i] = X[row(k, i)];
-            }
-        };
-        auto block1 = [&](int64_t k, auto set) __attribute__((always_inline)) {
-            constexpr int S = decltype(set)::value;   // register set of block k = LDS buffer of its B
-            // B of block k+1 into the other buffer; request block k+2's
-            if (tid < 128) sB1[1 - S][e_i][e_n] = bnext;
-            if (tid < 128 && k + 2 < nblk) bnext = bc_elem(k + 2, Bm);
-            if (k + 1 < nblk) load1(k + 1, Set<1 - S>{});
-            *reinterpret_cast<float2 *>(ck + k * D * kN) = make_float2(h[0], h[1]);
-            const int nb = static_cast<int>(L - k * kTB < kTB ? L - k * kTB : kTB);
-#pragma unroll
-            for (int i = 0; i < kTB; ++i) {
-                if (i < nb) {
-                    const float dt = dt_of(widen_v(rd1[S][i]));
-                    const float u = dt * widen_v(rx1[S][i]);
-#pragma unroll
-                    for (int g = 0; g < kG; ++g)
-                        h[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * Al[g]), h[g], u * sB1[S][i][n0 + g]);
-                }
-            }
-            __syncthreads();
-        };
-        if (nblk > 0) {
-            if (tid < 128) sB1[0][e_i][e_n] = bc_elem(0, Bm);
-            if (tid < 128 && nblk > 1) bnext = bc_elem(1, Bm);
-            load1(0, Set<0>{});
-        }
-        __syncthreads();
-        int64_t k = 0;
-        for (; k + 1 < nblk; k += 2) {
-            block1(k, Set<0>{});
-            block1(k + 1, Set<1>{});
-        }
-        if (k < nblk) block1(k, Set<0>{});
-    }
 
-    // ---- sweep 2: blocks in reverse
+    // ---- blocks in reverse (the checkpoints come from the forward kernel's checkpoint pass)
     float lam[kG], gA[kG];
     {
         float2 l2 = a.dh_last ? *reinterpret_cast<const float2 *>(a.dh_last + (b * D + d) * kN + n0)
@@ -157,26 +105,26 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     gA[0] = gA[1] = 0.0f;
     float gDp = 0.0f;   // sum of gy0 x over this thread's steps (step w of every block)
     const int64_t ndb = D / 64;
-    T rd[2][kTB], rx[2][kTB], rg[2][kTB], rz[2][kTB];   // [set][row]
-    float bcn = 0.0f;                                    // next block's B or C element (tid < 256)
-    auto load2 = [&](int64_t k, auto set) __attribute__((always_inline)) {
-        constexpr int S = decltype(set)::value;
+    // raw rows of one block; the next block's are requested once the current block's
+    // forward recompute has consumed them, so they arrive during its adjoint and reductions
+    T rd[kTB], rx[kTB], rg[kTB], rz[kTB];
+    float bcn = 0.0f;                     // next block's B or C element (tid < 256)
+    auto load2 = [&](int64_t k) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
             const int64_t r = row(k, i);
-            rd[S][i] = DL[r];
-            rx[S][i] = X[r];
-            rg[S][i] = GY[r];
-            if constexpr (HAS_Z) rz[S][i] = Z[r];
+            rd[i] = DL[r];
+            rx[i] = X[r];
+            rg[i] = GY[r];
+            if constexpr (HAS_Z) rz[i] = Z[r];
         }
         if (tid < 256) bcn = bc_elem(k, tid < 128 ? Bm : Cm);
     };
-    auto block2 = [&](int64_t k, auto set) __attribute__((always_inline)) {
-        constexpr int S = decltype(set)::value;
+    auto block2 = [&](int64_t k, auto full) __attribute__((always_inline)) {
+        constexpr bool F = decltype(full)::value;
         const int64_t t0 = k * kTB;
-        const int nb = static_cast<int>(L - t0 < kTB ? L - t0 : kTB);
+        const int nb = F ? kTB : static_cast<int>(L - t0);
         if (tid < 256) sBC[e_i][e_n][tid >> 7] = bcn;
-        if (k > 0) load2(k - 1, Set<1 - S>{});
         __syncthreads();
         float hs[kTB][kG], as[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
         {
@@ -185,20 +133,23 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         }
         h_in[0] = h[0];
         h_in[1] = h[1];
+        float4 bcs[kTB];   // (B0, C0, B1, C1) of this wave's states, every step of the block
+#pragma unroll
+        for (int i = 0; i < kTB; ++i) bcs[i] = *reinterpret_cast<const float4 *>(&sBC[i][n0][0]);
         // recompute the block forward; keep states, decays and per-step scalars
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
-            if (i < nb) {
-                const float raw = widen_v(rd[S][i]);
+            if (F || i < nb) {
+                const float raw = widen_v(rd[i]);
                 const float dt = dt_of(raw);
-                const float xv = widen_v(rx[S][i]);
+                const float xv = widen_v(rx[i]);
                 const float u = dt * xv;
-                const float gy = widen_v(rg[S][i]);
-                const float zv = HAS_Z ? widen_v(rz[S][i]) : 0.0f;
+                const float gy = widen_v(rg[i]);
+                const float zv = HAS_Z ? widen_v(rz[i]) : 0.0f;
                 dts[i] = dt;
                 us[i] = u;
                 g0s[i] = HAS_Z ? gy * silu_f(zv) : gy;
-                const float4 bc = *reinterpret_cast<const float4 *>(&sBC[i][n0][0]);   // B0 C0 B1 C1
+                const float4 bc = bcs[i];
                 float y0p = 0.0f;
                 {
                     const float dA0 = __builtin_amdgcn_exp2f(dt * Al[0]);
@@ -221,11 +172,12 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 }
             }
         }
+        if (k > 0) load2(k - 1);
         // adjoint, backwards through the block
 #pragma unroll
         for (int i = kTB - 1; i >= 0; --i) {
-            if (i < nb) {
-                const float4 bc = *reinterpret_cast<const float4 *>(&sBC[i][n0][0]);
+            if (F || i < nb) {
+                const float4 bc = bcs[i];
                 const float Bv[kG] = {bc.x, bc.z}, Cv[kG] = {bc.y, bc.w};
                 float S1 = 0.0f, S3 = 0.0f;
 #pragma unroll
@@ -291,14 +243,10 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         }
         __syncthreads();
     };
-    if (nblk > 0) load2(nblk - 1, Set<(1) & 1>{});
-    // block k uses register set (nblk - 1 - k) & 1 ^ 1, alternating from set 1
-    int64_t k = nblk - 1;
-    for (; k >= 1; k -= 2) {
-        block2(k, Set<1>{});
-        block2(k - 1, Set<0>{});
-    }
-    if (k == 0) block2(0, Set<1>{});
+    if (nblk > 0) load2(nblk - 1);
+    if (nblk > 0 && (nblk - 1) * kTB + kTB > L) block2(nblk - 1, std::false_type{});
+    else if (nblk > 0) block2(nblk - 1, std::true_type{});
+    for (int64_t k = nblk - 2; k >= 0; --k) block2(k, std::true_type{});   // every earlier block is full
     if (a.dh0) *reinterpret_cast<float2 *>(a.dh0 + (b * D + d) * kN + n0) = make_float2(lam[0], lam[1]);
     *reinterpret_cast<float2 *>(a.partA + (b * D + d) * kN + n0) = make_float2(gA[0], gA[1]);
     a.partD[(b * kW + w) * D + d] = gDp;

@@ -118,7 +118,9 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
     o[SUB * G] = cv;
 }
 
-template <typename T, int G, bool HAS_Z, bool CARRY>
+// CARRY: no y; store the chunk's delta sum and end state (chunk carries), or with CKPT
+// the state at the start of every 8-step group instead (checkpoints for the backward).
+template <typename T, int G, bool HAS_Z, bool CARRY, bool CKPT = false>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
     constexpr int NC = kN / G;          // compute waves
     constexpr int RPT = 2;              // rows per helper thread
@@ -290,6 +292,16 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             // single wave.
             if ((((sb * 2) / NSUB + (w >> 2)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
+            if constexpr (CKPT) {
+                if ((sb * SUB) % 8 == 0) {   // state before step t, t a multiple of 8
+                    const int64_t t = t0 + k * kTB + sb * SUB;
+                    if (t < t1) {
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            a.ckpt[((b * a.ck_nblk + t / 8) * D + d) * kN + n0 + g] = h[g];
+                    }
+                }
+            }
             if (sb + 1 < NSUB) {
 #pragma unroll
                 for (int q = 0; q < SUB / 2; ++q) du_n[q] = sDU[P][((sb + 1) * SUB / 2 + q) * 64 + lane];
@@ -358,7 +370,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         for (int g = 0; g < G; ++g) {
             Al[g] = a.A[d * kN + n0 + g] * kLog2e;
             float hv = 0.0f;
-            if (!CARRY) {
+            if (!CARRY || CKPT) {   // carries start from zero; checkpoints from h0
                 if (c == 0) {
                     if (a.h0) hv = a.h0[(b * D + d) * kN + n0 + g];
                 } else {
@@ -379,7 +391,8 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             compute_block(k, Par<0>{});
             __syncthreads();
         }
-        if constexpr (CARRY) {
+        if constexpr (CKPT) {
+        } else if constexpr (CARRY) {
             const int64_t slot = b * (a.n_chunks - 1) + c;
             if (w == 0) a.ws_S[slot * D + d] = dsum;
 #pragma unroll
@@ -482,6 +495,13 @@ hipError_t launch_t(const ScanArgs &a, dim3 grid, bool has_z, bool carry, size_t
     return hipGetLastError();
 }
 
+template <typename T, int G>
+hipError_t launch_ckpt_t(const ScanArgs &a, dim3 grid, size_t lds_reserve, hipStream_t s) {
+    hipLaunchKernelGGL((scan_fast_kernel<T, G, false, true, true>), grid, dim3(64 * waves_per_block<G>()),
+                       lds_reserve, s, a);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_dt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool has_z, bool carry,
                      hipStream_t s) {
@@ -502,6 +522,13 @@ hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipSt
         else hipLaunchKernelGGL((bc_pack_kernel<float, 4>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s) {
+    // one workgroup per CU when the grid allows (the carry kernel's static LDS is 16 KiB)
+    const size_t reserve = p.blocks <= static_cast<uint64_t>(kCUs) ? kLdsPerCU / 2 + 1024 - 16 * 1024 : 0;
+    if (bf16) return p.G == 2 ? launch_ckpt_t<uint16_t, 2>(a, grid, reserve, s) : launch_ckpt_t<uint16_t, 4>(a, grid, reserve, s);
+    return p.G == 2 ? launch_ckpt_t<float, 2>(a, grid, reserve, s) : launch_ckpt_t<float, 4>(a, grid, reserve, s);
 }
 
 hipError_t launch_scan_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z,

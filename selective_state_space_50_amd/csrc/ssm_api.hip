@@ -176,6 +176,29 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     }
     char *ws = static_cast<char *>(workspace);
     const bool bf16 = dtype == SSM_DTYPE_BF16;
+    // 1) checkpoints: the specialised forward kernel over the whole sequence, storing the
+    //    state before every 8th step (B/C packed first, as for the forward)
+    {
+        ScanArgs fa;
+        fa.B = batch; fa.L = seqlen; fa.D = dim; fa.N = dstate;
+        fa.x = x; fa.delta = delta; fa.z = nullptr; fa.Bm = B; fa.Cm = C;
+        fa.A = A; fa.Dskip = nullptr; fa.h0 = h0; fa.h_last = nullptr; fa.y = nullptr;
+        fa.softplus = delta_softplus;
+        fa.NW = p.fwd.NW;
+        fa.chunk_len = p.fwd.chunk_len;
+        fa.n_chunks = 1;
+        fa.ws_S = nullptr; fa.ws_H = nullptr;
+        fa.ws_BC = reinterpret_cast<float *>(ws + p.bc_off);
+        fa.bc_lpad = p.fwd.bc_lpad;
+        fa.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
+        fa.ck_nblk = p.nblk;
+        e = launch_bc_pack(fa, p.fwd, bf16, s);
+        if (e != hipSuccess) return hip_fail("B/C pack launch", e);
+        const unsigned dblocks = static_cast<unsigned>(dim / 64);
+        e = launch_scan_ckpt(fa, dim3(dblocks, static_cast<unsigned>(batch), 1), p.fwd, bf16, s);
+        if (e != hipSuccess) return hip_fail("checkpoint pass launch", e);
+    }
+    // 2) the reverse sweep and the reductions
     BwdArgs a;
     a.B = batch; a.L = seqlen; a.D = dim;
     a.x = x; a.delta = delta; a.z = z; a.dy = dy; a.Bm = B; a.Cm = C;

@@ -32,6 +32,8 @@ struct ScanArgs {
     float *ws_H;          // [B][n_chunks-1][D][N]  chunk end state, then carried-in state
     float *ws_BC;         // specialised kernel: packed fp32 B/C, 64-byte line per wave and sub-block
     int64_t bc_lpad;
+    float *ckpt = nullptr;   // checkpoint pass: [B][ck_nblk][D][N] state before every 8th step
+    int64_t ck_nblk = 0;
 };
 
 struct UpdArgs {
@@ -98,6 +100,8 @@ hipError_t launch_scan_generic(const ScanArgs &a, dim3 grid, const ScanPlan &p, 
 // Specialised path (plan.fast): dstate == 16, dim % 64 == 0, states_per_lane 2 or 4.
 hipError_t launch_scan_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16,
                             bool has_z, bool carry, hipStream_t s);
+// Specialised kernel, checkpoint pass (one chunk): the state before every 8th step into ckpt.
+hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s);
 // Specialised path pre-pass: pack B/C rows into ws_BC.
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s);

@@ -338,10 +338,21 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
     }
     BwdPlan p;
     p.nblk = ceil_div(seqlen, 8);
+    if (seqlen > 0) {
+        ssm_scan_opts one = {seqlen, 0, 0, 0, 0};   // the whole sequence as one chunk
+        st = plan_scan(batch, seqlen, dim, dstate, dtype, &one, &p.fwd);
+        if (st != SSM_OK) return st;
+        if (!p.fwd.fast || p.fwd.n_chunks != 1) {
+            set_error("ssm_scan_bwd: no single-pass plan for this shape");
+            return SSM_EUNSUPPORTED;
+        }
+    }
     const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen), D = static_cast<size_t>(dim);
     size_t ws = 0;
     p.ckpt_off = ws;
     ws = align_up(ws + B * static_cast<size_t>(p.nblk) * D * 16 * sizeof(float), kWsAlign);
+    p.bc_off = ws;
+    ws = align_up(ws + B * static_cast<size_t>(p.fwd.bc_lpad) * 16 * 2 * sizeof(float), kWsAlign);
     p.partBC_off = ws;
     ws = align_up(ws + 2 * B * (D / 64) * L * 16 * sizeof(float), kWsAlign);
     p.partA_off = ws;

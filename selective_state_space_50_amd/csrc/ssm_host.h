@@ -54,11 +54,12 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
                        const void *C, const float *Dskip, const void *z, const void *y,
                        int delta_softplus);
 
-// Workspace of ssm_scan_bwd: state checkpoints, per-workgroup shares of dB/dC,
-// per-batch-row shares of dA/dD.
+// Workspace of ssm_scan_bwd: packed B/C and state checkpoints of the forward
+// checkpoint pass, per-workgroup shares of dB/dC, per-batch-row shares of dA/dD.
 struct BwdPlan {
     int64_t nblk = 0;       // 8-step blocks of the reverse sweep
-    size_t ckpt_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0;
+    ScanPlan fwd;           // the checkpoint pass: the specialised forward kernel, one chunk
+    size_t ckpt_off = 0, bc_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0;
     size_t ws_bytes = 0;
 };
 
