@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         Al[g] = Av[g] * kLog2e;
     }
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
-    float *ck = a.ckpt + ((b * nblk) * D + d) * kN + n0;   // block k at + k * D * kN
+    const float *ck = a.ckpt + (b * nblk * kN + n0) * D + d;   // block k, state n0 + g at + (k * kN + g) * D
     auto dt_of = [&](float raw) { return a.softplus ? softplus_f(raw) : raw; };
     // rows of block k, clamped into the sequence (rows past its end are never used)
     auto row = [&](int64_t k, int i) {
@@ -109,7 +109,9 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     // forward recompute has consumed them, so they arrive during its adjoint and reductions
     T rd[kTB], rx[kTB], rg[kTB], rz[kTB];
     float bcn = 0.0f;                     // next block's B or C element (tid < 256)
+    float2 ckn;                           // next block's checkpoint
     auto load2 = [&](int64_t k) __attribute__((always_inline)) {
+        ckn = make_float2(ck[k * kN * D], ck[(k * kN + 1) * D]);
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
             const int64_t r = row(k, i);
@@ -127,10 +129,8 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         if (tid < 256) sBC[e_i][e_n][tid >> 7] = bcn;
         __syncthreads();
         float hs[kTB][kG], as[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
-        {
-            const float2 c2 = *reinterpret_cast<const float2 *>(ck + k * D * kN);
-            h[0] = c2.x; h[1] = c2.y;
-        }
+        h[0] = ckn.x;
+        h[1] = ckn.y;
         h_in[0] = h[0];
         h_in[1] = h[1];
         float4 bcs[kTB];   // (B0, C0, B1, C1) of this wave's states, every step of the block

@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                     if (t < t1) {
 #pragma unroll
                         for (int g = 0; g < G; ++g)
-                            a.ckpt[((b * a.ck_nblk + t / 8) * D + d) * kN + n0 + g] = h[g];
+                            a.ckpt[((b * a.ck_nblk + t / 8) * kN + n0 + g) * D + d] = h[g];
                     }
                 }
             }

@@ -32,7 +32,7 @@ struct ScanArgs {
     float *ws_H;          // [B][n_chunks-1][D][N]  chunk end state, then carried-in state
     float *ws_BC;         // specialised kernel: packed fp32 B/C, 64-byte line per wave and sub-block
     int64_t bc_lpad;
-    float *ckpt = nullptr;   // checkpoint pass: [B][ck_nblk][D][N] state before every 8th step
+    float *ckpt = nullptr;   // checkpoint pass: [B][ck_nblk][N][D] state before every 8th step
     int64_t ck_nblk = 0;
 };
 
@@ -54,7 +54,7 @@ struct BwdArgs {
     float *dA, *dD, *dh0;
     int softplus;
     int64_t nblk;         // 8-step blocks of the reverse sweep
-    float *ckpt;          // [B][nblk][D][16] state at the start of every block
+    float *ckpt;          // [B][nblk][16][D] state at the start of every block
     float *partBC;        // [2][B][D/64][L][16] per-workgroup shares of dB, dC
     float *partA;         // [B][D][16] per-batch-row shares of dA
     float *partD;         // [B][8][D] per-(row, wave) shares of dD
