@@ -207,6 +207,39 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Causal depthwise convolution along the sequence, then SiLU: the step before the scan
+ * in a Mamba block (skill page "State Space Models Mamba", MambaBlock listing: Conv1d
+ * with kernel size d_conv, padding d_conv - 1 and one group per channel, its output cut
+ * to the sequence length, then silu).  With W = width and xp the W - 1 inputs before
+ * the sequence (state_in, or zeros) followed by x:
+ *     y[b,t,d] = silu(bias[d] + sum_{k<W} w[d,k] * xp[b, t+k, d])     (silu = 1)
+ *     y[b,t,d] =      bias[d] + sum_{k<W} w[d,k] * xp[b, t+k, d]      (silu = 0)
+ *     state_out[b,d,:] = the last W - 1 values of xp[b, :, d]   (oldest first)
+ *
+ *   x         [batch, seqlen, dim]   dtype   required when seqlen > 0
+ *   w         [dim, width]           fp32    required
+ *   bias      [dim]                  fp32    NULL = no bias
+ *   state_in  [batch, dim, width-1]  dtype   NULL = zeros before the sequence
+ *   y         [batch, seqlen, dim]   dtype   output; must not overlap an input
+ *   state_out [batch, dim, width-1]  dtype   NULL = not stored; must not overlap an input
+ * 1 <= width <= 4 (SSM_EUNSUPPORTED above).  batch or dim == 0 is a no-op; seqlen == 0
+ * only passes state_in (or zeros) to state_out.
+ */
+int ssm_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                   const void *x, const float *w, const float *bias, const void *state_in,
+                   void *y, void *state_out, int silu, void *stream);
+
+/*
+ * One token of ssm_conv1d_fwd (generation form): state [batch, dim, width-1] (dtype,
+ * oldest input first) is read and updated in place, x and y are [batch, dim].
+ * L consecutive calls give the same y and final state as one ssm_conv1d_fwd over those
+ * L tokens.
+ */
+int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, void *state,
+                      const void *x, const float *w, const float *bias, void *y, int silu,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,8 @@ import os
 import re
 
 __all__ = ["scan_fwd", "scan_bwd", "state_update", "scan_plan", "scan_workspace_bytes",
-           "scan_bwd_workspace_bytes", "selective_scan", "lib", "SSMError", "LIB_PATH",
+           "scan_bwd_workspace_bytes", "selective_scan", "conv1d_fwd", "conv1d_update", "lib",
+           "SSMError", "LIB_PATH",
            "HEADER_PATH", "exported_api"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +79,10 @@ def lib():
     L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
     L.ssm_scan_bwd.restype = I32
     L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, P, SZ, P]
+    L.ssm_conv1d_fwd.restype = I32
+    L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
+    L.ssm_conv1d_update.restype = I32
+    L.ssm_conv1d_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, I32, P]
     if L.ssm_abi_version() != 1:
         raise ImportError(f"libssm ABI version {L.ssm_abi_version()} != 1")
     _lib = L
@@ -306,3 +311,54 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=Fa
             return g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"]
 
     return _Scan.apply(x, delta, A, B, C, D, z, h0)
+
+
+def conv1d_fwd(x, w, bias=None, state=None, *, silu=True, return_state=False, out=None, stream=None):
+    """Causal depthwise convolution along the sequence (+ SiLU): x [B, L, D] (bf16 or
+    fp32), w [D, W] fp32 (W <= 4), bias [D] fp32, state [B, D, W-1] in x's dtype (the
+    inputs before the sequence).  Returns y (and the final state when return_state)."""
+    import torch
+    if x.dim() != 3 or w.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, dim] and w [dim, width]")
+    Bsz, L, Dm = x.shape
+    W = w.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_fwd runs on the GPU only; tensors must be on a cuda device")
+    _need(w, "w", (Dm, W), torch.float32, dev)
+    _need(bias, "bias", (Dm,), torch.float32, dev)
+    _need(state, "state", (Bsz, Dm, W - 1), x.dtype, dev)
+    _need(x, "x", (Bsz, L, Dm), x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, L, Dm), x.dtype, dev)
+    st_out = torch.empty((Bsz, Dm, W - 1), dtype=x.dtype, device=dev) if return_state else None
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(lib().ssm_conv1d_fwd(Bsz, L, Dm, W, _dtype_code(x), _ptr(x), _ptr(w), _ptr(bias), _ptr(state),
+                                _ptr(out), _ptr(st_out), int(bool(silu)), ctypes.c_void_p(s.cuda_stream)),
+           "ssm_conv1d_fwd")
+    return (out, st_out) if return_state else out
+
+
+def conv1d_update(state, x, w, bias=None, *, silu=True, out=None, stream=None):
+    """One token of conv1d_fwd: state [B, D, W-1] (x's dtype) updated in place, x [B, D];
+    returns y [B, D]."""
+    import torch
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [batch, dim] and w [dim, width]")
+    Bsz, Dm = x.shape
+    W = w.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_update runs on the GPU only; tensors must be on a cuda device")
+    _need(w, "w", (Dm, W), torch.float32, dev)
+    _need(bias, "bias", (Dm,), torch.float32, dev)
+    _need(state, "state", (Bsz, Dm, W - 1), x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, Dm), x.dtype, dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(lib().ssm_conv1d_update(Bsz, Dm, W, _dtype_code(x), _ptr(state), _ptr(x), _ptr(w), _ptr(bias),
+                                   _ptr(out), int(bool(silu)), ctypes.c_void_p(s.cuda_stream)),
+           "ssm_conv1d_update")
+    return out

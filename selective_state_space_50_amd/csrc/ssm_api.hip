@@ -214,3 +214,35 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     e = launch_scan_bwd(a, bf16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
 }
+
+extern "C" int ssm_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                              const void *x, const float *w, const float *bias, const void *state_in,
+                              void *y, void *state_out, int silu, void *stream) {
+    using namespace ssm;
+    clear_error();
+    int st = check_conv1d_fwd(batch, seqlen, dim, width, dtype, x, w, bias, state_in, y, state_out, silu);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0 || (seqlen == 0 && (!state_out || width == 1))) return SSM_OK;
+    ConvArgs a;
+    a.B = batch; a.L = seqlen; a.D = dim; a.W = static_cast<int>(width);
+    a.x = x; a.w = w; a.bias = bias; a.state_in = state_in; a.y = y; a.state_out = state_out; a.silu = silu;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // (with seqlen == 0 only the state passes through)
+    hipError_t e = launch_conv1d_fwd(a, dtype == SSM_DTYPE_BF16, s);
+    return e == hipSuccess ? SSM_OK : hip_fail("conv1d launch", e);
+}
+
+extern "C" int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, void *state,
+                                 const void *x, const float *w, const float *bias, void *y, int silu,
+                                 void *stream) {
+    using namespace ssm;
+    clear_error();
+    int st = check_conv1d_update(batch, dim, width, dtype, state, x, w, bias, y, silu);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    ConvArgs a;
+    a.B = batch; a.L = 1; a.D = dim; a.W = static_cast<int>(width);
+    a.x = x; a.w = w; a.bias = bias; a.state_in = nullptr; a.y = y; a.state_out = state; a.silu = silu;
+    hipError_t e = launch_conv1d_update(a, dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : hip_fail("conv1d update launch", e);
+}

@@ -60,6 +60,17 @@ struct BwdArgs {
     float *partD;         // [B][8][D] per-(row, wave) shares of dD
 };
 
+struct ConvArgs {
+    int64_t B, L, D;
+    int W;                   // filter width (1..4)
+    const void *x;           // [B, L, D] (update: [B, D])
+    const float *w, *bias;   // [D, W], [D] or null
+    const void *state_in;    // [B, D, W-1] or null (forward)
+    void *y;                 // [B, L, D] (update: [B, D])
+    void *state_out;         // [B, D, W-1] or null (forward); the state, in place (update)
+    int silu;
+};
+
 __device__ __forceinline__ float widen(const uint16_t *p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
@@ -105,6 +116,9 @@ hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, boo
 // Specialised path pre-pass: pack B/C rows into ws_BC.
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s);
+// Causal depthwise convolution (+ SiLU): sequence form and single-token form.
+hipError_t launch_conv1d_fwd(const ConvArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_conv1d_update(const ConvArgs &a, bool bf16, hipStream_t s);
 // Backward pass (dstate == 16, dim % 64 == 0).
 hipError_t launch_scan_bwd(const BwdArgs &a, bool bf16, bool has_z, hipStream_t s);
 

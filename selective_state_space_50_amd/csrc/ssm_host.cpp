@@ -412,6 +412,77 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
     return SSM_OK;
 }
 
+namespace {
+int check_conv_common(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype, int silu) {
+    if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16) {
+        set_error("dtype=%d is neither SSM_DTYPE_F32 nor SSM_DTYPE_BF16", dtype);
+        return SSM_EINVAL;
+    }
+    if (batch < 0 || seqlen < 0 || dim < 0) {
+        set_error("negative size (batch=%lld, seqlen=%lld, dim=%lld)", (long long)batch, (long long)seqlen,
+                  (long long)dim);
+        return SSM_EINVAL;
+    }
+    if (width < 1) {
+        set_error("width=%lld must be at least 1", (long long)width);
+        return SSM_EINVAL;
+    }
+    if (width > 4) {
+        set_error("width=%lld: at most 4 is supported", (long long)width);
+        return SSM_EUNSUPPORTED;
+    }
+    if (silu != 0 && silu != 1) {
+        set_error("silu=%d is neither 0 nor 1", silu);
+        return SSM_EINVAL;
+    }
+    if (batch > 65535 || (seqlen + 31) / 32 > 65535 || (batch > 0 && dim > (int64_t(1) << 40) / (batch * (seqlen + 4)))) {
+        set_error("shape too large for one launch (batch=%lld, seqlen=%lld, dim=%lld)", (long long)batch,
+                  (long long)seqlen, (long long)dim);
+        return SSM_EUNSUPPORTED;
+    }
+    return SSM_OK;
+}
+}  // namespace
+
+int check_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                     const void *x, const float *w, const float *bias, const void *state_in,
+                     const void *y, const void *state_out, int silu) {
+    int st = check_conv_common(batch, seqlen, dim, width, dtype, silu);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    const char *missing = !w ? "w" : (seqlen > 0 && !x) ? "x" : (seqlen > 0 && !y) ? "y" : nullptr;
+    if (missing) {
+        set_error("required pointer %s is NULL", missing);
+        return SSM_EINVAL;
+    }
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    const int64_t tok = batch * seqlen * dim * es;
+    const int64_t stb = batch * dim * (width - 1) * es;
+    Range all[] = {range("x", x, tok), range("w", w, dim * width * 4), range("bias", bias, dim * 4),
+                   range("state_in", state_in, stb), range("y", y, tok), range("state_out", state_out, stb)};
+    st = check_aligned(all, 6);
+    if (st != SSM_OK) return st;
+    return check_no_overlap(all + 4, 2, all, 6);
+}
+
+int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, const void *state,
+                        const void *x, const float *w, const float *bias, const void *y, int silu) {
+    int st = check_conv_common(batch, 1, dim, width, dtype, silu);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    const char *missing = !w ? "w" : !x ? "x" : !y ? "y" : (width > 1 && !state) ? "state" : nullptr;
+    if (missing) {
+        set_error("required pointer %s is NULL", missing);
+        return SSM_EINVAL;
+    }
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    Range all[] = {range("x", x, batch * dim * es), range("w", w, dim * width * 4), range("bias", bias, dim * 4),
+                   range("state", state, batch * dim * (width - 1) * es), range("y", y, batch * dim * es)};
+    st = check_aligned(all, 5);
+    if (st != SSM_OK) return st;
+    return check_no_overlap(all + 3, 2, all, 5);
+}
+
 }  // namespace ssm
 
 extern "C" {

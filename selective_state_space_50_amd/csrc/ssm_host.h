@@ -74,6 +74,13 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
                    int delta_softplus, const void *workspace, size_t workspace_bytes, BwdPlan *plan);
 
+// Argument checks of the convolution entry points.
+int check_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                     const void *x, const float *w, const float *bias, const void *state_in,
+                     const void *y, const void *state_out, int silu);
+int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, const void *state,
+                        const void *x, const float *w, const float *bias, const void *y, int silu);
+
 inline size_t dtype_size(int dtype) { return dtype == SSM_DTYPE_BF16 ? 2 : 4; }
 
 }  // namespace ssm
