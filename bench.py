@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--secondary-only", action="store_true")
     ap.add_argument("--profile-decode", type=int, default=0, metavar="STEPS",
                     help="only run this many decode steps of h[256,4096,16] (for rocprofv3)")
+    ap.add_argument("--profile-conv", type=int, default=0, metavar="CALLS",
+                    help="only run this many conv1d calls at the headline shape (for rocprofv3)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -123,6 +125,13 @@ def main():
     if args.profile_decode:
         profile_decode(torch, ssm, synth, dev, args.profile_decode)
         log(f"decode profile run: {args.profile_decode} steps")
+        return
+    if args.profile_conv:
+        x, w, bias = _conv_inputs(torch, synth, dev)
+        for _ in range(args.profile_conv):
+            ssm.conv1d_fwd(x, w, bias)
+        torch.cuda.synchronize()
+        log(f"conv1d profile run: {args.profile_conv} calls")
         return
 
     result = {}
@@ -275,6 +284,17 @@ def _delta(shape, gen, dev, dtype):
     return torch.exp(lo + (hi - lo) * u).to(dtype)
 
 
+def _conv_inputs(torch, synth, dev):
+    """Headline-shape input of the convolution: x [4, 4096, 4096] bf16, width-4 filter."""
+    c = synth.CONFIGS[2]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    x = _randn((c["batch"], c["seqlen"], c["dim"]), gen, dev, torch.bfloat16)
+    w = torch.randn((c["dim"], 4), generator=gen, device=dev) * 0.5
+    bias = torch.randn((c["dim"],), generator=gen, device=dev) * 0.1
+    return x, w, bias
+
+
 def profile_decode(torch, ssm, synth, dev, steps):
     """A few decode steps on the decode workload's state (h [256, 4096, 16] fp32)."""
     c = synth.CONFIGS[4]
@@ -371,6 +391,33 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         f"eager from Python {eager_ms:.2f} ms")
     del xs, ds, zs, Bs, Cs, h
     torch.cuda.empty_cache()
+    # --- causal conv1d + SiLU at the headline shape (HBM-bound) ---
+    x, w, bias = _conv_inputs(torch, synth, dev)
+    yc = torch.empty_like(x)
+    for _ in range(3):
+        ssm.conv1d_fwd(x, w, bias, out=yc)
+    torch.cuda.synchronize()
+    ct = []
+    for _ in range(20):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        ssm.conv1d_fwd(x, w, bias, out=yc)
+        b_.record()
+        torch.cuda.synchronize()
+        ct.append(a_.elapsed_time(b_))
+    ct.sort()
+    conv_bytes = 2 * x.numel() * 2 + w.numel() * 4 + bias.numel() * 4
+    conv_gbs = conv_bytes / (ct[len(ct) // 2] * 1e-3) / 1e9
+    out["conv1d"] = {
+        "workload": "causal depthwise conv1d width 4 + SiLU, x [4, 4096, 4096] bf16",
+        "kernel_us_median": round(ct[len(ct) // 2] * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(conv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(conv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("conv1d_B4_L4096_D4096_W4_bf16", src_hash),
+                     "alg_bytes_per_launch": conv_bytes},
+    }
+    log(f"conv1d: {ct[len(ct) // 2] * 1e3:.1f} us median, {conv_gbs:.0f} GB/s ({conv_gbs / HBM_PEAK_GBS:.1%} of HBM)")
+    del x, yc
     # --- backward pass at the headline shape ---
     c = synth.CONFIGS[2]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
