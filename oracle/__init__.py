@@ -48,8 +48,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
-    lib.oracle_scan.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P,
-                                ctypes.c_int]
+    lib.oracle_scan.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P,
+                                P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_scan.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P,
                                     P, P, P, P, P, P, P, P, ctypes.c_int]
@@ -73,15 +73,21 @@ def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 
 
+DISCRETIZATIONS = {"mamba": 0, "zoh": 1, "bilinear": 2}
+
+
 def scan_f64(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=False,
-             ch_b=None, ch_d=None, nthreads=None):
+             ch_b=None, ch_d=None, nthreads=None, discretization="mamba", delta_bias=None):
     """Core call on float64 arrays.
 
     x, delta, z : [nchan, L] series of the listed channels (b = ch_b[i], d = ch_d[i])
     Bm, Cm      : [nb, L, N];  A: [nd, N];  Dskip: [nd] or None;  h0: [nchan, N] or None
+    discretization: "mamba", "zoh" or "bilinear";  delta_bias: [nd] or None
     Returns (y [nchan, L], h_last [nchan, N]).
     """
     lib = _load()
+    disc = DISCRETIZATIONS[discretization]
+    dbias = _f64(delta_bias)
     x, delta, z = _f64(x), _f64(delta), _f64(z)
     Bm, Cm, A, Dskip, h0 = _f64(Bm), _f64(Cm), _f64(A), _f64(Dskip), _f64(h0)
     nchan, L = x.shape
@@ -98,8 +104,11 @@ def scan_f64(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fa
         assert h0.shape == (nchan, N)
     y = np.empty((nchan, L), dtype=np.float64)
     h_last = np.empty((nchan, N), dtype=np.float64)
+    if dbias is not None:
+        assert dbias.shape == (A.shape[0],)
     rc = lib.oracle_scan(L, N, nchan, _ptr(ch_b), _ptr(ch_d), _ptr(x), _ptr(delta), _ptr(z),
-                         int(bool(delta_softplus)), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
+                         int(bool(delta_softplus)), disc, _ptr(dbias),
+                         _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
                          _ptr(h0), _ptr(y), _ptr(h_last),
                          int(nthreads or default_threads()))
     if rc != 0:
@@ -186,6 +195,8 @@ def scan(inp: dict, channels=None, nthreads=None):
     """Oracle of one selective-scan call on storage-form inputs (a ``synth`` dict).
 
     channels=None: every channel; returns y [B, L, D] and h_last [B, D, N] (float64).
+    Optional keys of ``inp``: "discretization" ("mamba", "zoh", "bilinear") and
+    "delta_bias" ([D] float32, added to delta before the softplus).
     channels=[(b, d), ...]: only those; returns y [nchan, L] and h_last [nchan, N].
     """
     dtype = inp["dtype"]
@@ -208,14 +219,15 @@ def scan(inp: dict, channels=None, nthreads=None):
     h0c = None if h0 is None else np.asarray(h0, dtype=np.float64)[cb, cd, :]
     y, h_last = scan_f64(series(x), series(delta), inp["A"], _widen(inp["B"], dtype),
                          _widen(inp["C"], dtype), inp["Dskip"], series(z), h0c,
-                         inp.get("delta_softplus", False), cb, cd, nthreads)
+                         inp.get("delta_softplus", False), cb, cd, nthreads,
+                         inp.get("discretization", "mamba"), inp.get("delta_bias"))
     if channels is None:
         return y.reshape(Bsz, D, L).transpose(0, 2, 1).copy(), h_last.reshape(Bsz, D, N)
     return y, h_last
 
 
 def state_update(h, step: dict, A, Dskip, dtype: str, channels=None, delta_softplus=False,
-                 nthreads=None):
+                 nthreads=None, discretization="mamba", delta_bias=None):
     """Oracle of one single-token state update (the scan body with L = 1).
 
     h: float64 state, [B, D, N] (channels=None) or [nchan, N] for the listed
@@ -241,7 +253,7 @@ def state_update(h, step: dict, A, Dskip, dtype: str, channels=None, delta_softp
     Bm = _widen(step["B"], dtype)[:, None, :]
     Cm = _widen(step["C"], dtype)[:, None, :]
     y, h_new = scan_f64(series(x), series(step["delta"]), A, Bm, Cm, Dskip, series(step.get("z")),
-                        h0, delta_softplus, cb, cd, nthreads)
+                        h0, delta_softplus, cb, cd, nthreads, discretization, delta_bias)
     if channels is None:
         return h_new.reshape(Bsz, D, N), y.reshape(Bsz, D)
     return h_new, y[:, 0]

@@ -12,6 +12,10 @@ Algorithm"; skill page, MambaBlock._selective_scan):
     h              = A_bar * h + B_bar * x[b, t, d]
     y[b, t, d]     = <h[b, d, :], C[b, t, :]> + D[d] * x[b, t, d]
     y              = y * silu(z[b, t, d])            (when a gate is given)
+
+with the other discretisations of ``_discretize_slab`` (zero-order hold, bilinear)
+in place of A_bar, B_bar, and an optional per-channel bias added to delta before
+the softplus.
 """
 from __future__ import annotations
 
@@ -26,13 +30,38 @@ def _softplus(u):
     return np.logaddexp(0.0, u)
 
 
-def scan_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=False):
+def _discretize_slab(kind, dt, A):
+    """A_bar and the factor F with B_bar = F * B, as [B, D, N] slabs, for a diagonal A.
+
+    "mamba": exp(dt A) and dt (managen.ai, Selective Scan Algorithm);
+    "zoh": exp(dt A) and A^-1 (exp(dt A) - 1), i.e. dt * phi(dt A) with
+    phi(u) = (e^u - 1) / u, phi(0) = 1 (skill page "Discretization" docstring;
+    brentwoodlivery, From Continuous to Discrete);
+    "bilinear": (1 + dt A / 2) / (1 - dt A / 2) and dt / (1 - dt A / 2)
+    (chipfoundryservices glossary, Lab 1)."""
+    u = dt * A[None, :, :]
+    if kind == "bilinear":
+        den = 1.0 - 0.5 * u
+        return (1.0 + 0.5 * u) / den, dt / den
+    a_bar = np.exp(u)
+    if kind == "zoh":
+        with np.errstate(divide="ignore", invalid="ignore"):
+            phi = np.where(u == 0.0, 1.0, np.expm1(u) / np.where(u == 0.0, 1.0, u))
+        return a_bar, dt * phi
+    return a_bar, np.broadcast_to(dt, a_bar.shape)
+
+
+def scan_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=False,
+            discretization="mamba", delta_bias=None):
     """All arrays float64.  x, delta, z: [B, L, D]; A: [D, N]; Bm, Cm: [B, L, N];
-    Dskip: [D]; h0: [B, D, N].  Returns y [B, L, D], h_last [B, D, N]."""
+    Dskip: [D]; h0: [B, D, N]; delta_bias: [D] (added before the softplus).
+    Returns y [B, L, D], h_last [B, D, N]."""
     x = np.asarray(x, dtype=np.float64)
     Bsz, L, D = x.shape
     N = A.shape[1]
     dl = np.asarray(delta, dtype=np.float64)
+    if delta_bias is not None:
+        dl = dl + np.asarray(delta_bias, dtype=np.float64)[None, None, :]
     if delta_softplus:
         dl = _softplus(dl)
     h = np.zeros((Bsz, D, N)) if h0 is None else np.array(h0, dtype=np.float64, copy=True)
@@ -40,8 +69,8 @@ def scan_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fal
     A = np.asarray(A, dtype=np.float64)
     for t in range(L):
         dt = dl[:, t, :][:, :, None]                      # [B, D, 1]
-        a_bar = np.exp(dt * A[None, :, :])                 # [B, D, N]
-        b_bar = dt * np.asarray(Bm, dtype=np.float64)[:, t, None, :]    # [B, D, N]
+        a_bar, fac = _discretize_slab(discretization, dt, A)             # [B, D, N]
+        b_bar = fac * np.asarray(Bm, dtype=np.float64)[:, t, None, :]    # [B, D, N]
         h = a_bar * h + b_bar * x[:, t, :, None]
         yt = np.einsum("bdn,bn->bd", h, np.asarray(Cm, dtype=np.float64)[:, t, :])
         if Dskip is not None:

@@ -9,11 +9,18 @@
  *
  *   h[n] = h0[n] (or 0)
  *   for t = 0 .. L-1:
- *       dt   = delta[t]                 (or log(1 + exp(delta[t])) in softplus mode)
- *       h[n] = exp(dt * A[d, n]) * h[n] + dt * B[b, t, n] * x[t]     for every n
+ *       dt   = delta[t] + dbias[d]      (dbias optional; log(1 + exp(.)) of it in softplus mode)
+ *       h[n] = A_bar(dt, A[d, n]) * h[n] + Bf(dt, A[d, n]) * B[b, t, n] * x[t]   for every n
  *       y[t] = sum_n C[b, t, n] * h[n] + Dskip[d] * x[t]
  *       y[t] = y[t] * z[t] / (1 + exp(-z[t]))       (only when a gate z is given)
  *   h_last = h
+ *
+ * Discretisations of the continuous (A, B) with step dt, A diagonal (A_bar,
+ * B_bar = Bf * B):
+ *   0 Mamba:    A_bar = exp(dt a),  Bf = dt  (the first-order B_bar of the Mamba listings)
+ *   1 ZOH:      A_bar = exp(dt a),  Bf = (exp(dt a) - 1) / a, and dt where a = 0 (its
+ *               limit), evaluated with expm1 so that small dt a keeps full precision
+ *   2 bilinear: A_bar = (1 + dt a / 2) / (1 - dt a / 2),  Bf = dt / (1 - dt a / 2)
  *
  * Sources (the five web pages on state space models / Mamba):
  *  - discretisation A_bar = exp(delta A), B_bar = delta B: "State Space
@@ -25,7 +32,14 @@
  *    "Training vs Inference Modes" (inference update h_k, output y_k);
  *  - output gate y * silu(z): managen.ai page, MambaBlock.forward;
  *  - delta = softplus(Linear(x)): dileepadev "State Space Models and Mamba",
- *    section "Mamba: Selective State Spaces".
+ *    section "Mamba: Selective State Spaces"; the linear map's bias added before
+ *    the softplus: skill page, MambaBlock listing (dt_proj with bias, then softplus);
+ *  - zero-order hold B_bar = (exp(dt A) - I) A^-1 B: the skill page's "Discretization"
+ *    docstring and brentwoodlivery's section "From Continuous to Discrete" and its
+ *    discretisation flashcard;
+ *  - bilinear A_bar = (I + dt/2 A)(I - dt/2 A)^-1, B_bar = (I - dt/2 A)^-1 B dt:
+ *    chipfoundryservices glossary "State Space Models & Mamba", Lab 1 and the
+ *    section "Discretization Method".
  *
  * Every value is double precision; the caller widens stored bf16/fp32 inputs
  * to double exactly before the call.  No blocking, no reordering: time runs
@@ -50,7 +64,8 @@ typedef struct {
     int64_t L, N, nchan;
     const int64_t *ch_b, *ch_d;
     const double *x, *delta, *z;
-    int delta_softplus;
+    int delta_softplus, disc;
+    const double *dbias;
     const double *Bm, *Cm, *A, *Dskip, *h0;
     double *y, *h_last;
     int64_t next;            /* next channel to take (guarded by lock) */
@@ -66,6 +81,22 @@ static double softplus(double u)
     return u + log1p(exp(-u));
 }
 
+/* A_bar and Bf (B_bar = Bf * B) of one state, for the discretisations listed above */
+static void discretize(int disc, double dt, double a, double *a_bar, double *bf)
+{
+    if (disc == 2) {
+        const double half = 0.5 * dt * a;
+        *a_bar = (1.0 + half) / (1.0 - half);
+        *bf = dt / (1.0 - half);
+        return;
+    }
+    *a_bar = exp(dt * a);
+    if (disc == 1)
+        *bf = a == 0.0 ? dt : expm1(dt * a) / a;
+    else
+        *bf = dt;
+}
+
 static void one_channel(const job_t *J, int64_t c)
 {
     const int64_t L = J->L, N = J->N;
@@ -76,6 +107,8 @@ static void one_channel(const job_t *J, int64_t c)
 
     for (int64_t t = 0; t < L; ++t) {
         double dt = J->delta[c * L + t];
+        if (J->dbias)
+            dt += J->dbias[d];
         if (J->delta_softplus)
             dt = softplus(dt);
         const double xt = J->x[c * L + t];
@@ -83,8 +116,9 @@ static void one_channel(const job_t *J, int64_t c)
         const double *Ct = J->Cm + (b * L + t) * N;
         double y = 0.0;
         for (int64_t n = 0; n < N; ++n) {
-            const double a_bar = exp(dt * J->A[d * N + n]);
-            const double b_bar = dt * Bt[n];
+            double a_bar, bf;
+            discretize(J->disc, dt, J->A[d * N + n], &a_bar, &bf);
+            const double b_bar = bf * Bt[n];
             h[n] = a_bar * h[n] + b_bar * xt;
         }
         for (int64_t n = 0; n < N; ++n)
@@ -117,13 +151,15 @@ static void *worker(void *arg)
     return NULL;
 }
 
-/* Returns 0 on success, -1 on bad arguments. */
+/* Returns 0 on success, -1 on bad arguments.  disc: 0 Mamba, 1 ZOH, 2 bilinear;
+ * dbias: [nd] or NULL. */
 int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const int64_t *ch_d,
                 const double *x, const double *delta, const double *z, int delta_softplus,
+                int disc, const double *dbias,
                 const double *Bm, const double *Cm, const double *A, const double *Dskip,
                 const double *h0, double *y, double *h_last, int nthreads)
 {
-    if (L < 0 || N < 0 || nchan < 0)
+    if (L < 0 || N < 0 || nchan < 0 || disc < 0 || disc > 2)
         return -1;
     if (nchan > 0 && (!ch_b || !ch_d || !y || (L > 0 && (!x || !delta || !Bm || !Cm)) || (N > 0 && !A)))
         return -1;
@@ -131,6 +167,7 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
     memset(&J, 0, sizeof(J));
     J.L = L; J.N = N; J.nchan = nchan; J.ch_b = ch_b; J.ch_d = ch_d;
     J.x = x; J.delta = delta; J.z = z; J.delta_softplus = delta_softplus;
+    J.disc = disc; J.dbias = dbias;
     J.Bm = Bm; J.Cm = Cm; J.A = A; J.Dskip = Dskip; J.h0 = h0;
     J.y = y; J.h_last = h_last; J.next = 0;
     pthread_mutex_init(&J.lock, NULL);
@@ -153,7 +190,7 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
 }
 
 /*
- * Backward (adjoint) of the same scan, for a loss whose gradients with respect
+ * Backward (adjoint) of the same scan (Mamba discretisation, no delta bias), for a loss whose gradients with respect
  * to the outputs are given: gy[t] = dLoss/dy[t] for every channel, and
  * g_last[n] = dLoss/dh_last[n] (or 0).  Plain reverse-mode differentiation of
  * the definition above, one channel at a time, no reordering:
@@ -323,4 +360,4 @@ int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, co
     return 0;
 }
 
-int oracle_abi_version(void) { return 2; }
+int oracle_abi_version(void) { return 3; }
