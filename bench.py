@@ -41,6 +41,12 @@ SLOTS_PER_UPDATE = 6.0
 # per (b, t, d): delta*x, D*x fma, gate: mul, exp (2), add, rcp (2), mul, mul
 SLOTS_PER_TOKEN_CHANNEL_GATED = 10.0
 SLOTS_PER_TOKEN_CHANNEL = 2.0
+# The other discretisations, per state update.  Zero-order hold: mul (s = delta*A*log2 e),
+# v_exp_f32 (2), fma ((e - 1) / A), mul (x*B), mul (by the factor), fma (state), fma
+# (readout) = 8; the series branch for small |delta A| and its select (6 more) are
+# accuracy work, not counted.  Bilinear: fma (1 - delta*A/2), v_rcp_f32 (2), mul
+# (delta*x*B), fma (2h + .), fma (r * . - h), fma (readout) = 7.
+SLOTS_PER_UPDATE_VARIANT = {"zoh": 8.0, "bilinear": 7.0}
 
 
 def kernel_source_hash():
@@ -390,6 +396,48 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     log(f"decode: {tot_ms:.2f} ms for {S} steps from a graph ({k_avg * 1e3:.1f} us/step); "
         f"eager from Python {eager_ms:.2f} ms")
     del xs, ds, zs, Bs, Cs, h
+    torch.cuda.empty_cache()
+    # --- the other discretisations at the headline shape ---
+    c = synth.CONFIGS[2]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    x, dl, z = (_randn((Bsz, L, D), gen, dev, bf) if k != "dl" else _delta((Bsz, L, D), gen, dev, bf)
+                for k in ("x", "dl", "z"))
+    Bm = _randn((Bsz, L, N), gen, dev, bf)
+    Cm = _randn((Bsz, L, N), gen, dev, bf)
+    A = torch.from_numpy(synth.make_A(2, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(2, D, "normal")).to(dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(max(ssm.scan_plan(Bsz, L, D, N, "bf16")["workspace_bytes"], 1), dtype=torch.uint8,
+                     device=dev)
+    out["variants"] = {}
+    for disc in ("zoh", "bilinear"):
+        for _ in range(3):
+            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
+        torch.cuda.synchronize()
+        vt = []
+        for _ in range(10):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
+            b_.record()
+            torch.cuda.synchronize()
+            vt.append(a_.elapsed_time(b_))
+        vt.sort()
+        ms = vt[len(vt) // 2]
+        upd = Bsz * L * D * N
+        slots = upd * SLOTS_PER_UPDATE_VARIANT[disc] + Bsz * L * D * SLOTS_PER_TOKEN_CHANNEL_GATED
+        ts = slots / (ms * 1e-3) / 1e12
+        out["variants"][disc] = {
+            "workload": c["name"] + f", {disc} discretisation",
+            "ms_median": round(ms, 4), "state_updates_per_s": upd / (ms * 1e-3),
+            "roofline": {"bound": "alu", "achieved": round(ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                         "unit": "Tslot/s", "frac": round(ts / VALU_PEAK_TSLOTS, 4),
+                         "alg_slots_per_launch": slots},
+            "timing": "median of 10 launches, each between two events (B/C pre-pass included)",
+        }
+        log(f"{disc}: {ms * 1e3:.1f} us/launch, {upd / (ms * 1e-3):.3e} updates/s, "
+            f"VALU {ts / VALU_PEAK_TSLOTS:.1%}")
+    del x, dl, z, Bm, Cm, y, ws
     torch.cuda.empty_cache()
     # --- causal conv1d + SiLU at the headline shape (HBM-bound) ---
     x, w, bias = _conv_inputs(torch, synth, dev)

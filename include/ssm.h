@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_DSTATE 16
 
 typedef enum ssm_dtype {
@@ -65,13 +65,44 @@ typedef enum ssm_status {
     SSM_EHIP = 4           /* the HIP runtime refused a launch */
 } ssm_status;
 
+/*
+ * How the continuous parameters (A, B) become the discrete step (A_bar, B_bar)
+ * for step size dt, A diagonal (one value a = A[d,n] per state):
+ *   SSM_DISC_MAMBA     A_bar = exp(dt a), B_bar = dt B.  The first-order B_bar of
+ *                      the Mamba listings (managen.ai "Selective Scan Algorithm";
+ *                      skill page MambaBlock._selective_scan).  The default.
+ *   SSM_DISC_ZOH       A_bar = exp(dt a), B_bar = (exp(dt a) - 1) / a * B, and dt B
+ *                      where a = 0 (zero-order hold: skill page "Discretization"
+ *                      docstring; brentwoodlivery "From Continuous to Discrete").
+ *   SSM_DISC_BILINEAR  A_bar = (1 + dt a / 2) / (1 - dt a / 2),
+ *                      B_bar = dt / (1 - dt a / 2) * B (chipfoundryservices glossary
+ *                      "State Space Models & Mamba", Lab 1).  Defined while
+ *                      dt a / 2 != 1, i.e. for every dt when a <= 0.
+ */
+typedef enum ssm_discretization {
+    SSM_DISC_MAMBA = 0,
+    SSM_DISC_ZOH = 1,
+    SSM_DISC_BILINEAR = 2
+} ssm_discretization;
+
+/* Optional variant of the recurrence for ssm_scan_fwd and ssm_state_update.  A NULL
+ * pointer means { SSM_DISC_MAMBA, 0, NULL }. */
+typedef struct ssm_variant {
+    int32_t discretization;    /* an ssm_discretization */
+    int32_t reserved;          /* must be 0 */
+    const float *delta_bias;   /* [dim] fp32 device pointer, added to delta before the
+                                  softplus (the bias of the linear map that produces delta:
+                                  skill page, MambaBlock listing, dt_proj); NULL = none */
+} ssm_variant;
+
 /* Optional tuning of ssm_scan_fwd.  A NULL pointer or a zero field means
  * "choose automatically".  None of these change the result beyond fp32
  * rounding order. */
 typedef struct ssm_scan_opts {
     int64_t chunk_len;     /* length of the sequence chunks scanned in parallel (>= 1) */
     int32_t states_per_lane; /* 1, 2, 4, 8 or 16 states of one channel per GPU lane */
-    int32_t time_block;    /* time steps staged per block: 8, 16 or 32 */
+    int32_t time_block;    /* time steps staged per block: 8, 16 or 32 (the generic kernel of
+                              the ZOH and bilinear variants always stages 8) */
     int32_t one_block_per_cu; /* 0: automatic; 1: reserve LDS so each CU runs one workgroup; -1: never */
     int32_t reserved;      /* must be 0 */
 } ssm_scan_opts;
@@ -129,6 +160,8 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   h_last    [batch, dim, dstate]   fp32    NULL = not stored; must not overlap h0
  *   y         [batch, seqlen, dim]   dtype   output; must not overlap any input
  *   delta_softplus  0: delta is the step size;  1: step size = log(1 + exp(delta))
+ *   variant   NULL (Mamba discretisation, no delta bias) or see ssm_variant; the
+ *             step size is then delta + delta_bias[d], before the softplus
  *   opts      NULL or tuning (see ssm_scan_opts)
  *   workspace device memory of ssm_scan_workspace_bytes() bytes (NULL if 0)
  *
@@ -139,8 +172,8 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
                  const void *x, const void *delta, const float *A, const void *B,
                  const void *C, const float *Dskip, const void *z, const float *h0,
-                 float *h_last, void *y, int delta_softplus, const ssm_scan_opts *opts,
-                 void *workspace, size_t workspace_bytes, void *stream);
+                 float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                 const ssm_scan_opts *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Single-token recurrent state update (generation form): one step of the
@@ -155,6 +188,7 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
  *   Dskip     [dim]                  fp32    NULL = no skip term
  *   z         [batch, dim]           dtype   NULL = no output gate
  *   y         [batch, dim]           dtype   output; must not overlap any input or h
+ *   delta_softplus, variant          as for ssm_scan_fwd
  *
  * L consecutive calls give the same y and final h as one ssm_scan_fwd over
  * those L tokens (up to fp32 rounding order).
@@ -162,7 +196,7 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
 int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, float *h,
                      const void *x, const void *delta, const float *A, const void *B,
                      const void *C, const float *Dskip, const void *z, void *y,
-                     int delta_softplus, void *stream);
+                     int delta_softplus, const ssm_variant *variant, void *stream);
 
 /* Host-only: bytes of device workspace ssm_scan_bwd needs for this shape (0 when
  * nothing is computed, or the shape is invalid or unsupported). */

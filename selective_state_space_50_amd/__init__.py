@@ -24,6 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
+ABI_VERSION = 2     # SSM_ABI_VERSION of include/ssm.h
 
 
 class SSMError(RuntimeError):
@@ -36,6 +37,14 @@ class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("states_per_lane", ctypes.c_int32),
                 ("time_block", ctypes.c_int32), ("one_block_per_cu", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class Variant(ctypes.Structure):
+    _fields_ = [("discretization", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("delta_bias", ctypes.c_void_p)]
+
+
+DISCRETIZATIONS = {"mamba": 0, "zoh": 1, "bilinear": 2}
 
 
 class ScanPlan(ctypes.Structure):
@@ -72,9 +81,10 @@ def lib():
     L.ssm_scan_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, ctypes.POINTER(ScanOpts)]
     L.ssm_scan_fwd.restype = I32
     L.ssm_scan_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, P, I32,
-                               ctypes.POINTER(ScanOpts), P, SZ, P]
+                               ctypes.POINTER(Variant), ctypes.POINTER(ScanOpts), P, SZ, P]
     L.ssm_state_update.restype = I32
-    L.ssm_state_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, I32, P]
+    L.ssm_state_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, I32,
+                                   ctypes.POINTER(Variant), P]
     L.ssm_scan_bwd_workspace_bytes.restype = SZ
     L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
     L.ssm_scan_bwd.restype = I32
@@ -83,8 +93,8 @@ def lib():
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
     L.ssm_conv1d_update.restype = I32
     L.ssm_conv1d_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, I32, P]
-    if L.ssm_abi_version() != 1:
-        raise ImportError(f"libssm ABI version {L.ssm_abi_version()} != 1")
+    if L.ssm_abi_version() != ABI_VERSION:
+        raise ImportError(f"libssm ABI version {L.ssm_abi_version()} != {ABI_VERSION}")
     _lib = L
     return L
 
@@ -113,6 +123,17 @@ def _opts(chunk_len=0, states_per_lane=0, time_block=0, one_block_per_cu=0):
     if not (chunk_len or states_per_lane or time_block or one_block_per_cu):
         return None
     return ScanOpts(int(chunk_len), int(states_per_lane), int(time_block), int(one_block_per_cu), 0)
+
+
+def _variant(discretization, delta_bias, dim, device):
+    """The ssm_variant of a call (None for the default: Mamba, no delta bias)."""
+    import torch
+    if discretization not in DISCRETIZATIONS:
+        raise ValueError(f"discretization {discretization!r} is not one of {sorted(DISCRETIZATIONS)}")
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, device)
+    if discretization == "mamba" and delta_bias is None:
+        return None
+    return Variant(DISCRETIZATIONS[discretization], 0, _ptr(delta_bias))
 
 
 def _dtype_code(t):
@@ -162,12 +183,15 @@ def _need(t, name, shape, dtype, device):
 
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
+             discretization="mamba", delta_bias=None,
              return_last_state=False, out=None, h_last=None, workspace=None, chunk_len=0,
              states_per_lane=0, time_block=0, one_block_per_cu=0, stream=None):
     """Selective scan y = S6(x, delta, A, B, C, D) [* silu(z)] on the GPU.
 
     x, delta, z: [B, L, D];  B, C: [B, L, N];  A: [D, N] fp32;  D: [D] fp32;
     h0: [B, D, N] fp32.  x/delta/z/B/C share one dtype (bfloat16 or float32).
+    discretization: "mamba" (A_bar = exp(dt A), B_bar = dt B), "zoh" or "bilinear";
+    delta_bias: [D] fp32 added to delta before the softplus.
     Returns y (same dtype as x), or (y, h_last) when return_last_state.
     """
     import torch
@@ -186,6 +210,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False
     _need(A, "A", (Dm, N), torch.float32, dev)
     _need(D, "D", (Dm,), torch.float32, dev)
     _need(h0, "h0", (Bsz, Dm, N), torch.float32, dev)
+    v = _variant(discretization, delta_bias, Dm, dev)
     code = _dtype_code(x)
     if out is None:
         out = torch.empty_like(x)
@@ -200,18 +225,20 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     st = lib().ssm_scan_fwd(Bsz, L, Dm, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                             _ptr(D), _ptr(z), _ptr(h0), _ptr(h_last), _ptr(out),
-                            int(bool(delta_softplus)), ctypes.byref(o) if o else None,
+                            int(bool(delta_softplus)), ctypes.byref(v) if v else None,
+                            ctypes.byref(o) if o else None,
                             _ptr(workspace) if ws_bytes else None, ws_bytes,
                             ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_scan_fwd")
     return (out, h_last) if return_last_state else out
 
 
-def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False, out=None,
-                 stream=None):
+def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False,
+                 discretization="mamba", delta_bias=None, out=None, stream=None):
     """One recurrent step: updates h [B, D, N] fp32 in place and returns y [B, D].
 
-    x, delta, z: [B, D];  B, C: [B, N];  A: [D, N] fp32;  D: [D] fp32.
+    x, delta, z: [B, D];  B, C: [B, N];  A: [D, N] fp32;  D: [D] fp32;
+    discretization and delta_bias as for scan_fwd.
     """
     import torch
     if h.dim() != 3:
@@ -228,6 +255,7 @@ def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False, 
     _need(C, "C", (Bsz, N), dt, dev)
     _need(A, "A", (Dm, N), torch.float32, dev)
     _need(D, "D", (Dm,), torch.float32, dev)
+    v = _variant(discretization, delta_bias, Dm, dev)
     code = _dtype_code(x)
     if out is None:
         out = torch.empty_like(x)
@@ -235,7 +263,7 @@ def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False, 
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     st = lib().ssm_state_update(Bsz, Dm, N, code, _ptr(h), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                                 _ptr(C), _ptr(D), _ptr(z), _ptr(out), int(bool(delta_softplus)),
-                                ctypes.c_void_p(s.cuda_stream))
+                                ctypes.byref(v) if v else None, ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_state_update")
     return out
 

@@ -7,12 +7,13 @@
 // DPP quad permutes.
 // Other shapes: lpc lanes per channel, G states per lane; the lane shares of
 // y are summed with cross-lane shuffles and the first lane finishes the output.
+// DISC selects the discretisation (disc_step in ssm_device.h).
 #include "ssm_device.h"
 
 namespace ssm {
 namespace {
 
-template <typename T, int G, bool HAS_Z>
+template <int DISC, typename T, int G, bool HAS_Z>
 __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int lpc = a.lpc;
@@ -30,9 +31,9 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
     float yp = 0.0f, xv = 0.0f;
     if (valid) {
         xv = widen(X, ch);
-        float dv = widen(DL, ch);
+        float dv = widen(DL, ch) + (a.dbias ? a.dbias[d] : 0.0f);
         if (a.softplus) dv = softplus_f(dv);
-        const float u = dv * xv;
+        const float u = DISC == kZOH ? xv : dv * xv;
         if (G == 4 && n0 + 4 <= N) {
             float4 hv = *reinterpret_cast<const float4 *>(a.h + ch * N + n0);
             const float4 av = *reinterpret_cast<const float4 *>(a.A + d * N + n0);
@@ -40,8 +41,9 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
             const float aa[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float dA = __builtin_amdgcn_exp2f(dv * (aa[g] * kLog2e));
-                hh[g] = __builtin_fmaf(dA, hh[g], u * widen(Bm, b * N + n0 + g));
+                float ab;
+                hh[g] = disc_step<DISC>(hh[g], dv, u, widen(Bm, b * N + n0 + g), aa[g] * kLog2e,
+                                        disc_aux<DISC>(aa[g]), ab);
                 yp = __builtin_fmaf(widen(Cm, b * N + n0 + g), hh[g], yp);
             }
             *reinterpret_cast<float4 *>(a.h + ch * N + n0) = make_float4(hh[0], hh[1], hh[2], hh[3]);
@@ -50,8 +52,10 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
             for (int g = 0; g < G; ++g) {
                 const int64_t n = n0 + g;
                 if (n < N) {
-                    const float dA = __builtin_amdgcn_exp2f(dv * (a.A[d * N + n] * kLog2e));
-                    float hv = __builtin_fmaf(dA, a.h[ch * N + n], u * widen(Bm, b * N + n));
+                    const float av = a.A[d * N + n];
+                    float ab;
+                    float hv = disc_step<DISC>(a.h[ch * N + n], dv, u, widen(Bm, b * N + n), av * kLog2e,
+                                               disc_aux<DISC>(av), ab);
                     a.h[ch * N + n] = hv;
                     yp = __builtin_fmaf(widen(Cm, b * N + n), hv, yp);
                 }
@@ -89,7 +93,7 @@ __device__ __forceinline__ float quad_sum(float v) {
 }
 
 // dstate == 16, dim % 64 == 0: block = 64 channels of one batch row, 4 lanes per channel.
-template <typename T, bool HAS_Z>
+template <int DISC, typename T, bool HAS_Z>
 __global__ void __launch_bounds__(256) state_update_q16_kernel(UpdArgs a) {
     constexpr int N = 16;
     const int tid = threadIdx.x;
@@ -109,13 +113,14 @@ __global__ void __launch_bounds__(256) state_update_q16_kernel(UpdArgs a) {
     load4(static_cast<const T *>(a.Bm) + b * N + sub * 4, bv);
     load4(static_cast<const T *>(a.Cm) + b * N + sub * 4, cv);
     const float xv = widen(X, cl);
-    float dv = widen(DL, cl);
+    float dv = widen(DL, cl) + (a.dbias ? a.dbias[dblk + cl] : 0.0f);
     if (a.softplus) dv = softplus_f(dv);
-    const float u = dv * xv;
+    const float u = DISC == kZOH ? xv : dv * xv;
     float yp = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        hv[g] = __builtin_fmaf(__builtin_amdgcn_exp2f(dv * (av[g] * kLog2e)), hv[g], u * bv[g]);
+        float ab;
+        hv[g] = disc_step<DISC>(hv[g], dv, u, bv[g], av[g] * kLog2e, disc_aux<DISC>(av[g]), ab);
         yp = __builtin_fmaf(cv[g], hv[g], yp);
     }
     *reinterpret_cast<float4 *>(hb + so) = make_float4(hv[0], hv[1], hv[2], hv[3]);
@@ -128,39 +133,38 @@ __global__ void __launch_bounds__(256) state_update_q16_kernel(UpdArgs a) {
     }
 }
 
+template <int DISC, typename T, bool HAS_Z>
+void launch_upd(const UpdArgs &a, hipStream_t s) {
+    if (a.N == 16 && a.D % 64 == 0) {
+        const dim3 grid(static_cast<unsigned>(a.B * a.D / 64));
+        hipLaunchKernelGGL((state_update_q16_kernel<DISC, T, HAS_Z>), grid, dim3(256), 0, s, a);
+        return;
+    }
+    const int64_t threads = a.B * a.D * a.lpc;
+    const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+    if (a.N % 4 == 0) hipLaunchKernelGGL((state_update_kernel<DISC, T, 4, HAS_Z>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((state_update_kernel<DISC, T, 1, HAS_Z>), grid, dim3(256), 0, s, a);
+}
+
+template <int DISC>
+void launch_upd_d(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s) {
+    if (bf16) {
+        if (has_z) launch_upd<DISC, uint16_t, true>(a, s);
+        else launch_upd<DISC, uint16_t, false>(a, s);
+    } else {
+        if (has_z) launch_upd<DISC, float, true>(a, s);
+        else launch_upd<DISC, float, false>(a, s);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_state_update(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s) {
-    if (a.N == 16 && a.D % 64 == 0) {
-        dim3 grid(static_cast<unsigned>(a.B * a.D / 64));
-        if (bf16) {
-            if (has_z) hipLaunchKernelGGL((state_update_q16_kernel<uint16_t, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((state_update_q16_kernel<uint16_t, false>), grid, dim3(256), 0, s, a);
-        } else {
-            if (has_z) hipLaunchKernelGGL((state_update_q16_kernel<float, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((state_update_q16_kernel<float, false>), grid, dim3(256), 0, s, a);
-        }
-        return hipGetLastError();
-    }
-    const int G = (a.N % 4 == 0) ? 4 : 1;
-    const int64_t threads = a.B * a.D * a.lpc;
-    dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-    if (G == 4) {
-        if (bf16) {
-            if (has_z) hipLaunchKernelGGL((state_update_kernel<uint16_t, 4, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((state_update_kernel<uint16_t, 4, false>), grid, dim3(256), 0, s, a);
-        } else {
-            if (has_z) hipLaunchKernelGGL((state_update_kernel<float, 4, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((state_update_kernel<float, 4, false>), grid, dim3(256), 0, s, a);
-        }
-    } else {
-        if (bf16) {
-            if (has_z) hipLaunchKernelGGL((state_update_kernel<uint16_t, 1, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((state_update_kernel<uint16_t, 1, false>), grid, dim3(256), 0, s, a);
-        } else {
-            if (has_z) hipLaunchKernelGGL((state_update_kernel<float, 1, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((state_update_kernel<float, 1, false>), grid, dim3(256), 0, s, a);
-        }
+// lanes per channel: a.lpc (G = 4 states per lane when N % 4 == 0, else 1)
+hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s) {
+    switch (disc) {
+        case kZOH: launch_upd_d<kZOH>(a, bf16, has_z, s); break;
+        case kBilinear: launch_upd_d<kBilinear>(a, bf16, has_z, s); break;
+        default: launch_upd_d<kMamba>(a, bf16, has_z, s); break;
     }
     return hipGetLastError();
 }

@@ -1,0 +1,6 @@
+// Specialised selective scan, zero-order-hold discretisation (kernel in scan_fast_kernel.h).
+#include "scan_fast_kernel.h"
+
+namespace ssm {
+SSM_SCAN_LAUNCHER(launch_scan_fast_zoh) { return launch_fast<kZOH>(a, grid, p, bf16, has_z, carry, s); }
+}  // namespace ssm

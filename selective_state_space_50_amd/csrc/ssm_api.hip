@@ -1,8 +1,9 @@
 // C-ABI entry points of libssm, the chunk-carry combine and the empty-sequence fill.
 //
-// Long sequences are cut into chunks: a carry pass stores, per chunk, the sum
-// of delta and the end state from h = 0; the combine folds them in order with
-// (P1, H1) o (P2, H2) = (P2 P1, P2 H1 + H2), P = exp(A sum delta) (skill page
+// Long sequences are cut into chunks: a carry pass stores, per chunk and state,
+// the chunk's decay P (the product of A_bar over the chunk: exp(A sum delta)
+// for the exponential discretisations) and the end state H from h = 0; the
+// combine folds them in order with (P1, H1) o (P2, H2) = (P2 P1, P2 H1 + H2) (skill page
 // "State Space Models Mamba", section "Hardware-Efficient Scan": the
 // recurrence is linear, so it admits an associative scan); a second scan pass
 // then starts every chunk from its carried-in state.
@@ -12,24 +13,20 @@ namespace ssm {
 namespace {
 
 // Fold chunk carries in sequence order, one thread per (b, d, n):
-//   h_in(0) = h0,  h_in(c+1) = exp(A * S_c) * h_in(c) + H_c
+//   h_in(0) = h0,  h_in(c+1) = P_c * h_in(c) + H_c
 // and overwrite slot c with h_in(c+1), the state chunk c+1 starts from.
 __global__ void __launch_bounds__(256) combine_kernel(ScanArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t D = a.D, N = a.N;
     if (i >= a.B * D * N) return;
-    const int64_t n = i % N;
-    const int64_t d = (i / N) % D;
+    const int64_t dn = i % (D * N);
     const int64_t b = i / (N * D);
-    const float al = a.A[d * N + n] * kLog2e;
     float h = a.h0 ? a.h0[i] : 0.0f;
     const int64_t C1 = a.n_chunks - 1;
     for (int64_t c = 0; c < C1; ++c) {
-        const int64_t slot = b * C1 + c;
-        const float P = __builtin_amdgcn_exp2f(al * a.ws_S[slot * D + d]);
-        float *Hp = a.ws_H + (slot * D + d) * N + n;
-        h = __builtin_fmaf(P, h, *Hp);
-        *Hp = h;
+        const int64_t at = (b * C1 + c) * D * N + dn;
+        h = __builtin_fmaf(a.ws_P[at], h, a.ws_H[at]);
+        a.ws_H[at] = h;
     }
 }
 
@@ -45,10 +42,16 @@ int hip_fail(const char *what, hipError_t e) {
     return SSM_EHIP;
 }
 
-hipError_t launch_scan_any(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z,
-                           bool carry, hipStream_t s) {
-    if (p.fast) return launch_scan_fast(a, grid, p, bf16, has_z, carry, s);
-    return launch_scan_generic(a, grid, p, bf16, has_z, carry, s);
+hipError_t launch_scan_any(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16,
+                           bool has_z, bool carry, hipStream_t s) {
+    if (p.fast) {
+        if (disc == kZOH) return launch_scan_fast_zoh(a, grid, p, bf16, has_z, carry, s);
+        if (disc == kBilinear) return launch_scan_fast_bilinear(a, grid, p, bf16, has_z, carry, s);
+        return launch_scan_fast_mamba(a, grid, p, bf16, has_z, carry, s);
+    }
+    if (disc == kZOH) return launch_scan_generic_zoh(a, grid, p, bf16, has_z, carry, s);
+    if (disc == kBilinear) return launch_scan_generic_bilinear(a, grid, p, bf16, has_z, carry, s);
+    return launch_scan_generic_mamba(a, grid, p, bf16, has_z, carry, s);
 }
 
 }  // namespace
@@ -57,13 +60,14 @@ hipError_t launch_scan_any(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool
 extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
                             const void *x, const void *delta, const float *A, const void *B,
                             const void *C, const float *Dskip, const void *z, const float *h0,
-                            float *h_last, void *y, int delta_softplus, const ssm_scan_opts *opts,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                            float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                            const ssm_scan_opts *opts, void *workspace, size_t workspace_bytes,
+                            void *stream) {
     using namespace ssm;
     clear_error();
     ScanPlan p;
     int st = check_scan(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last,
-                        y, delta_softplus, opts, workspace, workspace_bytes, &p);
+                        y, delta_softplus, variant, opts, workspace, workspace_bytes, &p);
     if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -80,10 +84,12 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;
     a.A = A; a.Dskip = Dskip; a.h0 = h0; a.h_last = h_last; a.y = y;
     a.softplus = delta_softplus;
+    a.dbias = variant_bias(variant);
+    const int disc = variant_disc(variant);
     a.NW = p.NW;
     a.chunk_len = p.chunk_len;
     a.n_chunks = p.n_chunks;
-    a.ws_S = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_S_off) : nullptr;
+    a.ws_P = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_P_off) : nullptr;
     a.ws_H = p.n_chunks > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_H_off) : nullptr;
     a.ws_BC = p.fast ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ws_BC_off) : nullptr;
     a.bc_lpad = p.bc_lpad;
@@ -99,7 +105,7 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     if (p.n_chunks > 1) {
         // 1) carries of every chunk but the last
         dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks - 1));
-        e = launch_scan_any(a, g1, p, bf16, false, true, s);
+        e = launch_scan_any(a, g1, p, disc, bf16, false, true, s);
         if (e != hipSuccess) return hip_fail("scan carry launch", e);
         // 2) fold the carries in order
         const int64_t n = batch * dim * dstate;
@@ -109,7 +115,7 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     }
     // 3) every chunk from its carried-in state, producing y
     dim3 g3(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks));
-    e = launch_scan_any(a, g3, p, bf16, has_z, false, s);
+    e = launch_scan_any(a, g3, p, disc, bf16, has_z, false, s);
     if (e != hipSuccess) return hip_fail("scan launch", e);
     return SSM_OK;
 }
@@ -117,23 +123,24 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
 extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, float *h,
                                 const void *x, const void *delta, const float *A, const void *B,
                                 const void *C, const float *Dskip, const void *z, void *y,
-                                int delta_softplus, void *stream) {
+                                int delta_softplus, const ssm_variant *variant, void *stream) {
     using namespace ssm;
     clear_error();
     int st = check_state_update(batch, dim, dstate, dtype, h, x, delta, A, B, C, Dskip, z, y,
-                                delta_softplus);
+                                delta_softplus, variant);
     if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
     UpdArgs a;
     a.B = batch; a.D = dim; a.N = dstate; a.h = h;
     a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C; a.A = A; a.Dskip = Dskip; a.y = y;
     a.softplus = delta_softplus;
+    a.dbias = variant_bias(variant);
     const int G = (dstate % 4 == 0) ? 4 : 1;
     int lpc = 1;
     while (lpc * G < dstate) lpc *= 2;
     a.lpc = lpc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_state_update(a, dtype == SSM_DTYPE_BF16, z != nullptr, s);
+    hipError_t e = launch_state_update(a, variant_disc(variant), dtype == SSM_DTYPE_BF16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("state update launch", e);
 }
 
@@ -187,7 +194,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         fa.NW = p.fwd.NW;
         fa.chunk_len = p.fwd.chunk_len;
         fa.n_chunks = 1;
-        fa.ws_S = nullptr; fa.ws_H = nullptr;
+        fa.ws_P = nullptr; fa.ws_H = nullptr;
         fa.ws_BC = reinterpret_cast<float *>(ws + p.bc_off);
         fa.bc_lpad = p.fwd.bc_lpad;
         fa.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);

@@ -5,7 +5,9 @@
 // skill page "State Space Models Mamba", MambaBlock._selective_scan):
 //     h = exp(delta * A[d,n]) * h + delta * B[b,t,n] * x
 //     y = sum_n C[b,t,n] * h + Dskip[d] * x,   then y * silu(z) if gated
-// exp(delta * A) is evaluated as 2^(delta * A * log2(e)) with v_exp_f32.
+// exp(delta * A) is evaluated as 2^(delta * A * log2(e)) with v_exp_f32.  The
+// zero-order-hold and bilinear discretisations replace (A_bar, B_bar); see
+// ssm_discretization in ssm.h and the step helpers below.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,9 +28,10 @@ struct ScanArgs {
     float *h_last;
     void *y;
     int softplus;
+    const float *dbias = nullptr;   // [D] added to delta before the softplus, or null
     int NW;               // waves per workgroup
     int64_t chunk_len, n_chunks;
-    float *ws_S;          // [B][n_chunks-1][D]     sum of delta over a chunk
+    float *ws_P;          // [B][n_chunks-1][D][N]  product of A_bar over a chunk
     float *ws_H;          // [B][n_chunks-1][D][N]  chunk end state, then carried-in state
     float *ws_BC;         // specialised kernel: packed fp32 B/C, 64-byte line per wave and sub-block
     int64_t bc_lpad;
@@ -43,6 +46,7 @@ struct UpdArgs {
     const float *A, *Dskip;
     void *y;
     int softplus;
+    const float *dbias;   // [D] or null
     int lpc;              // lanes per channel (power of two)
 };
 
@@ -105,17 +109,78 @@ __device__ __forceinline__ float silu_f(float zv) {
     return zv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * kLog2e));
 }
 
+// ---- discretisations (the values of ssm_discretization)
+constexpr int kMamba = 0, kZOH = 1, kBilinear = 2;
+
+// Per-state constant besides A log2(e): 1/A for the zero-order hold (infinite where
+// A = 0; that state always takes the series branch of zoh_factor), A/2 for the
+// bilinear map.
+template <int DISC>
+__device__ __forceinline__ float disc_aux(float A) {
+    if constexpr (DISC == kZOH) return 1.0f / A;
+    else if constexpr (DISC == kBilinear) return 0.5f * A;
+    else return 0.0f;
+}
+
+// Zero-order hold, B_bar / B = (exp(dt A) - 1) / A, with s = dt A log2(e) and
+// e = exp(dt A) = 2^s already computed.  e - 1 cancels when |dt A| is small, so there
+// the Taylor series dt (1 + z/2 + z^2/6 + z^3/24), z = dt A, is used instead (written in
+// s: z = s ln 2).  At the switch |z| = 0.1 the series' truncation (z^4 / 120) and the
+// rounding of e relative to e - 1 (about 2^-24 / |z|) are both below 1e-6.  The
+// direct branch is one fma: e / A - 1 / A rounded once.
+__device__ __forceinline__ float zoh_factor(float dt, float s, float e, float inv_a) {
+    constexpr float k1 = 0.34657359027997264f;    // ln2 / 2
+    constexpr float k2 = 0.08007550231970023f;    // ln2^2 / 6
+    constexpr float k3 = 0.013876027166205393f;   // ln2^3 / 24
+    constexpr float kSwitch = 0.14426950408889634f;   // |z| = 0.1 in units of s
+    const float ser = dt * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(k3, s, k2), s, k1), s, 1.0f);
+    const float dir = __builtin_fmaf(e, inv_a, -inv_a);
+    return __builtin_fabsf(s) < kSwitch ? ser : dir;
+}
+
+// One state update h <- A_bar h + B_bar x for every discretisation.  u is what the
+// staging prepared per (t, d): delta * x (Mamba, bilinear) or x (zero-order hold);
+// al = A log2(e), aux = disc_aux(A); abar receives A_bar (used by the carry passes).
+// Bilinear map, with r = 1 / (1 - dt A / 2): A_bar = 2 r - 1 and B_bar = r dt B, so
+// A_bar h + B_bar x = r (2 h + dt x B) - h  (r (1 - dt A / 2) = 1 up to the rounding of r).
+template <int DISC>
+__device__ __forceinline__ float disc_step(float h, float dt, float u, float bv, float al, float aux,
+                                           float &abar) {
+    if constexpr (DISC == kBilinear) {
+        const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(-dt, aux, 1.0f));
+        abar = __builtin_fmaf(2.0f, r, -1.0f);
+        return __builtin_fmaf(r, __builtin_fmaf(2.0f, h, u * bv), -h);
+    } else if constexpr (DISC == kZOH) {
+        const float s = dt * al;
+        const float e = __builtin_amdgcn_exp2f(s);
+        abar = e;
+        return __builtin_fmaf(e, h, zoh_factor(dt, s, e, aux) * (u * bv));
+    } else {
+        const float e = __builtin_amdgcn_exp2f(dt * al);
+        abar = e;
+        return __builtin_fmaf(e, h, u * bv);
+    }
+}
+
 // Launchers (each returns the hipGetLastError() of its launch).
-hipError_t launch_scan_generic(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16,
-                               bool has_z, bool carry, hipStream_t s);
+// The scan kernels of each discretisation live in their own translation units (built in
+// parallel): *_mamba in scan_generic.hip / scan_fast.hip, *_zoh and *_bilinear in the
+// files of those names.
+#define SSM_SCAN_LAUNCHER(name)                                                               \
+    hipError_t name(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z, \
+                    bool carry, hipStream_t s)
+SSM_SCAN_LAUNCHER(launch_scan_generic_mamba);
+SSM_SCAN_LAUNCHER(launch_scan_generic_zoh);
+SSM_SCAN_LAUNCHER(launch_scan_generic_bilinear);
 // Specialised path (plan.fast): dstate == 16, dim % 64 == 0, states_per_lane 2 or 4.
-hipError_t launch_scan_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16,
-                            bool has_z, bool carry, hipStream_t s);
+SSM_SCAN_LAUNCHER(launch_scan_fast_mamba);
+SSM_SCAN_LAUNCHER(launch_scan_fast_zoh);
+SSM_SCAN_LAUNCHER(launch_scan_fast_bilinear);
 // Specialised kernel, checkpoint pass (one chunk): the state before every 8th step into ckpt.
 hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s);
 // Specialised path pre-pass: pack B/C rows into ws_BC.
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
-hipError_t launch_state_update(const UpdArgs &a, bool bf16, bool has_z, hipStream_t s);
+hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s);
 // Causal depthwise convolution (+ SiLU): sequence form and single-token form.
 hipError_t launch_conv1d_fwd(const ConvArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvArgs &a, bool bf16, hipStream_t s);

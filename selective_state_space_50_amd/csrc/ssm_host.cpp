@@ -212,8 +212,8 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     if (p.n_chunks > 1) {
         const size_t carries = static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks - 1) *
                                static_cast<size_t>(dim);
-        p.ws_S_off = 0;
-        p.ws_H_off = align_up(carries * sizeof(float), kWsAlign);
+        p.ws_P_off = 0;
+        p.ws_H_off = align_up(carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
         ws = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
     }
     if (p.fast && seqlen > 0 && batch > 0 && dim > 0) {
@@ -241,17 +241,31 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     return SSM_OK;
 }
 
+namespace {
+int check_variant(const ssm_variant *v) {
+    if (!v) return SSM_OK;
+    if (v->discretization < SSM_DISC_MAMBA || v->discretization > SSM_DISC_BILINEAR || v->reserved != 0) {
+        set_error("variant.discretization=%d must be 0, 1 or 2 and variant.reserved 0", v->discretization);
+        return SSM_EINVAL;
+    }
+    return SSM_OK;
+}
+}  // namespace
+
 int check_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
                const void *x, const void *delta, const float *A, const void *B, const void *C,
                const float *Dskip, const void *z, const float *h0, const float *h_last,
-               const void *y, int delta_softplus, const ssm_scan_opts *opts,
-               const void *workspace, size_t workspace_bytes, ScanPlan *plan) {
+               const void *y, int delta_softplus, const ssm_variant *variant,
+               const ssm_scan_opts *opts, const void *workspace, size_t workspace_bytes,
+               ScanPlan *plan) {
     int st = plan_scan(batch, seqlen, dim, dstate, dtype, opts, plan);
     if (st != SSM_OK) return st;
     if (delta_softplus != 0 && delta_softplus != 1) {
         set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
         return SSM_EINVAL;
     }
+    st = check_variant(variant);
+    if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;  // nothing to compute or store
     const int64_t es = static_cast<int64_t>(dtype_size(dtype));
     const int64_t tok = batch * seqlen * dim * es;
@@ -271,6 +285,7 @@ int check_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int d
         range("Dskip", Dskip, dim * 4), range("h0", h0, st_bytes),
         range("h_last", h_last, st_bytes), range("y", y, seqlen > 0 ? tok : 0),
         range("workspace", workspace, static_cast<int64_t>(plan->ws_bytes)),
+        range("delta_bias", variant_bias(variant), dim * 4),
     };
     const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
     st = check_aligned(all, n_all);
@@ -291,13 +306,15 @@ int check_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int d
 int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, const float *h,
                        const void *x, const void *delta, const float *A, const void *B,
                        const void *C, const float *Dskip, const void *z, const void *y,
-                       int delta_softplus) {
+                       int delta_softplus, const ssm_variant *variant) {
     int st = check_dims(batch, 1, dim, dstate, dtype);
     if (st != SSM_OK) return st;
     if (delta_softplus != 0 && delta_softplus != 1) {
         set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
         return SSM_EINVAL;
     }
+    st = check_variant(variant);
+    if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
     if (batch * dim > (int64_t(1) << 34)) {   // 16 lanes per channel at most, 256-thread blocks
         set_error("batch*dim=%lld is too large for one launch", (long long)(batch * dim));
@@ -314,7 +331,7 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
         range("delta", delta, batch * dim * es), range("z", z, batch * dim * es),
         range("B", B, batch * dstate * es),     range("C", C, batch * dstate * es),
         range("A", A, dim * dstate * 4),        range("Dskip", Dskip, dim * 4),
-        range("y", y, batch * dim * es),
+        range("y", y, batch * dim * es),        range("delta_bias", variant_bias(variant), dim * 4),
     };
     const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
     st = check_aligned(all, n_all);

@@ -23,7 +23,7 @@ struct ScanPlan {
     int64_t chunk_len = 0;
     int64_t n_chunks = 1;
     size_t ws_bytes = 0;  // workspace for chunk carries (0 when n_chunks == 1)
-    size_t ws_S_off = 0;  // byte offset of the per-chunk delta sums [B][C-1][D]
+    size_t ws_P_off = 0;  // byte offset of the per-chunk state decays [B][C-1][D][N]
     size_t ws_H_off = 0;  // byte offset of the per-chunk end states [B][C-1][D][N]
     size_t ws_BC_off = 0; // specialised kernel: byte offset of the packed fp32 B/C rows
     int64_t bc_lpad = 0;  // specialised kernel: steps per chunk in the packed B/C rows (multiple of 16)
@@ -45,14 +45,19 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
 int check_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
                const void *x, const void *delta, const float *A, const void *B, const void *C,
                const float *Dskip, const void *z, const float *h0, const float *h_last,
-               const void *y, int delta_softplus, const ssm_scan_opts *opts,
-               const void *workspace, size_t workspace_bytes, ScanPlan *plan);
+               const void *y, int delta_softplus, const ssm_variant *variant,
+               const ssm_scan_opts *opts, const void *workspace, size_t workspace_bytes,
+               ScanPlan *plan);
 
 // Full argument check of ssm_state_update.
 int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, const float *h,
                        const void *x, const void *delta, const float *A, const void *B,
                        const void *C, const float *Dskip, const void *z, const void *y,
-                       int delta_softplus);
+                       int delta_softplus, const ssm_variant *variant);
+
+// The discretisation of a variant (NULL = SSM_DISC_MAMBA) and its delta bias.
+inline int variant_disc(const ssm_variant *v) { return v ? v->discretization : SSM_DISC_MAMBA; }
+inline const float *variant_bias(const ssm_variant *v) { return v ? v->delta_bias : nullptr; }
 
 // Workspace of ssm_scan_bwd: packed B/C and state checkpoints of the forward
 // checkpoint pass, per-workgroup shares of dB/dC, per-batch-row shares of dA/dD.

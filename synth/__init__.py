@@ -20,6 +20,8 @@ the MambaBlock listing of the skillsdirectory "State Space Models Mamba" page):
   that no structure across n holds
 * Dskip = ones, or N(1, 0.1)                     [D]
 * h0 ~ N(0, 1) when requested                    [B, D, N]  fp32
+* delta bias ~ N(0, 0.5) when requested          [D]  fp32 (the bias of the map that
+  produces delta; it scales the softplus step size by about e^bias)
 
 Every [B, L, *] tensor is drawn in fixed blocks of ``BLOCK_ROWS`` rows of the
 flattened (B*L) axis, each block from its own PCG64 stream keyed by
@@ -34,7 +36,7 @@ import numpy as np
 
 BLOCK_ROWS = 4096
 
-_TENSOR_IDS = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "h0": 8}
+_TENSOR_IDS = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "h0": 8, "dbias": 9}
 
 DELTA_MIN = 1e-3
 DELTA_MAX = 1e-1
@@ -130,6 +132,11 @@ def make_D(seed: int, dim: int, d_kind: str = "ones") -> np.ndarray:
         g = _rng(seed, "D", 0)
         return (1.0 + 0.1 * g.standard_normal(dim)).astype(np.float32)
     raise ValueError(d_kind)
+
+
+def make_delta_bias(seed: int, dim: int) -> np.ndarray:
+    g = _rng(seed, "dbias", 0)
+    return (0.5 * g.standard_normal(dim)).astype(np.float32)
 
 
 def make_h0(seed: int, batch: int, dim: int, dstate: int) -> np.ndarray:

@@ -30,8 +30,31 @@ int main() {
     float *h0 = static_cast<float *>(P(base + 8 * gap)), *hl = static_cast<float *>(P(base + 10 * gap));
     auto scan = [&](int64_t b, int64_t l, int64_t d, int64_t n, int dt, const void *x_, const void *y_,
                     const ssm_scan_opts *o, const void *w, size_t wb, const float *h0_, const float *hl_) {
-        return check_scan(b, l, d, n, dt, x_, dl, A, B, C, Dk, z, h0_, hl_, y_, 0, o, w, wb, &p);
+        return check_scan(b, l, d, n, dt, x_, dl, A, B, C, Dk, z, h0_, hl_, y_, 0, nullptr, o, w, wb, &p);
     };
+    // discretisation variants and the delta bias
+    {
+        float *bias = static_cast<float *>(P(base + 11 * gap));
+        const ssm_variant ok1{SSM_DISC_ZOH, 0, bias}, ok2{SSM_DISC_BILINEAR, 0, nullptr};
+        const ssm_variant bad1{3, 0, nullptr}, bad2{-1, 0, nullptr}, bad3{SSM_DISC_ZOH, 1, nullptr};
+        const ssm_variant mis{SSM_DISC_MAMBA, 0, static_cast<float *>(P(base + 11 * gap + 4))};
+        const ssm_variant ovl{SSM_DISC_MAMBA, 0, static_cast<float *>(y)};
+        auto sv = [&](const ssm_variant *v) {
+            return check_scan(4, 256, 4096, 16, 1, x, dl, A, B, C, Dk, z, h0, hl, y, 1, v, nullptr, ws,
+                              size_t(1) << 30, &p);
+        };
+        EXPECT(sv(&ok1) == SSM_OK);
+        EXPECT(sv(&ok2) == SSM_OK);
+        EXPECT(sv(&bad1) == SSM_EINVAL);
+        EXPECT(sv(&bad2) == SSM_EINVAL);
+        EXPECT(sv(&bad3) == SSM_EINVAL);
+        EXPECT(sv(&mis) == SSM_EINVAL);
+        EXPECT(std::strstr(ssm_last_error(), "delta_bias") != nullptr);
+        EXPECT(sv(&ovl) == SSM_EINVAL);
+        EXPECT(check_state_update(256, 4096, 16, 1, h0, x, dl, A, B, C, Dk, z, y, 0, &ok1) == SSM_OK);
+        EXPECT(check_state_update(256, 4096, 16, 1, h0, x, dl, A, B, C, Dk, z, y, 0, &bad1) == SSM_EINVAL);
+        EXPECT(check_state_update(256, 4096, 16, 1, h0, x, dl, A, B, C, Dk, z, y, 0, &mis) == SSM_EINVAL);
+    }
     // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
@@ -55,6 +78,7 @@ int main() {
     ssm_scan_opts o{1024, 0, 0, 0, 0};
     EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
     EXPECT(p.n_chunks == 8 && p.ws_bytes > 0 && p.ws_BC_off > p.ws_H_off && p.bc_lpad == 1024);
+    EXPECT(p.ws_P_off == 0 && p.ws_H_off == size_t(7) * 1024 * 16 * 4);   // per-state chunk decays, then end states
     const size_t need = p.ws_bytes;
     EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, ws, need - 1, h0, hl) == SSM_EWORKSPACE);
     EXPECT(scan(1, 8192, 1024, 16, 1, x, y, &o, ws, need, h0, hl) == SSM_OK);
@@ -84,13 +108,13 @@ int main() {
         }
     // state update
     float *h = h0;
-    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 0) == SSM_OK);
-    EXPECT(check_state_update(256, 4096, 16, 1, nullptr, x, dl, A, B, C, Dk, z, y, 0) == SSM_EINVAL);
-    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, x, 0) == SSM_EINVAL);
-    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 2) == SSM_EINVAL);
-    EXPECT(check_state_update(256, 4096, 32, 1, h, x, dl, A, B, C, Dk, z, y, 0) == SSM_EUNSUPPORTED);
+    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_OK);
+    EXPECT(check_state_update(256, 4096, 16, 1, nullptr, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_EINVAL);
+    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, x, 0, nullptr) == SSM_EINVAL);
+    EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 2, nullptr) == SSM_EINVAL);
+    EXPECT(check_state_update(256, 4096, 32, 1, h, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_EUNSUPPORTED);
     EXPECT(check_state_update(0, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                              nullptr, nullptr, nullptr, 0) == SSM_OK);
+                              nullptr, nullptr, nullptr, 0, nullptr) == SSM_OK);
     EXPECT(std::strcmp(ssm_status_str(SSM_EWORKSPACE), "workspace too small") == 0);
     std::printf("%s: %d failure(s)\n", fails ? "FAILED" : "ok", fails);
     return fails ? 1 : 0;

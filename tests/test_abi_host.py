@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_text(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     assert lib.ssm_status_str(0) == b"ok"
     assert lib.ssm_status_str(3) == b"workspace too small"
 
@@ -54,12 +54,13 @@ G4 = 1 << 32   # fake device addresses 4 GiB apart; never dereferenced
 
 
 def _scan_status(lib, *, B=1, L=8, D=64, N=16, dtype=1, x=G4, y=2 * G4, ws=None,
-                 ws_bytes=0, opts=None, softplus=0):
+                 ws_bytes=0, opts=None, softplus=0, variant=None):
     base = 1 << 40
     V = ctypes.c_void_p
     return lib.ssm_scan_fwd(B, L, D, N, dtype, V(base + x), V(base + 3 * G4), V(base + 4 * G4),
                             V(base + 5 * G4), V(base + 6 * G4), None, None, None, None,
                             V(base + y) if y is not None else None, softplus,
+                            ctypes.byref(variant) if variant else None,
                             ctypes.byref(opts) if opts else None, ws, ws_bytes, None)
 
 
@@ -79,9 +80,17 @@ def test_validation_rejects_before_launch(lib):
     assert _scan_status(lib, L=16, D=64) == 3        # packed B/C rows need a workspace
     assert _scan_status(lib, opts=ssm.ScanOpts(0, 3, 0, 0, 0)) == 1
     assert _scan_status(lib, opts=ssm.ScanOpts(0, 0, 0, 0, 7)) == 1
+    # discretisation variants: bad enum, nonzero reserved word, misaligned delta bias
+    assert _scan_status(lib, variant=ssm.Variant(3, 0, None)) == 1
+    assert _scan_status(lib, variant=ssm.Variant(1, 1, None)) == 1
+    assert _scan_status(lib, variant=ssm.Variant(2, 0, (1 << 40) + 7 * G4 + 4)) == 1
+    assert b"delta_bias" in lib.ssm_last_error()
     V = ctypes.c_void_p
     assert lib.ssm_state_update(4, 64, 16, 1, None, V(1 << 40), V(1 << 41), V(1 << 42), V(1 << 43),
-                                V(1 << 44), None, None, V(1 << 45), 0, None) == 1
+                                V(1 << 44), None, None, V(1 << 45), 0, None, None) == 1
+    assert lib.ssm_state_update(4, 64, 16, 1, V(1 << 39), V(1 << 40), V(1 << 41), V(1 << 42),
+                                V(1 << 43), V(1 << 44), None, None, V(1 << 45), 0,
+                                ctypes.byref(ssm.Variant(7, 0, None)), None) == 1
 
 
 def test_binding_refuses_cpu_tensors(lib):
