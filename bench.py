@@ -93,6 +93,8 @@ def main():
                     help="only run this many decode steps of h[256,4096,16] (for rocprofv3)")
     ap.add_argument("--profile-conv", type=int, default=0, metavar="CALLS",
                     help="only run this many conv1d calls at the headline shape (for rocprofv3)")
+    ap.add_argument("--profile-variant", choices=("zoh", "bilinear"), default=None,
+                    help="with --profile-run: time this discretisation instead of the Mamba one")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -161,8 +163,10 @@ def main():
         if plan["workspace_bytes"]:
             ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
 
+        disc = args.profile_variant if args.profile_run and args.profile_variant else "mamba"
+
         def step():
-            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws)
+            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
 
         for _ in range(args.warmup):
             step()
