@@ -36,7 +36,8 @@ import numpy as np
 
 BLOCK_ROWS = 4096
 
-_TENSOR_IDS = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "h0": 8, "dbias": 9}
+_TENSOR_IDS = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "h0": 8, "dbias": 9,
+               "ssd_A": 10}
 
 DELTA_MIN = 1e-3
 DELTA_MAX = 1e-1
@@ -168,6 +169,43 @@ def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str, seed
         "shape": (batch, seqlen, dim, dstate),
     }
     return out
+
+
+def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, dtype: str,
+               seed: int, gate: bool = False, softplus_input: bool = False, h0: bool = False,
+               delta_bias: bool = False) -> dict:
+    """Inputs of one multi-head SSD (Mamba-2 layer) scan, in storage form.
+
+    x, z [B, L, H, P] and B, C [B, L, N] ~ N(0, 1); delta [B, L, H] log-uniform in
+    [1e-3, 1e-1] (one step per head; u = log(expm1(delta)) in softplus mode); A [H]
+    float32 = -exp(U[log 1, log 16]) (one decay rate per head, the range Mamba-2
+    initialises A in); Dskip [H] ~ N(1, 0.1); h0 [B, H, P, N] ~ N(0, 1) float32;
+    delta_bias [H] ~ N(0, 0.5) (softplus mode) or 0.05 |N(0, 0.5)|.
+    """
+    rows = batch * seqlen
+    g = _rng(seed, "ssd_A", 0)
+    A = (-np.exp(g.uniform(0.0, np.log(16.0), nheads))).astype(np.float32)
+    bias = None
+    if delta_bias:
+        bias = make_delta_bias(seed, nheads)
+        if not softplus_input:
+            bias = (0.05 * np.abs(bias)).astype(np.float32)
+    return {
+        "x": token_rows(seed, "x", 0, rows, nheads * headdim, dtype).reshape(batch, seqlen, nheads, headdim),
+        "delta": token_rows(seed, "delta", 0, rows, nheads, dtype, softplus_input).reshape(batch, seqlen, nheads),
+        "z": (token_rows(seed, "z", 0, rows, nheads * headdim, dtype).reshape(batch, seqlen, nheads, headdim)
+              if gate else None),
+        "B": token_rows(seed, "B", 0, rows, dstate, dtype).reshape(batch, seqlen, dstate),
+        "C": token_rows(seed, "C", 0, rows, dstate, dtype).reshape(batch, seqlen, dstate),
+        "A": A,
+        "Dskip": make_D(seed, nheads, "normal"),
+        "h0": (_rng(seed, "h0", 0).standard_normal((batch, nheads, headdim, dstate), dtype=np.float32)
+               if h0 else None),
+        "delta_bias": bias,
+        "dtype": dtype,
+        "delta_softplus": bool(softplus_input),
+        "shape": (batch, seqlen, nheads, headdim, dstate),
+    }
 
 
 # The five workloads: (name, batch, seqlen, dim, dstate, dtype, gate, d_kind)

@@ -1,0 +1,195 @@
+"""Pins of the multi-head SSD (Mamba-2 layer) oracle, ``oracle/ssd_oracle.py``.
+
+None of them restates the oracle's loop:
+
+* the S6 oracle in C (pinned on its own by the worked example, the convolution view,
+  brute-force unrolling, ...) run on the H * P channels with A[d, n] = a_h for every
+  state and the head's step size broadcast over its channels;
+* the structured-matrix ("dual", attention-like) form the brentwoodlivery page names:
+  y = M x with M[t, s] = (C_t . B_s) exp(a (cum_t - cum_s)) dt_s for s <= t, built as a
+  dense matrix by brute force;
+* a = 0: the state is the running sum of dt_s x_s B_s^T, a closed form;
+* splitting the sequence and carrying the state; heads are independent of each other;
+* planted mistakes in a copy of the oracle each fail one of the above.
+"""
+from __future__ import annotations
+
+import inspect
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import ssd_oracle
+
+
+def _problem(seed, Bsz=2, L=20, H=3, P=4, N=5, gate=False, softplus=False, bias=False, h0=True):
+    rng = np.random.default_rng(seed)
+    p = {
+        "x": rng.standard_normal((Bsz, L, H, P)),
+        "delta": np.exp(rng.uniform(np.log(1e-3), np.log(0.5), (Bsz, L, H))),
+        "a": -np.exp(rng.uniform(0.0, np.log(16.0), H)),
+        "Bm": rng.standard_normal((Bsz, L, N)),
+        "Cm": rng.standard_normal((Bsz, L, N)),
+        "D": rng.normal(1.0, 0.1, H),
+        "z": rng.standard_normal((Bsz, L, H, P)) if gate else None,
+        "h0": rng.standard_normal((Bsz, H, P, N)) if h0 else None,
+        "bias": rng.normal(0.0, 0.3, H) if bias else None,
+    }
+    if softplus:
+        p["delta"] = np.log(np.expm1(p["delta"]))
+    return p
+
+
+def _run(p, fn=None, softplus=False):
+    fn = fn or ssd_oracle.ssd
+    return fn(p["x"], p["delta"], p["a"], p["Bm"], p["Cm"], p["D"], p["z"], p["h0"], softplus, p["bias"])
+
+
+def _via_s6(p, softplus=False):
+    """The S6 C oracle on channels d = h * P + p."""
+    x, dl, a = p["x"], p["delta"], p["a"]
+    Bsz, L, H, P = x.shape
+    N = p["Bm"].shape[2]
+    D = H * P
+    xs = x.reshape(Bsz, L, D)
+    ds = np.repeat(dl, P, axis=2)
+    A = np.repeat(a, P)[:, None] * np.ones((1, N))
+    Dk = np.repeat(p["D"], P)
+    zs = None if p["z"] is None else p["z"].reshape(Bsz, L, D)
+    bias = None if p["bias"] is None else np.repeat(p["bias"], P)
+    h0 = None if p["h0"] is None else p["h0"].reshape(Bsz, D, N)
+    cb, cd = np.meshgrid(np.arange(Bsz), np.arange(D), indexing="ij")
+    cb, cd = cb.reshape(-1), cd.reshape(-1)
+    ser = lambda t: None if t is None else t[cb, :, cd]
+    y, hl = oracle.scan_f64(ser(xs), ser(ds), A, p["Bm"], p["Cm"], Dk, ser(zs),
+                            None if h0 is None else h0[cb, cd, :], softplus, cb, cd, 1, "mamba", bias)
+    return (y.reshape(Bsz, D, L).transpose(0, 2, 1).reshape(Bsz, L, H, P),
+            hl.reshape(Bsz, H, P, N))
+
+
+def _dual(p):
+    """y = M x with M[t, s] = (C_t . B_s) exp(a (cum_t - cum_s)) dt_s (s <= t), plus the
+    start state's share exp(a cum_t) C_t . H0[p, :] and D x.  No gate, no softplus."""
+    x, dl, a, Bm, Cm = p["x"], p["delta"], p["a"], p["Bm"], p["Cm"]
+    Bsz, L, H, P = x.shape
+    y = np.zeros((Bsz, L, H, P))
+    for b in range(Bsz):
+        CB = Cm[b] @ Bm[b].T                                          # [L, L]
+        for h in range(H):
+            cum = np.cumsum(dl[b, :, h])
+            M = np.zeros((L, L))
+            for t in range(L):
+                for s in range(t + 1):
+                    M[t, s] = CB[t, s] * np.exp(a[h] * (cum[t] - cum[s])) * dl[b, s, h]
+            y[b, :, h, :] = M @ x[b, :, h, :]
+            if p["h0"] is not None:
+                y[b, :, h, :] += np.exp(a[h] * cum)[:, None] * (Cm[b] @ p["h0"][b, h].T)
+            y[b, :, h, :] += p["D"][h] * x[b, :, h, :]
+    return y
+
+
+@pytest.mark.parametrize("gate,softplus,bias", [(False, False, False), (True, False, False),
+                                                (True, True, True), (False, True, False)])
+def test_equals_s6_with_a_scalar_decay_per_head(gate, softplus, bias):
+    p = _problem(1, gate=gate, softplus=softplus, bias=bias)
+    y, h = _run(p, softplus=softplus)
+    yr, hr = _via_s6(p, softplus)
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(h, hr, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("h0", [False, True])
+def test_structured_matrix_form(h0):
+    p = _problem(2, L=24, h0=h0)
+    y, _ = _run(p)
+    np.testing.assert_allclose(y, _dual(p), rtol=1e-11, atol=1e-12)
+
+
+def test_no_decay_is_a_running_sum():
+    p = _problem(3)
+    p["a"][:] = 0.0
+    y, h = _run(p)
+    x, dl, Bm, Cm = p["x"], p["delta"], p["Bm"], p["Cm"]
+    drive = np.einsum("blh,blhp,bln->blhpn", dl, x, Bm)
+    states = p["h0"][:, None] + np.cumsum(drive, axis=1)              # [B, L, H, P, N]
+    yr = np.einsum("blhpn,bln->blhp", states, Cm) + p["D"][None, None, :, None] * x
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(h, states[:, -1], rtol=1e-12, atol=1e-12)
+
+
+def test_split_and_carry():
+    p = _problem(4, L=30, gate=True)
+    y, h = _run(p)
+    T = 13
+    first = {k: (v[:, :T] if k in ("x", "delta", "Bm", "Cm", "z") and v is not None else v) for k, v in p.items()}
+    second = {k: (v[:, T:] if k in ("x", "delta", "Bm", "Cm", "z") and v is not None else v) for k, v in p.items()}
+    y1, h1 = _run(first)
+    second["h0"] = h1
+    y2, h2 = _run(second)
+    np.testing.assert_array_equal(np.concatenate([y1, y2], axis=1), y)
+    np.testing.assert_array_equal(h2, h)
+
+
+def test_heads_are_independent():
+    p = _problem(5, H=4)
+    y, h = _run(p)
+    perm = np.array([2, 0, 3, 1])
+    q = dict(p)
+    q["x"], q["delta"], q["a"], q["D"] = p["x"][:, :, perm], p["delta"][:, :, perm], p["a"][perm], p["D"][perm]
+    q["h0"] = p["h0"][:, perm]
+    yq, hq = _run(q)
+    np.testing.assert_allclose(yq, y[:, :, perm], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(hq, h[:, perm], rtol=1e-14, atol=0)
+
+
+def test_storage_wrapper():
+    inp = synth.ssd_inputs(2, 9, 3, 4, 5, "bf16", seed=6, gate=True, softplus_input=True, h0=True,
+                           delta_bias=True)
+    y, h = ssd_oracle.ssd_storage(inp)
+    w = lambda t: synth.to_f64(t, "bf16")
+    yr, hr = ssd_oracle.ssd(w(inp["x"]), w(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["Dskip"],
+                            w(inp["z"]), inp["h0"], True, inp["delta_bias"])
+    np.testing.assert_array_equal(y, yr)
+    ys, hs = ssd_oracle.ssd_storage(inp, batches=[1], heads=[2, 0])
+    np.testing.assert_array_equal(ys, y[[1]][:, :, [2, 0]])
+    np.testing.assert_array_equal(hs, h[[1]][:, [2, 0]])
+
+
+_MUTANTS = {
+    "b_bar_without_dt": ("drive = (step[:, :, None] * x[:, t, :, :])", "drive = (x[:, t, :, :])"),
+    "decay_without_dt": ("decay = np.exp(step * a[None, :])", "decay = np.exp(a[None, :] + 0.0 * step)"),
+    "readout_before_update": ("state = decay * state + drive                                 # [B, H, P, N]\n        yt = np.einsum(\"bhpn,bn->bhp\", state, Cm[:, t, :])",
+                              "yt = np.einsum(\"bhpn,bn->bhp\", state, Cm[:, t, :])\n        state = decay * state + drive"),
+    "step_of_head_zero": ("step = dt[:, t, :]  ", "step = np.repeat(dt[:, t, :1], dt.shape[2], axis=1)  "),
+    "skip_dropped": ("yt = yt + np.asarray(D, dtype=np.float64)[None, :, None] * x[:, t, :, :]", "yt = yt"),
+    "gate_sigmoid": ("yt = yt * _silu(", "yt = yt * (lambda v: 1.0 / (1.0 + np.exp(-v)))("),
+}
+
+
+def _mutated(kind):
+    src = inspect.getsource(ssd_oracle.ssd)
+    old, new = _MUTANTS[kind]
+    assert old in src, kind
+    ns = dict(vars(ssd_oracle))
+    exec(src.replace(old, new), ns)
+    return ns["ssd"]
+
+
+@pytest.mark.parametrize("kind", sorted(_MUTANTS))
+def test_planted_mistake_is_caught(kind):
+    fn = _mutated(kind)
+    p = _problem(7, gate=True)
+    y, _ = _run(p, fn=fn)
+    yr, _ = _via_s6(p)
+    assert np.max(np.abs(y - yr)) > 1e-6, f"mutant {kind} passes the pin"
+
+
+def test_unmutated_copy_passes():
+    ns = dict(vars(ssd_oracle))
+    exec(inspect.getsource(ssd_oracle.ssd), ns)
+    p = _problem(7, gate=True)
+    y, _ = _run(p, fn=ns["ssd"])
+    yr, _ = _via_s6(p)
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-13)
