@@ -274,6 +274,35 @@ int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, void
                       const void *x, const float *w, const float *bias, void *y, int silu,
                       void *stream);
 
+/*
+ * Multi-head SSD scan: the state space model of a Mamba-2 layer (managen.ai, "Mamba:
+ * State Space Models Challenge Transformers", Mamba2Block: heads of d_head = 64
+ * channels, d_state = 128; brentwoodlivery, "State-space models (Mamba, S4)", section
+ * "Mamba 2 and Hybrid Architectures": the SSM as a structured matrix multiplication).
+ * For every batch row b, head h, channel p < headdim and state n < dstate:
+ *
+ *     dt       = delta[b,t,h] (+ delta_bias[h]; log(1 + exp(.)) of it when delta_softplus)
+ *     S[p,n]   = exp(dt * A[h]) * S[p,n] + dt * B[b,t,n] * x[b,t,h,p]
+ *     y[b,t,h,p] = sum_n C[b,t,n] * S[p,n] + Dskip[h] * x[b,t,h,p],  then * silu(z) if gated
+ *
+ * i.e. the recurrence of ssm_scan_fwd with one step size and one scalar decay per
+ * head, and B, C shared by every head.
+ *
+ *   x, z      [batch, seqlen, nheads, headdim]  bf16   z NULL = no gate
+ *   delta     [batch, seqlen, nheads]           bf16
+ *   A, Dskip, delta_bias  [nheads]              fp32   Dskip, delta_bias may be NULL
+ *   B, C      [batch, seqlen, dstate]           bf16
+ *   h0, h_last [batch, nheads, headdim, dstate] fp32   NULL = zero start / not stored
+ *   y         [batch, seqlen, nheads, headdim]  bf16   output; must not overlap an input
+ *
+ * Supported: headdim 64, dstate 128, bf16 (else SSM_EUNSUPPORTED).  No workspace.
+ * seqlen == 0 stores h0 (or zeros) in h_last; batch or nheads == 0 is a no-op.
+ */
+int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int dtype, const void *x, const void *delta, const float *A, const void *B,
+                const void *C, const float *Dskip, const void *z, const float *delta_bias,
+                const float *h0, float *h_last, void *y, int delta_softplus, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,12 +92,12 @@ def ssd_storage(inp: dict, batches=None, heads=None):
     dt = inp["dtype"]
     bs = slice(None) if batches is None else np.asarray(batches)
     hs = slice(None) if heads is None else np.asarray(heads)
-    pick4 = lambda t: None if t is None else _widen(t, dt)[bs][:, :, hs]
-    x = pick4(inp["x"])
-    z = pick4(inp.get("z"))
-    delta = _widen(inp["delta"], dt)[bs][:, :, hs]
-    Bm = _widen(inp["B"], dt)[bs]
-    Cm = _widen(inp["C"], dt)[bs]
+    pick = lambda t: None if t is None else _widen(np.asarray(t)[bs][:, :, hs], dt)
+    x = pick(inp["x"])
+    z = pick(inp.get("z"))
+    delta = pick(inp["delta"])
+    Bm = _widen(np.asarray(inp["B"])[bs], dt)
+    Cm = _widen(np.asarray(inp["C"])[bs], dt)
     a = np.asarray(inp["A"], dtype=np.float64)[hs]
     D = None if inp.get("Dskip") is None else np.asarray(inp["Dskip"], dtype=np.float64)[hs]
     bias = None if inp.get("delta_bias") is None else np.asarray(inp["delta_bias"], dtype=np.float64)[hs]

@@ -91,6 +91,8 @@ def lib():
     L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, P, SZ, P]
     L.ssm_conv1d_fwd.restype = I32
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
+    L.ssm_ssd_fwd.restype = I32
+    L.ssm_ssd_fwd.argtypes = [I64, I64, I64, I64, I64, I32] + [P] * 11 + [I32, P]
     L.ssm_conv1d_update.restype = I32
     L.ssm_conv1d_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, I32, P]
     if L.ssm_abi_version() != ABI_VERSION:
@@ -390,3 +392,42 @@ def conv1d_update(state, x, w, bias=None, *, silu=True, out=None, stream=None):
                                    _ptr(out), int(bool(silu)), ctypes.c_void_p(s.cuda_stream)),
            "ssm_conv1d_update")
     return out
+
+
+def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False, delta_bias=None,
+            return_last_state=False, out=None, h_last=None, stream=None):
+    """Multi-head SSD scan (the Mamba-2 layer's state space model) on the GPU.
+
+    x, z: [B, L, H, 64] bf16;  delta: [B, L, H] bf16;  A, D, delta_bias: [H] fp32;
+    B, C: [B, L, 128] bf16;  h0: [B, H, 64, 128] fp32.  Returns y [B, L, H, 64] (bf16),
+    or (y, h_last) when return_last_state.
+    """
+    import torch
+    if x.dim() != 4 or A.dim() != 1:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim] and A [nheads]")
+    Bsz, L, H, P = x.shape
+    N = B.shape[-1]
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd runs on the GPU only; tensors must be on a cuda device")
+    _need(delta, "delta", (Bsz, L, H), dt, dev)
+    _need(z, "z", (Bsz, L, H, P), dt, dev)
+    _need(B, "B", (Bsz, L, N), dt, dev)
+    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (H,), torch.float32, dev)
+    _need(h0, "h0", (Bsz, H, P, N), torch.float32, dev)
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, L, H, P), dt, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=dev)
+    _need(h_last, "h_last", (Bsz, H, P, N), torch.float32, dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_ssd_fwd(Bsz, L, H, P, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(h_last), _ptr(out),
+                           int(bool(delta_softplus)), ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_ssd_fwd")
+    return (out, h_last) if return_last_state else out

@@ -253,3 +253,31 @@ extern "C" int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int 
     hipError_t e = launch_conv1d_update(a, dtype == SSM_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : hip_fail("conv1d update launch", e);
 }
+
+extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                           int dtype, const void *x, const void *delta, const float *A, const void *B,
+                           const void *C, const float *Dskip, const void *z, const float *delta_bias,
+                           const float *h0, float *h_last, void *y, int delta_softplus, void *stream) {
+    using namespace ssm;
+    clear_error();
+    int st = check_ssd(batch, seqlen, nheads, headdim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias,
+                       h0, h_last, y, delta_softplus);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || nheads == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_last) return SSM_OK;
+        const int64_t n = batch * nheads * headdim * dstate;
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                           h_last, h0, n);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
+    }
+    SsdArgs a;
+    a.B = batch; a.L = seqlen; a.H = nheads;
+    a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;
+    a.A = A; a.Dskip = Dskip; a.dbias = delta_bias; a.h0 = h0; a.h_last = h_last; a.y = y;
+    a.softplus = delta_softplus;
+    hipError_t e = launch_ssd(a, s);
+    return e == hipSuccess ? SSM_OK : hip_fail("ssd launch", e);
+}

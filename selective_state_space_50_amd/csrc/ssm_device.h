@@ -64,6 +64,16 @@ struct BwdArgs {
     float *partD;         // [B][8][D] per-(row, wave) shares of dD
 };
 
+struct SsdArgs {
+    int64_t B, L, H;         // batch, sequence length, heads (head dim 64, state size 128)
+    const void *x, *delta, *z, *Bm, *Cm;   // x, z [B, L, H, 64]; delta [B, L, H]; B, C [B, L, 128]
+    const float *A, *Dskip, *dbias;         // [H] each (Dskip, dbias may be null)
+    const float *h0;         // [B, H, 64, 128] or null
+    float *h_last;           // [B, H, 64, 128] or null
+    void *y;                 // [B, L, H, 64]
+    int softplus;
+};
+
 struct ConvArgs {
     int64_t B, L, D;
     int W;                   // filter width (1..4)
@@ -184,6 +194,8 @@ hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z
 // Causal depthwise convolution (+ SiLU): sequence form and single-token form.
 hipError_t launch_conv1d_fwd(const ConvArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvArgs &a, bool bf16, hipStream_t s);
+// Multi-head SSD scan (bf16, head dim 64, state size 128): one workgroup per (batch row, head).
+hipError_t launch_ssd(const SsdArgs &a, hipStream_t s);
 // Backward pass (dstate == 16, dim % 64 == 0).
 hipError_t launch_scan_bwd(const BwdArgs &a, bool bf16, bool has_z, hipStream_t s);
 

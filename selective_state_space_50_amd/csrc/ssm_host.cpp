@@ -500,6 +500,59 @@ int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, co
     return check_no_overlap(all + 3, 2, all, 5);
 }
 
+int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+              const void *x, const void *delta, const float *A, const void *B, const void *C,
+              const float *Dskip, const void *z, const float *delta_bias, const float *h0,
+              const float *h_last, const void *y, int delta_softplus) {
+    if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16) {
+        set_error("dtype %d is neither SSM_DTYPE_F32 (0) nor SSM_DTYPE_BF16 (1)", dtype);
+        return SSM_EINVAL;
+    }
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1) {
+        set_error("bad size (batch=%lld seqlen=%lld nheads=%lld headdim=%lld dstate=%lld)", (long long)batch,
+                  (long long)seqlen, (long long)nheads, (long long)headdim, (long long)dstate);
+        return SSM_EINVAL;
+    }
+    if (delta_softplus != 0 && delta_softplus != 1) {
+        set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
+        return SSM_EINVAL;
+    }
+    if (headdim != 64 || dstate != 128 || dtype != SSM_DTYPE_BF16) {
+        set_error("the SSD scan supports headdim 64, dstate 128 and bf16 (got %lld, %lld, dtype %d)",
+                  (long long)headdim, (long long)dstate, dtype);
+        return SSM_EUNSUPPORTED;
+    }
+    if (batch > 0 && seqlen > 0 && nheads > 0 &&
+        (seqlen > kMaxElems / batch || nheads * headdim > kMaxElems / (batch * seqlen))) {
+        set_error("tensor of %lld x %lld x %lld x %lld elements is too large", (long long)batch,
+                  (long long)seqlen, (long long)nheads, (long long)headdim);
+        return SSM_EINVAL;
+    }
+    if (batch * nheads > (int64_t(1) << 31)) {
+        set_error("batch*nheads=%lld exceeds one launch", (long long)(batch * nheads));
+        return SSM_EUNSUPPORTED;
+    }
+    if (batch == 0 || nheads == 0) return SSM_OK;
+    const char *missing = !A ? "A" : (seqlen > 0 && !x) ? "x" : (seqlen > 0 && !delta) ? "delta"
+                        : (seqlen > 0 && !B) ? "B" : (seqlen > 0 && !C) ? "C" : (seqlen > 0 && !y) ? "y" : nullptr;
+    if (missing) {
+        set_error("required pointer %s is NULL", missing);
+        return SSM_EINVAL;
+    }
+    const int64_t tok = batch * seqlen * nheads * headdim * 2;
+    const int64_t st_bytes = batch * nheads * headdim * dstate * 4;
+    Range all[] = {
+        range("x", x, tok), range("delta", delta, batch * seqlen * nheads * 2), range("A", A, nheads * 4),
+        range("B", B, batch * seqlen * dstate * 2), range("C", C, batch * seqlen * dstate * 2),
+        range("Dskip", Dskip, nheads * 4), range("z", z, tok), range("delta_bias", delta_bias, nheads * 4),
+        range("h0", h0, st_bytes), range("h_last", h_last, st_bytes), range("y", y, seqlen > 0 ? tok : 0),
+    };
+    const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
+    int st = check_aligned(all, n_all);
+    if (st != SSM_OK) return st;
+    return check_no_overlap(all + 9, 2, all, n_all);   // h_last, y
+}
+
 }  // namespace ssm
 
 extern "C" {

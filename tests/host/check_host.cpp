@@ -115,6 +115,24 @@ int main() {
     EXPECT(check_state_update(256, 4096, 32, 1, h, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_EUNSUPPORTED);
     EXPECT(check_state_update(0, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                               nullptr, nullptr, nullptr, 0, nullptr) == SSM_OK);
+    // multi-head SSD scan
+    {
+        const float *bias = static_cast<const float *>(P(base + 11 * gap));
+        auto sd = [&](int64_t b, int64_t l, int64_t hh, int64_t pd, int64_t n, int dt, const void *y_, const float *hl_) {
+            return check_ssd(b, l, hh, pd, n, dt, x, dl, A, B, C, Dk, z, bias, h0, hl_, y_, 1);
+        };
+        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, hl) == SSM_OK);
+        EXPECT(sd(4, 4096, 64, 32, 128, SSM_DTYPE_BF16, y, hl) == SSM_EUNSUPPORTED);
+        EXPECT(sd(4, 4096, 64, 64, 16, SSM_DTYPE_BF16, y, hl) == SSM_EUNSUPPORTED);
+        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_F32, y, hl) == SSM_EUNSUPPORTED);
+        EXPECT(sd(4, 4096, 64, 64, 128, 7, y, hl) == SSM_EINVAL);
+        EXPECT(sd(-1, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, hl) == SSM_EINVAL);
+        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, nullptr, hl) == SSM_EINVAL);
+        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, P(base + 16), hl) == SSM_EINVAL);   // overlaps x
+        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, h0) == SSM_EINVAL);            // h_last on h0
+        EXPECT(sd(0, 4096, 64, 64, 128, SSM_DTYPE_BF16, nullptr, nullptr) == SSM_OK);
+        EXPECT(check_ssd(4, 16, 64, 64, 128, 1, x, dl, A, B, C, Dk, z, bias, h0, hl, y, 2) == SSM_EINVAL);
+    }
     EXPECT(std::strcmp(ssm_status_str(SSM_EWORKSPACE), "workspace too small") == 0);
     std::printf("%s: %d failure(s)\n", fails ? "FAILED" : "ok", fails);
     return fails ? 1 : 0;
