@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import math
 import json
 import os
 import platform
@@ -33,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0   # dense bf16 matrix-core peak
 # VALU issue slots per second with packed FP32 off: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 # Algorithmic VALU slots per state update: mul (delta*A), v_exp_f32 (2 slots: it issues at
@@ -93,6 +95,8 @@ def main():
                     help="only run this many decode steps of h[256,4096,16] (for rocprofv3)")
     ap.add_argument("--profile-conv", type=int, default=0, metavar="CALLS",
                     help="only run this many conv1d calls at the headline shape (for rocprofv3)")
+    ap.add_argument("--profile-ssd", type=int, default=0, metavar="CALLS",
+                    help="only run this many SSD (Mamba-2 layer) scans (for rocprofv3)")
     ap.add_argument("--profile-variant", choices=("zoh", "bilinear"), default=None,
                     help="with --profile-run: time this discretisation instead of the Mamba one")
     args = ap.parse_args()
@@ -133,6 +137,13 @@ def main():
     if args.profile_decode:
         profile_decode(torch, ssm, synth, dev, args.profile_decode)
         log(f"decode profile run: {args.profile_decode} steps")
+        return
+    if args.profile_ssd:
+        t = _ssd_inputs(torch, dev)
+        for _ in range(args.profile_ssd):
+            ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
+        torch.cuda.synchronize()
+        log(f"ssd profile run: {args.profile_ssd} calls")
         return
     if args.profile_conv:
         x, w, bias = _conv_inputs(torch, synth, dev)
@@ -305,6 +316,39 @@ def _conv_inputs(torch, synth, dev):
     return x, w, bias
 
 
+SSD_SHAPE = dict(batch=4, seqlen=4096, nheads=64, headdim=64, dstate=128)
+
+
+def _ssd_inputs(torch, dev):
+    """Mamba-2 layer SSD scan input: x, z [4, 4096, 64, 64] bf16, delta [4, 4096, 64],
+    B, C [4, 4096, 128], A [64] = -exp(U[0, log 16]), D [64] ~ N(1, 0.1)."""
+    c = SSD_SHAPE
+    Bsz, L, H, P, N = c["batch"], c["seqlen"], c["nheads"], c["headdim"], c["dstate"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    bf = torch.bfloat16
+    t = {"x": _randn((Bsz, L, H, P), gen, dev, bf), "z": _randn((Bsz, L, H, P), gen, dev, bf),
+         "delta": _delta((Bsz, L, H), gen, dev, bf), "B": _randn((Bsz, L, N), gen, dev, bf),
+         "C": _randn((Bsz, L, N), gen, dev, bf),
+         "A": -torch.exp(torch.rand((H,), generator=gen, device=dev) * math.log(16.0)),
+         "D": 1.0 + 0.1 * torch.randn((H,), generator=gen, device=dev)}
+    t["y"] = torch.empty_like(t["x"])
+    return t
+
+
+def ssd_alg(c, Q=64):
+    """Algorithmic work of one SSD scan call: HBM bytes (x, z, y once each, delta, B, C, A,
+    D) and matrix-core flops of the chunked form with chunk Q: per chunk and head, the
+    masked C B^T (lower triangle incl. diagonal, Q(Q+1)/2 entries of length N), its product
+    with x, the carried state's readout C S^T and the state update (Q*N*P each)."""
+    Bsz, L, H, P, N = c["batch"], c["seqlen"], c["nheads"], c["headdim"], c["dstate"]
+    byts = 3 * Bsz * L * H * P * 2 + Bsz * L * H * 2 + 2 * Bsz * L * N * 2 + 2 * H * 4
+    tri = Q * (Q + 1) // 2
+    per_chunk = 2 * tri * N + 2 * tri * P + 2 * Q * N * P + 2 * Q * N * P
+    flops = Bsz * H * ((L + Q - 1) // Q) * per_chunk
+    return byts, flops
+
+
 def profile_decode(torch, ssm, synth, dev, steps):
     """A few decode steps on the decode workload's state (h [256, 4096, 16] fp32)."""
     c = synth.CONFIGS[4]
@@ -442,6 +486,43 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         log(f"{disc}: {ms * 1e3:.1f} us/launch, {upd / (ms * 1e-3):.3e} updates/s, "
             f"VALU {ts / VALU_PEAK_TSLOTS:.1%}")
     del x, dl, z, Bm, Cm, y, ws
+    torch.cuda.empty_cache()
+    # --- multi-head SSD scan (Mamba-2 layer) on the matrix cores ---
+    t = _ssd_inputs(torch, dev)
+    for _ in range(3):
+        ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
+    torch.cuda.synchronize()
+    st = []
+    for _ in range(10):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
+        b_.record()
+        torch.cuda.synchronize()
+        st.append(a_.elapsed_time(b_))
+    st.sort()
+    ms = st[len(st) // 2]
+    byts, flops = ssd_alg(SSD_SHAPE)
+    gbs = byts / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    c = SSD_SHAPE
+    out["ssd"] = {
+        "workload": "Mamba-2 layer SSD scan B4 L4096 H64 P64 N128 bf16 gated",
+        "ms_median": round(ms, 4),
+        "state_updates_per_s": c["batch"] * c["seqlen"] * c["nheads"] * c["headdim"] * c["dstate"] / (ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("ssd_B4_L4096_H64_P64_N128_bf16_gated", src_hash),
+                     "alg_bytes_per_launch": byts},
+        "mfma": {"achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                 "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "alg_flops_per_launch": flops,
+                 "note": "algorithmic flops of the chunked form (chunk 64); the kernel issues about 1.7x "
+                         "that (split-bf16 operands, full diagonal tiles)"},
+        "timing": "median of 10 launches, each between two events",
+    }
+    log(f"ssd: {ms * 1e3:.1f} us/launch, HBM {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}), "
+        f"MFMA {tfs:.0f} TFLOP/s ({tfs / MFMA_BF16_PEAK_TFS:.1%})")
+    del t
     torch.cuda.empty_cache()
     # --- causal conv1d + SiLU at the headline shape (HBM-bound) ---
     x, w, bias = _conv_inputs(torch, synth, dev)

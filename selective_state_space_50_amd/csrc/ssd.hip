@@ -9,26 +9,37 @@
 // brentwoodlivery ("State-space models (Mamba, S4)", "Mamba 2 and Hybrid
 // Architectures") describes the layer as a structured matrix multiplication.  Over a
 // chunk of Q = 64 steps starting from state S_in, with cum_t = sum_{k<=t} dt_k a:
-//     y_t   = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dt_s x_s        (in-chunk, a masked GEMM pair)
-//           + exp(cum_t) C_t S_in^T                                      (carried state)
-//     S_out = exp(cum_Q) S_in + sum_s exp(cum_Q - cum_s) dt_s x_s B_s^T  (state passed on)
-// All four products run on v_mfma_f32_16x16x16_bf16.  x, B and C are exact in bf16;
-// the operands that carry fp32 values (the masked C B^T, the carried state, the
-// decayed B) are split into a bf16 high part and a bf16 low part (two MFMAs), which
-// keeps about 16 significant bits instead of 8.
+//     y_t   = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dt_s x_s  + D x_t     (in-chunk)
+//           + exp(cum_t) C_t S_in^T                                          (carried state)
+//     S_out = exp(cum_Q) S_in + sum_s exp(cum_Q - cum_s) dt_s x_s B_s^T      (state passed on)
+// All products run on v_mfma_f32_16x16x16_bf16.  x, B and C are exact in bf16; the
+// operands that carry fp32 values (the masked C B^T with D on its diagonal, the
+// carried state, the weighted x) are split into a bf16 high part and a bf16 low part
+// (two MFMAs), which keeps about 16 significant bits instead of 8.
 //
-// One workgroup (4 waves) walks the whole sequence of one (b, h): the state stays in
-// registers from chunk to chunk, nothing of size [chunks, P, N] goes to memory.  Wave
-// w owns channels 16w..16w+15 of the output and of the state.  The next chunk's rows
-// are loaded into registers while the current one computes.
+// One workgroup walks the whole sequence of one (b, h): the state stays in registers
+// from chunk to chunk, nothing of size [chunks, P, N] goes to memory.  Eight waves, two
+// per SIMD: wave w owns channel block pb = w % 4 (16 channels) and half hf = w / 4 of
+// the state (states 64 hf .. 64 hf + 63).  The carried-state readout only needs the
+// wave's own half of the state, so the two halves' output shares go to two staging
+// tiles that the epilogue adds; the in-chunk part is split between the halves by
+// output time block.  The next chunk's inputs are loaded into registers while the
+// current one computes.  x and B are also needed with time as the contiguous axis (x^T,
+// B^T): a wave reads one 128-byte row per 2-byte load instruction and each lane keeps
+// consecutive steps of its own channel or state, which reach LDS as 8-byte runs.  (Both
+// a transpose through an identity MFMA and 2-byte LDS gathers measured slower.)  Per
+// chunk, the first wave also tabulates the per-step factors every wave needs: the
+// decay to the chunk's end times the step size, and the decay from the chunk's start.
 //
 // MFMA operand layouts (16x16 tiles, lane l): A row l%16, k 4(l/16)+i; B column l%16,
 // k 4(l/16)+i; D row 4(l/16)+j, column l%16.  Every product is arranged so that a D
 // tile is already the operand layout of the product that consumes it: the masked
 // (C B^T)^T tile feeds the output product as its B operand, the state tile S^T feeds
 // the carried-state product as its A operand, and outputs come out transposed
-// ([p][t]), which a staging tile turns back into rows of 64 channels.
+// ([p][t]), which the staging tiles turn back into rows of 64 channels.
 #include "ssm_device.h"
+
+#include <type_traits>
 
 namespace ssm {
 namespace {
@@ -36,10 +47,11 @@ namespace {
 constexpr int kQ = 64;         // chunk length
 constexpr int kP = 64;         // head dimension
 constexpr int kNS = 128;       // state size
-constexpr int kQP = kQ + 8;    // padded rows of the [P][Q] and [N][Q] tiles (bf16)
+constexpr int kQP = kQ + 4;    // padded rows of the [P][Q] and [N][Q] tiles (bf16; 136 bytes)
 constexpr int kNP = kNS + 8;   // padded rows of the [Q][N] tiles (bf16)
-constexpr int kYP = kP + 4;    // padded rows of the fp32 output tile
+constexpr int kYP = kP + 4;    // padded rows of the fp32 output tiles
 constexpr int kTiles = 10;     // 16x16 tiles on and below the diagonal of a 64x64 chunk
+constexpr int kThreads = 512;
 
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -50,11 +62,13 @@ struct __align__(16) SsdSmem {
     uint16_t bm[kQ][kNP];      // B: [s][n]
     uint16_t bt[kNS][kQP];     // B^T: [n][s]
     uint16_t cm[kQ][kNP];      // C: [t][n]
-    s4 mhi[kTiles][64];        // masked, decayed (C B^T)^T tiles, operand-ready: high part
-    s4 mlo[kTiles][64];        //   and low part
-    float y[kQ][kYP];          // output tile of the chunk, [t][p]
+    s4 mhi[kTiles][64];        // masked, decayed (C B^T)^T tiles (+ D on the diagonal),
+    s4 mlo[kTiles][64];        //   operand-ready: high and low parts
+    float y[2][kQ][kYP];       // output shares of the two state halves, [t][p]
     float cum[kQ];             // running sum of dt * a * log2(e) within the chunk
     float dt[kQ];              // step sizes of the chunk (0 past the sequence)
+    float wend[kQ];            // exp(cum_Q - cum_s) dt_s: weight of step s in the state passed on
+    float ebeg[kQ];            // exp(cum_t): decay of the carried state to step t
 };
 
 __device__ __forceinline__ f4 mfma(s4 a, s4 b, f4 c) {
@@ -71,12 +85,18 @@ __device__ __forceinline__ void split4(float v0, float v1, float v2, float v3, s
 
 __device__ __forceinline__ s4 lds4(const uint16_t *p) { return *reinterpret_cast<const s4 *>(p); }
 
+
+
+// tile index of (s-block k, t-block i), k <= i
+__host__ __device__ constexpr int tile_of(int k, int i) { return i * (i + 1) / 2 + k; }
+
 template <bool HAS_Z>
-__global__ void __launch_bounds__(256) ssd_kernel(SsdArgs a) {
+__global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
     __shared__ SsdSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pb = w & 3, hf = w >> 2;
     const int lr = lane & 15, lg = lane >> 4;
 
     // workgroup -> (b, h): the hardware deals workgroups to the 8 XCDs in turn, so
@@ -93,113 +113,131 @@ __global__ void __launch_bounds__(256) ssd_kernel(SsdArgs a) {
     const float dbias = a.dbias ? a.dbias[h] : 0.0f;
     const int64_t nch = (L + kQ - 1) / kQ;
 
-    // state S^T, tile kk: lane holds n = 16 kk + 4 lg + j, p = 16 w + lr
-    f4 S[8];
+    // the wave's half of the state, S^T tile kk: lane holds n = 64 hf + 16 kk + 4 lg + j,
+    // p = 16 pb + lr
+    f4 S[4];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int n = 16 * kk + 4 * lg + j, p = 16 * w + lr;
+            const int n = 64 * hf + 16 * kk + 4 * lg + j, p = 16 * pb + lr;
             S[kk][j] = a.h0 ? a.h0[((b * H + h) * kP + p) * kNS + n] : 0.0f;
         }
-    }
 
-    const uint16_t *X = static_cast<const uint16_t *>(a.x);
-    const uint16_t *Z = static_cast<const uint16_t *>(a.z);
-    const uint16_t *DL = static_cast<const uint16_t *>(a.delta);
-    const uint16_t *BM = static_cast<const uint16_t *>(a.Bm);
-    const uint16_t *CM = static_cast<const uint16_t *>(a.Cm);
-    uint16_t *Y = static_cast<uint16_t *>(a.y);
+    const uint16_t *X = static_cast<const uint16_t *>(a.x) + (b * L * H + h) * kP;   // row t at + t H kP
+    const uint16_t *Z = static_cast<const uint16_t *>(a.z) + (b * L * H + h) * kP;
+    const uint16_t *DL = static_cast<const uint16_t *>(a.delta) + b * L * H + h;      // step t at + t H
+    const uint16_t *BM = static_cast<const uint16_t *>(a.Bm) + b * L * kNS;           // row t at + t kNS
+    const uint16_t *CM = static_cast<const uint16_t *>(a.Cm) + b * L * kNS;
+    uint16_t *Y = static_cast<uint16_t *>(a.y) + (b * L * H + h) * kP;
+    const int64_t xs = H * kP;   // elements between consecutive steps of x, z, y
 
-    // loads: x / z / y rows xt0 and xt0 + 32, channels xp0..xp0+7 (16 bytes); B / C rows
-    // bt0 + 16 r, states bn0..bn0+7; step sizes by the first wave, one step per lane
-    const int xt0 = tid >> 3, xp0 = (tid & 7) * 8;
-    const int bt0 = tid >> 4, bn0 = (tid & 15) * 8;
-    uint4 xq[2], zq[2], bq[4], cq[4];
+    // per-thread inputs of one chunk (every address is a wave-uniform row pointer plus a
+    // 32-bit lane offset):
+    //   z: row 8 w + lane / 8, channels (lane % 8) * 8 .. +7 (16 bytes)   (the epilogue's row and channels)
+    //   B, C: rows 4 w + lane / 16 + 32 r, states (lane % 16) * 8 .. +7 (16 bytes)
+    //   x^T: channel lane, steps 8 w + i (2 bytes each)
+    //   B^T: state 64 (w & 1) + lane, steps 16 (w >> 1) + i
+    //   delta: first wave, one step per lane
+    const int yt = 8 * w + (lane >> 3), yp = (lane & 7) * 8;
+    const uint32_t zoff = static_cast<uint32_t>((lane >> 3) * xs + yp);
+    const int bt = 4 * w + (lane >> 4), bn = (lane & 15) * 8;
+    const uint32_t boff = static_cast<uint32_t>((lane >> 4) * kNS + bn);
+    const int tn = 64 * (w & 1) + lane, ts = 16 * (w >> 1);
+    uint4 zq, bq[2], cq[2];
+    uint16_t xg[8], bg[16];
     uint16_t dq = 0;
-    auto load = [&](int64_t c) __attribute__((always_inline)) {
+    // full chunks need no bounds; in the last, partial chunk rows past the end are not
+    // loaded or reload the last row (staging zeroes them)
+    auto load = [&](int64_t c, auto partial) __attribute__((always_inline)) {
+        constexpr bool PART = decltype(partial)::value;
         const int64_t t0 = c * kQ;
+        auto row = [&](int64_t t) { return PART && t >= L ? L - 1 : t; };
+        if constexpr (HAS_Z) {
+            if (!PART || t0 + yt < L) zq = *reinterpret_cast<const uint4 *>(Z + (t0 + 8 * w) * xs + zoff);
+        }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            int64_t t = t0 + xt0 + 32 * r;
-            t = t < L ? t : L - 1;              // rows past the end reload the last one (zeroed when staged)
-            const int64_t off = ((b * L + t) * H + h) * kP + xp0;
-            xq[r] = *reinterpret_cast<const uint4 *>(X + off);
-            if constexpr (HAS_Z) zq[r] = *reinterpret_cast<const uint4 *>(Z + off);
+            const int64_t t = t0 + 4 * w + 32 * r;
+            if (!PART || t0 + bt + 32 * r < L) {
+                bq[r] = *reinterpret_cast<const uint4 *>(BM + t * kNS + boff);
+                cq[r] = *reinterpret_cast<const uint4 *>(CM + t * kNS + boff);
+            }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int64_t t = t0 + bt0 + 16 * r;
-            t = t < L ? t : L - 1;
-            const int64_t off = (b * L + t) * kNS + bn0;
-            bq[r] = *reinterpret_cast<const uint4 *>(BM + off);
-            cq[r] = *reinterpret_cast<const uint4 *>(CM + off);
-        }
+        for (int i = 0; i < 8; ++i) xg[i] = (X + row(t0 + 8 * w + i) * xs)[lane];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bg[i] = (BM + row(t0 + ts + i) * kNS)[tn];
         if (w == 0) {
-            int64_t t = t0 + lane;
-            t = t < L ? t : L - 1;
-            dq = DL[(b * L + t) * H + h];
+            const int64_t t = t0 + lane;
+            dq = DL[(PART && t >= L ? L - 1 : t) * H];
         }
     };
+    auto load_any = [&](int64_t c) __attribute__((always_inline)) {
+        if (c * kQ + kQ <= L) load(c, std::false_type{});
+        else load(c, std::true_type{});
+    };
 
-    auto stage = [&](int64_t c) __attribute__((always_inline)) {
+    auto stage = [&](int64_t c, auto partial) __attribute__((always_inline)) {
+        constexpr bool PART = decltype(partial)::value;
         const int64_t t0 = c * kQ;
+        auto pk = [&](uint16_t lo, uint16_t hi, int64_t t) {
+            uint32_t v = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+            if constexpr (PART) v = (t < L ? v & 0xffffu : 0u) | (t + 1 < L ? v & 0xffff0000u : 0u);
+            return v;
+        };
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int tl = xt0 + 32 * r;
-            const uint4 v = t0 + tl < L ? xq[r] : make_uint4(0, 0, 0, 0);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm.xt[xp0 + 2 * i][tl] = static_cast<uint16_t>(u[i]);
-                sm.xt[xp0 + 2 * i + 1][tl] = static_cast<uint16_t>(u[i] >> 16);
-            }
+        for (int qd = 0; qd < 2; ++qd) {
+            const int s0 = 8 * w + 4 * qd;
+            *reinterpret_cast<u2 *>(&sm.xt[lane][s0]) =
+                u2{pk(xg[4 * qd], xg[4 * qd + 1], t0 + s0), pk(xg[4 * qd + 2], xg[4 * qd + 3], t0 + s0 + 2)};
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tl = bt0 + 16 * r;
-            const bool ok = t0 + tl < L;
-            const uint4 bv = ok ? bq[r] : make_uint4(0, 0, 0, 0);
-            const uint4 cv = ok ? cq[r] : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&sm.bm[tl][bn0]) = bv;
-            *reinterpret_cast<uint4 *>(&sm.cm[tl][bn0]) = cv;
-            const uint32_t u[4] = {bv.x, bv.y, bv.z, bv.w};
+        for (int qd = 0; qd < 4; ++qd) {
+            const int s0 = ts + 4 * qd;
+            *reinterpret_cast<u2 *>(&sm.bt[tn][s0]) =
+                u2{pk(bg[4 * qd], bg[4 * qd + 1], t0 + s0), pk(bg[4 * qd + 2], bg[4 * qd + 3], t0 + s0 + 2)};
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm.bt[bn0 + 2 * i][tl] = static_cast<uint16_t>(u[i]);
-                sm.bt[bn0 + 2 * i + 1][tl] = static_cast<uint16_t>(u[i] >> 16);
-            }
+        for (int r = 0; r < 2; ++r) {
+            const int tl = bt + 32 * r;
+            const bool ok = !PART || t0 + tl < L;
+            *reinterpret_cast<uint4 *>(&sm.bm[tl][bn]) = ok ? bq[r] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&sm.cm[tl][bn]) = ok ? cq[r] : make_uint4(0, 0, 0, 0);
         }
         if (w == 0) {
             float dtv = widen_v(dq) + dbias;
             if (a.softplus) dtv = softplus_f(dtv);
-            if (t0 + lane >= L) dtv = 0.0f;     // padded steps: no decay, no input
+            if (PART && t0 + lane >= L) dtv = 0.0f;          // padded steps: no decay, no input
             float v = dtv * al2;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const float u = __shfl_up(v, o, 64);
                 if (lane >= o) v += u;
             }
+            const float last = __shfl(v, 63, 64);
             sm.cum[lane] = v;
             sm.dt[lane] = dtv;
+            sm.wend[lane] = __builtin_amdgcn_exp2f(last - v) * dtv;
+            sm.ebeg[lane] = __builtin_amdgcn_exp2f(v);
         }
     };
 
-    if (nch > 0) load(0);
+    // output time blocks of the in-chunk part: half 0 takes blocks 0 and 3, half 1 blocks
+    // 1 and 2 (equal work: the block i product has i + 1 tiles)
+    const int ia = hf == 0 ? 0 : 1, ib = hf == 0 ? 3 : 2;
+
+    if (nch > 0) load_any(0);
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t t0 = c * kQ;
-        stage(c);
-        uint4 xe[2], ze[2];   // x, z rows of this chunk for the epilogue
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            xe[r] = xq[r];
-            if constexpr (HAS_Z) ze[r] = zq[r];
-        }
-        if (c + 1 < nch) load(c + 1);
+        if (t0 + kQ <= L) stage(c, std::false_type{});
+        else stage(c, std::true_type{});
+        const uint4 ze = zq;   // z row of this chunk for the epilogue
+        if (c + 1 < nch) load_any(c + 1);
         __syncthreads();
 
-        // ---- masked, decayed (C B^T)^T tiles (s-block k <= t-block i), shared by all waves
-        for (int idx = w; idx < kTiles; idx += 4) {
+        // ---- masked, decayed (C B^T)^T tiles with D on the diagonal, shared by all waves
+        for (int idx = w; idx < kTiles; idx += 8) {
             const int i = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
             const int k = idx - i * (i + 1) / 2;
             f4 g = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -214,6 +252,7 @@ __global__ void __launch_bounds__(256) ssd_kernel(SsdArgs a) {
             for (int j = 0; j < 4; ++j) {
                 const int s = 16 * k + 4 * lg + j;
                 v[j] = s <= t ? g[j] * __builtin_amdgcn_exp2f(ct - sm.cum[s]) * sm.dt[s] : 0.0f;
+                if (s == t) v[j] += dsk;
             }
             s4 hi, lo;
             split4(v[0], v[1], v[2], v[3], hi, lo);
@@ -222,98 +261,97 @@ __global__ void __launch_bounds__(256) ssd_kernel(SsdArgs a) {
         }
         __syncthreads();
 
-        // ---- outputs y^T[p][t] of this wave's channels: in-chunk part + carried state
-        s4 shi[8], slo[8];
+        // ---- this wave's share of y^T[p][t] (channels of block pb): the carried-state
+        // readout over its half of the state for every time block, plus the in-chunk part
+        // for time blocks ia and ib
+        {
+            s4 shi[4], slo[4];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) split4(S[kk][0], S[kk][1], S[kk][2], S[kk][3], shi[kk], slo[kk]);
+            for (int kk = 0; kk < 4; ++kk) split4(S[kk][0], S[kk][1], S[kk][2], S[kk][3], shi[kk], slo[kk]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int i = 0; i < 4; ++i) {
+                f4 off = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k <= i; ++k) {
-                const int idx = i * (i + 1) / 2 + k;
-                const s4 xa = lds4(&sm.xt[16 * w + lr][16 * k + 4 * lg]);
-                acc = mfma(xa, sm.mhi[idx][lane], acc);
-                acc = mfma(xa, sm.mlo[idx][lane], acc);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const s4 cb = lds4(&sm.cm[16 * i + lr][64 * hf + 16 * kk + 4 * lg]);
+                    off = mfma(shi[kk], cb, off);
+                    off = mfma(slo[kk], cb, off);
+                }
+                const float e = sm.ebeg[16 * i + lr];
+                f4 acc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = e * off[j];
+                if (i == ia || i == ib) {
+                    for (int k = 0; k <= i; ++k) {
+                        const s4 xa = lds4(&sm.xt[16 * pb + lr][16 * k + 4 * lg]);
+                        acc = mfma(xa, sm.mhi[tile_of(k, i)][lane], acc);
+                        acc = mfma(xa, sm.mlo[tile_of(k, i)][lane], acc);
+                    }
+                }
+                // lane: p = 16 pb + 4 lg + j, t = 16 i + lr
+                *reinterpret_cast<float4 *>(&sm.y[hf][16 * i + lr][16 * pb + 4 * lg]) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
-            f4 off = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const s4 cb = lds4(&sm.cm[16 * i + lr][16 * kk + 4 * lg]);
-                off = mfma(shi[kk], cb, off);
-                off = mfma(slo[kk], cb, off);
-            }
-            const float e = __builtin_amdgcn_exp2f(sm.cum[16 * i + lr]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(e, off[j], acc[j]);
-            // lane: p = 16 w + 4 lg + j, t = 16 i + lr
-            *reinterpret_cast<float4 *>(&sm.y[16 * i + lr][16 * w + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
 
-        // ---- state passed on: S^T = exp(cum_Q) S^T + sum_s (exp(cum_Q - cum_s) dt_s B_s) x_s^T
+        // ---- state passed on (this wave's half):
+        //      S^T = exp(cum_Q) S^T + sum_s B_s^T (exp(cum_Q - cum_s) dt_s x_s)
         {
-            const float clast = sm.cum[kQ - 1];
-            const float dec = __builtin_amdgcn_exp2f(clast);
-            float wv[4][4];   // weight of step s = 16 k + 4 lg + i
+            const float dec = sm.ebeg[kQ - 1];
+            s4 xh[4], xl[4];   // weighted x operand (k = s = 16 k + 4 lg + i, column p = 16 pb + lr)
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < 4; ++k) {
+                const float4 wq = *reinterpret_cast<const float4 *>(&sm.wend[16 * k + 4 * lg]);
+                const float wv[4] = {wq.x, wq.y, wq.z, wq.w};
+                const u2 raw = __builtin_bit_cast(u2, lds4(&sm.xt[16 * pb + lr][16 * k + 4 * lg]));
+                split4(bf_lo(raw.x) * wv[0], bf_hi(raw.x) * wv[1], bf_lo(raw.y) * wv[2], bf_hi(raw.y) * wv[3],
+                       xh[k], xl[k]);
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = 16 * k + 4 * lg + i;
-                    wv[k][i] = __builtin_amdgcn_exp2f(clast - sm.cum[s]) * sm.dt[s];
-                }
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
+            for (int kk = 0; kk < 4; ++kk) {
                 f4 acc = S[kk] * dec;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const u2 raw = __builtin_bit_cast(u2, lds4(&sm.bt[16 * kk + lr][16 * k + 4 * lg]));
-                    s4 hi, lo;
-                    split4(bf_lo(raw.x) * wv[k][0], bf_hi(raw.x) * wv[k][1], bf_lo(raw.y) * wv[k][2],
-                           bf_hi(raw.y) * wv[k][3], hi, lo);
-                    const s4 xb = lds4(&sm.xt[16 * w + lr][16 * k + 4 * lg]);
-                    acc = mfma(hi, xb, acc);
-                    acc = mfma(lo, xb, acc);
+                    const s4 ba = lds4(&sm.bt[64 * hf + 16 * kk + lr][16 * k + 4 * lg]);
+                    acc = mfma(ba, xh[k], acc);
+                    acc = mfma(ba, xl[k], acc);
                 }
                 S[kk] = acc;
             }
         }
         __syncthreads();
 
-        // ---- epilogue: skip term, gate, bf16 rows of 64 channels
+        // ---- epilogue: add the two halves' shares, gate, one bf16 row segment per thread
+        if (t0 + yt < L) {
+            float yv[8];
+            const float4 *p0 = reinterpret_cast<const float4 *>(&sm.y[0][yt][yp]);
+            const float4 *p1 = reinterpret_cast<const float4 *>(&sm.y[1][yt][yp]);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int tl = xt0 + 32 * r;
-            const int64_t t = t0 + tl;
-            if (t < L) {
-                const float4 y0 = *reinterpret_cast<const float4 *>(&sm.y[tl][xp0]);
-                const float4 y1 = *reinterpret_cast<const float4 *>(&sm.y[tl][xp0 + 4]);
-                const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-                const uint32_t xu[4] = {xe[r].x, xe[r].y, xe[r].z, xe[r].w};
-                uint32_t zu[4] = {0, 0, 0, 0};
-                if constexpr (HAS_Z) { zu[0] = ze[r].x; zu[1] = ze[r].y; zu[2] = ze[r].z; zu[3] = ze[r].w; }
-                uint32_t o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v0 = __builtin_fmaf(dsk, bf_lo(xu[i]), yv[2 * i]);
-                    float v1 = __builtin_fmaf(dsk, bf_hi(xu[i]), yv[2 * i + 1]);
-                    if constexpr (HAS_Z) {
-                        v0 *= silu_f(bf_lo(zu[i]));
-                        v1 *= silu_f(bf_hi(zu[i]));
-                    }
-                    o[i] = pack_bf16(v0, v1);
-                }
-                *reinterpret_cast<uint4 *>(Y + ((b * L + t) * H + h) * kP + xp0) = make_uint4(o[0], o[1], o[2], o[3]);
+            for (int k = 0; k < 2; ++k) {
+                const float4 u = p0[k], v = p1[k];
+                yv[4 * k] = u.x + v.x; yv[4 * k + 1] = u.y + v.y; yv[4 * k + 2] = u.z + v.z; yv[4 * k + 3] = u.w + v.w;
             }
+            const uint32_t zu[4] = {ze.x, ze.y, ze.z, ze.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v0 = yv[2 * i], v1 = yv[2 * i + 1];
+                if constexpr (HAS_Z) {
+                    v0 *= silu_f(bf_lo(zu[i]));
+                    v1 *= silu_f(bf_hi(zu[i]));
+                }
+                o[i] = pack_bf16(v0, v1);
+            }
+            *reinterpret_cast<uint4 *>(Y + (t0 + 8 * w) * xs + zoff) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
 
     if (a.h_last) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = 16 * kk + 4 * lg + j, p = 16 * w + lr;
+                const int n = 64 * hf + 16 * kk + 4 * lg + j, p = 16 * pb + lr;
                 a.h_last[((b * H + h) * kP + p) * kNS + n] = S[kk][j];
             }
     }
@@ -324,8 +362,8 @@ __global__ void __launch_bounds__(256) ssd_kernel(SsdArgs a) {
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t s) {
     const int64_t W = a.B * a.H;
     const dim3 grid(static_cast<unsigned>(((W + 7) / 8) * 8));
-    if (a.z) hipLaunchKernelGGL((ssd_kernel<true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ssd_kernel<false>), grid, dim3(256), 0, s, a);
+    if (a.z) hipLaunchKernelGGL((ssd_kernel<true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((ssd_kernel<false>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
