@@ -48,7 +48,9 @@ constexpr int kQ = 64;         // chunk length
 constexpr int kP = 64;         // head dimension
 constexpr int kNS = 128;       // state size
 constexpr int kQP = kQ + 4;    // padded rows of the [P][Q] and [N][Q] tiles (bf16; 136 bytes)
-constexpr int kNP = kNS + 8;   // padded rows of the [Q][N] tiles (bf16)
+// padded rows of the [Q][N] tiles: 66 words, 2 mod 32, so the 8-byte operand reads of
+// 16 consecutive rows by each half-wave cover all 32 banks exactly twice
+constexpr int kNP = kNS + 4;
 constexpr int kYP = kP + 4;    // padded rows of the fp32 output tiles
 constexpr int kTiles = 10;     // 16x16 tiles on and below the diagonal of a 64x64 chunk
 constexpr int kThreads = 512;
@@ -202,8 +204,11 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
         for (int r = 0; r < 2; ++r) {
             const int tl = bt + 32 * r;
             const bool ok = !PART || t0 + tl < L;
-            *reinterpret_cast<uint4 *>(&sm.bm[tl][bn]) = ok ? bq[r] : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&sm.cm[tl][bn]) = ok ? cq[r] : make_uint4(0, 0, 0, 0);
+            const uint4 bv = ok ? bq[r] : make_uint4(0, 0, 0, 0), cv = ok ? cq[r] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<u2 *>(&sm.bm[tl][bn]) = u2{bv.x, bv.y};   // rows are 8-byte aligned
+            *reinterpret_cast<u2 *>(&sm.bm[tl][bn + 4]) = u2{bv.z, bv.w};
+            *reinterpret_cast<u2 *>(&sm.cm[tl][bn]) = u2{cv.x, cv.y};
+            *reinterpret_cast<u2 *>(&sm.cm[tl][bn + 4]) = u2{cv.z, cv.w};
         }
         if (w == 0) {
             float dtv = widen_v(dq) + dbias;
