@@ -12,7 +12,7 @@
 //     y_t   = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dt_s x_s  + D x_t     (in-chunk)
 //           + exp(cum_t) C_t S_in^T                                          (carried state)
 //     S_out = exp(cum_Q) S_in + sum_s exp(cum_Q - cum_s) dt_s x_s B_s^T      (state passed on)
-// All products run on v_mfma_f32_16x16x16_bf16.  x, B and C are exact in bf16; the
+// The products run on v_mfma_f32_16x16x32_bf16 (K = 32).  x, B and C are exact in bf16; the
 // operands that carry fp32 values (the masked C B^T with D on its diagonal, the
 // carried state, the weighted x) are split into a bf16 high part and a bf16 low part
 // (two MFMAs), which keeps about 16 significant bits instead of 8.
@@ -31,12 +31,16 @@
 // chunk, the first wave also tabulates the per-step factors every wave needs: the
 // decay to the chunk's end times the step size, and the decay from the chunk's start.
 //
-// MFMA operand layouts (16x16 tiles, lane l): A row l%16, k 4(l/16)+i; B column l%16,
-// k 4(l/16)+i; D row 4(l/16)+j, column l%16.  Every product is arranged so that a D
-// tile is already the operand layout of the product that consumes it: the masked
-// (C B^T)^T tile feeds the output product as its B operand, the state tile S^T feeds
-// the carried-state product as its A operand, and outputs come out transposed
-// ([p][t]), which the staging tiles turn back into rows of 64 channels.
+// MFMA operand layouts (lane l): K = 32: A row l%16, k 8(l/16)+i (i < 8), B column l%16,
+// same k; K = 16: k 4(l/16)+i (i < 4); D (both): row 4(l/16)+j, column l%16.  Every
+// product is arranged so that a D tile is already the operand layout of the product
+// that consumes it: the masked (C B^T)^T tile feeds the output product as its B
+// operand, the state tile S^T feeds the carried-state product as its A operand, and
+// outputs come out transposed ([p][t]), which the staging tiles turn back into rows of
+// 64 channels.  A D tile holds k = 4(l/16)+j, so a K = 32 operand built from two D
+// tiles takes its k in the order (first tile's 4, second tile's 4) per lane, and the
+// other operand of that product is read in the same order; the contraction does not
+// depend on the order of k.
 #include "ssm_device.h"
 
 #include <type_traits>
@@ -47,15 +51,18 @@ namespace {
 constexpr int kQ = 64;         // chunk length
 constexpr int kP = 64;         // head dimension
 constexpr int kNS = 128;       // state size
-constexpr int kQP = kQ + 4;    // padded rows of the [P][Q] and [N][Q] tiles (bf16; 136 bytes)
-// padded rows of the [Q][N] tiles: 66 words, 2 mod 32, so the 8-byte operand reads of
-// 16 consecutive rows by each half-wave cover all 32 banks exactly twice
-constexpr int kNP = kNS + 4;
+// padded rows (bf16): 144-byte rows of the [P][Q] and [N][Q] tiles and 272-byte rows of
+// the [Q][N] tiles, 16-byte aligned and 4 words apart modulo the 32 banks, so the
+// 16-byte operand reads of 8 consecutive rows hit distinct banks
+constexpr int kQP = kQ + 8;
+constexpr int kNP = kNS + 8;
 constexpr int kYP = kP + 4;    // padded rows of the fp32 output tiles
 constexpr int kTiles = 10;     // 16x16 tiles on and below the diagonal of a 64x64 chunk
 constexpr int kThreads = 512;
 
 typedef short s4 __attribute__((ext_vector_type(4)));
+typedef short s8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
@@ -76,6 +83,10 @@ struct __align__(16) SsdSmem {
 __device__ __forceinline__ f4 mfma(s4 a, s4 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f4 mfma32(s8 a, s8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ s8 cat(s4 a, s4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
 
 // four floats -> bf16 high part (round to nearest even) and the bf16 of the remainder
 __device__ __forceinline__ void split4(float v0, float v1, float v2, float v3, s4 &hi, s4 &lo) {
@@ -86,6 +97,7 @@ __device__ __forceinline__ void split4(float v0, float v1, float v2, float v3, s
 }
 
 __device__ __forceinline__ s4 lds4(const uint16_t *p) { return *reinterpret_cast<const s4 *>(p); }
+__device__ __forceinline__ s8 lds8(const uint16_t *p) { return *reinterpret_cast<const s8 *>(p); }
 
 
 
@@ -204,11 +216,8 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
         for (int r = 0; r < 2; ++r) {
             const int tl = bt + 32 * r;
             const bool ok = !PART || t0 + tl < L;
-            const uint4 bv = ok ? bq[r] : make_uint4(0, 0, 0, 0), cv = ok ? cq[r] : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<u2 *>(&sm.bm[tl][bn]) = u2{bv.x, bv.y};   // rows are 8-byte aligned
-            *reinterpret_cast<u2 *>(&sm.bm[tl][bn + 4]) = u2{bv.z, bv.w};
-            *reinterpret_cast<u2 *>(&sm.cm[tl][bn]) = u2{cv.x, cv.y};
-            *reinterpret_cast<u2 *>(&sm.cm[tl][bn + 4]) = u2{cv.z, cv.w};
+            *reinterpret_cast<uint4 *>(&sm.bm[tl][bn]) = ok ? bq[r] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&sm.cm[tl][bn]) = ok ? cq[r] : make_uint4(0, 0, 0, 0);
         }
         if (w == 0) {
             float dtv = widen_v(dq) + dbias;
@@ -247,8 +256,8 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
             const int k = idx - i * (i + 1) / 2;
             f4 g = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-                g = mfma(lds4(&sm.bm[16 * k + lr][16 * kk + 4 * lg]), lds4(&sm.cm[16 * i + lr][16 * kk + 4 * lg]), g);
+            for (int kk = 0; kk < 4; ++kk)
+                g = mfma32(lds8(&sm.bm[16 * k + lr][32 * kk + 8 * lg]), lds8(&sm.cm[16 * i + lr][32 * kk + 8 * lg]), g);
             // lane: s = 16 k + 4 lg + j, t = 16 i + lr;  M[t][s] = (C_t . B_s) exp(cum_t - cum_s) dt_s
             const int t = 16 * i + lr;
             const float ct = sm.cum[t];
@@ -277,18 +286,27 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
             for (int i = 0; i < 4; ++i) {
                 f4 off = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const s4 cb = lds4(&sm.cm[16 * i + lr][64 * hf + 16 * kk + 4 * lg]);
-                    off = mfma(shi[kk], cb, off);
-                    off = mfma(slo[kk], cb, off);
+                for (int k2 = 0; k2 < 2; ++k2) {   // state tiles 2 k2 and 2 k2 + 1, k in tile order
+                    const uint16_t *cr = &sm.cm[16 * i + lr][64 * hf + 32 * k2 + 4 * lg];
+                    const s8 cb = cat(lds4(cr), lds4(cr + 16));
+                    off = mfma32(cat(shi[2 * k2], shi[2 * k2 + 1]), cb, off);
+                    off = mfma32(cat(slo[2 * k2], slo[2 * k2 + 1]), cb, off);
                 }
                 const float e = sm.ebeg[16 * i + lr];
                 f4 acc;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[j] = e * off[j];
                 if (i == ia || i == ib) {
-                    for (int k = 0; k <= i; ++k) {
-                        const s4 xa = lds4(&sm.xt[16 * pb + lr][16 * k + 4 * lg]);
+                    const uint16_t *xr = &sm.xt[16 * pb + lr][4 * lg];
+                    int k = 0;
+#pragma unroll
+                    for (; k + 1 <= i; k += 2) {   // step blocks k and k + 1, k in tile order
+                        const s8 xa = cat(lds4(xr + 16 * k), lds4(xr + 16 * k + 16));
+                        acc = mfma32(xa, cat(sm.mhi[tile_of(k, i)][lane], sm.mhi[tile_of(k + 1, i)][lane]), acc);
+                        acc = mfma32(xa, cat(sm.mlo[tile_of(k, i)][lane], sm.mlo[tile_of(k + 1, i)][lane]), acc);
+                    }
+                    if (k == i) {
+                        const s4 xa = lds4(xr + 16 * k);
                         acc = mfma(xa, sm.mhi[tile_of(k, i)][lane], acc);
                         acc = mfma(xa, sm.mlo[tile_of(k, i)][lane], acc);
                     }
@@ -303,23 +321,28 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
         //      S^T = exp(cum_Q) S^T + sum_s B_s^T (exp(cum_Q - cum_s) dt_s x_s)
         {
             const float dec = sm.ebeg[kQ - 1];
-            s4 xh[4], xl[4];   // weighted x operand (k = s = 16 k + 4 lg + i, column p = 16 pb + lr)
+            s8 xh[2], xl[2];   // weighted x operand (k = s = 32 k2 + 8 lg + i, column p = 16 pb + lr)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 wq = *reinterpret_cast<const float4 *>(&sm.wend[16 * k + 4 * lg]);
-                const float wv[4] = {wq.x, wq.y, wq.z, wq.w};
-                const u2 raw = __builtin_bit_cast(u2, lds4(&sm.xt[16 * pb + lr][16 * k + 4 * lg]));
-                split4(bf_lo(raw.x) * wv[0], bf_hi(raw.x) * wv[1], bf_lo(raw.y) * wv[2], bf_hi(raw.y) * wv[3],
-                       xh[k], xl[k]);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.wend[32 * k2 + 8 * lg]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.wend[32 * k2 + 8 * lg + 4]);
+                const s8 raw = lds8(&sm.xt[16 * pb + lr][32 * k2 + 8 * lg]);
+                const u2 r0 = __builtin_bit_cast(u2, __builtin_shufflevector(raw, raw, 0, 1, 2, 3));
+                const u2 r1 = __builtin_bit_cast(u2, __builtin_shufflevector(raw, raw, 4, 5, 6, 7));
+                s4 h0, l0, h1, l1;
+                split4(bf_lo(r0.x) * w0.x, bf_hi(r0.x) * w0.y, bf_lo(r0.y) * w0.z, bf_hi(r0.y) * w0.w, h0, l0);
+                split4(bf_lo(r1.x) * w1.x, bf_hi(r1.x) * w1.y, bf_lo(r1.y) * w1.z, bf_hi(r1.y) * w1.w, h1, l1);
+                xh[k2] = cat(h0, h1);
+                xl[k2] = cat(l0, l1);
             }
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 f4 acc = S[kk] * dec;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const s4 ba = lds4(&sm.bt[64 * hf + 16 * kk + lr][16 * k + 4 * lg]);
-                    acc = mfma(ba, xh[k], acc);
-                    acc = mfma(ba, xl[k], acc);
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const s8 ba = lds8(&sm.bt[64 * hf + 16 * kk + lr][32 * k2 + 8 * lg]);
+                    acc = mfma32(ba, xh[k2], acc);
+                    acc = mfma32(ba, xl[k2], acc);
                 }
                 S[kk] = acc;
             }
