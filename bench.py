@@ -292,6 +292,23 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _host(t):
+    """A (sampled) device tensor as float64 on the host (bf16 and fp32 values are exact)."""
+    import numpy as np
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _cpu_entry(seconds, work, unit, sample, cores):
+    return {"value": work / seconds, "unit": unit, "cores": cores, "kind": "oracle", "seconds": round(seconds, 3),
+            "sample": sample}
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
 def _randn(shape, gen, dev, dtype):
     import torch
     return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(dtype)
@@ -371,6 +388,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     """Decode (1024 steps) and the million-token chunked scan.  Inputs drawn on the
     GPU with torch's seeded generator, same distributions as the headline input."""
     out = {}
+    deferred = []   # (entry, oracle call, work, unit, sample, threads), timed at the end
     gen = torch.Generator(device=dev)
     gen.manual_seed(4)
     bf = torch.bfloat16
@@ -443,6 +461,22 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     }
     log(f"decode: {tot_ms:.2f} ms for {S} steps from a graph ({k_avg * 1e3:.1f} us/step); "
         f"eager from Python {eager_ms:.2f} ms")
+    import numpy as np
+    import oracle
+    from oracle import conv_oracle, ssd_oracle
+    cores = oracle.default_threads()
+    # oracle beside it: every batch row, every 64th channel, the first 128 steps (L steps
+    # of the update from zero = one scan over those L tokens)
+    Ss, dsel = 1024, torch.arange(0, D, 64, device=dev)
+    ser = lambda t: _host(t[:Ss][:, :, dsel].permute(1, 2, 0)).reshape(Bsz * len(dsel), Ss)
+    cb = np.repeat(np.arange(Bsz), len(dsel))
+    cd = np.tile(np.arange(len(dsel)), Bsz)
+    # (host copies now; every oracle timing runs after the last GPU measurement, so that
+    # the GPU does not idle between them)
+    a_ = (ser(xs), ser(ds), _host(A[dsel]), _host(Bs[:Ss].permute(1, 0, 2)), _host(Cs[:Ss].permute(1, 0, 2)),
+          _host(Dk[dsel]), ser(zs), None, False, cb, cd, cores)
+    deferred.append((out["decode"], lambda a_=a_: oracle.scan_f64(*a_), Bsz * len(dsel) * Ss * N, "state-updates/s",
+                     f"{Bsz * len(dsel)} channels (every 64th) x all {Ss} steps, fp64 C oracle", cores))
     del xs, ds, zs, Bs, Cs, h
     torch.cuda.empty_cache()
     # --- the other discretisations at the headline shape ---
@@ -459,7 +493,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
                      device=dev)
     out["variants"] = {}
     for disc in ("zoh", "bilinear"):
-        for _ in range(3):
+        for _ in range(30):   # also brings the clocks back up after the host work before it
             ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
         torch.cuda.synchronize()
         vt = []
@@ -485,11 +519,20 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         }
         log(f"{disc}: {ms * 1e3:.1f} us/launch, {upd / (ms * 1e-3):.3e} updates/s, "
             f"VALU {ts / VALU_PEAK_TSLOTS:.1%}")
+        # oracle beside it: 256 channels of every batch row over the whole sequence
+        dsel = torch.arange(0, D, 4, device=dev)
+        ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)
+        cb = np.repeat(np.arange(Bsz), len(dsel))
+        cd = np.tile(np.arange(len(dsel)), Bsz)
+        a_ = (ser(x), ser(dl), _host(A[dsel]), _host(Bm), _host(Cm), _host(Dk[dsel]), ser(z), None, False,
+              cb, cd, cores, disc)
+        deferred.append((out["variants"][disc], lambda a_=a_: oracle.scan_f64(*a_), Bsz * len(dsel) * L * N,
+                         "state-updates/s", f"{Bsz * len(dsel)} channels (every 4th) x {L} steps, fp64 C oracle", cores))
     del x, dl, z, Bm, Cm, y, ws
     torch.cuda.empty_cache()
     # --- multi-head SSD scan (Mamba-2 layer) on the matrix cores ---
     t = _ssd_inputs(torch, dev)
-    for _ in range(3):
+    for _ in range(30):
         ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
     torch.cuda.synchronize()
     st = []
@@ -522,6 +565,11 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     }
     log(f"ssd: {ms * 1e3:.1f} us/launch, HBM {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}), "
         f"MFMA {tfs:.0f} TFLOP/s ({tfs / MFMA_BF16_PEAK_TFS:.1%})")
+    # oracle beside it: one (batch row, head) over the whole sequence (numpy, fp64)
+    a_ = (_host(t["x"][:1, :, :8]), _host(t["delta"][:1, :, :8]), _host(t["A"][:8]), _host(t["B"][:1]),
+          _host(t["C"][:1]), _host(t["D"][:8]), _host(t["z"][:1, :, :8]))
+    deferred.append((out["ssd"], lambda a_=a_: ssd_oracle.ssd(*a_), 8 * c["seqlen"] * c["headdim"] * c["dstate"],
+                     "state-updates/s", "8 heads of one batch row x 4096 steps, fp64 numpy oracle (one thread)", 1))
     del t
     torch.cuda.empty_cache()
     # --- causal conv1d + SiLU at the headline shape (HBM-bound) ---
@@ -554,6 +602,12 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
                      "alg_bytes_per_launch": conv_bytes},
     }
     log(f"conv1d: {ct[len(ct) // 2] * 1e3:.1f} us median, {conv_gbs:.0f} GB/s ({conv_gbs / HBM_PEAK_GBS:.1%} of HBM)")
+    out["conv1d"]["elements_per_s"] = x.numel() / (ct[len(ct) // 2] * 1e-3)
+    # oracle beside it: every 16th channel of the whole input (numpy, fp64)
+    dsel = torch.arange(0, x.shape[2], 2, device=dev)
+    a_ = (_host(x[:, :, dsel]), _host(w[dsel]), _host(bias[dsel]))
+    deferred.append((out["conv1d"], lambda a_=a_: conv_oracle.conv1d(*a_), x.shape[0] * x.shape[1] * len(dsel),
+                     "elements/s", f"every 2nd channel ({len(dsel)}) x 4 x 4096 steps, fp64 numpy oracle (one thread)", 1))
     del x, yc
     # --- backward pass at the headline shape ---
     c = synth.CONFIGS[2]
@@ -586,6 +640,15 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
     }
     log(f"backward: {ms:.3f} ms median ({upd / (ms * 1e-3):.3e} state-updates/s)")
+    # oracle beside it: 64 channels of every batch row over the whole sequence
+    dsel = torch.arange(0, D, 32, device=dev)   # (the oracle keeps per-channel dB, dC: [channels, L, N] each)
+    ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)
+    cb = np.repeat(np.arange(Bsz), len(dsel))
+    cd = np.tile(np.arange(len(dsel)), Bsz)
+    a_ = (ser(x), ser(dl), _host(A[dsel]), _host(Bm), _host(Cm), _host(Dk[dsel]), ser(z), None, ser(gy),
+          None, False, cb, cd, cores)
+    deferred.append((out["backward"], lambda a_=a_: oracle.scan_bwd_f64(*a_), Bsz * len(dsel) * L * N, "state-updates/s",
+                     f"{Bsz * len(dsel)} channels (every 32nd) x {L} steps, fp64 C oracle", cores))
     del x, dl, z, gy, Bm, Cm, ws
     torch.cuda.empty_cache()
     # --- million-token scan (chunk carries) ---
@@ -621,6 +684,19 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         "note": "all launches of one call (carry pass, combine, rescan) inside the events",
     }
     log(f"long sequence: {ms:.2f} ms/call, {upd / (ms * 1e-3):.3e} updates/s, plan {plan}")
+    # oracle beside it: 16 channels over the whole million steps
+    dsel = torch.arange(0, D, 64, device=dev)
+    ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)
+    cb = np.repeat(np.arange(Bsz), len(dsel))
+    cd = np.tile(np.arange(len(dsel)), Bsz)
+    a_ = (ser(x), ser(dl), _host(A[dsel]), _host(Bm), _host(Cm), _host(Dk[dsel]), None, None, False, cb, cd, cores)
+    deferred.append((out["long_sequence"], lambda a_=a_: oracle.scan_f64(*a_), Bsz * len(dsel) * L * N,
+                     "state-updates/s", f"{len(dsel)} channels x {L} steps, fp64 C oracle", cores))
+    # the oracle beside each measurement, on its bounded sample, after the last GPU timing
+    for entry, fn, work, unit, sample, nthr in deferred:
+        entry["cpu_baseline"] = _cpu_entry(_timed(fn), work, unit, sample, nthr)
+    log("oracle baselines of the secondary measurements: " +
+        ", ".join(f"{e['cpu_baseline']['value']:.3e} {e['cpu_baseline']['unit']}" for e, *_ in deferred))
     return out
 
 
