@@ -52,7 +52,7 @@ def _load():
                                 P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_scan.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P,
-                                    P, P, P, P, P, P, P, P, ctypes.c_int]
+                                    P, P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -117,7 +117,7 @@ def scan_f64(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fa
 
 
 def scan_bwd_f64(x, delta, A, Bm, Cm, Dskip, z, h0, gy, g_last, delta_softplus, ch_b, ch_d,
-                 nthreads=None):
+                 nthreads=None, delta_bias=None):
     """Core backward call on float64 arrays (layouts as ``scan_f64``; gy [nchan, L],
     g_last [nchan, N] or None).  Returns a dict of per-channel results: dx, ddelta, dz
     [nchan, L] (dz None without a gate), dB_c, dC_c [nchan, L, N], dA_c, dh0 [nchan, N],
@@ -125,6 +125,7 @@ def scan_bwd_f64(x, delta, A, Bm, Cm, Dskip, z, h0, gy, g_last, delta_softplus, 
     lib = _load()
     x, delta, z, gy = _f64(x), _f64(delta), _f64(z), _f64(gy)
     Bm, Cm, A, Dskip, h0, g_last = _f64(Bm), _f64(Cm), _f64(A), _f64(Dskip), _f64(h0), _f64(g_last)
+    dbias = _f64(delta_bias)
     nchan, L = x.shape
     N = A.shape[1]
     assert delta.shape == x.shape and gy.shape == x.shape and (z is None or z.shape == x.shape)
@@ -135,7 +136,7 @@ def scan_bwd_f64(x, delta, A, Bm, Cm, Dskip, z, h0, gy, g_last, delta_softplus, 
            "dB_c": np.empty((nchan, L, N)), "dC_c": np.empty((nchan, L, N)),
            "dA_c": np.empty((nchan, N)), "dD_c": np.empty(nchan), "dh0": np.empty((nchan, N))}
     rc = lib.oracle_scan_bwd(L, N, nchan, _ptr(ch_b), _ptr(ch_d), _ptr(x), _ptr(delta), _ptr(z),
-                             int(bool(delta_softplus)), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
+                             int(bool(delta_softplus)), _ptr(dbias), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
                              _ptr(h0), _ptr(gy), _ptr(g_last), _ptr(out["dx"]), _ptr(out["ddelta"]),
                              _ptr(out["dz"]), _ptr(out["dB_c"]), _ptr(out["dC_c"]), _ptr(out["dA_c"]),
                              _ptr(out["dD_c"]), _ptr(out["dh0"]), int(nthreads or default_threads()))
@@ -151,7 +152,8 @@ def scan_bwd(inp: dict, gy, g_last=None, nthreads=None):
     g_last: dLoss/dh_last [B, D, N] or None.  Returns float64 gradients with respect to
     every input: dx, ddelta, dz [B, L, D] (ddelta with respect to the raw input in
     softplus mode; dz None without a gate), dB, dC [B, L, N], dA [D, N], dD [D],
-    dh0 [B, D, N].
+    dh0 [B, D, N], and ddelta_bias [D] when ``inp`` has a "delta_bias" (the sum of ddelta
+    over batch rows and steps: the bias is added to every step's raw delta).
     """
     dtype = inp["dtype"]
     x, delta, z = inp["x"], inp["delta"], inp["z"]
@@ -170,7 +172,8 @@ def scan_bwd(inp: dict, gy, g_last=None, nthreads=None):
     glc = None if g_last is None else np.asarray(g_last, dtype=np.float64)[cb, cd, :]
     r = scan_bwd_f64(series(x), series(delta), inp["A"], _widen(inp["B"], dtype),
                      _widen(inp["C"], dtype), inp["Dskip"], series(z), h0c,
-                     series(gy, wide=False), glc, inp.get("delta_softplus", False), cb, cd, nthreads)
+                     series(gy, wide=False), glc, inp.get("delta_softplus", False), cb, cd, nthreads,
+                     inp.get("delta_bias"))
     back = lambda a: a.reshape(Bsz, D, L).transpose(0, 2, 1).copy()
     out = {"dx": back(r["dx"]), "ddelta": back(r["ddelta"]),
            "dz": None if r["dz"] is None else back(r["dz"]),
@@ -179,6 +182,8 @@ def scan_bwd(inp: dict, gy, g_last=None, nthreads=None):
            "dA": r["dA_c"].reshape(Bsz, D, N).sum(axis=0),
            "dD": r["dD_c"].reshape(Bsz, D).sum(axis=0),
            "dh0": r["dh0"].reshape(Bsz, D, N)}
+    if inp.get("delta_bias") is not None:
+        out["ddelta_bias"] = out["ddelta"].sum(axis=(0, 1))
     return out
 
 

@@ -82,7 +82,7 @@ def scan_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fal
 
 
 def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=False,
-                gy=None, g_last=None):
+                gy=None, g_last=None, delta_bias=None):
     """Reverse-mode derivative of ``scan_np`` for the loss <gy, y> + <g_last, h_last>.
 
     Written as the chain rule through the discretised operands: with
@@ -91,8 +91,9 @@ def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus
         dLoss/dh_{t-1} = A_bar_t * lam_t (+ the readout of step t-1),
     and A_bar = exp(dt A), B_bar = dt B carry those on to dt, A, B.  All float64;
     shapes as ``scan_np`` plus gy [B, L, D] and g_last [B, D, N] (either may be None
-    = zero).  Returns a dict dx, ddelta, dz, dB, dC, dA, dD, dh0 (dz None without a
-    gate; ddelta with respect to the raw input in softplus mode)."""
+    = zero) and delta_bias [D] (added to delta before the softplus).  Returns a dict dx,
+    ddelta, dz, dB, dC, dA, dD, dh0 (dz None without a gate; ddelta with respect to the
+    raw input in softplus mode) and ddelta_bias (None without a bias)."""
     x = np.asarray(x, dtype=np.float64)
     Bsz, L, D = x.shape
     A = np.asarray(A, dtype=np.float64)
@@ -100,6 +101,8 @@ def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus
     Bm = np.asarray(Bm, dtype=np.float64)
     Cm = np.asarray(Cm, dtype=np.float64)
     raw = np.asarray(delta, dtype=np.float64)
+    if delta_bias is not None:
+        raw = raw + np.asarray(delta_bias, dtype=np.float64)[None, None, :]
     dl = _softplus(raw) if delta_softplus else raw
     gy = np.zeros((Bsz, L, D)) if gy is None else np.asarray(gy, dtype=np.float64)
     zz = None if z is None else np.asarray(z, dtype=np.float64)
@@ -142,4 +145,6 @@ def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus
         out["dB"][:, t, :] += np.einsum("bdn,bd->bn", g_bbar, dl[:, t, :])
         lam = a_bar * lam
     out["dh0"] = lam
+    # the bias enters every step's raw delta: its gradient is the sum of those
+    out["ddelta_bias"] = None if delta_bias is None else out["ddelta"].sum(axis=(0, 1))
     return out

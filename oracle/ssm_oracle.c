@@ -190,7 +190,7 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
 }
 
 /*
- * Backward (adjoint) of the same scan (Mamba discretisation, no delta bias), for a loss whose gradients with respect
+ * Backward (adjoint) of the same scan (Mamba discretisation; dbias optional), for a loss whose gradients with respect
  * to the outputs are given: gy[t] = dLoss/dy[t] for every channel, and
  * g_last[n] = dLoss/dh_last[n] (or 0).  Plain reverse-mode differentiation of
  * the definition above, one channel at a time, no reordering:
@@ -210,8 +210,9 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
  *               ddt       += lam[n] (A[d,n] a_t[n] h_{t-1}[n] + B[t,n] x[t])
  *               dA[d,n]   += lam[n] dt_t a_t[n] h_{t-1}[n]
  *               lam[n]     = a_t[n] lam[n]                       (dLoss/dh_{t-1}[n])
- *       ddelta[t] = ddt (times sigmoid(delta[t]) in softplus mode, the derivative of
- *                   softplus at the raw input)
+ *       ddelta[t] = ddt (times sigmoid(delta[t] + dbias[d]) in softplus mode, the
+ *                   derivative of softplus at the raw input; the gradient of the bias is
+ *                   the sum of ddelta over the steps, which the caller forms)
  *   dh0[n] = lam[n]
  *
  * The per-channel contributions to the shared tensors are returned separately
@@ -224,6 +225,7 @@ typedef struct {
     const int64_t *ch_b, *ch_d;
     const double *x, *delta, *z;
     int delta_softplus;
+    const double *dbias;
     const double *Bm, *Cm, *A, *Dskip, *h0, *gy, *g_last;
     double *dx, *ddelta, *dz, *dB_c, *dC_c, *dA_c, *dD_c, *dh0;
     int64_t next;
@@ -243,8 +245,9 @@ static void one_channel_bwd(const bjob_t *J, int64_t c)
 
     for (int64_t n = 0; n < N; ++n)
         hs[n] = J->h0 ? J->h0[c * N + n] : 0.0;
+    const double bias = J->dbias ? J->dbias[d] : 0.0;
     for (int64_t t = 0; t < L; ++t) {
-        double dt = J->delta[c * L + t];
+        double dt = J->delta[c * L + t] + bias;
         if (J->delta_softplus)
             dt = softplus(dt);
         const double xt = J->x[c * L + t];
@@ -267,7 +270,7 @@ static void one_channel_bwd(const bjob_t *J, int64_t c)
     }
     double dD = 0.0;
     for (int64_t t = L - 1; t >= 0; --t) {
-        const double raw = J->delta[c * L + t];
+        const double raw = J->delta[c * L + t] + bias;
         const double dt = J->delta_softplus ? softplus(raw) : raw;
         const double xt = J->x[c * L + t];
         const double *Bt = J->Bm + (b * L + t) * N;
@@ -323,7 +326,7 @@ static void *worker_bwd(void *arg)
  * not written), Dskip, h0 and g_last may be NULL. */
 int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const int64_t *ch_d,
                     const double *x, const double *delta, const double *z, int delta_softplus,
-                    const double *Bm, const double *Cm, const double *A, const double *Dskip,
+                    const double *dbias, const double *Bm, const double *Cm, const double *A, const double *Dskip,
                     const double *h0, const double *gy, const double *g_last,
                     double *dx, double *ddelta, double *dz, double *dB_c, double *dC_c,
                     double *dA_c, double *dD_c, double *dh0, int nthreads)
@@ -337,7 +340,7 @@ int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, co
     bjob_t J;
     memset(&J, 0, sizeof(J));
     J.L = L; J.N = N; J.nchan = nchan; J.ch_b = ch_b; J.ch_d = ch_d;
-    J.x = x; J.delta = delta; J.z = z; J.delta_softplus = delta_softplus;
+    J.x = x; J.delta = delta; J.z = z; J.delta_softplus = delta_softplus; J.dbias = dbias;
     J.Bm = Bm; J.Cm = Cm; J.A = A; J.Dskip = Dskip; J.h0 = h0; J.gy = gy; J.g_last = g_last;
     J.dx = dx; J.ddelta = ddelta; J.dz = dz; J.dB_c = dB_c; J.dC_c = dC_c; J.dA_c = dA_c;
     J.dD_c = dD_c; J.dh0 = dh0; J.next = 0;
@@ -360,4 +363,4 @@ int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, co
     return 0;
 }
 
-int oracle_abi_version(void) { return 3; }
+int oracle_abi_version(void) { return 4; }

@@ -18,7 +18,7 @@ import oracle
 from oracle.numpy_ref import scan_bwd_np, scan_np
 
 
-def _problem(seed, Bsz=2, L=6, D=3, N=3, gate=True, h0=True, dskip=True):
+def _problem(seed, Bsz=2, L=6, D=3, N=3, gate=True, h0=True, dskip=True, bias=False):
     r = np.random.default_rng(seed)
     p = {
         "x": r.standard_normal((Bsz, L, D)),
@@ -29,6 +29,7 @@ def _problem(seed, Bsz=2, L=6, D=3, N=3, gate=True, h0=True, dskip=True):
         "A": -np.exp(r.standard_normal((D, N)) * 0.5),
         "D": r.standard_normal(D) if dskip else None,
         "h0": r.standard_normal((Bsz, D, N)) if h0 else None,
+        "bias": r.normal(0.0, 0.3, D) if bias else None,
     }
     gy = r.standard_normal((Bsz, L, D))
     gl = r.standard_normal((Bsz, D, N))
@@ -36,7 +37,8 @@ def _problem(seed, Bsz=2, L=6, D=3, N=3, gate=True, h0=True, dskip=True):
 
 
 def _loss(p, gy, gl, sp):
-    y, h = scan_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp)
+    y, h = scan_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp,
+                   delta_bias=p.get("bias"))
     return float((y * gy).sum() + (h * gl).sum())
 
 
@@ -49,9 +51,10 @@ def _c_bwd(p, gy, gl, sp):
     ser = lambda a: None if a is None else a[cb, :, cd]
     r = oracle.scan_bwd_f64(ser(p["x"]), ser(p["delta"]), p["A"], p["B"], p["C"], p["D"], ser(p["z"]),
                             None if p["h0"] is None else p["h0"][cb, cd, :], ser(gy),
-                            gl[cb, cd, :], sp, cb, cd, nthreads=2)
+                            gl[cb, cd, :], sp, cb, cd, nthreads=2, delta_bias=p.get("bias"))
     back = lambda a: a.reshape(Bsz, D, L).transpose(0, 2, 1)
     return {"x": back(r["dx"]), "delta": back(r["ddelta"]),
+            "bias": None if p.get("bias") is None else back(r["ddelta"]).sum(axis=(0, 1)),
             "z": None if r["dz"] is None else back(r["dz"]),
             "B": r["dB_c"].reshape(Bsz, D, L, N).sum(axis=1),
             "C": r["dC_c"].reshape(Bsz, D, L, N).sum(axis=1),
@@ -60,19 +63,19 @@ def _c_bwd(p, gy, gl, sp):
             "h0": r["dh0"].reshape(Bsz, D, N)}
 
 
-@pytest.mark.parametrize("seed,sp,gate,h0,dskip", [
-    (0, False, True, True, True), (1, True, True, True, True), (2, False, False, False, True),
-    (3, True, False, True, False),
+@pytest.mark.parametrize("seed,sp,gate,h0,dskip,bias", [
+    (0, False, True, True, True, False), (1, True, True, True, True, False), (2, False, False, False, True, False),
+    (3, True, False, True, False, False), (4, True, True, True, True, True), (5, False, True, False, True, True),
 ])
-def test_adjoint_equals_finite_differences(seed, sp, gate, h0, dskip):
-    p, gy, gl = _problem(seed, gate=gate, h0=h0, dskip=dskip)
+def test_adjoint_equals_finite_differences(seed, sp, gate, h0, dskip, bias):
+    p, gy, gl = _problem(seed, gate=gate, h0=h0, dskip=dskip, bias=bias)
     if sp:
         p["delta"] = np.log(np.expm1(p["delta"]))      # raw input u, dt = softplus(u)
     g = _c_bwd(p, gy, gl, sp)
     worst = 0.0
     for name, arr in p.items():
         if arr is None:
-            assert g[name] is None or name in ("D", "h0")
+            assert g[name] is None or name in ("D", "h0", "bias")
             continue
         it = np.nditer(arr, flags=["multi_index"])
         for _ in it:
@@ -117,30 +120,37 @@ def test_linear_in_incoming_gradient():
     g1, g2 = _c_bwd(p, gy, gl, False), _c_bwd(p, gy2, gl2, False)
     g12 = _c_bwd(p, a * gy + b * gy2, a * gl + b * gl2, False)
     for k in g12:
-        np.testing.assert_allclose(g12[k], a * g1[k] + b * g2[k], rtol=1e-10, atol=1e-10)
+        if g12[k] is not None:
+            np.testing.assert_allclose(g12[k], a * g1[k] + b * g2[k], rtol=1e-10, atol=1e-10)
 
 
-@pytest.mark.parametrize("sp", [False, True])
-def test_c_and_numpy_backward_agree(sp):
-    p, gy, gl = _problem(21, Bsz=3, L=50, D=6, N=7)
+@pytest.mark.parametrize("sp,bias", [(False, False), (True, False), (True, True)])
+def test_c_and_numpy_backward_agree(sp, bias):
+    p, gy, gl = _problem(21, Bsz=3, L=50, D=6, N=7, bias=bias)
     if sp:
         p["delta"] = np.log(np.expm1(p["delta"]))
     g = _c_bwd(p, gy, gl, sp)
-    n = scan_bwd_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl)
+    n = scan_bwd_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl,
+                    delta_bias=p["bias"])
     names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0"}
+    if bias:
+        names["bias"] = "ddelta_bias"
     for k, nk in names.items():
         np.testing.assert_allclose(g[k], n[nk], rtol=1e-11, atol=1e-11)
 
 
 def test_storage_wrapper_matches_core():
     import synth
-    inp = synth.scan_inputs(2, 33, 5, 16, "bf16", seed=5, gate=True, d_kind="normal", a_kind="random", h0=True)
+    inp = synth.scan_inputs(2, 33, 5, 16, "bf16", seed=5, gate=True, d_kind="normal", a_kind="random", h0=True,
+                            softplus_input=True)
+    inp["delta_bias"] = synth.make_delta_bias(5, 5)
     r = np.random.default_rng(3)
     gy = r.standard_normal((2, 33, 5))
     out = oracle.scan_bwd(inp, gy)
     w = lambda a: synth.to_f64(a, "bf16")
     n = scan_bwd_np(w(inp["x"]), w(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["Dskip"],
-                    w(inp["z"]), inp["h0"], False, gy, None)
+                    w(inp["z"]), inp["h0"], True, gy, None, delta_bias=inp["delta_bias"])
+    assert n["ddelta_bias"] is not None
     for k in n:
         np.testing.assert_allclose(out[k], n[k], rtol=1e-11, atol=1e-11)
 
@@ -157,6 +167,8 @@ _MUTANTS = {
     "dB_with_wrong_input": ("g_bbar = lam * x[:, t, :, None]", "g_bbar = lam * hs[t]"),
     "softplus_chain_dropped": ("g_dt / (1.0 + np.exp(-raw[:, t, :]))", "g_dt"),
     "dC_with_old_state": ("gy0, hs[t + 1])", "gy0, hs[t])"),
+    "bias_ignored": ("raw = raw + np.asarray(delta_bias", "raw = raw + 0.0 * np.asarray(delta_bias"),
+    "bias_gradient_of_one_row": ('out["ddelta"].sum(axis=(0, 1))', 'out["ddelta"][0].sum(axis=0)'),
 }
 
 
@@ -172,13 +184,18 @@ def _mutated_bwd(kind):
 
 
 def _fd_worst(fn, seed, sp):
-    p, gy, gl = _problem(seed)
+    # the softplus case also carries a delta bias
+    p, gy, gl = _problem(seed, bias=sp)
     if sp:
         p["delta"] = np.log(np.expm1(p["delta"]))
-    g = fn(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl)
-    names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0"}
+    g = fn(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl,
+           delta_bias=p["bias"])
+    names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0",
+             "bias": "ddelta_bias"}
     worst = 0.0
     for name, arr in p.items():
+        if arr is None:
+            continue
         it = np.nditer(arr, flags=["multi_index"])
         for _ in it:
             idx = it.multi_index
