@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 #define SSM_MAX_DSTATE 16
 
 typedef enum ssm_dtype {
@@ -213,12 +213,15 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *     dC_t += gy0 h_t,   dB_t += lam dt x_t,   dA += lam dt exp(dt A) h_{t-1}
  *     dx_t = D gy0 + dt sum_n lam B_t,  ddelta_t = sum_n lam (A exp(dt A) h_{t-1} + B_t x_t)
  *     lam = exp(dt A) lam,   dh0 = lam after t = 0
- * (ddelta_t is multiplied by sigmoid(delta_t) in softplus mode: the derivative with
- * respect to the raw input).
+ * (ddelta_t is multiplied by sigmoid(delta_t + delta_bias) in softplus mode: the
+ * derivative with respect to the raw input).  The discretisation is Mamba's (the
+ * ssm_variant default); a delta bias is taken as its own argument.
  *
  * Inputs as ssm_scan_fwd (same layouts and dtypes), plus
  *   dy        [batch, seqlen, dim]   dtype   required
  *   dh_last   [batch, dim, dstate]   fp32    NULL = zero
+ *   delta_bias [dim]                 fp32    NULL = no bias; else the step size is
+ *             delta + delta_bias[d] (before the softplus), as in ssm_variant
  * Outputs (device memory owned by the caller; none may overlap an input or another
  * output; each is fully overwritten):
  *   dx, ddelta [batch, seqlen, dim]  dtype   required
@@ -227,11 +230,14 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   dA        [dim, dstate]          fp32    required (sum over batch and time)
  *   dD        [dim]                  fp32    required when Dskip is given, else ignored
  *   dh0       [batch, dim, dstate]   fp32    NULL = not stored
+ *   ddelta_bias [dim]                fp32    required when delta_bias is given, else
+ *             ignored: the sum of ddelta over batch and time
  *   workspace device memory of ssm_scan_bwd_workspace_bytes() bytes (state
  *             checkpoints every 8 steps, partial sums)
  *
  * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  batch or dim
- * == 0 is a no-op; seqlen == 0 sets dh0 = dh_last (or zeros) and dA, dD to zero.
+ * == 0 is a no-op; seqlen == 0 sets dh0 = dh_last (or zeros) and dA, dD, ddelta_bias
+ * to zero.
  * Deterministic: every reduction runs in a fixed order.
  */
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
@@ -239,7 +245,8 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  const void *C, const float *Dskip, const void *z, const float *h0,
                  const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                  void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
-                 void *workspace, size_t workspace_bytes, void *stream);
+                 const float *delta_bias, float *ddelta_bias, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 /*
  * Causal depthwise convolution along the sequence, then SiLU: the step before the scan

@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 2     # SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 3     # SSM_ABI_VERSION of include/ssm.h
 
 
 class SSMError(RuntimeError):
@@ -88,7 +88,7 @@ def lib():
     L.ssm_scan_bwd_workspace_bytes.restype = SZ
     L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
     L.ssm_scan_bwd.restype = I32
-    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, P, SZ, P]
+    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, P, P, P, SZ, P]
     L.ssm_conv1d_fwd.restype = I32
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
     L.ssm_ssd_fwd.restype = I32
@@ -276,13 +276,14 @@ def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, *,
-             delta_softplus=False, need_dh0=True, workspace=None, stream=None):
-    """Gradients of a loss through scan_fwd, given dy = dLoss/dy [B, L, D] (same dtype as
-    x) and optionally dh_last = dLoss/dh_last [B, D, N] fp32.
+             delta_softplus=False, delta_bias=None, need_dh0=True, workspace=None, stream=None):
+    """Gradients of a loss through scan_fwd (Mamba discretisation), given dy = dLoss/dy
+    [B, L, D] (same dtype as x) and optionally dh_last = dLoss/dh_last [B, D, N] fp32.
+    delta_bias [D] fp32: as in scan_fwd.
 
     Returns a dict: dx, ddelta, dz (None without z) in x's dtype [B, L, D]; dB, dC in
-    x's dtype [B, L, N]; dA [D, N], dD [D] (None without D) and dh0 [B, D, N] in fp32
-    (dh0 None when need_dh0 is false).
+    x's dtype [B, L, N]; dA [D, N], dD [D] (None without D), ddelta_bias [D] (None
+    without a bias) and dh0 [B, D, N] in fp32 (dh0 None when need_dh0 is false).
     """
     import torch
     if x.dim() != 3 or A.dim() != 2:
@@ -298,7 +299,8 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
                                 (z, "z", (Bsz, L, Dm), dt), (B, "B", (Bsz, L, N), dt),
                                 (C, "C", (Bsz, L, N), dt), (A, "A", (Dm, N), torch.float32),
                                 (D, "D", (Dm,), torch.float32), (h0, "h0", (Bsz, Dm, N), torch.float32),
-                                (dy, "dy", (Bsz, L, Dm), dt), (dh_last, "dh_last", (Bsz, Dm, N), torch.float32)):
+                                (dy, "dy", (Bsz, L, Dm), dt), (dh_last, "dh_last", (Bsz, Dm, N), torch.float32),
+                                (delta_bias, "delta_bias", (Dm,), torch.float32)):
         _need(t, name, shape, tdt, dev)
     code = _dtype_code(x)
     out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
@@ -307,7 +309,8 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
            "dC": torch.empty((Bsz, L, N), dtype=dt, device=dev),
            "dA": torch.empty((Dm, N), dtype=torch.float32, device=dev),
            "dD": torch.empty((Dm,), dtype=torch.float32, device=dev) if D is not None else None,
-           "dh0": torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if need_dh0 else None}
+           "dh0": torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if need_dh0 else None,
+           "ddelta_bias": torch.empty((Dm,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
     ws_bytes = int(lib().ssm_scan_bwd_workspace_bytes(Bsz, L, Dm, N, code))
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -316,31 +319,32 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
                             _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["dx"]),
                             _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
                             _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]), int(bool(delta_softplus)),
-                            _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+                            _ptr(delta_bias), _ptr(out["ddelta_bias"]), _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_scan_bwd")
     return out
 
 
-def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=False):
+def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=False, delta_bias=None):
     """Differentiable selective scan: y = scan_fwd(...) with a torch autograd backward
-    through scan_bwd (gradients for every tensor argument)."""
+    through scan_bwd (gradients for every tensor argument, delta_bias included)."""
     import torch
 
     class _Scan(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, x, delta, A, B, C, D, z, h0):
-            y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus)
-            ctx.save_for_backward(x, delta, A, B, C, D, z, h0)
+        def forward(ctx, x, delta, A, B, C, D, z, h0, delta_bias):
+            y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus, delta_bias=delta_bias)
+            ctx.save_for_backward(x, delta, A, B, C, D, z, h0, delta_bias)
             return y
 
         @staticmethod
         def backward(ctx, gy):
-            x, delta, A, B, C, D, z, h0 = ctx.saved_tensors
+            x, delta, A, B, C, D, z, h0, delta_bias = ctx.saved_tensors
             g = scan_bwd(x, delta, A, B, C, D, z, h0, gy.contiguous(), delta_softplus=delta_softplus,
-                         need_dh0=h0 is not None and ctx.needs_input_grad[7])
-            return g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"]
+                         delta_bias=delta_bias, need_dh0=h0 is not None and ctx.needs_input_grad[7])
+            return (g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"],
+                    g["ddelta_bias"])
 
-    return _Scan.apply(x, delta, A, B, C, D, z, h0)
+    return _Scan.apply(x, delta, A, B, C, D, z, h0, delta_bias)
 
 
 def conv1d_fwd(x, w, bias=None, state=None, *, silu=True, return_state=False, out=None, stream=None):

@@ -11,6 +11,9 @@
 //     dA     += lam_t dt_t a_t h_{t-1}                          (summed over b, t)
 //     lam_{t-1} = a_t lam_t,      dh0 = lam_{-1}
 //     dz_t    = gy_t y0_t silu'(z_t),   y0_t = sum_n C_t h_t + D x_t
+// With a per-channel bias on the step size (dt = softplus(delta + bias), or delta + bias),
+// ddelta is taken with respect to the raw input, and the bias's gradient is its sum over
+// batch rows and steps.
 // (reverse of the step in managen.ai "Mamba: State Space Models Challenge Transformers",
 // section "Selective Scan Algorithm"; the need for gradients through the step size is in
 // the skill page "State Space Models Mamba", Verification Checklist).
@@ -26,7 +29,7 @@
 //      per (step, state) the 64 channels' terms give this workgroup's share of dB, dC.
 // The per-lane input rows (x, delta, dy, z) of the next block are loaded while the current
 // one is processed; the block's B_t, C_t rows go through LDS.  A finishing kernel sums the
-// shares of dB, dC over channel blocks and dA, dD over batch rows.
+// shares of dB, dC over channel blocks and dA, dD, dbias over batch rows.
 #include "ssm_device.h"
 
 #include <type_traits>
@@ -79,6 +82,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         Al[g] = Av[g] * kLog2e;
     }
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
+    const float dbv = a.dbias ? a.dbias[d] : 0.0f;
     const float *ck = a.ckpt + (b * nblk * kN + n0) * D + d;   // block k, state n0 + g at + (k * kN + g) * D
     auto dt_of = [&](float raw) { return a.softplus ? softplus_f(raw) : raw; };
     // rows of block k, clamped into the sequence (rows past its end are never used)
@@ -104,6 +108,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     }
     gA[0] = gA[1] = 0.0f;
     float gDp = 0.0f;   // sum of gy0 x over this thread's steps (step w of every block)
+    float gBp = 0.0f;   // sum of ddelta over the same steps (the bias's share)
     const int64_t ndb = D / 64;
     // raw rows of one block; the next block's are requested once the current block's
     // forward recompute has consumed them, so they arrive during its adjoint and reductions
@@ -140,7 +145,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
             if (F || i < nb) {
-                const float raw = widen_v(rd[i]);
+                const float raw = widen_v(rd[i]) + dbv;
                 const float dt = dt_of(raw);
                 const float xv = widen_v(rx[i]);
                 const float u = dt * xv;
@@ -221,6 +226,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 gDp = __builtin_fmaf(g0, xv, gDp);
                 float gdt = __builtin_fmaf(xv, S3, S1);
                 if (a.softplus) gdt *= sigmoid_f(raw);
+                gBp += gdt;
                 put(static_cast<T *>(a.ddelta) + b * L * D, t * D + d, gdt);
                 put(static_cast<T *>(a.dx) + b * L * D, t * D + d, __builtin_fmaf(dt, S3, dsk * g0));
             }
@@ -250,6 +256,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     if (a.dh0) *reinterpret_cast<float2 *>(a.dh0 + (b * D + d) * kN + n0) = make_float2(lam[0], lam[1]);
     *reinterpret_cast<float2 *>(a.partA + (b * D + d) * kN + n0) = make_float2(gA[0], gA[1]);
     a.partD[(b * kW + w) * D + d] = gDp;
+    if (a.ddbias) a.partDB[(b * kW + w) * D + d] = gBp;
 }
 
 // dB, dC [B][L][16] = sum over channel blocks of the workgroup shares
@@ -269,7 +276,7 @@ __global__ void __launch_bounds__(256) bwd_finish_bc_kernel(BwdArgs a) {
     put(static_cast<T *>(which ? a.dC : a.dB), r, s);
 }
 
-// dA [D][16] = sum over batch rows; dD [D] = sum over batch rows and waves
+// dA [D][16] = sum over batch rows; dD, dbias [D] = sums over batch rows and waves
 __global__ void __launch_bounds__(256) bwd_finish_ad_kernel(BwdArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nA = a.D * kN;
@@ -283,6 +290,12 @@ __global__ void __launch_bounds__(256) bwd_finish_ad_kernel(BwdArgs a) {
         for (int64_t b = 0; b < a.B; ++b)
             for (int w = 0; w < kW; ++w) s += a.partD[(b * kW + w) * a.D + d];
         a.dD[d] = s;
+    } else if (i >= nA + a.D && i < nA + 2 * a.D && a.ddbias) {
+        const int64_t d = i - nA - a.D;
+        float s = 0.0f;
+        for (int64_t b = 0; b < a.B; ++b)
+            for (int w = 0; w < kW; ++w) s += a.partDB[(b * kW + w) * a.D + d];
+        a.ddbias[d] = s;
     }
 }
 
@@ -297,7 +310,7 @@ hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
     hipLaunchKernelGGL((bwd_finish_bc_kernel<T>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nad = a.D * kN + a.D;
+    const int64_t nad = a.D * kN + 2 * a.D;
     hipLaunchKernelGGL(bwd_finish_ad_kernel, dim3(static_cast<unsigned>((nad + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }

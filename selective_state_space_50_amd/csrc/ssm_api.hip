@@ -149,13 +149,14 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
                             const void *C, const float *Dskip, const void *z, const float *h0,
                             const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                             void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                            const float *delta_bias, float *ddelta_bias, void *workspace,
+                            size_t workspace_bytes, void *stream) {
     using namespace ssm;
     clear_error();
     BwdPlan p;
     int st = check_scan_bwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy,
-                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, workspace,
-                            workspace_bytes, &p);
+                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, delta_bias,
+                            ddelta_bias, workspace, workspace_bytes, &p);
     if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -179,6 +180,12 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
             e = hipGetLastError();
             if (e != hipSuccess) return hip_fail("fill_state launch", e);
         }
+        if (delta_bias) {
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
+                               0, s, ddelta_bias, static_cast<const float *>(nullptr), dim);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        }
         return SSM_OK;
     }
     char *ws = static_cast<char *>(workspace);
@@ -191,6 +198,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         fa.x = x; fa.delta = delta; fa.z = nullptr; fa.Bm = B; fa.Cm = C;
         fa.A = A; fa.Dskip = nullptr; fa.h0 = h0; fa.h_last = nullptr; fa.y = nullptr;
         fa.softplus = delta_softplus;
+        fa.dbias = delta_bias;
         fa.NW = p.fwd.NW;
         fa.chunk_len = p.fwd.chunk_len;
         fa.n_chunks = 1;
@@ -218,6 +226,9 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.partBC = reinterpret_cast<float *>(ws + p.partBC_off);
     a.partA = reinterpret_cast<float *>(ws + p.partA_off);
     a.partD = reinterpret_cast<float *>(ws + p.partD_off);
+    a.dbias = delta_bias;
+    a.ddbias = delta_bias ? ddelta_bias : nullptr;
+    a.partDB = reinterpret_cast<float *>(ws + p.partDB_off);
     e = launch_scan_bwd(a, bf16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
 }

@@ -62,6 +62,9 @@ struct BwdArgs {
     float *partBC;        // [2][B][D/64][L][16] per-workgroup shares of dB, dC
     float *partA;         // [B][D][16] per-batch-row shares of dA
     float *partD;         // [B][8][D] per-(row, wave) shares of dD
+    const float *dbias;   // [D] added to delta before the softplus, or null
+    float *ddbias;        // [D] gradient of dbias (written when dbias is given)
+    float *partDB;        // [B][8][D] per-(row, wave) shares of ddbias
 };
 
 struct SsdArgs {

@@ -376,6 +376,8 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
     ws = align_up(ws + B * D * 16 * sizeof(float), kWsAlign);
     p.partD_off = ws;
     ws = align_up(ws + B * 8 * D * sizeof(float), kWsAlign);
+    p.partDB_off = ws;
+    ws = align_up(ws + B * 8 * D * sizeof(float), kWsAlign);
     p.ws_bytes = (batch == 0 || seqlen == 0 || dim == 0) ? 0 : ws;
     *plan = p;
     return SSM_OK;
@@ -386,7 +388,8 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const float *Dskip, const void *z, const float *h0, const void *dy,
                    const float *dh_last, const void *dx, const void *ddelta, const float *dA,
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
-                   int delta_softplus, const void *workspace, size_t workspace_bytes, BwdPlan *plan) {
+                   int delta_softplus, const float *delta_bias, const float *ddelta_bias,
+                   const void *workspace, size_t workspace_bytes, BwdPlan *plan) {
     int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
     if (st != SSM_OK) return st;
     if (delta_softplus != 0 && delta_softplus != 1) {
@@ -394,7 +397,8 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
         return SSM_EINVAL;
     }
     if (batch == 0 || dim == 0) return SSM_OK;
-    const char *missing = !A ? "A" : !dA ? "dA" : (z && !dz) ? "dz (z is given)" : (Dskip && !dD) ? "dD (Dskip is given)" : nullptr;
+    const char *missing = !A ? "A" : !dA ? "dA" : (z && !dz) ? "dz (z is given)" : (Dskip && !dD) ? "dD (Dskip is given)" :
+                          (delta_bias && !ddelta_bias) ? "ddelta_bias (delta_bias is given)" : nullptr;
     if (!missing && seqlen > 0)
         missing = !x ? "x" : !delta ? "delta" : !B ? "B" : !C ? "C" : !dy ? "dy" : !dx ? "dx" :
                   !ddelta ? "ddelta" : !dB ? "dB" : !dC ? "dC" : nullptr;
@@ -410,16 +414,18 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
         range("x", x, tok), range("delta", delta, tok), range("z", z, tok), range("B", B, bc),
         range("C", C, bc), range("A", A, dim * dstate * 4), range("Dskip", Dskip, dim * 4),
         range("h0", h0, stb), range("dy", dy, tok), range("dh_last", dh_last, stb),
+        range("delta_bias", delta_bias, dim * 4),
         // outputs from here on
         range("dx", dx, tok), range("ddelta", ddelta, tok), range("dA", dA, dim * dstate * 4),
         range("dB", dB, bc), range("dC", dC, bc), range("dD", Dskip ? dD : nullptr, dim * 4),
         range("dz", z ? dz : nullptr, tok), range("dh0", dh0, stb),
+        range("ddelta_bias", delta_bias ? ddelta_bias : nullptr, dim * 4),
         range("workspace", workspace, static_cast<int64_t>(plan->ws_bytes)),
     };
     const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
     st = check_aligned(all, n_all);
     if (st != SSM_OK) return st;
-    st = check_no_overlap(all + 10, n_all - 10, all, n_all);
+    st = check_no_overlap(all + 11, n_all - 11, all, n_all);
     if (st != SSM_OK) return st;
     if (plan->ws_bytes > 0 && (!workspace || workspace_bytes < plan->ws_bytes)) {
         set_error("workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,

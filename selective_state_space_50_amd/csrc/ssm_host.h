@@ -64,7 +64,7 @@ inline const float *variant_bias(const ssm_variant *v) { return v ? v->delta_bia
 struct BwdPlan {
     int64_t nblk = 0;       // 8-step blocks of the reverse sweep
     ScanPlan fwd;           // the checkpoint pass: the specialised forward kernel, one chunk
-    size_t ckpt_off = 0, bc_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0;
+    size_t ckpt_off = 0, bc_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0, partDB_off = 0;
     size_t ws_bytes = 0;
 };
 
@@ -77,7 +77,8 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const float *Dskip, const void *z, const float *h0, const void *dy,
                    const float *dh_last, const void *dx, const void *ddelta, const float *dA,
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
-                   int delta_softplus, const void *workspace, size_t workspace_bytes, BwdPlan *plan);
+                   int delta_softplus, const float *delta_bias, const float *ddelta_bias,
+                   const void *workspace, size_t workspace_bytes, BwdPlan *plan);
 
 // Argument checks of the convolution entry points.
 int check_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,

@@ -55,6 +55,28 @@ int main() {
         EXPECT(check_state_update(256, 4096, 16, 1, h0, x, dl, A, B, C, Dk, z, y, 0, &bad1) == SSM_EINVAL);
         EXPECT(check_state_update(256, 4096, 16, 1, h0, x, dl, A, B, C, Dk, z, y, 0, &mis) == SSM_EINVAL);
     }
+    // backward: the delta bias needs its gradient output, aligned and apart from the others
+    {
+        BwdPlan bp;
+        void *dx = P(base + 12 * gap), *ddl = P(base + 13 * gap), *dB = P(base + 14 * gap), *dC = P(base + 15 * gap);
+        float *dA = static_cast<float *>(P(base + 16 * gap)), *dD = static_cast<float *>(P(base + 17 * gap));
+        void *dz = P(base + 18 * gap), *dy = P(base + 19 * gap), *bws = P(base + 20 * gap);
+        float *bias = static_cast<float *>(P(base + 21 * gap)), *dbias = static_cast<float *>(P(base + 22 * gap));
+        auto bw = [&](const float *bi, const float *dbi) {
+            return check_scan_bwd(2, 1000, 256, 16, SSM_DTYPE_BF16, x, dl, A, B, C, Dk, z, nullptr, dy, nullptr,
+                                  dx, ddl, dA, dB, dC, dD, dz, nullptr, 1, bi, dbi, bws, size_t(1) << 30, &bp);
+        };
+        EXPECT(bw(nullptr, nullptr) == SSM_OK);
+        EXPECT(bw(bias, dbias) == SSM_OK);
+        EXPECT(bp.partDB_off > bp.partD_off && bp.ws_bytes >= bp.partDB_off + size_t(2) * 8 * 256 * 4);
+        EXPECT(bw(nullptr, dbias) == SSM_OK);    // ignored without a bias
+        EXPECT(bw(bias, nullptr) == SSM_EINVAL);
+        EXPECT(std::strstr(ssm_last_error(), "ddelta_bias") != nullptr);
+        EXPECT(bw(static_cast<float *>(P(base + 21 * gap + 4)), dbias) == SSM_EINVAL);
+        EXPECT(bw(bias, static_cast<float *>(dx)) == SSM_EINVAL);    // overlaps dx
+        EXPECT(std::strstr(ssm_last_error(), "overlaps") != nullptr);
+        EXPECT(bw(bias, bias) == SSM_EINVAL);                        // output on an input
+    }
     // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);

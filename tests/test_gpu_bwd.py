@@ -19,11 +19,15 @@ def ssm():
     return m
 
 
-def _case(Bsz, L, D, dt, gate, h0, dhl, sp, dskip, seed):
+def _case(Bsz, L, D, dt, gate, h0, dhl, sp, dskip, seed, bias=False):
     inp = synth.scan_inputs(Bsz, L, D, 16, dt, seed=seed, gate=gate, d_kind="normal",
                             a_kind="random", softplus_input=sp, h0=h0)
     if not dskip:
         inp["Dskip"] = None
+    if bias:
+        b = synth.make_delta_bias(seed, D)
+        # without the softplus the bias shifts the step itself: keep it small and positive
+        inp["delta_bias"] = b if sp else (0.05 * np.abs(b)).astype(np.float32)
     r = np.random.default_rng(seed + 1000)
     gy = synth.store(r.standard_normal((Bsz, L, D)).astype(np.float32), dt)
     gl = r.standard_normal((Bsz, D, 16)).astype(np.float32) if dhl else None
@@ -35,9 +39,10 @@ def _run(ssm, inp, gy, gl):
     dt = inp["dtype"]
     t = device_inputs(inp)
     Dt = t["D"]
+    db = None if inp.get("delta_bias") is None else torch.from_numpy(inp["delta_bias"]).cuda()
     g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], Dt, t["z"], t["h0"], to_dev(gy, dt),
                      None if gl is None else torch.from_numpy(gl).cuda(),
-                     delta_softplus=inp["delta_softplus"])
+                     delta_softplus=inp["delta_softplus"], delta_bias=db)
     torch.cuda.synchronize()
     return {k: (None if v is None else to_host(v)) for k, v in g.items()}
 
@@ -49,7 +54,7 @@ def _check(g, r, dt, label):
             assert g[k] is None, k
             continue
         worst[k] = assert_close_grad(g[k], r[k], dt, f"{label} {k}")
-    for k in ("dA", "dD", "dh0"):
+    for k in ("dA", "dD", "dh0", "ddelta_bias"):
         if g[k] is None:
             continue
         worst[k] = assert_close_grad(g[k], r[k], "f32", f"{label} {k}")   # fp32 outputs
@@ -83,6 +88,18 @@ def test_backward_parity(ssm, Bsz, L, D, dt, gate, h0, dhl, sp, dskip):
     _check(g, r, dt, f"{Bsz}x{L}x{D} {dt} gate={gate} h0={h0} dh_last={dhl} softplus={sp} D={dskip}")
 
 
+@pytest.mark.parametrize("Bsz,L,D,dt,sp", [(2, 100, 128, "bf16", True), (1, 333, 64, "f32", False),
+                                           (3, 1000, 256, "f32", True), (2, 1, 64, "bf16", True)])
+def test_backward_with_delta_bias(ssm, Bsz, L, D, dt, sp):
+    """A per-channel bias on the step size (Mamba's dt_proj bias): ddelta with respect to
+    the raw input, and the bias's own gradient, the sum over rows and steps."""
+    inp, gy, gl = _case(Bsz, L, D, dt, True, True, True, sp, True, seed=90 + L, bias=True)
+    g = _run(ssm, inp, gy, gl)
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    assert g["ddelta_bias"] is not None and r["ddelta_bias"] is not None
+    _check(g, r, dt, f"{Bsz}x{L}x{D} {dt} softplus={sp} delta bias")
+
+
 def test_backward_deterministic(ssm):
     inp, gy, gl = _case(2, 200, 128, "bf16", True, True, True, False, True, seed=7)
     a = _run(ssm, inp, gy, gl)
@@ -102,6 +119,11 @@ def test_backward_empty_and_unsupported(ssm):
                      Dk, None, None, x, hl)
     torch.cuda.synchronize()
     assert torch.equal(g["dh0"], hl) and float(g["dA"].abs().sum()) == 0.0 and float(g["dD"].abs().sum()) == 0.0
+    bias = torch.ones(64, device="cuda")
+    g = ssm.scan_bwd(x, x, A, torch.zeros((2, 0, 16), device="cuda"), torch.zeros((2, 0, 16), device="cuda"),
+                     Dk, None, None, x, hl, delta_bias=bias)
+    torch.cuda.synchronize()
+    assert float(g["ddelta_bias"].abs().sum()) == 0.0
     xs = torch.zeros((1, 4, 96), device="cuda")
     with pytest.raises(ssm.SSMError) as e:
         ssm.scan_bwd(xs, xs, torch.zeros((96, 16), device="cuda"), torch.zeros((1, 4, 16), device="cuda"),
@@ -113,13 +135,15 @@ def test_autograd_matches_oracle(ssm):
     """selective_scan's torch autograd backward is scan_bwd: gradients of <w, y> for
     every input against the oracle."""
     import torch
-    inp, gy, _ = _case(2, 50, 64, "f32", True, True, False, True, True, seed=3)
+    inp, gy, _ = _case(2, 50, 64, "f32", True, True, False, True, True, seed=3, bias=True)
     t = device_inputs(inp)
-    leaves = {k: t[k].clone().requires_grad_(True) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0")}
+    t["bias"] = torch.from_numpy(inp["delta_bias"]).cuda()
+    leaves = {k: t[k].clone().requires_grad_(True) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "bias")}
     y = ssm.selective_scan(leaves["x"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"], leaves["D"],
-                           leaves["z"], leaves["h0"], delta_softplus=True)
+                           leaves["z"], leaves["h0"], delta_softplus=True, delta_bias=leaves["bias"])
     (y * to_dev(gy, "f32")).sum().backward()
     r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"))
-    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0",
+             "bias": "ddelta_bias"}
     for k, rk in names.items():
         assert_close_grad(to_host(leaves[k].grad), r[rk], "f32", f"autograd {k}")
