@@ -80,9 +80,6 @@ struct __align__(16) SsdSmem {
     float ebeg[kQ];            // exp(cum_t): decay of the carried state to step t
 };
 
-__device__ __forceinline__ f4 mfma(s4 a, s4 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f4 mfma32(s8 a, s8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
@@ -305,10 +302,14 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
                         acc = mfma32(xa, cat(sm.mhi[tile_of(k, i)][lane], sm.mhi[tile_of(k + 1, i)][lane]), acc);
                         acc = mfma32(xa, cat(sm.mlo[tile_of(k, i)][lane], sm.mlo[tile_of(k + 1, i)][lane]), acc);
                     }
-                    if (k == i) {
-                        const s4 xa = lds4(xr + 16 * k);
-                        acc = mfma(xa, sm.mhi[tile_of(k, i)][lane], acc);
-                        acc = mfma(xa, sm.mlo[tile_of(k, i)][lane], acc);
+                    if (k == i) {   // the diagonal block alone: K = 32 with a zero upper half
+                        // (one opcode along the accumulation chain: a K = 16 product reading
+                        // as its accumulator the result of a K = 32 product issued just before
+                        // it can read stale values, and the compiler schedules no wait there)
+                        const s4 zero = {0, 0, 0, 0};
+                        const s8 xa = cat(lds4(xr + 16 * k), zero);
+                        acc = mfma32(xa, cat(sm.mhi[tile_of(k, i)][lane], zero), acc);
+                        acc = mfma32(xa, cat(sm.mlo[tile_of(k, i)][lane], zero), acc);
                     }
                 }
                 // lane: p = 16 pb + 4 lg + j, t = 16 i + lr
