@@ -147,3 +147,50 @@ def test_autograd_matches_oracle(ssm):
              "bias": "ddelta_bias"}
     for k, rk in names.items():
         assert_close_grad(to_host(leaves[k].grad), r[rk], "f32", f"autograd {k}")
+
+
+@pytest.mark.timeout(900)
+def test_backward_headline_shape_full(ssm):
+    """The backward at the B4 L4096 D4096 N16 bf16 gated layer, in the launch the bench
+    times (no h0, no dh_last, no dh0): every output against the fp64 oracle.  The oracle
+    runs over 1024-channel batches; dB, dC (sums over channels), dA, dD (sums over rows)
+    are accumulated over the batches."""
+    import torch
+    c = synth.CONFIGS[2]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    inp = synth.config_inputs(2)
+    gy = synth.store(np.random.default_rng(2024).standard_normal((Bsz, L, D), dtype=np.float32), "bf16")
+    t = device_inputs(inp)
+    g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, to_dev(gy, "bf16"),
+                     need_dh0=False)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddelta", "dz", "dB", "dC", "dA", "dD"):
+        assert bool(torch.isfinite(g[k].float()).all()), k
+    w = lambda a: synth.to_f64(a, "bf16")
+    Bw, Cw = w(inp["B"]), w(inp["C"])
+    dB = np.zeros((Bsz, L, N))
+    dC = np.zeros((Bsz, L, N))
+    dA = np.zeros((D, N))
+    dD = np.zeros(D)
+    worst = {}
+    K = 1024
+    for b in range(Bsz):
+        for d0 in range(0, D, K):
+            sl = slice(d0, d0 + K)
+            ser = lambda a: np.ascontiguousarray(a[b, :, sl].T)
+            r = oracle.scan_bwd_f64(w(ser(inp["x"])), w(ser(inp["delta"])), inp["A"], Bw, Cw, inp["Dskip"],
+                                    w(ser(inp["z"])), None, w(ser(gy)), None, False,
+                                    np.full(K, b), np.arange(d0, d0 + K))
+            for k in ("dx", "ddelta", "dz"):
+                gk = to_host(g[k][b, :, sl]).T
+                worst[k] = max(worst.get(k, 0.0), assert_close_grad(gk, r[k], "bf16", f"headline {k} b={b} d0={d0}"))
+            dB[b] += r["dB_c"].sum(axis=0)
+            dC[b] += r["dC_c"].sum(axis=0)
+            dA[sl] += r["dA_c"]
+            dD[sl] += r["dD_c"]
+    worst["dB"] = assert_close_grad(to_host(g["dB"]), dB, "bf16", "headline dB")
+    worst["dC"] = assert_close_grad(to_host(g["dC"]), dC, "bf16", "headline dC")
+    worst["dA"] = assert_close_grad(to_host(g["dA"]), dA, "f32", "headline dA")
+    worst["dD"] = assert_close_grad(to_host(g["dD"]), dD, "f32", "headline dD")
+    print("[parity] backward headline shape: worst ratios " + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()),
+          flush=True)

@@ -90,3 +90,16 @@ def test_conv_errors(ssm):
     with pytest.raises(ssm.SSMError) as e:
         ssm.conv1d_fwd(x, torch.zeros((8, 4), device="cuda"), out=x)   # y overlaps x
     assert e.value.status == ssm.SSM_EINVAL
+
+
+@pytest.mark.timeout(600)
+def test_conv_headline_shape_full(ssm):
+    """x [4, 4096, 4096] bf16, width 4, bias, SiLU (the layer shape the bench times), no
+    carried state: every output against the fp64 oracle."""
+    import torch
+    x, _, w, bias = _inputs(4, 4096, 4096, 4, "bf16", seed=4096)
+    y = ssm.conv1d_fwd(to_dev(x, "bf16"), torch.from_numpy(w).cuda(), torch.from_numpy(bias).cuda())
+    torch.cuda.synchronize()
+    yr, _ = conv1d(synth.to_f64(x, "bf16"), w, bias, None, True)
+    st = assert_close(to_host(y), yr, "bf16", "conv y (headline shape)")
+    print(f"[parity] conv1d headline shape: {st}", flush=True)
