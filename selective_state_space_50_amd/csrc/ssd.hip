@@ -29,8 +29,10 @@
 //  * eight staging waves prepare chunk c + 1 meanwhile: they stage its inputs (loaded
 //    into registers a chunk ahead) into the other half of the double-buffered LDS
 //    tiles, tabulate its per-step factors (the decay to the chunk's end times the step
-//    size, the decay from the chunk's start), and after the first barrier build its
-//    masked, decayed (C B^T)^T tiles.
+//    size, the decay from the chunk's start), and after the first barrier build eight
+//    of its ten masked, decayed (C B^T)^T tiles, one each; output waves 0 and 1 build
+//    the other two after their epilogue (with both on the staging waves, two of those
+//    would build two tiles while every other wave waited).
 // Two barriers per chunk.  x and B are also needed with time as the contiguous axis (x^T,
 // B^T): a wave reads one 128-byte row per 2-byte load instruction and each lane keeps
 // consecutive steps of its own channel or state, which reach LDS as 8-byte runs.  (Both
@@ -134,6 +136,34 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
     const float dsk = a.Dskip ? a.Dskip[h] : 0.0f;
     const int64_t nch = (L + kQ - 1) / kQ;
     const int64_t xs = H * kP;   // elements between consecutive steps of x, z, y
+
+    // ---- masked, decayed (C B^T)^T tiles of chunk c with D on the diagonal, read by every
+    // output wave: tiles idx0, idx0 + step, ... of the ten
+    auto tiles = [&](int64_t c, int idx0, int step) __attribute__((always_inline)) {
+        const SsdChunk &cb = sm.ch[c & 1];
+        for (int idx = idx0; idx < kTiles; idx += step) {
+            const int i = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
+            const int k = idx - i * (i + 1) / 2;
+            f4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                g = mfma32(lds8(&sm.bm[16 * k + lr][32 * kk + 8 * lg]), lds8(&cb.cm[16 * i + lr][32 * kk + 8 * lg]), g);
+            // lane: s = 16 k + 4 lg + j, t = 16 i + lr;  M[t][s] = (C_t . B_s) exp(cum_t - cum_s) dt_s
+            const int t = 16 * i + lr;
+            const float ct = cb.cum[t];
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s = 16 * k + 4 * lg + j;
+                v[j] = s <= t ? g[j] * __builtin_amdgcn_exp2f(ct - cb.cum[s]) * cb.dt[s] : 0.0f;
+                if (s == t) v[j] += dsk;
+            }
+            s4 hi, lo;
+            split4(v[0], v[1], v[2], v[3], hi, lo);
+            sm.mhi[idx][lane] = hi;
+            sm.mlo[idx][lane] = lo;
+        }
+    };
 
     if (wv < 8) {
         // ================= output waves: chunk c =================
@@ -275,6 +305,7 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
                 *reinterpret_cast<uint4 *>(Y + (t0 + 8 * w) * xs + zoff) = make_uint4(o[0], o[1], o[2], o[3]);
             }
             if (c + 1 < nch) load_z(c + 1);
+            if (w < 2 && c + 1 < nch) tiles(c + 1, 8 + w, kTiles);   // tiles 8 and 9 of chunk c + 1
             __syncthreads();   // shares read; chunk c + 1 staged and its tiles built
         }
 
@@ -386,47 +417,19 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
             else stage(c, std::true_type{});
         };
 
-        // ---- masked, decayed (C B^T)^T tiles of chunk c with D on the diagonal, shared by
-        // the output waves
-        auto tiles = [&](int64_t c) __attribute__((always_inline)) {
-            const SsdChunk &cb = sm.ch[c & 1];
-            for (int idx = w; idx < kTiles; idx += 8) {
-                const int i = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
-                const int k = idx - i * (i + 1) / 2;
-                f4 g = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    g = mfma32(lds8(&sm.bm[16 * k + lr][32 * kk + 8 * lg]), lds8(&cb.cm[16 * i + lr][32 * kk + 8 * lg]), g);
-                // lane: s = 16 k + 4 lg + j, t = 16 i + lr;  M[t][s] = (C_t . B_s) exp(cum_t - cum_s) dt_s
-                const int t = 16 * i + lr;
-                const float ct = cb.cum[t];
-                float v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = 16 * k + 4 * lg + j;
-                    v[j] = s <= t ? g[j] * __builtin_amdgcn_exp2f(ct - cb.cum[s]) * cb.dt[s] : 0.0f;
-                    if (s == t) v[j] += dsk;
-                }
-                s4 hi, lo;
-                split4(v[0], v[1], v[2], v[3], hi, lo);
-                sm.mhi[idx][lane] = hi;
-                sm.mlo[idx][lane] = lo;
-            }
-        };
-
         if (nch > 0) {
             load_any(0);
             stage_any(0);
             if (nch > 1) load_any(1);
             __syncthreads();   // chunk 0 staged
-            tiles(0);
+            tiles(0, w, 8);
             __syncthreads();   // chunk 0's tiles built
         }
         for (int64_t c = 0; c < nch; ++c) {
             if (c + 1 < nch) stage_any(c + 1);
             if (c + 2 < nch) load_any(c + 2);
             __syncthreads();   // chunk c's shares written (the tiles of chunk c are no longer read)
-            if (c + 1 < nch) tiles(c + 1);
+            if (c + 1 < nch) tiles(c + 1, w, kTiles);   // tile w of chunk c + 1 (8 and 9: output waves 0, 1)
             __syncthreads();
         }
     }
