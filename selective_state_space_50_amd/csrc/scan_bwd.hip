@@ -27,8 +27,12 @@
 //      decays in registers, run the adjoint backwards through the block, then reduce
 //      through LDS: per (step, channel) the eight waves' partial sums give dx, ddelta, dz;
 //      per (step, state) the 64 channels' terms give this workgroup's share of dB, dC.
-// The per-lane input rows (x, delta, dy, z) of the next block are loaded while the current
-// one is processed; the block's B_t, C_t rows go through LDS.  A finishing kernel sums the
+// Wave w loads step w of the next block's input rows (x, delta, dy, z) while the current
+// block is processed, and at the block's start turns them into that step's factors
+// (dt, dt x, dy silu(z)), shared with every wave through LDS: each row is loaded and each
+// factor computed once per workgroup, not once per wave.  The wave keeps its step's
+// values in registers for the per-(step, channel) pass, which is its own step.  The
+// block's B_t, C_t rows go through LDS.  A finishing kernel sums the
 // shares of dB, dC over channel blocks and dA, dD, dbias over batch rows.
 #include "ssm_device.h"
 
@@ -53,8 +57,8 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     __shared__ float sS[kW][kTB][3][64];
     // per wave, step, (dB term, dC term), state, lane
     __shared__ float sG[kW][kTB][2][kG][64];
-    // per step, lane: (dt, x, gy, z, raw delta) of the block, written by wave 0
-    __shared__ float sV[kTB][5][64];
+    // per step, lane: (dt, dt x, dy silu(z)) of the block, written by the step's wave
+    __shared__ float4 sP[kTB][64];
     // the block's B_t, C_t: [step][state][B, C]
     __shared__ float sBC[kTB][kN][2];
 
@@ -110,21 +114,18 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     float gDp = 0.0f;   // sum of gy0 x over this thread's steps (step w of every block)
     float gBp = 0.0f;   // sum of ddelta over the same steps (the bias's share)
     const int64_t ndb = D / 64;
-    // raw rows of one block; the next block's are requested once the current block's
-    // forward recompute has consumed them, so they arrive during its adjoint and reductions
-    T rd[kTB], rx[kTB], rg[kTB], rz[kTB];
+    // step w's raw rows of the next block, requested once the current block's forward
+    // recompute is issued, so they arrive during its adjoint and reductions
+    T pd, px, pg, pz = T{};
     float bcn = 0.0f;                     // next block's B or C element (tid < 256)
     float2 ckn;                           // next block's checkpoint
     auto load2 = [&](int64_t k) __attribute__((always_inline)) {
         ckn = make_float2(ck[k * kN * D], ck[(k * kN + 1) * D]);
-#pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-            const int64_t r = row(k, i);
-            rd[i] = DL[r];
-            rx[i] = X[r];
-            rg[i] = GY[r];
-            if constexpr (HAS_Z) rz[i] = Z[r];
-        }
+        const int64_t r = row(k, w);
+        pd = DL[r];
+        px = X[r];
+        pg = GY[r];
+        if constexpr (HAS_Z) pz = Z[r];
         if (tid < 256) bcn = bc_elem(k, tid < 128 ? Bm : Cm);
     };
     auto block2 = [&](int64_t k, auto full) __attribute__((always_inline)) {
@@ -132,6 +133,14 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         const int64_t t0 = k * kTB;
         const int nb = F ? kTB : static_cast<int>(L - t0);
         if (tid < 256) sBC[e_i][e_n][tid >> 7] = bcn;
+        // this wave's step of the block (rows past the sequence's end are clamped loads whose
+        // results no pass uses)
+        const float raw_w = widen_v(pd) + dbv;
+        const float dt_w = dt_of(raw_w);
+        const float xv_w = widen_v(px);
+        const float gy_w = widen_v(pg);
+        const float zv_w = HAS_Z ? widen_v(pz) : 0.0f;
+        sP[w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, 0.0f);
         __syncthreads();
         float hs[kTB][kG], as[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
         h[0] = ckn.x;
@@ -145,15 +154,12 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
             if (F || i < nb) {
-                const float raw = widen_v(rd[i]) + dbv;
-                const float dt = dt_of(raw);
-                const float xv = widen_v(rx[i]);
-                const float u = dt * xv;
-                const float gy = widen_v(rg[i]);
-                const float zv = HAS_Z ? widen_v(rz[i]) : 0.0f;
+                const float4 pv = sP[i][lane];
+                const float dt = pv.x;
+                const float u = pv.y;
                 dts[i] = dt;
                 us[i] = u;
-                g0s[i] = HAS_Z ? gy * silu_f(zv) : gy;
+                g0s[i] = pv.z;
                 const float4 bc = bcs[i];
                 float y0p = 0.0f;
                 {
@@ -168,13 +174,6 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                     y0p = __builtin_fmaf(bc.y, h[0], bc.w * h[1]);
                 }
                 sS[w][i][2][lane] = y0p;
-                if (w == 0) {
-                    sV[i][0][lane] = dt;
-                    sV[i][1][lane] = xv;
-                    sV[i][2][lane] = gy;
-                    sV[i][3][lane] = zv;
-                    sV[i][4][lane] = raw;
-                }
             }
         }
         if (k > 0) load2(k - 1);
@@ -213,8 +212,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                     S3 += sS[ww][i][1][lane];
                     y0 += sS[ww][i][2][lane];
                 }
-                const float dt = sV[i][0][lane], xv = sV[i][1][lane], gy = sV[i][2][lane];
-                const float zv = sV[i][3][lane], raw = sV[i][4][lane];
+                const float dt = dt_w, xv = xv_w, gy = gy_w, zv = zv_w, raw = raw_w;
                 y0 = __builtin_fmaf(dsk, xv, y0);
                 float g0 = gy;
                 if constexpr (HAS_Z) {
