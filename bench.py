@@ -49,6 +49,12 @@ SLOTS_PER_TOKEN_CHANNEL = 2.0
 # accuracy work, not counted.  Bilinear: fma (1 - delta*A/2), v_rcp_f32 (2), mul
 # (delta*x*B), fma (2h + .), fma (r * . - h), fma (readout) = 7.
 SLOTS_PER_UPDATE_VARIANT = {"zoh": 8.0, "bilinear": 7.0}
+# The backward, per state update: the checkpoint pass (mul, v_exp_f32 (2), mul, fma = 5),
+# the reverse sweep's recompute (the same 5 + the readout fma = 6), its adjoint (fma
+# lam += C g0, mul g0 h, mul lam u, fma lam B, mul a h, mul + fma for the A term, mul + fma
+# for dA, mul lam *= a = 10) and the sums of the dB, dC terms over channels (2) = 23.
+# The per-(t, d) work (dx, ddelta, dz and the sums over the state groups) is not counted.
+SLOTS_PER_UPDATE_BWD = 23.0
 
 
 def kernel_source_hash():
@@ -633,13 +639,18 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     bt.sort()
     ms = bt[len(bt) // 2]
     upd = Bsz * L * D * N
+    bwd_ts = upd * SLOTS_PER_UPDATE_BWD / (ms * 1e-3) / 1e12
     out["backward"] = {
         "workload": c["name"] + " backward (dx, ddelta, dz, dB, dC, dA, dD)",
         "ms_median": round(ms, 4), "ms_min": round(bt[0], 4),
         "state_updates_per_s": upd / (ms * 1e-3),
+        "roofline": {"bound": "alu", "achieved": round(bwd_ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                     "unit": "Tslot/s", "frac": round(bwd_ts / VALU_PEAK_TSLOTS, 4),
+                     "alg_slots_per_launch": upd * SLOTS_PER_UPDATE_BWD},
+        "timing": "median of 5 calls (checkpoint pass, reverse sweep, reductions), each between two events",
         "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
     }
-    log(f"backward: {ms:.3f} ms median ({upd / (ms * 1e-3):.3e} state-updates/s)")
+    log(f"backward: {ms:.3f} ms median ({upd / (ms * 1e-3):.3e} state-updates/s, VALU {bwd_ts / VALU_PEAK_TSLOTS:.1%})")
     # oracle beside it: 64 channels of every batch row over the whole sequence
     dsel = torch.arange(0, D, 32, device=dev)   # (the oracle keeps per-channel dB, dC: [channels, L, N] each)
     ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)
