@@ -34,6 +34,15 @@
 // values in registers for the per-(step, channel) pass, which is its own step.  The
 // block's B_t, C_t rows go through LDS.  A finishing kernel sums the
 // shares of dB, dC over channel blocks and dA, dD, dbias over batch rows.
+//
+// Long sequences with few channel blocks are cut into chunks (a multiple of 8 steps).
+// The adjoint obeys a linear recurrence of its own, lam_{t-1} = a_t (lam_t + C_t gy0_t),
+// which needs no states, so the chunk algebra of the forward carries over, run from the
+// end: a carry pass computes per chunk (every chunk but the first) the product P of its
+// decays and the adjoint H it leaves at its start from lam = 0; a combine folds them from
+// the last chunk down, lam_in(c) = P_{c+1} lam_in(c+1) + H_{c+1}, lam_in(last) = dh_last;
+// then every chunk's reverse sweep starts from its lam_in.  The checkpoint pass is the
+// forward's chunked scan (carries, combine, then every chunk from its carried-in state).
 #include "ssm_device.h"
 
 #include <type_traits>
@@ -60,17 +69,23 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     // per step, lane: (dt, dt x, dy silu(z)) of the block, written by the step's wave
     __shared__ float4 sP[kTB][64];
     // the block's B_t, C_t: [step][state][B, C]
-    __shared__ float sBC[kTB][kN][2];
+    __shared__ __align__(16) float sBC[kTB][kN][2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t D = a.D, L = a.L;
     const int64_t b = blockIdx.y;
+    const int64_t cc = blockIdx.z;        // sequence chunk
     const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
     const int64_t d = d0 + lane;
     const int n0 = w * kG;
-    const int64_t nblk = a.nblk;
+    const int64_t nblk = a.nblk;          // 8-step blocks of the whole sequence
+    // this chunk's steps [t0c, t1c) and 8-step blocks [kb0, kb1) (with several chunks the
+    // chunk length is a multiple of 8; a single chunk is the whole sequence)
+    const int64_t t0c = cc * a.chunk_len;
+    const int64_t t1c = (t0c + a.chunk_len < L) ? t0c + a.chunk_len : L;
+    const int64_t kb0 = t0c / kTB, kb1 = (t1c + kTB - 1) / kTB;
     const int64_t base = b * L * D + d;
     const T *X = static_cast<const T *>(a.x) + base;
     const T *DL = static_cast<const T *>(a.delta) + base;
@@ -106,8 +121,11 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     // ---- blocks in reverse (the checkpoints come from the forward kernel's checkpoint pass)
     float lam[kG], gA[kG];
     {
-        float2 l2 = a.dh_last ? *reinterpret_cast<const float2 *>(a.dh_last + (b * D + d) * kN + n0)
-                              : make_float2(0.f, 0.f);
+        // the adjoint entering the chunk from the right: dh_last for the last chunk, the
+        // combined carry otherwise
+        const float *lin = cc + 1 < a.n_chunks ? a.lc_H + ((b * (a.n_chunks - 1) + cc) * D + d) * kN + n0
+                                               : (a.dh_last ? a.dh_last + (b * D + d) * kN + n0 : nullptr);
+        float2 l2 = lin ? *reinterpret_cast<const float2 *>(lin) : make_float2(0.f, 0.f);
         lam[0] = l2.x; lam[1] = l2.y;
     }
     gA[0] = gA[1] = 0.0f;
@@ -176,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 sS[w][i][2][lane] = y0p;
             }
         }
-        if (k > 0) load2(k - 1);
+        if (k > kb0) load2(k - 1);
         // adjoint, backwards through the block
 #pragma unroll
         for (int i = kTB - 1; i >= 0; --i) {
@@ -247,14 +265,97 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         }
         __syncthreads();
     };
-    if (nblk > 0) load2(nblk - 1);
-    if (nblk > 0 && (nblk - 1) * kTB + kTB > L) block2(nblk - 1, std::false_type{});
-    else if (nblk > 0) block2(nblk - 1, std::true_type{});
-    for (int64_t k = nblk - 2; k >= 0; --k) block2(k, std::true_type{});   // every earlier block is full
-    if (a.dh0) *reinterpret_cast<float2 *>(a.dh0 + (b * D + d) * kN + n0) = make_float2(lam[0], lam[1]);
-    *reinterpret_cast<float2 *>(a.partA + (b * D + d) * kN + n0) = make_float2(gA[0], gA[1]);
-    a.partD[(b * kW + w) * D + d] = gDp;
-    if (a.ddbias) a.partDB[(b * kW + w) * D + d] = gBp;
+    if (kb1 > kb0) load2(kb1 - 1);
+    if (kb1 > kb0 && (kb1 - 1) * kTB + kTB > L) block2(kb1 - 1, std::false_type{});
+    else if (kb1 > kb0) block2(kb1 - 1, std::true_type{});
+    for (int64_t k = kb1 - 2; k >= kb0; --k) block2(k, std::true_type{});   // every earlier block is full
+    if (a.dh0 && cc == 0) *reinterpret_cast<float2 *>(a.dh0 + (b * D + d) * kN + n0) = make_float2(lam[0], lam[1]);
+    const int64_t cb = cc * a.B + b;      // (chunk, row) slot of the partial sums
+    *reinterpret_cast<float2 *>(a.partA + (cb * D + d) * kN + n0) = make_float2(gA[0], gA[1]);
+    a.partD[(cb * kW + w) * D + d] = gDp;
+    if (a.ddbias) a.partDB[(cb * kW + w) * D + d] = gBp;
+}
+
+// Adjoint carry of chunk cc = blockIdx.z + 1 (every chunk but the first): the product of
+// its decays, P = exp(A sum dt), and the adjoint at its start from lam = 0 at its end,
+// H: lam <- a_t (lam + C_t gy0_t) for t from the chunk's last step down to its first.
+// Same mapping as the reverse sweep: 64 channels of one row, wave w holds states 2w, 2w+1;
+// wave w loads step w of each 8-step block and shares its factors through LDS.
+template <typename T, bool HAS_Z>
+__global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
+    __shared__ float2 sP[kTB][64];     // per step, lane: (dt, dy silu(z))
+    __shared__ __align__(16) float sCm[kTB][kN];     // the block's C_t (read in pairs)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t D = a.D, L = a.L;
+    const int64_t b = blockIdx.y;
+    const int64_t cc = static_cast<int64_t>(blockIdx.z) + 1;
+    const int64_t d = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    const int n0 = w * kG;
+    const int64_t base = b * L * D + d;
+    const T *DL = static_cast<const T *>(a.delta) + base;
+    const T *Z = HAS_Z ? static_cast<const T *>(a.z) + base : nullptr;
+    const T *GY = static_cast<const T *>(a.dy) + base;
+    const T *Cm = static_cast<const T *>(a.Cm) + b * L * kN;
+    float Al[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) Al[g] = a.A[d * kN + n0 + g] * kLog2e;
+    const float dbv = a.dbias ? a.dbias[d] : 0.0f;
+    const int64_t t0c = cc * a.chunk_len;
+    const int64_t t1c = (t0c + a.chunk_len < L) ? t0c + a.chunk_len : L;
+    const int64_t kb0 = t0c / kTB, kb1 = (t1c + kTB - 1) / kTB;
+    const int c_i = tid >> 4, c_n = tid & 15;   // C element of the first 128 threads
+    float lam[kG] = {0.0f, 0.0f};
+    float dsum = 0.0f;
+    for (int64_t k = kb1 - 1; k >= kb0; --k) {
+        const int64_t tw = k * kTB + w;
+        const int64_t r = (tw < L ? tw : L - 1) * D;   // rows past the end: clamped, unused
+        {
+            float dt = widen(DL, r) + dbv;
+            if (a.softplus) dt = softplus_f(dt);
+            const float gy = widen(GY, r);
+            float g0 = gy;
+            if constexpr (HAS_Z) g0 = gy * silu_f(widen(Z, r));
+            sP[w][lane] = make_float2(dt, g0);
+        }
+        if (tid < 128) {
+            const int64_t t = k * kTB + c_i;
+            sCm[c_i][c_n] = widen(Cm, (t < L ? t : L - 1) * kN + c_n);
+        }
+        __syncthreads();
+        const int nb = (k * kTB + kTB <= t1c) ? kTB : static_cast<int>(t1c - k * kTB);
+        for (int i = nb - 1; i >= 0; --i) {
+            const float2 pv = sP[i][lane];
+            const float2 cv = *reinterpret_cast<const float2 *>(&sCm[i][n0]);
+            dsum += pv.x;
+            lam[0] = __builtin_fmaf(cv.x, pv.y, lam[0]) * __builtin_amdgcn_exp2f(pv.x * Al[0]);
+            lam[1] = __builtin_fmaf(cv.y, pv.y, lam[1]) * __builtin_amdgcn_exp2f(pv.x * Al[1]);
+        }
+        __syncthreads();
+    }
+    const int64_t slot = (b * (a.n_chunks - 1) + (cc - 1)) * D + d;
+    *reinterpret_cast<float2 *>(a.lc_P + slot * kN + n0) =
+        make_float2(__builtin_amdgcn_exp2f(Al[0] * dsum), __builtin_amdgcn_exp2f(Al[1] * dsum));
+    *reinterpret_cast<float2 *>(a.lc_H + slot * kN + n0) = make_float2(lam[0], lam[1]);
+}
+
+// Fold the adjoint carries from the last chunk down, one thread per (b, d, n):
+//   lam_in(last) = dh_last,  lam_in(c) = P_{c+1} lam_in(c+1) + H_{c+1}
+// and overwrite slot c (which held chunk c+1's carry) with lam_in(c).
+__global__ void __launch_bounds__(256) bwd_combine_kernel(BwdArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t DN = a.D * kN;
+    if (i >= a.B * DN) return;
+    const int64_t b = i / DN, dn = i - b * DN;
+    float lam = a.dh_last ? a.dh_last[i] : 0.0f;
+    const int64_t C1 = a.n_chunks - 1;
+    for (int64_t c = C1 - 1; c >= 0; --c) {
+        const int64_t at = (b * C1 + c) * DN + dn;
+        lam = __builtin_fmaf(a.lc_P[at], lam, a.lc_H[at]);
+        a.lc_H[at] = lam;
+    }
 }
 
 // dB, dC [B][L][16] = sum over channel blocks of the workgroup shares
@@ -274,35 +375,49 @@ __global__ void __launch_bounds__(256) bwd_finish_bc_kernel(BwdArgs a) {
     put(static_cast<T *>(which ? a.dC : a.dB), r, s);
 }
 
-// dA [D][16] = sum over batch rows; dD, dbias [D] = sums over batch rows and waves
+// dA [D][16] = sum over chunks and batch rows; dD, dbias [D] = sums over chunks, batch
+// rows and waves
 __global__ void __launch_bounds__(256) bwd_finish_ad_kernel(BwdArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nA = a.D * kN;
+    const int64_t rows = a.n_chunks * a.B;   // (chunk, row) slots
     if (i < nA) {
         float s = 0.0f;
-        for (int64_t b = 0; b < a.B; ++b) s += a.partA[b * nA + i];
+        for (int64_t cb = 0; cb < rows; ++cb) s += a.partA[cb * nA + i];
         a.dA[i] = s;
     } else if (i < nA + a.D && a.dD) {
         const int64_t d = i - nA;
         float s = 0.0f;
-        for (int64_t b = 0; b < a.B; ++b)
-            for (int w = 0; w < kW; ++w) s += a.partD[(b * kW + w) * a.D + d];
+        for (int64_t cb = 0; cb < rows; ++cb)
+            for (int w = 0; w < kW; ++w) s += a.partD[(cb * kW + w) * a.D + d];
         a.dD[d] = s;
     } else if (i >= nA + a.D && i < nA + 2 * a.D && a.ddbias) {
         const int64_t d = i - nA - a.D;
         float s = 0.0f;
-        for (int64_t b = 0; b < a.B; ++b)
-            for (int w = 0; w < kW; ++w) s += a.partDB[(b * kW + w) * a.D + d];
+        for (int64_t cb = 0; cb < rows; ++cb)
+            for (int w = 0; w < kW; ++w) s += a.partDB[(cb * kW + w) * a.D + d];
         a.ddbias[d] = s;
     }
 }
 
 template <typename T>
 hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B));
+    hipError_t e;
+    if (a.n_chunks > 1) {
+        const dim3 gc(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks - 1));
+        if (has_z) hipLaunchKernelGGL((bwd_carry_kernel<T, true>), gc, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((bwd_carry_kernel<T, false>), gc, dim3(kThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t n = a.B * a.D * kN;
+        hipLaunchKernelGGL(bwd_combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks));
     if (has_z) hipLaunchKernelGGL((scan_bwd_kernel<T, true>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((scan_bwd_kernel<T, false>), grid, dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nbc = 2 * a.B * a.L * kN;
     hipLaunchKernelGGL((bwd_finish_bc_kernel<T>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, s, a);

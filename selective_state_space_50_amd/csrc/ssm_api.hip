@@ -190,9 +190,12 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     }
     char *ws = static_cast<char *>(workspace);
     const bool bf16 = dtype == SSM_DTYPE_BF16;
-    // 1) checkpoints: the specialised forward kernel over the whole sequence, storing the
-    //    state before every 8th step (B/C packed first, as for the forward)
+    // 1) checkpoints: the specialised forward kernel over the sequence, storing the state
+    //    before every 8th step (B/C packed first, as for the forward); with several chunks
+    //    the forward's carries and combine come first, and every chunk starts from its
+    //    carried-in state
     {
+        char *fws = ws + p.fwd_off;
         ScanArgs fa;
         fa.B = batch; fa.L = seqlen; fa.D = dim; fa.N = dstate;
         fa.x = x; fa.delta = delta; fa.z = nullptr; fa.Bm = B; fa.Cm = C;
@@ -201,19 +204,30 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         fa.dbias = delta_bias;
         fa.NW = p.fwd.NW;
         fa.chunk_len = p.fwd.chunk_len;
-        fa.n_chunks = 1;
-        fa.ws_P = nullptr; fa.ws_H = nullptr;
-        fa.ws_BC = reinterpret_cast<float *>(ws + p.bc_off);
+        fa.n_chunks = p.fwd.n_chunks;
+        fa.ws_P = p.fwd.n_chunks > 1 ? reinterpret_cast<float *>(fws + p.fwd.ws_P_off) : nullptr;
+        fa.ws_H = p.fwd.n_chunks > 1 ? reinterpret_cast<float *>(fws + p.fwd.ws_H_off) : nullptr;
+        fa.ws_BC = reinterpret_cast<float *>(fws + p.fwd.ws_BC_off);
         fa.bc_lpad = p.fwd.bc_lpad;
         fa.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
         fa.ck_nblk = p.nblk;
         e = launch_bc_pack(fa, p.fwd, bf16, s);
         if (e != hipSuccess) return hip_fail("B/C pack launch", e);
         const unsigned dblocks = static_cast<unsigned>(dim / 64);
-        e = launch_scan_ckpt(fa, dim3(dblocks, static_cast<unsigned>(batch), 1), p.fwd, bf16, s);
+        if (p.fwd.n_chunks > 1) {
+            dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.fwd.n_chunks - 1));
+            e = launch_scan_any(fa, g1, p.fwd, kMamba, bf16, false, true, s);
+            if (e != hipSuccess) return hip_fail("checkpoint carry launch", e);
+            const int64_t n = batch * dim * dstate;
+            hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, fa);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("checkpoint carry combine launch", e);
+        }
+        e = launch_scan_ckpt(fa, dim3(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.fwd.n_chunks)),
+                             p.fwd, bf16, s);
         if (e != hipSuccess) return hip_fail("checkpoint pass launch", e);
     }
-    // 2) the reverse sweep and the reductions
+    // 2) the adjoint carries (several chunks), the reverse sweep and the reductions
     BwdArgs a;
     a.B = batch; a.L = seqlen; a.D = dim;
     a.x = x; a.delta = delta; a.z = z; a.dy = dy; a.Bm = B; a.Cm = C;
@@ -222,6 +236,8 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.dA = dA; a.dD = Dskip ? dD : nullptr; a.dh0 = dh0;
     a.softplus = delta_softplus;
     a.nblk = p.nblk;
+    a.n_chunks = p.n_chunks;
+    a.chunk_len = p.chunk_len;
     a.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
     a.partBC = reinterpret_cast<float *>(ws + p.partBC_off);
     a.partA = reinterpret_cast<float *>(ws + p.partA_off);
@@ -229,6 +245,8 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.dbias = delta_bias;
     a.ddbias = delta_bias ? ddelta_bias : nullptr;
     a.partDB = reinterpret_cast<float *>(ws + p.partDB_off);
+    a.lc_P = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcP_off) : nullptr;
+    a.lc_H = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcH_off) : nullptr;
     e = launch_scan_bwd(a, bf16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
 }

@@ -58,13 +58,15 @@ struct BwdArgs {
     float *dA, *dD, *dh0;
     int softplus;
     int64_t nblk;         // 8-step blocks of the reverse sweep
+    int64_t n_chunks, chunk_len;   // sequence chunks (chunk_len a multiple of 8)
     float *ckpt;          // [B][nblk][16][D] state at the start of every block
     float *partBC;        // [2][B][D/64][L][16] per-workgroup shares of dB, dC
-    float *partA;         // [B][D][16] per-batch-row shares of dA
-    float *partD;         // [B][8][D] per-(row, wave) shares of dD
+    float *partA;         // [n_chunks][B][D][16] per-(chunk, row) shares of dA
+    float *partD;         // [n_chunks][B][8][D] per-(chunk, row, wave) shares of dD
+    float *lc_P, *lc_H;   // [B][n_chunks-1][D][16] adjoint carries of chunks 1.., then lam_in
     const float *dbias;   // [D] added to delta before the softplus, or null
     float *ddbias;        // [D] gradient of dbias (written when dbias is given)
-    float *partDB;        // [B][8][D] per-(row, wave) shares of ddbias
+    float *partDB;        // [n_chunks][B][8][D] per-(chunk, row, wave) shares of ddbias
 };
 
 struct SsdArgs {

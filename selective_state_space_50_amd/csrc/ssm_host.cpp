@@ -188,7 +188,10 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
             }
         }
     }
-    p.chunk_len = seqlen > 0 ? ceil_div(seqlen, n_chunks) : 0;
+    // a requested chunk length is kept as given (the last chunk takes the rest); the
+    // planner's own count is balanced
+    if (o.chunk_len > 0 && seqlen > 0) p.chunk_len = o.chunk_len < seqlen ? o.chunk_len : seqlen;
+    else p.chunk_len = seqlen > 0 ? ceil_div(seqlen, n_chunks) : 0;
     p.n_chunks = seqlen > 0 ? ceil_div(seqlen, p.chunk_len > 0 ? p.chunk_len : 1) : 1;
     // grid: x = 64-channel blocks, y = batch rows, z = chunks (hardware limit 65535 on y and z)
     if (batch > 65535 || p.n_chunks > 65535 || dblocks > 0x7fffffff) {
@@ -356,28 +359,45 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
     BwdPlan p;
     p.nblk = ceil_div(seqlen, 8);
     if (seqlen > 0) {
-        ssm_scan_opts one = {seqlen, 0, 0, 0, 0};   // the whole sequence as one chunk
-        st = plan_scan(batch, seqlen, dim, dstate, dtype, &one, &p.fwd);
+        // the forward planner's chunking (it splits the sequence when the channel blocks
+        // alone leave most CUs idle), with the chunk length rounded up to a multiple of 16:
+        // checkpoints sit every 8 steps from each chunk's start
+        ScanPlan f0;
+        st = plan_scan(batch, seqlen, dim, dstate, dtype, nullptr, &f0);
         if (st != SSM_OK) return st;
-        if (!p.fwd.fast || p.fwd.n_chunks != 1) {
-            set_error("ssm_scan_bwd: no single-pass plan for this shape");
+        const int64_t cl = f0.n_chunks > 1 ? ceil_div(ceil_div(seqlen, f0.n_chunks), 16) * 16 : seqlen;
+        ssm_scan_opts o = {cl, 0, 0, 0, 0};
+        st = plan_scan(batch, seqlen, dim, dstate, dtype, &o, &p.fwd);
+        if (st != SSM_OK) return st;
+        if (!p.fwd.fast || (p.fwd.n_chunks > 1 && p.fwd.chunk_len % 16 != 0)) {
+            set_error("ssm_scan_bwd: no chunk plan for this shape");
             return SSM_EUNSUPPORTED;
         }
+        p.n_chunks = p.fwd.n_chunks;
+        p.chunk_len = p.fwd.chunk_len;
     }
     const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen), D = static_cast<size_t>(dim);
+    const size_t NC = static_cast<size_t>(p.n_chunks);
     size_t ws = 0;
+    p.fwd_off = ws;
+    ws = align_up(ws + p.fwd.ws_bytes, kWsAlign);
     p.ckpt_off = ws;
     ws = align_up(ws + B * static_cast<size_t>(p.nblk) * D * 16 * sizeof(float), kWsAlign);
-    p.bc_off = ws;
-    ws = align_up(ws + B * static_cast<size_t>(p.fwd.bc_lpad) * 16 * 2 * sizeof(float), kWsAlign);
     p.partBC_off = ws;
     ws = align_up(ws + 2 * B * (D / 64) * L * 16 * sizeof(float), kWsAlign);
     p.partA_off = ws;
-    ws = align_up(ws + B * D * 16 * sizeof(float), kWsAlign);
+    ws = align_up(ws + NC * B * D * 16 * sizeof(float), kWsAlign);
     p.partD_off = ws;
-    ws = align_up(ws + B * 8 * D * sizeof(float), kWsAlign);
+    ws = align_up(ws + NC * B * 8 * D * sizeof(float), kWsAlign);
     p.partDB_off = ws;
-    ws = align_up(ws + B * 8 * D * sizeof(float), kWsAlign);
+    ws = align_up(ws + NC * B * 8 * D * sizeof(float), kWsAlign);
+    if (p.n_chunks > 1) {
+        const size_t carries = B * (NC - 1) * D * 16 * sizeof(float);
+        p.lcP_off = ws;
+        ws = align_up(ws + carries, kWsAlign);
+        p.lcH_off = ws;
+        ws = align_up(ws + carries, kWsAlign);
+    }
     p.ws_bytes = (batch == 0 || seqlen == 0 || dim == 0) ? 0 : ws;
     *plan = p;
     return SSM_OK;

@@ -63,8 +63,11 @@ inline const float *variant_bias(const ssm_variant *v) { return v ? v->delta_bia
 // checkpoint pass, per-workgroup shares of dB/dC, per-batch-row shares of dA/dD.
 struct BwdPlan {
     int64_t nblk = 0;       // 8-step blocks of the reverse sweep
-    ScanPlan fwd;           // the checkpoint pass: the specialised forward kernel, one chunk
-    size_t ckpt_off = 0, bc_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0, partDB_off = 0;
+    int64_t n_chunks = 1, chunk_len = 0;   // sequence chunks (chunk_len a multiple of 16 when several)
+    ScanPlan fwd;           // the checkpoint pass: the specialised forward kernel, same chunks
+    size_t fwd_off = 0;     // the forward plan's workspace (its carries and packed B/C)
+    size_t ckpt_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0, partDB_off = 0;
+    size_t lcP_off = 0, lcH_off = 0;   // adjoint carries (several chunks only)
     size_t ws_bytes = 0;
 };
 

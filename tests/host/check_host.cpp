@@ -76,6 +76,18 @@ int main() {
         EXPECT(bw(bias, static_cast<float *>(dx)) == SSM_EINVAL);    // overlaps dx
         EXPECT(std::strstr(ssm_last_error(), "overlaps") != nullptr);
         EXPECT(bw(bias, bias) == SSM_EINVAL);                        // output on an input
+        // chunking: one chunk when the channel blocks fill the GPU; otherwise the forward
+        // planner's count, chunks a multiple of 16 steps, and the adjoint carries
+        EXPECT(plan_scan_bwd(4, 4096, 4096, 16, SSM_DTYPE_BF16, &bp) == SSM_OK);
+        EXPECT(bp.n_chunks == 1 && bp.chunk_len == 4096 && bp.lcP_off == 0 && bp.fwd.n_chunks == 1);
+        EXPECT(plan_scan_bwd(2, 1001, 256, 16, SSM_DTYPE_F32, &bp) == SSM_OK);
+        EXPECT(bp.n_chunks == 1 && bp.chunk_len == 1001 && bp.nblk == 126);
+        EXPECT(plan_scan_bwd(1, 5000, 128, 16, SSM_DTYPE_BF16, &bp) == SSM_OK);
+        EXPECT(bp.n_chunks == 3 && bp.chunk_len == 1680 && bp.fwd.chunk_len == 1680 && bp.fwd.n_chunks == 3);
+        EXPECT(bp.lcH_off > bp.lcP_off && bp.lcP_off > bp.partDB_off && bp.ws_bytes >= bp.lcH_off + size_t(2) * 128 * 16 * 4);
+        EXPECT(plan_scan_bwd(1, 1048576, 1024, 16, SSM_DTYPE_BF16, &bp) == SSM_OK);
+        EXPECT(bp.n_chunks == 16 && bp.chunk_len == 65536 && bp.nblk == 131072);
+        EXPECT(bp.fwd.ws_bytes > 0 && bp.ckpt_off >= bp.fwd.ws_bytes);
     }
     // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);

@@ -194,3 +194,63 @@ def test_backward_headline_shape_full(ssm):
     worst["dD"] = assert_close_grad(to_host(g["dD"]), dD, "f32", "headline dD")
     print("[parity] backward headline shape: worst ratios " + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()),
           flush=True)
+
+
+CHUNKED = [
+    # B, L, D, dtype, gate, h0, dh_last, softplus, bias: few channel blocks, so the sequence
+    # is cut into chunks (3 x 1680; 1504 + 1496; 1376, 1376 and 1348 with a partial last block)
+    (1, 5000, 128, "bf16", True, True, True, True, True),
+    (2, 3000, 64, "f32", True, True, True, False, False),
+    (1, 4100, 64, "bf16", False, False, True, True, False),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,dt,gate,h0,dhl,sp,bias", CHUNKED)
+def test_backward_chunked_parity(ssm, Bsz, L, D, dt, gate, h0, dhl, sp, bias):
+    """Long sequences over few channels: the chunked backward (checkpoints from the
+    forward's chunk carries, adjoint carries folded from the last chunk down, one reverse
+    sweep per chunk) against the fp64 oracle, every output."""
+    inp, gy, gl = _case(Bsz, L, D, dt, gate, h0, dhl, sp, True, seed=300 + L, bias=bias)
+    g = _run(ssm, inp, gy, gl)
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    if not gate:
+        r["dz"] = None
+    _check(g, r, dt, f"chunked {Bsz}x{L}x{D} {dt} gate={gate} h0={h0} dh_last={dhl} softplus={sp} bias={bias}")
+
+
+@pytest.mark.timeout(900)
+def test_backward_long_sequence_sampled(ssm):
+    """The million-token layer B1 L1048576 D1024 bf16 (16 chunks of 65536): every output
+    finite, and dx, ddelta, dA, dD of sampled channels against the fp64 oracle (with one
+    batch row, the oracle's per-channel dA, dD are the whole sums)."""
+    import torch
+    c = synth.CONFIGS[3]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    inp = synth.config_inputs(3)
+    rng = np.random.default_rng(3003)
+    gy = np.empty((Bsz, L, D), dtype=np.uint16)
+    for r0 in range(0, L, 65536):
+        gy[:, r0:r0 + 65536] = synth.store(rng.standard_normal((Bsz, min(65536, L - r0), D), dtype=np.float32), "bf16")
+    print("[parity] long-sequence backward: inputs generated", flush=True)
+    t = device_inputs(inp)
+    g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], None, None, to_dev(gy, "bf16"),
+                     need_dh0=False)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddelta", "dB", "dC", "dA", "dD"):
+        assert bool(torch.isfinite(g[k].float()).all()), k
+    from tests.gpu_util import sample_channels
+    ch = sample_channels(Bsz, D, 8)
+    cb = np.array([b for b, _ in ch])
+    cd = np.array([d for _, d in ch])
+    w = lambda a: synth.to_f64(a, "bf16")
+    ser = lambda a: w(np.ascontiguousarray(a[cb, :, cd]))
+    r = oracle.scan_bwd_f64(ser(inp["x"]), ser(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["Dskip"],
+                            None, None, ser(gy), None, False, cb, cd)
+    tcb, tcd = torch.tensor(cb, device="cuda"), torch.tensor(cd, device="cuda")
+    worst = {}
+    for k in ("dx", "ddelta"):
+        worst[k] = assert_close_grad(to_host(g[k][tcb, :, tcd]), r[k], "bf16", f"long {k}")
+    worst["dA"] = assert_close_grad(to_host(g["dA"][tcd]), r["dA_c"], "f32", "long dA")
+    worst["dD"] = assert_close_grad(to_host(g["dD"][tcd]), r["dD_c"], "f32", "long dD")
+    print("[parity] long-sequence backward: worst ratios " + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()),
+          flush=True)
