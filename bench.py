@@ -703,6 +703,50 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     a_ = (ser(x), ser(dl), _host(A[dsel]), _host(Bm), _host(Cm), _host(Dk[dsel]), None, None, False, cb, cd, cores)
     deferred.append((out["long_sequence"], lambda a_=a_: oracle.scan_f64(*a_), Bsz * len(dsel) * L * N,
                      "state-updates/s", f"{len(dsel)} channels x {L} steps, fp64 C oracle", cores))
+    del y, ws
+    torch.cuda.empty_cache()
+    # --- the million-token backward (chunked: checkpoints from the chunk carries, adjoint
+    # carries, one reverse sweep per chunk) ---
+    gy = _randn((Bsz, L, D), gen, dev, bf)
+    wsb = torch.empty(ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16"), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb, need_dh0=False)
+    torch.cuda.synchronize()
+    bt = []
+    for _ in range(3):
+        a_e, b_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_e.record()
+        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb, need_dh0=False)
+        b_e.record()
+        torch.cuda.synchronize()
+        bt.append(a_e.elapsed_time(b_e))
+    bt.sort()
+    ms = bt[len(bt) // 2]
+    bwd_ts = upd * SLOTS_PER_UPDATE_BWD / (ms * 1e-3) / 1e12
+    out["long_sequence_backward"] = {
+        "workload": c["name"] + " backward (dx, ddelta, dB, dC, dA, dD)",
+        "ms_median": round(ms, 3), "state_updates_per_s": upd / (ms * 1e-3),
+        "roofline": {"bound": "alu", "achieved": round(bwd_ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                     "unit": "Tslot/s", "frac": round(bwd_ts / VALU_PEAK_TSLOTS, 4),
+                     "alg_slots_per_launch": upd * SLOTS_PER_UPDATE_BWD},
+        "timing": "median of 3 calls, each between two events",
+        "note": "chunks of the forward planner (16 x 65536 steps): chunked checkpoint pass, adjoint carries and "
+                "their combine, reverse sweep per chunk; the carry passes are not counted as algorithmic work",
+    }
+    log(f"long-sequence backward: {ms:.2f} ms/call ({upd / (ms * 1e-3):.3e} state-updates/s, "
+        f"VALU {bwd_ts / VALU_PEAK_TSLOTS:.1%})")
+    # oracle beside it: 2 channels over the whole million steps (its per-channel dB, dC are
+    # [channels, L, N] each)
+    dsel = torch.arange(0, D, 512, device=dev)
+    ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)
+    cb = np.repeat(np.arange(Bsz), len(dsel))
+    cd = np.tile(np.arange(len(dsel)), Bsz)
+    a_ = (ser(x), ser(dl), _host(A[dsel]), _host(Bm), _host(Cm), _host(Dk[dsel]), None, None, ser(gy),
+          None, False, cb, cd, cores)
+    deferred.append((out["long_sequence_backward"], lambda a_=a_: oracle.scan_bwd_f64(*a_), Bsz * len(dsel) * L * N,
+                     "state-updates/s", f"{len(dsel)} channels x {L} steps, fp64 C oracle", cores))
+    del x, dl, gy, Bm, Cm, wsb
+    torch.cuda.empty_cache()
     # the oracle beside each measurement, on its bounded sample, after the last GPU timing
     for entry, fn, work, unit, sample, nthr in deferred:
         entry["cpu_baseline"] = _cpu_entry(_timed(fn), work, unit, sample, nthr)
