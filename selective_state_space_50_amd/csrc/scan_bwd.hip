@@ -279,12 +279,16 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
 // Adjoint carry of chunk cc = blockIdx.z + 1 (every chunk but the first): the product of
 // its decays, P = exp(A sum dt), and the adjoint at its start from lam = 0 at its end,
 // H: lam <- a_t (lam + C_t gy0_t) for t from the chunk's last step down to its first.
-// Same mapping as the reverse sweep: 64 channels of one row, wave w holds states 2w, 2w+1;
-// wave w loads step w of each 8-step block and shares its factors through LDS.
+// Same mapping as the reverse sweep: 64 channels of one row, wave w holds states 2w, 2w+1.
+// The chunk is walked in 32-step blocks from its end; wave w loads steps w, w + 8, ... of
+// the block before the one being walked (so the loads have a whole block to arrive) and
+// shares their factors through LDS; each thread loads one C element of the block.
+constexpr int kCB = 32;   // steps per block of the carry pass
+
 template <typename T, bool HAS_Z>
 __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
-    __shared__ float2 sP[kTB][64];     // per step, lane: (dt, dy silu(z))
-    __shared__ __align__(16) float sCm[kTB][kN];     // the block's C_t (read in pairs)
+    __shared__ float2 sP[kCB][64];                     // per step, lane: (dt, dy silu(z))
+    __shared__ __align__(16) float sCm[kCB][kN];       // the block's C_t (read in pairs)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -305,33 +309,53 @@ __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
     const float dbv = a.dbias ? a.dbias[d] : 0.0f;
     const int64_t t0c = cc * a.chunk_len;
     const int64_t t1c = (t0c + a.chunk_len < L) ? t0c + a.chunk_len : L;
-    const int64_t kb0 = t0c / kTB, kb1 = (t1c + kTB - 1) / kTB;
-    const int c_i = tid >> 4, c_n = tid & 15;   // C element of the first 128 threads
+    const int64_t nb = (t1c - t0c + kCB - 1) / kCB;   // blocks of the chunk, the last one may be short
+    constexpr int kQ = kCB / kW;                      // steps per wave and block
+    T pd[kQ], pg[kQ], pz[kQ];
+    float pc = 0.0f;
+    // rows of block j (rows past the sequence's end are clamped; rows past the chunk's end
+    // are loaded and not used)
+    auto load = [&](int64_t j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const int64_t t = t0c + j * kCB + w + kW * q;
+            const int64_t r = (t < L ? t : L - 1) * D;
+            pd[q] = DL[r];
+            pg[q] = GY[r];
+            if constexpr (HAS_Z) pz[q] = Z[r];
+        }
+        const int64_t t = t0c + j * kCB + (tid >> 4);
+        pc = widen(Cm, (t < L ? t : L - 1) * kN + (tid & 15));
+    };
     float lam[kG] = {0.0f, 0.0f};
     float dsum = 0.0f;
-    for (int64_t k = kb1 - 1; k >= kb0; --k) {
-        const int64_t tw = k * kTB + w;
-        const int64_t r = (tw < L ? tw : L - 1) * D;   // rows past the end: clamped, unused
-        {
-            float dt = widen(DL, r) + dbv;
+    auto step = [&](int i) __attribute__((always_inline)) {
+        const float2 pv = sP[i][lane];
+        const float2 cv = *reinterpret_cast<const float2 *>(&sCm[i][n0]);
+        dsum += pv.x;
+        lam[0] = __builtin_fmaf(cv.x, pv.y, lam[0]) * __builtin_amdgcn_exp2f(pv.x * Al[0]);
+        lam[1] = __builtin_fmaf(cv.y, pv.y, lam[1]) * __builtin_amdgcn_exp2f(pv.x * Al[1]);
+    };
+    if (nb > 0) load(nb - 1);
+    for (int64_t j = nb - 1; j >= 0; --j) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            float dt = widen_v(pd[q]) + dbv;
             if (a.softplus) dt = softplus_f(dt);
-            const float gy = widen(GY, r);
+            const float gy = widen_v(pg[q]);
             float g0 = gy;
-            if constexpr (HAS_Z) g0 = gy * silu_f(widen(Z, r));
-            sP[w][lane] = make_float2(dt, g0);
+            if constexpr (HAS_Z) g0 = gy * silu_f(widen_v(pz[q]));
+            sP[w + kW * q][lane] = make_float2(dt, g0);
         }
-        if (tid < 128) {
-            const int64_t t = k * kTB + c_i;
-            sCm[c_i][c_n] = widen(Cm, (t < L ? t : L - 1) * kN + c_n);
-        }
+        sCm[tid >> 4][tid & 15] = pc;
         __syncthreads();
-        const int nb = (k * kTB + kTB <= t1c) ? kTB : static_cast<int>(t1c - k * kTB);
-        for (int i = nb - 1; i >= 0; --i) {
-            const float2 pv = sP[i][lane];
-            const float2 cv = *reinterpret_cast<const float2 *>(&sCm[i][n0]);
-            dsum += pv.x;
-            lam[0] = __builtin_fmaf(cv.x, pv.y, lam[0]) * __builtin_amdgcn_exp2f(pv.x * Al[0]);
-            lam[1] = __builtin_fmaf(cv.y, pv.y, lam[1]) * __builtin_amdgcn_exp2f(pv.x * Al[1]);
+        if (j > 0) load(j - 1);
+        const int64_t tb = t0c + j * kCB;
+        if (tb + kCB <= t1c) {
+#pragma unroll
+            for (int i = kCB - 1; i >= 0; --i) step(i);
+        } else {
+            for (int i = static_cast<int>(t1c - tb) - 1; i >= 0; --i) step(i);
         }
         __syncthreads();
     }
