@@ -109,7 +109,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU (every kernel works on one device's share); run with --gpus 1",
                           "requested_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if args.profile_run:

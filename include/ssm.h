@@ -60,7 +60,7 @@ typedef enum ssm_dtype {
 typedef enum ssm_status {
     SSM_OK = 0,
     SSM_EINVAL = 1,        /* bad shape, null or misaligned pointer, overlapping output */
-    SSM_EUNSUPPORTED = 2,  /* valid request this build does not implement (dstate > 16) */
+    SSM_EUNSUPPORTED = 2,  /* valid request the library does not implement (e.g. dstate > 16) */
     SSM_EWORKSPACE = 3,    /* workspace missing or smaller than ssm_scan_workspace_bytes() */
     SSM_EHIP = 4           /* the HIP runtime refused a launch */
 } ssm_status;
