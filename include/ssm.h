@@ -271,6 +271,37 @@ int ssm_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, in
                    const void *x, const float *w, const float *bias, const void *state_in,
                    void *y, void *state_out, int silu, void *stream);
 
+/* Host-only: bytes of device workspace ssm_conv1d_bwd needs (0 when nothing is
+ * computed or the shape is invalid). */
+size_t ssm_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                                      int dtype);
+
+/*
+ * Backward of ssm_conv1d_fwd: gradients of a loss given dy = dLoss/dy, by the chain
+ * rule through the same definition (the final state is not differentiated):
+ *     g = dy * silu'(a) (dy when silu == 0),   silu'(a) = s (1 + a (1 - s)), s = sigmoid(a)
+ *     dx[t] = sum_k w[d,k] g[t + W - 1 - k]  (terms with t + W - 1 - k < seqlen)
+ *     dw[d,k] = sum_{b,t} g[t] xp[t + k],   dbias[d] = sum_{b,t} g[t]
+ *     dstate[b,d,j] = sum_k w[d,k] g[j - k]  (the gradient of state_in, j < width-1)
+ *
+ * Inputs as ssm_conv1d_fwd (x, w, bias, state_in, silu), plus
+ *   dy        [batch, seqlen, dim]   dtype   required
+ * Outputs (device memory owned by the caller, fully overwritten, none overlapping an
+ * input or another output):
+ *   dx        [batch, seqlen, dim]   dtype   required
+ *   dw        [dim, width]           fp32    required
+ *   dbias     [dim]                  fp32    NULL = not computed (allowed with bias NULL)
+ *   dstate    [batch, dim, width-1]  dtype   NULL = not computed (allowed with state_in NULL:
+ *             the gradient of a zero starting state)
+ *   workspace device memory of ssm_conv1d_bwd_workspace_bytes() bytes (per-tile sums)
+ * seqlen == 0 sets dw, dbias, dstate to zero; batch or dim == 0 is a no-op.
+ * Deterministic: the sums run in a fixed order.
+ */
+int ssm_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                   const void *x, const float *w, const float *bias, const void *state_in,
+                   const void *dy, void *dx, float *dw, float *dbias, void *dstate, int silu,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * One token of ssm_conv1d_fwd (generation form): state [batch, dim, width-1] (dtype,
  * oldest input first) is read and updated in place, x and y are [batch, dim].

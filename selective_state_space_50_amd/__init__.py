@@ -95,6 +95,10 @@ def lib():
     L.ssm_ssd_fwd.argtypes = [I64, I64, I64, I64, I64, I32] + [P] * 11 + [I32, P]
     L.ssm_conv1d_update.restype = I32
     L.ssm_conv1d_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, I32, P]
+    L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
+    L.ssm_conv1d_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
+    L.ssm_conv1d_bwd.restype = I32
+    L.ssm_conv1d_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 9 + [I32, P, SZ, P]
     if L.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"libssm ABI version {L.ssm_abi_version()} != {ABI_VERSION}")
     _lib = L
@@ -372,6 +376,64 @@ def conv1d_fwd(x, w, bias=None, state=None, *, silu=True, return_state=False, ou
                                 _ptr(out), _ptr(st_out), int(bool(silu)), ctypes.c_void_p(s.cuda_stream)),
            "ssm_conv1d_fwd")
     return (out, st_out) if return_state else out
+
+
+def conv1d_bwd(x, w, bias=None, state=None, dy=None, *, silu=True, need_dstate=None, workspace=None, stream=None):
+    """Gradients of a loss through conv1d_fwd given dy = dLoss/dy [B, L, D] (x's dtype).
+    Returns a dict: dx [B, L, D] (x's dtype), dw [D, W] fp32, dbias [D] fp32 (None without
+    a bias) and dstate [B, D, W-1] (x's dtype; by default only when a state is given)."""
+    import torch
+    if x.dim() != 3 or w.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, dim] and w [dim, width]")
+    Bsz, L, Dm = x.shape
+    W = w.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_bwd runs on the GPU only; tensors must be on a cuda device")
+    if dy is None:
+        raise ValueError("dy is required")
+    _need(w, "w", (Dm, W), torch.float32, dev)
+    _need(bias, "bias", (Dm,), torch.float32, dev)
+    _need(state, "state", (Bsz, Dm, W - 1), x.dtype, dev)
+    _need(x, "x", (Bsz, L, Dm), x.dtype, dev)
+    _need(dy, "dy", (Bsz, L, Dm), x.dtype, dev)
+    if need_dstate is None:
+        need_dstate = state is not None
+    out = {"dx": torch.empty_like(x), "dw": torch.empty((Dm, W), dtype=torch.float32, device=dev),
+           "dbias": torch.empty((Dm,), dtype=torch.float32, device=dev) if bias is not None else None,
+           "dstate": torch.empty((Bsz, Dm, W - 1), dtype=x.dtype, device=dev) if need_dstate else None}
+    code = _dtype_code(x)
+    ws_bytes = int(lib().ssm_conv1d_bwd_workspace_bytes(Bsz, L, Dm, W, code))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check(lib().ssm_conv1d_bwd(Bsz, L, Dm, W, code, _ptr(x), _ptr(w), _ptr(bias), _ptr(state), _ptr(dy),
+                                _ptr(out["dx"]), _ptr(out["dw"]), _ptr(out["dbias"]), _ptr(out["dstate"]),
+                                int(bool(silu)), _ptr(workspace) if ws_bytes else None, ws_bytes,
+                                ctypes.c_void_p(s.cuda_stream)), "ssm_conv1d_bwd")
+    return out
+
+
+def causal_conv1d(x, w, bias=None, state=None, silu=True):
+    """Differentiable causal depthwise convolution (+ SiLU): y = conv1d_fwd(...) with a
+    torch autograd backward through conv1d_bwd (gradients for x, w, bias and state)."""
+    import torch
+
+    class _Conv(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, w, bias, state):
+            y = conv1d_fwd(x, w, bias, state, silu=silu)
+            ctx.save_for_backward(x, w, bias, state)
+            return y
+
+        @staticmethod
+        def backward(ctx, gy):
+            x, w, bias, state = ctx.saved_tensors
+            g = conv1d_bwd(x, w, bias, state, gy.contiguous(), silu=silu,
+                           need_dstate=state is not None and ctx.needs_input_grad[3])
+            return g["dx"], g["dw"], g["dbias"], g["dstate"]
+
+    return _Conv.apply(x, w, bias, state)
 
 
 def conv1d_update(state, x, w, bias=None, *, silu=True, out=None, stream=None):

@@ -9,6 +9,18 @@
 // Forward: a thread owns CPT adjacent channels (one 8- or 16-byte vector per row) and a
 // tile of kTT steps, keeping the last W - 1 rows in registers as it slides; the rows of
 // a tile are requested eight at a time before use.  Decode: one thread per (b, d).
+//
+// Backward (chain rule through the same definition, for dy = dLoss/dy):
+//     g[t] = dy[t] * silu'(a[t])   (dy[t] with silu off),  silu'(a) = s (1 + a (1 - s))
+//     dxp[t + k] += w[k] g[t]  ->  dx[t] = dxp[t + W - 1],  dstate[j] = dxp[j] (j < W - 1)
+//     dw[k] = sum_{b, t} g[t] xp[t + k],   dbias = sum_{b, t} g[t]
+// A thread owns CPT channels and the dx rows of a tile of kConvBwdTile steps.  It walks
+// t from the tile's start to W - 2 steps past its end (recomputing a and g there, as
+// the next tile does for its own first rows), sliding the window of W - 1 inputs and a
+// window of W pending dx rows; a dx row is complete, and stored, once g of its last
+// tap is in.  Its own steps' dw, dbias terms go to a per-tile partial sum that a
+// finishing kernel adds up over rows and tiles.  The first tile also completes the
+// rows before the sequence: the gradient of the starting state.
 #include "ssm_device.h"
 
 namespace ssm {
@@ -147,6 +159,153 @@ __global__ void __launch_bounds__(256) conv1d_update_kernel(ConvArgs a) {
     put(static_cast<T *>(a.y), i, act(s, a.silu));
 }
 
+template <typename T, int W, int CPT>
+__global__ void __launch_bounds__(256) conv1d_bwd_kernel(ConvArgs a) {
+    const int64_t D = a.D, L = a.L;
+    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * CPT;   // first channel
+    if (c0 >= D) return;
+    const int64_t b = blockIdx.z;
+    const int64_t tile = blockIdx.y;
+    const int64_t t0 = tile * kConvBwdTile;
+    const int64_t s1 = (t0 + kConvBwdTile < L) ? t0 + kConvBwdTile : L;   // dx rows [t0, s1)
+    const T *X = static_cast<const T *>(a.x) + b * L * D + c0;
+    const T *DY = static_cast<const T *>(a.dy) + b * L * D + c0;
+    T *DX = static_cast<T *>(a.dx) + b * L * D + c0;
+    float wk[W][CPT], bs[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) wk[k][j] = a.w[(c0 + j) * W + k];
+        bs[j] = a.bias ? a.bias[c0 + j] : 0.0f;
+    }
+    // win[k] = xp at t + k (k < W - 1): the rows before x[t]; acc[k] = pending dx of
+    // xp row t + k (k < W), i.e. of step t + k - (W - 1)
+    float win[W > 1 ? W - 1 : 1][CPT], acc[W][CPT], gw[W][CPT], gb[CPT];
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) {
+        const int64_t t = t0 - (W - 1) + k;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            float v = 0.0f;
+            if (t >= 0) v = widen(static_cast<const T *>(a.x), (b * L + t) * D + c0 + j);
+            else if (a.state_in) v = widen(static_cast<const T *>(a.state_in), ((b * D + c0 + j) * (W - 1)) + (t + W - 1));
+            win[k][j] = v;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        gb[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            acc[k][j] = 0.0f;
+            gw[k][j] = 0.0f;
+        }
+    }
+    const int nt = static_cast<int>(s1 - t0) + W - 1;   // steps t0 .. s1 + W - 2
+    for (int i0 = 0; i0 < nt; i0 += 8) {
+        Row<T, CPT> xr[8], yr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t t = t0 + i0 + i;
+            const int64_t tc = t < L ? t : L - 1;   // clamped: always in bounds
+            xr[i] = Row<T, CPT>::load(X + tc * D);
+            yr[i] = Row<T, CPT>::load(DY + tc * D);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i0 + i < nt) {
+                const int64_t t = t0 + i0 + i;
+                const bool live = t < L;          // g is zero past the sequence
+                const bool own = t < s1;          // this tile's steps carry the dw, dbias terms
+                float out[CPT];
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) {
+                    const float xv = live ? xr[i].get(j) : 0.0f;
+                    float av = bs[j];
+#pragma unroll
+                    for (int k = 0; k < W - 1; ++k) av = __builtin_fmaf(wk[k][j], win[k][j], av);
+                    av = __builtin_fmaf(wk[W - 1][j], xv, av);
+                    float g = live ? yr[i].get(j) : 0.0f;
+                    if (a.silu) {
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-av * kLog2e));
+                        g *= sg * __builtin_fmaf(av, 1.0f - sg, 1.0f);
+                    }
+                    if (own) {
+#pragma unroll
+                        for (int k = 0; k < W - 1; ++k) gw[k][j] = __builtin_fmaf(g, win[k][j], gw[k][j]);
+                        gw[W - 1][j] = __builtin_fmaf(g, xv, gw[W - 1][j]);
+                        gb[j] += g;
+                    }
+#pragma unroll
+                    for (int k = 0; k < W; ++k) acc[k][j] = __builtin_fmaf(wk[k][j], g, acc[k][j]);
+                    out[j] = acc[0][j];   // xp row t: step t - (W - 1), now complete
+#pragma unroll
+                    for (int k = 0; k + 1 < W; ++k) acc[k][j] = acc[k + 1][j];
+                    acc[W - 1][j] = 0.0f;
+#pragma unroll
+                    for (int k = 0; k + 1 < W - 1; ++k) win[k][j] = win[k + 1][j];
+                    if (W > 1) win[W > 1 ? W - 2 : 0][j] = xv;
+                }
+                const int64_t sd = t - (W - 1);   // the step whose dx row is complete
+                if (sd >= t0 && sd < s1) {
+                    Row<T, CPT>::store(DX + sd * D, out);
+                } else if (sd < 0 && a.dstate) {   // first tile: a row of the starting state
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j)
+                        put(static_cast<T *>(a.dstate), (b * D + c0 + j) * (W - 1) + (sd + W - 1), out[j]);
+                }
+            }
+        }
+    }
+    float *P = a.part + ((b * gridDim.y + tile) * D + c0) * (W + 1);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) P[j * (W + 1) + k] = gw[k][j];
+        P[j * (W + 1) + W] = gb[j];
+    }
+}
+
+// dw [D, W], dbias [D] = sums of the per-(row, tile) partials; a thread per (d, k)
+__global__ void __launch_bounds__(256) conv1d_bwd_finish_kernel(ConvArgs a, int64_t tiles) {
+    const int64_t W1 = a.W + 1;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (d, k), k <= W
+    if (i >= a.D * W1) return;
+    const int64_t d = i / W1, k = i - d * W1;
+    float s = 0.0f;
+    for (int64_t r = 0; r < a.B * tiles; ++r) s += a.part[r * a.D * W1 + i];
+    if (k < a.W) a.dw[d * a.W + k] = s;
+    else if (a.dbias) a.dbias[d] = s;
+}
+
+template <typename T, int W>
+hipError_t bwd_w(const ConvArgs &a, hipStream_t s) {
+    const bool vec = a.D % 4 == 0;
+    const int cpt = vec ? 4 : 1;
+    const int64_t threads = (a.D + cpt - 1) / cpt;
+    const int64_t tiles = (a.L + kConvBwdTile - 1) / kConvBwdTile;
+    const dim3 grid(static_cast<unsigned>((threads + 255) / 256), static_cast<unsigned>(tiles),
+                    static_cast<unsigned>(a.B));
+    if (vec) hipLaunchKernelGGL((conv1d_bwd_kernel<T, W, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((conv1d_bwd_kernel<T, W, 1>), grid, dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = a.D * (W + 1);
+    hipLaunchKernelGGL(conv1d_bwd_finish_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a,
+                       tiles);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bwd_t(const ConvArgs &a, hipStream_t s) {
+    switch (a.W) {
+        case 1: return bwd_w<T, 1>(a, s);
+        case 2: return bwd_w<T, 2>(a, s);
+        case 3: return bwd_w<T, 3>(a, s);
+        default: return bwd_w<T, 4>(a, s);
+    }
+}
+
 template <typename T, int W>
 hipError_t fwd_w(const ConvArgs &a, hipStream_t s) {
     const bool vec = a.D % 4 == 0;
@@ -196,6 +355,10 @@ hipError_t launch_conv1d_fwd(const ConvArgs &a, bool bf16, hipStream_t s) {
 
 hipError_t launch_conv1d_update(const ConvArgs &a, bool bf16, hipStream_t s) {
     return bf16 ? upd_t<uint16_t>(a, s) : upd_t<float>(a, s);
+}
+
+hipError_t launch_conv1d_bwd(const ConvArgs &a, bool bf16, hipStream_t s) {
+    return bf16 ? bwd_t<uint16_t>(a, s) : bwd_t<float>(a, s);
 }
 
 }  // namespace ssm

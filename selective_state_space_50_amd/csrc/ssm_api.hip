@@ -30,6 +30,12 @@ __global__ void __launch_bounds__(256) combine_kernel(ScanArgs a) {
     }
 }
 
+// n 16-bit words of zeros (any output of a gradient that has no terms)
+__global__ void __launch_bounds__(256) zero16_kernel(uint16_t *p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 // h_last = h0 (or zeros) for an empty sequence.
 __global__ void __launch_bounds__(256) fill_state_kernel(float *h_last, const float *h0, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -266,6 +272,48 @@ extern "C" int ssm_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_
     // (with seqlen == 0 only the state passes through)
     hipError_t e = launch_conv1d_fwd(a, dtype == SSM_DTYPE_BF16, s);
     return e == hipSuccess ? SSM_OK : hip_fail("conv1d launch", e);
+}
+
+extern "C" size_t ssm_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                                                 int dtype) {
+    (void)dtype;
+    return ssm::conv1d_bwd_ws_bytes(batch, seqlen, dim, width);
+}
+
+extern "C" int ssm_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                              const void *x, const float *w, const float *bias, const void *state_in,
+                              const void *dy, void *dx, float *dw, float *dbias, void *dstate, int silu,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    using namespace ssm;
+    clear_error();
+    int st = check_conv1d_bwd(batch, seqlen, dim, width, dtype, x, w, bias, state_in, dy, dx, dw, dbias, dstate,
+                              silu, workspace, workspace_bytes);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (width == 1) dstate = nullptr;
+    hipError_t e;
+    if (seqlen == 0) {
+        // no steps: every gradient is zero
+        auto zero = [&](void *p, int64_t bytes) {
+            if (!p || bytes <= 0) return hipSuccess;
+            const int64_t n = bytes / 2;
+            hipLaunchKernelGGL(zero16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                               static_cast<uint16_t *>(p), n);
+            return hipGetLastError();
+        };
+        e = zero(dw, dim * width * 4);
+        if (e == hipSuccess) e = zero(dbias, dim * 4);
+        if (e == hipSuccess) e = zero(dstate, batch * dim * (width - 1) * static_cast<int64_t>(dtype_size(dtype)));
+        return e == hipSuccess ? SSM_OK : hip_fail("zero fill launch", e);
+    }
+    ConvArgs a;
+    a.B = batch; a.L = seqlen; a.D = dim; a.W = static_cast<int>(width);
+    a.x = x; a.w = w; a.bias = bias; a.state_in = state_in; a.y = nullptr; a.state_out = nullptr; a.silu = silu;
+    a.dy = dy; a.dx = dx; a.dw = dw; a.dbias = dbias; a.dstate = dstate;
+    a.part = static_cast<float *>(workspace);
+    e = launch_conv1d_bwd(a, dtype == SSM_DTYPE_BF16, s);
+    return e == hipSuccess ? SSM_OK : hip_fail("conv1d backward launch", e);
 }
 
 extern "C" int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, void *state,

@@ -88,6 +88,12 @@ struct ConvArgs {
     void *y;                 // [B, L, D] (update: [B, D])
     void *state_out;         // [B, D, W-1] or null (forward); the state, in place (update)
     int silu;
+    // backward
+    const void *dy;          // [B, L, D]
+    void *dx;                // [B, L, D]
+    float *dw, *dbias;       // [D, W], [D] or null
+    void *dstate;            // [B, D, W-1] or null: gradient of the starting state
+    float *part;             // [B][L tiles][D][W + 1] per-tile sums of dw, dbias
 };
 
 __device__ __forceinline__ float widen(const uint16_t *p, int64_t i) {
@@ -199,6 +205,7 @@ hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z
 // Causal depthwise convolution (+ SiLU): sequence form and single-token form.
 hipError_t launch_conv1d_fwd(const ConvArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_conv1d_bwd(const ConvArgs &a, bool bf16, hipStream_t s);
 // Multi-head SSD scan (bf16, head dim 64, state size 128): one workgroup per (batch row, head).
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t s);
 // Backward pass (dstate == 16, dim % 64 == 0).

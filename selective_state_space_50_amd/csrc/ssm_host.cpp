@@ -508,6 +508,52 @@ int check_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, 
     return check_no_overlap(all + 4, 2, all, 6);
 }
 
+size_t conv1d_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || width < 1 || width > 4) return 0;
+    const size_t tiles = static_cast<size_t>(ceil_div(seqlen, kConvBwdTile));
+    return static_cast<size_t>(batch) * tiles * static_cast<size_t>(dim) * static_cast<size_t>(width + 1) *
+           sizeof(float);
+}
+
+int check_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                     const void *x, const float *w, const float *bias, const void *state_in,
+                     const void *dy, const void *dx, const float *dw, const float *dbias,
+                     const void *dstate, int silu, const void *workspace, size_t workspace_bytes) {
+    int st = check_conv_common(batch, seqlen, dim, width, dtype, silu);
+    if (st != SSM_OK) return st;
+    if (ceil_div(seqlen, kConvBwdTile) > 65535 || batch > 65535) {
+        set_error("grid too large (batch=%lld, seqlen=%lld): at most 65535 rows and 65535 x %d steps",
+                  (long long)batch, (long long)seqlen, kConvBwdTile);
+        return SSM_EUNSUPPORTED;
+    }
+    if (batch == 0 || dim == 0) return SSM_OK;
+    const char *missing = !w ? "w" : !dw ? "dw" : (seqlen > 0 && !x) ? "x" : (seqlen > 0 && !dy) ? "dy" :
+                          (seqlen > 0 && !dx) ? "dx" : nullptr;
+    if (missing) {
+        set_error("required pointer %s is NULL", missing);
+        return SSM_EINVAL;
+    }
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    const int64_t tok = batch * seqlen * dim * es;
+    const int64_t stb = batch * dim * (width - 1) * es;
+    const size_t need = conv1d_bwd_ws_bytes(batch, seqlen, dim, width);
+    Range all[] = {range("x", x, tok), range("w", w, dim * width * 4), range("bias", bias, dim * 4),
+                   range("state_in", state_in, stb), range("dy", dy, tok),
+                   // outputs from here on
+                   range("dx", dx, tok), range("dw", dw, dim * width * 4), range("dbias", dbias, dim * 4),
+                   range("dstate", width > 1 ? dstate : nullptr, stb),
+                   range("workspace", workspace, static_cast<int64_t>(need))};
+    st = check_aligned(all, 10);
+    if (st != SSM_OK) return st;
+    st = check_no_overlap(all + 5, 5, all, 10);
+    if (st != SSM_OK) return st;
+    if (need > 0 && (!workspace || workspace_bytes < need)) {
+        set_error("workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+        return SSM_EWORKSPACE;
+    }
+    return SSM_OK;
+}
+
 int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, const void *state,
                         const void *x, const float *w, const float *bias, const void *y, int silu) {
     int st = check_conv_common(batch, 1, dim, width, dtype, silu);

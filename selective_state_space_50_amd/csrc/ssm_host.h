@@ -87,6 +87,14 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
 int check_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
                      const void *x, const float *w, const float *bias, const void *state_in,
                      const void *y, const void *state_out, int silu);
+constexpr int kConvBwdTile = 64;   // steps per thread (and per partial sum) in the convolution's backward
+
+// Bytes of the convolution backward's workspace (per-(row, tile) sums of dw, dbias).
+size_t conv1d_bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width);
+int check_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,
+                     const void *x, const float *w, const float *bias, const void *state_in,
+                     const void *dy, const void *dx, const float *dw, const float *dbias,
+                     const void *dstate, int silu, const void *workspace, size_t workspace_bytes);
 int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, const void *state,
                         const void *x, const float *w, const float *bias, const void *y, int silu);
 
