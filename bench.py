@@ -609,12 +609,45 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     }
     log(f"conv1d: {ct[len(ct) // 2] * 1e3:.1f} us median, {conv_gbs:.0f} GB/s ({conv_gbs / HBM_PEAK_GBS:.1%} of HBM)")
     out["conv1d"]["elements_per_s"] = x.numel() / (ct[len(ct) // 2] * 1e-3)
-    # oracle beside it: every 16th channel of the whole input (numpy, fp64)
+    # oracle beside it: every 2nd channel of the whole input (numpy, fp64)
     dsel = torch.arange(0, x.shape[2], 2, device=dev)
     a_ = (_host(x[:, :, dsel]), _host(w[dsel]), _host(bias[dsel]))
     deferred.append((out["conv1d"], lambda a_=a_: conv_oracle.conv1d(*a_), x.shape[0] * x.shape[1] * len(dsel),
                      "elements/s", f"every 2nd channel ({len(dsel)}) x 4 x 4096 steps, fp64 numpy oracle (one thread)", 1))
-    del x, yc
+    # --- its backward (dx, dw, dbias) at the same shape ---
+    gyc = _randn(tuple(x.shape), gen, dev, bf)
+    cws = torch.empty(ssm.conv1d_bwd_workspace_bytes(*x.shape, w.shape[1], "bf16"), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ssm.conv1d_bwd(x, w, bias, None, gyc, workspace=cws)
+    torch.cuda.synchronize()
+    ct = []
+    for _ in range(5):
+        a_e, b_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_e.record()
+        for _ in range(10):
+            ssm.conv1d_bwd(x, w, bias, None, gyc, workspace=cws)
+        b_e.record()
+        torch.cuda.synchronize()
+        ct.append(a_e.elapsed_time(b_e) / 10)
+    ct.sort()
+    # algorithmic bytes: x and dy read, dx written (the per-tile sums are the kernel's own)
+    cb_bytes = 3 * x.numel() * 2 + w.numel() * 4 * 2 + bias.numel() * 4 * 2
+    cb_gbs = cb_bytes / (ct[len(ct) // 2] * 1e-3) / 1e9
+    out["conv1d_backward"] = {
+        "workload": "causal depthwise conv1d width 4 + SiLU backward (dx, dw, dbias), x [4, 4096, 4096] bf16",
+        "us_median": round(ct[len(ct) // 2] * 1e3, 2),
+        "timing": "median over 5 repetitions of 10 back-to-back calls (both launches) between two events",
+        "roofline": {"bound": "hbm", "achieved": round(cb_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(cb_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": cb_bytes},
+        "elements_per_s": x.numel() / (ct[len(ct) // 2] * 1e-3),
+    }
+    log(f"conv1d backward: {ct[len(ct) // 2] * 1e3:.1f} us median, {cb_gbs:.0f} GB/s ({cb_gbs / HBM_PEAK_GBS:.1%} of HBM)")
+    # oracle beside it: every 8th channel of the whole input (numpy, fp64)
+    dsel = torch.arange(0, x.shape[2], 8, device=dev)
+    a_ = (_host(x[:, :, dsel]), _host(w[dsel]), _host(bias[dsel]), None, _host(gyc[:, :, dsel]))
+    deferred.append((out["conv1d_backward"], lambda a_=a_: conv_oracle.conv1d_bwd(*a_), x.shape[0] * x.shape[1] * len(dsel),
+                     "elements/s", f"every 8th channel ({len(dsel)}) x 4 x 4096 steps, fp64 numpy oracle (one thread)", 1))
+    del x, yc, gyc, cws
     # --- backward pass at the headline shape ---
     c = synth.CONFIGS[2]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]

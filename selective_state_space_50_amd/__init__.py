@@ -378,6 +378,11 @@ def conv1d_fwd(x, w, bias=None, state=None, *, silu=True, return_state=False, ou
     return (out, st_out) if return_state else out
 
 
+def conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, dtype="bf16") -> int:
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    return int(lib().ssm_conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, code))
+
+
 def conv1d_bwd(x, w, bias=None, state=None, dy=None, *, silu=True, need_dstate=None, workspace=None, stream=None):
     """Gradients of a loss through conv1d_fwd given dy = dLoss/dy [B, L, D] (x's dtype).
     Returns a dict: dx [B, L, D] (x's dtype), dw [D, W] fp32, dbias [D] fp32 (None without

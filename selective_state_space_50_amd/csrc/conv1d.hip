@@ -266,16 +266,36 @@ __global__ void __launch_bounds__(256) conv1d_bwd_kernel(ConvArgs a) {
     }
 }
 
-// dw [D, W], dbias [D] = sums of the per-(row, tile) partials; a thread per (d, k)
+// dw [D, W], dbias [D] = sums of the per-(row, tile) partials: a column sum of a
+// [rows][D (W + 1)] matrix.  A workgroup takes 32 columns; its 8 row groups each sum every
+// 8th row with 8 loads in flight, and the 8 group sums are added in a fixed order.
 __global__ void __launch_bounds__(256) conv1d_bwd_finish_kernel(ConvArgs a, int64_t tiles) {
-    const int64_t W1 = a.W + 1;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (d, k), k <= W
-    if (i >= a.D * W1) return;
-    const int64_t d = i / W1, k = i - d * W1;
+    __shared__ float red[8][32];
+    const int64_t W1 = a.W + 1, cols = a.D * W1, rows = a.B * tiles;
+    const int cx = threadIdx.x & 31, ry = threadIdx.x >> 5;   // column in the block, row group
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 32 + cx;
     float s = 0.0f;
-    for (int64_t r = 0; r < a.B * tiles; ++r) s += a.part[r * a.D * W1 + i];
-    if (k < a.W) a.dw[d * a.W + k] = s;
-    else if (a.dbias) a.dbias[d] = s;
+    if (i < cols) {
+        int64_t r = ry;
+        for (; r + 56 < rows; r += 64) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = a.part[(r + 8 * u) * cols + i];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; r < rows; r += 8) s += a.part[r * cols + i];
+    }
+    red[ry][cx] = s;
+    __syncthreads();
+    if (ry == 0 && i < cols) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) t += red[g][cx];
+        const int64_t d = i / W1, k = i - d * W1;
+        if (k < a.W) a.dw[d * a.W + k] = t;
+        else if (a.dbias) a.dbias[d] = t;
+    }
 }
 
 template <typename T, int W>
@@ -291,7 +311,7 @@ hipError_t bwd_w(const ConvArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = a.D * (W + 1);
-    hipLaunchKernelGGL(conv1d_bwd_finish_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(conv1d_bwd_finish_kernel, dim3(static_cast<unsigned>((n + 31) / 32)), dim3(256), 0, s, a,
                        tiles);
     return hipGetLastError();
 }
