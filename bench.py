@@ -101,6 +101,8 @@ def main():
                     help="only run this many decode steps of h[256,4096,16] (for rocprofv3)")
     ap.add_argument("--profile-conv", type=int, default=0, metavar="CALLS",
                     help="only run this many conv1d calls at the headline shape (for rocprofv3)")
+    ap.add_argument("--profile-bwd", type=int, default=0, metavar="CALLS",
+                    help="only run this many backward calls at the headline shape (for rocprofv3)")
     ap.add_argument("--profile-ssd", type=int, default=0, metavar="CALLS",
                     help="only run this many SSD (Mamba-2 layer) scans (for rocprofv3)")
     ap.add_argument("--profile-variant", choices=("zoh", "bilinear"), default=None,
@@ -143,6 +145,23 @@ def main():
     if args.profile_decode:
         profile_decode(torch, ssm, synth, dev, args.profile_decode)
         log(f"decode profile run: {args.profile_decode} steps")
+        return
+    if args.profile_bwd:
+        c = synth.CONFIGS[2]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4)
+        bf = torch.bfloat16
+        Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+        x, dl, z, gy = (_randn((Bsz, L, D), gen, dev, bf) if k != "dl" else _delta((Bsz, L, D), gen, dev, bf)
+                        for k in ("x", "dl", "z", "gy"))
+        Bm, Cm = _randn((Bsz, L, N), gen, dev, bf), _randn((Bsz, L, N), gen, dev, bf)
+        A = torch.from_numpy(synth.make_A(2, D, N)).to(dev)
+        Dk = torch.from_numpy(synth.make_D(2, D, "normal")).to(dev)
+        ws = torch.empty(ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16"), dtype=torch.uint8, device=dev)
+        for _ in range(args.profile_bwd):
+            ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
+        torch.cuda.synchronize()
+        log(f"backward profile run: {args.profile_bwd} calls")
         return
     if args.profile_ssd:
         t = _ssd_inputs(torch, dev)

@@ -24,9 +24,12 @@
 //   1. forward, storing the state at the start of every 8-step block (checkpoints): the
 //      specialised forward kernel in its checkpoint mode, launched before this kernel;
 //   2. blocks in reverse: reload the block's checkpoint, recompute its 8 states and
-//      decays in registers, run the adjoint backwards through the block, then reduce
-//      through LDS: per (step, channel) the eight waves' partial sums give dx, ddelta, dz;
-//      per (step, state) the 64 channels' terms give this workgroup's share of dB, dC.
+//      decays in registers, run the adjoint backwards through the block, then reduce:
+//      per (step, channel) the eight waves' partial sums give dx, ddelta, dz (through
+//      LDS); per (step, state) the 64 channels' terms give this workgroup's share of dB,
+//      dC (in registers: a wave's 32 (step, term, state) values are summed over its 64
+//      lanes by a reduce-scatter of cross-lane swaps, after which lane l holds the sum of
+//      value l / 2).
 // Wave w loads step w of the next block's input rows (x, delta, dy, z) while the current
 // block is processed, and at the block's start turns them into that step's factors
 // (dt, dt x, dy silu(z)), shared with every wave through LDS: each row is loaded and each
@@ -62,14 +65,14 @@ __device__ __forceinline__ float sigmoid_f(float v) {
 
 template <typename T, bool HAS_Z>
 __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
+    // double-buffered by block parity, so that a block's writes never meet the previous
+    // block's reads and two barriers per block suffice:
     // per wave, step, lane: partial sums over the wave's states of (lam*A*a*h_prev, lam*B, C*h)
-    __shared__ float sS[kW][kTB][3][64];
-    // per wave, step, (dB term, dC term), state, lane
-    __shared__ float sG[kW][kTB][2][kG][64];
+    __shared__ float sS[2][kW][kTB][3][64];
     // per step, lane: (dt, dt x, dy silu(z)) of the block, written by the step's wave
-    __shared__ float4 sP[kTB][64];
+    __shared__ float4 sP[2][kTB][64];
     // the block's B_t, C_t: [step][state][B, C]
-    __shared__ __align__(16) float sBC[kTB][kN][2];
+    __shared__ __align__(16) float sBC[2][kTB][kN][2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -150,7 +153,8 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         constexpr bool F = decltype(full)::value;
         const int64_t t0 = k * kTB;
         const int nb = F ? kTB : static_cast<int>(L - t0);
-        if (tid < 256) sBC[e_i][e_n][tid >> 7] = bcn;
+        const int pb = static_cast<int>(k & 1);   // buffer of this block
+        if (tid < 256) sBC[pb][e_i][e_n][tid >> 7] = bcn;
         // this wave's step of the block (rows past the sequence's end are clamped loads whose
         // results no pass uses)
         const float raw_w = widen_v(pd) + dbv;
@@ -158,7 +162,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         const float xv_w = widen_v(px);
         const float gy_w = widen_v(pg);
         const float zv_w = HAS_Z ? widen_v(pz) : 0.0f;
-        sP[w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, 0.0f);
+        sP[pb][w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, 0.0f);
         __syncthreads();
         float hs[kTB][kG], as[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
         h[0] = ckn.x;
@@ -166,13 +170,14 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         h_in[0] = h[0];
         h_in[1] = h[1];
         float4 bcs[kTB];   // (B0, C0, B1, C1) of this wave's states, every step of the block
+        float tv[kTB * 4];  // (dB term, dC term) of every step and state: [step][term][state]
 #pragma unroll
-        for (int i = 0; i < kTB; ++i) bcs[i] = *reinterpret_cast<const float4 *>(&sBC[i][n0][0]);
+        for (int i = 0; i < kTB; ++i) bcs[i] = *reinterpret_cast<const float4 *>(&sBC[pb][i][n0][0]);
         // recompute the block forward; keep states, decays and per-step scalars
 #pragma unroll
         for (int i = 0; i < kTB; ++i) {
             if (F || i < nb) {
-                const float4 pv = sP[i][lane];
+                const float4 pv = sP[pb][i][lane];
                 const float dt = pv.x;
                 const float u = pv.y;
                 dts[i] = dt;
@@ -191,7 +196,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                     as[i][1] = dA1;
                     y0p = __builtin_fmaf(bc.y, h[0], bc.w * h[1]);
                 }
-                sS[w][i][2][lane] = y0p;
+                sS[pb][w][i][2][lane] = y0p;
             }
         }
         if (k > kb0) load2(k - 1);
@@ -205,17 +210,52 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int g = 0; g < kG; ++g) {
                     lam[g] = __builtin_fmaf(Cv[g], g0s[i], lam[g]);
-                    sG[w][i][1][g][lane] = g0s[i] * hs[i][g];
-                    sG[w][i][0][g][lane] = lam[g] * us[i];
+                    tv[i * 4 + 2 + g] = g0s[i] * hs[i][g];
+                    tv[i * 4 + g] = lam[g] * us[i];
                     S3 = __builtin_fmaf(lam[g], Bv[g], S3);
                     const float ah = as[i][g] * (i > 0 ? hs[i > 0 ? i - 1 : 0][g] : h_in[g]);   // a_t h_{t-1}
                     S1 = __builtin_fmaf(lam[g] * Av[g], ah, S1);
                     gA[g] = __builtin_fmaf(lam[g] * dts[i], ah, gA[g]);
                     lam[g] *= as[i][g];
                 }
-                sS[w][i][0][lane] = S1;
-                sS[w][i][1][lane] = S3;
+                sS[pb][w][i][0][lane] = S1;
+                sS[pb][w][i][1][lane] = S3;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) tv[i * 4 + q] = 0.0f;
             }
+        }
+        // this wave's share of dB, dC: the 32 values summed over the 64 lanes
+        {
+            auto fl = [](unsigned v) { return __builtin_bit_cast(float, v); };
+            auto ui = [](float v) { return __builtin_bit_cast(unsigned, v); };
+            auto dpp = [](float v, auto ctrl) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                             decltype(ctrl)::value, 0xF, 0xF, false));
+            };
+            float r1[16], r2[8], r3[4], r4[2];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {   // lanes l and l ^ 32: the lower half keeps values j, the upper j + 16
+                const auto p = __builtin_amdgcn_permlane32_swap(ui(tv[j]), ui(tv[j + 16]), false, false);
+                r1[j] = fl(p[0]) + fl(p[1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {    // rows of 16 lanes paired (l ^ 16): even rows keep j, odd rows j + 8
+                const auto p = __builtin_amdgcn_permlane16_swap(ui(r1[j]), ui(r1[j + 8]), false, false);
+                r2[j] = fl(p[0]) + fl(p[1]);
+            }
+            const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)      // l ^ 8 (row rotation by 8)
+                r3[j] = (b3 ? r2[j + 4] : r2[j]) + dpp(b3 ? r2[j] : r2[j + 4], std::integral_constant<int, 0x128>{});
+#pragma unroll
+            for (int j = 0; j < 2; ++j)      // l and 7 - l within each 8 lanes (half-row mirror)
+                r4[j] = (b2 ? r3[j + 2] : r3[j]) + dpp(b2 ? r3[j] : r3[j + 2], std::integral_constant<int, 0x141>{});
+            float r5 = (b1 ? r4[1] : r4[0]) + dpp(b1 ? r4[0] : r4[1], std::integral_constant<int, 0x4E>{});   // l ^ 2
+            r5 += dpp(r5, std::integral_constant<int, 0xB1>{});                                                  // l ^ 1
+            const int ri = lane >> 3, which = (lane >> 2) & 1, g = (lane >> 1) & 1;   // value lane / 2
+            if ((lane & 1) == 0 && ri < nb)
+                a.partBC[(((static_cast<int64_t>(which) * a.B + b) * ndb + blockIdx.x) * L + t0 + ri) * kN + n0 + g] = r5;
         }
         __syncthreads();
         // per (step, channel): thread (w, lane) finishes step w of its channel
@@ -226,9 +266,9 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 float S1 = 0.0f, S3 = 0.0f, y0 = 0.0f;
 #pragma unroll
                 for (int ww = 0; ww < kW; ++ww) {
-                    S1 += sS[ww][i][0][lane];
-                    S3 += sS[ww][i][1][lane];
-                    y0 += sS[ww][i][2][lane];
+                    S1 += sS[pb][ww][i][0][lane];
+                    S3 += sS[pb][ww][i][1][lane];
+                    y0 += sS[pb][ww][i][2][lane];
                 }
                 const float dt = dt_w, xv = xv_w, gy = gy_w, zv = zv_w, raw = raw_w;
                 y0 = __builtin_fmaf(dsk, xv, y0);
@@ -247,23 +287,6 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 put(static_cast<T *>(a.dx) + b * L * D, t * D + d, __builtin_fmaf(dt, S3, dsk * g0));
             }
         }
-        // per (step, state, term): sum over the 64 channels, two threads per sum
-        {
-            const int q = tid >> 1, half = tid & 1;
-            const int ri = q >> 5, which = (q >> 4) & 1, n = q & 15;
-            const float *rowp = &sG[n >> 1][ri][which][n & 1][half * 32];
-            float sacc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {   // staggered 16-byte chunks: fewer bank conflicts
-                const int c = ((j + q) & 7) * 4;
-                const float4 v = *reinterpret_cast<const float4 *>(rowp + c);
-                sacc += (v.x + v.y) + (v.z + v.w);
-            }
-            sacc += __shfl_xor(sacc, 1);
-            if (half == 0 && ri < nb)
-                a.partBC[(((static_cast<int64_t>(which) * a.B + b) * ndb + blockIdx.x) * L + t0 + ri) * kN + n] = sacc;
-        }
-        __syncthreads();
     };
     if (kb1 > kb0) load2(kb1 - 1);
     if (kb1 > kb0 && (kb1 - 1) * kTB + kTB > L) block2(kb1 - 1, std::false_type{});
