@@ -254,3 +254,21 @@ def test_backward_long_sequence_sampled(ssm):
     worst["dD"] = assert_close_grad(to_host(g["dD"][tcd]), r["dD_c"], "f32", "long dD")
     print("[parity] long-sequence backward: worst ratios " + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()),
           flush=True)
+
+
+def test_backward_degenerate_steps_and_decays(ssm):
+    """delta = 0 on whole channels and steps, A = 0 on some states, one large step: every
+    gradient against the oracle."""
+    inp, gy, gl = _case(2, 300, 128, "f32", True, True, True, False, True, seed=62)
+    d = synth.to_f64(inp["delta"], "f32").copy()
+    d[:, :, ::7] = 0.0
+    d[:, 100:110, :] = 0.0
+    d[:, 200, ::3] = 20.0
+    inp["delta"] = d.astype(np.float32)
+    A = inp["A"].copy()
+    A[:, 0] = 0.0
+    A[::5, 1] = 0.0
+    inp["A"] = A
+    g = _run(ssm, inp, gy, gl)
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"), gl)
+    _check(g, r, "f32", "degenerate steps and decays")

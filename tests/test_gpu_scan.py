@@ -271,3 +271,26 @@ def test_parity_config3(ssm):
     plan = ssm.scan_plan(1, 1 << 20, 1024, 16, "bf16")
     assert plan["n_chunks"] > 1
     _config_parity(ssm, 3, sample=48)
+
+
+@pytest.mark.parametrize("D,N,dt", [(128, 16, "bf16"), (70, 5, "f32")])
+def test_degenerate_steps_and_decays(ssm, D, N, dt):
+    """The method's degenerate cases against the oracle (specialised and generic kernels):
+    delta = 0 (the state is held, the input ignored) on whole channels and on whole steps,
+    A = 0 (no decay: a running sum) on some states, and a large delta (A_bar near 0: the
+    state is nearly replaced by the step's input)."""
+    inp = synth.scan_inputs(2, 300, D, N, dt, seed=61, gate=True, d_kind="normal", a_kind="random", h0=True)
+    d = synth.to_f64(inp["delta"], dt).copy()
+    d[:, :, ::7] = 0.0
+    d[:, 100:110, :] = 0.0
+    d[:, 200, ::3] = 20.0
+    inp["delta"] = synth.store(d.astype(np.float32), dt)
+    A = inp["A"].copy()
+    A[:, 0] = 0.0
+    A[::5, 1] = 0.0
+    inp["A"] = A
+    y, h = _run(ssm, inp)
+    yr, hr = oracle.scan(inp)
+    st = assert_close(y, yr, dt)
+    assert_close(h, hr, "f32", "h_last")
+    _log(f"degenerate D={D} N={N} {dt}", st)

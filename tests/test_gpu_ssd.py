@@ -117,3 +117,22 @@ def test_ssd_determinism(ssm):
     y1, h1 = _run(ssm, inp)
     y2, h2 = _run(ssm, inp)
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_ssd_degenerate_steps_and_decays(ssm):
+    """A head with a = 0 (no decay), delta = 0 on whole steps and on one head (state held),
+    and a large step, against the oracle."""
+    inp = synth.ssd_inputs(2, 200, 4, 64, 128, "bf16", seed=63, gate=True, h0=True)
+    d = synth.to_f64(inp["delta"], "bf16").copy()
+    d[:, 50:70, :] = 0.0
+    d[:, :, 3] = 0.0
+    d[:, 120, 1] = 20.0
+    inp["delta"] = synth.store(d.astype(np.float32), "bf16")
+    A = inp["A"].copy()
+    A[2] = 0.0
+    inp["A"] = A
+    y, h = _run(ssm, inp)
+    yr, hr = ssd_oracle.ssd_storage(inp)
+    st = assert_close(to_host(y), yr, "bf16")
+    assert_close(to_host(h), hr, "f32", "h_last")
+    print(f"[parity] ssd degenerate: {json.dumps(st)}", flush=True)
