@@ -51,7 +51,7 @@ def _load():
     lib.oracle_scan.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P,
                                 P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_scan.restype = ctypes.c_int
-    lib.oracle_scan_bwd.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P,
+    lib.oracle_scan_bwd.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P,
                                     P, P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
     _lib = lib
@@ -117,12 +117,13 @@ def scan_f64(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fa
 
 
 def scan_bwd_f64(x, delta, A, Bm, Cm, Dskip, z, h0, gy, g_last, delta_softplus, ch_b, ch_d,
-                 nthreads=None, delta_bias=None):
+                 nthreads=None, delta_bias=None, discretization="mamba"):
     """Core backward call on float64 arrays (layouts as ``scan_f64``; gy [nchan, L],
     g_last [nchan, N] or None).  Returns a dict of per-channel results: dx, ddelta, dz
     [nchan, L] (dz None without a gate), dB_c, dC_c [nchan, L, N], dA_c, dh0 [nchan, N],
     dD_c [nchan]."""
     lib = _load()
+    disc = DISCRETIZATIONS[discretization]
     x, delta, z, gy = _f64(x), _f64(delta), _f64(z), _f64(gy)
     Bm, Cm, A, Dskip, h0, g_last = _f64(Bm), _f64(Cm), _f64(A), _f64(Dskip), _f64(h0), _f64(g_last)
     dbias = _f64(delta_bias)
@@ -136,7 +137,7 @@ def scan_bwd_f64(x, delta, A, Bm, Cm, Dskip, z, h0, gy, g_last, delta_softplus, 
            "dB_c": np.empty((nchan, L, N)), "dC_c": np.empty((nchan, L, N)),
            "dA_c": np.empty((nchan, N)), "dD_c": np.empty(nchan), "dh0": np.empty((nchan, N))}
     rc = lib.oracle_scan_bwd(L, N, nchan, _ptr(ch_b), _ptr(ch_d), _ptr(x), _ptr(delta), _ptr(z),
-                             int(bool(delta_softplus)), _ptr(dbias), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
+                             int(bool(delta_softplus)), disc, _ptr(dbias), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
                              _ptr(h0), _ptr(gy), _ptr(g_last), _ptr(out["dx"]), _ptr(out["ddelta"]),
                              _ptr(out["dz"]), _ptr(out["dB_c"]), _ptr(out["dC_c"]), _ptr(out["dA_c"]),
                              _ptr(out["dD_c"]), _ptr(out["dh0"]), int(nthreads or default_threads()))
@@ -153,7 +154,8 @@ def scan_bwd(inp: dict, gy, g_last=None, nthreads=None):
     every input: dx, ddelta, dz [B, L, D] (ddelta with respect to the raw input in
     softplus mode; dz None without a gate), dB, dC [B, L, N], dA [D, N], dD [D],
     dh0 [B, D, N], and ddelta_bias [D] when ``inp`` has a "delta_bias" (the sum of ddelta
-    over batch rows and steps: the bias is added to every step's raw delta).
+    over batch rows and steps: the bias is added to every step's raw delta).  The
+    discretisation is ``inp["discretization"]`` ("mamba" when absent).
     """
     dtype = inp["dtype"]
     x, delta, z = inp["x"], inp["delta"], inp["z"]
@@ -173,7 +175,7 @@ def scan_bwd(inp: dict, gy, g_last=None, nthreads=None):
     r = scan_bwd_f64(series(x), series(delta), inp["A"], _widen(inp["B"], dtype),
                      _widen(inp["C"], dtype), inp["Dskip"], series(z), h0c,
                      series(gy, wide=False), glc, inp.get("delta_softplus", False), cb, cd, nthreads,
-                     inp.get("delta_bias"))
+                     inp.get("delta_bias"), inp.get("discretization", "mamba"))
     back = lambda a: a.reshape(Bsz, D, L).transpose(0, 2, 1).copy()
     out = {"dx": back(r["dx"]), "ddelta": back(r["ddelta"]),
            "dz": None if r["dz"] is None else back(r["dz"]),

@@ -81,15 +81,44 @@ def scan_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=Fal
     return y, h
 
 
+def _discretize_grad_slab(kind, dt, A):
+    """The operands of ``_discretize_slab`` and their partial derivatives, as slabs:
+    (A_bar, F, dA_bar/ddt, dF/ddt, dA_bar/dA, dF/dA), B_bar = F * B.
+
+    mamba: A_bar = e^u (u = dt A), F = dt: derivatives A e^u, 1, dt e^u, 0.
+    zoh: F = dt phi(u), phi(u) = (e^u - 1) / u: dF/ddt = e^u, dF/dA = dt^2 psi(u) with
+    psi(u) = d phi / du = (u e^u - e^u + 1) / u^2 (1/2 + u/3 + u^2/8 + u^3/30 + u^4/144
+    near 0, where the closed form cancels).
+    bilinear: with r = 1 / (1 - u/2), A_bar = 2 r - 1, F = r dt: dA_bar/ddt = r^2 A,
+    dF/ddt = r^2, dA_bar/dA = r^2 dt, dF/dA = r^2 dt^2 / 2."""
+    u = dt * A[None, :, :]
+    if kind == "bilinear":
+        r = 1.0 / (1.0 - 0.5 * u)
+        r2 = r * r
+        return (2.0 * r - 1.0, r * dt, r2 * A[None], np.broadcast_to(r2, u.shape) * 1.0, r2 * dt,
+                r2 * dt * dt / 2.0)
+    e = np.exp(u)
+    if kind == "zoh":
+        small = np.abs(u) < 1e-2
+        us = np.where(small, 1.0, u)
+        phi = np.where(u == 0.0, 1.0, np.expm1(u) / np.where(u == 0.0, 1.0, u))
+        psi_series = 0.5 + u * (1.0 / 3.0 + u * (1.0 / 8.0 + u * (1.0 / 30.0 + u / 144.0)))
+        psi = np.where(small, psi_series, (us * np.exp(us) - np.expm1(us)) / (us * us))
+        return e, dt * phi, A[None] * e, e, dt * e, dt * dt * psi
+    one = np.ones(u.shape)
+    return e, dt * one, A[None] * e, one, dt * e, np.zeros(u.shape)
+
+
 def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus=False,
-                gy=None, g_last=None, delta_bias=None):
+                gy=None, g_last=None, delta_bias=None, discretization="mamba"):
     """Reverse-mode derivative of ``scan_np`` for the loss <gy, y> + <g_last, h_last>.
 
     Written as the chain rule through the discretised operands: with
     lam_t = dLoss/dh_t (after step t), the step h_t = A_bar_t h_{t-1} + B_bar_t x_t gives
         dLoss/dA_bar_t = lam_t * h_{t-1},   dLoss/dB_bar_t = lam_t * x_t,
         dLoss/dh_{t-1} = A_bar_t * lam_t (+ the readout of step t-1),
-    and A_bar = exp(dt A), B_bar = dt B carry those on to dt, A, B.  All float64;
+    and the discretisation (A_bar(dt, A), B_bar = F(dt, A) B; see
+    ``_discretize_grad_slab``) carries those on to dt, A, B.  All float64;
     shapes as ``scan_np`` plus gy [B, L, D] and g_last [B, D, N] (either may be None
     = zero) and delta_bias [D] (added to delta before the softplus).  Returns a dict dx,
     ddelta, dz, dB, dC, dA, dD, dh0 (dz None without a gate; ddelta with respect to the
@@ -111,9 +140,8 @@ def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus
     hs[0] = 0.0 if h0 is None else np.asarray(h0, dtype=np.float64)
     y0 = np.empty((Bsz, L, D))
     for t in range(L):
-        a_bar = np.exp(dl[:, t, :, None] * A[None])
-        b_bar = dl[:, t, :, None] * Bm[:, t, None, :]
-        hs[t + 1] = a_bar * hs[t] + b_bar * x[:, t, :, None]
+        a_bar, fac = _discretize_slab(discretization, dl[:, t, :, None], A)[:2]
+        hs[t + 1] = a_bar * hs[t] + fac * Bm[:, t, None, :] * x[:, t, :, None]
         y0[:, t, :] = np.einsum("bdn,bn->bd", hs[t + 1], Cm[:, t, :])
         if Dskip is not None:
             y0[:, t, :] += np.asarray(Dskip, dtype=np.float64)[None, :] * x[:, t, :]
@@ -135,14 +163,15 @@ def scan_bwd_np(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None, delta_softplus
         # readout y0 = <h_t, C_t>: into C and into the state adjoint
         out["dC"][:, t, :] += np.einsum("bd,bdn->bn", gy0, hs[t + 1])
         lam = lam + gy0[:, :, None] * Cm[:, t, None, :]
-        a_bar = np.exp(dl[:, t, :, None] * A[None])
+        a_bar, fac, da_dt, df_dt, da_dA, df_dA = _discretize_grad_slab(discretization, dl[:, t, :, None], A)
         g_abar = lam * hs[t]                       # dLoss/dA_bar_t
         g_bbar = lam * x[:, t, :, None]            # dLoss/dB_bar_t
-        out["dx"][:, t, :] += np.einsum("bdn,bdn->bd", lam, dl[:, t, :, None] * Bm[:, t, None, :])
-        g_dt = np.einsum("bdn,bdn->bd", g_abar, a_bar * A[None]) + np.einsum("bdn,bn->bd", g_bbar, Bm[:, t, :])
+        g_fac = g_bbar * Bm[:, t, None, :]         # dLoss/dF_t
+        out["dx"][:, t, :] += np.einsum("bdn,bdn->bd", lam, fac * Bm[:, t, None, :])
+        g_dt = np.einsum("bdn,bdn->bd", g_abar, da_dt) + np.einsum("bdn,bdn->bd", g_fac, df_dt)
         out["ddelta"][:, t, :] = g_dt / (1.0 + np.exp(-raw[:, t, :])) if delta_softplus else g_dt
-        out["dA"] += np.einsum("bdn,bdn->dn", g_abar, a_bar * dl[:, t, :, None])
-        out["dB"][:, t, :] += np.einsum("bdn,bd->bn", g_bbar, dl[:, t, :])
+        out["dA"] += np.einsum("bdn,bdn->dn", g_abar, da_dA) + np.einsum("bdn,bdn->dn", g_fac, df_dA)
+        out["dB"][:, t, :] += np.einsum("bdn,bdn->bn", g_bbar, fac)
         lam = a_bar * lam
     out["dh0"] = lam
     # the bias enters every step's raw delta: its gradient is the sum of those

@@ -97,6 +97,43 @@ static void discretize(int disc, double dt, double a, double *a_bar, double *bf)
         *bf = dt;
 }
 
+/* The same A_bar and Bf with their partial derivatives with respect to dt and a:
+ *   Mamba:    dA_bar/ddt = a e^u, dBf/ddt = 1, dA_bar/da = dt e^u, dBf/da = 0   (u = dt a)
+ *   ZOH:      Bf = dt phi(u), phi(u) = (e^u - 1) / u:  dBf/ddt = e^u,
+ *             dBf/da = dt^2 psi(u), psi = phi' = (u e^u - e^u + 1) / u^2, taken from its
+ *             Taylor series 1/2 + u/3 + u^2/8 + u^3/30 + u^4/144 where |u| < 1e-2 (the
+ *             closed form cancels there); A_bar's derivatives as Mamba's
+ *   bilinear: r = 1 / (1 - u/2), A_bar = 2 r - 1, Bf = r dt:  dA_bar/ddt = r^2 a,
+ *             dBf/ddt = r^2, dA_bar/da = r^2 dt, dBf/da = r^2 dt^2 / 2 */
+static void discretize_grad(int disc, double dt, double a, double *a_bar, double *bf, double *da_dt,
+                            double *dbf_dt, double *da_da, double *dbf_da)
+{
+    discretize(disc, dt, a, a_bar, bf);
+    const double u = dt * a;
+    if (disc == 2) {
+        const double r = 1.0 / (1.0 - 0.5 * u);
+        *da_dt = r * r * a;
+        *dbf_dt = r * r;
+        *da_da = r * r * dt;
+        *dbf_da = r * r * dt * dt / 2.0;
+        return;
+    }
+    *da_dt = a * *a_bar;
+    *da_da = dt * *a_bar;
+    if (disc == 1) {
+        double psi;
+        if (fabs(u) < 1e-2)
+            psi = 0.5 + u * (1.0 / 3.0 + u * (1.0 / 8.0 + u * (1.0 / 30.0 + u / 144.0)));
+        else
+            psi = (u * exp(u) - expm1(u)) / (u * u);
+        *dbf_dt = *a_bar;
+        *dbf_da = dt * dt * psi;
+    } else {
+        *dbf_dt = 1.0;
+        *dbf_da = 0.0;
+    }
+}
+
 static void one_channel(const job_t *J, int64_t c)
 {
     const int64_t L = J->L, N = J->N;
@@ -190,13 +227,14 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
 }
 
 /*
- * Backward (adjoint) of the same scan (Mamba discretisation; dbias optional), for a loss whose gradients with respect
+ * Backward (adjoint) of the same scan (any of the three discretisations; dbias optional), for a loss whose gradients with respect
  * to the outputs are given: gy[t] = dLoss/dy[t] for every channel, and
  * g_last[n] = dLoss/dh_last[n] (or 0).  Plain reverse-mode differentiation of
  * the definition above, one channel at a time, no reordering:
  *
- *   forward, kept for the reverse sweep:  h_{t-1}[n], a_t[n] = exp(dt_t A[d,n]),
- *                                         y0[t] = sum_n C[t,n] h_t[n] + D x[t]
+ *   forward, kept for the reverse sweep:  h_{t-1}[n], y0[t] = sum_n C[t,n] h_t[n] + D x[t]
+ *   with a_t[n] = A_bar(dt_t, A[d,n]) and f_t[n] = Bf(dt_t, A[d,n]) (B_bar = f B) and their
+ *   partial derivatives from discretize_grad
  *   lam[n] = g_last[n]                    (dLoss/dh_t[n] arriving from step t+1)
  *   for t = L-1 .. 0:
  *       gy0      = gy[t] * silu(z[t])     (gy[t] without a gate)
@@ -205,10 +243,10 @@ int oracle_scan(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const 
  *       dx[t]    = D gy0
  *       for n:  lam[n]    += C[t,n] gy0                          (now dLoss/dh_t[n])
  *               dC[t,n]   += gy0 h_t[n]
- *               dB[t,n]   += lam[n] dt_t x[t]
- *               dx[t]     += lam[n] dt_t B[t,n]
- *               ddt       += lam[n] (A[d,n] a_t[n] h_{t-1}[n] + B[t,n] x[t])
- *               dA[d,n]   += lam[n] dt_t a_t[n] h_{t-1}[n]
+ *               dB[t,n]   += lam[n] f_t[n] x[t]
+ *               dx[t]     += lam[n] f_t[n] B[t,n]
+ *               ddt       += lam[n] (da/ddt h_{t-1}[n] + df/ddt B[t,n] x[t])
+ *               dA[d,n]   += lam[n] (da/dA h_{t-1}[n] + df/dA B[t,n] x[t])
  *               lam[n]     = a_t[n] lam[n]                       (dLoss/dh_{t-1}[n])
  *       ddelta[t] = ddt (times sigmoid(delta[t] + dbias[d]) in softplus mode, the
  *                   derivative of softplus at the raw input; the gradient of the bias is
@@ -224,7 +262,7 @@ typedef struct {
     int64_t L, N, nchan;
     const int64_t *ch_b, *ch_d;
     const double *x, *delta, *z;
-    int delta_softplus;
+    int delta_softplus, disc;
     const double *dbias;
     const double *Bm, *Cm, *A, *Dskip, *h0, *gy, *g_last;
     double *dx, *ddelta, *dz, *dB_c, *dC_c, *dA_c, *dD_c, *dh0;
@@ -255,7 +293,9 @@ static void one_channel_bwd(const bjob_t *J, int64_t c)
         const double *Ct = J->Cm + (b * L + t) * N;
         double y = 0.0;
         for (int64_t n = 0; n < N; ++n) {
-            const double h = exp(dt * J->A[d * N + n]) * hs[t * N + n] + dt * Bt[n] * xt;
+            double a_bar, bf;
+            discretize(J->disc, dt, J->A[d * N + n], &a_bar, &bf);
+            const double h = a_bar * hs[t * N + n] + bf * Bt[n] * xt;
             hs[(t + 1) * N + n] = h;
             y += Ct[n] * h;
         }
@@ -287,14 +327,15 @@ static void one_channel_bwd(const bjob_t *J, int64_t c)
         double gx = J->Dskip ? J->Dskip[d] * gy0 : 0.0;
         double gdt = 0.0;
         for (int64_t n = 0; n < N; ++n) {
-            const double a = exp(dt * J->A[d * N + n]);
+            double a, f, da_dt, df_dt, da_da, df_da;
+            discretize_grad(J->disc, dt, J->A[d * N + n], &a, &f, &da_dt, &df_dt, &da_da, &df_da);
             const double hprev = hs[t * N + n];
             lam[n] += Ct[n] * gy0;
             J->dC_c[(c * L + t) * N + n] = gy0 * hs[(t + 1) * N + n];
-            J->dB_c[(c * L + t) * N + n] = lam[n] * dt * xt;
-            gx += lam[n] * dt * Bt[n];
-            gdt += lam[n] * (J->A[d * N + n] * a * hprev + Bt[n] * xt);
-            J->dA_c[c * N + n] += lam[n] * dt * a * hprev;
+            J->dB_c[(c * L + t) * N + n] = lam[n] * f * xt;
+            gx += lam[n] * f * Bt[n];
+            gdt += lam[n] * (da_dt * hprev + df_dt * Bt[n] * xt);
+            J->dA_c[c * N + n] += lam[n] * (da_da * hprev + df_da * Bt[n] * xt);
             lam[n] = a * lam[n];
         }
         J->dx[c * L + t] = gx;
@@ -323,15 +364,15 @@ static void *worker_bwd(void *arg)
 }
 
 /* Returns 0 on success, -1 on bad arguments.  z may be NULL (no gate; dz is then
- * not written), Dskip, h0 and g_last may be NULL. */
+ * not written), Dskip, h0 and g_last may be NULL.  disc as for oracle_scan. */
 int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, const int64_t *ch_d,
                     const double *x, const double *delta, const double *z, int delta_softplus,
-                    const double *dbias, const double *Bm, const double *Cm, const double *A, const double *Dskip,
+                    int disc, const double *dbias, const double *Bm, const double *Cm, const double *A, const double *Dskip,
                     const double *h0, const double *gy, const double *g_last,
                     double *dx, double *ddelta, double *dz, double *dB_c, double *dC_c,
                     double *dA_c, double *dD_c, double *dh0, int nthreads)
 {
-    if (L < 0 || N < 0 || nchan < 0)
+    if (L < 0 || N < 0 || nchan < 0 || disc < 0 || disc > 2)
         return -1;
     if (nchan > 0 && (!ch_b || !ch_d || !dD_c || !dh0 || (N > 0 && (!A || !dA_c)) ||
                       (L > 0 && (!x || !delta || !Bm || !Cm || !gy || !dx || !ddelta || !dB_c || !dC_c)) ||
@@ -340,7 +381,8 @@ int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, co
     bjob_t J;
     memset(&J, 0, sizeof(J));
     J.L = L; J.N = N; J.nchan = nchan; J.ch_b = ch_b; J.ch_d = ch_d;
-    J.x = x; J.delta = delta; J.z = z; J.delta_softplus = delta_softplus; J.dbias = dbias;
+    J.x = x; J.delta = delta; J.z = z; J.delta_softplus = delta_softplus; J.disc = disc;
+    J.dbias = dbias;
     J.Bm = Bm; J.Cm = Cm; J.A = A; J.Dskip = Dskip; J.h0 = h0; J.gy = gy; J.g_last = g_last;
     J.dx = dx; J.ddelta = ddelta; J.dz = dz; J.dB_c = dB_c; J.dC_c = dC_c; J.dA_c = dA_c;
     J.dD_c = dD_c; J.dh0 = dh0; J.next = 0;
@@ -363,4 +405,4 @@ int oracle_scan_bwd(int64_t L, int64_t N, int64_t nchan, const int64_t *ch_b, co
     return 0;
 }
 
-int oracle_abi_version(void) { return 4; }
+int oracle_abi_version(void) { return 5; }

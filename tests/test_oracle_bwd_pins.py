@@ -36,13 +36,13 @@ def _problem(seed, Bsz=2, L=6, D=3, N=3, gate=True, h0=True, dskip=True, bias=Fa
     return p, gy, gl
 
 
-def _loss(p, gy, gl, sp):
+def _loss(p, gy, gl, sp, disc="mamba"):
     y, h = scan_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp,
-                   delta_bias=p.get("bias"))
+                   discretization=disc, delta_bias=p.get("bias"))
     return float((y * gy).sum() + (h * gl).sum())
 
 
-def _c_bwd(p, gy, gl, sp):
+def _c_bwd(p, gy, gl, sp, disc="mamba"):
     """Backward through the C oracle on float64 arrays (channels in (b, d) order)."""
     Bsz, L, D = p["x"].shape
     N = p["A"].shape[1]
@@ -51,7 +51,8 @@ def _c_bwd(p, gy, gl, sp):
     ser = lambda a: None if a is None else a[cb, :, cd]
     r = oracle.scan_bwd_f64(ser(p["x"]), ser(p["delta"]), p["A"], p["B"], p["C"], p["D"], ser(p["z"]),
                             None if p["h0"] is None else p["h0"][cb, cd, :], ser(gy),
-                            gl[cb, cd, :], sp, cb, cd, nthreads=2, delta_bias=p.get("bias"))
+                            gl[cb, cd, :], sp, cb, cd, nthreads=2, delta_bias=p.get("bias"),
+                            discretization=disc)
     back = lambda a: a.reshape(Bsz, D, L).transpose(0, 2, 1)
     return {"x": back(r["dx"]), "delta": back(r["ddelta"]),
             "bias": None if p.get("bias") is None else back(r["ddelta"]).sum(axis=(0, 1)),
@@ -124,14 +125,19 @@ def test_linear_in_incoming_gradient():
             np.testing.assert_allclose(g12[k], a * g1[k] + b * g2[k], rtol=1e-10, atol=1e-10)
 
 
-@pytest.mark.parametrize("sp,bias", [(False, False), (True, False), (True, True)])
-def test_c_and_numpy_backward_agree(sp, bias):
+@pytest.mark.parametrize("sp,bias,disc", [(False, False, "mamba"), (True, False, "mamba"), (True, True, "mamba"),
+                                         (False, False, "zoh"), (True, True, "zoh"), (False, False, "bilinear"),
+                                         (True, True, "bilinear")])
+def test_c_and_numpy_backward_agree(sp, bias, disc):
     p, gy, gl = _problem(21, Bsz=3, L=50, D=6, N=7, bias=bias)
+    # states whose dt A falls in the zero-order hold's series branch, and A = 0
+    p["A"][0, 0] = 0.0
+    p["A"][1, :3] = -1e-3
     if sp:
         p["delta"] = np.log(np.expm1(p["delta"]))
-    g = _c_bwd(p, gy, gl, sp)
+    g = _c_bwd(p, gy, gl, sp, disc)
     n = scan_bwd_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl,
-                    delta_bias=p["bias"])
+                    delta_bias=p["bias"], discretization=disc)
     names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0"}
     if bias:
         names["bias"] = "ddelta_bias"
@@ -155,41 +161,54 @@ def test_storage_wrapper_matches_core():
         np.testing.assert_allclose(out[k], n[k], rtol=1e-11, atol=1e-11)
 
 
-# Planted mistakes in a copy of the numpy backward: each must fail the finite-difference
-# pin (so the pin would catch that mistake in the oracle).
+# Planted mistakes in a copy of the numpy backward (or of its discretisation derivatives):
+# each must fail the finite-difference pin of its discretisation.
 _MUTANTS = {
-    "silu_prime_dropped": ("sg * (1.0 + zz[:, t, :] * (1.0 - sg))", "sg"),
-    "readout_dropped": ("lam = lam + gy0[:, :, None] * Cm[:, t, None, :]", "lam = lam"),
-    "dA_without_dt": ("a_bar * dl[:, t, :, None])", "a_bar)"),
-    "dx_without_dt": ("dl[:, t, :, None] * Bm[:, t, None, :])", "Bm[:, t, None, :])"),
-    "ddelta_without_A": ("a_bar * A[None])", "a_bar)"),
-    "dh0_not_decayed": ("        lam = a_bar * lam\n", "        lam = lam\n"),
-    "dB_with_wrong_input": ("g_bbar = lam * x[:, t, :, None]", "g_bbar = lam * hs[t]"),
-    "softplus_chain_dropped": ("g_dt / (1.0 + np.exp(-raw[:, t, :]))", "g_dt"),
-    "dC_with_old_state": ("gy0, hs[t + 1])", "gy0, hs[t])"),
-    "bias_ignored": ("raw = raw + np.asarray(delta_bias", "raw = raw + 0.0 * np.asarray(delta_bias"),
-    "bias_gradient_of_one_row": ('out["ddelta"].sum(axis=(0, 1))', 'out["ddelta"][0].sum(axis=0)'),
+    # kind: (function, old text, new text, discretisation)
+    "silu_prime_dropped": ("scan_bwd_np", "sg * (1.0 + zz[:, t, :] * (1.0 - sg))", "sg", "mamba"),
+    "readout_dropped": ("scan_bwd_np", "lam = lam + gy0[:, :, None] * Cm[:, t, None, :]", "lam = lam", "mamba"),
+    "dA_without_dt": ("_discretize_grad_slab", "one, dt * e, np.zeros(u.shape)", "one, e, np.zeros(u.shape)",
+                      "mamba"),
+    "dx_without_the_factor": ("scan_bwd_np", "lam, fac * Bm[:, t, None, :])", "lam, Bm[:, t, None, :])", "mamba"),
+    "ddelta_without_A": ("_discretize_grad_slab", "A[None] * e, one,", "e, one,", "mamba"),
+    "dh0_not_decayed": ("scan_bwd_np", "        lam = a_bar * lam\n", "        lam = lam\n", "mamba"),
+    "dB_with_wrong_input": ("scan_bwd_np", "g_bbar = lam * x[:, t, :, None]", "g_bbar = lam * hs[t]", "mamba"),
+    "softplus_chain_dropped": ("scan_bwd_np", "g_dt / (1.0 + np.exp(-raw[:, t, :]))", "g_dt", "mamba"),
+    "dC_with_old_state": ("scan_bwd_np", "gy0, hs[t + 1])", "gy0, hs[t])", "mamba"),
+    "bias_ignored": ("scan_bwd_np", "raw = raw + np.asarray(delta_bias", "raw = raw + 0.0 * np.asarray(delta_bias",
+                     "mamba"),
+    "bias_gradient_of_one_row": ("scan_bwd_np", 'out["ddelta"].sum(axis=(0, 1))', 'out["ddelta"][0].sum(axis=0)',
+                                 "mamba"),
+    "zoh_dF_dA_dropped": ("_discretize_grad_slab", "dt * e, dt * dt * psi", "dt * e, 0.0 * psi", "zoh"),
+    "zoh_dF_ddt_as_mamba": ("_discretize_grad_slab", "A[None] * e, e, dt * e", "A[None] * e, 1.0 + 0.0 * e, dt * e",
+                            "zoh"),
+    "zoh_psi_sign": ("_discretize_grad_slab", "(us * np.exp(us) - np.expm1(us))", "(us * np.exp(us) + np.expm1(us))",
+                     "zoh"),
+    "bilinear_r_not_squared": ("_discretize_grad_slab", "r2 = r * r", "r2 = r", "bilinear"),
+    "bilinear_dF_dA_halved_twice": ("_discretize_grad_slab", "r2 * dt * dt / 2.0)", "r2 * dt * dt / 4.0)", "bilinear"),
 }
 
 
 def _mutated_bwd(kind):
     import inspect
     from oracle import numpy_ref
-    src = inspect.getsource(numpy_ref.scan_bwd_np)
-    old, new = _MUTANTS[kind]
-    assert old in src, kind
+    fname, old, new, _ = _MUTANTS[kind]
+    src = inspect.getsource(getattr(numpy_ref, fname))
+    assert src.count(old) == 1, kind
     ns = dict(vars(numpy_ref))
     exec(src.replace(old, new), ns)
+    if fname != "scan_bwd_np":   # re-bind the backward to the mutated helper
+        exec(inspect.getsource(numpy_ref.scan_bwd_np), ns)
     return ns["scan_bwd_np"]
 
 
-def _fd_worst(fn, seed, sp):
+def _fd_worst(fn, seed, sp, disc="mamba"):
     # the softplus case also carries a delta bias
     p, gy, gl = _problem(seed, bias=sp)
     if sp:
         p["delta"] = np.log(np.expm1(p["delta"]))
     g = fn(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], sp, gy, gl,
-           delta_bias=p["bias"])
+           delta_bias=p["bias"], discretization=disc)
     names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD", "h0": "dh0",
              "bias": "ddelta_bias"}
     worst = 0.0
@@ -202,9 +221,9 @@ def _fd_worst(fn, seed, sp):
             v = arr[idx]
             eps = 1e-6 * max(1.0, abs(v))
             arr[idx] = v + eps
-            lp = _loss(p, gy, gl, sp)
+            lp = _loss(p, gy, gl, sp, disc)
             arr[idx] = v - eps
-            lm = _loss(p, gy, gl, sp)
+            lm = _loss(p, gy, gl, sp, disc)
             arr[idx] = v
             fd = (lp - lm) / (2 * eps)
             worst = max(worst, abs(fd - g[names[name]][idx]) / max(1.0, abs(fd)))
@@ -214,8 +233,31 @@ def _fd_worst(fn, seed, sp):
 @pytest.mark.parametrize("kind", sorted(_MUTANTS))
 def test_planted_backward_mistake_is_caught(kind):
     fn = _mutated_bwd(kind)
-    assert max(_fd_worst(fn, 30, False), _fd_worst(fn, 31, True)) > 1e-3, f"mutant {kind} passes the pin"
+    disc = _MUTANTS[kind][3]
+    assert max(_fd_worst(fn, 30, False, disc), _fd_worst(fn, 31, True, disc)) > 1e-3, f"mutant {kind} passes the pin"
 
 
-def test_unmutated_backward_copy_passes():
-    assert max(_fd_worst(scan_bwd_np, 30, False), _fd_worst(scan_bwd_np, 31, True)) < 1e-6
+@pytest.mark.parametrize("disc", ["mamba", "zoh", "bilinear"])
+def test_unmutated_backward_copy_passes(disc):
+    assert max(_fd_worst(scan_bwd_np, 30, False, disc), _fd_worst(scan_bwd_np, 31, True, disc)) < 1e-6
+
+
+def test_zoh_backward_through_tiny_and_zero_steps_times_A():
+    """The zero-order hold's series branch (|dt A| < 1e-2, and A = 0 exactly) against
+    finite differences of the forward oracle."""
+    p, gy, gl = _problem(33)
+    p["A"][:, 0] = 0.0
+    p["A"][:, 1] = -1e-4
+    p["delta"][0, :2] = 1e-3
+    g = scan_bwd_np(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"], False, gy, gl,
+                    discretization="zoh")
+    for (d, n) in ((0, 0), (1, 1), (2, 0), (0, 2)):
+        eps = 1e-6
+        v = p["A"][d, n]
+        p["A"][d, n] = v + eps
+        lp = _loss(p, gy, gl, False, "zoh")
+        p["A"][d, n] = v - eps
+        lm = _loss(p, gy, gl, False, "zoh")
+        p["A"][d, n] = v
+        fd = (lp - lm) / (2 * eps)
+        assert abs(fd - g["dA"][d, n]) <= 1e-6 * max(1.0, abs(fd)), (d, n, fd, g["dA"][d, n])
