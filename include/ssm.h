@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 #define SSM_MAX_DSTATE 16
 
 typedef enum ssm_dtype {
@@ -214,12 +214,17 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *     dx_t = D gy0 + dt sum_n lam B_t,  ddelta_t = sum_n lam (A exp(dt A) h_{t-1} + B_t x_t)
  *     lam = exp(dt A) lam,   dh0 = lam after t = 0
  * (ddelta_t is multiplied by sigmoid(delta_t + delta_bias) in softplus mode: the
- * derivative with respect to the raw input).  The discretisation is Mamba's (the
- * ssm_variant default); a delta bias is taken as its own argument.
+ * derivative with respect to the raw input).  That is the Mamba discretisation; with
+ * SSM_DISC_ZOH or SSM_DISC_BILINEAR the chain rule runs through that map's A_bar(dt, a)
+ * and B_bar = f(dt, a) B instead (dB_t += lam f x_t, dx_t = D gy0 + sum_n lam f B_t,
+ * ddelta_t = sum_n lam (dA_bar/ddt h_{t-1} + df/ddt B_t x_t),
+ * dA += lam (dA_bar/da h_{t-1} + df/da B_t x_t), lam = A_bar lam).
  *
  * Inputs as ssm_scan_fwd (same layouts and dtypes), plus
  *   dy        [batch, seqlen, dim]   dtype   required
  *   dh_last   [batch, dim, dstate]   fp32    NULL = zero
+ *   discretization                   an ssm_discretization (as the forward call's
+ *             variant); any other value is SSM_EINVAL
  *   delta_bias [dim]                 fp32    NULL = no bias; else the step size is
  *             delta + delta_bias[d] (before the softplus), as in ssm_variant
  * Outputs (device memory owned by the caller; none may overlap an input or another
@@ -245,7 +250,7 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  const void *C, const float *Dskip, const void *z, const float *h0,
                  const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                  void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
-                 const float *delta_bias, float *ddelta_bias, void *workspace,
+                 int discretization, const float *delta_bias, float *ddelta_bias, void *workspace,
                  size_t workspace_bytes, void *stream);
 
 /*

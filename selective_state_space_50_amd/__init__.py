@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 3     # SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 4     # SSM_ABI_VERSION of include/ssm.h
 
 
 class SSMError(RuntimeError):
@@ -88,7 +88,7 @@ def lib():
     L.ssm_scan_bwd_workspace_bytes.restype = SZ
     L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
     L.ssm_scan_bwd.restype = I32
-    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, P, P, P, SZ, P]
+    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, I32, P, P, P, SZ, P]
     L.ssm_conv1d_fwd.restype = I32
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
     L.ssm_ssd_fwd.restype = I32
@@ -280,9 +280,10 @@ def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, *,
-             delta_softplus=False, delta_bias=None, need_dh0=True, workspace=None, stream=None):
-    """Gradients of a loss through scan_fwd (Mamba discretisation), given dy = dLoss/dy
-    [B, L, D] (same dtype as x) and optionally dh_last = dLoss/dh_last [B, D, N] fp32.
+             delta_softplus=False, discretization="mamba", delta_bias=None, need_dh0=True,
+             workspace=None, stream=None):
+    """Gradients of a loss through scan_fwd, given dy = dLoss/dy [B, L, D] (same dtype as
+    x) and optionally dh_last = dLoss/dh_last [B, D, N] fp32.  discretization and
     delta_bias [D] fp32: as in scan_fwd.
 
     Returns a dict: dx, ddelta, dz (None without z) in x's dtype [B, L, D]; dB, dC in
@@ -299,6 +300,8 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
         raise ValueError("scan_bwd runs on the GPU only; tensors must be on a cuda device")
     if dy is None:
         raise ValueError("dy is required")
+    if discretization not in DISCRETIZATIONS:
+        raise ValueError(f"discretization {discretization!r} is not one of {sorted(DISCRETIZATIONS)}")
     for t, name, shape, tdt in ((x, "x", (Bsz, L, Dm), dt), (delta, "delta", (Bsz, L, Dm), dt),
                                 (z, "z", (Bsz, L, Dm), dt), (B, "B", (Bsz, L, N), dt),
                                 (C, "C", (Bsz, L, N), dt), (A, "A", (Dm, N), torch.float32),
@@ -323,12 +326,13 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
                             _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["dx"]),
                             _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
                             _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]), int(bool(delta_softplus)),
-                            _ptr(delta_bias), _ptr(out["ddelta_bias"]), _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+                            DISCRETIZATIONS[discretization], _ptr(delta_bias), _ptr(out["ddelta_bias"]), _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_scan_bwd")
     return out
 
 
-def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=False, delta_bias=None):
+def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=False, delta_bias=None,
+                   discretization="mamba"):
     """Differentiable selective scan: y = scan_fwd(...) with a torch autograd backward
     through scan_bwd (gradients for every tensor argument, delta_bias included)."""
     import torch
@@ -336,7 +340,8 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=Fa
     class _Scan(torch.autograd.Function):
         @staticmethod
         def forward(ctx, x, delta, A, B, C, D, z, h0, delta_bias):
-            y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus, delta_bias=delta_bias)
+            y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus,
+                         discretization=discretization, delta_bias=delta_bias)
             ctx.save_for_backward(x, delta, A, B, C, D, z, h0, delta_bias)
             return y
 
@@ -344,7 +349,7 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=Fa
         def backward(ctx, gy):
             x, delta, A, B, C, D, z, h0, delta_bias = ctx.saved_tensors
             g = scan_bwd(x, delta, A, B, C, D, z, h0, gy.contiguous(), delta_softplus=delta_softplus,
-                         delta_bias=delta_bias, need_dh0=h0 is not None and ctx.needs_input_grad[7])
+                         discretization=discretization, delta_bias=delta_bias, need_dh0=h0 is not None and ctx.needs_input_grad[7])
             return (g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"],
                     g["ddelta_bias"])
 

@@ -14,6 +14,18 @@
 // With a per-channel bias on the step size (dt = softplus(delta + bias), or delta + bias),
 // ddelta is taken with respect to the raw input, and the bias's gradient is its sum over
 // batch rows and steps.
+// The zero-order-hold and bilinear discretisations replace a_t = exp(dt A) and the input
+// factor dt (B_bar = f B) by their own a(dt, A), f(dt, A); the chain rule then gives
+//     dB_t += lam f x_t,   dx_t = D gy0_t + sum_n lam f B_t,
+//     ddt_t = sum_n lam (da/ddt h_{t-1} + df/ddt B_t x_t),
+//     dA   += lam (da/dA h_{t-1} + df/dA B_t x_t)
+// with, for u = dt A:
+//     zero-order hold  a = e^u, f = (e^u - 1)/A:  da/ddt = A a, df/ddt = a, da/dA = dt a,
+//                      df/dA = dt^2 psi(u), psi(u) = (u e^u - e^u + 1)/u^2
+//     bilinear         r = 1/(1 - u/2), a = 2r - 1, f = r dt:  da/ddt = r^2 A,
+//                      df/ddt = r^2, da/dA = r^2 dt, df/dA = r^2 dt^2 / 2
+// (the discretisations of the skill page's "Discretization" docstring, brentwoodlivery's
+// "From Continuous to Discrete" and the chipfoundryservices glossary's Lab 1).
 // (reverse of the step in managen.ai "Mamba: State Space Models Challenge Transformers",
 // section "Selective Scan Algorithm"; the need for gradients through the step size is in
 // the skill page "State Space Models Mamba", Verification Checklist).
@@ -63,13 +75,29 @@ __device__ __forceinline__ float sigmoid_f(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
-template <typename T, bool HAS_Z>
+// psi(u) = (u e^u - e^u + 1) / u^2, the derivative of (e^u - 1)/u, given a = e^u: its
+// Taylor series through u^6 where |u| < 1/2 (the closed form cancels there; the
+// series' truncation, u^7 / 45360, is below 2e-7 of psi at the switch), else the closed
+// form with 1 - a formed exactly.
+__device__ __forceinline__ float zoh_psi(float u, float a) {
+    const float ser = __builtin_fmaf(
+        __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(__builtin_fmaf(__builtin_fmaf(
+            1.0f / 5760.0f, u, 1.0f / 840.0f), u, 1.0f / 144.0f), u, 1.0f / 30.0f), u, 0.125f), u,
+            1.0f / 3.0f), u, 0.5f);
+    const float dir = __builtin_fmaf(u, a, 1.0f - a) * __builtin_amdgcn_rcpf(u * u);
+    return __builtin_fabsf(u) < 0.5f ? ser : dir;
+}
+
+template <typename T, bool HAS_Z, int DISC>
 __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
+    // per wave, step, lane: partial sums over the wave's states: lam da/ddt h_prev, lam f B,
+    // C h, and for the zero-order hold and bilinear maps lam df/ddt B (equal to lam f B /
+    // dt in Mamba's)
+    constexpr int NS = DISC == kMamba ? 3 : 4;
     // double-buffered by block parity, so that a block's writes never meet the previous
-    // block's reads and two barriers per block suffice:
-    // per wave, step, lane: partial sums over the wave's states of (lam*A*a*h_prev, lam*B, C*h)
-    __shared__ float sS[2][kW][kTB][3][64];
-    // per step, lane: (dt, dt x, dy silu(z)) of the block, written by the step's wave
+    // block's reads and two barriers per block suffice
+    __shared__ float sS[2][kW][kTB][NS][64];
+    // per step, lane: (dt, dt x, dy silu(z), x) of the block, written by the step's wave
     __shared__ float4 sP[2][kTB][64];
     // the block's B_t, C_t: [step][state][B, C]
     __shared__ __align__(16) float sBC[2][kTB][kN][2];
@@ -97,11 +125,12 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     const T *Bm = static_cast<const T *>(a.Bm) + b * L * kN;
     const T *Cm = static_cast<const T *>(a.Cm) + b * L * kN;
 
-    float Av[kG], Al[kG];
+    float Av[kG], Al[kG], aux[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
         Av[g] = a.A[d * kN + n0 + g];
         Al[g] = Av[g] * kLog2e;
+        aux[g] = disc_aux<DISC>(Av[g]);
     }
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
     const float dbv = a.dbias ? a.dbias[d] : 0.0f;
@@ -162,9 +191,10 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         const float xv_w = widen_v(px);
         const float gy_w = widen_v(pg);
         const float zv_w = HAS_Z ? widen_v(pz) : 0.0f;
-        sP[pb][w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, 0.0f);
+        sP[pb][w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, xv_w);
         __syncthreads();
-        float hs[kTB][kG], as[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
+        // us: dt x (Mamba) or x; fs: f (zero-order hold) or r (bilinear)
+        float hs[kTB][kG], as[kTB][kG], fs[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
         h[0] = ckn.x;
         h[1] = ckn.y;
         h_in[0] = h[0];
@@ -181,11 +211,11 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 const float dt = pv.x;
                 const float u = pv.y;
                 dts[i] = dt;
-                us[i] = u;
+                us[i] = DISC == kMamba ? u : pv.w;
                 g0s[i] = pv.z;
                 const float4 bc = bcs[i];
                 float y0p = 0.0f;
-                {
+                if constexpr (DISC == kMamba) {
                     const float dA0 = __builtin_amdgcn_exp2f(dt * Al[0]);
                     h[0] = __builtin_fmaf(dA0, h[0], u * bc.x);
                     hs[i][0] = h[0];
@@ -194,8 +224,27 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                     h[1] = __builtin_fmaf(dA1, h[1], u * bc.z);
                     hs[i][1] = h[1];
                     as[i][1] = dA1;
-                    y0p = __builtin_fmaf(bc.y, h[0], bc.w * h[1]);
+                } else {
+                    const float Bv[kG] = {bc.x, bc.z};
+#pragma unroll
+                    for (int g = 0; g < kG; ++g) {
+                        if constexpr (DISC == kZOH) {   // as the forward: e h + f (x B)
+                            const float sx = dt * Al[g];
+                            const float e = __builtin_amdgcn_exp2f(sx);
+                            const float f = zoh_factor(dt, sx, e, aux[g]);
+                            h[g] = __builtin_fmaf(e, h[g], f * (pv.w * Bv[g]));
+                            as[i][g] = e;
+                            fs[i][g] = f;
+                        } else {                        // as the forward: r (2 h + dt x B) - h
+                            const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(-dt, aux[g], 1.0f));
+                            h[g] = __builtin_fmaf(r, __builtin_fmaf(2.0f, h[g], u * Bv[g]), -h[g]);
+                            as[i][g] = __builtin_fmaf(2.0f, r, -1.0f);
+                            fs[i][g] = r;
+                        }
+                        hs[i][g] = h[g];
+                    }
                 }
+                y0p = __builtin_fmaf(bc.y, h[0], bc.w * h[1]);
                 sS[pb][w][i][2][lane] = y0p;
             }
         }
@@ -206,20 +255,47 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
             if (F || i < nb) {
                 const float4 bc = bcs[i];
                 const float Bv[kG] = {bc.x, bc.z}, Cv[kG] = {bc.y, bc.w};
-                float S1 = 0.0f, S3 = 0.0f;
+                float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f;
 #pragma unroll
                 for (int g = 0; g < kG; ++g) {
                     lam[g] = __builtin_fmaf(Cv[g], g0s[i], lam[g]);
                     tv[i * 4 + 2 + g] = g0s[i] * hs[i][g];
-                    tv[i * 4 + g] = lam[g] * us[i];
-                    S3 = __builtin_fmaf(lam[g], Bv[g], S3);
-                    const float ah = as[i][g] * (i > 0 ? hs[i > 0 ? i - 1 : 0][g] : h_in[g]);   // a_t h_{t-1}
-                    S1 = __builtin_fmaf(lam[g] * Av[g], ah, S1);
-                    gA[g] = __builtin_fmaf(lam[g] * dts[i], ah, gA[g]);
+                    const float hp = i > 0 ? hs[i > 0 ? i - 1 : 0][g] : h_in[g];   // h_{t-1}
+                    if constexpr (DISC == kMamba) {
+                        tv[i * 4 + g] = lam[g] * us[i];
+                        S3 = __builtin_fmaf(lam[g], Bv[g], S3);
+                        const float ah = as[i][g] * hp;
+                        S1 = __builtin_fmaf(lam[g] * Av[g], ah, S1);
+                        gA[g] = __builtin_fmaf(lam[g] * dts[i], ah, gA[g]);
+                    } else {
+                        const float dt = dts[i], xv = us[i], ab = as[i][g];
+                        float f, da_dt, df_dt, da_dA, df_dA;
+                        if constexpr (DISC == kZOH) {
+                            f = fs[i][g];
+                            da_dt = Av[g] * ab;
+                            df_dt = ab;
+                            da_dA = dt * ab;
+                            df_dA = dt * dt * zoh_psi(dt * Av[g], ab);
+                        } else {
+                            const float r = fs[i][g], r2 = r * r;
+                            f = r * dt;
+                            da_dt = r2 * Av[g];
+                            df_dt = r2;
+                            da_dA = r2 * dt;
+                            df_dA = 0.5f * r2 * dt * dt;
+                        }
+                        const float lf = lam[g] * f;
+                        tv[i * 4 + g] = lf * xv;
+                        S3 = __builtin_fmaf(lf, Bv[g], S3);
+                        S2 = __builtin_fmaf(lam[g] * df_dt, Bv[g], S2);
+                        S1 = __builtin_fmaf(lam[g] * da_dt, hp, S1);
+                        gA[g] = __builtin_fmaf(lam[g], __builtin_fmaf(da_dA, hp, df_dA * (Bv[g] * xv)), gA[g]);
+                    }
                     lam[g] *= as[i][g];
                 }
                 sS[pb][w][i][0][lane] = S1;
                 sS[pb][w][i][1][lane] = S3;
+                if constexpr (NS == 4) sS[pb][w][i][3][lane] = S2;
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) tv[i * 4 + q] = 0.0f;
@@ -263,12 +339,13 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
             const int i = w;
             if (i < nb) {
                 const int64_t t = t0 + i;
-                float S1 = 0.0f, S3 = 0.0f, y0 = 0.0f;
+                float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, y0 = 0.0f;
 #pragma unroll
                 for (int ww = 0; ww < kW; ++ww) {
                     S1 += sS[pb][ww][i][0][lane];
                     S3 += sS[pb][ww][i][1][lane];
                     y0 += sS[pb][ww][i][2][lane];
+                    if constexpr (NS == 4) S2 += sS[pb][ww][i][3][lane];
                 }
                 const float dt = dt_w, xv = xv_w, gy = gy_w, zv = zv_w, raw = raw_w;
                 y0 = __builtin_fmaf(dsk, xv, y0);
@@ -280,11 +357,12 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                         gy * y0 * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f)));
                 }
                 gDp = __builtin_fmaf(g0, xv, gDp);
-                float gdt = __builtin_fmaf(xv, S3, S1);
+                float gdt = __builtin_fmaf(xv, DISC == kMamba ? S3 : S2, S1);
                 if (a.softplus) gdt *= sigmoid_f(raw);
                 gBp += gdt;
                 put(static_cast<T *>(a.ddelta) + b * L * D, t * D + d, gdt);
-                put(static_cast<T *>(a.dx) + b * L * D, t * D + d, __builtin_fmaf(dt, S3, dsk * g0));
+                put(static_cast<T *>(a.dx) + b * L * D, t * D + d,
+                    DISC == kMamba ? __builtin_fmaf(dt, S3, dsk * g0) : __builtin_fmaf(dsk, g0, S3));
             }
         }
     };
@@ -300,7 +378,8 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
 }
 
 // Adjoint carry of chunk cc = blockIdx.z + 1 (every chunk but the first): the product of
-// its decays, P = exp(A sum dt), and the adjoint at its start from lam = 0 at its end,
+// its decays, P = exp(A sum dt) (the product of the bilinear a_t with BIL), and the
+// adjoint at its start from lam = 0 at its end,
 // H: lam <- a_t (lam + C_t gy0_t) for t from the chunk's last step down to its first.
 // Same mapping as the reverse sweep: 64 channels of one row, wave w holds states 2w, 2w+1.
 // The chunk is walked in 32-step blocks from its end; wave w loads steps w, w + 8, ... of
@@ -308,7 +387,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
 // shares their factors through LDS; each thread loads one C element of the block.
 constexpr int kCB = 32;   // steps per block of the carry pass
 
-template <typename T, bool HAS_Z>
+template <typename T, bool HAS_Z, bool BIL>
 __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
     __shared__ float2 sP[kCB][64];                     // per step, lane: (dt, dy silu(z))
     __shared__ __align__(16) float sCm[kCB][kN];       // the block's C_t (read in pairs)
@@ -326,9 +405,12 @@ __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
     const T *Z = HAS_Z ? static_cast<const T *>(a.z) + base : nullptr;
     const T *GY = static_cast<const T *>(a.dy) + base;
     const T *Cm = static_cast<const T *>(a.Cm) + b * L * kN;
-    float Al[kG];
+    float Al[kG], ah[kG];
 #pragma unroll
-    for (int g = 0; g < kG; ++g) Al[g] = a.A[d * kN + n0 + g] * kLog2e;
+    for (int g = 0; g < kG; ++g) {
+        Al[g] = a.A[d * kN + n0 + g] * kLog2e;
+        ah[g] = disc_aux<kBilinear>(a.A[d * kN + n0 + g]);   // A / 2
+    }
     const float dbv = a.dbias ? a.dbias[d] : 0.0f;
     const int64_t t0c = cc * a.chunk_len;
     const int64_t t1c = (t0c + a.chunk_len < L) ? t0c + a.chunk_len : L;
@@ -352,12 +434,24 @@ __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
     };
     float lam[kG] = {0.0f, 0.0f};
     float dsum = 0.0f;
+    float prod[kG] = {1.0f, 1.0f};   // product of the bilinear a_t
     auto step = [&](int i) __attribute__((always_inline)) {
         const float2 pv = sP[i][lane];
         const float2 cv = *reinterpret_cast<const float2 *>(&sCm[i][n0]);
-        dsum += pv.x;
-        lam[0] = __builtin_fmaf(cv.x, pv.y, lam[0]) * __builtin_amdgcn_exp2f(pv.x * Al[0]);
-        lam[1] = __builtin_fmaf(cv.y, pv.y, lam[1]) * __builtin_amdgcn_exp2f(pv.x * Al[1]);
+        if constexpr (BIL) {
+            float ab[kG];
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                ab[g] = __builtin_fmaf(2.0f, __builtin_amdgcn_rcpf(__builtin_fmaf(-pv.x, ah[g], 1.0f)), -1.0f);
+                prod[g] *= ab[g];
+            }
+            lam[0] = __builtin_fmaf(cv.x, pv.y, lam[0]) * ab[0];
+            lam[1] = __builtin_fmaf(cv.y, pv.y, lam[1]) * ab[1];
+        } else {
+            dsum += pv.x;
+            lam[0] = __builtin_fmaf(cv.x, pv.y, lam[0]) * __builtin_amdgcn_exp2f(pv.x * Al[0]);
+            lam[1] = __builtin_fmaf(cv.y, pv.y, lam[1]) * __builtin_amdgcn_exp2f(pv.x * Al[1]);
+        }
     };
     if (nb > 0) load(nb - 1);
     for (int64_t j = nb - 1; j >= 0; --j) {
@@ -384,7 +478,8 @@ __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
     }
     const int64_t slot = (b * (a.n_chunks - 1) + (cc - 1)) * D + d;
     *reinterpret_cast<float2 *>(a.lc_P + slot * kN + n0) =
-        make_float2(__builtin_amdgcn_exp2f(Al[0] * dsum), __builtin_amdgcn_exp2f(Al[1] * dsum));
+        BIL ? make_float2(prod[0], prod[1])
+            : make_float2(__builtin_amdgcn_exp2f(Al[0] * dsum), __builtin_amdgcn_exp2f(Al[1] * dsum));
     *reinterpret_cast<float2 *>(a.lc_H + slot * kN + n0) = make_float2(lam[0], lam[1]);
 }
 
@@ -447,13 +542,14 @@ __global__ void __launch_bounds__(256) bwd_finish_ad_kernel(BwdArgs a) {
     }
 }
 
-template <typename T>
+template <typename T, int DISC>
 hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
     hipError_t e;
+    constexpr bool BIL = DISC == kBilinear;
     if (a.n_chunks > 1) {
         const dim3 gc(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks - 1));
-        if (has_z) hipLaunchKernelGGL((bwd_carry_kernel<T, true>), gc, dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((bwd_carry_kernel<T, false>), gc, dim3(kThreads), 0, s, a);
+        if (has_z) hipLaunchKernelGGL((bwd_carry_kernel<T, true, BIL>), gc, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((bwd_carry_kernel<T, false, BIL>), gc, dim3(kThreads), 0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = a.B * a.D * kN;
@@ -462,8 +558,8 @@ hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const dim3 grid(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks));
-    if (has_z) hipLaunchKernelGGL((scan_bwd_kernel<T, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<T, false>), grid, dim3(kThreads), 0, s, a);
+    if (has_z) hipLaunchKernelGGL((scan_bwd_kernel<T, true, DISC>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<T, false, DISC>), grid, dim3(kThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nbc = 2 * a.B * a.L * kN;
@@ -475,10 +571,17 @@ hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DISC>
+hipError_t launch_d(const BwdArgs &a, bool bf16, bool has_z, hipStream_t s) {
+    return bf16 ? launch_t<uint16_t, DISC>(a, has_z, s) : launch_t<float, DISC>(a, has_z, s);
+}
+
 }  // namespace
 
-hipError_t launch_scan_bwd(const BwdArgs &a, bool bf16, bool has_z, hipStream_t s) {
-    return bf16 ? launch_t<uint16_t>(a, has_z, s) : launch_t<float>(a, has_z, s);
+hipError_t launch_scan_bwd(const BwdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s) {
+    if (disc == kZOH) return launch_d<kZOH>(a, bf16, has_z, s);
+    if (disc == kBilinear) return launch_d<kBilinear>(a, bf16, has_z, s);
+    return launch_d<kMamba>(a, bf16, has_z, s);
 }
 
 }  // namespace ssm

@@ -6,13 +6,6 @@
 namespace ssm {
 namespace {
 
-template <typename T, int G>
-hipError_t launch_ckpt_t(const ScanArgs &a, dim3 grid, size_t lds_reserve, hipStream_t s) {
-    hipLaunchKernelGGL((scan_fast_kernel<kMamba, T, G, false, true, true>), grid,
-                       dim3(64 * waves_per_block<G>()), lds_reserve, s, a);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s) {
@@ -28,11 +21,12 @@ hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s) {
-    // one workgroup per CU when the grid allows (the carry kernel's static LDS is 16 KiB)
-    const size_t reserve = p.blocks <= static_cast<uint64_t>(kCUs) ? kLdsPerCU / 2 + 1024 - 16 * 1024 : 0;
-    if (bf16) return p.G == 2 ? launch_ckpt_t<uint16_t, 2>(a, grid, reserve, s) : launch_ckpt_t<uint16_t, 4>(a, grid, reserve, s);
-    return p.G == 2 ? launch_ckpt_t<float, 2>(a, grid, reserve, s) : launch_ckpt_t<float, 4>(a, grid, reserve, s);
+SSM_CKPT_LAUNCHER(launch_scan_ckpt_mamba) { return launch_ckpt<kMamba>(a, grid, p, bf16, s); }
+
+hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, hipStream_t s) {
+    if (disc == kZOH) return launch_scan_ckpt_zoh(a, grid, p, bf16, s);
+    if (disc == kBilinear) return launch_scan_ckpt_bilinear(a, grid, p, bf16, s);
+    return launch_scan_ckpt_mamba(a, grid, p, bf16, s);
 }
 
 SSM_SCAN_LAUNCHER(launch_scan_fast_mamba) { return launch_fast<kMamba>(a, grid, p, bf16, has_z, carry, s); }

@@ -533,5 +533,21 @@ hipError_t launch_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf1
                 : launch_dt<DISC, float>(a, grid, p, has_z, carry, s);
 }
 
+template <int DISC, typename T, int G>
+hipError_t launch_ckpt_t(const ScanArgs &a, dim3 grid, size_t lds_reserve, hipStream_t s) {
+    hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, false, true, true>), grid,
+                       dim3(64 * waves_per_block<G>()), lds_reserve, s, a);
+    return hipGetLastError();
+}
+
+template <int DISC>
+hipError_t launch_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s) {
+    // one workgroup per CU when the grid allows (the carry kernel's static LDS is 16 KiB)
+    const size_t reserve = p.blocks <= static_cast<uint64_t>(kCUs) ? kLdsPerCU / 2 + 1024 - 16 * 1024 : 0;
+    if (bf16) return p.G == 2 ? launch_ckpt_t<DISC, uint16_t, 2>(a, grid, reserve, s)
+                              : launch_ckpt_t<DISC, uint16_t, 4>(a, grid, reserve, s);
+    return p.G == 2 ? launch_ckpt_t<DISC, float, 2>(a, grid, reserve, s) : launch_ckpt_t<DISC, float, 4>(a, grid, reserve, s);
+}
+
 }  // namespace
 }  // namespace ssm

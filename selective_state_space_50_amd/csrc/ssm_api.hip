@@ -155,14 +155,14 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
                             const void *C, const float *Dskip, const void *z, const float *h0,
                             const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                             void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
-                            const float *delta_bias, float *ddelta_bias, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+                            int discretization, const float *delta_bias, float *ddelta_bias,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     using namespace ssm;
     clear_error();
     BwdPlan p;
     int st = check_scan_bwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy,
-                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, delta_bias,
-                            ddelta_bias, workspace, workspace_bytes, &p);
+                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization,
+                            delta_bias, ddelta_bias, workspace, workspace_bytes, &p);
     if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -222,7 +222,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         const unsigned dblocks = static_cast<unsigned>(dim / 64);
         if (p.fwd.n_chunks > 1) {
             dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.fwd.n_chunks - 1));
-            e = launch_scan_any(fa, g1, p.fwd, kMamba, bf16, false, true, s);
+            e = launch_scan_any(fa, g1, p.fwd, discretization, bf16, false, true, s);
             if (e != hipSuccess) return hip_fail("checkpoint carry launch", e);
             const int64_t n = batch * dim * dstate;
             hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, fa);
@@ -230,7 +230,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
             if (e != hipSuccess) return hip_fail("checkpoint carry combine launch", e);
         }
         e = launch_scan_ckpt(fa, dim3(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.fwd.n_chunks)),
-                             p.fwd, bf16, s);
+                             p.fwd, discretization, bf16, s);
         if (e != hipSuccess) return hip_fail("checkpoint pass launch", e);
     }
     // 2) the adjoint carries (several chunks), the reverse sweep and the reductions
@@ -253,7 +253,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.partDB = reinterpret_cast<float *>(ws + p.partDB_off);
     a.lc_P = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcP_off) : nullptr;
     a.lc_H = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcH_off) : nullptr;
-    e = launch_scan_bwd(a, bf16, z != nullptr, s);
+    e = launch_scan_bwd(a, discretization, bf16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
 }
 

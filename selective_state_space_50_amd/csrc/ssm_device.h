@@ -197,8 +197,14 @@ SSM_SCAN_LAUNCHER(launch_scan_generic_bilinear);
 SSM_SCAN_LAUNCHER(launch_scan_fast_mamba);
 SSM_SCAN_LAUNCHER(launch_scan_fast_zoh);
 SSM_SCAN_LAUNCHER(launch_scan_fast_bilinear);
-// Specialised kernel, checkpoint pass (one chunk): the state before every 8th step into ckpt.
-hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s);
+// Specialised kernel, checkpoint pass: the state before every 8th step into ckpt (every
+// chunk from its carried-in state); launch_scan_ckpt dispatches on the discretisation.
+#define SSM_CKPT_LAUNCHER(name) \
+    hipError_t name(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, hipStream_t s)
+SSM_CKPT_LAUNCHER(launch_scan_ckpt_mamba);
+SSM_CKPT_LAUNCHER(launch_scan_ckpt_zoh);
+SSM_CKPT_LAUNCHER(launch_scan_ckpt_bilinear);
+hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, hipStream_t s);
 // Specialised path pre-pass: pack B/C rows into ws_BC.
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s);
@@ -209,6 +215,6 @@ hipError_t launch_conv1d_bwd(const ConvArgs &a, bool bf16, hipStream_t s);
 // Multi-head SSD scan (bf16, head dim 64, state size 128): one workgroup per (batch row, head).
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t s);
 // Backward pass (dstate == 16, dim % 64 == 0).
-hipError_t launch_scan_bwd(const BwdArgs &a, bool bf16, bool has_z, hipStream_t s);
+hipError_t launch_scan_bwd(const BwdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s);
 
 }  // namespace ssm

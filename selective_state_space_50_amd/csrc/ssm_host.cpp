@@ -408,12 +408,17 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const float *Dskip, const void *z, const float *h0, const void *dy,
                    const float *dh_last, const void *dx, const void *ddelta, const float *dA,
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
-                   int delta_softplus, const float *delta_bias, const float *ddelta_bias,
+                   int delta_softplus, int discretization, const float *delta_bias,
+                   const float *ddelta_bias,
                    const void *workspace, size_t workspace_bytes, BwdPlan *plan) {
     int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
     if (st != SSM_OK) return st;
     if (delta_softplus != 0 && delta_softplus != 1) {
         set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
+        return SSM_EINVAL;
+    }
+    if (discretization < SSM_DISC_MAMBA || discretization > SSM_DISC_BILINEAR) {
+        set_error("discretization=%d is not an ssm_discretization", discretization);
         return SSM_EINVAL;
     }
     if (batch == 0 || dim == 0) return SSM_OK;

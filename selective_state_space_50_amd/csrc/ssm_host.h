@@ -80,7 +80,8 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const float *Dskip, const void *z, const float *h0, const void *dy,
                    const float *dh_last, const void *dx, const void *ddelta, const float *dA,
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
-                   int delta_softplus, const float *delta_bias, const float *ddelta_bias,
+                   int delta_softplus, int discretization, const float *delta_bias,
+                   const float *ddelta_bias,
                    const void *workspace, size_t workspace_bytes, BwdPlan *plan);
 
 // Argument checks of the convolution entry points.

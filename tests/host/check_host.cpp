@@ -62,11 +62,17 @@ int main() {
         float *dA = static_cast<float *>(P(base + 16 * gap)), *dD = static_cast<float *>(P(base + 17 * gap));
         void *dz = P(base + 18 * gap), *dy = P(base + 19 * gap), *bws = P(base + 20 * gap);
         float *bias = static_cast<float *>(P(base + 21 * gap)), *dbias = static_cast<float *>(P(base + 22 * gap));
-        auto bw = [&](const float *bi, const float *dbi) {
+        auto bw = [&](const float *bi, const float *dbi, int disc = SSM_DISC_MAMBA) {
             return check_scan_bwd(2, 1000, 256, 16, SSM_DTYPE_BF16, x, dl, A, B, C, Dk, z, nullptr, dy, nullptr,
-                                  dx, ddl, dA, dB, dC, dD, dz, nullptr, 1, bi, dbi, bws, size_t(1) << 30, &bp);
+                                  dx, ddl, dA, dB, dC, dD, dz, nullptr, 1, disc, bi, dbi, bws, size_t(1) << 30,
+                                  &bp);
         };
         EXPECT(bw(nullptr, nullptr) == SSM_OK);
+        EXPECT(bw(nullptr, nullptr, SSM_DISC_ZOH) == SSM_OK);
+        EXPECT(bw(bias, dbias, SSM_DISC_BILINEAR) == SSM_OK);
+        EXPECT(bw(nullptr, nullptr, 3) == SSM_EINVAL);
+        EXPECT(std::strstr(ssm_last_error(), "discretization") != nullptr);
+        EXPECT(bw(nullptr, nullptr, -1) == SSM_EINVAL);
         EXPECT(bw(bias, dbias) == SSM_OK);
         EXPECT(bp.partDB_off > bp.partD_off && bp.ws_bytes >= bp.partDB_off + size_t(2) * 8 * 256 * 4);
         EXPECT(bw(nullptr, dbias) == SSM_OK);    // ignored without a bias

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_text(lib):
-    assert lib.ssm_abi_version() == 3
+    assert lib.ssm_abi_version() == 4
     assert lib.ssm_status_str(0) == b"ok"
     assert lib.ssm_status_str(3) == b"workspace too small"
 

@@ -42,7 +42,8 @@ def _run(ssm, inp, gy, gl):
     db = None if inp.get("delta_bias") is None else torch.from_numpy(inp["delta_bias"]).cuda()
     g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], Dt, t["z"], t["h0"], to_dev(gy, dt),
                      None if gl is None else torch.from_numpy(gl).cuda(),
-                     delta_softplus=inp["delta_softplus"], delta_bias=db)
+                     delta_softplus=inp["delta_softplus"], delta_bias=db,
+                     discretization=inp.get("discretization", "mamba"))
     torch.cuda.synchronize()
     return {k: (None if v is None else to_host(v)) for k, v in g.items()}
 
@@ -272,3 +273,114 @@ def test_backward_degenerate_steps_and_decays(ssm):
     g = _run(ssm, inp, gy, gl)
     r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"), gl)
     _check(g, r, "f32", "degenerate steps and decays")
+
+
+VARIANTS = [
+    # B, L, D, dtype, gate, h0, dh_last, softplus, bias
+    (1, 1, 64, "f32", False, False, False, False, False),
+    (2, 17, 64, "f32", True, True, True, False, True),
+    (2, 100, 128, "bf16", True, True, True, True, True),
+    (3, 333, 192, "f32", False, True, False, True, False),
+    (1, 1000, 256, "bf16", True, False, True, True, True),
+]
+
+
+@pytest.mark.parametrize("disc", ["zoh", "bilinear"])
+@pytest.mark.parametrize("Bsz,L,D,dt,gate,h0,dhl,sp,bias", VARIANTS)
+def test_backward_variant_parity(ssm, disc, Bsz, L, D, dt, gate, h0, dhl, sp, bias):
+    """The zero-order-hold and bilinear discretisations' backward: every output against
+    the fp64 oracle."""
+    inp, gy, gl = _case(Bsz, L, D, dt, gate, h0, dhl, sp, True, seed=500 + L, bias=bias)
+    inp["discretization"] = disc
+    g = _run(ssm, inp, gy, gl)
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    if not gate:
+        r["dz"] = None
+    _check(g, r, dt, f"{disc} {Bsz}x{L}x{D} {dt} gate={gate} h0={h0} dh_last={dhl} softplus={sp} bias={bias}")
+
+
+@pytest.mark.parametrize("disc,Bsz,L,D,dt,bias", [("zoh", 1, 5000, 128, "bf16", True),
+                                                 ("bilinear", 1, 5000, 128, "bf16", True),
+                                                 ("bilinear", 2, 3000, 64, "f32", False)])
+def test_backward_variant_chunked_parity(ssm, disc, Bsz, L, D, dt, bias):
+    """Chunked backward of the variants: the bilinear map's adjoint carry multiplies its
+    a_t (no exponential of a sum)."""
+    inp, gy, gl = _case(Bsz, L, D, dt, True, True, True, True, True, seed=700 + L, bias=bias)
+    inp["discretization"] = disc
+    g = _run(ssm, inp, gy, gl)
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    _check(g, r, dt, f"{disc} chunked {Bsz}x{L}x{D} {dt} bias={bias}")
+
+
+def test_backward_zoh_series_branch_and_zero_A(ssm):
+    """Zero-order hold where dt A is tiny or zero (the series branches of f and of its
+    A-derivative), and zero steps: every gradient against the oracle."""
+    inp, gy, gl = _case(2, 300, 128, "f32", True, True, True, False, True, seed=63)
+    inp["discretization"] = "zoh"
+    A = inp["A"].copy()
+    A[:, 0] = 0.0
+    A[::3, 1] = -1e-3
+    A[1::3, 2] = -0.3
+    inp["A"] = A
+    d = synth.to_f64(inp["delta"], "f32").copy()
+    d[:, :, ::11] = 0.0
+    d[:, 50:60, :] = 1e-4
+    inp["delta"] = d.astype(np.float32)
+    g = _run(ssm, inp, gy, gl)
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"), gl)
+    _check(g, r, "f32", "zoh series branch, A = 0")
+
+
+@pytest.mark.parametrize("disc", ["zoh", "bilinear"])
+def test_autograd_variant_matches_oracle(ssm, disc):
+    import torch
+    inp, gy, _ = _case(2, 50, 64, "f32", True, True, False, True, True, seed=4, bias=True)
+    inp["discretization"] = disc
+    t = device_inputs(inp)
+    t["bias"] = torch.from_numpy(inp["delta_bias"]).cuda()
+    leaves = {k: t[k].clone().requires_grad_(True) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "bias")}
+    y = ssm.selective_scan(leaves["x"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"], leaves["D"],
+                           leaves["z"], leaves["h0"], delta_softplus=True, delta_bias=leaves["bias"],
+                           discretization=disc)
+    (y * to_dev(gy, "f32")).sum().backward()
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"))
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0",
+             "bias": "ddelta_bias"}
+    for k, rk in names.items():
+        assert_close_grad(to_host(leaves[k].grad), r[rk], "f32", f"autograd {disc} {k}")
+
+
+@pytest.mark.parametrize("disc", ["zoh", "bilinear"])
+def test_backward_variant_headline_shape_sampled(ssm, disc):
+    """The variants' backward at the B4 L4096 D4096 N16 bf16 gated layer: every output
+    finite; dx, ddelta, dz of every row of 6 sampled dims, and dA, dD of those dims (sums
+    over the 4 rows), against the fp64 oracle."""
+    import torch
+    c = synth.CONFIGS[2]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    inp = synth.config_inputs(2)
+    inp["discretization"] = disc
+    gy = synth.store(np.random.default_rng(2025).standard_normal((Bsz, L, D), dtype=np.float32), "bf16")
+    t = device_inputs(inp)
+    g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, to_dev(gy, "bf16"),
+                     need_dh0=False, discretization=disc)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddelta", "dz", "dB", "dC", "dA", "dD"):
+        assert bool(torch.isfinite(g[k].float()).all()), k
+    dims = np.array([0, 63, 64, 1777, 2048, 4095])
+    cb = np.repeat(np.arange(Bsz), len(dims))
+    cd = np.tile(dims, Bsz)
+    w = lambda a: synth.to_f64(a, "bf16")
+    ser = lambda a: w(np.ascontiguousarray(a[cb, :, cd]))
+    r = oracle.scan_bwd_f64(ser(inp["x"]), ser(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["Dskip"],
+                            ser(inp["z"]), None, ser(gy), None, False, cb, cd, discretization=disc)
+    tcb, tcd = torch.tensor(cb, device="cuda"), torch.tensor(cd, device="cuda")
+    worst = {}
+    for k in ("dx", "ddelta", "dz"):
+        worst[k] = assert_close_grad(to_host(g[k][tcb, :, tcd]), r[k], "bf16", f"{disc} headline {k}")
+    dA = r["dA_c"].reshape(Bsz, len(dims), N).sum(axis=0)
+    dDs = r["dD_c"].reshape(Bsz, len(dims)).sum(axis=0)
+    worst["dA"] = assert_close_grad(to_host(g["dA"][torch.tensor(dims, device="cuda")]), dA, "f32", f"{disc} headline dA")
+    worst["dD"] = assert_close_grad(to_host(g["dD"][torch.tensor(dims, device="cuda")]), dDs, "f32", f"{disc} headline dD")
+    print(f"[parity] {disc} backward headline shape (sampled): worst ratios "
+          + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()), flush=True)
