@@ -703,6 +703,25 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
     }
     log(f"backward: {ms:.3f} ms median ({upd / (ms * 1e-3):.3e} state-updates/s, VALU {bwd_ts / VALU_PEAK_TSLOTS:.1%})")
+    # the same backward under the other discretisations (their derivatives cost more VALU
+    # work per state update than Mamba's; timed, not priced against the roofline)
+    out["backward"]["variants"] = {}
+    for disc in ("zoh", "bilinear"):
+        for _ in range(2):
+            ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False, discretization=disc)
+        torch.cuda.synchronize()
+        vt = []
+        for _ in range(5):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False, discretization=disc)
+            b_.record()
+            torch.cuda.synchronize()
+            vt.append(a_.elapsed_time(b_))
+        vt.sort()
+        vms = vt[len(vt) // 2]
+        out["backward"]["variants"][disc] = {"ms_median": round(vms, 4), "state_updates_per_s": upd / (vms * 1e-3)}
+        log(f"backward, {disc}: {vms:.3f} ms median ({upd / (vms * 1e-3):.3e} state-updates/s)")
     # oracle beside it: 64 channels of every batch row over the whole sequence
     dsel = torch.arange(0, D, 32, device=dev)   # (the oracle keeps per-channel dB, dC: [channels, L, N] each)
     ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)
