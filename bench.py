@@ -722,6 +722,58 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         vms = vt[len(vt) // 2]
         out["backward"]["variants"][disc] = {"ms_median": round(vms, 4), "state_updates_per_s": upd / (vms * 1e-3)}
         log(f"backward, {disc}: {vms:.3f} ms median ({upd / (vms * 1e-3):.3e} state-updates/s)")
+    # a training step's scan: the forward that saves the checkpoints, then the backward
+    # given them (it skips its own forward sweep), against the forward + the backward alone
+    y = torch.empty_like(x)
+    fws_b, ck_b = ssm.scan_save_sizes(Bsz, L, D, N, "bf16")
+    fws = torch.empty(max(fws_b, 1), dtype=torch.uint8, device=dev)
+    ck = torch.empty((Bsz, (L + 7) // 8, N, D), dtype=torch.float32, device=dev)
+    pws = torch.empty(max(ssm.scan_plan(Bsz, L, D, N, "bf16")["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    bws = torch.empty(ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16", saved_checkpoints=True), dtype=torch.uint8,
+                      device=dev)
+
+    def fwd_plain():
+        ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=pws)
+
+    def fwd_save():
+        ssm.scan_fwd_save(x, dl, A, Bm, Cm, Dk, z, out=y, checkpoints=ck, workspace=fws)
+
+    def bwd_full():
+        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
+
+    def bwd_saved():
+        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=bws, need_dh0=False, checkpoints=ck)
+
+    def med(fns):
+        for _ in range(2):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        tt = []
+        for _ in range(5):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            for f in fns:
+                f()
+            b_.record()
+            torch.cuda.synchronize()
+            tt.append(a_.elapsed_time(b_))
+        tt.sort()
+        return tt[len(tt) // 2]
+
+    t_save, t_bsaved = med([fwd_save]), med([bwd_saved])
+    t_pair_saved, t_pair_plain = med([fwd_save, bwd_saved]), med([fwd_plain, bwd_full])
+    out["backward"]["training_step"] = {
+        "workload": c["name"] + " forward + backward (all gradients)",
+        "ms_forward_saving_checkpoints": round(t_save, 4), "ms_backward_from_checkpoints": round(t_bsaved, 4),
+        "ms_step_with_saved_checkpoints": round(t_pair_saved, 4),
+        "ms_step_recomputing_checkpoints": round(t_pair_plain, 4),
+        "checkpoint_bytes": ck_b,
+        "timing": "medians of 5, each call or pair between two events",
+    }
+    log(f"training step: forward saving checkpoints {t_save:.3f} ms + backward from them {t_bsaved:.3f} ms; "
+        f"pair {t_pair_saved:.3f} ms against {t_pair_plain:.3f} ms for forward + recomputing backward")
+    del y, fws, ck, pws, bws
     # oracle beside it: 64 channels of every batch row over the whole sequence
     dsel = torch.arange(0, D, 32, device=dev)   # (the oracle keeps per-channel dB, dC: [channels, L, N] each)
     ser = lambda t: _host(t[:, :, dsel].permute(0, 2, 1)).reshape(Bsz * len(dsel), L)

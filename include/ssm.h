@@ -198,10 +198,42 @@ int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, floa
                      const void *C, const float *Dskip, const void *z, void *y,
                      int delta_softplus, const ssm_variant *variant, void *stream);
 
+/*
+ * Host-only: sizes for ssm_scan_fwd_save at this shape: the device workspace it needs
+ * (*workspace_bytes, 0 when none) and the bytes of its checkpoint output
+ * (*checkpoint_bytes = batch * ceil(seqlen / 8) * 16 * dim * 4).  Both are set to 0 and
+ * an ssm_status returned when the shape is invalid or unsupported (dstate must be 16 and
+ * dim a multiple of 64, as for ssm_scan_bwd); SSM_EINVAL when either pointer is NULL.
+ */
+int ssm_scan_save_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                        size_t *workspace_bytes, size_t *checkpoint_bytes);
+
+/*
+ * ssm_scan_fwd that also stores what ssm_scan_bwd would otherwise recompute: the state
+ * h before every 8th step (t = 0, 8, 16, ...), for the reverse sweep of a training step.
+ * Same recurrence, arguments, layouts and results as ssm_scan_fwd (y and h_last agree
+ * with it up to the rounding of a different sequence chunking, bit for bit when neither
+ * call splits the sequence), without ssm_scan_opts: the sequence is chunked as the
+ * backward chunks it.  Additionally
+ *   checkpoints  [batch][ceil(seqlen/8)][16][dim] fp32, device memory owned by the
+ *                caller, ssm_scan_save_sizes() bytes, 16-byte aligned, overlapping no
+ *                other argument; fully overwritten.  Entry [b][k][n][d] is the state
+ *                of (b, d, n) before step 8k.
+ *   workspace    device memory of ssm_scan_save_sizes() bytes (NULL if 0)
+ * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  seqlen == 0 sets
+ * h_last = h0 (or zeros) and stores no checkpoints.
+ */
+int ssm_scan_fwd_save(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                      const void *x, const void *delta, const float *A, const void *B,
+                      const void *C, const float *Dskip, const void *z, const float *h0,
+                      float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                      float *checkpoints, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Host-only: bytes of device workspace ssm_scan_bwd needs for this shape (0 when
- * nothing is computed, or the shape is invalid or unsupported). */
+ * nothing is computed, or the shape is invalid or unsupported); with
+ * saved_checkpoints != 0, for a call given checkpoints (less: no checkpoint pass). */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                                    int dtype);
+                                    int dtype, int saved_checkpoints);
 
 /*
  * Backward pass of ssm_scan_fwd: gradients of a loss with respect to every input,
@@ -237,8 +269,13 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   dh0       [batch, dim, dstate]   fp32    NULL = not stored
  *   ddelta_bias [dim]                fp32    required when delta_bias is given, else
  *             ignored: the sum of ddelta over batch and time
- *   workspace device memory of ssm_scan_bwd_workspace_bytes() bytes (state
- *             checkpoints every 8 steps, partial sums)
+ *   checkpoints  NULL: the call first runs the forward again, storing the state before
+ *             every 8th step in its workspace; else the checkpoints that ssm_scan_fwd_save
+ *             stored for these same inputs (x, delta, A, B, C, h0, delta_softplus,
+ *             discretisation, delta_bias), read only.  Checkpoints of other inputs give
+ *             meaningless gradients; nothing can detect that.
+ *   workspace device memory of ssm_scan_bwd_workspace_bytes(..., checkpoints != NULL)
+ *             bytes (partial sums, and without saved checkpoints the checkpoints)
  *
  * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  batch or dim
  * == 0 is a no-op; seqlen == 0 sets dh0 = dh_last (or zeros) and dA, dD, ddelta_bias
@@ -250,8 +287,8 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  const void *C, const float *Dskip, const void *z, const float *h0,
                  const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                  void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
-                 int discretization, const float *delta_bias, float *ddelta_bias, void *workspace,
-                 size_t workspace_bytes, void *stream);
+                 int discretization, const float *delta_bias, float *ddelta_bias,
+                 const float *checkpoints, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Causal depthwise convolution along the sequence, then SiLU: the step before the scan

@@ -13,7 +13,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["scan_fwd", "scan_bwd", "state_update", "scan_plan", "scan_workspace_bytes",
+__all__ = ["scan_fwd", "scan_fwd_save", "scan_save_sizes", "scan_bwd", "state_update", "scan_plan", "scan_workspace_bytes",
            "scan_bwd_workspace_bytes", "selective_scan", "conv1d_fwd", "conv1d_update", "lib",
            "SSMError", "LIB_PATH",
            "HEADER_PATH", "exported_api"]
@@ -86,9 +86,13 @@ def lib():
     L.ssm_state_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, I32,
                                    ctypes.POINTER(Variant), P]
     L.ssm_scan_bwd_workspace_bytes.restype = SZ
-    L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32]
+    L.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I32, I32]
     L.ssm_scan_bwd.restype = I32
-    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, I32, P, P, P, SZ, P]
+    L.ssm_scan_bwd.argtypes = [I64, I64, I64, I64, I32] + [P] * 18 + [I32, I32, P, P, P, P, SZ, P]
+    L.ssm_scan_save_sizes.restype = I32
+    L.ssm_scan_save_sizes.argtypes = [I64, I64, I64, I64, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    L.ssm_scan_fwd_save.restype = I32
+    L.ssm_scan_fwd_save.argtypes = [I64, I64, I64, I64, I32] + [P] * 10 + [I32, ctypes.POINTER(Variant), P, P, SZ, P]
     L.ssm_conv1d_fwd.restype = I32
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
     L.ssm_ssd_fwd.restype = I32
@@ -274,17 +278,74 @@ def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False,
     return out
 
 
-def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16") -> int:
+def scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype="bf16", saved_checkpoints=False) -> int:
     code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
-    return int(lib().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, code))
+    return int(lib().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, code, int(bool(saved_checkpoints))))
+
+
+def scan_save_sizes(batch, seqlen, dim, dstate, dtype="bf16"):
+    """(workspace bytes, checkpoint bytes) of scan_fwd_save at this shape."""
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    ws, ck = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().ssm_scan_save_sizes(batch, seqlen, dim, dstate, code, ctypes.byref(ws), ctypes.byref(ck)),
+           "ssm_scan_save_sizes")
+    return int(ws.value), int(ck.value)
+
+
+def scan_fwd_save(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
+                  discretization="mamba", delta_bias=None, return_last_state=False, out=None,
+                  h_last=None, checkpoints=None, workspace=None, stream=None):
+    """scan_fwd that also stores the state before every 8th step for scan_bwd (its
+    ``checkpoints`` argument), on the backward's sequence chunking.  Arguments as
+    scan_fwd (dstate 16 and dim a multiple of 64 only).  Returns (y, checkpoints), or
+    (y, h_last, checkpoints) when return_last_state; checkpoints is a flat fp32 tensor
+    [B, ceil(L/8), N, D]."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, dim] and A [dim, dstate]")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd_save runs on the GPU only; tensors must be on a cuda device")
+    for t, name, shape, tdt in ((x, "x", (Bsz, L, Dm), dt), (delta, "delta", (Bsz, L, Dm), dt),
+                                (z, "z", (Bsz, L, Dm), dt), (B, "B", (Bsz, L, N), dt), (C, "C", (Bsz, L, N), dt),
+                                (A, "A", (Dm, N), torch.float32), (D, "D", (Dm,), torch.float32),
+                                (h0, "h0", (Bsz, Dm, N), torch.float32)):
+        _need(t, name, shape, tdt, dev)
+    v = _variant(discretization, delta_bias, Dm, dev)
+    code = _dtype_code(x)
+    ws_bytes, ck_bytes = scan_save_sizes(Bsz, L, Dm, N, "bf16" if code == DTYPE_BF16 else "f32")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, L, Dm), dt, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
+    _need(h_last, "h_last", (Bsz, Dm, N), torch.float32, dev)
+    nck = (L + 7) // 8
+    if checkpoints is None:
+        checkpoints = torch.empty((Bsz, nck, N, Dm), dtype=torch.float32, device=dev)
+    _need(checkpoints, "checkpoints", (Bsz, nck, N, Dm), torch.float32, dev)
+    assert checkpoints.numel() * 4 == ck_bytes
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_scan_fwd_save(Bsz, L, Dm, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(z), _ptr(h0), _ptr(h_last), _ptr(out),
+                                 int(bool(delta_softplus)), ctypes.byref(v) if v else None,
+                                 _ptr(checkpoints), _ptr(workspace) if ws_bytes else None, ws_bytes,
+                                 ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_scan_fwd_save")
+    return (out, h_last, checkpoints) if return_last_state else (out, checkpoints)
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, *,
              delta_softplus=False, discretization="mamba", delta_bias=None, need_dh0=True,
-             workspace=None, stream=None):
+             checkpoints=None, workspace=None, stream=None):
     """Gradients of a loss through scan_fwd, given dy = dLoss/dy [B, L, D] (same dtype as
     x) and optionally dh_last = dLoss/dh_last [B, D, N] fp32.  discretization and
-    delta_bias [D] fp32: as in scan_fwd.
+    delta_bias [D] fp32: as in scan_fwd.  checkpoints: what scan_fwd_save stored for these
+    same inputs (the call then skips its own forward sweep), or None.
 
     Returns a dict: dx, ddelta, dz (None without z) in x's dtype [B, L, D]; dB, dC in
     x's dtype [B, L, N]; dA [D, N], dD [D] (None without D), ddelta_bias [D] (None
@@ -309,6 +370,8 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
                                 (dy, "dy", (Bsz, L, Dm), dt), (dh_last, "dh_last", (Bsz, Dm, N), torch.float32),
                                 (delta_bias, "delta_bias", (Dm,), torch.float32)):
         _need(t, name, shape, tdt, dev)
+    if checkpoints is not None:
+        _need(checkpoints, "checkpoints", (Bsz, (L + 7) // 8, N, Dm), torch.float32, dev)
     code = _dtype_code(x)
     out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
            "dz": torch.empty_like(x) if z is not None else None,
@@ -318,7 +381,7 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
            "dD": torch.empty((Dm,), dtype=torch.float32, device=dev) if D is not None else None,
            "dh0": torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if need_dh0 else None,
            "ddelta_bias": torch.empty((Dm,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
-    ws_bytes = int(lib().ssm_scan_bwd_workspace_bytes(Bsz, L, Dm, N, code))
+    ws_bytes = int(lib().ssm_scan_bwd_workspace_bytes(Bsz, L, Dm, N, code, int(checkpoints is not None)))
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
@@ -326,7 +389,9 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
                             _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["dx"]),
                             _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
                             _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]), int(bool(delta_softplus)),
-                            DISCRETIZATIONS[discretization], _ptr(delta_bias), _ptr(out["ddelta_bias"]), _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+                            DISCRETIZATIONS[discretization], _ptr(delta_bias), _ptr(out["ddelta_bias"]),
+                            _ptr(checkpoints), _ptr(workspace) if ws_bytes else None, ws_bytes,
+                            ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_scan_bwd")
     return out
 
@@ -334,22 +399,30 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
 def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=False, delta_bias=None,
                    discretization="mamba"):
     """Differentiable selective scan: y = scan_fwd(...) with a torch autograd backward
-    through scan_bwd (gradients for every tensor argument, delta_bias included)."""
+    through scan_bwd (gradients for every tensor argument, delta_bias included).  The
+    forward stores the state checkpoints (scan_fwd_save) when the backward supports the
+    shape (dstate 16, dim a multiple of 64), so that the backward skips its own forward
+    sweep."""
     import torch
 
     class _Scan(torch.autograd.Function):
         @staticmethod
         def forward(ctx, x, delta, A, B, C, D, z, h0, delta_bias):
-            y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus,
-                         discretization=discretization, delta_bias=delta_bias)
-            ctx.save_for_backward(x, delta, A, B, C, D, z, h0, delta_bias)
+            ck = None
+            if A.shape[1] == 16 and x.shape[2] % 64 == 0 and x.shape[1] > 0:
+                y, ck = scan_fwd_save(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus,
+                                      discretization=discretization, delta_bias=delta_bias)
+            else:
+                y = scan_fwd(x, delta, A, B, C, D, z, h0, delta_softplus=delta_softplus,
+                             discretization=discretization, delta_bias=delta_bias)
+            ctx.save_for_backward(x, delta, A, B, C, D, z, h0, delta_bias, ck)
             return y
 
         @staticmethod
         def backward(ctx, gy):
-            x, delta, A, B, C, D, z, h0, delta_bias = ctx.saved_tensors
+            x, delta, A, B, C, D, z, h0, delta_bias, ck = ctx.saved_tensors
             g = scan_bwd(x, delta, A, B, C, D, z, h0, gy.contiguous(), delta_softplus=delta_softplus,
-                         discretization=discretization, delta_bias=delta_bias, need_dh0=h0 is not None and ctx.needs_input_grad[7])
+                         discretization=discretization, delta_bias=delta_bias, checkpoints=ck, need_dh0=h0 is not None and ctx.needs_input_grad[7])
             return (g["dx"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["dh0"],
                     g["ddelta_bias"])
 

@@ -1,5 +1,6 @@
 // Specialised selective scan (dstate == 16, dim % 64 == 0): the Mamba
-// discretisation, the B/C pre-pass and the backward's checkpoint pass.  The
+// discretisation, the B/C pre-pass, the backward's checkpoint pass and the forward that
+// saves those checkpoints.  The
 // kernel itself is in scan_fast_kernel.h.
 #include "scan_fast_kernel.h"
 
@@ -22,6 +23,14 @@ hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipSt
 }
 
 SSM_CKPT_LAUNCHER(launch_scan_ckpt_mamba) { return launch_ckpt<kMamba>(a, grid, p, bf16, s); }
+SSM_SAVE_LAUNCHER(launch_scan_save_mamba) { return launch_save<kMamba>(a, grid, p, bf16, has_z, s); }
+
+hipError_t launch_scan_save(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, bool has_z,
+                            hipStream_t s) {
+    if (disc == kZOH) return launch_scan_save_zoh(a, grid, p, bf16, has_z, s);
+    if (disc == kBilinear) return launch_scan_save_bilinear(a, grid, p, bf16, has_z, s);
+    return launch_scan_save_mamba(a, grid, p, bf16, has_z, s);
+}
 
 hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, hipStream_t s) {
     if (disc == kZOH) return launch_scan_ckpt_zoh(a, grid, p, bf16, s);

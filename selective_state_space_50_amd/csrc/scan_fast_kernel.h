@@ -126,7 +126,8 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
 
 // CARRY: no y; store the chunk's decay (product of A_bar) and end state (chunk carries),
 // or with CKPT the state at the start of every 8-step group instead (checkpoints for the
-// backward).  DISC: the discretisation (kMamba, kZOH, kBilinear).
+// backward).  CKPT without CARRY: the ordinary forward (y, h_last) that also stores those
+// checkpoints.  DISC: the discretisation (kMamba, kZOH, kBilinear).
 template <int DISC, typename T, int G, bool HAS_Z, bool CARRY, bool CKPT = false>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
     constexpr int NC = kN / G;          // compute waves
@@ -408,7 +409,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             compute_block(k, Par<0>{});
             __syncthreads();
         }
-        if constexpr (CKPT) {
+        if constexpr (CARRY && CKPT) {
         } else if constexpr (CARRY) {
             const int64_t slot = b * (a.n_chunks - 1) + c;
 #pragma unroll
@@ -531,6 +532,23 @@ hipError_t launch_fast(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf1
                        hipStream_t s) {
     return bf16 ? launch_dt<DISC, uint16_t>(a, grid, p, has_z, carry, s)
                 : launch_dt<DISC, float>(a, grid, p, has_z, carry, s);
+}
+
+// the forward that also stores the checkpoints (same residency as the forward)
+template <int DISC, typename T, int G>
+hipError_t launch_save_t(const ScanArgs &a, dim3 grid, bool has_z, size_t lds_reserve, hipStream_t s) {
+    const dim3 block(64 * waves_per_block<G>());
+    if (has_z) hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, true, false, true>), grid, block, lds_reserve, s, a);
+    else hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, false, false, true>), grid, block, lds_reserve, s, a);
+    return hipGetLastError();
+}
+
+template <int DISC>
+hipError_t launch_save(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z, hipStream_t s) {
+    if (bf16) return p.G == 2 ? launch_save_t<DISC, uint16_t, 2>(a, grid, has_z, p.lds_reserve, s)
+                              : launch_save_t<DISC, uint16_t, 4>(a, grid, has_z, p.lds_reserve, s);
+    return p.G == 2 ? launch_save_t<DISC, float, 2>(a, grid, has_z, p.lds_reserve, s)
+                    : launch_save_t<DISC, float, 4>(a, grid, has_z, p.lds_reserve, s);
 }
 
 template <int DISC, typename T, int G>

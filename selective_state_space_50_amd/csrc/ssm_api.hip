@@ -63,28 +63,17 @@ hipError_t launch_scan_any(const ScanArgs &a, dim3 grid, const ScanPlan &p, int 
 }  // namespace
 }  // namespace ssm
 
-extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                            const void *x, const void *delta, const float *A, const void *B,
-                            const void *C, const float *Dskip, const void *z, const float *h0,
-                            float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
-                            const ssm_scan_opts *opts, void *workspace, size_t workspace_bytes,
-                            void *stream) {
-    using namespace ssm;
-    clear_error();
-    ScanPlan p;
-    int st = check_scan(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last,
-                        y, delta_softplus, variant, opts, workspace, workspace_bytes, &p);
-    if (st != SSM_OK) return st;
-    if (batch == 0 || dim == 0) return SSM_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (seqlen == 0) {
-        if (!h_last) return SSM_OK;
-        const int64_t n = batch * dim * dstate;
-        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                           0, s, h_last, h0, n);
-        hipError_t e = hipGetLastError();
-        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
-    }
+namespace ssm {
+namespace {
+
+// The forward on a checked plan: B/C pre-pass, chunk carries and their combine (several
+// chunks), then every chunk from its carried-in state producing y (and, given ckpt, the
+// state before every 8th step, for the backward).
+int run_scan(const ScanPlan &p, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+             const void *x, const void *delta, const float *A, const void *B, const void *C,
+             const float *Dskip, const void *z, const float *h0, float *h_last, void *y,
+             int delta_softplus, const ssm_variant *variant, void *workspace, float *ckpt,
+             int64_t ck_nblk, hipStream_t s) {
     ScanArgs a;
     a.B = batch; a.L = seqlen; a.D = dim; a.N = dstate;
     a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;
@@ -119,11 +108,42 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         e = hipGetLastError();
         if (e != hipSuccess) return hip_fail("carry combine launch", e);
     }
-    // 3) every chunk from its carried-in state, producing y
+    // 3) every chunk from its carried-in state, producing y (and the checkpoints)
     dim3 g3(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks));
-    e = launch_scan_any(a, g3, p, disc, bf16, has_z, false, s);
+    a.ckpt = ckpt;
+    a.ck_nblk = ck_nblk;
+    e = ckpt ? launch_scan_save(a, g3, p, disc, bf16, has_z, s) : launch_scan_any(a, g3, p, disc, bf16, has_z, false, s);
     if (e != hipSuccess) return hip_fail("scan launch", e);
     return SSM_OK;
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                            const void *x, const void *delta, const float *A, const void *B,
+                            const void *C, const float *Dskip, const void *z, const float *h0,
+                            float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                            const ssm_scan_opts *opts, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    using namespace ssm;
+    clear_error();
+    ScanPlan p;
+    int st = check_scan(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last,
+                        y, delta_softplus, variant, opts, workspace, workspace_bytes, &p);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_last) return SSM_OK;
+        const int64_t n = batch * dim * dstate;
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                           0, s, h_last, h0, n);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
+    }
+    return run_scan(p, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
+                    delta_softplus, variant, workspace, nullptr, 0, s);
 }
 
 extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, float *h,
@@ -150,19 +170,45 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int 
     return e == hipSuccess ? SSM_OK : hip_fail("state update launch", e);
 }
 
+extern "C" int ssm_scan_fwd_save(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                 const void *x, const void *delta, const float *A, const void *B,
+                                 const void *C, const float *Dskip, const void *z, const float *h0,
+                                 float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                                 float *checkpoints, void *workspace, size_t workspace_bytes, void *stream) {
+    using namespace ssm;
+    clear_error();
+    BwdPlan bp;
+    int st = check_scan_save(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
+                             delta_softplus, variant, checkpoints, workspace, workspace_bytes, &bp);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {   // no steps and no checkpoints: h_last = h0
+        if (!h_last) return SSM_OK;
+        const int64_t n = batch * dim * dstate;
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                           0, s, h_last, h0, n);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
+    }
+    return run_scan(bp.fwd, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
+                    delta_softplus, variant, workspace, checkpoints, bp.nblk, s);
+}
+
 extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
                             const void *x, const void *delta, const float *A, const void *B,
                             const void *C, const float *Dskip, const void *z, const float *h0,
                             const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                             void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
                             int discretization, const float *delta_bias, float *ddelta_bias,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                            const float *checkpoints, void *workspace, size_t workspace_bytes,
+                            void *stream) {
     using namespace ssm;
     clear_error();
     BwdPlan p;
     int st = check_scan_bwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy,
                             dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization,
-                            delta_bias, ddelta_bias, workspace, workspace_bytes, &p);
+                            delta_bias, ddelta_bias, checkpoints, workspace, workspace_bytes, &p);
     if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -199,8 +245,9 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     // 1) checkpoints: the specialised forward kernel over the sequence, storing the state
     //    before every 8th step (B/C packed first, as for the forward); with several chunks
     //    the forward's carries and combine come first, and every chunk starts from its
-    //    carried-in state
-    {
+    //    carried-in state.  Skipped when the caller passes the checkpoints that
+    //    ssm_scan_fwd_save stored.
+    if (!checkpoints) {
         char *fws = ws + p.fwd_off;
         ScanArgs fa;
         fa.B = batch; fa.L = seqlen; fa.D = dim; fa.N = dstate;
@@ -244,7 +291,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.nblk = p.nblk;
     a.n_chunks = p.n_chunks;
     a.chunk_len = p.chunk_len;
-    a.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
+    a.ckpt = checkpoints ? const_cast<float *>(checkpoints) : reinterpret_cast<float *>(ws + p.ckpt_off);
     a.partBC = reinterpret_cast<float *>(ws + p.partBC_off);
     a.partA = reinterpret_cast<float *>(ws + p.partA_off);
     a.partD = reinterpret_cast<float *>(ws + p.partD_off);

@@ -205,6 +205,14 @@ SSM_CKPT_LAUNCHER(launch_scan_ckpt_mamba);
 SSM_CKPT_LAUNCHER(launch_scan_ckpt_zoh);
 SSM_CKPT_LAUNCHER(launch_scan_ckpt_bilinear);
 hipError_t launch_scan_ckpt(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, hipStream_t s);
+// Specialised kernel, forward that also stores those checkpoints (y, h_last as the forward).
+#define SSM_SAVE_LAUNCHER(name) \
+    hipError_t name(const ScanArgs &a, dim3 grid, const ScanPlan &p, bool bf16, bool has_z, hipStream_t s)
+SSM_SAVE_LAUNCHER(launch_scan_save_mamba);
+SSM_SAVE_LAUNCHER(launch_scan_save_zoh);
+SSM_SAVE_LAUNCHER(launch_scan_save_bilinear);
+hipError_t launch_scan_save(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, bool has_z,
+                            hipStream_t s);
 // Specialised path pre-pass: pack B/C rows into ws_BC.
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s);

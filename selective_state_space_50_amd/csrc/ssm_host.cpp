@@ -379,10 +379,6 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
     const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen), D = static_cast<size_t>(dim);
     const size_t NC = static_cast<size_t>(p.n_chunks);
     size_t ws = 0;
-    p.fwd_off = ws;
-    ws = align_up(ws + p.fwd.ws_bytes, kWsAlign);
-    p.ckpt_off = ws;
-    ws = align_up(ws + B * static_cast<size_t>(p.nblk) * D * 16 * sizeof(float), kWsAlign);
     p.partBC_off = ws;
     ws = align_up(ws + 2 * B * (D / 64) * L * 16 * sizeof(float), kWsAlign);
     p.partA_off = ws;
@@ -398,7 +394,14 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
         p.lcH_off = ws;
         ws = align_up(ws + carries, kWsAlign);
     }
-    p.ws_bytes = (batch == 0 || seqlen == 0 || dim == 0) ? 0 : ws;
+    p.fwd_off = ws;
+    p.ws_bytes_saved = ws;
+    ws = align_up(ws + p.fwd.ws_bytes, kWsAlign);
+    p.ckpt_off = ws;
+    p.ckpt_bytes = B * static_cast<size_t>(p.nblk) * D * 16 * sizeof(float);
+    ws = align_up(ws + p.ckpt_bytes, kWsAlign);
+    p.ws_bytes = ws;
+    if (batch == 0 || seqlen == 0 || dim == 0) p.ws_bytes = p.ws_bytes_saved = p.ckpt_bytes = 0;
     *plan = p;
     return SSM_OK;
 }
@@ -409,7 +412,7 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const float *dh_last, const void *dx, const void *ddelta, const float *dA,
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
                    int delta_softplus, int discretization, const float *delta_bias,
-                   const float *ddelta_bias,
+                   const float *ddelta_bias, const float *checkpoints,
                    const void *workspace, size_t workspace_bytes, BwdPlan *plan) {
     int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
     if (st != SSM_OK) return st;
@@ -445,19 +448,62 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
         range("dB", dB, bc), range("dC", dC, bc), range("dD", Dskip ? dD : nullptr, dim * 4),
         range("dz", z ? dz : nullptr, tok), range("dh0", dh0, stb),
         range("ddelta_bias", delta_bias ? ddelta_bias : nullptr, dim * 4),
-        range("workspace", workspace, static_cast<int64_t>(plan->ws_bytes)),
+        range("workspace", workspace, static_cast<int64_t>(checkpoints ? plan->ws_bytes_saved : plan->ws_bytes)),
+        range("checkpoints", checkpoints, static_cast<int64_t>(plan->ckpt_bytes)),   // an input
     };
     const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
     st = check_aligned(all, n_all);
     if (st != SSM_OK) return st;
-    st = check_no_overlap(all + 11, n_all - 11, all, n_all);
+    st = check_no_overlap(all + 11, n_all - 12, all, n_all);
     if (st != SSM_OK) return st;
-    if (plan->ws_bytes > 0 && (!workspace || workspace_bytes < plan->ws_bytes)) {
-        set_error("workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
-                  plan->ws_bytes);
+    const size_t need = checkpoints ? plan->ws_bytes_saved : plan->ws_bytes;
+    if (seqlen > 0 && need > 0 && (!workspace || workspace_bytes < need)) {
+        set_error("workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
         return SSM_EWORKSPACE;
     }
     return SSM_OK;
+}
+
+int check_scan_save(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                    const void *x, const void *delta, const float *A, const void *B, const void *C,
+                    const float *Dskip, const void *z, const float *h0, const float *h_last,
+                    const void *y, int delta_softplus, const ssm_variant *variant,
+                    const float *checkpoints, const void *workspace, size_t workspace_bytes,
+                    BwdPlan *plan) {
+    int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
+    if (st != SSM_OK) return st;
+    // the forward's own checks, on the backward's chunk plan (so that the checkpoints sit
+    // every 8 steps from each chunk's start, as the reverse sweep reads them)
+    ssm_scan_opts o = {plan->chunk_len, 0, 0, 0, 0};
+    ScanPlan fp;
+    st = check_scan(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
+                    delta_softplus, variant, seqlen > 0 ? &o : nullptr, workspace, workspace_bytes, &fp);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0 || seqlen == 0) return SSM_OK;
+    if (fp.n_chunks != plan->fwd.n_chunks || fp.chunk_len != plan->fwd.chunk_len || !fp.fast) {
+        set_error("ssm_scan_fwd_save: no chunk plan for this shape");
+        return SSM_EUNSUPPORTED;
+    }
+    if (!checkpoints) {
+        set_error("required pointer checkpoints is NULL");
+        return SSM_EINVAL;
+    }
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    const int64_t tok = batch * seqlen * dim * es;
+    const int64_t bc = batch * seqlen * dstate * es;
+    const int64_t stb = batch * dim * dstate * 4;
+    Range all[] = {
+        range("checkpoints", checkpoints, static_cast<int64_t>(plan->ckpt_bytes)),
+        range("x", x, tok), range("delta", delta, tok), range("z", z, tok), range("B", B, bc),
+        range("C", C, bc), range("A", A, dim * dstate * 4), range("Dskip", Dskip, dim * 4),
+        range("h0", h0, stb), range("h_last", h_last, stb), range("y", y, tok),
+        range("workspace", workspace, static_cast<int64_t>(fp.ws_bytes)),
+        range("delta_bias", variant_bias(variant), dim * 4),
+    };
+    const int n_all = static_cast<int>(sizeof(all) / sizeof(all[0]));
+    st = check_aligned(all, 1);
+    if (st != SSM_OK) return st;
+    return check_no_overlap(all, 1, all, n_all);
 }
 
 namespace {
@@ -634,11 +680,29 @@ int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, in
 
 extern "C" {
 
-size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype) {
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                    int saved_checkpoints) {
     ssm::clear_error();
     ssm::BwdPlan p;
     if (ssm::plan_scan_bwd(batch, seqlen, dim, dstate, dtype, &p) != SSM_OK) return 0;
-    return p.ws_bytes;
+    return saved_checkpoints ? p.ws_bytes_saved : p.ws_bytes;
+}
+
+int ssm_scan_save_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                        size_t *workspace_bytes, size_t *checkpoint_bytes) {
+    ssm::clear_error();
+    if (!workspace_bytes || !checkpoint_bytes) {
+        ssm::set_error("required pointer %s is NULL", !workspace_bytes ? "workspace_bytes" : "checkpoint_bytes");
+        return SSM_EINVAL;
+    }
+    *workspace_bytes = 0;
+    *checkpoint_bytes = 0;
+    ssm::BwdPlan p;
+    const int st = ssm::plan_scan_bwd(batch, seqlen, dim, dstate, dtype, &p);
+    if (st != SSM_OK) return st;
+    if (batch > 0 && seqlen > 0 && dim > 0) *workspace_bytes = p.fwd.ws_bytes;
+    *checkpoint_bytes = p.ckpt_bytes;
+    return SSM_OK;
 }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }

@@ -59,16 +59,21 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
 inline int variant_disc(const ssm_variant *v) { return v ? v->discretization : SSM_DISC_MAMBA; }
 inline const float *variant_bias(const ssm_variant *v) { return v ? v->delta_bias : nullptr; }
 
-// Workspace of ssm_scan_bwd: packed B/C and state checkpoints of the forward
-// checkpoint pass, per-workgroup shares of dB/dC, per-batch-row shares of dA/dD.
+// Workspace of ssm_scan_bwd: per-workgroup shares of dB/dC, per-(chunk, row) shares of
+// dA/dD, the adjoint carries, then (last, so that a call given saved checkpoints needs
+// only the part before them) the forward checkpoint pass's own workspace and the state
+// checkpoints.
 struct BwdPlan {
     int64_t nblk = 0;       // 8-step blocks of the reverse sweep
     int64_t n_chunks = 1, chunk_len = 0;   // sequence chunks (chunk_len a multiple of 16 when several)
     ScanPlan fwd;           // the checkpoint pass: the specialised forward kernel, same chunks
-    size_t fwd_off = 0;     // the forward plan's workspace (its carries and packed B/C)
-    size_t ckpt_off = 0, partBC_off = 0, partA_off = 0, partD_off = 0, partDB_off = 0;
+    size_t partBC_off = 0, partA_off = 0, partD_off = 0, partDB_off = 0;
     size_t lcP_off = 0, lcH_off = 0;   // adjoint carries (several chunks only)
-    size_t ws_bytes = 0;
+    size_t fwd_off = 0;     // the forward plan's workspace (its carries and packed B/C)
+    size_t ckpt_off = 0;    // checkpoints [B][nblk][16][D] fp32
+    size_t ckpt_bytes = 0;
+    size_t ws_bytes = 0;        // with the checkpoint pass
+    size_t ws_bytes_saved = 0;  // given saved checkpoints (= fwd_off)
 };
 
 int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
@@ -81,8 +86,16 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const float *dh_last, const void *dx, const void *ddelta, const float *dA,
                    const void *dB, const void *dC, const float *dD, const void *dz, const float *dh0,
                    int delta_softplus, int discretization, const float *delta_bias,
-                   const float *ddelta_bias,
+                   const float *ddelta_bias, const float *checkpoints,
                    const void *workspace, size_t workspace_bytes, BwdPlan *plan);
+// Full argument check of ssm_scan_fwd_save: ssm_scan_fwd's on the backward's chunk plan,
+// plus the checkpoint output.  Fills *plan (the backward's) on success.
+int check_scan_save(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                    const void *x, const void *delta, const float *A, const void *B, const void *C,
+                    const float *Dskip, const void *z, const float *h0, const float *h_last,
+                    const void *y, int delta_softplus, const ssm_variant *variant,
+                    const float *checkpoints, const void *workspace, size_t workspace_bytes,
+                    BwdPlan *plan);
 
 // Argument checks of the convolution entry points.
 int check_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,

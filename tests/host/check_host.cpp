@@ -62,10 +62,10 @@ int main() {
         float *dA = static_cast<float *>(P(base + 16 * gap)), *dD = static_cast<float *>(P(base + 17 * gap));
         void *dz = P(base + 18 * gap), *dy = P(base + 19 * gap), *bws = P(base + 20 * gap);
         float *bias = static_cast<float *>(P(base + 21 * gap)), *dbias = static_cast<float *>(P(base + 22 * gap));
-        auto bw = [&](const float *bi, const float *dbi, int disc = SSM_DISC_MAMBA) {
+        auto bw = [&](const float *bi, const float *dbi, int disc = SSM_DISC_MAMBA, const float *ck = nullptr,
+                      size_t wsb = size_t(1) << 30) {
             return check_scan_bwd(2, 1000, 256, 16, SSM_DTYPE_BF16, x, dl, A, B, C, Dk, z, nullptr, dy, nullptr,
-                                  dx, ddl, dA, dB, dC, dD, dz, nullptr, 1, disc, bi, dbi, bws, size_t(1) << 30,
-                                  &bp);
+                                  dx, ddl, dA, dB, dC, dD, dz, nullptr, 1, disc, bi, dbi, ck, bws, wsb, &bp);
         };
         EXPECT(bw(nullptr, nullptr) == SSM_OK);
         EXPECT(bw(nullptr, nullptr, SSM_DISC_ZOH) == SSM_OK);
@@ -94,6 +94,42 @@ int main() {
         EXPECT(plan_scan_bwd(1, 1048576, 1024, 16, SSM_DTYPE_BF16, &bp) == SSM_OK);
         EXPECT(bp.n_chunks == 16 && bp.chunk_len == 65536 && bp.nblk == 131072);
         EXPECT(bp.fwd.ws_bytes > 0 && bp.ckpt_off >= bp.fwd.ws_bytes);
+        // saved checkpoints: the checkpoint pass's regions sit last, so the call given them
+        // needs only the part before them
+        EXPECT(bp.ws_bytes_saved == bp.fwd_off && bp.ckpt_off >= bp.fwd_off + bp.fwd.ws_bytes);
+        EXPECT(bp.ckpt_bytes == size_t(1) * 131072 * 16 * 1024 * 4 && bp.ws_bytes >= bp.ckpt_off + bp.ckpt_bytes);
+        float *ck = static_cast<float *>(P(base + 23 * gap));
+        EXPECT(plan_scan_bwd(2, 1000, 256, 16, SSM_DTYPE_BF16, &bp) == SSM_OK);
+        const size_t saved = bp.ws_bytes_saved, full = bp.ws_bytes;
+        EXPECT(saved < full && bp.ckpt_bytes == size_t(2) * 125 * 16 * 256 * 4);
+        EXPECT(bw(nullptr, nullptr, SSM_DISC_MAMBA, ck, saved) == SSM_OK);
+        EXPECT(bw(nullptr, nullptr, SSM_DISC_MAMBA, nullptr, saved) == SSM_EWORKSPACE);
+        EXPECT(bw(nullptr, nullptr, SSM_DISC_MAMBA, ck, saved - 1) == SSM_EWORKSPACE);
+        EXPECT(bw(nullptr, nullptr, SSM_DISC_MAMBA, static_cast<float *>(dx), full) == SSM_EINVAL);   // dx on it
+        EXPECT(std::strstr(ssm_last_error(), "overlaps") != nullptr);
+        EXPECT(bw(nullptr, nullptr, SSM_DISC_MAMBA, static_cast<float *>(P(base + 23 * gap + 8)), full) == SSM_EINVAL);
+        // the forward that stores them: the forward's checks on the backward's chunks
+        void *sy = P(base + 24 * gap);
+        auto sv = [&](int64_t Bn, int64_t Ln, int64_t Dn, int64_t Nn, float *c, void *yy, size_t wsb) {
+            return check_scan_save(Bn, Ln, Dn, Nn, SSM_DTYPE_BF16, x, dl, A, B, C, Dk, z, nullptr, nullptr, yy, 0,
+                                   nullptr, c, bws, wsb, &bp);
+        };
+        EXPECT(sv(2, 1000, 256, 16, ck, sy, size_t(1) << 30) == SSM_OK);
+        EXPECT(bp.n_chunks == 1 && bp.fwd.fast);
+        EXPECT(sv(2, 1000, 256, 16, nullptr, sy, size_t(1) << 30) == SSM_EINVAL);
+        EXPECT(sv(2, 1000, 256, 16, ck, sy, 0) == SSM_EWORKSPACE);            // packed B/C rows
+        EXPECT(sv(2, 1000, 256, 16, static_cast<float *>(sy), sy, size_t(1) << 30) == SSM_EINVAL);
+        EXPECT(sv(2, 1000, 256, 12, ck, sy, size_t(1) << 30) == SSM_EUNSUPPORTED);
+        EXPECT(sv(2, 1000, 96, 16, ck, sy, size_t(1) << 30) == SSM_EUNSUPPORTED);
+        EXPECT(sv(1, 5000, 128, 16, ck, sy, size_t(1) << 30) == SSM_OK);
+        EXPECT(bp.n_chunks == 3 && bp.fwd.chunk_len == 1680);
+        size_t wsz = 1, ckz = 1;
+        EXPECT(ssm_scan_save_sizes(1, 5000, 128, 16, SSM_DTYPE_BF16, &wsz, &ckz) == SSM_OK);
+        EXPECT(wsz == bp.fwd.ws_bytes && ckz == size_t(625) * 16 * 128 * 4);
+        EXPECT(ssm_scan_save_sizes(1, 5000, 96, 16, SSM_DTYPE_BF16, &wsz, &ckz) == SSM_EUNSUPPORTED && wsz == 0);
+        EXPECT(ssm_scan_save_sizes(1, 5000, 128, 16, SSM_DTYPE_BF16, nullptr, &ckz) == SSM_EINVAL);
+        EXPECT(ssm_scan_bwd_workspace_bytes(2, 1000, 256, 16, SSM_DTYPE_BF16, 1) == saved);
+        EXPECT(ssm_scan_bwd_workspace_bytes(2, 1000, 256, 16, SSM_DTYPE_BF16, 0) == full);
     }
     // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);
