@@ -86,6 +86,11 @@ template <typename V>
 __device__ __forceinline__ void st_at(void *base, uint32_t byte_off, V v) {
     *reinterpret_cast<V *>(static_cast<char *>(base) + byte_off) = v;
 }
+// non-temporal store (outputs written once and not read again by this launch)
+template <typename V>
+__device__ __forceinline__ void st_at_nt(void *base, uint32_t byte_off, V v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<V *>(static_cast<char *>(base) + byte_off));
+}
 
 // Read-only for the whole launch (written by the pre-pass launch): the constant
 // address space lets wave-uniform reads become scalar loads into SGPRs.
@@ -260,8 +265,11 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                     o[j] = yv;
                 }
                 const uint32_t off = off0 + static_cast<uint32_t>(q * D32) * ES;
-                if constexpr (sizeof(T) == 2) st_at<uint32_t>(yb, off, pack_bf16(o[0], o[1]));
-                else st_at<float2>(yb, off, make_float2(o[0], o[1]));
+                if constexpr (sizeof(T) == 2) st_at_nt<uint32_t>(yb, off, pack_bf16(o[0], o[1]));
+                else {
+                    typedef float f32x2 __attribute__((ext_vector_type(2)));
+                    st_at_nt<f32x2>(yb, off, f32x2{o[0], o[1]});
+                }
             }
         }
     };
@@ -306,9 +314,10 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 if ((sb * SUB) % 8 == 0) {   // state before step t, t a multiple of 8
                     const int64_t t = t0 + k * kTB + sb * SUB;
                     if (t < t1) {
+                        // non-temporal: read back only by the backward's reverse sweep, long after
 #pragma unroll
                         for (int g = 0; g < G; ++g)
-                            a.ckpt[((b * a.ck_nblk + t / 8) * kN + n0 + g) * D + d] = h[g];
+                            __builtin_nontemporal_store(h[g], &a.ckpt[((b * a.ck_nblk + t / 8) * kN + n0 + g) * D + d]);
                     }
                 }
             }
