@@ -38,8 +38,10 @@ struct Row<uint16_t, 4> {
         return (i & 1) ? bf_hi(v) : bf_lo(v);
     }
     __device__ static Row load(const uint16_t *p) { Row o; o.r = *reinterpret_cast<const uint2 *>(p); return o; }
+    // outputs are written once: non-temporal stores
     __device__ static void store(uint16_t *p, const float (&v)[4]) {
-        *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, reinterpret_cast<u32x2 *>(p));
     }
 };
 template <>
@@ -48,7 +50,8 @@ struct Row<float, 4> {
     __device__ float get(int i) const { return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w; }
     __device__ static Row load(const float *p) { Row o; o.r = *reinterpret_cast<const float4 *>(p); return o; }
     __device__ static void store(float *p, const float (&v)[4]) {
-        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
     }
 };
 template <typename T>

@@ -302,7 +302,9 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
                     }
                     o[i] = pack_bf16(v0, v1);
                 }
-                *reinterpret_cast<uint4 *>(Y + (t0 + 8 * w) * xs + zoff) = make_uint4(o[0], o[1], o[2], o[3]);
+                // y is written once: a non-temporal store
+                typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4 *>(Y + (t0 + 8 * w) * xs + zoff));
             }
             if (c + 1 < nch) load_z(c + 1);
             if (w < 2 && c + 1 < nch) tiles(c + 1, 8 + w, kTiles);   // tiles 8 and 9 of chunk c + 1
