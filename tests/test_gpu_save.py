@@ -86,7 +86,8 @@ def test_save_forward_equals_plain_forward_single_chunk(ssm):
 def test_backward_from_saved_checkpoints_is_identical(ssm, Bsz, L, D, dt, disc):
     """The backward given the saved checkpoints skips its own forward sweep; every
     gradient is bit-identical to the call that recomputes them (the same kernel
-    arithmetic on the same chunks), and dx against the oracle."""
+    arithmetic on the same chunks; that call's parity with the oracle is tested in
+    test_gpu_bwd)."""
     import torch
     inp = _inputs(Bsz, L, D, dt, seed=3 * L + D, disc=disc)
     t = device_inputs(inp)
@@ -120,3 +121,36 @@ def test_save_rejects_unsupported_and_empty(ssm):
                                   torch.zeros((2, 0, 16), device="cuda"), None, None, h0, return_last_state=True)
     torch.cuda.synchronize()
     assert y.numel() == 0 and ck.numel() == 0 and torch.equal(hl, h0)
+
+
+@pytest.mark.timeout(600)
+def test_training_step_headline_shape(ssm):
+    """The B4 L4096 D4096 N16 bf16 gated layer in the launches the bench times: the saving
+    forward's y is bit-identical to scan_fwd's, the backward from its checkpoints is
+    bit-identical to the recomputing backward, and sampled checkpoints match the oracle's
+    prefix states."""
+    import torch
+    c = synth.CONFIGS[2]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    inp = synth.config_inputs(2)
+    t = device_inputs(inp)
+    gy = to_dev(synth.store(np.random.default_rng(2026).standard_normal((Bsz, L, D), dtype=np.float32), "bf16"),
+                "bf16")
+    y, ck = ssm.scan_fwd_save(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    y2 = ssm.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    g0 = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, gy, need_dh0=False)
+    g1 = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, gy, need_dh0=False,
+                      checkpoints=ck)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    for k in g0:
+        if g0[k] is not None:
+            assert torch.equal(g0[k], g1[k]), k
+    # checkpoint 100 (the state before step 800) of a few channels against the oracle
+    ch = [(0, 0), (1, 777), (3, 4095), (2, 2048)]
+    sub = dict(inp)
+    for key in ("x", "delta", "z", "B", "C"):
+        sub[key] = np.ascontiguousarray(inp[key][:, :800])
+    _, rh = oracle.scan(sub, channels=ch)                  # [4, N]
+    got = np.stack([to_host(ck[b, 100, :, d]) for b, d in ch])
+    assert compare(got, rh, "f32", "checkpoint 100")["bad"] == 0
