@@ -90,13 +90,13 @@ __device__ __forceinline__ float zoh_psi(float u, float a) {
 
 template <typename T, bool HAS_Z, int DISC>
 __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
-    // per wave, step, lane: partial sums over the wave's states: lam da/ddt h_prev, lam f B,
-    // C h, and for the zero-order hold and bilinear maps lam df/ddt B (equal to lam f B /
-    // dt in Mamba's)
-    constexpr int NS = DISC == kMamba ? 3 : 4;
+    // per wave, step, lane: partial sums over the wave's states, one 16-byte entry (one LDS
+    // instruction each way): (lam da/ddt h_prev, lam f B, C h, and for the zero-order hold
+    // and bilinear maps lam df/ddt B; equal to lam f B / dt in Mamba's, which leaves it 0)
+    constexpr bool S2U = DISC != kMamba;
     // double-buffered by block parity, so that a block's writes never meet the previous
     // block's reads and two barriers per block suffice
-    __shared__ float sS[2][kW][kTB][NS][64];
+    __shared__ float4 sS[2][kW][kTB][64];
     // per step, lane: (dt, dt x, dy silu(z), x) of the block, written by the step's wave
     __shared__ float4 sP[2][kTB][64];
     // the block's B_t, C_t: [step][state][B, C]
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         sP[pb][w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, xv_w);
         __syncthreads();
         // us: dt x (Mamba) or x; fs: f (zero-order hold) or r (bilinear)
-        float hs[kTB][kG], as[kTB][kG], fs[kTB][kG], dts[kTB], us[kTB], g0s[kTB], h_in[kG];
+        float hs[kTB][kG], as[kTB][kG], fs[kTB][kG], dts[kTB], us[kTB], g0s[kTB], y0s[kTB], h_in[kG];
         h[0] = ckn.x;
         h[1] = ckn.y;
         h_in[0] = h[0];
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                     }
                 }
                 y0p = __builtin_fmaf(bc.y, h[0], bc.w * h[1]);
-                sS[pb][w][i][2][lane] = y0p;
+                y0s[i] = y0p;
             }
         }
         if (k > kb0) load2(k - 1);
@@ -293,9 +293,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                     }
                     lam[g] *= as[i][g];
                 }
-                sS[pb][w][i][0][lane] = S1;
-                sS[pb][w][i][1][lane] = S3;
-                if constexpr (NS == 4) sS[pb][w][i][3][lane] = S2;
+                sS[pb][w][i][lane] = make_float4(S1, S3, y0s[i], S2);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) tv[i * 4 + q] = 0.0f;
@@ -342,10 +340,11 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, y0 = 0.0f;
 #pragma unroll
                 for (int ww = 0; ww < kW; ++ww) {
-                    S1 += sS[pb][ww][i][0][lane];
-                    S3 += sS[pb][ww][i][1][lane];
-                    y0 += sS[pb][ww][i][2][lane];
-                    if constexpr (NS == 4) S2 += sS[pb][ww][i][3][lane];
+                    const float4 v = sS[pb][ww][i][lane];
+                    S1 += v.x;
+                    S3 += v.y;
+                    y0 += v.z;
+                    if constexpr (S2U) S2 += v.w;
                 }
                 const float dt = dt_w, xv = xv_w, gy = gy_w, zv = zv_w, raw = raw_w;
                 y0 = __builtin_fmaf(dsk, xv, y0);
