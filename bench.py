@@ -147,7 +147,7 @@ def main():
         log(f"decode profile run: {args.profile_decode} steps")
         return
     if args.profile_bwd:
-        c = synth.CONFIGS[2]
+        c = synth.CONFIGS["mamba1p4b_layer"]
         gen = torch.Generator(device=dev)
         gen.manual_seed(4)
         bf = torch.bfloat16
@@ -179,12 +179,12 @@ def main():
         return
 
     result = {}
-    cfg = synth.CONFIGS[2]
+    cfg = synth.CONFIGS["mamba1p4b_layer"]
     B, L, D, N = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
     updates = B * L * D * N
     if not args.secondary_only:
         t0 = time.time()
-        inp = synth.config_inputs(2)
+        inp = synth.config_inputs("mamba1p4b_layer")
         log(f"generated {cfg['name']} inputs in {time.time() - t0:.1f}s")
 
         def up(a):
@@ -349,7 +349,7 @@ def _delta(shape, gen, dev, dtype):
 
 def _conv_inputs(torch, synth, dev):
     """Headline-shape input of the convolution: x [4, 4096, 4096] bf16, width-4 filter."""
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["mamba1p4b_layer"]
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
     x = _randn((c["batch"], c["seqlen"], c["dim"]), gen, dev, torch.bfloat16)
@@ -393,7 +393,7 @@ def ssd_alg(c, Q=64):
 
 def profile_decode(torch, ssm, synth, dev, steps):
     """A few decode steps on the decode workload's state (h [256, 4096, 16] fp32)."""
-    c = synth.CONFIGS[4]
+    c = synth.CONFIGS["decode"]
     Bsz, D, N = c["batch"], c["dim"], c["dstate"]
     gen = torch.Generator(device=dev)
     gen.manual_seed(4)
@@ -418,7 +418,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     gen.manual_seed(4)
     bf = torch.bfloat16
     # --- decode: h[256, 4096, 16] fp32, 1024 gated steps from zero ---
-    c = synth.CONFIGS[4]
+    c = synth.CONFIGS["decode"]
     Bsz, D, N, S = c["batch"], c["dim"], c["dstate"], c["seqlen"]
     A = torch.from_numpy(synth.make_A(4, D, N)).to(dev)
     Dk = torch.from_numpy(synth.make_D(4, D, "normal")).to(dev)
@@ -505,7 +505,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     del xs, ds, zs, Bs, Cs, h
     torch.cuda.empty_cache()
     # --- the other discretisations at the headline shape ---
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["mamba1p4b_layer"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
     x, dl, z = (_randn((Bsz, L, D), gen, dev, bf) if k != "dl" else _delta((Bsz, L, D), gen, dev, bf)
                 for k in ("x", "dl", "z"))
@@ -668,7 +668,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
                      "elements/s", f"every 8th channel ({len(dsel)}) x 4 x 4096 steps, fp64 numpy oracle (one thread)", 1))
     del x, yc, gyc, cws
     # --- backward pass at the headline shape ---
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["mamba1p4b_layer"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
     x, dl, z, gy = (_randn((Bsz, L, D), gen, dev, bf) if k != "dl" else _delta((Bsz, L, D), gen, dev, bf)
                     for k in ("x", "dl", "z", "gy"))
@@ -786,7 +786,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     del x, dl, z, gy, Bm, Cm, ws
     torch.cuda.empty_cache()
     # --- million-token scan (chunk carries) ---
-    c = synth.CONFIGS[3]
+    c = synth.CONFIGS["million_token"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
     x = _randn((Bsz, L, D), gen, dev, bf)
     dl = _delta((Bsz, L, D), gen, dev, bf)

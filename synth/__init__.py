@@ -210,24 +210,25 @@ def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, 
 
 # The five workloads: (name, batch, seqlen, dim, dstate, dtype, gate, d_kind)
 CONFIGS = {
-    0: dict(name="tiny scan B1 L256 D64 N16 fp32", batch=1, seqlen=256, dim=64, dstate=16,
+    "tiny_f32": dict(seed=0, name="tiny scan B1 L256 D64 N16 fp32", batch=1, seqlen=256, dim=64, dstate=16,
             dtype="f32", gate=False, d_kind="ones"),
-    1: dict(name="Mamba-130M-layer scan B8 L2048 D1536 N16 bf16 gated", batch=8, seqlen=2048,
+    "mamba130m_layer": dict(seed=1, name="Mamba-130M-layer scan B8 L2048 D1536 N16 bf16 gated", batch=8, seqlen=2048,
             dim=1536, dstate=16, dtype="bf16", gate=True, d_kind="ones"),
-    2: dict(name="Mamba-1.4B-layer scan B4 L4096 D4096 N16 bf16 gated", batch=4, seqlen=4096,
+    "mamba1p4b_layer": dict(seed=2, name="Mamba-1.4B-layer scan B4 L4096 D4096 N16 bf16 gated", batch=4, seqlen=4096,
             dim=4096, dstate=16, dtype="bf16", gate=True, d_kind="normal"),
-    3: dict(name="million-token scan B1 L1048576 D1024 N16 bf16", batch=1, seqlen=1 << 20,
+    "million_token": dict(seed=3, name="million-token scan B1 L1048576 D1024 N16 bf16", batch=1, seqlen=1 << 20,
             dim=1024, dstate=16, dtype="bf16", gate=False, d_kind="normal"),
-    4: dict(name="decode state update h[256,4096,16] x 1024 steps bf16 gated", batch=256,
+    "decode": dict(seed=4, name="decode state update h[256,4096,16] x 1024 steps bf16 gated", batch=256,
             seqlen=1024, dim=4096, dstate=16, dtype="bf16", gate=True, d_kind="normal"),
 }
 
 
-def config_inputs(k: int, seed: int | None = None, **overrides) -> dict:
-    c = dict(CONFIGS[k])
+def config_inputs(name: str, seed: int | None = None, **overrides) -> dict:
+    """Inputs of the named workload (its own seed unless ``seed`` is given)."""
+    c = dict(CONFIGS[name])
     c.update(overrides)
     return scan_inputs(c["batch"], c["seqlen"], c["dim"], c["dstate"], c["dtype"],
-                       k if seed is None else seed, gate=c["gate"], d_kind=c["d_kind"],
+                       c["seed"] if seed is None else seed, gate=c["gate"], d_kind=c["d_kind"],
                        a_kind=c.get("a_kind", "mamba"), softplus_input=c.get("softplus_input", False),
                        h0=c.get("h0", False))
 

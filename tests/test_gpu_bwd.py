@@ -157,9 +157,9 @@ def test_backward_headline_shape_full(ssm):
     runs over 1024-channel batches; dB, dC (sums over channels), dA, dD (sums over rows)
     are accumulated over the batches."""
     import torch
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["mamba1p4b_layer"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
-    inp = synth.config_inputs(2)
+    inp = synth.config_inputs("mamba1p4b_layer")
     gy = synth.store(np.random.default_rng(2024).standard_normal((Bsz, L, D), dtype=np.float32), "bf16")
     t = device_inputs(inp)
     g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, to_dev(gy, "bf16"),
@@ -225,9 +225,9 @@ def test_backward_long_sequence_sampled(ssm):
     finite, and dx, ddelta, dA, dD of sampled channels against the fp64 oracle (with one
     batch row, the oracle's per-channel dA, dD are the whole sums)."""
     import torch
-    c = synth.CONFIGS[3]
+    c = synth.CONFIGS["million_token"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
-    inp = synth.config_inputs(3)
+    inp = synth.config_inputs("million_token")
     rng = np.random.default_rng(3003)
     gy = np.empty((Bsz, L, D), dtype=np.uint16)
     for r0 in range(0, L, 65536):
@@ -356,9 +356,9 @@ def test_backward_variant_headline_shape_sampled(ssm, disc):
     finite; dx, ddelta, dz of every row of 6 sampled dims, and dA, dD of those dims (sums
     over the 4 rows), against the fp64 oracle."""
     import torch
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["mamba1p4b_layer"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
-    inp = synth.config_inputs(2)
+    inp = synth.config_inputs("mamba1p4b_layer")
     inp["discretization"] = disc
     gy = synth.store(np.random.default_rng(2025).standard_normal((Bsz, L, D), dtype=np.float32), "bf16")
     t = device_inputs(inp)

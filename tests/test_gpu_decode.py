@@ -69,11 +69,11 @@ def test_scan_equals_steps(ssm):
 
 
 @pytest.mark.timeout(1200)
-def test_parity_config4_decode_1024_steps(ssm):
+def test_parity_decode_1024_steps(ssm):
     """h [256, 4096, 16] fp32 from zero, 1024 gated bf16 steps; every step's y on sampled
     channels, and the final state on those channels."""
     import torch
-    c = synth.CONFIGS[4]
+    c = synth.CONFIGS["decode"]
     Bsz, D, N, steps = c["batch"], c["dim"], c["dstate"], c["seqlen"]
     A = synth.make_A(4, D, N)
     Dk = synth.make_D(4, D, "normal")

@@ -130,9 +130,9 @@ def test_training_step_headline_shape(ssm):
     bit-identical to the recomputing backward, and sampled checkpoints match the oracle's
     prefix states."""
     import torch
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["mamba1p4b_layer"]
     Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
-    inp = synth.config_inputs(2)
+    inp = synth.config_inputs("mamba1p4b_layer")
     t = device_inputs(inp)
     gy = to_dev(synth.store(np.random.default_rng(2026).standard_normal((Bsz, L, D), dtype=np.float32), "bf16"),
                 "bf16")

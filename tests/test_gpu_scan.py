@@ -227,7 +227,7 @@ def _config_parity(ssm, k, sample=None, seed=None, **kw):
     import torch
     c = synth.CONFIGS[k]
     inp = synth.config_inputs(k, seed=seed)
-    print(f"[parity] config {k} ({c['name']}) seed={seed if seed is not None else k} generated", flush=True)
+    print(f"[parity] {k} ({c['name']}) seed={seed if seed is not None else c['seed']} generated", flush=True)
     dt = c["dtype"]
     if sample is None:
         y, h = _run(ssm, inp, **kw)
@@ -246,31 +246,31 @@ def _config_parity(ssm, k, sample=None, seed=None, **kw):
         yr, hr = oracle.scan(inp, channels=ch)
         st = assert_close(yg, yr, dt)
         assert_close(hg, hr, "f32", "h_last")
-    _log(f"config {k}", st)
+    _log(f"workload {k}", st)
     return st
 
 
-def test_parity_config0(ssm):
-    _config_parity(ssm, 0)
-    _config_parity(ssm, 0, seed=100)
+def test_parity_tiny_f32(ssm):
+    _config_parity(ssm, "tiny_f32")
+    _config_parity(ssm, "tiny_f32", seed=100)
 
 
 @pytest.mark.timeout(900)
-def test_parity_config1(ssm):
-    _config_parity(ssm, 1)
+def test_parity_mamba130m_layer(ssm):
+    _config_parity(ssm, "mamba130m_layer")
 
 
 @pytest.mark.timeout(900)
-def test_parity_config2(ssm):
-    _config_parity(ssm, 2)
+def test_parity_mamba1p4b_layer(ssm):
+    _config_parity(ssm, "mamba1p4b_layer")
 
 
 @pytest.mark.timeout(900)
-def test_parity_config3(ssm):
+def test_parity_million_token(ssm):
     """Million-token scan: sampled channels over the whole length (chunk carries path)."""
     plan = ssm.scan_plan(1, 1 << 20, 1024, 16, "bf16")
     assert plan["n_chunks"] > 1
-    _config_parity(ssm, 3, sample=48)
+    _config_parity(ssm, "million_token", sample=48)
 
 
 @pytest.mark.parametrize("D,N,dt", [(128, 16, "bf16"), (70, 5, "f32")])

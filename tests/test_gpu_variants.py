@@ -109,8 +109,8 @@ def test_variant_headline_shape_sampled(ssm, disc):
     """The B4 L4096 D4096 N16 bf16 gated layer with each variant: sampled channels over the
     whole length against the oracle."""
     import torch
-    c = synth.CONFIGS[2]
-    inp = synth.config_inputs(2)
+    c = synth.CONFIGS["mamba1p4b_layer"]
+    inp = synth.config_inputs("mamba1p4b_layer")
     inp["discretization"] = disc
     inp["delta_bias"] = None
     yd, hd = _run_dev(ssm, inp)
