@@ -326,7 +326,8 @@ def scan_fwd_save(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=
     if checkpoints is None:
         checkpoints = torch.empty((Bsz, nck, N, Dm), dtype=torch.float32, device=dev)
     _need(checkpoints, "checkpoints", (Bsz, nck, N, Dm), torch.float32, dev)
-    assert checkpoints.numel() * 4 == ck_bytes
+    if not checkpoints.is_contiguous() or checkpoints.numel() * 4 != ck_bytes:
+        raise ValueError(f"checkpoints must be a contiguous fp32 tensor of {ck_bytes} bytes")
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
