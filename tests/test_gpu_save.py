@@ -20,8 +20,8 @@ def ssm():
     return m
 
 
-def _inputs(Bsz, L, D, dt, seed, disc="mamba", bias=True, h0=True):
-    inp = synth.scan_inputs(Bsz, L, D, 16, dt, seed=seed, gate=True, d_kind="normal", a_kind="random",
+def _inputs(Bsz, L, D, dt, seed, disc="mamba", bias=True, h0=True, gate=True):
+    inp = synth.scan_inputs(Bsz, L, D, 16, dt, seed=seed, gate=gate, d_kind="normal", a_kind="random",
                             softplus_input=True, h0=h0)
     if bias:
         inp["delta_bias"] = synth.make_delta_bias(seed, D)
@@ -154,3 +154,30 @@ def test_training_step_headline_shape(ssm):
     _, rh = oracle.scan(sub, channels=ch)                  # [4, N]
     got = np.stack([to_host(ck[b, 100, :, d]) for b, d in ch])
     assert compare(got, rh, "f32", "checkpoint 100")["bad"] == 0
+
+
+@pytest.mark.parametrize("Bsz,L,D,dt,disc", [(2, 3000, 64, "f32", "mamba"), (2, 77, 128, "bf16", "zoh")])
+def test_save_without_gate_h0_or_bias(ssm, Bsz, L, D, dt, disc):
+    """No gate, no h0, no delta bias (chunked in the first case): y, h_last and the last
+    checkpoint against the oracle; the backward from the checkpoints bit-identical to the
+    recomputing one."""
+    import torch
+    inp = _inputs(Bsz, L, D, dt, seed=11 * L + D, disc=disc, bias=False, h0=False, gate=False)
+    t = device_inputs(inp)
+    y, hl, ck, _ = _save(ssm, inp, t)
+    ry, rh = oracle.scan(inp)
+    assert compare(to_host(y), ry, dt)["bad"] == 0
+    assert compare(to_host(hl), rh, "f32", "h_last")["bad"] == 0
+    k = ck.shape[1] - 1
+    sub = dict(inp)
+    for key in ("x", "delta", "B", "C"):
+        sub[key] = np.ascontiguousarray(inp[key][:, :8 * k])
+    assert compare(to_host(ck[:, k]).transpose(0, 2, 1), oracle.scan(sub)[1], "f32", "last checkpoint")["bad"] == 0
+    gy = to_dev(synth.store(np.random.default_rng(L).standard_normal((Bsz, L, D)).astype(np.float32), dt), dt)
+    kw = dict(delta_softplus=True, discretization=disc)
+    g0 = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], None, None, gy, **kw)
+    g1 = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], None, None, gy, checkpoints=ck, **kw)
+    torch.cuda.synchronize()
+    for key in g0:
+        if g0[key] is not None:
+            assert torch.equal(g0[key], g1[key]), key
