@@ -75,17 +75,16 @@ __device__ __forceinline__ float sigmoid_f(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
-// psi(u) = (u e^u - e^u + 1) / u^2, the derivative of (e^u - 1)/u, given a = e^u: its
-// Taylor series through u^6 where |u| < 1/2 (the closed form cancels there; the
-// series' truncation, u^7 / 45360, is below 2e-7 of psi at the switch), else the closed
-// form with 1 - a formed exactly.
-__device__ __forceinline__ float zoh_psi(float u, float a) {
-    const float ser = __builtin_fmaf(
+// psi(u) = (u e^u - e^u + 1) / u^2, the derivative of (e^u - 1)/u, by its Taylor
+// series through u^6, used where |u| < 1/2: there the closed form cancels, and the
+// series' truncation, u^7 / 45360, is below 2e-7 of psi at the switch.  Beyond it the
+// zero-order hold's df/dA = dt^2 psi(u) is formed as (dt a - f) / A (f = (a - 1) / A),
+// one fma and one multiply by the stored 1/A.
+__device__ __forceinline__ float zoh_psi_series(float u) {
+    return __builtin_fmaf(
         __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(__builtin_fmaf(__builtin_fmaf(
             1.0f / 5760.0f, u, 1.0f / 840.0f), u, 1.0f / 144.0f), u, 1.0f / 30.0f), u, 0.125f), u,
             1.0f / 3.0f), u, 0.5f);
-    const float dir = __builtin_fmaf(u, a, 1.0f - a) * __builtin_amdgcn_rcpf(u * u);
-    return __builtin_fabsf(u) < 0.5f ? ser : dir;
 }
 
 template <typename T, bool HAS_Z, int DISC>
@@ -275,7 +274,11 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                             da_dt = Av[g] * ab;
                             df_dt = ab;
                             da_dA = dt * ab;
-                            df_dA = dt * dt * zoh_psi(dt * Av[g], ab);
+                            // dt^2 psi(u): the series near u = 0 (and at A = 0), else
+                            // (dt a - f) / A, which is the same quantity since f = (a - 1) / A
+                            const float u = dt * Av[g];
+                            df_dA = __builtin_fabsf(u) < 0.5f ? dt * dt * zoh_psi_series(u)
+                                                               : __builtin_fmaf(dt, ab, -fs[i][g]) * aux[g];
                         } else {
                             const float r = fs[i][g], r2 = r * r;
                             f = r * dt;
