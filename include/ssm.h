@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 #define SSM_MAX_DSTATE 16
 
 typedef enum ssm_dtype {
@@ -104,7 +104,12 @@ typedef struct ssm_scan_opts {
     int32_t time_block;    /* time steps staged per block: 8, 16 or 32 (the generic kernel of
                               the ZOH and bilinear variants always stages 8) */
     int32_t one_block_per_cu; /* 0: automatic; 1: reserve LDS so each CU runs one workgroup; -1: never */
-    int32_t reserved;      /* must be 0 */
+    int32_t a_structure;   /* 0: automatic -- with the Mamba discretisation and dstate 16, a
+                              workgroup whose channels all satisfy A[d, n + k] - A[d, n] =
+                              A[d, k] - A[d, 0] (k = 16 / states_per_lane; e.g. A[d,n] = -(n+1))
+                              forms exp(dt A[d, n + k]) as exp(dt A[d, n]) * exp(dt (A[d,k] -
+                              A[d,0])): one exp per lane and step instead of one per state.  The
+                              check runs on the device.  -1: always one exp per state. */
 } ssm_scan_opts;
 
 /* What ssm_scan_fwd will launch for a given shape (host-only query). */

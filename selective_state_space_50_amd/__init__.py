@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 4     # SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 5     # SSM_ABI_VERSION of include/ssm.h
 
 
 class SSMError(RuntimeError):
@@ -36,7 +36,7 @@ class SSMError(RuntimeError):
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("states_per_lane", ctypes.c_int32),
                 ("time_block", ctypes.c_int32), ("one_block_per_cu", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("a_structure", ctypes.c_int32)]
 
 
 class Variant(ctypes.Structure):
@@ -66,6 +66,12 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libssm.so not found at {LIB_PATH}: build it first "
                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    # torch first: its HIP runtime is then the one libssm.so binds to (a process must not
+    # load a second copy of the runtime, which would see no devices)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     I64, I32, P, SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     L.ssm_abi_version.restype = I32
@@ -129,10 +135,11 @@ def exported_api():
     return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
 
 
-def _opts(chunk_len=0, states_per_lane=0, time_block=0, one_block_per_cu=0):
-    if not (chunk_len or states_per_lane or time_block or one_block_per_cu):
+def _opts(chunk_len=0, states_per_lane=0, time_block=0, one_block_per_cu=0, general_a=False):
+    if not (chunk_len or states_per_lane or time_block or one_block_per_cu or general_a):
         return None
-    return ScanOpts(int(chunk_len), int(states_per_lane), int(time_block), int(one_block_per_cu), 0)
+    return ScanOpts(int(chunk_len), int(states_per_lane), int(time_block), int(one_block_per_cu),
+                    -1 if general_a else 0)
 
 
 def _variant(discretization, delta_bias, dim, device):
@@ -195,13 +202,14 @@ def _need(t, name, shape, dtype, device):
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
              discretization="mamba", delta_bias=None,
              return_last_state=False, out=None, h_last=None, workspace=None, chunk_len=0,
-             states_per_lane=0, time_block=0, one_block_per_cu=0, stream=None):
+             states_per_lane=0, time_block=0, one_block_per_cu=0, general_a=False, stream=None):
     """Selective scan y = S6(x, delta, A, B, C, D) [* silu(z)] on the GPU.
 
     x, delta, z: [B, L, D];  B, C: [B, L, N];  A: [D, N] fp32;  D: [D] fp32;
     h0: [B, D, N] fp32.  x/delta/z/B/C share one dtype (bfloat16 or float32).
     discretization: "mamba" (A_bar = exp(dt A), B_bar = dt B), "zoh" or "bilinear";
     delta_bias: [D] fp32 added to delta before the softplus.
+    general_a: always one exp per state (never the structured-A path, ssm_scan_opts.a_structure).
     Returns y (same dtype as x), or (y, h_last) when return_last_state.
     """
     import torch
@@ -228,7 +236,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False
     if return_last_state and h_last is None:
         h_last = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
     _need(h_last, "h_last", (Bsz, Dm, N), torch.float32, dev)
-    o = _opts(chunk_len, states_per_lane, time_block, one_block_per_cu)
+    o = _opts(chunk_len, states_per_lane, time_block, one_block_per_cu, general_a)
     ws_bytes = int(lib().ssm_scan_workspace_bytes(Bsz, L, Dm, N, code, ctypes.byref(o) if o else None))
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

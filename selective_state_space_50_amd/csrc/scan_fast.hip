@@ -9,16 +9,22 @@ namespace {
 
 }  // namespace
 
-hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s) {
+hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, int disc, bool bf16, hipStream_t s) {
     const int64_t total = a.B * a.n_chunks * a.bc_lpad * kN;
     const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+    // the Mamba kernels map lane slot g of compute wave w to state w + g * (16 / G)
+    const bool strided = disc == kMamba;
+#define SSM_PACK(T, G)                                                                                  \
+    if (strided) hipLaunchKernelGGL((bc_pack_kernel<T, G, true>), grid, dim3(256), 0, s, a);           \
+    else hipLaunchKernelGGL((bc_pack_kernel<T, G, false>), grid, dim3(256), 0, s, a);
     if (bf16) {
-        if (p.G == 2) hipLaunchKernelGGL((bc_pack_kernel<uint16_t, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((bc_pack_kernel<uint16_t, 4>), grid, dim3(256), 0, s, a);
+        if (p.G == 2) { SSM_PACK(uint16_t, 2) }
+        else { SSM_PACK(uint16_t, 4) }
     } else {
-        if (p.G == 2) hipLaunchKernelGGL((bc_pack_kernel<float, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((bc_pack_kernel<float, 4>), grid, dim3(256), 0, s, a);
+        if (p.G == 2) { SSM_PACK(float, 2) }
+        else { SSM_PACK(float, 4) }
     }
+#undef SSM_PACK
     return hipGetLastError();
 }
 

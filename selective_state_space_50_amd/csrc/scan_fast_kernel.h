@@ -37,10 +37,10 @@ constexpr int kN = 16;
 // Time steps per block.  (32 steps for the G = 2 kernel would fill the LDS exactly but
 // measured no faster: the barriers are not what limits the kernel.)
 constexpr int kTB = 16;
-// Helper register sets: the loads of block k are issued kRS - 1 blocks before block k is
-// staged (fewer sets for fp32 inputs, whose raw rows take twice the registers).
+// Helper register sets: a ring of four, block k in set k % 4, so the loads of block k are
+// issued three blocks before block k is staged.
 template <typename T>
-constexpr int reg_sets() { return sizeof(T) == 2 ? 4 : 2; }
+constexpr int reg_sets() { return 4; }
 // Helper waves: one per SIMD.  A helper thread owns two rows (a step pair) and two
 // adjacent channels of every block.
 template <int G>
@@ -68,35 +68,34 @@ struct Vec<uint16_t, 2> {
     uint32_t r;
     __device__ void zero() { r = 0; }
     __device__ float get(int i) const { return i == 0 ? bf_lo(r) : bf_hi(r); }
+    __device__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+        r = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(off), 0, 0);
+    }
 };
 template <>
 struct Vec<float, 2> {
-    float2 r;
-    __device__ void zero() { r = make_float2(0.f, 0.f); }
-    __device__ float get(int i) const { return i == 0 ? r.x : r.y; }
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 r;
+    __device__ void zero() { r = u32x2{0u, 0u}; }
+    __device__ float get(int i) const { return __uint_as_float(i == 0 ? r.x : r.y); }
+    __device__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+        r = __builtin_amdgcn_raw_buffer_load_b64(rs, static_cast<int>(off), 0, 0);
+    }
 };
 
-// Loads/stores at a wave-uniform base plus a 32-bit unsigned byte offset, so the
-// address is formed by the memory unit (SGPR base + VGPR offset), not by VALU.
-template <typename V>
-__device__ __forceinline__ V ld_at(const void *base, uint32_t byte_off) {
-    return *reinterpret_cast<const V *>(static_cast<const char *>(base) + byte_off);
-}
-template <typename V>
-__device__ __forceinline__ void st_at(void *base, uint32_t byte_off, V v) {
-    *reinterpret_cast<V *>(static_cast<char *>(base) + byte_off) = v;
-}
-// non-temporal store (outputs written once and not read again by this launch)
-template <typename V>
-__device__ __forceinline__ void st_at_nt(void *base, uint32_t byte_off, V v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<V *>(static_cast<char *>(base) + byte_off));
+// Buffer resource over [base, base + bytes): loads past the end return zeros and stores past
+// it are dropped, so the rows of a block beyond its chunk need neither address clamps nor
+// per-row branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
 // Read-only for the whole launch (written by the pre-pass launch): the constant
 // address space lets wave-uniform reads become scalar loads into SGPRs.
 typedef const float __attribute__((address_space(4))) cfloat;
 
-// Pre-pass: the B and C values of token t = c*chunk_len + tl, state n = w*G + g, go to
+// Pre-pass: the B and C values of token t = c*chunk_len + tl, state n of compute wave w and
+// lane slot g (n = w*G + g, or n = w + g*NC with STRIDED), go to
 //   ws_BC[b][c][tl / 16][w][(tl % 16) / SUB][B or C][tl % SUB][g],   SUB = 8 / G,
 // fp32, zero past the chunk (or the sequence) so the last block of a chunk reads zeros.
 // A compute wave's sub-block of SUB steps is one 64-byte line: SUB*G values of B, then
@@ -104,7 +103,7 @@ typedef const float __attribute__((address_space(4))) cfloat;
 // The lines of the NC compute waves are interleaved per block: those that the waves of a
 // workgroup read at the same time are adjacent instead of one chunk apart (a stride that
 // maps them all to the same sets of the scalar cache).
-template <typename T, int G>
+template <typename T, int G, bool STRIDED>
 __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b, c, tl, n)
     const int64_t lp = a.bc_lpad;
@@ -121,7 +120,7 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
         cv = widen(static_cast<const T *>(a.Cm), (b * a.L + t) * kN + n);
     }
     constexpr int SUB = 8 / G;
-    const int w = n / G, g = n % G;
+    const int w = STRIDED ? n % (kN / G) : n / G, g = STRIDED ? n / (kN / G) : n % G;
     const int tb = static_cast<int>(tl % kTB);
     const int64_t blk = (b * a.n_chunks + c) * (lp / kTB) + tl / kTB;
     float *o = a.ws_BC + ((blk * (kN / G) + w) * (kTB / SUB) + tb / SUB) * (2 * SUB * G) + (tb % SUB) * G + g;
@@ -133,8 +132,20 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
 // or with CKPT the state at the start of every 8-step group instead (checkpoints for the
 // backward).  CKPT without CARRY: the ordinary forward (y, h_last) that also stores those
 // checkpoints.  DISC: the discretisation (kMamba, kZOH, kBilinear).
+//
+// Structured A (the Mamba discretisation).  Exp(dt A[d,n]) is the one transcendental of a
+// state update.  The Mamba kernels give compute wave w the states n = w + g*NC (g < G) of
+// its lane's channel.  When A[d, n + NC] - A[d, n] is one constant c_d for every n of the
+// channel -- true of the usual initialisation A[d,n] = -(n+1) (skill page "State Space
+// Models Mamba", MambaBlock: A_log = log(1..N)) -- the decays of a lane's states satisfy
+// exp(dt A[n + NC]) = exp(dt A[n]) exp(dt c_d).  The helpers then stage E = exp(dt c_d)
+// once per (t, d) next to (dt, dt x), and a lane takes one exp per step plus G - 1
+// multiplies instead of G exps.  Each workgroup checks the structure of its 64 channels on
+// the device at its start (no host synchronisation); a workgroup whose A lacks it, or a
+// call that asks for the general path (ScanArgs::structured == 0), takes the general path.
 template <int DISC, typename T, int G, bool HAS_Z, bool CARRY, bool CKPT = false>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
+    constexpr bool ST = DISC == kMamba;   // structured-A capable, strided state mapping
     constexpr int NC = kN / G;          // compute waves
     constexpr int RPT = 2;              // rows per helper thread
     static_assert(kTB / RPT * 32 == helper_waves<G>() * 64, "helpers cover the block in row pairs x channel pairs");
@@ -144,13 +155,18 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     //   sY  [P][w][i/2][lane] float2 = (share of y_i, share of y_i+1)
     // one object, staging first: every staging address stays below 64 KiB, in reach of
     // the 16-bit immediate offset of the LDS instructions
+    // Staging slots are a ring of four (block j in slot j % 4): the helpers stage two blocks
+    // ahead, so the compute waves can request the first operands of block j + 1 while they
+    // still scan block j.  y shares are double-buffered by block parity.
     struct Smem {
-        float4 du[2][kTB / 2 * 64];
+        float4 du[4][kTB / 2 * 64];
+        float2 e[4][ST ? kTB / 2 * 64 : 1];   // structured A: (E_i, E_i+1)
         float2 y[2][CARRY ? 1 : NC * kTB / 2 * 64];
     };
     __shared__ Smem smem;
     auto &sDU = smem.du;
     auto &sY = smem.y;
+    auto &sE = smem.e;
     constexpr int kRS = reg_sets<T>();
 
     const int tid = threadIdx.x;
@@ -169,7 +185,9 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     // ---- compute-wave state: G states of channel d0 + lane, A scaled by log2(e), the
     // discretisation's second per-state constant, and (bilinear carries) the running
     // product of A_bar
-    const int n0 = (helper ? 0 : w) * G;
+    const int wc = helper ? 0 : w;
+    // state of lane slot g
+    auto st_n = [&](int g) __attribute__((always_inline)) { return ST ? wc + g * NC : wc * G + g; };
     const int64_t d = d0 + lane;
     float Al[G], aux[G], h[G], pc[G];
     float dsum = 0.0f;
@@ -191,60 +209,77 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     T *Yb = static_cast<T *>(a.y) + b * L * D + d0;
     constexpr uint32_t ES = sizeof(T);
     const uint32_t off0 = static_cast<uint32_t>(r0 * D32 + cp) * ES;    // row r0
+    const uint32_t rowb = static_cast<uint32_t>(D32) * ES;             // bytes per row
+    const uint32_t offq[RPT] = {off0, off0 + rowb};                    // rows r0, r0 + 1
     float dsk[2], dbv[2];   // skip term and delta bias of the thread's channel pair
+    float cst[2];           // structured A: (A[d, NC] - A[d, 0]) log2(e) of the pair
+    bool stage_e = false;   // the helpers stage E = exp(dt c_d)
     // raw prefetch registers, a ring of kRS sets (block j lives in set j % kRS), so the
     // loads of a block are issued kRS - 1 blocks before they are staged
     Vec<T, 2> rx[kRS][RPT], rd[kRS][RPT], rz[kRS][RPT];   // [set][row]
-    Vec<T, 2> ex[2][RPT], ez[2][RPT];   // raw x, z kept for the epilogue [block parity][row]
+    float ex[4][RPT][2];                // x (widened) kept for the epilogue [block % 4][row][channel]
+    Vec<T, 2> ez[4][RPT];               // raw z kept for the epilogue [block % 4][row]
 
     // helpers: raw rows of block kb into register set S.  Branch-free, so that every call
     // issues the same loads and the compiler can count exactly which of them are still in
-    // flight when a block is staged: a block past the last one reloads the last block, and
-    // rows past the end of the chunk reload its last row (staging zeroes those rows).
+    // flight when a block is staged: the buffer range of a block ends at its chunk's end, so
+    // its rows past that end (and every row of a block past the last) read zeros.
     auto load_block = [&](int64_t kb, auto set) __attribute__((always_inline)) {
         constexpr int S = decltype(set)::value;
-        const int64_t tb0 = t0 + (kb < nblk ? kb : nblk - 1) * kTB;
-        const int32_t last = static_cast<int32_t>(t1 - 1 - tb0);   // last row of the block
-        const T *xb = X + tb0 * D;      // uniform row bases
-        const T *db = DL + tb0 * D;
-        const T *zb = HAS_Z ? Z + tb0 * D : nullptr;
+        const int64_t tb0 = t0 + kb * kTB;
+        const int64_t rows = kb < nblk ? (t1 - tb0 < kTB ? t1 - tb0 : kTB) : 0;
+        const uint32_t bytes = static_cast<uint32_t>(rows) * rowb;
+        const int64_t eo = kb < nblk ? tb0 * D : 0;   // uniform row base
+        const auto rX = buf_rsrc(X + eo, bytes), rD = buf_rsrc(DL + eo, bytes);
 #pragma unroll
         for (int q = 0; q < RPT; ++q) {
-            const int32_t row = r0 + q < last ? r0 + q : last;
-            const uint32_t off = static_cast<uint32_t>(row * D32 + cp) * ES;
-            rx[S][q].r = ld_at<decltype(rx[S][q].r)>(xb, off);
-            rd[S][q].r = ld_at<decltype(rd[S][q].r)>(db, off);
-            if constexpr (HAS_Z && !CARRY) rz[S][q].r = ld_at<decltype(rz[S][q].r)>(zb, off);
+            rx[S][q].load(rX, offq[q]);
+            rd[S][q].load(rD, offq[q]);
+        }
+        if constexpr (HAS_Z && !CARRY) {
+            const auto rZ = buf_rsrc(Z + eo, bytes);
+#pragma unroll
+            for (int q = 0; q < RPT; ++q) rz[S][q].load(rZ, offq[q]);
         }
     };
 
     auto stage_block = [&](int64_t tb0, auto par, auto set, auto full, auto softplus) __attribute__((always_inline)) {   // helpers
-        constexpr int P = decltype(par)::value;   // block parity = LDS buffer
+        constexpr int P = decltype(par)::value;   // staging slot = block % 4
         constexpr int S = decltype(set)::value;   // register set of the block
-        float dv[RPT][2], uv[RPT][2];
+        float dv[RPT][2], uv[RPT][2], ev[RPT][2];
 #pragma unroll
         for (int q = 0; q < RPT; ++q) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                float dl = rd[S][q].get(j) + dbv[j];
-                float xv = rx[S][q].get(j);
-                if constexpr (decltype(softplus)::value) dl = softplus_f(dl);
+                float dl = rd[S][q].get(j);
+                const float xr = rx[S][q].get(j);
+                float xv = xr;
+                ex[P][q][j] = xr;
+                if constexpr (decltype(softplus)::value) {   // the general staging: bias, softplus
+                    dl += dbv[j];
+                    if (a.softplus) dl = softplus_f(dl);
+                }
                 if constexpr (!decltype(full)::value) {
                     if (tb0 + r0 + q >= t1) { dl = 0.0f; xv = 0.0f; }   // padded steps leave h unchanged
                 }
                 dv[q][j] = dl;
                 uv[q][j] = DISC == kZOH ? xv : dl * xv;
+                if constexpr (ST) ev[q][j] = __builtin_amdgcn_exp2f(dl * cst[j]);
             }
-            ex[P][q] = rx[S][q];
             if constexpr (HAS_Z && !CARRY) ez[P][q] = rz[S][q];
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
+        if constexpr (ST) {
+            if (stage_e)   // (E_r0, E_r0+1) of channel cp, then of channel cp + 1
+                *reinterpret_cast<float4 *>(&sE[P][rp * 64 + cp]) = make_float4(ev[0][0], ev[1][0], ev[0][1], ev[1][1]);
+        }
     };
 
-    auto epilogue = [&](int64_t tb0, auto par, auto full) __attribute__((always_inline)) {   // helpers: finish rows r0, r0+1
-        constexpr int P = decltype(par)::value;
+    auto epilogue = [&](int64_t tb0, auto slot, auto full) __attribute__((always_inline)) {   // helpers: finish rows r0, r0+1
+        constexpr int SL = decltype(slot)::value;   // block % 4
+        constexpr int P = SL & 1;                   // block parity: y shares
         // (y_r0 ch cp, y_r0+1 ch cp, y_r0 ch cp+1, y_r0+1 ch cp+1)
         float4 acc = *reinterpret_cast<const float4 *>(&sY[P][rp * 64 + cp]);
 #pragma unroll
@@ -253,23 +288,25 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         const float ys[RPT][2] = {{acc.x, acc.z}, {acc.y, acc.w}};   // [row][channel]
-        T *yb = Yb + tb0 * D;           // uniform row base
+        // rows past the chunk fall outside the store range and are dropped
+        const int64_t rows = decltype(full)::value ? kTB : t1 - tb0;
+        const auto rY = buf_rsrc(Yb + tb0 * D, static_cast<uint32_t>(rows) * rowb);
 #pragma unroll
         for (int q = 0; q < RPT; ++q) {
-            if (decltype(full)::value || tb0 + r0 + q < t1) {
-                float o[2];
+            float o[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float yv = __builtin_fmaf(dsk[j], ex[P][q].get(j), ys[q][j]);
-                    if constexpr (HAS_Z) yv *= silu_f(ez[P][q].get(j));
-                    o[j] = yv;
-                }
-                const uint32_t off = off0 + static_cast<uint32_t>(q * D32) * ES;
-                if constexpr (sizeof(T) == 2) st_at_nt<uint32_t>(yb, off, pack_bf16(o[0], o[1]));
-                else {
-                    typedef float f32x2 __attribute__((ext_vector_type(2)));
-                    st_at_nt<f32x2>(yb, off, f32x2{o[0], o[1]});
-                }
+            for (int j = 0; j < 2; ++j) {
+                float yv = __builtin_fmaf(dsk[j], ex[SL][q][j], ys[q][j]);
+                if constexpr (HAS_Z) yv *= silu_f(ez[SL][q].get(j));
+                o[j] = yv;
+            }
+            // non-temporal: y is not read again by this launch
+            if constexpr (sizeof(T) == 2) {
+                __builtin_amdgcn_raw_buffer_store_b32(pack_bf16(o[0], o[1]), rY, static_cast<int>(offq[q]), 0, 2);
+            } else {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(o[0]), __float_as_uint(o[1])}, rY,
+                                                      static_cast<int>(offq[q]), 0, 2);
             }
         }
     };
@@ -291,12 +328,25 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         for (int j = 0; j < NBC; ++j) bc_nx[j] = src[j];
     };
 
-    auto compute_block = [&](int64_t k, auto par) __attribute__((always_inline)) {   // compute waves: 16 steps of G states
-        constexpr int P = decltype(par)::value;
-        float4 du_c[SUB / 2], du_n[SUB / 2];
-        float bc_c[NBC];
+    // (delta, u) and (structured) E of the sub-block about to be computed: requested during
+    // the previous sub-block, or during the last sub-block of the previous block
+    float4 du_c[SUB / 2];
+    float2 e_c[SUB / 2];
+    auto load_du = [&](int64_t k, int sb, float4 *du, float2 *ev, auto str) __attribute__((always_inline)) {
+        const int slot = static_cast<int>(k & 3);
 #pragma unroll
-        for (int q = 0; q < SUB / 2; ++q) du_c[q] = sDU[P][q * 64 + lane];
+        for (int q = 0; q < SUB / 2; ++q) {
+            du[q] = sDU[slot][(sb * SUB / 2 + q) * 64 + lane];
+            if constexpr (decltype(str)::value) ev[q] = sE[slot][(sb * SUB / 2 + q) * 64 + lane];
+        }
+    };
+
+    auto compute_block = [&](int64_t k, auto par, auto str) __attribute__((always_inline)) {   // compute waves: 16 steps of G states
+        constexpr int P = decltype(par)::value;      // block parity: y shares
+        constexpr bool STR = decltype(str)::value;   // structured-A path
+        float4 du_n[SUB / 2];
+        float2 e_n[SUB / 2];
+        float bc_c[NBC];
 #pragma unroll
         for (int j = 0; j < NBC; ++j) bc_c[j] = bc_nx[j];
         // sub-block 0's operands land before the next prefetch is queued behind them
@@ -304,6 +354,13 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
+            // This sub-block's operands were requested a sub-block ago: wait for them before
+            // requesting the next ones (LDS and scalar loads share one counter, and scalar
+            // loads return out of order, so a wait after the next requests would include them).
+            if (sb > 0) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                __builtin_amdgcn_sched_barrier(0);
+            }
             // The two compute waves of a SIMD take turns at the higher priority every half
             // block.  Left to the age-ordered issue, the older one would run ahead, reach the
             // barrier first and leave the younger one to finish alone at the issue rate of a
@@ -317,15 +374,15 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                         // non-temporal: read back only by the backward's reverse sweep, long after
 #pragma unroll
                         for (int g = 0; g < G; ++g)
-                            __builtin_nontemporal_store(h[g], &a.ckpt[((b * a.ck_nblk + t / 8) * kN + n0 + g) * D + d]);
+                            __builtin_nontemporal_store(h[g], &a.ckpt[((b * a.ck_nblk + t / 8) * kN + st_n(g)) * D + d]);
                     }
                 }
             }
             if (sb + 1 < NSUB) {
-#pragma unroll
-                for (int q = 0; q < SUB / 2; ++q) du_n[q] = sDU[P][((sb + 1) * SUB / 2 + q) * 64 + lane];
+                load_du(k, sb + 1, du_n, e_n, str);
                 load_bc(k, sb + 1);
             } else if (k + 1 < nblk) {
+                load_du(k + 1, 0, du_n, e_n, str);   // staged two blocks ahead: already in LDS
                 load_bc(k + 1, 0);
             }
             // keep those loads here: the scheduler would otherwise sink them to their use
@@ -335,34 +392,50 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 const float4 du = du_c[q];
                 const float *bB = bc_c + 2 * q * G;             // B of steps 2q, 2q+1: [step][g]
                 const float *bC = bc_c + SUB * G + 2 * q * G;   // C of the same steps
+                // one step of state slot g: general, or (structured) the decay of slot g - 1
+                // times E
+                auto upd = [&](int g, float dt, float u, float bv, float ev, float &e) __attribute__((always_inline)) {
+                    if (STR && g > 0) {
+                        e *= ev;   // exp(dt A[n + NC]) = exp(dt A[n]) exp(dt c_d)
+                        h[g] = __builtin_fmaf(e, h[g], u * bv);
+                        return e;
+                    }
+                    float ab;
+                    h[g] = disc_step<DISC>(h[g], dt, u, bv, Al[g], aux[g], ab);
+                    e = ab;
+                    return ab;
+                };
+                const float ev0 = STR ? e_c[q].x : 0.0f, ev1 = STR ? e_c[q].y : 0.0f;
                 if constexpr (CARRY) {
                     if constexpr (DISC != kBilinear) {
                         dsum += du.x;
                         dsum += du.z;
                     }
+                    float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        float ab0, ab1;
-                        h[g] = disc_step<DISC>(h[g], du.x, du.y, bB[g], Al[g], aux[g], ab0);
-                        h[g] = disc_step<DISC>(h[g], du.z, du.w, bB[G + g], Al[g], aux[g], ab1);
+                        const float ab0 = upd(g, du.x, du.y, bB[g], ev0, e0);
+                        const float ab1 = upd(g, du.z, du.w, bB[G + g], ev1, e1);
                         if constexpr (DISC == kBilinear) pc[g] *= ab0 * ab1;
                     }
                 } else {
-                    float y0, y1;
+                    float y0, y1, e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        float ab;
-                        h[g] = disc_step<DISC>(h[g], du.x, du.y, bB[g], Al[g], aux[g], ab);
+                        upd(g, du.x, du.y, bB[g], ev0, e0);
                         y0 = g == 0 ? bC[0] * h[0] : __builtin_fmaf(bC[g], h[g], y0);
-                        h[g] = disc_step<DISC>(h[g], du.z, du.w, bB[G + g], Al[g], aux[g], ab);
+                        upd(g, du.z, du.w, bB[G + g], ev1, e1);
                         y1 = g == 0 ? bC[G] * h[0] : __builtin_fmaf(bC[G + g], h[g], y1);
                     }
                     sY[P][(w * kTB / 2 + sb * SUB / 2 + q) * 64 + lane] = make_float2(y0, y1);
                 }
             }
-            if (sb + 1 < NSUB) {
 #pragma unroll
-                for (int q = 0; q < SUB / 2; ++q) du_c[q] = du_n[q];
+            for (int q = 0; q < SUB / 2; ++q) {
+                du_c[q] = du_n[q];
+                if constexpr (STR) e_c[q] = e_n[q];
+            }
+            if (sb + 1 < NSUB) {
 #pragma unroll
                 for (int j = 0; j < NBC; ++j) bc_c[j] = bc_nx[j];
             }
@@ -371,7 +444,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
 
     auto stage_any = [&](int64_t tb0, auto par, auto set) __attribute__((always_inline)) {
         const bool full = tb0 + kTB <= t1;
-        if (a.softplus) {
+        if (a.softplus || a.dbias) {
             if (full) stage_block(tb0, par, set, Full{}, std::true_type{});
             else stage_block(tb0, par, set, Part{}, std::true_type{});
         } else {
@@ -385,53 +458,69 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     };
 
     // The two roles run separate loops with one barrier per block each (and one after the
-    // prologue).  At block k the compute waves scan LDS buffer k & 1 while the helpers finish
-    // block k-1 (its y shares, buffer (k-1) & 1), stage block k+1 into buffer (k+1) & 1 and
-    // request block k+kRS into the register set that block k used.
+    // prologue, which stages blocks 0 and 1).  At block k the compute waves scan staging slot
+    // k % 4 (and request the first operands of block k + 1 from slot (k + 1) % 4) while the
+    // helpers finish block k - 1 (its y shares, buffer (k - 1) & 1), stage block k + 2 into
+    // slot (k + 2) % 4 and request block k + 2 + kRS into the register set that block k + 2
+    // used.
     if (!helper) {
         if (nblk > 0) load_bc(0, 0);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float av = a.A[d * kN + n0 + g];
+            const float av = a.A[d * kN + st_n(g)];
             Al[g] = av * kLog2e;
             aux[g] = disc_aux<DISC>(av);
             pc[g] = 1.0f;
             float hv = 0.0f;
             if (!CARRY || CKPT) {   // carries start from zero; checkpoints from h0
                 if (c == 0) {
-                    if (a.h0) hv = a.h0[(b * D + d) * kN + n0 + g];
+                    if (a.h0) hv = a.h0[(b * D + d) * kN + st_n(g)];
                 } else {
-                    hv = a.ws_H[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + n0 + g];
+                    hv = a.ws_H[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + st_n(g)];
                 }
             }
             h[g] = hv;
         }
-        __syncthreads();
+        // structured-A vote: every lane checks A[d, n + NC] - A[d, n] == A[d, NC] - A[d, 0]
+        int ok = 0;
+        if constexpr (ST) {
+            ok = a.structured;
+            const float *Ad = a.A + d * kN;
+            const float cd = Ad[NC] - Ad[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) ok &= (Ad[st_n(g)] - Ad[st_n(g - 1)]) == cd ? 1 : 0;
+        }
+        const bool structured = ST ? __syncthreads_and(ok) != 0 : (__syncthreads(), false);
         int64_t k = 0;
-        for (; k + 1 < nblk; k += 2) {
-            compute_block(k, Par<0>{});
-            __syncthreads();
-            compute_block(k + 1, Par<1>{});
-            __syncthreads();
-        }
-        if (k < nblk) {
-            compute_block(k, Par<0>{});
-            __syncthreads();
-        }
+        auto run = [&](auto str) __attribute__((always_inline)) {
+            if (nblk > 0) load_du(0, 0, du_c, e_c, str);
+            for (; k + 1 < nblk; k += 2) {
+                compute_block(k, Par<0>{}, str);
+                __syncthreads();
+                compute_block(k + 1, Par<1>{}, str);
+                __syncthreads();
+            }
+            if (k < nblk) {
+                compute_block(k, Par<0>{}, str);
+                __syncthreads();
+            }
+        };
+        if (ST && structured) run(std::integral_constant<bool, ST>{});
+        else run(std::false_type{});
         if constexpr (CARRY && CKPT) {
         } else if constexpr (CARRY) {
             const int64_t slot = b * (a.n_chunks - 1) + c;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 // the chunk's decay: exp(A * sum of delta), or the product of the bilinear A_bar
-                a.ws_P[(slot * D + d) * kN + n0 + g] =
+                a.ws_P[(slot * D + d) * kN + st_n(g)] =
                     DISC == kBilinear ? pc[g] : __builtin_amdgcn_exp2f(Al[g] * dsum);
-                a.ws_H[(slot * D + d) * kN + n0 + g] = h[g];
+                a.ws_H[(slot * D + d) * kN + st_n(g)] = h[g];
             }
         } else {
             if (a.h_last && c == a.n_chunks - 1) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + n0 + g] = h[g];
+                for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + st_n(g)] = h[g];
             }
         }
     } else if (pfw) {
@@ -456,7 +545,8 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
 #pragma unroll
         for (int j = 1; j < kPD; ++j)
             if (j < nblk) touch(j);
-        __syncthreads();
+        if constexpr (ST) (void)__syncthreads_and(1);   // the structured-A vote
+        else __syncthreads();
         for (int64_t k = 0; k < nblk; ++k) {
             if (k + kPD < nblk) touch(k + kPD);
             __syncthreads();
@@ -469,33 +559,39 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         for (int j = 0; j < 2; ++j) {
             dsk[j] = (!CARRY && a.Dskip) ? a.Dskip[d0 + cp + j] : 0.0f;
             dbv[j] = a.dbias ? a.dbias[d0 + cp + j] : 0.0f;
+            cst[j] = ST ? (a.A[(d0 + cp + j) * kN + NC] - a.A[(d0 + cp + j) * kN]) * kLog2e : 0.0f;
         }
+        stage_e = ST && a.structured;
         // keep the D loads out of the in-order queue of the block prefetch
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        static_assert(kRS == 2 || kRS == 4, "the loop below is unrolled by four");
         if (nblk > 0) {
             load_block(0, Par<0>{});
             load_block(1, Par<1>{});
-            if constexpr (kRS == 4) {
-                load_block(2, Par<2>{});
-                load_block(3, Par<3>{});
-            }
+            load_block(2, Par<2>{});
+            load_block(3, Par<3>{});
             stage_any(t0, Par<0>{}, Par<0>{});
+            load_block(kRS, Par<0>{});
+            if (nblk > 1) stage_any(t0 + kTB, Par<1>{}, Par<1>{});
+            load_block(kRS + 1, Par<1>{});
         }
-        __syncthreads();
-        // block k >= 1, k % 4 == S: every block before the last is full
+        if constexpr (ST) (void)__syncthreads_and(1);   // the structured-A vote
+        else __syncthreads();
+        // iteration k >= 1, k % 4 == S: finish block k - 1, stage block k + 2 (slot and register
+        // set (S + 2) % 4), then reuse that register set for block k + 2 + kRS.  Every block
+        // before the last is full.
+        static_assert(kRS == 4, "register set = staging slot = block % 4");
         auto step = [&](int64_t k, auto set) __attribute__((always_inline)) {
             constexpr int S = decltype(set)::value;
-            constexpr int P = S & 1;
+            constexpr int S2 = (S + 2) % 4;
             const int64_t tb0 = t0 + k * kTB;
-            if constexpr (!CARRY) epilogue(tb0 - kTB, Par<1 - P>{}, Full{});
-            if (k + 1 < nblk) stage_any(tb0 + kTB, Par<1 - P>{}, Par<(S + 1) % kRS>{});
-            load_block(k + kRS, Par<S % kRS>{});
+            if constexpr (!CARRY) epilogue(tb0 - kTB, Par<(S + 3) % 4>{}, Full{});
+            if (k + 2 < nblk) stage_any(tb0 + 2 * kTB, Par<S2>{}, Par<S2>{});
+            load_block(k + 2 + kRS, Par<S2>{});
             __syncthreads();
         };
-        if (nblk > 0) {   // block 0: nothing to finish yet
-            if (nblk > 1) stage_any(t0 + kTB, Par<1>{}, Par<1>{});
-            load_block(kRS, Par<0>{});
+        if (nblk > 0) {   // iteration 0: nothing to finish yet
+            if (nblk > 2) stage_any(t0 + 2 * kTB, Par<2>{}, Par<2>{});
+            load_block(kRS + 2, Par<2>{});
             __syncthreads();
         }
         int64_t k = 1;
@@ -511,8 +607,12 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         if constexpr (!CARRY) {
             if (nblk > 0) {
                 const int64_t last = t0 + (nblk - 1) * kTB;
-                if ((nblk - 1) & 1) epilogue_any(last, Par<1>{});
-                else epilogue_any(last, Par<0>{});
+                switch ((nblk - 1) & 3) {
+                case 0: epilogue_any(last, Par<0>{}); break;
+                case 1: epilogue_any(last, Par<1>{}); break;
+                case 2: epilogue_any(last, Par<2>{}); break;
+                default: epilogue_any(last, Par<3>{}); break;
+                }
             }
         }
     }

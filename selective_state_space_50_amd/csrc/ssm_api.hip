@@ -81,6 +81,7 @@ int run_scan(const ScanPlan &p, int64_t batch, int64_t seqlen, int64_t dim, int6
     a.softplus = delta_softplus;
     a.dbias = variant_bias(variant);
     const int disc = variant_disc(variant);
+    a.structured = p.structured ? 1 : 0;
     a.NW = p.NW;
     a.chunk_len = p.chunk_len;
     a.n_chunks = p.n_chunks;
@@ -94,7 +95,7 @@ int run_scan(const ScanPlan &p, int64_t batch, int64_t seqlen, int64_t dim, int6
     hipError_t e;
     if (p.fast) {
         // 0) B/C rows of every chunk to fp32, interleaved per state group, zero-padded
-        e = launch_bc_pack(a, p, bf16, s);
+        e = launch_bc_pack(a, p, disc, bf16, s);
         if (e != hipSuccess) return hip_fail("B/C pack launch", e);
     }
     if (p.n_chunks > 1) {
@@ -255,6 +256,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         fa.A = A; fa.Dskip = nullptr; fa.h0 = h0; fa.h_last = nullptr; fa.y = nullptr;
         fa.softplus = delta_softplus;
         fa.dbias = delta_bias;
+        fa.structured = p.fwd.structured ? 1 : 0;
         fa.NW = p.fwd.NW;
         fa.chunk_len = p.fwd.chunk_len;
         fa.n_chunks = p.fwd.n_chunks;
@@ -264,7 +266,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         fa.bc_lpad = p.fwd.bc_lpad;
         fa.ckpt = reinterpret_cast<float *>(ws + p.ckpt_off);
         fa.ck_nblk = p.nblk;
-        e = launch_bc_pack(fa, p.fwd, bf16, s);
+        e = launch_bc_pack(fa, p.fwd, discretization, bf16, s);
         if (e != hipSuccess) return hip_fail("B/C pack launch", e);
         const unsigned dblocks = static_cast<unsigned>(dim / 64);
         if (p.fwd.n_chunks > 1) {

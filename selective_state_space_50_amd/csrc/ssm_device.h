@@ -37,6 +37,7 @@ struct ScanArgs {
     int64_t bc_lpad;
     float *ckpt = nullptr;   // checkpoint pass: [B][ck_nblk][N][D] state before every 8th step
     int64_t ck_nblk = 0;
+    int structured = 0;      // 1: the chained kernel may take its structured-A path (checked on the device)
 };
 
 struct UpdArgs {
@@ -214,7 +215,7 @@ SSM_SAVE_LAUNCHER(launch_scan_save_bilinear);
 hipError_t launch_scan_save(const ScanArgs &a, dim3 grid, const ScanPlan &p, int disc, bool bf16, bool has_z,
                             hipStream_t s);
 // Specialised path pre-pass: pack B/C rows into ws_BC.
-hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, bool bf16, hipStream_t s);
+hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, int disc, bool bf16, hipStream_t s);
 hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z, hipStream_t s);
 // Causal depthwise convolution (+ SiLU): sequence form and single-token form.
 hipError_t launch_conv1d_fwd(const ConvArgs &a, bool bf16, hipStream_t s);

@@ -108,8 +108,12 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     if (st != SSM_OK) return st;
     ssm_scan_opts o{0, 0, 0, 0, 0};
     if (opts) o = *opts;
-    if (o.one_block_per_cu < -1 || o.one_block_per_cu > 1 || o.reserved != 0) {
-        set_error("opts.one_block_per_cu=%d must be -1, 0 or 1 and opts.reserved 0", o.one_block_per_cu);
+    if (o.one_block_per_cu < -1 || o.one_block_per_cu > 1) {
+        set_error("opts.one_block_per_cu=%d must be -1, 0 or 1", o.one_block_per_cu);
+        return SSM_EINVAL;
+    }
+    if (o.a_structure != 0 && o.a_structure != -1) {
+        set_error("opts.a_structure=%d must be 0 or -1", o.a_structure);
         return SSM_EINVAL;
     }
     if (o.chunk_len < 0) {
@@ -228,6 +232,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
                                static_cast<size_t>(p.bc_lpad) * 16 * 2 * sizeof(float),
                       kWsAlign);
     }
+    p.structured = o.a_structure == 0;
     p.ws_bytes = ws;
     p.blocks = static_cast<uint64_t>(dblocks) * static_cast<uint64_t>(batch) *
                static_cast<uint64_t>(p.n_chunks);

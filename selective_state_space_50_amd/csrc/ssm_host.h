@@ -30,6 +30,7 @@ struct ScanPlan {
     uint64_t blocks = 0;  // workgroups of the main scan launch
     bool fast = false;    // dstate == 16 and dim % 64 == 0: the specialised kernel runs
     size_t lds_reserve = 0;  // dynamic LDS that caps residency at one workgroup per CU
+    bool structured = true;  // the Mamba kernels may take their structured-A path (device check)
 };
 
 // Per-thread error text (ssm_last_error).
