@@ -181,6 +181,24 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  const ssm_scan_opts *opts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssm_scan_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It takes no workspace:
+ * its workspace is a fixed device array of ssm_noalloc_scratch_bytes() bytes (64 MiB) that
+ * the library holds on every GPU it runs on until the process ends.  The call allocates
+ * and frees nothing.  A shape whose workspace (ssm_scan_workspace_bytes with the same
+ * opts) exceeds the array returns SSM_EWORKSPACE before any launch.  Every call on one
+ * GPU shares that GPU's array, so calls that overlap on one GPU (on different streams, or
+ * from threads the caller does not order) race: the caller must serialise them.  All
+ * other arguments, results and errors are those of ssm_scan_fwd.
+ */
+size_t ssm_noalloc_scratch_bytes(void);
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                         const void *x, const void *delta, const float *A, const void *B,
+                         const void *C, const float *Dskip, const void *z, const float *h0,
+                         float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                         const ssm_scan_opts *opts, void *stream);
+
+/*
  * Single-token recurrent state update (generation form): one step of the
  * recurrence for every (b, d), with the state kept in HBM between calls.
  * brentwoodlivery, "Training vs Inference Modes": keep h_{k-1}, receive x_k,

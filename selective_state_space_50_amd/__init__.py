@@ -88,6 +88,11 @@ def lib():
     L.ssm_scan_fwd.restype = I32
     L.ssm_scan_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, P, I32,
                                ctypes.POINTER(Variant), ctypes.POINTER(ScanOpts), P, SZ, P]
+    L.ssm_noalloc_scratch_bytes.restype = SZ
+    L.ssm_noalloc_scratch_bytes.argtypes = []
+    L.ssm_scan_fwd_noalloc.restype = I32
+    L.ssm_scan_fwd_noalloc.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, P, I32,
+                                       ctypes.POINTER(Variant), ctypes.POINTER(ScanOpts), P]
     L.ssm_state_update.restype = I32
     L.ssm_state_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, I32,
                                    ctypes.POINTER(Variant), P]
@@ -249,6 +254,40 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False
                             ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_scan_fwd")
     return (out, h_last) if return_last_state else out
+
+
+def scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
+                     discretization="mamba", delta_bias=None, out=None, h_last=None, chunk_len=0,
+                     states_per_lane=0, general_a=False, stream=None):
+    """scan_fwd through ssm_scan_fwd_noalloc: the library's fixed scratch array stands in for
+    the workspace, so the call itself allocates no device memory when ``out`` (and
+    ``h_last``, if wanted) are given.  Returns y, or (y, h_last) when h_last is given."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, dim] and A [dim, dstate]")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd_noalloc runs on the GPU only; tensors must be on a cuda device")
+    for t, name, shape, tdt in ((x, "x", (Bsz, L, Dm), dt), (delta, "delta", (Bsz, L, Dm), dt),
+                                (z, "z", (Bsz, L, Dm), dt), (B, "B", (Bsz, L, N), dt),
+                                (C, "C", (Bsz, L, N), dt), (A, "A", (Dm, N), torch.float32),
+                                (D, "D", (Dm,), torch.float32), (h0, "h0", (Bsz, Dm, N), torch.float32),
+                                (h_last, "h_last", (Bsz, Dm, N), torch.float32)):
+        _need(t, name, shape, tdt, dev)
+    v = _variant(discretization, delta_bias, Dm, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (Bsz, L, Dm), dt, dev)
+    o = _opts(chunk_len, states_per_lane, 0, 0, general_a)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_scan_fwd_noalloc(Bsz, L, Dm, N, _dtype_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                    _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(h_last), _ptr(out),
+                                    int(bool(delta_softplus)), ctypes.byref(v) if v else None,
+                                    ctypes.byref(o) if o else None, ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_scan_fwd_noalloc")
+    return (out, h_last) if h_last is not None else out
 
 
 def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False,

@@ -9,6 +9,8 @@
 // then starts every chunk from its carried-in state.
 #include "ssm_device.h"
 
+#include <mutex>
+
 namespace ssm {
 namespace {
 
@@ -145,6 +147,80 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     }
     return run_scan(p, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
                     delta_softplus, variant, workspace, nullptr, 0, s);
+}
+
+// ---- the forward for callers that cannot allocate: its workspace is a fixed device array
+
+namespace ssm {
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;   // SSM_NOALLOC_SCRATCH_BYTES
+constexpr int kMaxDevices = 64;
+// One copy per GPU, held from the library's load until the process ends.  In host code this
+// name is not a device address: host code uses the per-device address from
+// hipGetSymbolAddress (scratch_ptr) wherever it needs the array's memory.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device (looked up once per device).
+int scratch_ptr(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device %d is beyond the %d devices the fixed scratch supports", dev, kMaxDevices);
+        return SSM_EUNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSM_OK;
+}
+}  // namespace
+}  // namespace ssm
+
+extern "C" size_t ssm_noalloc_scratch_bytes(void) { return ssm::kScratchBytes; }
+
+extern "C" int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                                    const void *x, const void *delta, const float *A, const void *B,
+                                    const void *C, const float *Dskip, const void *z, const float *h0,
+                                    float *h_last, void *y, int delta_softplus, const ssm_variant *variant,
+                                    const ssm_scan_opts *opts, void *stream) {
+    using namespace ssm;
+    clear_error();
+    ScanPlan p;
+    int st = plan_scan(batch, seqlen, dim, dstate, dtype, opts, &p);
+    if (st != SSM_OK) return st;
+    if (p.ws_bytes > kScratchBytes) {
+        set_error("this shape needs %zu bytes of workspace; the fixed scratch holds %zu (use ssm_scan_fwd "
+                  "with a caller-allocated workspace)", p.ws_bytes, kScratchBytes);
+        return SSM_EWORKSPACE;
+    }
+    void *ws = nullptr;
+    if (p.ws_bytes > 0 && batch > 0 && dim > 0 && seqlen > 0) {
+        st = scratch_ptr(&ws);
+        if (st != SSM_OK) return st;
+    }
+    st = check_scan(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
+                    delta_softplus, variant, opts, ws, ws ? kScratchBytes : 0, &p);
+    if (st != SSM_OK) return st;
+    if (batch == 0 || dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_last) return SSM_OK;
+        const int64_t n = batch * dim * dstate;
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                           0, s, h_last, h0, n);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
+    }
+    return run_scan(p, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
+                    delta_softplus, variant, ws, nullptr, 0, s);
 }
 
 extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, float *h,
