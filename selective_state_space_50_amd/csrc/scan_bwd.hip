@@ -485,20 +485,30 @@ __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
     *reinterpret_cast<float2 *>(a.lc_H + slot * kN + n0) = make_float2(lam[0], lam[1]);
 }
 
-// Fold the adjoint carries from the last chunk down, one thread per (b, d, n):
+// Fold the adjoint carries from the last chunk down with a parallel scan (segment_scan):
 //   lam_in(last) = dh_last,  lam_in(c) = P_{c+1} lam_in(c+1) + H_{c+1}
 // and overwrite slot c (which held chunk c+1's carry) with lam_in(c).
+template <int S>
 __global__ void __launch_bounds__(256) bwd_combine_kernel(BwdArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    // one segment of S lanes per (b, d, n); lane j holds chunk slot C1 - 1 - (t + j) of a
+    // tile: the fold runs from the last chunk down, so later chunks sit in lower lanes
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t DN = a.D * kN;
-    if (i >= a.B * DN) return;
-    const int64_t b = i / DN, dn = i - b * DN;
-    float lam = a.dh_last ? a.dh_last[i] : 0.0f;
+    const int64_t item = gid / S;
+    const int j = static_cast<int>(gid % S);
+    const bool ok = item < a.B * DN;
+    const int64_t b = ok ? item / DN : 0, dn = ok ? item - b * DN : 0;
     const int64_t C1 = a.n_chunks - 1;
-    for (int64_t c = C1 - 1; c >= 0; --c) {
+    float carry = (ok && a.dh_last) ? a.dh_last[item] : 0.0f;
+    for (int64_t t = 0; t < C1; t += S) {
+        const int64_t c = C1 - 1 - (t + j);
+        const bool v = ok && c >= 0;
         const int64_t at = (b * C1 + c) * DN + dn;
-        lam = __builtin_fmaf(a.lc_P[at], lam, a.lc_H[at]);
-        a.lc_H[at] = lam;
+        float P = v ? a.lc_P[at] : 1.0f, H = v ? a.lc_H[at] : 0.0f;
+        segment_scan<S>(P, H);
+        const float lam = __builtin_fmaf(P, carry, H);
+        if (v) a.lc_H[at] = lam;
+        carry = __shfl(lam, S - 1, S);
     }
 }
 
@@ -555,7 +565,14 @@ hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n = a.B * a.D * kN;
-        hipLaunchKernelGGL(bwd_combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
+        const int64_t C1 = a.n_chunks - 1;
+        int lg = 0;
+        while ((1 << lg) < C1 && lg < 6) ++lg;
+        void (*k[7])(BwdArgs) = {bwd_combine_kernel<1>, bwd_combine_kernel<2>, bwd_combine_kernel<4>,
+                                 bwd_combine_kernel<8>, bwd_combine_kernel<16>, bwd_combine_kernel<32>,
+                                 bwd_combine_kernel<64>};
+        const int64_t threads = n << lg;
+        hipLaunchKernelGGL(k[lg], dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -176,11 +176,16 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     const bool pfw = has_prefetch_wave<G>() && w >= NC + helper_waves<G>();
     const int64_t D = a.D, L = a.L;
     const int64_t b = blockIdx.y;
-    const int64_t c = blockIdx.z;
+    const int64_t c = blockIdx.z + a.c_first;
     const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int64_t t0 = c * a.chunk_len;
-    const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
-    const int64_t nblk = (t1 - t0 + kTB - 1) / kTB;
+    const int64_t cs = c * a.chunk_len;                                // the chunk's first step
+    const int64_t ce = (cs + a.chunk_len < L) ? cs + a.chunk_len : L;  // and its end
+    const int64_t t0 = cs + a.t_off;                                   // this launch's steps [t0, t1)
+    const int64_t t1 = (a.t_span > 0 && t0 + a.t_span < ce) ? t0 + a.t_span : ce;
+    const int64_t nblk = t1 > t0 ? (t1 - t0 + kTB - 1) / kTB : 0;
+    // a continuation launch runs only the chunks whose flag the carry combine set
+    if (a.flag_in && a.flag_in[(b * (a.n_chunks - 1) + c - 1) * gridDim.x + blockIdx.x] == 0) return;
+    if (a.flags && c > 0 && threadIdx.x == 0) a.flags[(b * (a.n_chunks - 1) + c - 1) * gridDim.x + blockIdx.x] = 0;
 
     // ---- compute-wave state: G states of channel d0 + lane, A scaled by log2(e), the
     // discretisation's second per-state constant, and (bilinear carries) the running
@@ -195,7 +200,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     // rows of the NC waves alternate every kTB steps
     // (global and constant address spaces share 64-bit addresses on gfx950)
     cfloat *bcw = reinterpret_cast<cfloat *>(reinterpret_cast<uintptr_t>(
-        a.ws_BC + ((b * a.n_chunks + c) * (a.bc_lpad / kTB) * NC + (helper ? 0 : w)) * kTB * (2 * G)));
+        a.ws_BC + (((b * a.n_chunks + c) * (a.bc_lpad / kTB) + a.t_off / kTB) * NC + (helper ? 0 : w)) * kTB * (2 * G)));
 
     // ---- helper role
     const int hid = tid - NC * 64;
@@ -213,6 +218,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     const uint32_t offq[RPT] = {off0, off0 + rowb};                    // rows r0, r0 + 1
     float dsk[2], dbv[2];   // skip term and delta bias of the thread's channel pair
     float cst[2];           // structured A: (A[d, NC] - A[d, 0]) log2(e) of the pair
+    float ssum[2] = {0.0f, 0.0f}, spre[2] = {0.0f, 0.0f};   // delta sums (ScanArgs::S_part)
     bool stage_e = false;   // the helpers stage E = exp(dt c_d)
     // raw prefetch registers, a ring of kRS sets (block j lives in set j % kRS), so the
     // loads of a block are issued kRS - 1 blocks before they are staged
@@ -264,13 +270,24 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 }
                 dv[q][j] = dl;
                 uv[q][j] = DISC == kZOH ? xv : dl * xv;
-                if constexpr (ST) ev[q][j] = __builtin_amdgcn_exp2f(dl * cst[j]);
+                if constexpr (ST) {
+                    if (stage_e) ev[q][j] = __builtin_amdgcn_exp2f(dl * cst[j]);
+                }
             }
             if constexpr (HAS_Z && !CARRY) ez[P][q] = rz[S][q];
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             sDU[P][rp * 64 + cp + j] = make_float4(dv[0][j], uv[0][j], dv[1][j], uv[1][j]);
+        if (a.S_part) {   // sums of delta over the chunk and over its first y_skip steps
+            const bool pre = tb0 < cs + a.y_skip;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float s2 = dv[0][j] + dv[1][j];
+                ssum[j] += s2;
+                if (pre) spre[j] += s2;
+            }
+        }
         if constexpr (ST) {
             if (stage_e)   // (E_r0, E_r0+1) of channel cp, then of channel cp + 1
                 *reinterpret_cast<float4 *>(&sE[P][rp * 64 + cp]) = make_float4(ev[0][0], ev[1][0], ev[0][1], ev[1][1]);
@@ -472,11 +489,13 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             aux[g] = disc_aux<DISC>(av);
             pc[g] = 1.0f;
             float hv = 0.0f;
-            if (!CARRY || CKPT) {   // carries start from zero; checkpoints from h0
+            // carries, and the local scan's chunks >= 1, start from zero; chunk 0 from h0; the
+            // other chunks from their carried-in states
+            if (!CARRY || CKPT) {
                 if (c == 0) {
                     if (a.h0) hv = a.h0[(b * D + d) * kN + st_n(g)];
-                } else {
-                    hv = a.ws_H[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + st_n(g)];
+                } else if (!a.ws_Hl) {
+                    hv = (a.h_in ? a.h_in : a.ws_H)[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + st_n(g)];
                 }
             }
             h[g] = hv;
@@ -521,6 +540,15 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             if (a.h_last && c == a.n_chunks - 1) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) a.h_last[(b * D + d) * kN + st_n(g)] = h[g];
+            }
+            if (a.ws_Hl) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) a.ws_Hl[((b * a.n_chunks + c) * D + d) * kN + st_n(g)] = h[g];
+            }
+            if (a.h_out && c > 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    a.h_out[((b * (a.n_chunks - 1) + (c - 1)) * D + d) * kN + st_n(g)] = h[g];
             }
         }
     } else if (pfw) {
@@ -584,7 +612,9 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             constexpr int S = decltype(set)::value;
             constexpr int S2 = (S + 2) % 4;
             const int64_t tb0 = t0 + k * kTB;
-            if constexpr (!CARRY) epilogue(tb0 - kTB, Par<(S + 3) % 4>{}, Full{});
+            if constexpr (!CARRY) {
+                if (c == 0 || tb0 - kTB >= cs + a.y_skip) epilogue(tb0 - kTB, Par<(S + 3) % 4>{}, Full{});
+            }
             if (k + 2 < nblk) stage_any(tb0 + 2 * kTB, Par<S2>{}, Par<S2>{});
             load_block(k + 2 + kRS, Par<S2>{});
             __syncthreads();
@@ -605,14 +635,22 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         if (k + 1 < nblk) step(k + 1, Par<2>{});
         if (k + 2 < nblk) step(k + 2, Par<3>{});
         if constexpr (!CARRY) {
-            if (nblk > 0) {
-                const int64_t last = t0 + (nblk - 1) * kTB;
+            const int64_t last = t0 + (nblk - 1) * kTB;
+            if (nblk > 0 && (c == 0 || last >= cs + a.y_skip)) {
                 switch ((nblk - 1) & 3) {
                 case 0: epilogue_any(last, Par<0>{}); break;
                 case 1: epilogue_any(last, Par<1>{}); break;
                 case 2: epilogue_any(last, Par<2>{}); break;
                 default: epilogue_any(last, Par<3>{}); break;
                 }
+            }
+        }
+        if (a.S_part) {   // this thread's rows of every block; the combine adds the 8 row pairs
+            const int64_t C = a.n_chunks;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                a.S_part[((b * C + c) * 8 + rp) * D + d0 + cp + j] = ssum[j];
+                a.S_part[(((a.B + b) * C + c) * 8 + rp) * D + d0 + cp + j] = spre[j];
             }
         }
     }

@@ -14,22 +14,116 @@
 namespace ssm {
 namespace {
 
-// Fold chunk carries in sequence order, one thread per (b, d, n):
+// Carries of the carry pass, folded in sequence order with a parallel scan (segment_scan in
+// ssm_device.h): one segment of S
+// lanes per (b, d, n), lane j holding chunk t + j of a tile of S chunks (padded with the
+// identity (1, 0)); the state entering the tile is the carry.
 //   h_in(0) = h0,  h_in(c+1) = P_c * h_in(c) + H_c
-// and overwrite slot c with h_in(c+1), the state chunk c+1 starts from.
+// overwrites slot c with h_in(c+1), the state chunk c+1 starts from.
+template <int S>
 __global__ void __launch_bounds__(256) combine_kernel(ScanArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t D = a.D, N = a.N;
-    if (i >= a.B * D * N) return;
-    const int64_t dn = i % (D * N);
-    const int64_t b = i / (N * D);
-    float h = a.h0 ? a.h0[i] : 0.0f;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t DN = a.D * a.N;
+    const int64_t item = gid / S;   // (b, d, n)
+    const int j = static_cast<int>(gid % S);
+    const bool ok = item < a.B * DN;
+    const int64_t b = ok ? item / DN : 0, dn = ok ? item % DN : 0;
     const int64_t C1 = a.n_chunks - 1;
-    for (int64_t c = 0; c < C1; ++c) {
-        const int64_t at = (b * C1 + c) * D * N + dn;
-        h = __builtin_fmaf(a.ws_P[at], h, a.ws_H[at]);
-        a.ws_H[at] = h;
+    float carry = (ok && a.h0) ? a.h0[item] : 0.0f;
+    for (int64_t t = 0; t < C1; t += S) {
+        const int64_t c = t + j;
+        const bool v = ok && c < C1;
+        const int64_t at = (b * C1 + c) * DN + dn;
+        float P = v ? a.ws_P[at] : 1.0f, H = v ? a.ws_H[at] : 0.0f;
+        segment_scan<S>(P, H);
+        const float hin = __builtin_fmaf(P, carry, H);
+        if (v) a.ws_H[at] = hin;
+        carry = __shfl(hin, S - 1, S);
     }
+}
+
+// Carries of the local scans (every chunk scanned from its own start, ScanArgs::ws_Hl and
+// the delta sums S_part): chunk c's decay is P_c = exp(A sum of its delta); chunk 0 starts
+// from h0, so its end state is exact and P_0 = 0.  The scan gives each chunk c >= 1 its
+// carried-in state h_in(c) (into ws_H) and the last chunk's true end state (h_last).  It also
+// decides whether the carried-in state still matters after the prefix that the rescan
+// covers: the part of chunk c's state that comes from h_in decays as exp(A * cumulative
+// delta), so after the first y_skip steps it is h_in * exp(A * S_pre) and keeps shrinking
+// when A <= 0.  Below 2^-100 its share of any output is far under fp32 resolution; otherwise
+// (or when A > 0) the chunk's flag is set and the rest of the chunk is rescanned too.
+template <int S>
+__global__ void __launch_bounds__(256) local_combine_kernel(ScanArgs a, float *h_last) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t D = a.D, N = a.N, DN = D * N, C = a.n_chunks;
+    const int64_t item = gid / S;   // (b, d, n)
+    const int j = static_cast<int>(gid % S);
+    const bool ok = item < a.B * DN;
+    const int64_t b = ok ? item / DN : 0, dn = ok ? item % DN : 0;
+    const int64_t d = dn / N;
+    const float Av = ok ? a.A[dn] : 0.0f;
+    const float al = Av * kLog2e;
+    constexpr float kNegligible = 7.888609052210118e-31f;   // 2^-100
+    float carry = 0.0f;
+    for (int64_t t = 0; t < C; t += S) {
+        const int64_t c = t + j;
+        const bool v = ok && c < C;
+        float sf = 0.0f, sp = 0.0f;
+        if (v) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                sf += a.S_part[((b * C + c) * 8 + r) * D + d];
+                sp += a.S_part[(((a.B + b) * C + c) * 8 + r) * D + d];
+            }
+        }
+        float P = v ? (c == 0 ? 0.0f : __builtin_amdgcn_exp2f(al * sf)) : 1.0f;
+        float H = v ? a.ws_Hl[(b * C + c) * DN + dn] : 0.0f;
+        segment_scan<S>(P, H);
+        const float hend = __builtin_fmaf(P, carry, H);   // chunk c's true end state
+        float hin = __shfl_up(hend, 1, S);                 // chunk c's start state
+        if (j == 0) hin = carry;
+        if (v && c >= 1) {
+            a.ws_H[((b * (C - 1) + (c - 1)) * DN) + dn] = hin;
+            const float g = __builtin_fabsf(hin) * __builtin_amdgcn_exp2f(al * sp);
+            if (Av > 0.0f || !(g <= kNegligible))
+                atomicOr(&a.flags[(b * (C - 1) + (c - 1)) * (D / 64) + d / 64], 1);
+        }
+        if (v && c == C - 1 && h_last) h_last[b * DN + dn] = hend;
+        carry = __shfl(hend, S - 1, S);
+    }
+}
+
+// Segment width: the chunk count rounded up to a power of two, at most a wave
+int seg_width(int64_t n) {
+    int S = 1;
+    while (S < n && S < 64) S *= 2;
+    return S;
+}
+
+template <typename K>
+hipError_t launch_seg(K kernels[7], int S, int64_t items, hipStream_t s, const ScanArgs &a) {
+    int lg = 0;
+    while ((1 << lg) < S) ++lg;
+    const int64_t threads = items * S;
+    hipLaunchKernelGGL(kernels[lg], dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const ScanArgs &a, hipStream_t s) {
+    void (*k[7])(ScanArgs) = {combine_kernel<1>, combine_kernel<2>, combine_kernel<4>, combine_kernel<8>,
+                              combine_kernel<16>, combine_kernel<32>, combine_kernel<64>};
+    return launch_seg(k, seg_width(a.n_chunks - 1), a.B * a.D * a.N, s, a);
+}
+
+hipError_t launch_local_combine(const ScanArgs &a, float *h_last, hipStream_t s) {
+    void (*k[7])(ScanArgs, float *) = {local_combine_kernel<1>, local_combine_kernel<2>, local_combine_kernel<4>,
+                                       local_combine_kernel<8>, local_combine_kernel<16>,
+                                       local_combine_kernel<32>, local_combine_kernel<64>};
+    const int S = seg_width(a.n_chunks);
+    int lg = 0;
+    while ((1 << lg) < S) ++lg;
+    const int64_t threads = a.B * a.D * a.N * S;
+    hipLaunchKernelGGL(k[lg], dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a, h_last);
+    return hipGetLastError();
 }
 
 // n 16-bit words of zeros (any output of a gradient that has no terms)
@@ -100,15 +194,49 @@ int run_scan(const ScanPlan &p, int64_t batch, int64_t seqlen, int64_t dim, int6
         e = launch_bc_pack(a, p, disc, bf16, s);
         if (e != hipSuccess) return hip_fail("B/C pack launch", e);
     }
+    if (p.local && disc != kBilinear && !ckpt) {
+        // Long chunks, exponential decays: every chunk scanned once from its own start
+        // (chunk 0 from h0), its y written except for the first kLocalPrefix steps of chunks
+        // >= 1; the carries folded by a parallel scan; those prefixes rescanned from the
+        // carried-in states; the rest of a chunk rescanned only where the carried-in state
+        // has not died out by then (flags).  About 1.06x the work of one pass, against 1.8x
+        // for a carry pass followed by a full rescan.
+        const unsigned C = static_cast<unsigned>(p.n_chunks);
+        char *wsb = static_cast<char *>(workspace);
+        a.ws_Hl = reinterpret_cast<float *>(wsb + p.ws_Hl_off);
+        a.S_part = reinterpret_cast<float *>(wsb + p.ws_S_off);
+        a.flags = reinterpret_cast<int *>(wsb + p.ws_F_off);
+        a.y_skip = kLocalPrefix;
+        a.h_last = nullptr;
+        e = launch_scan_any(a, dim3(dblocks, static_cast<unsigned>(batch), C), p, disc, bf16, has_z, false, s);
+        if (e != hipSuccess) return hip_fail("local scan launch", e);
+        e = launch_local_combine(a, h_last, s);
+        if (e != hipSuccess) return hip_fail("local carry combine launch", e);
+        ScanArgs r = a;   // the prefixes of chunks >= 1, from their carried-in states
+        r.ws_Hl = nullptr; r.S_part = nullptr; r.flags = nullptr; r.y_skip = 0;
+        r.c_first = 1;
+        r.t_span = kLocalPrefix;
+        r.h_in = a.ws_H;
+        r.h_out = a.ws_P;
+        dim3 gr(dblocks, static_cast<unsigned>(batch), C - 1);
+        e = launch_scan_any(r, gr, p, disc, bf16, has_z, false, s);
+        if (e != hipSuccess) return hip_fail("prefix rescan launch", e);
+        r.t_off = kLocalPrefix;   // the rest of the flagged chunks, from the prefix's end state
+        r.t_span = 0;
+        r.h_in = a.ws_P;
+        r.h_out = nullptr;
+        r.flag_in = a.flags;
+        e = launch_scan_any(r, gr, p, disc, bf16, has_z, false, s);
+        if (e != hipSuccess) return hip_fail("continuation rescan launch", e);
+        return SSM_OK;
+    }
     if (p.n_chunks > 1) {
         // 1) carries of every chunk but the last
         dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.n_chunks - 1));
         e = launch_scan_any(a, g1, p, disc, bf16, false, true, s);
         if (e != hipSuccess) return hip_fail("scan carry launch", e);
         // 2) fold the carries in order
-        const int64_t n = batch * dim * dstate;
-        hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
-        e = hipGetLastError();
+        e = launch_combine(a, s);
         if (e != hipSuccess) return hip_fail("carry combine launch", e);
     }
     // 3) every chunk from its carried-in state, producing y (and the checkpoints)
@@ -349,9 +477,7 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
             dim3 g1(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.fwd.n_chunks - 1));
             e = launch_scan_any(fa, g1, p.fwd, discretization, bf16, false, true, s);
             if (e != hipSuccess) return hip_fail("checkpoint carry launch", e);
-            const int64_t n = batch * dim * dstate;
-            hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, fa);
-            e = hipGetLastError();
+            e = launch_combine(fa, s);
             if (e != hipSuccess) return hip_fail("checkpoint carry combine launch", e);
         }
         e = launch_scan_ckpt(fa, dim3(dblocks, static_cast<unsigned>(batch), static_cast<unsigned>(p.fwd.n_chunks)),

@@ -37,7 +37,19 @@ struct ScanArgs {
     int64_t bc_lpad;
     float *ckpt = nullptr;   // checkpoint pass: [B][ck_nblk][N][D] state before every 8th step
     int64_t ck_nblk = 0;
-    int structured = 0;      // 1: the chained kernel may take its structured-A path (checked on the device)
+    int structured = 0;      // 1: the Mamba kernels may take their structured-A path (checked on the device)
+    // Sequences in chunks, carries from local scans (the specialised kernel; see run_scan):
+    int64_t c_first = 0;     // chunk of blockIdx.z == 0
+    int64_t t_off = 0;       // the launch starts t_off steps into each chunk (a multiple of 16)
+    int64_t t_span = 0;      // and covers at most t_span steps of it (0: to the chunk's end)
+    int64_t y_skip = 0;      // chunks >= 1 leave y of their first y_skip steps unwritten
+    const float *h_in = nullptr;   // [B][n_chunks-1][D][N] start states of chunks >= 1 (null: ws_H)
+    float *h_out = nullptr;        // [B][n_chunks-1][D][N] end states of chunks >= 1, or null
+    float *ws_Hl = nullptr;        // [B][n_chunks][D][N] end state of every chunk from its own start
+                                   // (set: the local scan, whose chunks >= 1 start from zero)
+    float *S_part = nullptr;       // [2][B][n_chunks][8][D] partial sums of delta: whole chunk, first y_skip steps
+    int *flags = nullptr;          // [B][n_chunks-1][D/64] cleared by the local scan
+    const int *flag_in = nullptr;  // only workgroups whose flag is set run
 };
 
 struct UpdArgs {
@@ -181,6 +193,24 @@ __device__ __forceinline__ float disc_step(float h, float dt, float u, float bv,
         const float e = __builtin_amdgcn_exp2f(dt * al);
         abar = e;
         return __builtin_fmaf(e, h, u * bv);
+    }
+}
+
+// Inclusive scan of the elements held by the S lanes of a segment (S a power of two <= 64;
+// lane j of the segment holds element j, earlier elements in lower lanes) under the chunk
+// operator (P1, H1) o (P2, H2) = (P2 P1, P2 H1 + H2): log2(S) rounds of cross-lane moves.
+// Every lane of the wave must take part (shuffles read the other lanes' registers).
+template <int S>
+__device__ __forceinline__ void segment_scan(float &P, float &H) {
+    const int j = threadIdx.x & (S - 1);
+#pragma unroll
+    for (int off = 1; off < S; off <<= 1) {
+        const float Pp = __shfl_up(P, off, S);
+        const float Hp = __shfl_up(H, off, S);
+        if (j >= off) {
+            H = __builtin_fmaf(P, Hp, H);
+            P = P * Pp;
+        }
     }
 }
 

@@ -223,6 +223,20 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         p.ws_H_off = align_up(carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
         ws = align_up(p.ws_H_off + carries * static_cast<size_t>(dstate) * sizeof(float), kWsAlign);
     }
+    if (p.fast && p.n_chunks > 1 && p.chunk_len >= kLocalMinChunk) {
+        // local-scan carries: every chunk's own end state, the partial sums of delta, flags
+        p.local = true;
+        const size_t bcdn = static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks) *
+                            static_cast<size_t>(dim) * static_cast<size_t>(dstate);
+        p.ws_Hl_off = ws;
+        ws = align_up(ws + bcdn * sizeof(float), kWsAlign);
+        p.ws_S_off = ws;
+        ws = align_up(ws + 2 * static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks) * 8 *
+                               static_cast<size_t>(dim) * sizeof(float), kWsAlign);
+        p.ws_F_off = ws;
+        ws = align_up(ws + static_cast<size_t>(batch) * static_cast<size_t>(p.n_chunks - 1) *
+                               static_cast<size_t>(dim / 64) * sizeof(int), kWsAlign);
+    }
     if (p.fast && seqlen > 0 && batch > 0 && dim > 0) {
         // [batch][chunks][bc_lpad/16][16/G][16/SUB][B, C][SUB][G] fp32 (SUB = 8/G), zero past
         // each chunk's end

@@ -31,7 +31,16 @@ struct ScanPlan {
     bool fast = false;    // dstate == 16 and dim % 64 == 0: the specialised kernel runs
     size_t lds_reserve = 0;  // dynamic LDS that caps residency at one workgroup per CU
     bool structured = true;  // the Mamba kernels may take their structured-A path (device check)
+    // Long chunks (chunk_len >= kLocalMinChunk): the workspace also holds what the local-scan
+    // carries need (ScanArgs::ws_Hl, S_part, flags; ws_P then receives the prefix rescan's end
+    // states).  run_scan uses them for the exponential discretisations.
+    bool local = false;
+    size_t ws_Hl_off = 0, ws_S_off = 0, ws_F_off = 0;
 };
+// Local-scan carries: the prefix of every chunk >= 1 that is rescanned from its carried-in
+// state, and the shortest chunk for which the local-scan carries are used.
+constexpr int64_t kLocalPrefix = 4096;
+constexpr int64_t kLocalMinChunk = 4 * kLocalPrefix;
 
 // Per-thread error text (ssm_last_error).
 void set_error(const char *fmt, ...);

@@ -267,10 +267,11 @@ def test_parity_mamba1p4b_layer(ssm):
 
 @pytest.mark.timeout(900)
 def test_parity_million_token(ssm):
-    """Million-token scan: sampled channels over the whole length (chunk carries path)."""
+    """Million-token scan (the local-scan carries: 16 chunks of 65536 steps): 256 sampled
+    channels over all 2^20 steps, and h_last."""
     plan = ssm.scan_plan(1, 1 << 20, 1024, 16, "bf16")
-    assert plan["n_chunks"] > 1
-    _config_parity(ssm, "million_token", sample=48)
+    assert plan["n_chunks"] > 1 and plan["chunk_len"] >= 16384
+    _config_parity(ssm, "million_token", sample=256)
 
 
 @pytest.mark.parametrize("D,N,dt", [(128, 16, "bf16"), (70, 5, "f32")])
@@ -374,3 +375,59 @@ def test_structured_a_no_drift_fp32_long(ssm):
 def test_parity_mamba1p4b_layer_general_path(ssm):
     """The headline workload through the general path (one exp per state)."""
     _config_parity(ssm, "mamba1p4b_layer", general_a=True)
+
+
+# ---- long chunks: local scans + parallel carry combine + prefix rescan ---------------
+
+LOCAL = [
+    # B, L, D, dtype, gate, h0, disc, delta_scale, a_zero, chunk
+    (1, 40000, 64, "f32", True, True, "mamba", 1.0, False, 16384),
+    (2, 36000, 128, "bf16", True, False, "mamba", 1.0, False, 16384),
+    (1, 33000, 64, "f32", False, True, "zoh", 1.0, False, 16400),
+    # slowly decaying chunks (steps 5x smaller: about 18 of cumulative step over the 4096-step
+    # prefix, so the carried-in state is still ~1e-8 of itself there, far above the 2^-100
+    # cut): the combine flags the chunks and the continuation pass rescans the rest of them.
+    # (Much smaller steps make the fp32 recurrence's own rounding exceed the fp32 rule's 1e-5
+    # floor in every evaluation order, chunked or not.)
+    (1, 40000, 64, "f32", True, True, "mamba", 0.2, False, 16384),
+    (1, 34000, 128, "bf16", False, True, "mamba", 1.0, True, 16384),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("Bsz,L,D,dt,gate,h0,disc,dscale,azero,chunk", LOCAL)
+def test_local_scan_carries(ssm, Bsz, L, D, dt, gate, h0, disc, dscale, azero, chunk):
+    """Chunks of >= 16384 steps take the local-scan path (every chunk scanned from its own
+    start, carries folded by the parallel combine, the first 4096 steps of every later chunk
+    rescanned from its carried-in state, the rest only where that state has not died out).
+    Every output against the oracle, including the fallback (tiny steps, or A = 0 states:
+    no decay, so the carried-in state never dies out)."""
+    inp = synth.scan_inputs(Bsz, L, D, 16, dt, seed=800 + L, gate=gate, d_kind="normal", h0=h0)
+    if dscale != 1.0:
+        d = synth.to_f64(inp["delta"], dt) * dscale
+        inp["delta"] = synth.store(d.astype(np.float32), dt)
+    if azero:
+        A = inp["A"].copy()
+        A[::3, 0] = 0.0
+        inp["A"] = A
+    inp["discretization"] = disc
+    plan = ssm.scan_plan(Bsz, L, D, 16, dt, chunk_len=chunk)
+    assert plan["n_chunks"] > 1 and plan["chunk_len"] >= 16384
+    y, h = _run(ssm, inp, chunk_len=chunk, discretization=disc)
+    yr, hr = oracle.scan(inp)
+    _log(f"local-carries {Bsz}x{L}x{D} {dt} {disc} dscale={dscale} azero={azero}", assert_close(y, yr, dt))
+    # A = 0 states have no decay: their h_last is a plain sum of L terms, whose fp32 rounding
+    # (~sqrt(L) ulp of the partial sums) can exceed the fixed 1e-5 floor in any summation
+    # order.  Those entries are compared with the one-pass GPU result instead.
+    undecayed = np.broadcast_to(inp["A"] == 0.0, h.shape)
+    assert_close(h[~undecayed], hr[~undecayed], "f32", "h_last")
+    # the carry pass + full rescan (chunks under 16384 steps) on the same input
+    y2, h2 = _run(ssm, inp, chunk_len=16000, discretization=disc)
+    assert_close(y2, yr, dt)
+    assert_close(h2[~undecayed], hr[~undecayed], "f32", "h_last")
+    # and one pass over the whole sequence: the chunked results differ from it by rounding only
+    y1, h1 = _run(ssm, inp, chunk_len=L, discretization=disc)
+    if dt == "f32":
+        assert np.max(np.abs(y - y1)) <= 2e-5 * max(1.0, float(np.max(np.abs(y1))))
+    if undecayed.any():
+        assert np.max(np.abs(h - h1)[undecayed]) <= 1e-4 * max(1.0, float(np.max(np.abs(h1))))
