@@ -37,24 +37,28 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0   # dense bf16 matrix-core peak
 # VALU issue slots per second with packed FP32 off: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Algorithmic VALU slots per state update: mul (delta*A), v_exp_f32 (2 slots: it issues at
-# half the FMA rate on gfx950), mul (delta*x*B), fma (state), fma (readout)
-SLOTS_PER_UPDATE = 6.0
-# per (b, t, d): delta*x, D*x fma, gate: mul, exp (2), add, rcp (2), mul, mul
-SLOTS_PER_TOKEN_CHANNEL_GATED = 10.0
-SLOTS_PER_TOKEN_CHANNEL = 2.0
-# The other discretisations, per state update.  Zero-order hold: mul (s = delta*A*log2 e),
-# v_exp_f32 (2), fma ((e - 1) / A), mul (x*B), mul (by the factor), fma (state), fma
-# (readout) = 8; the series branch for small |delta A| and its select (6 more) are
-# accuracy work, not counted.  Bilinear: fma (1 - delta*A/2), v_rcp_f32 (2), mul
-# (delta*x*B), fma (2h + .), fma (r * . - h), fma (readout) = 7.
-SLOTS_PER_UPDATE_VARIANT = {"zoh": 8.0, "bilinear": 7.0}
-# The backward, per state update: the checkpoint pass (mul, v_exp_f32 (2), mul, fma = 5),
-# the reverse sweep's recompute (the same 5 + the readout fma = 6), its adjoint (fma
-# lam += C g0, mul g0 h, mul lam u, fma lam B, mul a h, mul + fma for the A term, mul + fma
-# for dA, mul lam *= a = 10) and the sums of the dB, dC terms over channels (2) = 23.
-# The per-(t, d) work (dx, ddelta, dz and the sums over the state groups) is not counted.
-SLOTS_PER_UPDATE_BWD = 23.0
+
+
+def slot_model(x_exp, x_rcp):
+    """Algorithmic VALU issue slots, with a v_exp_f32 costing x_exp and a v_rcp_f32 x_rcp FMA
+    slots (both measured by ssm_issue_probe at run time).
+
+    per state update, Mamba form, general A: mul (delta*A), exp, mul (delta*x*B), fma (state),
+        fma (readout) = 4 + x_exp; the structured-A path (what A = -(n+1) takes): half an exp
+        and half a mul per update (one per lane and step, two states), one mul by E, and the
+        three others = 4 + x_exp / 2, plus E staged once per (t, d): mul + exp;
+    per (b, t, d): delta*x, D*x fma, gate (mul, exp, add, rcp, mul, mul) = 6 + x_exp + x_rcp
+        (ungated: 2);
+    zero-order hold: mul, exp, fma ((e - 1) / A), mul (x*B), mul (by the factor), fma, fma
+        = 6 + x_exp (the series branch and its select are accuracy work, not counted);
+    bilinear: fma (1 - delta*A/2), rcp, mul (delta*x*B), fma (2h + .), fma (r * . - h), fma
+        (readout) = 5 + x_rcp;
+    backward: checkpoint pass (mul, exp, mul, fma), recompute (the same + readout fma), adjoint
+        (fma, mul, mul, fma, mul, mul + fma for the A term, mul + fma for dA, mul = 10) and the
+        sums of the dB, dC terms over channels (2) = 19 + 2 x_exp."""
+    return {"update": 4.0 + x_exp, "update_structured": 4.0 + x_exp / 2.0, "e_stage": 1.0 + x_exp,
+            "token_gated": 6.0 + x_exp + x_rcp, "token": 2.0,
+            "zoh": 6.0 + x_exp, "bilinear": 5.0 + x_rcp, "bwd": 19.0 + 2.0 * x_exp}
 
 
 def kernel_source_hash():
@@ -105,6 +109,10 @@ def main():
                     help="only run this many backward calls at the headline shape (for rocprofv3)")
     ap.add_argument("--profile-ssd", type=int, default=0, metavar="CALLS",
                     help="only run this many SSD (Mamba-2 layer) scans (for rocprofv3)")
+    ap.add_argument("--profile-long", type=int, default=0, metavar="CALLS",
+                    help="only run this many million-token scans (B1 L1048576 D1024 N16 bf16; for rocprofv3)")
+    ap.add_argument("--profile-decode-graph", type=int, default=0, metavar="REPLAYS",
+                    help="only replay the 1024-step decode graph this many times (for rocprofv3)")
     ap.add_argument("--profile-variant", choices=("zoh", "bilinear"), default=None,
                     help="with --profile-run: time this discretisation instead of the Mamba one")
     args = ap.parse_args()
@@ -145,6 +153,20 @@ def main():
     if args.profile_decode:
         profile_decode(torch, ssm, synth, dev, args.profile_decode)
         log(f"decode profile run: {args.profile_decode} steps")
+        return
+    if args.profile_long:
+        x, dl, A, Bm, Cm, Dk, y, ws = _long_inputs(torch, ssm, synth, dev)
+        for _ in range(args.profile_long):
+            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"million-token profile run: {args.profile_long} calls")
+        return
+    if args.profile_decode_graph:
+        run = _decode_graph(torch, ssm, synth, dev)
+        for _ in range(args.profile_decode_graph):
+            run()
+        torch.cuda.synchronize()
+        log(f"decode graph profile run: {args.profile_decode_graph} replays of 1024 steps")
         return
     if args.profile_bwd:
         c = synth.CONFIGS["mamba1p4b_layer"]
@@ -201,48 +223,85 @@ def main():
 
         disc = args.profile_variant if args.profile_run and args.profile_variant else "mamba"
 
-        def step():
-            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
+        def step(general=False):
+            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc, general_a=general)
+
+        # Issue rates of this GPU (fp32 FMA, v_exp_f32, v_rcp_f32): a transcendental costs
+        # fma_rate / its rate issue slots in the slot model of the roofline.
+        rates = ssm.issue_rates()
+        x_exp = rates["fma"] / rates["exp"]
+        x_rcp = rates["fma"] / rates["rcp"]
+        log(f"issue rates: fma {rates['fma']:.3e}, exp {rates['exp']:.3e}, rcp {rates['rcp']:.3e} lane-ops/s "
+            f"-> exp {x_exp:.2f}, rcp {x_rcp:.2f} FMA slots")
+        # Each timed launch follows an untimed 1 GiB write that evicts the L2s and the 256 MB
+        # Infinity Cache, so every launch reads its inputs from HBM.
+        flush = None if args.profile_run else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+        def timed(n, general=False, flushed=True, read_flush=False):
+            ms = []
+            for _ in range(n):
+                if flushed and flush is not None:
+                    if read_flush:
+                        flush.view(torch.int64).amax()   # evicts by reading: leaves no dirty lines
+                    else:
+                        flush.fill_(1)
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+                step(general)
+                b_.record()
+                ms.append((a_, b_))
+            torch.cuda.synchronize()
+            return sorted(a_.elapsed_time(b_) for a_, b_ in ms)
 
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
         steps = args.steps
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        for i in range(steps):
-            ev[i][0].record()
-            step()
-            ev[i][1].record()
-        torch.cuda.synchronize()
+        kms = timed(steps)
         elapsed = time.perf_counter() - t_start
-        kms = [s.elapsed_time(e) for s, e in ev]
+        k_med = kms[len(kms) // 2]
+        k_min = kms[0]
         k_avg = sum(kms) / len(kms)
-        k_min = min(kms)
-        ms_per_step = elapsed * 1e3 / steps
-        value = updates * steps / elapsed
+        ms_per_step = k_med
+        value = updates / (k_med * 1e-3)
         alg_bytes = scan_bytes(B, L, D, N, 2, True)
-        alg_slots = updates * SLOTS_PER_UPDATE + B * L * D * SLOTS_PER_TOKEN_CHANNEL_GATED
-        hbm_gbs = alg_bytes / (k_avg * 1e-3) / 1e9
-        alu_tslots = alg_slots / (k_avg * 1e-3) / 1e12
+        # algorithmic VALU slots: the structured-A path (what runs on this A = -(n+1)) takes one
+        # exp per lane and step for two states and one multiply for the other, plus E staged
+        # once per (t, d); the general path one exp per state update
+        spu_struct = 4.0 + x_exp / 2.0
+        spu_general = 4.0 + x_exp
+        per_td = 6.0 + x_exp + x_rcp            # delta*x, D*x, the gate (mul, exp, add, rcp, mul, mul)
+        alg_slots = updates * spu_struct + B * L * D * (per_td + 1.0 + x_exp)
+        alg_slots_general = updates * spu_general + B * L * D * per_td
+        hbm_gbs = alg_bytes / (k_med * 1e-3) / 1e9
+        alu_tslots = alg_slots / (k_med * 1e-3) / 1e12
         traffic = load_traffic("scan_B4_L4096_D4096_N16_bf16_gated", src_hash)
         roofline = {"bound": "alu", "achieved": round(alu_tslots, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                     "unit": "Tslot/s", "frac": round(alu_tslots / VALU_PEAK_TSLOTS, 4),
                     "traffic": traffic,
-                    "kernel": "scan_kernel<bf16, G=%d, TB=%d, gated>" % (plan["states_per_lane"], plan["time_block"]),
-                    "kernel_ms_avg": round(k_avg, 5), "kernel_ms_min": round(k_min, 5),
+                    "kernel": "scan_fast_kernel<mamba, bf16, G=%d, gated> + bc_pack" % plan["states_per_lane"],
+                    "path": "structured A (one exp per lane and step)",
+                    "kernel_ms_median": round(k_med, 5), "kernel_ms_min": round(k_min, 5),
+                    "kernel_ms_avg": round(k_avg, 5),
                     "alg_slots_per_launch": alg_slots, "alg_bytes_per_launch": alg_bytes,
+                    "slot_model": {"exp_slots_measured": round(x_exp, 3), "rcp_slots_measured": round(x_rcp, 3),
+                                   "slots_per_update": round(spu_struct, 3),
+                                   "slots_per_token_channel": round(per_td + 1.0 + x_exp, 3),
+                                   "issue_rates_lane_ops_per_s": {k: float("%.4g" % v) for k, v in rates.items()}},
                     "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}}
-        log(f"scan: {k_avg * 1e3:.1f} us/launch avg ({k_min * 1e3:.1f} min), {value:.3e} updates/s, "
+        log(f"scan (flushed): {k_med * 1e3:.1f} us/launch median ({k_min * 1e3:.1f} min), {value:.3e} updates/s, "
             f"HBM {hbm_gbs:.0f} GB/s ({hbm_gbs / HBM_PEAK_GBS:.1%}), VALU {alu_tslots / VALU_PEAK_TSLOTS:.1%}")
         result.update({
             "metric": "state-updates/s (B*L*D*N), scan B4 L4096 D4096 N16",
             "value": value, "unit": "state-updates/s", "n_gpus": 1, "steps": steps,
             "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "dtype_note": "the arithmetic and the state are fp32; x, delta, z, B, C and y are stored as bf16",
+            "timing": "median of the timed launches, each between two events on the launch stream and each "
+                      "after an untimed 1 GiB write (L2 and Infinity Cache evicted); value = B*L*D*N / median",
             "data": "synthetic (seeded generator: x,z,B,C ~ N(0,1), delta log-uniform [1e-3,1e-1], "
                     "A=-(n+1), D ~ N(1,0.1))",
             "config": {"workload": cfg["name"], "batch": B, "seqlen": L, "dim": D, "dstate": N,
@@ -252,20 +311,14 @@ def main():
             "source_hash": src_hash,
         })
         if not args.profile_run:
-            # Cold-cache launches: each preceded by an untimed 1 GiB write that evicts the L2s
-            # and the 256 MB Infinity Cache.  And a plain device copy for the HBM bandwidth
-            # this box reaches.
-            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-            cold = []
-            for _ in range(10):
-                flush.fill_(1)
-                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a_.record()
-                step()
-                b_.record()
-                torch.cuda.synchronize()
-                cold.append(a_.elapsed_time(b_))
-            cold.sort()
+            # the general path (one exp per state: what a trained, unstructured A takes), and the
+            # warm figure: launches back to back, nothing evicted in between
+            gms = timed(steps, general=True)
+            g_med = gms[len(gms) // 2]
+            wms = timed(steps, flushed=False)
+            w_med = wms[len(wms) // 2]
+            rms = timed(steps, read_flush=True)
+            r_med = rms[len(rms) // 2]
             dst = torch.empty_like(flush)
             cp = []
             for _ in range(5):
@@ -277,10 +330,24 @@ def main():
                 cp.append(a_.elapsed_time(b_))
             copy_gbs = 2 * (1 << 30) / (min(cp) * 1e-3) / 1e9
             result_extra = {
-                "cold_cache": {"kernel_ms_median": round(cold[len(cold) // 2], 5), "kernel_ms_min": round(cold[0], 5),
-                               "note": "each launch after an untimed 1 GiB write (L2 and Infinity Cache evicted)"},
+                "general_a_path": {
+                    "kernel_ms_median": round(g_med, 5), "state_updates_per_s": updates / (g_med * 1e-3),
+                    "roofline": {"bound": "alu", "achieved": round(alg_slots_general / (g_med * 1e-3) / 1e12, 3),
+                                 "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
+                                 "frac": round(alg_slots_general / (g_med * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+                                 "slots_per_update": round(spu_general, 3),
+                                 "hbm_frac": round(alg_bytes / (g_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                    "note": "ssm_scan_opts.a_structure = -1: one exp per state update, the path any A without "
+                            "the structure takes; same flushed protocol"},
+                "warm": {"kernel_ms_median": round(w_med, 5), "state_updates_per_s": updates / (w_med * 1e-3),
+                         "note": "launches back to back, no eviction in between"},
+                "read_flushed": {"kernel_ms_median": round(r_med, 5), "state_updates_per_s": updates / (r_med * 1e-3),
+                                 "note": "each launch after an untimed 1 GiB read instead of the write: caches "
+                                         "evicted without leaving dirty lines to write back"},
                 "copy_probe": {"GB/s": round(copy_gbs, 1), "note": "1 GiB device-to-device copy, read + write bytes"}}
-            log(f"cold cache: {cold[len(cold) // 2] * 1e3:.1f} us median; copy probe {copy_gbs:.0f} GB/s")
+            log(f"general path (flushed): {g_med * 1e3:.1f} us median; warm: {w_med * 1e3:.1f} us median; "
+                f"read-flushed: {r_med * 1e3:.1f} us median; "
+                f"copy probe {copy_gbs:.0f} GB/s")
             del flush, dst
         else:
             result_extra = {}
@@ -312,7 +379,10 @@ def main():
             del xs, ds, zs
 
     if not args.no_secondary:
-        result["secondary"] = secondary(torch, ssm, synth, dev, log, src_hash)
+        if args.secondary_only:
+            rates = ssm.issue_rates()
+        sm = slot_model(rates["fma"] / rates["exp"], rates["fma"] / rates["rcp"])
+        result["secondary"] = secondary(torch, ssm, synth, dev, log, src_hash, sm)
 
     print(json.dumps(result), flush=True)
 
@@ -409,7 +479,55 @@ def profile_decode(torch, ssm, synth, dev, steps):
     torch.cuda.synchronize()
 
 
-def secondary(torch, ssm, synth, dev, log, src_hash):
+def _long_inputs(torch, ssm, synth, dev):
+    """The million-token layer's input (B1 L1048576 D1024 N16 bf16), drawn on the GPU."""
+    c = synth.CONFIGS["million_token"]
+    Bsz, L, D, N = c["batch"], c["seqlen"], c["dim"], c["dstate"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    bf = torch.bfloat16
+    x, dl = _randn((Bsz, L, D), gen, dev, bf), _delta((Bsz, L, D), gen, dev, bf)
+    Bm, Cm = _randn((Bsz, L, N), gen, dev, bf), _randn((Bsz, L, N), gen, dev, bf)
+    A = torch.from_numpy(synth.make_A(3, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(3, D, "normal")).to(dev)
+    ws = torch.empty(max(ssm.scan_plan(Bsz, L, D, N, "bf16")["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+    return x, dl, A, Bm, Cm, Dk, torch.empty_like(x), ws
+
+
+def _decode_graph(torch, ssm, synth, dev):
+    """A HIP graph of the decode workload's 1024 gated steps on h [256, 4096, 16] fp32 from
+    zero; returns a function that zeroes h and replays it."""
+    c = synth.CONFIGS["decode"]
+    Bsz, D, N, S = c["batch"], c["dim"], c["dstate"], c["seqlen"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    bf = torch.bfloat16
+    A = torch.from_numpy(synth.make_A(4, D, N)).to(dev)
+    Dk = torch.from_numpy(synth.make_D(4, D, "normal")).to(dev)
+    xs, ds, zs = _randn((S, Bsz, D), gen, dev, bf), _delta((S, Bsz, D), gen, dev, bf), _randn((S, Bsz, D), gen, dev, bf)
+    Bs, Cs = _randn((S, Bsz, N), gen, dev, bf), _randn((S, Bsz, N), gen, dev, bf)
+    h = torch.zeros((Bsz, D, N), device=dev)
+    y = torch.empty((Bsz, D), dtype=bf, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ssm.state_update(h, xs[0], ds[0], A, Bs[0], Cs[0], Dk, zs[0], out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(S):
+            ssm.state_update(h, xs[s], ds[s], A, Bs[s], Cs[s], Dk, zs[s], out=y)
+    keep = (xs, ds, zs, Bs, Cs, A, Dk, y)
+
+    def run():
+        h.zero_()
+        graph.replay()
+        return keep
+    return run
+
+
+def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     """Decode (1024 steps) and the million-token chunked scan.  Inputs drawn on the
     GPU with torch's seeded generator, same distributions as the headline input."""
     out = {}
@@ -532,7 +650,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         vt.sort()
         ms = vt[len(vt) // 2]
         upd = Bsz * L * D * N
-        slots = upd * SLOTS_PER_UPDATE_VARIANT[disc] + Bsz * L * D * SLOTS_PER_TOKEN_CHANNEL_GATED
+        slots = upd * sm[disc] + Bsz * L * D * sm["token_gated"]
         ts = slots / (ms * 1e-3) / 1e12
         out["variants"][disc] = {
             "workload": c["name"] + f", {disc} discretisation",
@@ -691,14 +809,14 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     bt.sort()
     ms = bt[len(bt) // 2]
     upd = Bsz * L * D * N
-    bwd_ts = upd * SLOTS_PER_UPDATE_BWD / (ms * 1e-3) / 1e12
+    bwd_ts = upd * sm["bwd"] / (ms * 1e-3) / 1e12
     out["backward"] = {
         "workload": c["name"] + " backward (dx, ddelta, dz, dB, dC, dA, dD)",
         "ms_median": round(ms, 4), "ms_min": round(bt[0], 4),
         "state_updates_per_s": upd / (ms * 1e-3),
         "roofline": {"bound": "alu", "achieved": round(bwd_ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "Tslot/s", "frac": round(bwd_ts / VALU_PEAK_TSLOTS, 4),
-                     "alg_slots_per_launch": upd * SLOTS_PER_UPDATE_BWD},
+                     "alg_slots_per_launch": upd * sm["bwd"]},
         "timing": "median of 5 calls (checkpoint pass, reverse sweep, reductions), each between two events",
         "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
     }
@@ -810,12 +928,16 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
     ms = sum(a.elapsed_time(b) for a, b in ev) / reps
     upd = Bsz * L * D * N
     byts = scan_bytes(Bsz, L, D, N, 2, False)
-    slots = upd * SLOTS_PER_UPDATE + Bsz * L * D * SLOTS_PER_TOKEN_CHANNEL
+    slots = upd * sm["update_structured"] + Bsz * L * D * (sm["token"] + sm["e_stage"])
     out["long_sequence"] = {
         "workload": c["name"], "state_updates_per_s": upd / (ms * 1e-3), "ms_per_call": ms,
         "plan": plan, "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "alu_frac_single_pass_work": round(slots / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
-        "note": "all launches of one call (carry pass, combine, rescan) inside the events",
+        "workspace_bytes": plan["workspace_bytes"],
+        "note": "all launches of one call inside the events: B/C pre-pass, every chunk scanned from its own "
+                "start, the carry combine (a parallel scan over chunks), the 4096-step prefix of every later "
+                "chunk rescanned from its carried-in state, and the continuation launch (whose workgroups exit "
+                "at once: no chunk's carried-in state survives its prefix on this input)",
     }
     log(f"long sequence: {ms:.2f} ms/call, {upd / (ms * 1e-3):.3e} updates/s, plan {plan}")
     # oracle beside it: 16 channels over the whole million steps
@@ -845,13 +967,13 @@ def secondary(torch, ssm, synth, dev, log, src_hash):
         bt.append(a_e.elapsed_time(b_e))
     bt.sort()
     ms = bt[len(bt) // 2]
-    bwd_ts = upd * SLOTS_PER_UPDATE_BWD / (ms * 1e-3) / 1e12
+    bwd_ts = upd * sm["bwd"] / (ms * 1e-3) / 1e12
     out["long_sequence_backward"] = {
         "workload": c["name"] + " backward (dx, ddelta, dB, dC, dA, dD)",
         "ms_median": round(ms, 3), "state_updates_per_s": upd / (ms * 1e-3),
         "roofline": {"bound": "alu", "achieved": round(bwd_ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "Tslot/s", "frac": round(bwd_ts / VALU_PEAK_TSLOTS, 4),
-                     "alg_slots_per_launch": upd * SLOTS_PER_UPDATE_BWD},
+                     "alg_slots_per_launch": upd * sm["bwd"]},
         "timing": "median of 3 calls, each between two events",
         "note": "chunks of the forward planner (16 x 65536 steps): chunked checkpoint pass, adjoint carries and "
                 "their combine, reverse sweep per chunk; the carry passes are not counted as algorithmic work",

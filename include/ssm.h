@@ -125,6 +125,20 @@ typedef struct ssm_scan_plan {
     uint64_t lds_reserve;    /* extra LDS bytes per workgroup that keep one workgroup per CU (0 = none) */
 } ssm_scan_plan;
 
+/*
+ * Issue-rate probe (measurement only; the scan does not call it).  Launches `workgroups`
+ * workgroups of `waves_per_workgroup` waves in which every lane runs 8 independent chains of
+ * `iters` operations: op 0 an fp32 FMA, op 1 v_exp_f32, op 2 v_rcp_f32.  The caller times the
+ * launch on `stream` (e.g. with events) and divides 64 * waves * workgroups * 8 * iters by
+ * the time.  Whether the scan is bound by memory (as the skill page "State Space Models
+ * Mamba" has it in its "SSM vs Transformer" table and Common Pitfalls) or by the ALU turns
+ * on these rates: a state update is one exp plus four multiplies or FMAs.  `sink` is a
+ * device buffer of at least 64 * waves_per_workgroup floats that the kernel may write.
+ * Returns SSM_EINVAL for out-of-range arguments.
+ */
+int ssm_issue_probe(int op, int64_t workgroups, int64_t waves_per_workgroup, int64_t iters, float *sink,
+                    void *stream);
+
 /* ABI version of the loaded library (SSM_ABI_VERSION at build time). */
 int ssm_abi_version(void);
 
@@ -300,9 +314,9 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   workspace device memory of ssm_scan_bwd_workspace_bytes(..., checkpoints != NULL)
  *             bytes (partial sums, and without saved checkpoints the checkpoints)
  *
- * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  batch or dim
- * == 0 is a no-op; seqlen == 0 sets dh0 = dh_last (or zeros) and dA, dD, ddelta_bias
- * to zero.
+ * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  dim == 0 is a
+ * no-op; batch == 0 or seqlen == 0 sets dA, dD, ddelta_bias to zero (and, with seqlen ==
+ * 0, dh0 = dh_last or zeros).
  * Deterministic: every reduction runs in a fixed order.
  */
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
@@ -359,7 +373,7 @@ size_t ssm_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim
  *   dstate    [batch, dim, width-1]  dtype   NULL = not computed (allowed with state_in NULL:
  *             the gradient of a zero starting state)
  *   workspace device memory of ssm_conv1d_bwd_workspace_bytes() bytes (per-tile sums)
- * seqlen == 0 sets dw, dbias, dstate to zero; batch or dim == 0 is a no-op.
+ * batch == 0 or seqlen == 0 sets dw, dbias, dstate to zero; dim == 0 is a no-op.
  * Deterministic: the sums run in a fixed order.
  */
 int ssm_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,

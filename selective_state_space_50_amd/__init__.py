@@ -88,6 +88,8 @@ def lib():
     L.ssm_scan_fwd.restype = I32
     L.ssm_scan_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, P, P, P, P, I32,
                                ctypes.POINTER(Variant), ctypes.POINTER(ScanOpts), P, SZ, P]
+    L.ssm_issue_probe.restype = I32
+    L.ssm_issue_probe.argtypes = [I32, I64, I64, I64, P, P]
     L.ssm_noalloc_scratch_bytes.restype = SZ
     L.ssm_noalloc_scratch_bytes.argtypes = []
     L.ssm_scan_fwd_noalloc.restype = I32
@@ -288,6 +290,31 @@ def scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softpl
                                     ctypes.byref(o) if o else None, ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_scan_fwd_noalloc")
     return (out, h_last) if h_last is not None else out
+
+
+def issue_rates(workgroups=256, waves_per_workgroup=16, iters=4096, reps=5):
+    """Measured VALU issue rates (lane operations per second) of an fp32 FMA, v_exp_f32 and
+    v_rcp_f32 on the current GPU (ssm_issue_probe, timed with events; median of reps)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    sink = torch.empty(64 * waves_per_workgroup, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    ops = workgroups * waves_per_workgroup * 64 * 8 * iters
+    out = {}
+    for op, name in ((0, "fma"), (1, "exp"), (2, "rcp")):
+        times = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            _check(lib().ssm_issue_probe(op, workgroups, waves_per_workgroup, iters, _ptr(sink),
+                                         ctypes.c_void_p(s.cuda_stream)), "ssm_issue_probe")
+            e1.record(s)
+            e1.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        times.sort()
+        out[name] = ops / (times[len(times) // 2] * 1e-3)
+    return out
 
 
 def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_softplus=False,

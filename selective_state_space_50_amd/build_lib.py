@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libssm.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("ssm_api.hip", "scan_fast.hip", "scan_fast_zoh.hip", "scan_fast_bilinear.hip",
             "scan_generic.hip", "scan_generic_zoh.hip", "scan_generic_bilinear.hip", "decode.hip",
-            "scan_bwd.hip", "conv1d.hip", "ssd.hip", "ssm_host.cpp")]
+            "scan_bwd.hip", "conv1d.hip", "ssd.hip", "probe.hip", "ssm_host.cpp")]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -415,12 +415,12 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
                             dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization,
                             delta_bias, ddelta_bias, checkpoints, workspace, workspace_bytes, &p);
     if (st != SSM_OK) return st;
-    if (batch == 0 || dim == 0) return SSM_OK;
+    if (dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (seqlen == 0) {
-        // no steps: dh0 = dh_last, and the reductions over steps are zero
-        if (dh0) {
+    if (batch == 0 || seqlen == 0) {
+        // no rows or no steps: dh0 = dh_last, and the reductions over rows and steps are zero
+        if (dh0 && batch > 0) {
             const int64_t n = batch * dim * dstate;
             hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                                0, s, dh0, dh_last, n);
@@ -540,12 +540,12 @@ extern "C" int ssm_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_
     int st = check_conv1d_bwd(batch, seqlen, dim, width, dtype, x, w, bias, state_in, dy, dx, dw, dbias, dstate,
                               silu, workspace, workspace_bytes);
     if (st != SSM_OK) return st;
-    if (batch == 0 || dim == 0) return SSM_OK;
+    if (dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (width == 1) dstate = nullptr;
     hipError_t e;
-    if (seqlen == 0) {
-        // no steps: every gradient is zero
+    if (batch == 0 || seqlen == 0) {
+        // no rows or no steps: every gradient is zero
         auto zero = [&](void *p, int64_t bytes) {
             if (!p || bytes <= 0) return hipSuccess;
             const int64_t n = bytes / 2;

@@ -443,10 +443,11 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
         set_error("discretization=%d is not an ssm_discretization", discretization);
         return SSM_EINVAL;
     }
-    if (batch == 0 || dim == 0) return SSM_OK;
+    // with batch == 0 the parameter gradients (dA, dD, ddelta_bias) are still written: zeros
+    if (dim == 0) return SSM_OK;
     const char *missing = !A ? "A" : !dA ? "dA" : (z && !dz) ? "dz (z is given)" : (Dskip && !dD) ? "dD (Dskip is given)" :
                           (delta_bias && !ddelta_bias) ? "ddelta_bias (delta_bias is given)" : nullptr;
-    if (!missing && seqlen > 0)
+    if (!missing && seqlen > 0 && batch > 0)
         missing = !x ? "x" : !delta ? "delta" : !B ? "B" : !C ? "C" : !dy ? "dy" : !dx ? "dx" :
                   !ddelta ? "ddelta" : !dB ? "dB" : !dC ? "dC" : nullptr;
     if (missing) {
@@ -596,9 +597,10 @@ int check_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, 
                   (long long)batch, (long long)seqlen, kConvBwdTile);
         return SSM_EUNSUPPORTED;
     }
-    if (batch == 0 || dim == 0) return SSM_OK;
-    const char *missing = !w ? "w" : !dw ? "dw" : (seqlen > 0 && !x) ? "x" : (seqlen > 0 && !dy) ? "dy" :
-                          (seqlen > 0 && !dx) ? "dx" : nullptr;
+    // with batch == 0 the filter gradients (dw, dbias) are still written: zeros
+    if (dim == 0) return SSM_OK;
+    const bool rows = seqlen > 0 && batch > 0;
+    const char *missing = !w ? "w" : !dw ? "dw" : (rows && !x) ? "x" : (rows && !dy) ? "dy" : (rows && !dx) ? "dx" : nullptr;
     if (missing) {
         set_error("required pointer %s is NULL", missing);
         return SSM_EINVAL;

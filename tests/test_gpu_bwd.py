@@ -125,6 +125,14 @@ def test_backward_empty_and_unsupported(ssm):
                      Dk, None, None, x, hl, delta_bias=bias)
     torch.cuda.synchronize()
     assert float(g["ddelta_bias"].abs().sum()) == 0.0
+    # no rows: the parameter gradients are written, as zeros, over whatever the buffers held
+    x0 = torch.zeros((0, 5, 64), device="cuda")
+    b0 = torch.zeros((0, 5, 16), device="cuda")
+    g = ssm.scan_bwd(x0, x0, A, b0, b0, Dk, None, None, x0, None, delta_bias=bias)
+    torch.cuda.synchronize()
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert g[k] is not None and float(g[k].abs().sum()) == 0.0, k
+    assert g["dh0"].numel() == 0
     xs = torch.zeros((1, 4, 96), device="cuda")
     with pytest.raises(ssm.SSMError) as e:
         ssm.scan_bwd(xs, xs, torch.zeros((96, 16), device="cuda"), torch.zeros((1, 4, 16), device="cuda"),

@@ -158,6 +158,11 @@ def test_conv_bwd_empty_sequence(ssm):
     torch.cuda.synchronize()
     assert float(g["dw"].abs().sum()) == 0.0 and float(g["dbias"].abs().sum()) == 0.0
     assert float(g["dstate"].float().abs().sum()) == 0.0
+    # no rows: dw and dbias are written as zeros
+    x0 = torch.zeros((0, 6, 8), dtype=torch.bfloat16, device="cuda")
+    g = ssm.conv1d_bwd(x0, w, torch.ones(8, device="cuda"), None, x0)
+    torch.cuda.synchronize()
+    assert float(g["dw"].abs().sum()) == 0.0 and float(g["dbias"].abs().sum()) == 0.0
 
 
 @pytest.mark.timeout(600)
