@@ -93,29 +93,36 @@ __device__ __forceinline__ float quad_sum(float v) {
 }
 
 // dstate == 16, dim % 64 == 0: block = 64 channels of one batch row, 4 lanes per channel.
+// Every load is issued before the first use (z and D included, so no wave ends on a
+// dependent load), and the state moves with 16-byte buffer loads and stores carrying the
+// non-temporal hint: steps replayed back to back ran about 12% faster with the hint on
+// both the load and the store of h than with neither.
 template <int DISC, typename T, bool HAS_Z>
 __global__ void __launch_bounds__(256) state_update_q16_kernel(UpdArgs a) {
     constexpr int N = 16;
+    constexpr int kNT = 2;              // cache policy bits: non-temporal
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int tid = threadIdx.x;
     const int sub = tid & 3;            // states 4*sub .. 4*sub+3
     const int cl = tid >> 2;            // channel within the block
     const int64_t ch0 = static_cast<int64_t>(blockIdx.x) * 64;
     const int64_t b = ch0 / a.D;        // uniform
     const int64_t dblk = ch0 - b * a.D;
-    const uint32_t so = static_cast<uint32_t>(cl * N + sub * 4);   // lane offset into [64][16]
-    float *hb = a.h + ch0 * N;
+    const int so = (cl * N + sub * 4) * 4;   // lane byte offset into the block's [64][16] fp32 state
+    const auto rH = __builtin_amdgcn_make_buffer_rsrc(a.h + ch0 * N, 0, 64 * N * 4, 0x00020000);
     const float *Ab = a.A + dblk * N;
-    const T *X = static_cast<const T *>(a.x) + ch0;
-    const T *DL = static_cast<const T *>(a.delta) + ch0;
-    float hv[4], av[4], bv[4], cv[4];
-    load4(hb + so, hv);
-    load4(Ab + so, av);
+    const u32x4 hr = __builtin_amdgcn_raw_buffer_load_b128(rH, so, 0, kNT);
+    float av[4], bv[4], cv[4];
+    load4(Ab + so / 4, av);
     load4(static_cast<const T *>(a.Bm) + b * N + sub * 4, bv);
     load4(static_cast<const T *>(a.Cm) + b * N + sub * 4, cv);
-    const float xv = widen(X, cl);
-    float dv = widen(DL, cl) + (a.dbias ? a.dbias[dblk + cl] : 0.0f);
+    const float xv = widen(static_cast<const T *>(a.x) + ch0, cl);
+    float dv = widen(static_cast<const T *>(a.delta) + ch0, cl) + (a.dbias ? a.dbias[dblk + cl] : 0.0f);
+    const float zv = HAS_Z ? widen(static_cast<const T *>(a.z) + ch0, cl) : 0.0f;
+    const float dsk = a.Dskip ? a.Dskip[dblk + cl] : 0.0f;
     if (a.softplus) dv = softplus_f(dv);
     const float u = DISC == kZOH ? xv : dv * xv;
+    float hv[4] = {__uint_as_float(hr.x), __uint_as_float(hr.y), __uint_as_float(hr.z), __uint_as_float(hr.w)};
     float yp = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -123,12 +130,12 @@ __global__ void __launch_bounds__(256) state_update_q16_kernel(UpdArgs a) {
         hv[g] = disc_step<DISC>(hv[g], dv, u, bv[g], av[g] * kLog2e, disc_aux<DISC>(av[g]), ab);
         yp = __builtin_fmaf(cv[g], hv[g], yp);
     }
-    *reinterpret_cast<float4 *>(hb + so) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    const u32x4 hw = {__float_as_uint(hv[0]), __float_as_uint(hv[1]), __float_as_uint(hv[2]), __float_as_uint(hv[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(hw, rH, so, 0, kNT);
     yp = quad_sum(yp);
     if (sub == 0) {
-        float yv = yp;
-        if (a.Dskip) yv = __builtin_fmaf(a.Dskip[dblk + cl], xv, yv);
-        if (HAS_Z) yv *= silu_f(widen(static_cast<const T *>(a.z) + ch0, cl));
+        float yv = a.Dskip ? __builtin_fmaf(dsk, xv, yp) : yp;
+        if (HAS_Z) yv *= silu_f(zv);
         put(static_cast<T *>(a.y) + ch0, cl, yv);
     }
 }
