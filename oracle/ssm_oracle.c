@@ -177,13 +177,17 @@ static void one_channel(const job_t *J, int64_t c)
 static void *worker(void *arg)
 {
     job_t *J = (job_t *)arg;
+    /* channels are handed out in runs, so short series do not queue on the lock */
+    const int64_t run = J->L * (J->N + 1) >= 4096 ? 1 : 256;
     for (;;) {
         pthread_mutex_lock(&J->lock);
-        const int64_t c = J->next++;
+        const int64_t c0 = J->next;
+        J->next += run;
         pthread_mutex_unlock(&J->lock);
-        if (c >= J->nchan)
+        if (c0 >= J->nchan)
             break;
-        one_channel(J, c);
+        for (int64_t c = c0; c < c0 + run && c < J->nchan; ++c)
+            one_channel(J, c);
     }
     return NULL;
 }
@@ -352,13 +356,16 @@ static void one_channel_bwd(const bjob_t *J, int64_t c)
 static void *worker_bwd(void *arg)
 {
     bjob_t *J = (bjob_t *)arg;
+    const int64_t run = J->L * (J->N + 1) >= 4096 ? 1 : 256;
     for (;;) {
         pthread_mutex_lock(&J->lock);
-        const int64_t c = J->next++;
+        const int64_t c0 = J->next;
+        J->next += run;
         pthread_mutex_unlock(&J->lock);
-        if (c >= J->nchan)
+        if (c0 >= J->nchan)
             break;
-        one_channel_bwd(J, c);
+        for (int64_t c = c0; c < c0 + run && c < J->nchan; ++c)
+            one_channel_bwd(J, c);
     }
     return NULL;
 }

@@ -70,8 +70,9 @@ def test_scan_equals_steps(ssm):
 
 @pytest.mark.timeout(1200)
 def test_parity_decode_1024_steps(ssm):
-    """h [256, 4096, 16] fp32 from zero, 1024 gated bf16 steps; every step's y on sampled
-    channels, and the final state on those channels."""
+    """h [256, 4096, 16] fp32 from zero, 1024 gated bf16 steps: the oracle runs every
+    channel, so every step's y is compared on all 1,048,576 channels and the final state
+    on all 16,777,216 states."""
     import torch
     c = synth.CONFIGS["decode"]
     Bsz, D, N, steps = c["batch"], c["dim"], c["dstate"], c["seqlen"]
@@ -79,23 +80,20 @@ def test_parity_decode_1024_steps(ssm):
     Dk = synth.make_D(4, D, "normal")
     At, Dt = torch.from_numpy(A).cuda(), torch.from_numpy(Dk).cuda()
     h = torch.zeros((Bsz, D, N), device="cuda")
-    ch = sample_channels(Bsz, D, 256)
-    cb = np.array([b for b, _ in ch]); cd = np.array([d for _, d in ch])
-    h_ref = np.zeros((len(ch), N))
+    h_ref = np.zeros((Bsz, D, N))
+    threads = oracle.default_threads()
     worst = 0.0
     for s in range(steps):
         step = synth.decode_step_inputs(4, s, Bsz, D, N, "bf16")
         t = _step_dev(step, "bf16")
         y = ssm.state_update(h, t["x"], t["delta"], At, t["B"], t["C"], Dt, t["z"])
-        h_ref, y_ref = oracle.state_update(h_ref, step, A, Dk, "bf16", channels=ch, nthreads=4)
-        yg = to_host(y)[cb, cd]
-        st = assert_close(yg, y_ref, "bf16", f"y step {s}")
+        h_ref, y_ref = oracle.state_update(h_ref, step, A, Dk, "bf16", nthreads=threads)
+        st = assert_close(to_host(y), y_ref, "bf16", f"y step {s}")
         worst = max(worst, st["worst_ratio"])
-        if s % 256 == 0:
+        if s % 128 == 0:
             print(f"[parity] decode step {s}: worst ratio so far {worst:.3f}", flush=True)
     torch.cuda.synchronize()
-    hg = to_host(h)[cb, cd]
-    st = assert_close(hg, h_ref, "f32", "h after 1024 steps")
+    st = assert_close(to_host(h), h_ref, "f32", "h after 1024 steps")
     print(f"[parity] decode 1024 steps ok: y worst ratio {worst:.3f}, h {st}", flush=True)
 
 
