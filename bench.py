@@ -115,6 +115,8 @@ def main():
                     help="only replay the 1024-step decode graph this many times (for rocprofv3)")
     ap.add_argument("--profile-variant", choices=("zoh", "bilinear"), default=None,
                     help="with --profile-run: time this discretisation instead of the Mamba one")
+    ap.add_argument("--profile-general", action="store_true",
+                    help="with --profile-run: time the general-A path (one exp per state update)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -259,7 +261,7 @@ def main():
         steps = args.steps
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        kms = timed(steps)
+        kms = timed(steps, general=args.profile_run and args.profile_general)
         elapsed = time.perf_counter() - t_start
         k_med = kms[len(kms) // 2]
         k_min = kms[0]
