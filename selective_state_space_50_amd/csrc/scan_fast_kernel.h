@@ -178,17 +178,27 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     const bool helper = w >= NC;        // wave-uniform role: not a compute wave
     const bool pfw = has_prefetch_wave<G>() && w >= NC + helper_waves<G>();
     const int64_t D = a.D, L = a.L;
-    const int64_t b = blockIdx.y;
-    const int64_t c = blockIdx.z + a.c_first;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
+    // The hardware deals workgroups to the 8 XCDs in turn by linear id.  Renumber them so
+    // that each XCD takes a contiguous run of (channel group, row, chunk) tiles: the channel
+    // groups of one row and chunk then read their packed B/C through one XCD's L2 instead
+    // of every XCD fetching it.  (Only when the count divides evenly, so the map is a
+    // permutation.)
+    const int64_t gx = gridDim.x, gxy = gx * gridDim.y;
+    const int64_t nwg = gxy * gridDim.z;
+    int64_t lin = blockIdx.x + gx * blockIdx.y + gxy * blockIdx.z;
+    if (nwg % 8 == 0) lin = (lin % 8) * (nwg / 8) + lin / 8;
+    const int64_t bx = lin % gx;
+    const int64_t b = (lin % gxy) / gx;
+    const int64_t c = lin / gxy + a.c_first;
+    const int64_t d0 = bx * 64;
     const int64_t cs = c * a.chunk_len;                                // the chunk's first step
     const int64_t ce = (cs + a.chunk_len < L) ? cs + a.chunk_len : L;  // and its end
     const int64_t t0 = cs + a.t_off;                                   // this launch's steps [t0, t1)
     const int64_t t1 = (a.t_span > 0 && t0 + a.t_span < ce) ? t0 + a.t_span : ce;
     const int64_t nblk = t1 > t0 ? (t1 - t0 + kTB - 1) / kTB : 0;
     // a continuation launch runs only the chunks whose flag the carry combine set
-    if (a.flag_in && a.flag_in[(b * (a.n_chunks - 1) + c - 1) * gridDim.x + blockIdx.x] == 0) return;
-    if (a.flags && c > 0 && threadIdx.x == 0) a.flags[(b * (a.n_chunks - 1) + c - 1) * gridDim.x + blockIdx.x] = 0;
+    if (a.flag_in && a.flag_in[(b * (a.n_chunks - 1) + c - 1) * gx + bx] == 0) return;
+    if (a.flags && c > 0 && threadIdx.x == 0) a.flags[(b * (a.n_chunks - 1) + c - 1) * gx + bx] = 0;
 
     // ---- compute-wave state: G states of channel d0 + lane, A scaled by log2(e), the
     // discretisation's second per-state constant, and (bilinear carries) the running
