@@ -268,7 +268,8 @@ int ssm_scan_fwd_save(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
 
 /* Host-only: bytes of device workspace ssm_scan_bwd needs for this shape (0 when
  * nothing is computed, or the shape is invalid or unsupported); with
- * saved_checkpoints != 0, for a call given checkpoints (less: no checkpoint pass). */
+ * saved_checkpoints != 0, for a call given checkpoints (less: no checkpoint pass).  For
+ * shapes other than dstate 16 with dim a multiple of 64 it includes the padded copies. */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                     int dtype, int saved_checkpoints);
 
@@ -314,9 +315,12 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   workspace device memory of ssm_scan_bwd_workspace_bytes(..., checkpoints != NULL)
  *             bytes (partial sums, and without saved checkpoints the checkpoints)
  *
- * dstate must be 16 and dim a multiple of 64, else SSM_EUNSUPPORTED.  dim == 0 is a
- * no-op; batch == 0 or seqlen == 0 sets dA, dD, ddelta_bias to zero (and, with seqlen ==
- * 0, dh0 = dh_last or zeros).
+ * Any 1 <= dstate <= 16 and any dim.  dstate == 16 with dim a multiple of 64 runs the
+ * native kernels in place; other shapes run them on copies padded (in the workspace) to
+ * the next multiple of 64 channels and to 16 states, whose padding carries x = 0 and
+ * B = C = 0 and so adds nothing to any gradient; those shapes take no saved
+ * checkpoints (SSM_EUNSUPPORTED).  dim == 0 is a no-op; batch == 0 or seqlen == 0 sets
+ * dA, dD, ddelta_bias to zero (and, with seqlen == 0, dh0 = dh_last or zeros).
  * Deterministic: every reduction runs in a fixed order.
  */
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,

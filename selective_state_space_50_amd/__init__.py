@@ -475,8 +475,8 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, delta_softplus=Fa
                    discretization="mamba"):
     """Differentiable selective scan: y = scan_fwd(...) with a torch autograd backward
     through scan_bwd (gradients for every tensor argument, delta_bias included).  The
-    forward stores the state checkpoints (scan_fwd_save) when the backward supports the
-    shape (dstate 16, dim a multiple of 64), so that the backward skips its own forward
+    forward stores the state checkpoints (scan_fwd_save) when the shape allows them
+    (dstate 16, dim a multiple of 64), so that the backward skips its own forward
     sweep."""
     import torch
 

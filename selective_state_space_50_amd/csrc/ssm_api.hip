@@ -400,51 +400,18 @@ extern "C" int ssm_scan_fwd_save(int64_t batch, int64_t seqlen, int64_t dim, int
                     delta_softplus, variant, workspace, checkpoints, bp.nblk, s);
 }
 
-extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
-                            const void *x, const void *delta, const float *A, const void *B,
-                            const void *C, const float *Dskip, const void *z, const float *h0,
-                            const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
-                            void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
-                            int discretization, const float *delta_bias, float *ddelta_bias,
-                            const float *checkpoints, void *workspace, size_t workspace_bytes,
-                            void *stream) {
-    using namespace ssm;
-    clear_error();
-    BwdPlan p;
-    int st = check_scan_bwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy,
-                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization,
-                            delta_bias, ddelta_bias, checkpoints, workspace, workspace_bytes, &p);
-    if (st != SSM_OK) return st;
-    if (dim == 0) return SSM_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+namespace ssm {
+namespace {
+
+// The backward on the native shape (dstate 16, dim a multiple of 64), after the checks.
+int bwd_native(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+               const void *x, const void *delta, const float *A, const void *B,
+               const void *C, const float *Dskip, const void *z, const float *h0,
+               const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
+               void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
+               int discretization, const float *delta_bias, float *ddelta_bias,
+               const float *checkpoints, void *workspace, const BwdPlan &p, hipStream_t s) {
     hipError_t e;
-    if (batch == 0 || seqlen == 0) {
-        // no rows or no steps: dh0 = dh_last, and the reductions over rows and steps are zero
-        if (dh0 && batch > 0) {
-            const int64_t n = batch * dim * dstate;
-            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                               0, s, dh0, dh_last, n);
-            e = hipGetLastError();
-            if (e != hipSuccess) return hip_fail("fill_state launch", e);
-        }
-        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim * dstate + 255) / 256)),
-                           dim3(256), 0, s, dA, static_cast<const float *>(nullptr), dim * dstate);
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail("fill_state launch", e);
-        if (Dskip && dD) {
-            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
-                               0, s, dD, static_cast<const float *>(nullptr), dim);
-            e = hipGetLastError();
-            if (e != hipSuccess) return hip_fail("fill_state launch", e);
-        }
-        if (delta_bias) {
-            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
-                               0, s, ddelta_bias, static_cast<const float *>(nullptr), dim);
-            e = hipGetLastError();
-            if (e != hipSuccess) return hip_fail("fill_state launch", e);
-        }
-        return SSM_OK;
-    }
     char *ws = static_cast<char *>(workspace);
     const bool bf16 = dtype == SSM_DTYPE_BF16;
     // 1) checkpoints: the specialised forward kernel over the sequence, storing the state
@@ -506,6 +473,171 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     a.lc_H = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcH_off) : nullptr;
     e = launch_scan_bwd(a, discretization, bf16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
+}
+
+// dst [n0][m1][m2] from src [n0][n1][n2] (n1 <= m1, n2 <= m2); entries src does not cover
+// (or all, when src is null) take fill
+template <typename E>
+__global__ void __launch_bounds__(256) pad3_kernel(E *dst, const E *src, int64_t n0, int64_t n1, int64_t n2,
+                                                   int64_t m1, int64_t m2, E fill) {
+    const int64_t total = n0 * m1 * m2;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i2 = i % m2, r = i / m2, i1 = r % m1, i0 = r / m1;
+        dst[i] = (src && i1 < n1 && i2 < n2) ? src[(i0 * n1 + i1) * n2 + i2] : fill;
+    }
+}
+
+// dst [n0][n1][n2] from the leading block of src [n0][m1][m2]
+template <typename E>
+__global__ void __launch_bounds__(256) unpad3_kernel(E *dst, const E *src, int64_t n0, int64_t n1, int64_t n2,
+                                                     int64_t m1, int64_t m2) {
+    const int64_t total = n0 * n1 * n2;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i2 = i % n2, r = i / n2, i1 = r % n1, i0 = r / n1;
+        dst[i] = src[(i0 * m1 + i1) * m2 + i2];
+    }
+}
+
+dim3 grid_for(int64_t n) {
+    const int64_t b = (n + 255) / 256;
+    return dim3(static_cast<unsigned>(b < 1 ? 1 : b > 16384 ? 16384 : b));
+}
+
+// es-byte elements (2 or 4); fill as a float (its bf16 bits for 2-byte elements)
+hipError_t pad3(void *dst, const void *src, int64_t n0, int64_t n1, int64_t n2, int64_t m1, int64_t m2,
+                size_t es, float fill, hipStream_t s) {
+    const dim3 g = grid_for(n0 * m1 * m2);
+    if (es == 2)
+        hipLaunchKernelGGL(pad3_kernel<uint16_t>, g, dim3(256), 0, s, static_cast<uint16_t *>(dst),
+                           static_cast<const uint16_t *>(src), n0, n1, n2, m1, m2,
+                           static_cast<uint16_t>(__builtin_bit_cast(uint32_t, fill) >> 16));
+    else
+        hipLaunchKernelGGL(pad3_kernel<float>, g, dim3(256), 0, s, static_cast<float *>(dst),
+                           static_cast<const float *>(src), n0, n1, n2, m1, m2, fill);
+    return hipGetLastError();
+}
+
+hipError_t unpad3(void *dst, const void *src, int64_t n0, int64_t n1, int64_t n2, int64_t m1, int64_t m2,
+                  size_t es, hipStream_t s) {
+    const dim3 g = grid_for(n0 * n1 * n2);
+    if (es == 2)
+        hipLaunchKernelGGL(unpad3_kernel<uint16_t>, g, dim3(256), 0, s, static_cast<uint16_t *>(dst),
+                           static_cast<const uint16_t *>(src), n0, n1, n2, m1, m2);
+    else
+        hipLaunchKernelGGL(unpad3_kernel<float>, g, dim3(256), 0, s, static_cast<float *>(dst),
+                           static_cast<const float *>(src), n0, n1, n2, m1, m2);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                            const void *x, const void *delta, const float *A, const void *B,
+                            const void *C, const float *Dskip, const void *z, const float *h0,
+                            const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
+                            void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
+                            int discretization, const float *delta_bias, float *ddelta_bias,
+                            const float *checkpoints, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    using namespace ssm;
+    clear_error();
+    BwdPlan p;
+    int st = check_scan_bwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy,
+                            dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization,
+                            delta_bias, ddelta_bias, checkpoints, workspace, workspace_bytes, &p);
+    if (st != SSM_OK) return st;
+    if (dim == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (batch == 0 || seqlen == 0) {
+        // no rows or no steps: dh0 = dh_last, and the reductions over rows and steps are zero
+        if (dh0 && batch > 0) {
+            const int64_t n = batch * dim * dstate;
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                               0, s, dh0, dh_last, n);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        }
+        hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim * dstate + 255) / 256)),
+                           dim3(256), 0, s, dA, static_cast<const float *>(nullptr), dim * dstate);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        if (Dskip && dD) {
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
+                               0, s, dD, static_cast<const float *>(nullptr), dim);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        }
+        if (delta_bias) {
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
+                               0, s, ddelta_bias, static_cast<const float *>(nullptr), dim);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("fill_state launch", e);
+        }
+        return SSM_OK;
+    }
+    char *ws = static_cast<char *>(workspace);
+    if (p.pad) {
+        // dstate < 16 or dim not a multiple of 64: the native backward on padded copies
+        BwdPlan in;
+        st = plan_scan_bwd(batch, seqlen, p.Dp, 16, dtype, &in);
+        if (st != SSM_OK) return st;
+        const size_t es = dtype_size(dtype);
+        const int64_t BL = batch * seqlen, Dp = p.Dp, N = dstate;
+        auto at = [&](int i) { return static_cast<void *>(ws + p.pad_off[i]); };
+        auto atf = [&](int i) { return reinterpret_cast<float *>(ws + p.pad_off[i]); };
+        // inputs: tokens [B L D] -> [B L Dp], B/C [B L N] -> [B L 16], A [D N] -> [Dp 16] (-1 outside),
+        // D and the bias [D] -> [Dp], h0 and dh_last [B D N] -> [B Dp 16]
+        struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; float fill; } ins[] = {
+            {at(kPX), x, BL, 1, dim, 1, Dp, es, 0.0f},
+            {at(kPDelta), delta, BL, 1, dim, 1, Dp, es, 0.0f},
+            {at(kPZ), z, BL, 1, dim, 1, Dp, es, 0.0f},
+            {at(kPDy), dy, BL, 1, dim, 1, Dp, es, 0.0f},
+            {at(kPB), B, BL, 1, N, 1, 16, es, 0.0f},
+            {at(kPC), C, BL, 1, N, 1, 16, es, 0.0f},
+            {at(kPA), A, 1, dim, N, Dp, 16, 4, -1.0f},
+            {at(kPDskip), Dskip, 1, 1, dim, 1, Dp, 4, 0.0f},
+            {at(kPBias), delta_bias, 1, 1, dim, 1, Dp, 4, 0.0f},
+            {at(kPH0), h0, batch, dim, N, Dp, 16, 4, 0.0f},
+            {at(kPDhLast), dh_last, batch, dim, N, Dp, 16, 4, 0.0f},
+        };
+        for (const auto &c : ins) {
+            if (!c.src && c.dst != at(kPA)) continue;   // absent optional inputs stay absent
+            e = pad3(c.dst, c.src, c.n0, c.n1, c.n2, c.m1, c.m2, c.es, c.fill, s);
+            if (e != hipSuccess) return hip_fail("pad launch", e);
+        }
+        st = bwd_native(batch, seqlen, Dp, 16, dtype, at(kPX), at(kPDelta), atf(kPA), at(kPB), at(kPC),
+                        Dskip ? atf(kPDskip) : nullptr, z ? at(kPZ) : nullptr, h0 ? atf(kPH0) : nullptr,
+                        at(kPDy), dh_last ? atf(kPDhLast) : nullptr, at(kPDx), at(kPDdelta), atf(kPDA),
+                        at(kPDB), at(kPDC), Dskip ? atf(kPDD) : nullptr, z ? at(kPDz) : nullptr,
+                        dh0 ? atf(kPDh0) : nullptr, delta_softplus, discretization,
+                        delta_bias ? atf(kPBias) : nullptr, delta_bias ? atf(kPDBias) : nullptr, nullptr,
+                        ws + p.inner_off, in, s);
+        if (st != SSM_OK) return st;
+        struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; } outs[] = {
+            {dx, at(kPDx), BL, 1, dim, 1, Dp, es},
+            {ddelta, at(kPDdelta), BL, 1, dim, 1, Dp, es},
+            {z ? dz : nullptr, at(kPDz), BL, 1, dim, 1, Dp, es},
+            {dB, at(kPDB), BL, 1, N, 1, 16, es},
+            {dC, at(kPDC), BL, 1, N, 1, 16, es},
+            {dA, at(kPDA), 1, dim, N, Dp, 16, 4},
+            {Dskip ? dD : nullptr, at(kPDD), 1, 1, dim, 1, Dp, 4},
+            {delta_bias ? ddelta_bias : nullptr, at(kPDBias), 1, 1, dim, 1, Dp, 4},
+            {dh0, at(kPDh0), batch, dim, N, Dp, 16, 4},
+        };
+        for (const auto &c : outs) {
+            if (!c.dst) continue;
+            e = unpad3(c.dst, c.src, c.n0, c.n1, c.n2, c.m1, c.m2, c.es, s);
+            if (e != hipSuccess) return hip_fail("unpad launch", e);
+        }
+        return SSM_OK;
+    }
+    return bwd_native(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, dy, dh_last, dx,
+                      ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization, delta_bias,
+                      ddelta_bias, checkpoints, workspace, p, s);
 }
 
 extern "C" int ssm_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype,

@@ -366,10 +366,40 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
                   BwdPlan *plan) {
     int st = check_dims(batch, seqlen, dim, dstate, dtype);
     if (st != SSM_OK) return st;
-    if (dstate != 16 || dim % 64 != 0 || dim >= (int64_t(1) << 24)) {
-        set_error("ssm_scan_bwd supports dstate == 16 and dim a multiple of 64 (got dstate=%lld, dim=%lld)",
-                  (long long)dstate, (long long)dim);
+    if (dim >= (int64_t(1) << 24) - 64) {
+        set_error("ssm_scan_bwd: dim=%lld is too large", (long long)dim);
         return SSM_EUNSUPPORTED;
+    }
+    if (dstate != 16 || dim % 64 != 0) {
+        // run on copies padded to dim Dp and 16 states: the padding channels carry x = 0, the
+        // padding states B = C = 0 (and A = -1), so neither adds to any gradient
+        BwdPlan p;
+        p.pad = true;
+        p.Dp = ceil_div(dim, 64) * 64;
+        BwdPlan in;
+        st = plan_scan_bwd(batch, seqlen, p.Dp, 16, dtype, &in);
+        if (st != SSM_OK) return st;
+        const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen);
+        const size_t Dp = static_cast<size_t>(p.Dp), es = dtype_size(dtype);
+        const size_t tok = B * L * Dp * es, bc = B * L * 16 * es, st16 = B * Dp * 16 * sizeof(float);
+        const size_t bytes[kPadBufs] = {tok, tok, tok, tok, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
+                                        Dp * sizeof(float), st16, st16,
+                                        tok, tok, tok, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
+                                        Dp * sizeof(float), st16};
+        size_t ws = 0;
+        for (int i = 0; i < kPadBufs; ++i) {
+            p.pad_off[i] = ws;
+            ws = align_up(ws + bytes[i], kWsAlign);
+        }
+        p.inner_off = ws;
+        p.nblk = in.nblk;
+        p.n_chunks = in.n_chunks;
+        p.chunk_len = in.chunk_len;
+        p.ws_bytes = p.ws_bytes_saved = align_up(ws + in.ws_bytes, kWsAlign);
+        p.ckpt_bytes = 0;
+        if (batch == 0 || seqlen == 0 || dim == 0) p.ws_bytes = p.ws_bytes_saved = 0;
+        *plan = p;
+        return SSM_OK;
     }
     if (batch > 65535) {
         set_error("batch=%lld: at most 65535 rows", (long long)batch);
@@ -435,6 +465,11 @@ int check_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    const void *workspace, size_t workspace_bytes, BwdPlan *plan) {
     int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
     if (st != SSM_OK) return st;
+    if (plan->pad && checkpoints) {
+        set_error("saved checkpoints need dstate == 16 and dim a multiple of 64 (got dstate=%lld, dim=%lld)",
+                  (long long)dstate, (long long)dim);
+        return SSM_EUNSUPPORTED;
+    }
     if (delta_softplus != 0 && delta_softplus != 1) {
         set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
         return SSM_EINVAL;
@@ -492,6 +527,11 @@ int check_scan_save(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
                     BwdPlan *plan) {
     int st = plan_scan_bwd(batch, seqlen, dim, dstate, dtype, plan);
     if (st != SSM_OK) return st;
+    if (plan->pad) {
+        set_error("ssm_scan_fwd_save supports dstate == 16 and dim a multiple of 64 (got dstate=%lld, dim=%lld)",
+                  (long long)dstate, (long long)dim);
+        return SSM_EUNSUPPORTED;
+    }
     // the forward's own checks, on the backward's chunk plan (so that the checkpoints sit
     // every 8 steps from each chunk's start, as the reverse sweep reads them)
     ssm_scan_opts o = {plan->chunk_len, 0, 0, 0, 0};
@@ -721,6 +761,11 @@ int ssm_scan_save_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
     ssm::BwdPlan p;
     const int st = ssm::plan_scan_bwd(batch, seqlen, dim, dstate, dtype, &p);
     if (st != SSM_OK) return st;
+    if (p.pad) {
+        ssm::set_error("ssm_scan_fwd_save supports dstate == 16 and dim a multiple of 64 (got dstate=%lld, dim=%lld)",
+                       (long long)dstate, (long long)dim);
+        return SSM_EUNSUPPORTED;
+    }
     if (batch > 0 && seqlen > 0 && dim > 0) *workspace_bytes = p.fwd.ws_bytes;
     *checkpoint_bytes = p.ckpt_bytes;
     return SSM_OK;

@@ -73,6 +73,12 @@ inline const float *variant_bias(const ssm_variant *v) { return v ? v->delta_bia
 // dA/dD, the adjoint carries, then (last, so that a call given saved checkpoints needs
 // only the part before them) the forward checkpoint pass's own workspace and the state
 // checkpoints.
+// Buffers of the padded backward, in workspace order: inputs, then outputs.
+enum PadBuf {
+    kPX, kPDelta, kPZ, kPDy, kPB, kPC, kPA, kPDskip, kPBias, kPH0, kPDhLast,
+    kPDx, kPDdelta, kPDz, kPDB, kPDC, kPDA, kPDD, kPDBias, kPDh0, kPadBufs
+};
+
 struct BwdPlan {
     int64_t nblk = 0;       // 8-step blocks of the reverse sweep
     int64_t n_chunks = 1, chunk_len = 0;   // sequence chunks (chunk_len a multiple of 16 when several)
@@ -84,6 +90,13 @@ struct BwdPlan {
     size_t ckpt_bytes = 0;
     size_t ws_bytes = 0;        // with the checkpoint pass
     size_t ws_bytes_saved = 0;  // given saved checkpoints (= fwd_off)
+    // Other shapes (dstate < 16 or dim not a multiple of 64) run the same kernels on copies
+    // padded to dim Dp (the next multiple of 64) and 16 states, in the workspace; the pad
+    // region comes first, the native plan's workspace (of the padded shape) after it.
+    bool pad = false;
+    int64_t Dp = 0;
+    size_t pad_off[kPadBufs] = {};
+    size_t inner_off = 0;
 };
 
 int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,

@@ -130,6 +130,21 @@ int main() {
         EXPECT(ssm_scan_save_sizes(1, 5000, 128, 16, SSM_DTYPE_BF16, nullptr, &ckz) == SSM_EINVAL);
         EXPECT(ssm_scan_bwd_workspace_bytes(2, 1000, 256, 16, SSM_DTYPE_BF16, 1) == saved);
         EXPECT(ssm_scan_bwd_workspace_bytes(2, 1000, 256, 16, SSM_DTYPE_BF16, 0) == full);
+        // other shapes: the native plan of the copies padded to 64 channels and 16 states,
+        // after the padded buffers; no saved checkpoints
+        BwdPlan in;
+        EXPECT(plan_scan_bwd(2, 100, 40, 8, SSM_DTYPE_BF16, &bp) == SSM_OK);
+        EXPECT(plan_scan_bwd(2, 100, 64, 16, SSM_DTYPE_BF16, &in) == SSM_OK);
+        EXPECT(bp.pad && bp.Dp == 64 && !in.pad && bp.nblk == in.nblk);
+        EXPECT(bp.pad_off[kPDx] >= size_t(4) * 2 * 100 * 64 * 2 && bp.inner_off > bp.pad_off[kPDh0]);
+        EXPECT(bp.ws_bytes >= bp.inner_off + in.ws_bytes && bp.ws_bytes_saved == bp.ws_bytes);
+        EXPECT(ssm_scan_bwd_workspace_bytes(2, 100, 40, 8, SSM_DTYPE_BF16, 0) == bp.ws_bytes);
+        EXPECT(plan_scan_bwd(1, 10, 128, 3, SSM_DTYPE_F32, &bp) == SSM_OK && bp.pad && bp.Dp == 128);
+        EXPECT(plan_scan_bwd(1, 10, 128, 17, SSM_DTYPE_F32, &bp) == SSM_EUNSUPPORTED);
+        EXPECT(check_scan_bwd(2, 100, 40, 8, SSM_DTYPE_BF16, x, dl, A, B, C, nullptr, nullptr, nullptr, dl, nullptr,
+                              dx, ddl, dA, dB, dC, nullptr, nullptr, nullptr, 0, SSM_DISC_MAMBA, nullptr,
+                              nullptr, ck, bws, size_t(1) << 30, &bp) == SSM_EUNSUPPORTED);
+        EXPECT(std::strstr(ssm_last_error(), "checkpoints") != nullptr);
     }
     // the specialised path packs B/C rows into the workspace: 4 x 4096 x 16 x (B, C) fp32
     EXPECT(scan(4, 4096, 4096, 16, SSM_DTYPE_BF16, x, y, nullptr, nullptr, 0, h0, hl) == SSM_EWORKSPACE);

@@ -101,6 +101,51 @@ def test_backward_with_delta_bias(ssm, Bsz, L, D, dt, sp):
     _check(g, r, dt, f"{Bsz}x{L}x{D} {dt} softplus={sp} delta bias")
 
 
+GENERIC = [
+    # B, L, D, N, dtype, discretisation, gate, h0, dh_last, softplus, bias
+    (2, 50, 40, 16, "f32", "mamba", True, True, True, False, False),
+    (1, 33, 64, 8, "bf16", "mamba", True, False, True, False, False),
+    (2, 100, 96, 4, "f32", "zoh", False, True, True, True, False),
+    (1, 70, 130, 1, "bf16", "bilinear", True, True, False, False, False),
+    (3, 17, 10, 5, "f32", "mamba", True, True, True, True, True),
+    (1, 300, 200, 12, "bf16", "mamba", True, True, True, False, True),
+    (2, 1, 3, 2, "f32", "zoh", True, False, True, False, False),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,N,dt,disc,gate,h0,dhl,sp,bias", GENERIC)
+def test_backward_generic_shapes(ssm, Bsz, L, D, N, dt, disc, gate, h0, dhl, sp, bias):
+    """dstate below 16 or dim not a multiple of 64: the backward runs the native kernels on
+    copies padded to a multiple of 64 channels and 16 states; every output against the
+    oracle."""
+    seed = 300 + L + D + N
+    inp = synth.scan_inputs(Bsz, L, D, N, dt, seed=seed, gate=gate, d_kind="normal", a_kind="random",
+                            softplus_input=sp, h0=h0)
+    inp["discretization"] = disc
+    if bias:
+        b = synth.make_delta_bias(seed, D)
+        inp["delta_bias"] = b if sp else (0.05 * np.abs(b)).astype(np.float32)
+    r = np.random.default_rng(seed + 1000)
+    gy = synth.store(r.standard_normal((Bsz, L, D)).astype(np.float32), dt)
+    gl = r.standard_normal((Bsz, D, N)).astype(np.float32) if dhl else None
+    g = _run(ssm, inp, gy, gl)
+    ref = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    if not gate:
+        ref["dz"] = None
+    _check(g, ref, dt, f"generic {Bsz}x{L}x{D} N={N} {dt} {disc} gate={gate} softplus={sp} bias={bias}")
+
+
+def test_backward_generic_rejects_saved_checkpoints(ssm):
+    """Saved checkpoints exist only for dstate 16 and dim a multiple of 64."""
+    import torch
+    x = torch.zeros((1, 8, 40), device="cuda")
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.scan_bwd(x, x, torch.zeros((40, 16), device="cuda"), torch.zeros((1, 8, 16), device="cuda"),
+                     torch.zeros((1, 8, 16), device="cuda"), None, None, None, x,
+                     checkpoints=torch.zeros((1, 1, 16, 40), device="cuda"))
+    assert e.value.status == ssm.SSM_EUNSUPPORTED
+
+
 def test_backward_deterministic(ssm):
     inp, gy, gl = _case(2, 200, 128, "bf16", True, True, True, False, True, seed=7)
     a = _run(ssm, inp, gy, gl)
@@ -134,9 +179,9 @@ def test_backward_empty_and_unsupported(ssm):
         assert g[k] is not None and float(g[k].abs().sum()) == 0.0, k
     assert g["dh0"].numel() == 0
     xs = torch.zeros((1, 4, 96), device="cuda")
-    with pytest.raises(ssm.SSMError) as e:
-        ssm.scan_bwd(xs, xs, torch.zeros((96, 16), device="cuda"), torch.zeros((1, 4, 16), device="cuda"),
-                     torch.zeros((1, 4, 16), device="cuda"), None, None, None, xs)
+    with pytest.raises(ssm.SSMError) as e:   # more than 16 states
+        ssm.scan_bwd(xs, xs, torch.zeros((96, 17), device="cuda"), torch.zeros((1, 4, 17), device="cuda"),
+                     torch.zeros((1, 4, 17), device="cuda"), None, None, None, xs)
     assert e.value.status == ssm.SSM_EUNSUPPORTED
 
 
