@@ -821,6 +821,9 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
                      "alg_slots_per_launch": upd * sm["bwd"]},
         "timing": "median of 5 calls (checkpoint pass, reverse sweep, reductions), each between two events",
         "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
+        "workspace_bytes": ws.numel(),
+        "workspace_bytes_given_saved_checkpoints": ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16", True),
+        "checkpoint_bytes": ssm.scan_save_sizes(Bsz, L, D, N, "bf16")[1],
     }
     log(f"backward: {ms:.3f} ms median ({upd / (ms * 1e-3):.3e} state-updates/s, VALU {bwd_ts / VALU_PEAK_TSLOTS:.1%})")
     # the same backward under the other discretisations (their derivatives cost more VALU
@@ -979,6 +982,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         "timing": "median of 3 calls, each between two events",
         "note": "chunks of the forward planner (16 x 65536 steps): chunked checkpoint pass, adjoint carries and "
                 "their combine, reverse sweep per chunk; the carry passes are not counted as algorithmic work",
+        "workspace_bytes": wsb.numel(),
+        "checkpoint_bytes": ssm.scan_save_sizes(Bsz, L, D, N, "bf16")[1],
     }
     log(f"long-sequence backward: {ms:.2f} ms/call ({upd / (ms * 1e-3):.3e} state-updates/s, "
         f"VALU {bwd_ts / VALU_PEAK_TSLOTS:.1%})")
