@@ -50,7 +50,7 @@ extern "C" {
 #endif
 
 #define SSM_ABI_VERSION 5
-#define SSM_MAX_DSTATE 16
+#define SSM_MAX_DSTATE 256
 
 typedef enum ssm_dtype {
     SSM_DTYPE_F32 = 0,
@@ -185,8 +185,9 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   workspace device memory of ssm_scan_workspace_bytes() bytes (NULL if 0)
  *
  * batch, seqlen or dim == 0 is a valid no-op (with seqlen == 0, h_last
- * receives h0 or zeros).  1 <= dstate <= 16, else SSM_EINVAL (< 1) or
- * SSM_EUNSUPPORTED (> 16).
+ * receives h0 or zeros).  1 <= dstate <= SSM_MAX_DSTATE (256), else SSM_EINVAL (< 1)
+ * or SSM_EUNSUPPORTED (> 256); dstate 16 with dim a multiple of 64 runs the specialised
+ * kernel, every other shape the generic one.
  */
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
                  const void *x, const void *delta, const float *A, const void *B,
@@ -315,8 +316,9 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   workspace device memory of ssm_scan_bwd_workspace_bytes(..., checkpoints != NULL)
  *             bytes (partial sums, and without saved checkpoints the checkpoints)
  *
- * Any 1 <= dstate <= 16 and any dim.  dstate == 16 with dim a multiple of 64 runs the
- * native kernels in place; other shapes run them on copies padded (in the workspace) to
+ * Any 1 <= dstate <= 16 (more is SSM_EUNSUPPORTED) and any dim.  dstate == 16 with dim a
+ * multiple of 64 runs the native kernels in place; other shapes run them on copies
+ * padded (in the workspace) to
  * the next multiple of 64 channels and to 16 states, whose padding carries x = 0 and
  * B = C = 0 and so adds nothing to any gradient; those shapes take no saved
  * checkpoints (SSM_EUNSUPPORTED).  dim == 0 is a no-op; batch == 0 or seqlen == 0 sets

@@ -1,4 +1,6 @@
-// Generic selective-scan kernel: any dim, 1 <= dstate <= 16, any states per lane.
+// Generic selective-scan kernel: any dim, 1 <= dstate <= 256, any states per lane.  Up to 16
+// states the waves hold G of them each (at most 16 / G waves); beyond, G = 16 and up to 16
+// waves (MAXT = 1024 threads).
 //
 // One workgroup = 64 channels of one batch row and one sequence chunk:
 //   * lane   -> channel d (loads and stores of x, delta, z, y coalesce along d);
@@ -57,8 +59,8 @@ __device__ __forceinline__ void lds_vec(const float *p, float (&v)[G]) {
 
 // Main scan kernel.  CARRY = true: chunk carry pass (no y; stores the chunk's
 // decay and end state from zero).  CARRY = false: y pass.  DISC: the discretisation.
-template <int DISC, typename T, int G, int TB, bool HAS_Z, bool CARRY>
-__global__ void __launch_bounds__(64 * (16 / G)) scan_kernel(ScanArgs a) {
+template <int DISC, typename T, int G, int TB, bool HAS_Z, bool CARRY, int MAXT = 64 * (16 / G)>
+__global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
     extern __shared__ float smem[];
     const int NW = a.NW;
     const int NP = NW * G;
@@ -113,7 +115,10 @@ __global__ void __launch_bounds__(64 * (16 / G)) scan_kernel(ScanArgs a) {
 
     // staging: thread (w, lane) owns rows i = w + j*NW of the [TB][64] tiles,
     // and finishes (sums, skip term, gate, store) the same rows
-    constexpr int kRowsMax = 8;     // ceil(TB / NW) <= 8 is guaranteed by the plan
+    // more than 16 states (G = 16, MAXT = 1024): at least two waves, 8-step blocks, and no
+    // operand prefetch, so that the 16 states' registers fit beside 15 other waves
+    constexpr bool kBig = G == 16 && MAXT == 1024;
+    constexpr int kRowsMax = kBig ? 4 : 8;     // ceil(TB / NW) <= 8 is guaranteed by the plan
     const int rows = (TB + NW - 1) / NW;
     // B/C rows: element e = tid + j*nthr of the [TB][NP] tile
     constexpr int kBCMax = (TB * 16 + 63) / 64;
@@ -188,24 +193,33 @@ __global__ void __launch_bounds__(64 * (16 / G)) scan_kernel(ScanArgs a) {
         const int64_t tb0 = t0 + k * TB;
         __syncthreads();   // stage of block k visible; y shares of block k-1 consumed
         // ---- recurrence over the TB staged steps: G states per lane ----
-        // LDS operands of step i+1 are read while step i computes.
+        // LDS operands of step i+1 are read while step i computes (not in the big variant).
         float2 du_n = sDU[lane];
-        float bv_n[G], cv_n[G];
-        lds_vec<G>(sB + n0, bv_n);
-        if constexpr (!CARRY) lds_vec<G>(sC + n0, cv_n);
+        float bv_n[kBig ? 1 : G], cv_n[kBig ? 1 : G];
+        if constexpr (!kBig) {
+            lds_vec<G>(sB + n0, bv_n);
+            if constexpr (!CARRY) lds_vec<G>(sC + n0, cv_n);
+        }
 #pragma unroll
         for (int i = 0; i < TB; ++i) {
             const float2 du = du_n;
             float bv[G], cv[G];
+            if constexpr (kBig) {
+                lds_vec<G>(sB + i * NP + n0, bv);
+                if constexpr (!CARRY) lds_vec<G>(sC + i * NP + n0, cv);
+            } else {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                bv[g] = bv_n[g];
-                if constexpr (!CARRY) cv[g] = cv_n[g];
+                for (int g = 0; g < G; ++g) {
+                    bv[g] = bv_n[g];
+                    if constexpr (!CARRY) cv[g] = cv_n[g];
+                }
             }
             if (i + 1 < TB) {
                 du_n = sDU[(i + 1) * 64 + lane];
-                lds_vec<G>(sB + (i + 1) * NP + n0, bv_n);
-                if constexpr (!CARRY) lds_vec<G>(sC + (i + 1) * NP + n0, cv_n);
+                if constexpr (!kBig) {
+                    lds_vec<G>(sB + (i + 1) * NP + n0, bv_n);
+                    if constexpr (!CARRY) lds_vec<G>(sC + (i + 1) * NP + n0, cv_n);
+                }
             }
             if constexpr (CARRY) {
                 if constexpr (DISC != kBilinear) dsum += du.x;
@@ -274,11 +288,11 @@ __global__ void __launch_bounds__(64 * (16 / G)) scan_kernel(ScanArgs a) {
 }
 
 
-template <int DISC, typename T, int G, int TB, bool HAS_Z, bool CARRY>
+template <int DISC, typename T, int G, int TB, bool HAS_Z, bool CARRY, int MAXT = 64 * (16 / G)>
 hipError_t launch_scan_t(const ScanArgs &a, dim3 grid, int NW, hipStream_t s) {
     const Smem S = smem_layout(TB, NW, G, CARRY);
     const size_t lds = static_cast<size_t>(S.total) * sizeof(float);
-    hipLaunchKernelGGL((scan_kernel<DISC, T, G, TB, HAS_Z, CARRY>), grid, dim3(NW * 64), lds, s, a);
+    hipLaunchKernelGGL((scan_kernel<DISC, T, G, TB, HAS_Z, CARRY, MAXT>), grid, dim3(NW * 64), lds, s, a);
     return hipGetLastError();
 }
 
@@ -299,6 +313,8 @@ hipError_t launch_scan_tb(const ScanArgs &a, dim3 grid, int NW, int TB, hipStrea
 
 template <int DISC, typename T, bool HAS_Z, bool CARRY>
 hipError_t launch_scan_g(const ScanArgs &a, dim3 grid, const ScanPlan &p, hipStream_t s) {
+    // more than 16 states: 16 per lane, up to 16 waves, 8-step blocks (the planner's choice)
+    if (p.G * p.NW > 16) return launch_scan_t<DISC, T, 16, 8, HAS_Z, CARRY, 1024>(a, grid, p.NW, s);
     switch (p.G) {
         case 1: return launch_scan_tb<DISC, T, 1, HAS_Z, CARRY>(a, grid, p.NW, p.TB, s);
         case 2: return launch_scan_tb<DISC, T, 2, HAS_Z, CARRY>(a, grid, p.NW, p.TB, s);

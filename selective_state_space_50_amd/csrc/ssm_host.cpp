@@ -130,8 +130,17 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
         return SSM_EINVAL;
     }
     ScanPlan p;
-    // states per lane: default 4 (a quarter of the N=16 state in each of four waves)
+    // states per lane: default 4 (a quarter of the N=16 state in each of four waves); more
+    // than 16 states take 16 per lane in up to 16 waves, with 8-step blocks
     int G = o.states_per_lane;
+    if (dstate > 16) {
+        if ((G != 0 && G != 16) || (o.time_block != 0 && o.time_block != 8)) {
+            set_error("dstate=%lld > 16 runs 16 states per lane and 8-step blocks (opts asked %d, %d)",
+                      (long long)dstate, G, o.time_block);
+            return SSM_EINVAL;
+        }
+        G = 16;
+    }
     if (G == 0) {
         G = 1;
         while (G < dstate && G < 4) G *= 2;
@@ -154,7 +163,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
     } else {
         p.TB = 8;
         for (int tb : {32, 16}) {
-            if (rows_ok(tb) && lds_ok(tb)) {
+            if (dstate <= 16 && rows_ok(tb) && lds_ok(tb)) {
                 p.TB = tb;
                 break;
             }
@@ -180,7 +189,7 @@ int plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dt
                 n_chunks = want < cap ? want : cap;
                 if (n_chunks < 1) n_chunks = 1;
             }
-        } else {
+        } else if (dstate <= 16) {   // (more states: one pass; the chunked form needs opts)
             const int64_t waves = batch * dblocks * p.NW;
             const int64_t kSimds = 1024;      // 256 CUs x 4 SIMDs
             const int64_t kMinChunk = 2048;   // keeps the carry pass's share small
@@ -338,7 +347,7 @@ int check_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, co
     st = check_variant(variant);
     if (st != SSM_OK) return st;
     if (batch == 0 || dim == 0) return SSM_OK;
-    if (batch * dim > (int64_t(1) << 34)) {   // 16 lanes per channel at most, 256-thread blocks
+    if (batch * dim > (int64_t(1) << 34)) {   // 64 lanes per channel at most, 256-thread blocks
         set_error("batch*dim=%lld is too large for one launch", (long long)(batch * dim));
         return SSM_EUNSUPPORTED;
     }
@@ -368,6 +377,10 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
     if (st != SSM_OK) return st;
     if (dim >= (int64_t(1) << 24) - 64) {
         set_error("ssm_scan_bwd: dim=%lld is too large", (long long)dim);
+        return SSM_EUNSUPPORTED;
+    }
+    if (dstate > 16) {
+        set_error("ssm_scan_bwd supports dstate <= 16 (got %lld)", (long long)dstate);
         return SSM_EUNSUPPORTED;
     }
     if (dstate != 16 || dim % 64 != 0) {

@@ -153,7 +153,12 @@ int main() {
     EXPECT(p.ws_bytes == size_t(4) * 4096 * 16 * 2 * 4 && p.bc_lpad == 4096);
     EXPECT(p.lds_reserve + 16384 + 2 * (16 / p.G) * 4096 > 80 * 1024 && p.lds_reserve + 16384 + 2 * (16 / p.G) * 4096 <= 160 * 1024);
     EXPECT(scan(4, 4096, 4096, 16, 2, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
-    EXPECT(scan(4, 4096, 4096, 17, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EUNSUPPORTED);
+    EXPECT(scan(4, 4096, 4096, 257, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EUNSUPPORTED);
+    // more than 16 states: the generic kernel, 16 states per lane, 8-step blocks, one pass
+    EXPECT(scan(4, 4096, 64, 17, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
+    EXPECT(!p.fast && p.G == 16 && p.NW == 2 && p.TB == 8 && p.n_chunks == 1);
+    EXPECT(scan(1, 4096, 64, 256, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_OK);
+    EXPECT(!p.fast && p.G == 16 && p.NW == 16 && p.TB == 8 && p.n_chunks == 1);
     EXPECT(scan(4, 4096, 4096, 0, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
     EXPECT(scan(-1, 4096, 4096, 16, 1, x, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
     EXPECT(scan(4, 4096, 4096, 16, 1, nullptr, y, nullptr, ws, size_t(1) << 30, h0, hl) == SSM_EINVAL);
@@ -203,7 +208,7 @@ int main() {
     EXPECT(check_state_update(256, 4096, 16, 1, nullptr, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_EINVAL);
     EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, x, 0, nullptr) == SSM_EINVAL);
     EXPECT(check_state_update(256, 4096, 16, 1, h, x, dl, A, B, C, Dk, z, y, 2, nullptr) == SSM_EINVAL);
-    EXPECT(check_state_update(256, 4096, 32, 1, h, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_EUNSUPPORTED);
+    EXPECT(check_state_update(256, 4096, 257, 1, h, x, dl, A, B, C, Dk, z, y, 0, nullptr) == SSM_EUNSUPPORTED);
     EXPECT(check_state_update(0, 4096, 16, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                               nullptr, nullptr, nullptr, 0, nullptr) == SSM_OK);
     // multi-head SSD scan

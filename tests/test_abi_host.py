@@ -66,7 +66,7 @@ def _scan_status(lib, *, B=1, L=8, D=64, N=16, dtype=1, x=G4, y=2 * G4, ws=None,
 
 def test_validation_rejects_before_launch(lib):
     assert _scan_status(lib, dtype=5) == 1
-    assert _scan_status(lib, N=17) == 2
+    assert _scan_status(lib, N=257) == 2
     assert _scan_status(lib, N=0) == 1
     assert _scan_status(lib, B=-1) == 1
     assert _scan_status(lib, y=None) == 1

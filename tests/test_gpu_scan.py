@@ -188,11 +188,11 @@ def test_empty_and_degenerate(ssm):
 def test_errors_launch_nothing(ssm):
     import torch
     x = torch.zeros((1, 4, 8), dtype=torch.bfloat16, device="cuda")
-    Bm = torch.zeros((1, 4, 20), dtype=torch.bfloat16, device="cuda")
-    A = torch.zeros((8, 20), device="cuda")
+    Bm = torch.zeros((1, 4, 300), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((8, 300), device="cuda")
     with pytest.raises(ssm.SSMError) as e:
         ssm.scan_fwd(x, x, A, Bm, Bm)
-    assert e.value.status == 2  # dstate > 16 is unsupported
+    assert e.value.status == 2  # dstate > 256 is unsupported
     y = torch.zeros((1, 4, 8), dtype=torch.bfloat16, device="cuda")
     Bm = torch.zeros((1, 4, 4), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ssm.SSMError) as e:   # y overlapping x
