@@ -418,7 +418,9 @@ int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, void
  *   h0, h_last [batch, nheads, headdim, dstate] fp32   NULL = zero start / not stored
  *   y         [batch, seqlen, nheads, headdim]  bf16   output; must not overlap an input
  *
- * Supported: headdim 64, dstate 128, bf16 (else SSM_EUNSUPPORTED).  No workspace.
+ * headdim 64, dstate 128, bf16: the matrix-core kernel.  Any other headdim >= 1, dstate <=
+ * 256 (more is SSM_EUNSUPPORTED), and fp32 (dtype SSM_DTYPE_F32 for x, z, delta, B, C, y):
+ * the generic scan kernel over the nheads * headdim channels, one pass.  No workspace.
  * seqlen == 0 stores h0 (or zeros) in h_last; batch or nheads == 0 is a no-op.
  */
 int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,

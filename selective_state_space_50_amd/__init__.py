@@ -622,9 +622,10 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
             return_last_state=False, out=None, h_last=None, stream=None):
     """Multi-head SSD scan (the Mamba-2 layer's state space model) on the GPU.
 
-    x, z: [B, L, H, 64] bf16;  delta: [B, L, H] bf16;  A, D, delta_bias: [H] fp32;
-    B, C: [B, L, 128] bf16;  h0: [B, H, 64, 128] fp32.  Returns y [B, L, H, 64] (bf16),
-    or (y, h_last) when return_last_state.
+    x, z: [B, L, H, P];  delta: [B, L, H];  B, C: [B, L, N] (all bf16, or all fp32);
+    A, D, delta_bias: [H] fp32;  h0: [B, H, P, N] fp32.  P = 64, N = 128 in bf16 runs on the
+    matrix cores; other P, N <= 256 and fp32 on the generic scan kernel.  Returns y
+    [B, L, H, P] (x's dtype), or (y, h_last) when return_last_state.
     """
     import torch
     if x.dim() != 4 or A.dim() != 1:

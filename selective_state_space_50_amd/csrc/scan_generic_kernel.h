@@ -73,6 +73,9 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
     const int64_t c = blockIdx.z;
     const int64_t d = static_cast<int64_t>(blockIdx.x) * 64 + lane;
     const bool dvalid = d < D;
+    // per-channel parameters, or per-head ones in the multi-head layout
+    const int64_t dh = a.head_dim > 0 ? d / a.head_dim : d;
+    const int64_t DS = a.head_dim > 0 ? D / a.head_dim : D;   // delta's row length
     const int64_t t0 = c * a.chunk_len;
     const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
     const int n0 = w * G;
@@ -95,7 +98,7 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
     for (int g = 0; g < G; ++g) {
         const int64_t n = n0 + g;
         const bool ok = dvalid && n < N;
-        const float av = ok ? a.A[d * N + n] : 0.0f;
+        const float av = ok ? (a.head_dim > 0 ? a.A[dh] : a.A[d * N + n]) : 0.0f;
         Al[g] = av * kLog2e;
         aux[g] = disc_aux<DISC>(av);
         pc[g] = 1.0f;
@@ -109,8 +112,8 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
         }
         h[g] = hv;
     }
-    const float dsk = (!CARRY && dvalid && a.Dskip) ? a.Dskip[d] : 0.0f;
-    const float dbias = (dvalid && a.dbias) ? a.dbias[d] : 0.0f;
+    const float dsk = (!CARRY && dvalid && a.Dskip) ? a.Dskip[dh] : 0.0f;
+    const float dbias = (dvalid && a.dbias) ? a.dbias[dh] : 0.0f;
     float dsum = 0.0f;
 
     // staging: thread (w, lane) owns rows i = w + j*NW of the [TB][64] tiles,
@@ -135,7 +138,7 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
                 const bool ok = dvalid && i < TB && t < t1;
                 const int64_t off = (b * L + t) * D + d;
                 rx[j] = ok ? X[off] : T(0);
-                rd[j] = ok ? DL[off] : T(0);
+                rd[j] = ok ? DL[(b * L + t) * DS + dh] : T(0);
                 if (HAS_Z && !CARRY) rz[j] = ok ? Z[off] : T(0);
             }
         }

@@ -733,6 +733,32 @@ extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_
         hipError_t e = hipGetLastError();
         return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
     }
+    if (headdim != 64 || dstate != 128 || dtype != SSM_DTYPE_BF16) {
+        // other head dims, state sizes and fp32: the generic scan kernel over the H * P
+        // channels in its multi-head layout (one step size, decay, D and bias per head; B, C
+        // shared), in one pass (no workspace)
+        const int64_t dim = nheads * headdim;
+        ssm_scan_opts o = {seqlen, 0, 8, 0, -1};
+        ScanPlan p;
+        st = plan_scan(batch, seqlen, dim, dstate, dtype, &o, &p);
+        if (st != SSM_OK) return st;
+        ScanArgs a;
+        a.B = batch; a.L = seqlen; a.D = dim; a.N = dstate;
+        a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;
+        a.A = A; a.Dskip = Dskip; a.h0 = h0; a.h_last = h_last; a.y = y;
+        a.softplus = delta_softplus;
+        a.dbias = delta_bias;
+        a.NW = p.NW;
+        a.chunk_len = p.chunk_len;
+        a.n_chunks = 1;
+        a.ws_P = a.ws_H = a.ws_BC = nullptr;
+        a.bc_lpad = 0;
+        a.head_dim = headdim;
+        const dim3 g(static_cast<unsigned>((dim + kChannelsPerBlock - 1) / kChannelsPerBlock),
+                     static_cast<unsigned>(batch), 1);
+        hipError_t e = launch_scan_any(a, g, p, kMamba, dtype == SSM_DTYPE_BF16, z != nullptr, false, s);
+        return e == hipSuccess ? SSM_OK : hip_fail("ssd (generic) launch", e);
+    }
     SsdArgs a;
     a.B = batch; a.L = seqlen; a.H = nheads;
     a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;

@@ -50,6 +50,10 @@ struct ScanArgs {
     float *S_part = nullptr;       // [2][B][n_chunks][8][D] partial sums of delta: whole chunk, first y_skip steps
     int *flags = nullptr;          // [B][n_chunks-1][D/64] cleared by the local scan
     const int *flag_in = nullptr;  // only workgroups whose flag is set run
+    // Generic kernel only: > 0 makes the channels heads of head_dim channels each (the
+    // multi-head SSD layout): delta [B][L][D / head_dim], and A, Dskip, dbias one value per
+    // head (A the same for every state).
+    int64_t head_dim = 0;
 };
 
 struct UpdArgs {

@@ -714,9 +714,12 @@ int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, in
         set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
         return SSM_EINVAL;
     }
-    if (headdim != 64 || dstate != 128 || dtype != SSM_DTYPE_BF16) {
-        set_error("the SSD scan supports headdim 64, dstate 128 and bf16 (got %lld, %lld, dtype %d)",
-                  (long long)headdim, (long long)dstate, dtype);
+    if (dstate > SSM_MAX_DSTATE) {
+        set_error("the SSD scan supports dstate <= %d (got %lld)", SSM_MAX_DSTATE, (long long)dstate);
+        return SSM_EUNSUPPORTED;
+    }
+    if (nheads > 0 && headdim > (int64_t(1) << 24) / nheads) {
+        set_error("nheads * headdim = %lld * %lld is too large", (long long)nheads, (long long)headdim);
         return SSM_EUNSUPPORTED;
     }
     if (batch > 0 && seqlen > 0 && nheads > 0 &&
@@ -736,11 +739,12 @@ int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, in
         set_error("required pointer %s is NULL", missing);
         return SSM_EINVAL;
     }
-    const int64_t tok = batch * seqlen * nheads * headdim * 2;
+    const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+    const int64_t tok = batch * seqlen * nheads * headdim * es;
     const int64_t st_bytes = batch * nheads * headdim * dstate * 4;
     Range all[] = {
-        range("x", x, tok), range("delta", delta, batch * seqlen * nheads * 2), range("A", A, nheads * 4),
-        range("B", B, batch * seqlen * dstate * 2), range("C", C, batch * seqlen * dstate * 2),
+        range("x", x, tok), range("delta", delta, batch * seqlen * nheads * es), range("A", A, nheads * 4),
+        range("B", B, batch * seqlen * dstate * es), range("C", C, batch * seqlen * dstate * es),
         range("Dskip", Dskip, nheads * 4), range("z", z, tok), range("delta_bias", delta_bias, nheads * 4),
         range("h0", h0, st_bytes), range("h_last", h_last, st_bytes), range("y", y, seqlen > 0 ? tok : 0),
     };

@@ -218,9 +218,11 @@ int main() {
             return check_ssd(b, l, hh, pd, n, dt, x, dl, A, B, C, Dk, z, bias, h0, hl_, y_, 1);
         };
         EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, hl) == SSM_OK);
-        EXPECT(sd(4, 4096, 64, 32, 128, SSM_DTYPE_BF16, y, hl) == SSM_EUNSUPPORTED);
-        EXPECT(sd(4, 4096, 64, 64, 16, SSM_DTYPE_BF16, y, hl) == SSM_EUNSUPPORTED);
-        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_F32, y, hl) == SSM_EUNSUPPORTED);
+        // other head dims, state sizes and fp32 take the generic kernel; more than 256 states no
+        EXPECT(sd(4, 4096, 64, 32, 128, SSM_DTYPE_BF16, y, hl) == SSM_OK);
+        EXPECT(sd(4, 4096, 64, 64, 16, SSM_DTYPE_BF16, y, hl) == SSM_OK);
+        EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_F32, y, hl) == SSM_OK);
+        EXPECT(sd(4, 4096, 64, 64, 257, SSM_DTYPE_BF16, y, hl) == SSM_EUNSUPPORTED);
         EXPECT(sd(4, 4096, 64, 64, 128, 7, y, hl) == SSM_EINVAL);
         EXPECT(sd(-1, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, hl) == SSM_EINVAL);
         EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, nullptr, hl) == SSM_EINVAL);

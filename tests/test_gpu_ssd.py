@@ -105,11 +105,42 @@ def test_ssd_empty_and_errors(ssm):
     torch.cuda.synchronize()
     assert y.numel() == 0 and torch.equal(h, t["h0"])
     x = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(ssm.SSMError) as e:
+    with pytest.raises(ssm.SSMError) as e:   # more than 256 states
         ssm.ssd_fwd(x, torch.zeros(1, 8, 2, dtype=torch.bfloat16, device="cuda"), torch.zeros(2, device="cuda"),
-                    torch.zeros(1, 8, 128, dtype=torch.bfloat16, device="cuda"),
-                    torch.zeros(1, 8, 128, dtype=torch.bfloat16, device="cuda"))
+                    torch.zeros(1, 8, 300, dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros(1, 8, 300, dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == ssm.SSM_EUNSUPPORTED
+
+
+GENERIC = [
+    # B, L, H, P, N, dtype, gate, h0, softplus, bias
+    (2, 100, 3, 32, 64, "bf16", True, True, False, False),
+    (1, 77, 2, 64, 128, "f32", True, True, True, True),
+    (2, 50, 4, 16, 16, "bf16", False, True, False, True),
+    (1, 40, 2, 128, 256, "f32", True, False, False, False),
+    (2, 30, 3, 10, 7, "f32", True, True, True, False),
+    (1, 65, 5, 64, 64, "bf16", True, False, False, False),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,H,P,N,dt,gate,h0,sp,bias", GENERIC)
+def test_ssd_generic_shapes(ssm, Bsz, L, H, P, N, dt, gate, h0, sp, bias):
+    """Head dims and state sizes other than 64 / 128, and fp32: the generic scan kernel over
+    the H * P channels with one step size, decay, D and bias per head; every output against
+    the oracle."""
+    inp = synth.ssd_inputs(Bsz, L, H, P, N, dt, seed=700 + L + P + N, gate=gate, softplus_input=sp, h0=h0,
+                           delta_bias=bias)
+    import torch
+    t = {k: to_dev(inp[k], dt) for k in ("x", "delta", "z", "B", "C")}
+    for k in ("A", "Dskip", "delta_bias", "h0"):
+        t[k] = None if inp.get(k) is None else torch.from_numpy(inp[k]).cuda()
+    y, h = ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], t["z"], t["h0"],
+                       delta_softplus=inp["delta_softplus"], delta_bias=t["delta_bias"], return_last_state=True)
+    torch.cuda.synchronize()
+    yr, hr = ssd_oracle.ssd_storage(inp)
+    st = assert_close(to_host(y), yr, dt)
+    assert_close(to_host(h), hr, "f32", "h_last")
+    print(f"[parity] ssd generic {Bsz}x{L}x{H} P={P} N={N} {dt}: {json.dumps(st)}", flush=True)
 
 
 def test_ssd_determinism(ssm):
