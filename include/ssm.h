@@ -28,14 +28,18 @@
  *   bf16 outputs are rounded to nearest-even from the fp32 accumulator.
  * - The caller owns and allocates all memory, including the scan workspace
  *   (size from ssm_scan_workspace_bytes).  The library never allocates,
- *   frees or synchronises.
+ *   frees or synchronises (but see SSM_SYNC below).
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
  *   Argument checks run on the host before any launch; a rejected call
  *   launches nothing and writes nothing.  Faults inside a kernel surface at
  *   the caller's next synchronisation.
  * - Return value: an ssm_status.  On anything but SSM_OK a one-line reason is
  *   available from ssm_last_error() (per thread).  Nothing aborts, throws
- *   across the ABI or prints.
+ *   across the ABI or prints (but see SSM_LOG below).
+ * - Debugging aids, read once from the environment: SSM_LOG=1 prints one line per
+ *   call on stderr saying what the call launches (kernel path, plan, workspace);
+ *   SSM_SYNC=1 makes every launch wait for its stream, so that a kernel that fails
+ *   is reported as SSM_EHIP by the call that launched it.
  * - Thread safety: the library holds no global state beyond the per-thread
  *   error text; concurrent calls on different streams are independent.
  */

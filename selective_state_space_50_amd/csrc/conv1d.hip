@@ -311,12 +311,12 @@ hipError_t bwd_w(const ConvArgs &a, hipStream_t s) {
                     static_cast<unsigned>(a.B));
     if (vec) hipLaunchKernelGGL((conv1d_bwd_kernel<T, W, 4>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((conv1d_bwd_kernel<T, W, 1>), grid, dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_status(s);
     if (e != hipSuccess) return e;
     const int64_t n = a.D * (W + 1);
     hipLaunchKernelGGL(conv1d_bwd_finish_kernel, dim3(static_cast<unsigned>((n + 31) / 32)), dim3(256), 0, s, a,
                        tiles);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 template <typename T>
@@ -340,12 +340,12 @@ hipError_t fwd_w(const ConvArgs &a, hipStream_t s) {
     if (a.L > 0) {
         if (vec) hipLaunchKernelGGL((conv1d_fwd_kernel<T, W, 4>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((conv1d_fwd_kernel<T, W, 1>), grid, dim3(256), 0, s, a);
-        e = hipGetLastError();
+        e = launch_status(s);
     }
     if (e != hipSuccess || !a.state_out || W == 1) return e;
     const int64_t n = a.B * a.D * (W - 1);
     hipLaunchKernelGGL((conv1d_state_kernel<T>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 template <typename T>
@@ -367,7 +367,7 @@ hipError_t upd_t(const ConvArgs &a, hipStream_t s) {
         case 3: hipLaunchKernelGGL((conv1d_update_kernel<T, 3>), grid, dim3(256), 0, s, a); break;
         default: hipLaunchKernelGGL((conv1d_update_kernel<T, 4>), grid, dim3(256), 0, s, a); break;
     }
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 }  // namespace

@@ -34,7 +34,7 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
         float dv = widen(DL, ch) + (a.dbias ? a.dbias[d] : 0.0f);
         if (a.softplus) dv = softplus_f(dv);
         const float u = DISC == kZOH ? xv : dv * xv;
-        if (G == 4 && n0 + 4 <= N) {
+        if (G == 4 && N % 4 == 0 && n0 + 4 <= N) {
             float4 hv = *reinterpret_cast<const float4 *>(a.h + ch * N + n0);
             const float4 av = *reinterpret_cast<const float4 *>(a.A + d * N + n0);
             float hh[4] = {hv.x, hv.y, hv.z, hv.w};
@@ -149,7 +149,7 @@ void launch_upd(const UpdArgs &a, hipStream_t s) {
     }
     const int64_t threads = a.B * a.D * a.lpc;
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-    if (a.N % 4 == 0) hipLaunchKernelGGL((state_update_kernel<DISC, T, 4, HAS_Z>), grid, dim3(256), 0, s, a);
+    if (a.N % 4 == 0 || a.N > 64) hipLaunchKernelGGL((state_update_kernel<DISC, T, 4, HAS_Z>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((state_update_kernel<DISC, T, 1, HAS_Z>), grid, dim3(256), 0, s, a);
 }
 
@@ -173,7 +173,7 @@ hipError_t launch_state_update(const UpdArgs &a, int disc, bool bf16, bool has_z
         case kBilinear: launch_upd_d<kBilinear>(a, bf16, has_z, s); break;
         default: launch_upd_d<kMamba>(a, bf16, has_z, s); break;
     }
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 }  // namespace ssm

@@ -51,7 +51,7 @@ extern "C" int ssm_issue_probe(int op, int64_t workgroups, int64_t waves_per_wor
     if (op == 0) hipLaunchKernelGGL(issue_probe_kernel<0>, grid, block, 0, s, sink, iters);
     else if (op == 1) hipLaunchKernelGGL(issue_probe_kernel<1>, grid, block, 0, s, sink, iters);
     else hipLaunchKernelGGL(issue_probe_kernel<2>, grid, block, 0, s, sink, iters);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_status(s);
     if (e != hipSuccess) {
         set_error("issue probe launch: %s", hipGetErrorString(e));
         return SSM_EHIP;

@@ -562,7 +562,7 @@ hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
         const dim3 gc(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks - 1));
         if (has_z) hipLaunchKernelGGL((bwd_carry_kernel<T, true, BIL>), gc, dim3(kThreads), 0, s, a);
         else hipLaunchKernelGGL((bwd_carry_kernel<T, false, BIL>), gc, dim3(kThreads), 0, s, a);
-        e = hipGetLastError();
+        e = launch_status(s);
         if (e != hipSuccess) return e;
         const int64_t n = a.B * a.D * kN;
         const int64_t C1 = a.n_chunks - 1;
@@ -573,21 +573,21 @@ hipError_t launch_t(const BwdArgs &a, bool has_z, hipStream_t s) {
                                  bwd_combine_kernel<64>};
         const int64_t threads = n << lg;
         hipLaunchKernelGGL(k[lg], dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
-        e = hipGetLastError();
+        e = launch_status(s);
         if (e != hipSuccess) return e;
     }
     const dim3 grid(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks));
     if (has_z) hipLaunchKernelGGL((scan_bwd_kernel<T, true, DISC>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((scan_bwd_kernel<T, false, DISC>), grid, dim3(kThreads), 0, s, a);
-    e = hipGetLastError();
+    e = launch_status(s);
     if (e != hipSuccess) return e;
     const int64_t nbc = 2 * a.B * a.L * kN;
     hipLaunchKernelGGL((bwd_finish_bc_kernel<T>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, s, a);
-    e = hipGetLastError();
+    e = launch_status(s);
     if (e != hipSuccess) return e;
     const int64_t nad = a.D * kN + 2 * a.D;
     hipLaunchKernelGGL(bwd_finish_ad_kernel, dim3(static_cast<unsigned>((nad + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 template <int DISC>

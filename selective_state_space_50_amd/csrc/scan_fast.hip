@@ -25,7 +25,7 @@ hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, int disc, bool b
         else { SSM_PACK(float, 4) }
     }
 #undef SSM_PACK
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 SSM_CKPT_LAUNCHER(launch_scan_ckpt_mamba) { return launch_ckpt<kMamba>(a, grid, p, bf16, s); }

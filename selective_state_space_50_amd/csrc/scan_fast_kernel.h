@@ -677,7 +677,7 @@ hipError_t launch_t(const ScanArgs &a, dim3 grid, bool has_z, bool carry, size_t
     if (carry) hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, false, true>), grid, block, 0, s, a);
     else if (has_z) hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, true, false>), grid, block, lds_reserve, s, a);
     else hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, false, false>), grid, block, lds_reserve, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 template <int DISC, typename T>
@@ -700,7 +700,7 @@ hipError_t launch_save_t(const ScanArgs &a, dim3 grid, bool has_z, size_t lds_re
     const dim3 block(64 * waves_per_block<G>());
     if (has_z) hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, true, false, true>), grid, block, lds_reserve, s, a);
     else hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, false, false, true>), grid, block, lds_reserve, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 template <int DISC>
@@ -715,7 +715,7 @@ template <int DISC, typename T, int G>
 hipError_t launch_ckpt_t(const ScanArgs &a, dim3 grid, size_t lds_reserve, hipStream_t s) {
     hipLaunchKernelGGL((scan_fast_kernel<DISC, T, G, false, true, true>), grid,
                        dim3(64 * waves_per_block<G>()), lds_reserve, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 template <int DISC>

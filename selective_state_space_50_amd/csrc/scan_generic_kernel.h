@@ -296,7 +296,7 @@ hipError_t launch_scan_t(const ScanArgs &a, dim3 grid, int NW, hipStream_t s) {
     const Smem S = smem_layout(TB, NW, G, CARRY);
     const size_t lds = static_cast<size_t>(S.total) * sizeof(float);
     hipLaunchKernelGGL((scan_kernel<DISC, T, G, TB, HAS_Z, CARRY, MAXT>), grid, dim3(NW * 64), lds, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 // The zero-order-hold and bilinear kernels always stage 8 steps per block (a block size

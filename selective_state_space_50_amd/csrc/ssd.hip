@@ -444,7 +444,7 @@ hipError_t launch_ssd(const SsdArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(((W + 7) / 8) * 8));
     if (a.z) hipLaunchKernelGGL((ssd_kernel<true>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((ssd_kernel<false>), grid, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 }  // namespace ssm

@@ -12,6 +12,14 @@
 #include <mutex>
 
 namespace ssm {
+
+hipError_t launch_status(hipStream_t s) {
+    static const bool sync = env_flag("SSM_SYNC");
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && sync) e = hipStreamSynchronize(s);
+    return e;
+}
+
 namespace {
 
 // Carries of the carry pass, folded in sequence order with a parallel scan (segment_scan in
@@ -105,7 +113,7 @@ hipError_t launch_seg(K kernels[7], int S, int64_t items, hipStream_t s, const S
     while ((1 << lg) < S) ++lg;
     const int64_t threads = items * S;
     hipLaunchKernelGGL(kernels[lg], dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 hipError_t launch_combine(const ScanArgs &a, hipStream_t s) {
@@ -123,7 +131,7 @@ hipError_t launch_local_combine(const ScanArgs &a, float *h_last, hipStream_t s)
     while ((1 << lg) < S) ++lg;
     const int64_t threads = a.B * a.D * a.N * S;
     hipLaunchKernelGGL(k[lg], dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a, h_last);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 // n 16-bit words of zeros (any output of a gradient that has no terms)
@@ -177,6 +185,12 @@ int run_scan(const ScanPlan &p, int64_t batch, int64_t seqlen, int64_t dim, int6
     a.softplus = delta_softplus;
     a.dbias = variant_bias(variant);
     const int disc = variant_disc(variant);
+    log_call("scan B=%lld L=%lld D=%lld N=%lld dtype=%d disc=%d: %s kernel, %d states/lane, %d waves, %d-step "
+             "blocks, %lld chunk(s) of %lld%s, structured-A check %s, workspace %zu B%s",
+             (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, dtype, disc,
+             p.fast ? "specialised" : "generic", p.G, p.NW, p.TB, (long long)p.n_chunks, (long long)p.chunk_len,
+             p.local && disc != kBilinear && !ckpt ? " (local scans)" : "", p.structured ? "on" : "off",
+             p.ws_bytes, ckpt ? ", storing checkpoints" : "");
     a.structured = p.structured ? 1 : 0;
     a.NW = p.NW;
     a.chunk_len = p.chunk_len;
@@ -270,7 +284,7 @@ extern "C" int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         const int64_t n = batch * dim * dstate;
         hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                            0, s, h_last, h0, n);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_status(s);
         return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
     }
     return run_scan(p, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
@@ -344,7 +358,7 @@ extern "C" int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, 
         const int64_t n = batch * dim * dstate;
         hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                            0, s, h_last, h0, n);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_status(s);
         return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
     }
     return run_scan(p, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
@@ -366,10 +380,14 @@ extern "C" int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int 
     a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C; a.A = A; a.Dskip = Dskip; a.y = y;
     a.softplus = delta_softplus;
     a.dbias = variant_bias(variant);
-    const int G = (dstate % 4 == 0) ? 4 : 1;
+    // four states per lane (one 16-byte access when dstate % 4 == 0), one when fewer than 64
+    // states are not a multiple of four; at most 64 lanes per channel
+    const int G = (dstate % 4 == 0 || dstate > 64) ? 4 : 1;
     int lpc = 1;
     while (lpc * G < dstate) lpc *= 2;
     a.lpc = lpc;
+    log_call("state_update B=%lld D=%lld N=%lld dtype=%d: %d states per lane, %d lanes per channel",
+             (long long)batch, (long long)dim, (long long)dstate, dtype, G, lpc);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_state_update(a, variant_disc(variant), dtype == SSM_DTYPE_BF16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("state update launch", e);
@@ -393,7 +411,7 @@ extern "C" int ssm_scan_fwd_save(int64_t batch, int64_t seqlen, int64_t dim, int
         const int64_t n = batch * dim * dstate;
         hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                            0, s, h_last, h0, n);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_status(s);
         return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
     }
     return run_scan(bp.fwd, batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, h0, h_last, y,
@@ -516,7 +534,7 @@ hipError_t pad3(void *dst, const void *src, int64_t n0, int64_t n1, int64_t n2, 
     else
         hipLaunchKernelGGL(pad3_kernel<float>, g, dim3(256), 0, s, static_cast<float *>(dst),
                            static_cast<const float *>(src), n0, n1, n2, m1, m2, fill);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 hipError_t unpad3(void *dst, const void *src, int64_t n0, int64_t n1, int64_t n2, int64_t m1, int64_t m2,
@@ -528,7 +546,7 @@ hipError_t unpad3(void *dst, const void *src, int64_t n0, int64_t n1, int64_t n2
     else
         hipLaunchKernelGGL(unpad3_kernel<float>, g, dim3(256), 0, s, static_cast<float *>(dst),
                            static_cast<const float *>(src), n0, n1, n2, m1, m2);
-    return hipGetLastError();
+    return launch_status(s);
 }
 
 }  // namespace
@@ -549,6 +567,11 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
                             dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_softplus, discretization,
                             delta_bias, ddelta_bias, checkpoints, workspace, workspace_bytes, &p);
     if (st != SSM_OK) return st;
+    log_call("scan_bwd B=%lld L=%lld D=%lld N=%lld dtype=%d disc=%d: %s, %lld chunk(s) of %lld, %s, workspace %zu B",
+             (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, dtype, discretization,
+             p.pad ? "native kernels on padded copies" : "native kernels", (long long)p.n_chunks,
+             (long long)p.chunk_len, checkpoints ? "saved checkpoints" : "own checkpoint pass",
+             checkpoints ? p.ws_bytes_saved : p.ws_bytes);
     if (dim == 0) return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -558,23 +581,23 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
             const int64_t n = batch * dim * dstate;
             hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                                0, s, dh0, dh_last, n);
-            e = hipGetLastError();
+            e = launch_status(s);
             if (e != hipSuccess) return hip_fail("fill_state launch", e);
         }
         hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim * dstate + 255) / 256)),
                            dim3(256), 0, s, dA, static_cast<const float *>(nullptr), dim * dstate);
-        e = hipGetLastError();
+        e = launch_status(s);
         if (e != hipSuccess) return hip_fail("fill_state launch", e);
         if (Dskip && dD) {
             hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
                                0, s, dD, static_cast<const float *>(nullptr), dim);
-            e = hipGetLastError();
+            e = launch_status(s);
             if (e != hipSuccess) return hip_fail("fill_state launch", e);
         }
         if (delta_bias) {
             hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((dim + 255) / 256)), dim3(256),
                                0, s, ddelta_bias, static_cast<const float *>(nullptr), dim);
-            e = hipGetLastError();
+            e = launch_status(s);
             if (e != hipSuccess) return hip_fail("fill_state launch", e);
         }
         return SSM_OK;
@@ -683,7 +706,7 @@ extern "C" int ssm_conv1d_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_
             const int64_t n = bytes / 2;
             hipLaunchKernelGGL(zero16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
                                static_cast<uint16_t *>(p), n);
-            return hipGetLastError();
+            return launch_status(s);
         };
         e = zero(dw, dim * width * 4);
         if (e == hipSuccess) e = zero(dbias, dim * 4);
@@ -730,9 +753,13 @@ extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_
         const int64_t n = batch * nheads * headdim * dstate;
         hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
                            h_last, h0, n);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_status(s);
         return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
     }
+    log_call("ssd B=%lld L=%lld H=%lld P=%lld N=%lld dtype=%d: %s", (long long)batch, (long long)seqlen,
+             (long long)nheads, (long long)headdim, (long long)dstate, dtype,
+             headdim == 64 && dstate == 128 && dtype == SSM_DTYPE_BF16 ? "matrix-core kernel"
+                                                                       : "generic scan kernel, multi-head layout");
     if (headdim != 64 || dstate != 128 || dtype != SSM_DTYPE_BF16) {
         // other head dims, state sizes and fp32: the generic scan kernel over the H * P
         // channels in its multi-head layout (one step size, decay, D and bias per head; B, C

@@ -218,7 +218,13 @@ __device__ __forceinline__ void segment_scan(float &P, float &H) {
     }
 }
 
-// Launchers (each returns the hipGetLastError() of its launch).
+// The status of the launch just made on stream s (hipGetLastError).  With SSM_SYNC=1 in the
+// environment it also waits for s, so that a kernel that fails is reported, as SSM_EHIP, by
+// the entry point that launched it rather than by a later call: a debugging aid that
+// serialises the host with the GPU.
+hipError_t launch_status(hipStream_t s);
+
+// Launchers (each returns the launch_status of its launch).
 // The scan kernels of each discretisation live in their own translation units (built in
 // parallel): *_mamba in scan_generic.hip / scan_fast.hip, *_zoh and *_bilinear in the
 // files of those names.

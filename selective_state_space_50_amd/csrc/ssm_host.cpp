@@ -2,6 +2,7 @@
 #include "ssm_host.h"
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
@@ -92,6 +93,22 @@ int check_aligned(const Range *all, int n) {
     return SSM_OK;
 }
 }  // namespace
+
+bool env_flag(const char *name) {
+    const char *v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+void log_call(const char *fmt, ...) {
+    static const bool on = env_flag("SSM_LOG");
+    if (!on) return;
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "[ssm] %s\n", buf);
+}
 
 void set_error(const char *fmt, ...) {
     va_list ap;

@@ -44,6 +44,12 @@ constexpr int64_t kLocalMinChunk = 4 * kLocalPrefix;
 
 // Per-thread error text (ssm_last_error).
 void set_error(const char *fmt, ...);
+// Whether the environment variable name is set to something other than "" or "0" (read
+// once per name by its callers).
+bool env_flag(const char *name);
+// SSM_LOG=1: one line per call on stderr describing what the entry point launches (shape,
+// kernel path, plan).  Nothing is printed otherwise.
+void log_call(const char *fmt, ...);
 void clear_error();
 
 // Shape and option checks + plan.  Returns an ssm_status.

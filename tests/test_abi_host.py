@@ -122,3 +122,21 @@ def test_host_checks_under_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok: 0 failure(s)" in r.stdout
+
+
+def test_ssm_log_prints_the_plan():
+    """SSM_LOG=1: every call says on stderr what it launches (the launch itself fails here,
+    without a GPU, after the line is printed); unset, nothing is printed."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import tests.test_abi_host as t, selective_state_space_50_amd as ssm; "
+            "print(t._scan_status(ssm.lib(), D=65, N=8))")
+    env = {k: v for k, v in os.environ.items() if k not in ("SSM_LOG", "SSM_SYNC")}
+    on = subprocess.run([sys.executable, "-c", code], env={**env, "SSM_LOG": "1"}, cwd=root,
+                        capture_output=True, text=True, timeout=300)
+    assert "[ssm] scan B=1 L=8 D=65 N=8 dtype=1 disc=0: generic kernel" in on.stderr, on.stderr[-2000:]
+    off = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert "[ssm]" not in off.stderr

@@ -30,6 +30,7 @@ LARGE = [
     (1, 33, 64, 128, "f32", True, True, False, "mamba", "mamba"),
     (1, 20, 96, 256, "f32", True, True, False, "random", "mamba"),
     (2, 9, 5, 200, "bf16", False, True, False, "random", "zoh"),
+    (1, 12, 70, 255, "f32", True, True, False, "random", "mamba"),
 ]
 
 
@@ -68,7 +69,8 @@ def test_scan_more_than_16_states_chunked(ssm, N, chunk):
 
 
 @pytest.mark.parametrize("Bsz,D,N,dt", [(2, 70, 32, "f32"), (3, 64, 64, "bf16"), (1, 33, 256, "f32"),
-                                        (2, 128, 100, "bf16")])
+                                        (2, 128, 100, "bf16"), (2, 40, 130, "f32"), (1, 65, 255, "bf16"),
+                                        (2, 10, 37, "f32")])
 def test_state_update_more_than_16_states(ssm, Bsz, D, N, dt):
     import torch
     A = synth.make_A(7, D, N, "random")
