@@ -938,6 +938,13 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         "workload": c["name"], "state_updates_per_s": upd / (ms * 1e-3), "ms_per_call": ms,
         "plan": plan, "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "alu_frac_single_pass_work": round(slots / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+        "roofline": {"bound": "alu", "achieved": round(slots / (ms * 1e-3) / 1e12, 3),
+                     "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
+                     "frac": round(slots / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
+                     "traffic": load_traffic("long_B1_L1048576_D1024_N16_bf16", src_hash),
+                     "alg_slots_per_call": slots, "alg_bytes_per_call": byts,
+                     "note": "slots of one pass over the sequence (structured path); the call also rescans "
+                             "the 4096-step prefixes of 15 chunks"},
         "workspace_bytes": plan["workspace_bytes"],
         "note": "all launches of one call inside the events: B/C pre-pass, every chunk scanned from its own "
                 "start, the carry combine (a parallel scan over chunks), the 4096-step prefix of every later "
