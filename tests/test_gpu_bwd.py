@@ -203,6 +203,28 @@ def test_autograd_matches_oracle(ssm):
         assert_close_grad(to_host(leaves[k].grad), r[rk], "f32", f"autograd {k}")
 
 
+def test_autograd_generic_shape(ssm):
+    """selective_scan with 8 states over 40 channels: the generic forward, then the backward
+    on padded copies; gradients of <w, y> for every input against the oracle."""
+    import torch
+    seed = 77
+    inp = synth.scan_inputs(2, 33, 40, 8, "f32", seed=seed, gate=True, d_kind="normal", a_kind="random",
+                            softplus_input=True, h0=True)
+    inp["delta_bias"] = synth.make_delta_bias(seed, 40)
+    gy = synth.store(np.random.default_rng(seed).standard_normal((2, 33, 40)).astype(np.float32), "f32")
+    t = device_inputs(inp)
+    t["bias"] = torch.from_numpy(inp["delta_bias"]).cuda()
+    leaves = {k: t[k].clone().requires_grad_(True) for k in ("x", "delta", "A", "B", "C", "D", "z", "h0", "bias")}
+    y = ssm.selective_scan(leaves["x"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"], leaves["D"],
+                           leaves["z"], leaves["h0"], delta_softplus=True, delta_bias=leaves["bias"])
+    (y * to_dev(gy, "f32")).sum().backward()
+    r = oracle.scan_bwd(inp, synth.to_f64(gy, "f32"))
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0",
+             "bias": "ddelta_bias"}
+    for k, rk in names.items():
+        assert_close_grad(to_host(leaves[k].grad), r[rk], "f32", f"autograd generic {k}")
+
+
 @pytest.mark.timeout(900)
 def test_backward_headline_shape_full(ssm):
     """The backward at the B4 L4096 D4096 N16 bf16 gated layer, in the launch the bench

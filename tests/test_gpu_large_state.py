@@ -88,6 +88,24 @@ def test_state_update_more_than_16_states(ssm, Bsz, D, N, dt):
         assert_close(to_host(h), h_ref, "f32", "h")
 
 
+def test_scan_more_than_16_states_with_delta_bias(ssm):
+    """A per-channel step-size bias (before the softplus) with 48 states, all three maps."""
+    import torch
+    for disc in ("mamba", "zoh", "bilinear"):
+        inp = synth.scan_inputs(2, 60, 70, 48, "f32", seed=650, gate=True, d_kind="normal", a_kind="random",
+                                softplus_input=True, h0=True)
+        inp["discretization"] = disc
+        inp["delta_bias"] = synth.make_delta_bias(650, 70)
+        t = device_inputs(inp)
+        y, h = ssm.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                            delta_softplus=True, discretization=disc,
+                            delta_bias=torch.from_numpy(inp["delta_bias"]).cuda(), return_last_state=True)
+        torch.cuda.synchronize()
+        yr, hr = oracle.scan(inp)
+        assert_close(to_host(y), yr, "f32", f"y {disc}")
+        assert_close(to_host(h), hr, "f32", f"h_last {disc}")
+
+
 def test_more_than_256_states_rejected(ssm):
     import torch
     x = torch.zeros((1, 4, 64), device="cuda")
