@@ -37,16 +37,7 @@ struct Row<uint16_t, 4> {
         const uint32_t v = i < 2 ? r.x : r.y;
         return (i & 1) ? bf_hi(v) : bf_lo(v);
     }
-    // inputs are streamed once (besides the W - 1 halo rows of a tile): non-temporal loads,
-    // which took the forward from 70 to 60 us and the backward from 114 to 104 us in a
-    // same-process A/B at x [4, 4096, 4096]
-    __device__ static Row load(const uint16_t *p) {
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-        Row o;
-        o.r = make_uint2(v.x, v.y);
-        return o;
-    }
+    __device__ static Row load(const uint16_t *p) { Row o; o.r = *reinterpret_cast<const uint2 *>(p); return o; }
     // outputs are written once: non-temporal stores
     __device__ static void store(uint16_t *p, const float (&v)[4]) {
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -57,13 +48,7 @@ template <>
 struct Row<float, 4> {
     float4 r;
     __device__ float get(int i) const { return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w; }
-    __device__ static Row load(const float *p) {
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-        Row o;
-        o.r = make_float4(v.x, v.y, v.z, v.w);
-        return o;
-    }
+    __device__ static Row load(const float *p) { Row o; o.r = *reinterpret_cast<const float4 *>(p); return o; }
     __device__ static void store(float *p, const float (&v)[4]) {
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
