@@ -34,6 +34,7 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
         float dv = widen(DL, ch) + (a.dbias ? a.dbias[d] : 0.0f);
         if (a.softplus) dv = softplus_f(dv);
         const float u = DISC == kZOH ? xv : dv * xv;
+        const float dv2 = dv * dv;
         if (G == 4 && N % 4 == 0 && n0 + 4 <= N) {
             float4 hv = *reinterpret_cast<const float4 *>(a.h + ch * N + n0);
             const float4 av = *reinterpret_cast<const float4 *>(a.A + d * N + n0);
@@ -42,8 +43,8 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float ab;
-                hh[g] = disc_step<DISC>(hh[g], dv, u, widen(Bm, b * N + n0 + g), aa[g] * kLog2e,
-                                        disc_aux<DISC>(aa[g]), ab);
+                hh[g] = disc_step<DISC>(hh[g], dv, dv2, u, widen(Bm, b * N + n0 + g), aa[g] * kLog2e,
+                                        disc_const<DISC>(aa[g]), ab);
                 yp = __builtin_fmaf(widen(Cm, b * N + n0 + g), hh[g], yp);
             }
             *reinterpret_cast<float4 *>(a.h + ch * N + n0) = make_float4(hh[0], hh[1], hh[2], hh[3]);
@@ -54,8 +55,8 @@ __global__ void __launch_bounds__(256) state_update_kernel(UpdArgs a) {
                 if (n < N) {
                     const float av = a.A[d * N + n];
                     float ab;
-                    float hv = disc_step<DISC>(a.h[ch * N + n], dv, u, widen(Bm, b * N + n), av * kLog2e,
-                                               disc_aux<DISC>(av), ab);
+                    float hv = disc_step<DISC>(a.h[ch * N + n], dv, dv2, u, widen(Bm, b * N + n), av * kLog2e,
+                                               disc_const<DISC>(av), ab);
                     a.h[ch * N + n] = hv;
                     yp = __builtin_fmaf(widen(Cm, b * N + n), hv, yp);
                 }
@@ -127,7 +128,7 @@ __global__ void __launch_bounds__(256) state_update_q16_kernel(UpdArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         float ab;
-        hv[g] = disc_step<DISC>(hv[g], dv, u, bv[g], av[g] * kLog2e, disc_aux<DISC>(av[g]), ab);
+        hv[g] = disc_step<DISC>(hv[g], dv, dv * dv, u, bv[g], av[g] * kLog2e, disc_const<DISC>(av[g]), ab);
         yp = __builtin_fmaf(cv[g], hv[g], yp);
     }
     const u32x4 hw = {__float_as_uint(hv[0]), __float_as_uint(hv[1]), __float_as_uint(hv[2]), __float_as_uint(hv[3])};

@@ -124,12 +124,13 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     const T *Bm = static_cast<const T *>(a.Bm) + b * L * kN;
     const T *Cm = static_cast<const T *>(a.Cm) + b * L * kN;
 
-    float Av[kG], Al[kG], aux[kG];
+    float Av[kG], Al[kG];
+    DiscK<DISC> kc[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
         Av[g] = a.A[d * kN + n0 + g];
         Al[g] = Av[g] * kLog2e;
-        aux[g] = disc_aux<DISC>(Av[g]);
+        kc[g] = disc_const<DISC>(Av[g]);
     }
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
     const float dbv = a.dbias ? a.dbias[d] : 0.0f;
@@ -230,12 +231,12 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                         if constexpr (DISC == kZOH) {   // as the forward: e h + f (x B)
                             const float sx = dt * Al[g];
                             const float e = __builtin_amdgcn_exp2f(sx);
-                            const float f = zoh_factor(dt, sx, e, aux[g]);
+                            const float f = zoh_factor(dt, dt * dt, sx, e, kc[g]);
                             h[g] = __builtin_fmaf(e, h[g], f * (pv.w * Bv[g]));
                             as[i][g] = e;
                             fs[i][g] = f;
                         } else {                        // as the forward: r (2 h + dt x B) - h
-                            const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(-dt, aux[g], 1.0f));
+                            const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(-dt, kc[g].v, 1.0f));
                             h[g] = __builtin_fmaf(r, __builtin_fmaf(2.0f, h[g], u * Bv[g]), -h[g]);
                             as[i][g] = __builtin_fmaf(2.0f, r, -1.0f);
                             fs[i][g] = r;
@@ -278,7 +279,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                             // (dt a - f) / A, which is the same quantity since f = (a - 1) / A
                             const float u = dt * Av[g];
                             df_dA = __builtin_fabsf(u) < 0.5f ? dt * dt * zoh_psi_series(u)
-                                                               : __builtin_fmaf(dt, ab, -fs[i][g]) * aux[g];
+                                                               : __builtin_fmaf(dt, ab, -fs[i][g]) * kc[g].inv_a;
                         } else {
                             const float r = fs[i][g], r2 = r * r;
                             f = r * dt;
@@ -411,7 +412,7 @@ __global__ void __launch_bounds__(kThreads) bwd_carry_kernel(BwdArgs a) {
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
         Al[g] = a.A[d * kN + n0 + g] * kLog2e;
-        ah[g] = disc_aux<kBilinear>(a.A[d * kN + n0 + g]);   // A / 2
+        ah[g] = disc_const<kBilinear>(a.A[d * kN + n0 + g]).v;   // A / 2
     }
     const float dbv = a.dbias ? a.dbias[d] : 0.0f;
     const int64_t t0c = cc * a.chunk_len;

@@ -12,8 +12,9 @@ namespace {
 hipError_t launch_bc_pack(const ScanArgs &a, const ScanPlan &p, int disc, bool bf16, hipStream_t s) {
     const int64_t total = a.B * a.n_chunks * a.bc_lpad * kN;
     const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-    // the Mamba kernels map lane slot g of compute wave w to state w + g * (16 / G)
-    const bool strided = disc == kMamba;
+    // the Mamba and zero-order-hold kernels map lane slot g of compute wave w to state
+    // w + g * (16 / G)
+    const bool strided = disc != kBilinear;
 #define SSM_PACK(T, G)                                                                                  \
     if (strided) hipLaunchKernelGGL((bc_pack_kernel<T, G, true>), grid, dim3(256), 0, s, a);           \
     else hipLaunchKernelGGL((bc_pack_kernel<T, G, false>), grid, dim3(256), 0, s, a);

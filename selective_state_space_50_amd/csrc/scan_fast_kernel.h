@@ -136,8 +136,8 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
 // backward).  CKPT without CARRY: the ordinary forward (y, h_last) that also stores those
 // checkpoints.  DISC: the discretisation (kMamba, kZOH, kBilinear).
 //
-// Structured A (the Mamba discretisation).  Exp(dt A[d,n]) is the one transcendental of a
-// state update.  The Mamba kernels give compute wave w the states n = w + g*NC (g < G) of
+// Structured A (the Mamba and zero-order-hold discretisations).  Exp(dt A[d,n]) is the one
+// transcendental of a state update.  These kernels give compute wave w the states n = w + g*NC (g < G) of
 // its lane's channel.  When A[d, n + NC] - A[d, n] is one constant c_d for every n of the
 // channel -- true of the usual initialisation A[d,n] = -(n+1) (skill page "State Space
 // Models Mamba", MambaBlock: A_log = log(1..N)) -- the decays of a lane's states satisfy
@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
 // call that asks for the general path (ScanArgs::structured == 0), takes the general path.
 template <int DISC, typename T, int G, bool HAS_Z, bool CARRY, bool CKPT = false>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
-    constexpr bool ST = DISC == kMamba;   // structured-A capable, strided state mapping
+    constexpr bool ST = DISC != kBilinear;   // structured-A capable, strided state mapping
     constexpr int NC = kN / G;          // compute waves
     constexpr int RPT = 2;              // rows per helper thread
     static_assert(kTB / RPT * 32 == helper_waves<G>() * 64, "helpers cover the block in row pairs x channel pairs");
@@ -207,7 +207,8 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     // state of lane slot g
     auto st_n = [&](int g) __attribute__((always_inline)) { return ST ? wc + g * NC : wc * G + g; };
     const int64_t d = d0 + lane;
-    float Al[G], aux[G], h[G], pc[G];
+    float Al[G], h[G], pc[G];
+    DiscK<DISC> kc[G];
     float dsum = 0.0f;
     // packed B/C of this wave's states in block 0 of this chunk: [step][g][B, C]; the
     // rows of the NC waves alternate every kTB steps
@@ -423,18 +424,23 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 const float *bB = bc_c + 2 * q * G;             // B of steps 2q, 2q+1: [step][g]
                 const float *bC = bc_c + SUB * G + 2 * q * G;   // C of the same steps
                 // one step of state slot g: general, or (structured) the decay of slot g - 1
-                // times E
-                auto upd = [&](int g, float dt, float u, float bv, float ev, float &e) __attribute__((always_inline)) {
+                // times E.  dt2 = dt^2 (zero-order hold), once per step for the G slots.
+                auto upd = [&](int g, float dt, float dt2, float u, float bv, float ev, float &e) __attribute__((always_inline)) {
                     if (STR && g > 0) {
                         e *= ev;   // exp(dt A[n + NC]) = exp(dt A[n]) exp(dt c_d)
-                        h[g] = __builtin_fmaf(e, h[g], u * bv);
+                        if constexpr (DISC == kZOH)
+                            h[g] = __builtin_fmaf(e, h[g], zoh_factor(dt, dt2, dt * Al[g], e, kc[g]) * (u * bv));
+                        else
+                            h[g] = __builtin_fmaf(e, h[g], u * bv);
                         return e;
                     }
                     float ab;
-                    h[g] = disc_step<DISC>(h[g], dt, u, bv, Al[g], aux[g], ab);
+                    h[g] = disc_step<DISC>(h[g], dt, dt2, u, bv, Al[g], kc[g], ab);
                     e = ab;
                     return ab;
                 };
+                const float dt2a = DISC == kZOH ? du.x * du.x : 0.0f;
+                const float dt2b = DISC == kZOH ? du.z * du.z : 0.0f;
                 const float ev0 = STR ? e_c[q].x : 0.0f, ev1 = STR ? e_c[q].y : 0.0f;
                 if constexpr (CARRY) {
                     if constexpr (DISC != kBilinear) {
@@ -444,17 +450,17 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                     float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        const float ab0 = upd(g, du.x, du.y, bB[g], ev0, e0);
-                        const float ab1 = upd(g, du.z, du.w, bB[G + g], ev1, e1);
+                        const float ab0 = upd(g, du.x, dt2a, du.y, bB[g], ev0, e0);
+                        const float ab1 = upd(g, du.z, dt2b, du.w, bB[G + g], ev1, e1);
                         if constexpr (DISC == kBilinear) pc[g] *= ab0 * ab1;
                     }
                 } else {
                     float y0, y1, e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        upd(g, du.x, du.y, bB[g], ev0, e0);
+                        upd(g, du.x, dt2a, du.y, bB[g], ev0, e0);
                         y0 = g == 0 ? bC[0] * h[0] : __builtin_fmaf(bC[g], h[g], y0);
-                        upd(g, du.z, du.w, bB[G + g], ev1, e1);
+                        upd(g, du.z, dt2b, du.w, bB[G + g], ev1, e1);
                         y1 = g == 0 ? bC[G] * h[0] : __builtin_fmaf(bC[G + g], h[g], y1);
                     }
                     sY[P][(w * kTB / 2 + sb * SUB / 2 + q) * 64 + lane] = make_float2(y0, y1);
@@ -499,7 +505,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         for (int g = 0; g < G; ++g) {
             const float av = a.A[d * kN + st_n(g)];
             Al[g] = av * kLog2e;
-            aux[g] = disc_aux<DISC>(av);
+            kc[g] = disc_const<DISC>(av);
             pc[g] = 1.0f;
             float hv = 0.0f;
             // carries, and the local scan's chunks >= 1, start from zero; chunk 0 from h0; the

@@ -93,14 +93,15 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
 
     // per-lane state: G states of channel d, with A pre-scaled by log2(e), the
     // discretisation's second per-state constant, and (bilinear carries) the product of A_bar
-    float Al[G], aux[G], h[G], pc[G];
+    float Al[G], h[G], pc[G];
+    DiscK<DISC> kc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int64_t n = n0 + g;
         const bool ok = dvalid && n < N;
         const float av = ok ? (a.head_dim > 0 ? a.A[dh] : a.A[d * N + n]) : 0.0f;
         Al[g] = av * kLog2e;
-        aux[g] = disc_aux<DISC>(av);
+        kc[g] = disc_const<DISC>(av);
         pc[g] = 1.0f;
         float hv = 0.0f;
         if (!CARRY && ok) {
@@ -224,12 +225,13 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
                     if constexpr (!CARRY) lds_vec<G>(sC + (i + 1) * NP + n0, cv_n);
                 }
             }
+            const float dt2 = du.x * du.x;
             if constexpr (CARRY) {
                 if constexpr (DISC != kBilinear) dsum += du.x;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     float ab;
-                    h[g] = disc_step<DISC>(h[g], du.x, du.y, bv[g], Al[g], aux[g], ab);
+                    h[g] = disc_step<DISC>(h[g], du.x, dt2, du.y, bv[g], Al[g], kc[g], ab);
                     if constexpr (DISC == kBilinear) pc[g] *= ab;
                 }
             } else {
@@ -237,7 +239,7 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     float ab;
-                    h[g] = disc_step<DISC>(h[g], du.x, du.y, bv[g], Al[g], aux[g], ab);
+                    h[g] = disc_step<DISC>(h[g], du.x, dt2, du.y, bv[g], Al[g], kc[g], ab);
                     yp = g == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[g], h[g], yp);
                 }
                 sY[(w * TB + i) * 64 + lane] = yp;

@@ -150,49 +150,77 @@ __device__ __forceinline__ float silu_f(float zv) {
 // ---- discretisations (the values of ssm_discretization)
 constexpr int kMamba = 0, kZOH = 1, kBilinear = 2;
 
-// Per-state constant besides A log2(e): 1/A for the zero-order hold (infinite where
-// A = 0; that state always takes the series branch of zoh_factor), A/2 for the
-// bilinear map.
+// Per-state constants of a discretisation besides A log2(e): A/2 for the bilinear map,
+// the zero-order hold's in DiscK<kZOH> (zoh_const), nothing for the Mamba map.
 template <int DISC>
-__device__ __forceinline__ float disc_aux(float A) {
-    if constexpr (DISC == kZOH) return 1.0f / A;
-    else if constexpr (DISC == kBilinear) return 0.5f * A;
-    else return 0.0f;
-}
+struct DiscK {
+    float v;
+};
+template <>
+struct DiscK<kZOH> {
+    float c1, c2, c3;   // A log2(e) times the series coefficients ln2/2, ln2^2/6, ln2^3/24
+    float inv_a, off;   // 1/A and -1/A - beta (0 and -inf where 1/A is not finite)
+};
 
-// Zero-order hold, B_bar / B = (exp(dt A) - 1) / A, with s = dt A log2(e) and
-// e = exp(dt A) = 2^s already computed.  e - 1 cancels when |dt A| is small, so there
-// the Taylor series dt (1 + z/2 + z^2/6 + z^3/24), z = dt A, is used instead (written in
-// s: z = s ln 2).  At the switch |z| = 0.1 the series' truncation (z^4 / 120) and the
-// rounding of e relative to e - 1 (about 2^-24 / |z|) are both below 1e-6.  The
-// direct branch is one fma: e / A - 1 / A rounded once.
-__device__ __forceinline__ float zoh_factor(float dt, float s, float e, float inv_a) {
+// Zero-order hold, f = B_bar / B = (exp(z) - 1) / A with z = dt A, s = z log2(e) and
+// e = exp(z) = 2^s already computed.  Two estimates of f, both never above it:
+//  * the series dt (1 + z/2 + z^2/6 + z^3/24) = dt + dt^2 A log2(e) (k1 + k2 s + k3 s^2):
+//    the terms it drops sum to dt e^xi z^4 / 120 >= 0 (Lagrange remainder), so it is
+//    below f; its error grows as z^4;
+//  * the direct form (e - 1)/A, lowered by beta = 8 2^-24 / |A|: e carries a few ulps of
+//    rounding (less than 8 2^-24 in absolute terms near 1), which e - 1 turns into an
+//    error of up to 8 2^-24 / |A| when z is small; it is one fma, e / A + (-1/A - beta).
+// The larger of the two is therefore the closer to f: one max instead of a comparison and
+// a select.  Over every z the result is within 6e-6 of f (relative), worst where the two
+// errors cross near |z| = 0.15.  Where A = 0 (or 1/A overflows) the direct form is -inf
+// and the series is exactly dt.
+__device__ __forceinline__ DiscK<kZOH> zoh_const(float A) {
     constexpr float k1 = 0.34657359027997264f;    // ln2 / 2
     constexpr float k2 = 0.08007550231970023f;    // ln2^2 / 6
     constexpr float k3 = 0.013876027166205393f;   // ln2^3 / 24
-    constexpr float kSwitch = 0.14426950408889634f;   // |z| = 0.1 in units of s
-    const float ser = dt * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(k3, s, k2), s, k1), s, 1.0f);
-    const float dir = __builtin_fmaf(e, inv_a, -inv_a);
-    return __builtin_fabsf(s) < kSwitch ? ser : dir;
+    const float al = A * kLog2e;
+    DiscK<kZOH> k;
+    k.c1 = al * k1;
+    k.c2 = al * k2;
+    k.c3 = al * k3;
+    const float inv = 1.0f / A;
+    const bool fin = __builtin_fabsf(inv) <= 3.4028234663852886e38f;
+    k.inv_a = fin ? inv : 0.0f;
+    k.off = fin ? -inv - 4.76837158203125e-07f * __builtin_fabsf(inv) : -__builtin_inff();   // 8 2^-24
+    return k;
+}
+
+__device__ __forceinline__ float zoh_factor(float dt, float dt2, float s, float e, const DiscK<kZOH> &k) {
+    const float ser = __builtin_fmaf(dt2, __builtin_fmaf(__builtin_fmaf(k.c3, s, k.c2), s, k.c1), dt);
+    const float dir = __builtin_fmaf(e, k.inv_a, k.off);
+    return __builtin_fmaxf(ser, dir);
+}
+
+template <int DISC>
+__device__ __forceinline__ DiscK<DISC> disc_const(float A) {
+    if constexpr (DISC == kZOH) return zoh_const(A);
+    else if constexpr (DISC == kBilinear) return DiscK<DISC>{0.5f * A};
+    else return DiscK<DISC>{0.0f};
 }
 
 // One state update h <- A_bar h + B_bar x for every discretisation.  u is what the
 // staging prepared per (t, d): delta * x (Mamba, bilinear) or x (zero-order hold);
-// al = A log2(e), aux = disc_aux(A); abar receives A_bar (used by the carry passes).
+// dt2 = dt^2 (read by the zero-order hold only); al = A log2(e), k = disc_const(A); abar
+// receives A_bar (used by the carry passes).
 // Bilinear map, with r = 1 / (1 - dt A / 2): A_bar = 2 r - 1 and B_bar = r dt B, so
 // A_bar h + B_bar x = r (2 h + dt x B) - h  (r (1 - dt A / 2) = 1 up to the rounding of r).
 template <int DISC>
-__device__ __forceinline__ float disc_step(float h, float dt, float u, float bv, float al, float aux,
-                                           float &abar) {
+__device__ __forceinline__ float disc_step(float h, float dt, float dt2, float u, float bv, float al,
+                                           const DiscK<DISC> &k, float &abar) {
     if constexpr (DISC == kBilinear) {
-        const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(-dt, aux, 1.0f));
+        const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(-dt, k.v, 1.0f));
         abar = __builtin_fmaf(2.0f, r, -1.0f);
         return __builtin_fmaf(r, __builtin_fmaf(2.0f, h, u * bv), -h);
     } else if constexpr (DISC == kZOH) {
         const float s = dt * al;
         const float e = __builtin_amdgcn_exp2f(s);
         abar = e;
-        return __builtin_fmaf(e, h, zoh_factor(dt, s, e, aux) * (u * bv));
+        return __builtin_fmaf(e, h, zoh_factor(dt, dt2, s, e, k) * (u * bv));
     } else {
         const float e = __builtin_amdgcn_exp2f(dt * al);
         abar = e;

@@ -186,3 +186,58 @@ def test_variant_argument_errors(ssm):
         ssm.scan_fwd(x, x, A, B, B, delta_bias=torch.zeros(63, device="cuda"))
     with pytest.raises(TypeError):
         ssm.scan_fwd(x, x, A, B, B, delta_bias=torch.zeros(64, device="cuda", dtype=torch.bfloat16))
+
+
+def test_zoh_factor_one_step(ssm):
+    """One zero-order-hold step from h = 0 with x = B = 1 leaves h = (exp(dt A) - 1) / A,
+    the factor itself.  Over dt A from -30 to +2 (both signs, |dt A| down to 1e-9, A = 0 and
+    A = -1e-30), through the single-token update and through a one-step scan (specialised
+    kernel), every state is within 1e-5 of the closed form, relative."""
+    import torch
+    D, N = 1024, 16
+    rng = np.random.default_rng(5)
+    dt = np.exp(rng.uniform(np.log(1e-4), np.log(3.0), D)).astype(np.float32)
+    mag = np.exp(rng.uniform(np.log(1e-9), np.log(30.0), (D, N)))
+    sign = np.where(rng.random((D, N)) < 0.9, -1.0, 1.0)
+    z = sign * mag
+    z[sign > 0] = np.minimum(z[sign > 0], 2.0)
+    A = (z / dt[:, None]).astype(np.float32)
+    A[::7, 0] = 0.0
+    A[3::7, 1] = -1e-30
+    A64, dt64 = A.astype(np.float64), dt.astype(np.float64)[:, None]
+    zz = dt64 * A64
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ref = np.where(A64 == 0, dt64, np.expm1(zz) / np.where(A64 == 0, 1.0, A64))
+    At = torch.from_numpy(A).cuda()
+    dtt = torch.from_numpy(dt).cuda()[None]
+    ones = torch.ones((1, D), device="cuda")
+    B1 = torch.ones((1, N), device="cuda")
+    h = torch.zeros((1, D, N), device="cuda")
+    ssm.state_update(h, ones, dtt, At, B1, B1, None, None, discretization="zoh")
+    _, hl = ssm.scan_fwd(ones[:, None], dtt[:, None], At, B1[:, None], B1[:, None], None, None, None,
+                         discretization="zoh", return_last_state=True)
+    torch.cuda.synchronize()
+    for name, g in (("update", h[0]), ("scan", hl[0])):
+        g = to_host(g)
+        rel = np.abs(g - ref) / np.abs(ref)
+        print(f"[zoh factor] {name}: worst relative error {rel.max():.3g}", flush=True)
+        assert rel.max() <= 1e-5, (name, float(rel.max()))
+
+
+ZOH_STRUCT = [
+    # B, L, D, dtype, gate, h0, softplus, G, chunk
+    (2, 333, 128, "f32", True, True, False, 2, 0),
+    (1, 700, 64, "bf16", True, True, True, 2, 0),
+    (2, 500, 64, "f32", False, True, False, 2, 70),
+    (1, 999, 64, "f32", True, True, False, 4, 100),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,dt,gate,h0,sp,G,chunk", ZOH_STRUCT)
+def test_zoh_structured_a(ssm, Bsz, L, D, dt, gate, h0, sp, G, chunk):
+    """The zero-order hold with A = -(n+1): the structured path (the decay of a lane's second
+    state is the first's times exp(dt c_d)) and the general path both match the oracle."""
+    inp = _inputs(Bsz, L, D, 16, dt, 800 + L + G, gate, h0, sp, "zoh", False, a_kind="mamba")
+    for general in (False, True):
+        _check(ssm, inp, f"zoh structured-A {Bsz}x{L}x{D} {dt} G={G} chunk={chunk} general={general}",
+               states_per_lane=G, chunk_len=chunk, general_a=general)
