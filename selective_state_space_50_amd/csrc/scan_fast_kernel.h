@@ -93,6 +93,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
+// dt^2 of the first (I = 0) or second step of a staged (E, E', dt^2, dt'^2) entry; 0 for an
+// (E, E') entry, which carries none
+template <int I, class V>
+__device__ __forceinline__ float ev_dt2(const V &v) {
+    if constexpr (sizeof(V) == 16) return I == 0 ? v.z : v.w;
+    else return 0.0f;
+}
+
 // Read-only for the whole launch (written by the pre-pass launch): the constant
 // address space lets wave-uniform reads become scalar loads into SGPRs.
 typedef const float __attribute__((address_space(4))) cfloat;
@@ -149,6 +157,11 @@ __global__ void __launch_bounds__(256) bc_pack_kernel(ScanArgs a) {
 template <int DISC, typename T, int G, bool HAS_Z, bool CARRY, bool CKPT = false>
 __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(ScanArgs a) {
     constexpr bool ST = DISC != kBilinear;   // structured-A capable, strided state mapping
+    // Zero-order hold with two states per lane: the helpers also stage dt^2 per (t, d) next
+    // to E, so a compute lane does not square dt per step.  (With G = 4 the larger table
+    // would not let two workgroups share a CU; those lanes square dt themselves.)
+    constexpr bool DT2 = DISC == kZOH && G == 2;
+    using EV = std::conditional_t<DT2, float4, float2>;   // (E_i, E_i+1[, dt2_i, dt2_i+1])
     constexpr int NC = kN / G;          // compute waves
     constexpr int RPT = 2;              // rows per helper thread
     static_assert(kTB / RPT * 32 == helper_waves<G>() * 64, "helpers cover the block in row pairs x channel pairs");
@@ -163,8 +176,9 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     // still scan block j.  y shares are double-buffered by block parity.
     struct Smem {
         float4 du[4][kTB / 2 * 64];
-        float2 e[4][ST ? kTB / 2 * 64 : 1];   // structured A: (E_i, E_i+1)
-        float2 y[2][CARRY ? 1 : NC * kTB / 2 * 64];
+        EV e[4][ST ? kTB / 2 * 64 : 1];   // structured A: (E_i, E_i+1), and dt^2 with DT2
+        // (carries: no y, but the NC words of the structured-A vote)
+        float2 y[2][CARRY ? NC / 2 : NC * kTB / 2 * 64];
     };
     __shared__ Smem smem;
     auto &sDU = smem.du;
@@ -302,7 +316,12 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 if (pre) spre[j] += s2;
             }
         }
-        if constexpr (ST) {
+        if constexpr (DT2) {   // (E_r0, E_r0+1, dt2_r0, dt2_r0+1) of channels cp and cp + 1
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                sE[P][rp * 64 + cp + j] = make_float4(stage_e ? ev[0][j] : 0.0f, stage_e ? ev[1][j] : 0.0f,
+                                                      dv[0][j] * dv[0][j], dv[1][j] * dv[1][j]);
+        } else if constexpr (ST) {
             if (stage_e)   // (E_r0, E_r0+1) of channel cp, then of channel cp + 1
                 *reinterpret_cast<float4 *>(&sE[P][rp * 64 + cp]) = make_float4(ev[0][0], ev[1][0], ev[0][1], ev[1][1]);
         }
@@ -362,13 +381,13 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
     // (delta, u) and (structured) E of the sub-block about to be computed: requested during
     // the previous sub-block, or during the last sub-block of the previous block
     float4 du_c[SUB / 2];
-    float2 e_c[SUB / 2];
-    auto load_du = [&](int64_t k, int sb, float4 *du, float2 *ev, auto str) __attribute__((always_inline)) {
+    EV e_c[SUB / 2];
+    auto load_du = [&](int64_t k, int sb, float4 *du, EV *ev, auto str) __attribute__((always_inline)) {
         const int slot = static_cast<int>(k & 3);
 #pragma unroll
         for (int q = 0; q < SUB / 2; ++q) {
             du[q] = sDU[slot][(sb * SUB / 2 + q) * 64 + lane];
-            if constexpr (decltype(str)::value) ev[q] = sE[slot][(sb * SUB / 2 + q) * 64 + lane];
+            if constexpr (decltype(str)::value || DT2) ev[q] = sE[slot][(sb * SUB / 2 + q) * 64 + lane];
         }
     };
 
@@ -376,7 +395,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
         constexpr int P = decltype(par)::value;      // block parity: y shares
         constexpr bool STR = decltype(str)::value;   // structured-A path
         float4 du_n[SUB / 2];
-        float2 e_n[SUB / 2];
+        EV e_n[SUB / 2];
         float bc_c[NBC];
 #pragma unroll
         for (int j = 0; j < NBC; ++j) bc_c[j] = bc_nx[j];
@@ -425,13 +444,23 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 const float *bC = bc_c + SUB * G + 2 * q * G;   // C of the same steps
                 // one step of state slot g: general, or (structured) the decay of slot g - 1
                 // times E.  dt2 = dt^2 (zero-order hold), once per step for the G slots.
-                auto upd = [&](int g, float dt, float dt2, float u, float bv, float ev, float &e) __attribute__((always_inline)) {
+                // Zero-order hold on the structured path: s0 = dt A[n] log2(e) of slot 0 serves
+                // every slot's series (their coefficients are rescaled to it), so slots g > 0
+                // need neither their own exp nor their own s.
+                auto upd = [&](int g, float dt, float dt2, float u, float bv, float ev, float &e, float &s0) __attribute__((always_inline)) {
+                    if constexpr (STR && DISC == kZOH) {
+                        if (g == 0) {
+                            s0 = dt * Al[0];
+                            e = __builtin_amdgcn_exp2f(s0);
+                        } else {
+                            e *= ev;
+                        }
+                        h[g] = __builtin_fmaf(e, h[g], zoh_factor(dt, dt2, s0, e, kc[g]) * (u * bv));
+                        return e;
+                    }
                     if (STR && g > 0) {
                         e *= ev;   // exp(dt A[n + NC]) = exp(dt A[n]) exp(dt c_d)
-                        if constexpr (DISC == kZOH)
-                            h[g] = __builtin_fmaf(e, h[g], zoh_factor(dt, dt2, dt * Al[g], e, kc[g]) * (u * bv));
-                        else
-                            h[g] = __builtin_fmaf(e, h[g], u * bv);
+                        h[g] = __builtin_fmaf(e, h[g], u * bv);
                         return e;
                     }
                     float ab;
@@ -439,28 +468,28 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                     e = ab;
                     return ab;
                 };
-                const float dt2a = DISC == kZOH ? du.x * du.x : 0.0f;
-                const float dt2b = DISC == kZOH ? du.z * du.z : 0.0f;
+                const float dt2a = DT2 ? ev_dt2<0>(e_c[q]) : DISC == kZOH ? du.x * du.x : 0.0f;
+                const float dt2b = DT2 ? ev_dt2<1>(e_c[q]) : DISC == kZOH ? du.z * du.z : 0.0f;
                 const float ev0 = STR ? e_c[q].x : 0.0f, ev1 = STR ? e_c[q].y : 0.0f;
                 if constexpr (CARRY) {
                     if constexpr (DISC != kBilinear) {
                         dsum += du.x;
                         dsum += du.z;
                     }
-                    float e0 = 0.0f, e1 = 0.0f;
+                    float e0 = 0.0f, e1 = 0.0f, s0a = 0.0f, s0b = 0.0f;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        const float ab0 = upd(g, du.x, dt2a, du.y, bB[g], ev0, e0);
-                        const float ab1 = upd(g, du.z, dt2b, du.w, bB[G + g], ev1, e1);
+                        const float ab0 = upd(g, du.x, dt2a, du.y, bB[g], ev0, e0, s0a);
+                        const float ab1 = upd(g, du.z, dt2b, du.w, bB[G + g], ev1, e1, s0b);
                         if constexpr (DISC == kBilinear) pc[g] *= ab0 * ab1;
                     }
                 } else {
-                    float y0, y1, e0 = 0.0f, e1 = 0.0f;
+                    float y0, y1, e0 = 0.0f, e1 = 0.0f, s0a = 0.0f, s0b = 0.0f;
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        upd(g, du.x, dt2a, du.y, bB[g], ev0, e0);
+                        upd(g, du.x, dt2a, du.y, bB[g], ev0, e0, s0a);
                         y0 = g == 0 ? bC[0] * h[0] : __builtin_fmaf(bC[g], h[g], y0);
-                        upd(g, du.z, dt2b, du.w, bB[G + g], ev1, e1);
+                        upd(g, du.z, dt2b, du.w, bB[G + g], ev1, e1, s0b);
                         y1 = g == 0 ? bC[G] * h[0] : __builtin_fmaf(bC[G + g], h[g], y1);
                     }
                     sY[P][(w * kTB / 2 + sb * SUB / 2 + q) * 64 + lane] = make_float2(y0, y1);
@@ -469,7 +498,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
 #pragma unroll
             for (int q = 0; q < SUB / 2; ++q) {
                 du_c[q] = du_n[q];
-                if constexpr (STR) e_c[q] = e_n[q];
+                if constexpr (STR || DT2) e_c[q] = e_n[q];
             }
             if (sb + 1 < NSUB) {
 #pragma unroll
@@ -527,8 +556,25 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             const float cd = Ad[NC] - Ad[0];
 #pragma unroll
             for (int g = 1; g < G; ++g) ok &= (Ad[st_n(g)] - Ad[st_n(g - 1)]) == cd ? 1 : 0;
+            if constexpr (DISC == kZOH) ok &= Al[0] != 0.0f ? 1 : 0;   // the series is taken in s0
         }
-        const bool structured = ST ? __syncthreads_and(ok) != 0 : (__syncthreads(), false);
+        // Each compute wave posts its verdict in a word of the parity-1 y buffer, which is
+        // first written in block 1, after a barrier that every wave reaches only once it has
+        // read the verdicts.  (__syncthreads_and would reserve LDS of its own, which takes the
+        // G = 4 kernel past the half of the LDS that lets two workgroups share a CU.)
+        int *votes = reinterpret_cast<int *>(&sY[1][0]);
+        if constexpr (ST) {
+            const int all = __all(ok);
+            if (lane == 0) votes[w] = all;
+        }
+        __syncthreads();
+        bool structured = false;
+        if constexpr (ST) {
+            int v = 1;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) v &= votes[i];
+            structured = v != 0;
+        }
         int64_t k = 0;
         auto run = [&](auto str) __attribute__((always_inline)) {
             if (nblk > 0) load_du(0, 0, du_c, e_c, str);
@@ -543,8 +589,20 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
                 __syncthreads();
             }
         };
-        if (ST && structured) run(std::integral_constant<bool, ST>{});
-        else run(std::false_type{});
+        if (ST && structured) {
+            if constexpr (DISC == kZOH) {
+                // series coefficients of slot g in s0: s_g = rho s0 with rho = A[n_g] / A[n_0]
+#pragma unroll
+                for (int g = 1; g < G; ++g) {
+                    const float rho = Al[g] / Al[0];
+                    kc[g].c2 *= rho;
+                    kc[g].c3 *= rho * rho;
+                }
+            }
+            run(std::integral_constant<bool, ST>{});
+        } else {
+            run(std::false_type{});
+        }
         if constexpr (CARRY && CKPT) {
         } else if constexpr (CARRY) {
             const int64_t slot = b * (a.n_chunks - 1) + c;
@@ -592,8 +650,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
 #pragma unroll
         for (int j = 1; j < kPD; ++j)
             if (j < nblk) touch(j);
-        if constexpr (ST) (void)__syncthreads_and(1);   // the structured-A vote
-        else __syncthreads();
+        __syncthreads();   // the structured-A vote
         for (int64_t k = 0; k < nblk; ++k) {
             if (k + kPD < nblk) touch(k + kPD);
             __syncthreads();
@@ -621,8 +678,7 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             if (nblk > 1) stage_any(t0 + kTB, Par<1>{}, Par<1>{});
             load_block(kRS + 1, Par<1>{});
         }
-        if constexpr (ST) (void)__syncthreads_and(1);   // the structured-A vote
-        else __syncthreads();
+        __syncthreads();   // the structured-A vote
         // iteration k >= 1, k % 4 == S: finish block k - 1, stage block k + 2 (slot and register
         // set (S + 2) % 4), then reuse that register set for block k + 2 + kRS.  Every block
         // before the last is full.

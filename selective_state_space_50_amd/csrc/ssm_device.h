@@ -190,7 +190,8 @@ __device__ __forceinline__ DiscK<kZOH> zoh_const(float A) {
     return k;
 }
 
-__device__ __forceinline__ float zoh_factor(float dt, float dt2, float s, float e, const DiscK<kZOH> &k) {
+template <class K>   // DiscK<kZOH>
+__device__ __forceinline__ float zoh_factor(float dt, float dt2, float s, float e, const K &k) {
     const float ser = __builtin_fmaf(dt2, __builtin_fmaf(__builtin_fmaf(k.c3, s, k.c2), s, k.c1), dt);
     const float dir = __builtin_fmaf(e, k.inv_a, k.off);
     return __builtin_fmaxf(ser, dir);
