@@ -556,7 +556,11 @@ __global__ void __launch_bounds__(64 * waves_per_block<G>()) scan_fast_kernel(Sc
             const float cd = Ad[NC] - Ad[0];
 #pragma unroll
             for (int g = 1; g < G; ++g) ok &= (Ad[st_n(g)] - Ad[st_n(g - 1)]) == cd ? 1 : 0;
-            if constexpr (DISC == kZOH) ok &= Al[0] != 0.0f ? 1 : 0;   // the series is taken in s0
+            if constexpr (DISC == kZOH) {   // the series is taken in s0: A[n_g] / A[n_0] must be moderate
+                ok &= Al[0] != 0.0f ? 1 : 0;
+#pragma unroll
+                for (int g = 1; g < G; ++g) ok &= __builtin_fabsf(Al[g]) <= 64.0f * __builtin_fabsf(Al[0]) ? 1 : 0;
+            }
         }
         // Each compute wave posts its verdict in a word of the parity-1 y buffer, which is
         // first written in block 1, after a barrier that every wave reaches only once it has

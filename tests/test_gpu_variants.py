@@ -241,3 +241,15 @@ def test_zoh_structured_a(ssm, Bsz, L, D, dt, gate, h0, sp, G, chunk):
     for general in (False, True):
         _check(ssm, inp, f"zoh structured-A {Bsz}x{L}x{D} {dt} G={G} chunk={chunk} general={general}",
                states_per_lane=G, chunk_len=chunk, general_a=general)
+
+
+@pytest.mark.parametrize("a0", [-0.125, -2.0 ** -12])
+def test_zoh_structured_a_wide_ratio(ssm, a0):
+    """A[d, n] = a0 - n/2 has the structure (exact differences of -4 eight states apart), and
+    the second state's series is taken in the first state's s with its coefficients scaled by
+    A[n+8]/A[n]: 33 for a0 = -1/8 (structured path), 16385 for a0 = -2^-12 (beyond the bound
+    of 64, so the general path).  Both match the oracle."""
+    inp = _inputs(2, 300, 128, 16, "f32", 900, True, True, False, "zoh", False)
+    A = np.broadcast_to((a0 - 0.5 * np.arange(16)).astype(np.float32), (128, 16)).copy()
+    inp["A"] = A
+    _check(ssm, inp, f"zoh A = {a0} - n/2", states_per_lane=2)
