@@ -431,3 +431,26 @@ def test_local_scan_carries(ssm, Bsz, L, D, dt, gate, h0, disc, dscale, azero, c
         assert np.max(np.abs(y - y1)) <= 2e-5 * max(1.0, float(np.max(np.abs(y1))))
     if undecayed.any():
         assert np.max(np.abs(h - h1)[undecayed]) <= 1e-4 * max(1.0, float(np.max(np.abs(h1))))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("disc", ["mamba", "zoh"])
+def test_parity_batch8_four_states_per_lane(ssm, disc):
+    """B8 L1024 D4096 N16 bf16 gated, A = -(n+1): the planner runs four states per lane with
+    two workgroups per CU (512 workgroups).  Sampled channels over the whole length against
+    the oracle, structured and general paths."""
+    import torch
+    Bsz, L, D, N = 8, 1024, 4096, 16
+    plan = ssm.scan_plan(Bsz, L, D, N, "bf16")
+    assert plan["specialised"] == 1 and plan["states_per_lane"] == 4 and plan["blocks"] == 512, plan
+    inp = synth.scan_inputs(Bsz, L, D, N, "bf16", seed=88, gate=True, d_kind="normal", a_kind="mamba")
+    inp["discretization"] = disc
+    ch = sample_channels(Bsz, D, 64)
+    yr, hr = oracle.scan(inp, channels=ch)
+    cb = torch.tensor([b for b, _ in ch], device="cuda")
+    cd = torch.tensor([d for _, d in ch], device="cuda")
+    for general in (False, True):
+        yd, hd = _run_dev(ssm, inp, discretization=disc, general_a=general)
+        st = assert_close(to_host(yd[cb, :, cd]), yr, "bf16")
+        assert_close(to_host(hd[cb, cd]), hr, "f32", "h_last")
+        _log(f"B8 {disc} G=4 general={general}", st)
