@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 #define SSM_MAX_DSTATE 256
 
 typedef enum ssm_dtype {
@@ -413,22 +413,26 @@ int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, void
  *     y[b,t,h,p] = sum_n C[b,t,n] * S[p,n] + Dskip[h] * x[b,t,h,p],  then * silu(z) if gated
  *
  * i.e. the recurrence of ssm_scan_fwd with one step size and one scalar decay per
- * head, and B, C shared by every head.
+ * head.  The heads fall into ngroups groups of nheads / ngroups consecutive heads, and
+ * the heads of a group share one B and one C row per token: head h reads group
+ * g = h / (nheads / ngroups) (ngroups = 1: every head shares B and C).
  *
  *   x, z      [batch, seqlen, nheads, headdim]  bf16   z NULL = no gate
  *   delta     [batch, seqlen, nheads]           bf16
  *   A, Dskip, delta_bias  [nheads]              fp32   Dskip, delta_bias may be NULL
- *   B, C      [batch, seqlen, dstate]           bf16
+ *   B, C      [batch, seqlen, ngroups, dstate]  bf16
  *   h0, h_last [batch, nheads, headdim, dstate] fp32   NULL = zero start / not stored
  *   y         [batch, seqlen, nheads, headdim]  bf16   output; must not overlap an input
  *
  * headdim 64, dstate 128, bf16: the matrix-core kernel.  Any other headdim >= 1, dstate <=
  * 256 (more is SSM_EUNSUPPORTED), and fp32 (dtype SSM_DTYPE_F32 for x, z, delta, B, C, y):
- * the generic scan kernel over the nheads * headdim channels, one pass.  No workspace.
+ * the generic scan kernel over the nheads * headdim channels, one pass; with ngroups > 1
+ * it needs (nheads / ngroups) * headdim to be a multiple of 64 (else SSM_EUNSUPPORTED).
+ * ngroups must be >= 1 and divide nheads (else SSM_EINVAL).  No workspace.
  * seqlen == 0 stores h0 (or zeros) in h_last; batch or nheads == 0 is a no-op.
  */
 int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                int dtype, const void *x, const void *delta, const float *A, const void *B,
+                int64_t ngroups, int dtype, const void *x, const void *delta, const float *A, const void *B,
                 const void *C, const float *Dskip, const void *z, const float *delta_bias,
                 const float *h0, float *h_last, void *y, int delta_softplus, void *stream);
 

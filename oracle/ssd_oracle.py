@@ -22,7 +22,10 @@ gate y * silu(z)):
         y          = y * silu(z[b, t, h, p])       (when a gate is given)
 
 with B and C one vector of width N per token, shared by every head (a single
-group).  The structured-matrix form the page names is the same map written as
+group).  With G groups (Mamba-2 layers split the heads into groups of consecutive
+heads), B and C are [B, L, G, N] and head h reads group h // (H / G): each group is the
+single-group map on its own heads with its own B and C.  The structured-matrix form the
+page names is the same map written as
 y = M (x) with M[t, s] = C_t . B_s * exp(a (cum_t - cum_s)) * dt_s for s <= t
 (cum = running sum of dt): a masked, decayed product C B^T, i.e. linear attention
 with a decay mask.  The tests check the recurrence below against that form.
@@ -46,9 +49,26 @@ def _silu(v):
 def ssd(x, delta, a, Bm, Cm, D=None, z=None, h0=None, delta_softplus=False, delta_bias=None):
     """All arrays float64 (or anything numpy widens exactly).
 
-    x, z: [B, L, H, P];  delta: [B, L, H];  a: [H];  Bm, Cm: [B, L, N];  D: [H];
-    h0: [B, H, P, N];  delta_bias: [H].  Returns y [B, L, H, P] and h_last [B, H, P, N].
+    x, z: [B, L, H, P];  delta: [B, L, H];  a: [H];  Bm, Cm: [B, L, N], or [B, L, G, N] for G
+    groups of H / G consecutive heads;  D: [H];  h0: [B, H, P, N];  delta_bias: [H].
+    Returns y [B, L, H, P] and h_last [B, H, P, N].
     """
+    Bm = np.asarray(Bm)
+    if Bm.ndim == 4:   # groups: the single-group map per group of heads
+        G = Bm.shape[2]
+        H = np.asarray(x).shape[2]
+        assert H % G == 0, (H, G)
+        hg = H // G
+        ys, hs = [], []
+        for g in range(G):
+            sel = slice(g * hg, (g + 1) * hg)
+            pick = lambda t, ax: None if t is None else np.take(np.asarray(t), np.arange(g * hg, (g + 1) * hg), axis=ax)
+            yg, hlg = ssd(pick(x, 2), pick(delta, 2), np.asarray(a)[sel], Bm[:, :, g], np.asarray(Cm)[:, :, g],
+                          None if D is None else np.asarray(D)[sel], pick(z, 2), pick(h0, 1), delta_softplus,
+                          None if delta_bias is None else np.asarray(delta_bias)[sel])
+            ys.append(yg)
+            hs.append(hlg)
+        return np.concatenate(ys, axis=2), np.concatenate(hs, axis=1)
     x = np.asarray(x, dtype=np.float64)
     Bsz, L, H, P = x.shape
     Bm = np.asarray(Bm, dtype=np.float64)
@@ -90,6 +110,19 @@ def ssd_storage(inp: dict, batches=None, heads=None):
     patterns or float32, widened exactly.  batches / heads select a subset (lists of
     indices); the result then covers only those rows and heads."""
     dt = inp["dtype"]
+    if np.asarray(inp["B"]).ndim == 4 and heads is not None:
+        # groups and a subset of heads: each selected head with its own group's B and C
+        H, G = np.asarray(inp["x"]).shape[2], np.asarray(inp["B"]).shape[2]
+        ys, hls = [], []
+        for h in heads:
+            g = h // (H // G)
+            one = dict(inp)
+            one["B"] = np.asarray(inp["B"])[:, :, g]
+            one["C"] = np.asarray(inp["C"])[:, :, g]
+            yh, hh = ssd_storage(one, batches, [h])
+            ys.append(yh)
+            hls.append(hh)
+        return np.concatenate(ys, axis=2), np.concatenate(hls, axis=1)
     bs = slice(None) if batches is None else np.asarray(batches)
     hs = slice(None) if heads is None else np.asarray(heads)
     pick = lambda t: None if t is None else _widen(np.asarray(t)[bs][:, :, hs], dt)

@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 5     # SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 6     # SSM_ABI_VERSION of include/ssm.h
 
 
 class SSMError(RuntimeError):
@@ -109,7 +109,7 @@ def lib():
     L.ssm_conv1d_fwd.restype = I32
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
     L.ssm_ssd_fwd.restype = I32
-    L.ssm_ssd_fwd.argtypes = [I64, I64, I64, I64, I64, I32] + [P] * 11 + [I32, P]
+    L.ssm_ssd_fwd.argtypes = [I64, I64, I64, I64, I64, I64, I32] + [P] * 11 + [I32, P]
     L.ssm_conv1d_update.restype = I32
     L.ssm_conv1d_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, I32, P]
     L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
@@ -622,7 +622,8 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
             return_last_state=False, out=None, h_last=None, stream=None):
     """Multi-head SSD scan (the Mamba-2 layer's state space model) on the GPU.
 
-    x, z: [B, L, H, P];  delta: [B, L, H];  B, C: [B, L, N] (all bf16, or all fp32);
+    x, z: [B, L, H, P];  delta: [B, L, H];  B, C: [B, L, N], or [B, L, G, N] for G groups
+    of H / G consecutive heads each sharing one B and C row (all bf16, or all fp32);
     A, D, delta_bias: [H] fp32;  h0: [B, H, P, N] fp32.  P = 64, N = 128 in bf16 runs on the
     matrix cores; other P, N <= 256 and fp32 on the generic scan kernel.  Returns y
     [B, L, H, P] (x's dtype), or (y, h_last) when return_last_state.
@@ -632,13 +633,15 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
         raise ValueError("x must be [batch, seqlen, nheads, headdim] and A [nheads]")
     Bsz, L, H, P = x.shape
     N = B.shape[-1]
+    G = B.shape[2] if B.dim() == 4 else 1
+    bc_shape = (Bsz, L, G, N) if B.dim() == 4 else (Bsz, L, N)
     dev, dt = x.device, x.dtype
     if dev.type != "cuda":
         raise ValueError("ssd_fwd runs on the GPU only; tensors must be on a cuda device")
     _need(delta, "delta", (Bsz, L, H), dt, dev)
     _need(z, "z", (Bsz, L, H, P), dt, dev)
-    _need(B, "B", (Bsz, L, N), dt, dev)
-    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(B, "B", bc_shape, dt, dev)
+    _need(C, "C", bc_shape, dt, dev)
     _need(A, "A", (H,), torch.float32, dev)
     _need(D, "D", (H,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (H,), torch.float32, dev)
@@ -651,7 +654,7 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
         h_last = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=dev)
     _need(h_last, "h_last", (Bsz, H, P, N), torch.float32, dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
-    st = lib().ssm_ssd_fwd(Bsz, L, H, P, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+    st = lib().ssm_ssd_fwd(Bsz, L, H, P, N, G, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                            _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(h_last), _ptr(out),
                            int(bool(delta_softplus)), ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_ssd_fwd")

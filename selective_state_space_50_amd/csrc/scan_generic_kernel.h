@@ -76,6 +76,10 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
     // per-channel parameters, or per-head ones in the multi-head layout
     const int64_t dh = a.head_dim > 0 ? d / a.head_dim : d;
     const int64_t DS = a.head_dim > 0 ? D / a.head_dim : D;   // delta's row length
+    // B/C group of this workgroup's channels (multi-head layout with groups), and the row
+    // length of B and C
+    const int64_t bcg = a.bc_groups > 1 ? static_cast<int64_t>(blockIdx.x) * 64 / a.bc_group_ch : 0;
+    const int64_t BCR = a.bc_groups * N;
     const int64_t t0 = c * a.chunk_len;
     const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
     const int n0 = w * G;
@@ -150,7 +154,7 @@ __global__ void __launch_bounds__(MAXT) scan_kernel(ScanArgs a) {
                 const int i = e / NP, n = e - (e / NP) * NP;
                 const int64_t t = tb0 + i;
                 const bool ok = n < N && t < t1;
-                const int64_t off = (b * L + t) * N + n;
+                const int64_t off = (b * L + t) * BCR + bcg * N + n;
                 rb[j] = ok ? Bm[off] : T(0);
                 if (!CARRY) rc[j] = ok ? Cm[off] : T(0);
             }

@@ -4,7 +4,8 @@
 // State Space Models Challenge Transformers", Mamba2Block: d_head 64, d_state 128):
 //     dt = delta[b,t,h] (+ bias[h], softplus optional),  A_bar = exp(dt a_h)
 //     S[p,n] = A_bar S[p,n] + dt B[b,t,n] x[b,t,h,p],    y[b,t,h,p] = C[b,t,:] . S[p,:] + D_h x
-// and y * silu(z) when gated.  B and C are shared by all heads.
+// and y * silu(z) when gated.  B and C are shared by the heads of a group (the heads fall
+// into G groups of consecutive heads; G = 1: one B and one C row per token for all heads).
 //
 // brentwoodlivery ("State-space models (Mamba, S4)", "Mamba 2 and Hybrid
 // Architectures") describes the layer as a structured matrix multiplication.  Over a
@@ -125,8 +126,8 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
     const int lr = lane & 15, lg = lane >> 4;
 
     // workgroup -> (b, h): the hardware deals workgroups to the 8 XCDs in turn, so
-    // consecutive (b, h) go to the same XCD and the heads of one batch row share the
-    // B/C rows in that XCD's L2
+    // consecutive (b, h) go to the same XCD and the heads of one batch row (and group)
+    // share the B/C rows in that XCD's L2
     const int64_t W = a.B * a.H;
     const int64_t per = (W + 7) / 8;
     const int64_t q = (static_cast<int64_t>(blockIdx.x) % 8) * per + blockIdx.x / 8;
@@ -326,8 +327,11 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
         const float dbias = a.dbias ? a.dbias[h] : 0.0f;
         const uint16_t *X = static_cast<const uint16_t *>(a.x) + (b * L * H + h) * kP;   // row t at + t H kP
         const uint16_t *DL = static_cast<const uint16_t *>(a.delta) + b * L * H + h;      // step t at + t H
-        const uint16_t *BM = static_cast<const uint16_t *>(a.Bm) + b * L * kNS;           // row t at + t kNS
-        const uint16_t *CM = static_cast<const uint16_t *>(a.Cm) + b * L * kNS;
+        // B, C rows of this head's group: row t at + t BR
+        const int64_t BR = a.G * kNS;
+        const int64_t grp = h / (H / a.G);
+        const uint16_t *BM = static_cast<const uint16_t *>(a.Bm) + b * L * BR + grp * kNS;
+        const uint16_t *CM = static_cast<const uint16_t *>(a.Cm) + b * L * BR + grp * kNS;
 
         // per-thread inputs of one chunk (every address is a wave-uniform row pointer plus a
         // 32-bit lane offset):
@@ -336,7 +340,7 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
         //   B^T: state 64 (w & 1) + lane, steps 16 (w >> 1) + i
         //   delta: first wave, one step per lane
         const int bt = 4 * w + (lane >> 4), bn = (lane & 15) * 8;
-        const uint32_t boff = static_cast<uint32_t>((lane >> 4) * kNS + bn);
+        const uint32_t boff = static_cast<uint32_t>((lane >> 4) * BR + bn);
         const int tn = 64 * (w & 1) + lane, ts = 16 * (w >> 1);
         uint4 bq[2], cq[2];
         uint16_t xg[8], bg[16];
@@ -351,14 +355,14 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
             for (int r = 0; r < 2; ++r) {
                 const int64_t t = t0 + 4 * w + 32 * r;
                 if (!PART || t0 + bt + 32 * r < L) {
-                    bq[r] = *reinterpret_cast<const uint4 *>(BM + t * kNS + boff);
-                    cq[r] = *reinterpret_cast<const uint4 *>(CM + t * kNS + boff);
+                    bq[r] = *reinterpret_cast<const uint4 *>(BM + t * BR + boff);
+                    cq[r] = *reinterpret_cast<const uint4 *>(CM + t * BR + boff);
                 }
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) xg[i] = (X + row(t0 + 8 * w + i) * xs)[lane];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) bg[i] = (BM + row(t0 + ts + i) * kNS)[tn];
+            for (int i = 0; i < 16; ++i) bg[i] = (BM + row(t0 + ts + i) * BR)[tn];
             if (w == 0) {
                 const int64_t t = t0 + lane;
                 dq = DL[(PART && t >= L ? L - 1 : t) * H];

@@ -738,12 +738,12 @@ extern "C" int ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int 
 }
 
 extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                           int dtype, const void *x, const void *delta, const float *A, const void *B,
+                           int64_t ngroups, int dtype, const void *x, const void *delta, const float *A, const void *B,
                            const void *C, const float *Dskip, const void *z, const float *delta_bias,
                            const float *h0, float *h_last, void *y, int delta_softplus, void *stream) {
     using namespace ssm;
     clear_error();
-    int st = check_ssd(batch, seqlen, nheads, headdim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias,
+    int st = check_ssd(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, x, delta, A, B, C, Dskip, z, delta_bias,
                        h0, h_last, y, delta_softplus);
     if (st != SSM_OK) return st;
     if (batch == 0 || nheads == 0) return SSM_OK;
@@ -756,8 +756,8 @@ extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_
         hipError_t e = launch_status(s);
         return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
     }
-    log_call("ssd B=%lld L=%lld H=%lld P=%lld N=%lld dtype=%d: %s", (long long)batch, (long long)seqlen,
-             (long long)nheads, (long long)headdim, (long long)dstate, dtype,
+    log_call("ssd B=%lld L=%lld H=%lld P=%lld N=%lld groups=%lld dtype=%d: %s", (long long)batch,
+             (long long)seqlen, (long long)nheads, (long long)headdim, (long long)dstate, (long long)ngroups, dtype,
              headdim == 64 && dstate == 128 && dtype == SSM_DTYPE_BF16 ? "matrix-core kernel"
                                                                        : "generic scan kernel, multi-head layout");
     if (headdim != 64 || dstate != 128 || dtype != SSM_DTYPE_BF16) {
@@ -781,13 +781,15 @@ extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_
         a.ws_P = a.ws_H = a.ws_BC = nullptr;
         a.bc_lpad = 0;
         a.head_dim = headdim;
+        a.bc_groups = ngroups;
+        a.bc_group_ch = (nheads / ngroups) * headdim;
         const dim3 g(static_cast<unsigned>((dim + kChannelsPerBlock - 1) / kChannelsPerBlock),
                      static_cast<unsigned>(batch), 1);
         hipError_t e = launch_scan_any(a, g, p, kMamba, dtype == SSM_DTYPE_BF16, z != nullptr, false, s);
         return e == hipSuccess ? SSM_OK : hip_fail("ssd (generic) launch", e);
     }
     SsdArgs a;
-    a.B = batch; a.L = seqlen; a.H = nheads;
+    a.B = batch; a.L = seqlen; a.H = nheads; a.G = ngroups;
     a.x = x; a.delta = delta; a.z = z; a.Bm = B; a.Cm = C;
     a.A = A; a.Dskip = Dskip; a.dbias = delta_bias; a.h0 = h0; a.h_last = h_last; a.y = y;
     a.softplus = delta_softplus;

@@ -54,6 +54,10 @@ struct ScanArgs {
     // multi-head SSD layout): delta [B][L][D / head_dim], and A, Dskip, dbias one value per
     // head (A the same for every state).
     int64_t head_dim = 0;
+    // Multi-head layout with B/C groups: B, C [B][L][bc_groups][N]; the channels
+    // [g bc_group_ch, (g + 1) bc_group_ch) read group g (bc_group_ch a multiple of 64, so a
+    // workgroup's 64 channels share one group).
+    int64_t bc_groups = 1, bc_group_ch = 0;
 };
 
 struct UpdArgs {
@@ -88,7 +92,8 @@ struct BwdArgs {
 
 struct SsdArgs {
     int64_t B, L, H;         // batch, sequence length, heads (head dim 64, state size 128)
-    const void *x, *delta, *z, *Bm, *Cm;   // x, z [B, L, H, 64]; delta [B, L, H]; B, C [B, L, 128]
+    int64_t G = 1;           // B/C groups: head h reads group h / (H / G)
+    const void *x, *delta, *z, *Bm, *Cm;   // x, z [B, L, H, 64]; delta [B, L, H]; B, C [B, L, G, 128]
     const float *A, *Dskip, *dbias;         // [H] each (Dskip, dbias may be null)
     const float *h0;         // [B, H, 64, 128] or null
     float *h_last;           // [B, H, 64, 128] or null

@@ -714,7 +714,7 @@ int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, co
     return check_no_overlap(all + 3, 2, all, 5);
 }
 
-int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int dtype,
               const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *Dskip, const void *z, const float *delta_bias, const float *h0,
               const float *h_last, const void *y, int delta_softplus) {
@@ -731,8 +731,20 @@ int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, in
         set_error("delta_softplus=%d is neither 0 nor 1", delta_softplus);
         return SSM_EINVAL;
     }
+    if (ngroups < 1 || (nheads > 0 && nheads % ngroups != 0)) {
+        set_error("ngroups=%lld must be >= 1 and divide nheads=%lld", (long long)ngroups, (long long)nheads);
+        return SSM_EINVAL;
+    }
     if (dstate > SSM_MAX_DSTATE) {
         set_error("the SSD scan supports dstate <= %d (got %lld)", SSM_MAX_DSTATE, (long long)dstate);
+        return SSM_EUNSUPPORTED;
+    }
+    const bool mfma = headdim == 64 && dstate == 128 && dtype == SSM_DTYPE_BF16;
+    if (!mfma && ngroups > 1 && ((nheads / ngroups) * headdim) % 64 != 0) {
+        // the generic kernel stages one B/C row per 64-channel workgroup
+        set_error("with ngroups=%lld each group's %lld channels must be a multiple of 64 (head dim %lld, "
+                  "dstate %lld, dtype %d)", (long long)ngroups, (long long)((nheads / ngroups) * headdim),
+                  (long long)headdim, (long long)dstate, dtype);
         return SSM_EUNSUPPORTED;
     }
     if (nheads > 0 && headdim > (int64_t(1) << 24) / nheads) {
@@ -761,7 +773,7 @@ int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, in
     const int64_t st_bytes = batch * nheads * headdim * dstate * 4;
     Range all[] = {
         range("x", x, tok), range("delta", delta, batch * seqlen * nheads * es), range("A", A, nheads * 4),
-        range("B", B, batch * seqlen * dstate * es), range("C", C, batch * seqlen * dstate * es),
+        range("B", B, batch * seqlen * ngroups * dstate * es), range("C", C, batch * seqlen * ngroups * dstate * es),
         range("Dskip", Dskip, nheads * 4), range("z", z, tok), range("delta_bias", delta_bias, nheads * 4),
         range("h0", h0, st_bytes), range("h_last", h_last, st_bytes), range("y", y, seqlen > 0 ? tok : 0),
     };

@@ -142,7 +142,7 @@ int check_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, co
                         const void *x, const float *w, const float *bias, const void *y, int silu);
 
 // Argument checks of the multi-head SSD scan (ssm_ssd_fwd).
-int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+int check_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int dtype,
               const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *Dskip, const void *z, const float *delta_bias, const float *h0,
               const float *h_last, const void *y, int delta_softplus);

@@ -214,8 +214,12 @@ int main() {
     // multi-head SSD scan
     {
         const float *bias = static_cast<const float *>(P(base + 11 * gap));
+        auto sdg = [&](int64_t b, int64_t l, int64_t hh, int64_t pd, int64_t n, int64_t g, int dt, const void *y_,
+                       const float *hl_) {
+            return check_ssd(b, l, hh, pd, n, g, dt, x, dl, A, B, C, Dk, z, bias, h0, hl_, y_, 1);
+        };
         auto sd = [&](int64_t b, int64_t l, int64_t hh, int64_t pd, int64_t n, int dt, const void *y_, const float *hl_) {
-            return check_ssd(b, l, hh, pd, n, dt, x, dl, A, B, C, Dk, z, bias, h0, hl_, y_, 1);
+            return sdg(b, l, hh, pd, n, 1, dt, y_, hl_);
         };
         EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, hl) == SSM_OK);
         // other head dims, state sizes and fp32 take the generic kernel; more than 256 states no
@@ -229,7 +233,16 @@ int main() {
         EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, P(base + 16), hl) == SSM_EINVAL);   // overlaps x
         EXPECT(sd(4, 4096, 64, 64, 128, SSM_DTYPE_BF16, y, h0) == SSM_EINVAL);            // h_last on h0
         EXPECT(sd(0, 4096, 64, 64, 128, SSM_DTYPE_BF16, nullptr, nullptr) == SSM_OK);
-        EXPECT(check_ssd(4, 16, 64, 64, 128, 1, x, dl, A, B, C, Dk, z, bias, h0, hl, y, 2) == SSM_EINVAL);
+        EXPECT(check_ssd(4, 16, 64, 64, 128, 1, 1, x, dl, A, B, C, Dk, z, bias, h0, hl, y, 2) == SSM_EINVAL);
+        // B/C groups: ngroups >= 1 dividing nheads; on the generic kernel a group's channels
+        // must fill whole 64-channel workgroups
+        EXPECT(sdg(4, 4096, 64, 64, 128, 8, SSM_DTYPE_BF16, y, hl) == SSM_OK);
+        EXPECT(sdg(4, 4096, 64, 64, 128, 64, SSM_DTYPE_BF16, y, hl) == SSM_OK);
+        EXPECT(sdg(4, 4096, 64, 64, 128, 0, SSM_DTYPE_BF16, y, hl) == SSM_EINVAL);
+        EXPECT(sdg(4, 4096, 64, 64, 128, 3, SSM_DTYPE_BF16, y, hl) == SSM_EINVAL);
+        EXPECT(sdg(4, 4096, 64, 32, 128, 32, SSM_DTYPE_BF16, y, hl) == SSM_OK);           // 2 heads x 32
+        EXPECT(sdg(4, 4096, 64, 32, 128, 64, SSM_DTYPE_BF16, y, hl) == SSM_EUNSUPPORTED); // 1 head x 32
+        EXPECT(sdg(4, 4096, 64, 64, 128, 4, SSM_DTYPE_F32, y, hl) == SSM_OK);
     }
     EXPECT(std::strcmp(ssm_status_str(SSM_EWORKSPACE), "workspace too small") == 0);
     std::printf("%s: %d failure(s)\n", fails ? "FAILED" : "ok", fails);

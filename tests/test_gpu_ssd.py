@@ -168,3 +168,64 @@ def test_ssd_degenerate_steps_and_decays(ssm):
     st = assert_close(to_host(y), yr, "bf16")
     assert_close(to_host(h), hr, "f32", "h_last")
     print(f"[parity] ssd degenerate: {json.dumps(st)}", flush=True)
+
+
+GROUPED = [
+    # B, L, H, G, P, N, dtype, gate, h0, softplus, bias   (P = 64, N = 128, bf16: matrix cores)
+    (2, 300, 4, 2, 64, 128, "bf16", True, True, False, False),
+    (1, 200, 6, 3, 64, 128, "bf16", False, True, True, True),
+    (2, 130, 8, 8, 64, 128, "bf16", True, False, False, False),
+    (2, 100, 4, 2, 32, 64, "bf16", True, True, False, False),      # generic: 64 channels per group
+    (1, 77, 4, 4, 64, 16, "f32", True, True, True, True),
+    (2, 60, 8, 2, 16, 32, "f32", False, True, False, False),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,H,G,P,N,dt,gate,h0,sp,bias", GROUPED)
+def test_ssd_bc_groups(ssm, Bsz, L, H, G, P, N, dt, gate, h0, sp, bias):
+    """B, C [B, L, G, N]: the heads of group g = h // (H / G) read group g's rows.  Every
+    output against the oracle (which runs each group's heads with that group's B and C)."""
+    import torch
+    inp = synth.ssd_inputs(Bsz, L, H, P, N, dt, seed=1300 + L + G, gate=gate, softplus_input=sp, h0=h0,
+                           delta_bias=bias, ngroups=G)
+    t = {k: to_dev(inp[k], dt) for k in ("x", "delta", "z", "B", "C")}
+    for k in ("A", "Dskip", "delta_bias", "h0"):
+        t[k] = None if inp.get(k) is None else torch.from_numpy(inp[k]).cuda()
+    y, h = ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], t["z"], t["h0"],
+                       delta_softplus=inp["delta_softplus"], delta_bias=t["delta_bias"], return_last_state=True)
+    torch.cuda.synchronize()
+    yr, hr = ssd_oracle.ssd_storage(inp)
+    st = assert_close(to_host(y), yr, dt)
+    assert_close(to_host(h), hr, "f32", "h_last")
+    print(f"[parity] ssd {G} groups {Bsz}x{L}x{H} P={P} N={N} {dt}: {json.dumps(st)}", flush=True)
+
+
+def test_ssd_bc_groups_errors(ssm):
+    import torch
+    bf = torch.bfloat16
+    x = torch.zeros(1, 8, 4, 32, dtype=bf, device="cuda")
+    d = torch.zeros(1, 8, 4, dtype=bf, device="cuda")
+    A = torch.zeros(4, device="cuda")
+    with pytest.raises(ssm.SSMError) as e:   # 3 groups do not divide 4 heads
+        bc = torch.zeros(1, 8, 3, 64, dtype=bf, device="cuda")
+        ssm.ssd_fwd(x, d, A, bc, bc)
+    assert e.value.status == ssm.SSM_EINVAL
+    with pytest.raises(ssm.SSMError) as e:   # generic kernel: a group of 32 channels
+        bc = torch.zeros(1, 8, 4, 64, dtype=bf, device="cuda")
+        ssm.ssd_fwd(x, d, A, bc, bc)
+    assert e.value.status == ssm.SSM_EUNSUPPORTED
+
+
+@pytest.mark.timeout(600)
+def test_ssd_layer_shape_with_groups_sampled(ssm):
+    """B4 L4096 H64 with 8 groups of 8 heads (matrix cores): 20 (batch row, head) pairs that
+    cover every group, over the whole sequence."""
+    import torch
+    inp = synth.ssd_inputs(4, 4096, 64, 64, 128, "bf16", seed=17, gate=True, ngroups=8)
+    y, h = _run(ssm, inp)
+    assert bool(torch.isfinite(y.float()).all())
+    heads = [0, 7, 9, 18, 27, 36, 45, 54, 63, 62]
+    yr, hr = ssd_oracle.ssd_storage(inp, batches=[0, 3], heads=heads)
+    st = assert_close(to_host(y[[0, 3]][:, :, heads]), yr, "bf16")
+    assert_close(to_host(h[[0, 3]][:, heads]), hr, "f32", "h_last")
+    print(f"[parity] ssd layer, 8 groups: {json.dumps(st)}", flush=True)

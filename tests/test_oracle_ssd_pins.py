@@ -193,3 +193,50 @@ def test_unmutated_copy_passes():
     y, _ = _run(p, fn=ns["ssd"])
     yr, _ = _via_s6(p)
     np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-13)
+
+
+def _grouped(seed, G, HG, **kw):
+    """A problem with G groups of HG heads: B, C [B, L, G, N]."""
+    p = _problem(seed, H=G * HG, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    Bsz, L, N = p["Bm"].shape
+    p["Bm"] = rng.standard_normal((Bsz, L, G, N))
+    p["Cm"] = rng.standard_normal((Bsz, L, G, N))
+    return p
+
+
+def _group_slice(p, g, HG):
+    hs = slice(g * HG, (g + 1) * HG)
+    q = dict(p)
+    q["x"], q["delta"], q["a"], q["D"] = p["x"][:, :, hs], p["delta"][:, :, hs], p["a"][hs], p["D"][hs]
+    q["z"] = None if p["z"] is None else p["z"][:, :, hs]
+    q["h0"] = None if p["h0"] is None else p["h0"][:, hs]
+    q["bias"] = None if p["bias"] is None else p["bias"][hs]
+    q["Bm"], q["Cm"] = p["Bm"][:, :, g], p["Cm"][:, :, g]
+    return q
+
+
+@pytest.mark.parametrize("G,HG,gate", [(2, 2, False), (3, 1, True), (2, 3, True)])
+def test_groups_equal_s6_per_group(G, HG, gate):
+    """B/C groups: the heads of group g, run through the S6 C oracle with group g's B and C
+    rows, give the grouped oracle's outputs for those heads."""
+    p = _grouped(11, G, HG, gate=gate)
+    y, h = _run(p)
+    for g in range(G):
+        yr, hr = _via_s6(_group_slice(p, g, HG))
+        hs = slice(g * HG, (g + 1) * HG)
+        np.testing.assert_allclose(y[:, :, hs], yr, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(h[:, hs], hr, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("old,new", [("Bm[:, :, g], np.asarray(Cm)[:, :, g]", "Bm[:, :, G - 1 - g], np.asarray(Cm)[:, :, g]"),
+                                     ("sel = slice(g * hg, (g + 1) * hg)", "sel = slice(0, hg)")])
+def test_planted_group_mistake_is_caught(old, new):
+    src = inspect.getsource(ssd_oracle.ssd)
+    assert old in src
+    ns = dict(vars(ssd_oracle))
+    exec(src.replace(old, new), ns)
+    p = _grouped(12, 2, 2)
+    y, _ = _run(p, fn=ns["ssd"])
+    yr, _ = _via_s6(_group_slice(p, 1, 2))
+    assert np.max(np.abs(y[:, :, 2:4] - yr)) > 1e-6
