@@ -71,6 +71,22 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def time_calls(torch, fn, n):
+    """n calls of fn queued back to back, each between two events on the current stream,
+    and one synchronisation at the end (a synchronisation after every call lets the GPU
+    idle between calls, and a call that starts on an idle GPU runs slower).  Returns the
+    per-call times in ms, sorted."""
+    ev = []
+    for _ in range(n):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        fn()
+        b_.record()
+        ev.append((a_, b_))
+    torch.cuda.synchronize()
+    return sorted(a_.elapsed_time(b_) for a_, b_ in ev)
+
+
 def load_traffic(name, src_hash):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
     only while the kernel sources are unchanged since they were taken."""
@@ -653,15 +669,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         for _ in range(30):   # also brings the clocks back up after the host work before it
             ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
         torch.cuda.synchronize()
-        vt = []
-        for _ in range(10):
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_.record()
-            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
-            b_.record()
-            torch.cuda.synchronize()
-            vt.append(a_.elapsed_time(b_))
-        vt.sort()
+        vt = time_calls(torch, lambda disc=disc: ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws,
+                                                              discretization=disc), 10)
         ms = vt[len(vt) // 2]
         upd = Bsz * L * D * N
         slots = upd * sm[disc] + Bsz * L * D * sm["token_gated"]
@@ -672,7 +681,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
             "roofline": {"bound": "alu", "achieved": round(ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                          "unit": "Tslot/s", "frac": round(ts / VALU_PEAK_TSLOTS, 4),
                          "alg_slots_per_launch": slots},
-            "timing": "median of 10 launches, each between two events (B/C pre-pass included)",
+            "timing": "median of 10 launches queued back to back, each between two events (B/C pre-pass included)",
         }
         log(f"{disc}: {ms * 1e3:.1f} us/launch, {upd / (ms * 1e-3):.3e} updates/s, "
             f"VALU {ts / VALU_PEAK_TSLOTS:.1%}")
@@ -692,15 +701,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     for _ in range(30):
         ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
     torch.cuda.synchronize()
-    st = []
-    for _ in range(10):
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
-        b_.record()
-        torch.cuda.synchronize()
-        st.append(a_.elapsed_time(b_))
-    st.sort()
+    st = time_calls(torch, lambda: ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                               out=t["y"]), 10)
     ms = st[len(st) // 2]
     byts, flops = ssd_alg(SSD_SHAPE)
     gbs = byts / (ms * 1e-3) / 1e9
@@ -718,7 +720,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
                  "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "alg_flops_per_launch": flops,
                  "note": "algorithmic flops of the chunked form (chunk 64); the kernel issues about 1.7x "
                          "that (split-bf16 operands, full diagonal tiles)"},
-        "timing": "median of 10 launches, each between two events",
+        "timing": "median of 10 launches queued back to back, each between two events",
     }
     log(f"ssd: {ms * 1e3:.1f} us/launch, HBM {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}), "
         f"MFMA {tfs:.0f} TFLOP/s ({tfs / MFMA_BF16_PEAK_TFS:.1%})")
@@ -812,15 +814,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     for _ in range(2):
         ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
     torch.cuda.synchronize()
-    bt = []
-    for _ in range(5):
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
-        b_.record()
-        torch.cuda.synchronize()
-        bt.append(a_.elapsed_time(b_))
-    bt.sort()
+    bt = time_calls(torch, lambda: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False), 5)
     ms = bt[len(bt) // 2]
     upd = Bsz * L * D * N
     bwd_ts = upd * sm["bwd"] / (ms * 1e-3) / 1e12
@@ -831,7 +825,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         "roofline": {"bound": "alu", "achieved": round(bwd_ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "Tslot/s", "frac": round(bwd_ts / VALU_PEAK_TSLOTS, 4),
                      "alg_slots_per_launch": upd * sm["bwd"]},
-        "timing": "median of 5 calls (checkpoint pass, reverse sweep, reductions), each between two events",
+        "timing": "median of 5 calls queued back to back (checkpoint pass, reverse sweep, reductions), each between two events",
         "note": "forward sweep with state checkpoints every 8 steps, then the reverse sweep with recompute",
         "workspace_bytes": ws.numel(),
         "workspace_bytes_given_saved_checkpoints": ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16", True),
@@ -845,15 +839,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         for _ in range(2):
             ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False, discretization=disc)
         torch.cuda.synchronize()
-        vt = []
-        for _ in range(5):
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_.record()
-            ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False, discretization=disc)
-            b_.record()
-            torch.cuda.synchronize()
-            vt.append(a_.elapsed_time(b_))
-        vt.sort()
+        vt = time_calls(torch, lambda disc=disc: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws,
+                                                              need_dh0=False, discretization=disc), 5)
         vms = vt[len(vt) // 2]
         out["backward"]["variants"][disc] = {"ms_median": round(vms, 4), "state_updates_per_s": upd / (vms * 1e-3)}
         log(f"backward, {disc}: {vms:.3f} ms median ({upd / (vms * 1e-3):.3e} state-updates/s)")
@@ -884,16 +871,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
             for f in fns:
                 f()
         torch.cuda.synchronize()
-        tt = []
-        for _ in range(5):
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_.record()
-            for f in fns:
-                f()
-            b_.record()
-            torch.cuda.synchronize()
-            tt.append(a_.elapsed_time(b_))
-        tt.sort()
+        tt = time_calls(torch, lambda: [f() for f in fns], 5)
         return tt[len(tt) // 2]
 
     t_save, t_bsaved = med([fwd_save]), med([bwd_saved])
@@ -904,7 +882,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         "ms_step_with_saved_checkpoints": round(t_pair_saved, 4),
         "ms_step_recomputing_checkpoints": round(t_pair_plain, 4),
         "checkpoint_bytes": ck_b,
-        "timing": "medians of 5, each call or pair between two events",
+        "timing": "medians of 5 queued back to back, each call or pair between two events",
     }
     log(f"training step: forward saving checkpoints {t_save:.3f} ms + backward from them {t_bsaved:.3f} ms; "
         f"pair {t_pair_saved:.3f} ms against {t_pair_plain:.3f} ms for forward + recomputing backward")
@@ -981,15 +959,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     for _ in range(2):
         ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb, need_dh0=False)
     torch.cuda.synchronize()
-    bt = []
-    for _ in range(3):
-        a_e, b_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_e.record()
-        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb, need_dh0=False)
-        b_e.record()
-        torch.cuda.synchronize()
-        bt.append(a_e.elapsed_time(b_e))
-    bt.sort()
+    bt = time_calls(torch, lambda: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb,
+                                                need_dh0=False), 3)
     ms = bt[len(bt) // 2]
     bwd_ts = upd * sm["bwd"] / (ms * 1e-3) / 1e12
     out["long_sequence_backward"] = {
@@ -998,7 +969,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         "roofline": {"bound": "alu", "achieved": round(bwd_ts, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "Tslot/s", "frac": round(bwd_ts / VALU_PEAK_TSLOTS, 4),
                      "alg_slots_per_launch": upd * sm["bwd"]},
-        "timing": "median of 3 calls, each between two events",
+        "timing": "median of 3 calls queued back to back, each between two events",
         "note": "chunks of the forward planner (16 x 65536 steps): chunked checkpoint pass, adjoint carries and "
                 "their combine, reverse sweep per chunk; the carry passes are not counted as algorithmic work",
         "workspace_bytes": wsb.numel(),
