@@ -277,10 +277,12 @@ def main():
         # Settle: a fresh process's first ~50 flushed launches run up to 15% slower than the
         # ones after them (285 -> 267 -> 252 us in successive groups of 25 on one MI355X, flat
         # from there over 400 launches), so the timed launches follow that many untimed ones
-        # under the same flushed protocol, then the warmup steps.
-        for _ in range(args.settle if flush is not None else 0):
-            flush.fill_(1)
-            step()
+        # under the same flushed protocol, then the warmup steps.  (A profiling run settles too,
+        # on the path it profiles, so that its trace's later dispatches are the settled ones.)
+        for _ in range(args.settle):
+            if flush is not None:
+                flush.fill_(1)
+            step(args.profile_run and args.profile_general)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -325,7 +327,7 @@ def main():
         result.update({
             "metric": "state-updates/s (B*L*D*N), scan B4 L4096 D4096 N16",
             "value": value, "unit": "state-updates/s", "n_gpus": 1, "steps": steps,
-            "warmup": args.warmup, "settle_launches": 0 if args.profile_run else args.settle,
+            "warmup": args.warmup, "settle_launches": args.settle,
             "ms_per_step": ms_per_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "dtype_note": "the arithmetic and the state are fp32; x, delta, z, B, C and y are stored as bf16",
