@@ -87,6 +87,22 @@ def time_calls(torch, fn, n):
     return sorted(a_.elapsed_time(b_) for a_, b_ in ev)
 
 
+def settle_calls(torch, fn, ms=50.0):
+    """Untimed calls of fn for about ms of GPU time (at least two): the GPU runs a workload
+    slower for its first ~25 ms after the host work between workloads."""
+    fn()
+    torch.cuda.synchronize()
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record()
+    fn()
+    b_.record()
+    torch.cuda.synchronize()
+    n = max(1, int(ms / max(a_.elapsed_time(b_), 1e-3)))
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+
+
 def load_traffic(name, src_hash):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
     only while the kernel sources are unchanged since they were taken."""
@@ -610,7 +626,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     with torch.cuda.graph(graph):
         run_decode_steps()
     reps = []
-    for _ in range(3):
+    for _ in range(5):   # (the first replays also settle the GPU after the host work before them)
         h.zero_()
         torch.cuda.synchronize()
         e0.record()
@@ -630,7 +646,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
                      "frac": round(step_bytes / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("state_update_B256_D4096_N16_bf16_gated", src_hash),
                      "kernel_us_avg": round(k_avg * 1e3, 2), "alg_bytes_per_launch": step_bytes},
-        "timing": "HIP graph of the 1024-step loop, best of 3 replays; per-step = replay / 1024",
+        "timing": "HIP graph of the 1024-step loop, best of 5 replays; per-step = replay / 1024",
         "eager_ms_total": round(eager_ms, 2),
         "note": "h (67 MB) fits the 256 MB Infinity Cache, so steps after the first can beat HBM",
     }
@@ -668,9 +684,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
                      device=dev)
     out["variants"] = {}
     for disc in ("zoh", "bilinear"):
-        for _ in range(30):   # also brings the clocks back up after the host work before it
-            ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws, discretization=disc)
-        torch.cuda.synchronize()
+        settle_calls(torch, lambda disc=disc: ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws,
+                                                           discretization=disc))
         vt = time_calls(torch, lambda disc=disc: ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, z, out=y, workspace=ws,
                                                               discretization=disc), 10)
         ms = vt[len(vt) // 2]
@@ -700,9 +715,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     torch.cuda.empty_cache()
     # --- multi-head SSD scan (Mamba-2 layer) on the matrix cores ---
     t = _ssd_inputs(torch, dev)
-    for _ in range(30):
-        ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
-    torch.cuda.synchronize()
+    settle_calls(torch, lambda: ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"]))
     st = time_calls(torch, lambda: ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
                                                out=t["y"]), 10)
     ms = st[len(st) // 2]
@@ -736,9 +749,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     # --- causal conv1d + SiLU at the headline shape (HBM-bound) ---
     x, w, bias = _conv_inputs(torch, synth, dev)
     yc = torch.empty_like(x)
-    for _ in range(3):
-        ssm.conv1d_fwd(x, w, bias, out=yc)
-    torch.cuda.synchronize()
+    settle_calls(torch, lambda: ssm.conv1d_fwd(x, w, bias, out=yc))
     # 20 launches back to back between two events (a single launch would also time the
     # host's launch latency, longer than this kernel's gaps), 5 repetitions
     ct = []
@@ -772,9 +783,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     # --- its backward (dx, dw, dbias) at the same shape ---
     gyc = _randn(tuple(x.shape), gen, dev, bf)
     cws = torch.empty(ssm.conv1d_bwd_workspace_bytes(*x.shape, w.shape[1], "bf16"), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        ssm.conv1d_bwd(x, w, bias, None, gyc, workspace=cws)
-    torch.cuda.synchronize()
+    settle_calls(torch, lambda: ssm.conv1d_bwd(x, w, bias, None, gyc, workspace=cws))
     ct = []
     for _ in range(5):
         a_e, b_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -813,9 +822,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     A = torch.from_numpy(synth.make_A(2, D, N)).to(dev)
     Dk = torch.from_numpy(synth.make_D(2, D, "normal")).to(dev)
     ws = torch.empty(ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16"), dtype=torch.uint8, device=dev)
-    for _ in range(2):
-        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False)
-    torch.cuda.synchronize()
+    settle_calls(torch, lambda: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False))
     bt = time_calls(torch, lambda: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False), 5)
     ms = bt[len(bt) // 2]
     upd = Bsz * L * D * N
@@ -838,9 +845,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     # work per state update than Mamba's; timed, not priced against the roofline)
     out["backward"]["variants"] = {}
     for disc in ("zoh", "bilinear"):
-        for _ in range(2):
-            ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws, need_dh0=False, discretization=disc)
-        torch.cuda.synchronize()
+        settle_calls(torch, lambda disc=disc: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws,
+                                                           need_dh0=False, discretization=disc))
         vt = time_calls(torch, lambda disc=disc: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=ws,
                                                               need_dh0=False, discretization=disc), 5)
         vms = vt[len(vt) // 2]
@@ -869,10 +875,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, z, None, gy, workspace=bws, need_dh0=False, checkpoints=ck)
 
     def med(fns):
-        for _ in range(2):
-            for f in fns:
-                f()
-        torch.cuda.synchronize()
+        settle_calls(torch, lambda: [f() for f in fns])
         tt = time_calls(torch, lambda: [f() for f in fns], 5)
         return tt[len(tt) // 2]
 
@@ -912,9 +915,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     plan = ssm.scan_plan(Bsz, L, D, N, "bf16")
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
-    for _ in range(2):
-        ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, out=y, workspace=ws)
-    torch.cuda.synchronize()
+    settle_calls(torch, lambda: ssm.scan_fwd(x, dl, A, Bm, Cm, Dk, out=y, workspace=ws))
     reps = 5
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i in range(reps):
@@ -958,9 +959,7 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
     # carries, one reverse sweep per chunk) ---
     gy = _randn((Bsz, L, D), gen, dev, bf)
     wsb = torch.empty(ssm.scan_bwd_workspace_bytes(Bsz, L, D, N, "bf16"), dtype=torch.uint8, device=dev)
-    for _ in range(2):
-        ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb, need_dh0=False)
-    torch.cuda.synchronize()
+    settle_calls(torch, lambda: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb, need_dh0=False))
     bt = time_calls(torch, lambda: ssm.scan_bwd(x, dl, A, Bm, Cm, Dk, None, None, gy, workspace=wsb,
                                                 need_dh0=False), 3)
     ms = bt[len(bt) // 2]
