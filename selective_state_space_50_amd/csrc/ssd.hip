@@ -116,7 +116,9 @@ __device__ __forceinline__ s8 lds8(const uint16_t *p) { return *reinterpret_cast
 // tile index of (s-block k, t-block i), k <= i
 __host__ __device__ constexpr int tile_of(int k, int i) { return i * (i + 1) / 2 + k; }
 
-template <bool HAS_Z>
+// G1: one B/C group (rows kNS apart, a compile-time stride; with a runtime stride the row
+// address arithmetic took the kernel past its register budget and it spilled)
+template <bool HAS_Z, bool G1>
 __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
     __shared__ SsdSmem sm;
     const int tid = threadIdx.x;
@@ -328,8 +330,8 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
         const uint16_t *X = static_cast<const uint16_t *>(a.x) + (b * L * H + h) * kP;   // row t at + t H kP
         const uint16_t *DL = static_cast<const uint16_t *>(a.delta) + b * L * H + h;      // step t at + t H
         // B, C rows of this head's group: row t at + t BR
-        const int64_t BR = a.G * kNS;
-        const int64_t grp = h / (H / a.G);
+        const int64_t BR = G1 ? kNS : a.G * kNS;
+        const int64_t grp = G1 ? 0 : h / (H / a.G);
         const uint16_t *BM = static_cast<const uint16_t *>(a.Bm) + b * L * BR + grp * kNS;
         const uint16_t *CM = static_cast<const uint16_t *>(a.Cm) + b * L * BR + grp * kNS;
 
@@ -361,8 +363,18 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) xg[i] = (X + row(t0 + 8 * w + i) * xs)[lane];
+            if constexpr (G1) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) bg[i] = (BM + row(t0 + ts + i) * BR)[tn];
+                for (int i = 0; i < 16; ++i) bg[i] = (BM + row(t0 + ts + i) * BR)[tn];
+            } else {
+                // (a runtime row stride: each row offset made wave-uniform, so every load takes
+                // a scalar row base and one lane offset instead of a 64-bit address per row)
+                const uint32_t br = static_cast<uint32_t>(BR);
+                const uint16_t *Bc = BM + t0 * BR;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    bg[i] = (Bc + __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row(t0 + ts + i) - t0) * br))[tn];
+            }
             if (w == 0) {
                 const int64_t t = t0 + lane;
                 dq = DL[(PART && t >= L ? L - 1 : t) * H];
@@ -446,8 +458,13 @@ __global__ void __launch_bounds__(kThreads) ssd_kernel(SsdArgs a) {
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t s) {
     const int64_t W = a.B * a.H;
     const dim3 grid(static_cast<unsigned>(((W + 7) / 8) * 8));
-    if (a.z) hipLaunchKernelGGL((ssd_kernel<true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((ssd_kernel<false>), grid, dim3(kThreads), 0, s, a);
+    if (a.G == 1) {
+        if (a.z) hipLaunchKernelGGL((ssd_kernel<true, true>), grid, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((ssd_kernel<false, true>), grid, dim3(kThreads), 0, s, a);
+    } else {
+        if (a.z) hipLaunchKernelGGL((ssd_kernel<true, false>), grid, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((ssd_kernel<false, false>), grid, dim3(kThreads), 0, s, a);
+    }
     return launch_status(s);
 }
 

@@ -53,3 +53,19 @@ def test_scan_kernel_occupancy_budgets(tmp_path, src, disc):
         assert r["vgpr_count"] <= 128, (name, r)
         assert r.get("vgpr_spill_count", 0) == 0, (name, r)
     assert seen == 8, sorted(ks)
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="no hipcc")
+def test_ssd_kernel_register_budget(tmp_path):
+    """The matrix-core SSD kernel runs 16 waves per workgroup (four per SIMD), so at most 128
+    VGPRs per lane; none of its instantiations may spill vector registers to scratch (a
+    runtime B/C row stride once did, and cost 14% of the launch)."""
+    ks = _kernels("ssd.hip", tmp_path)
+    seen = 0
+    for name, r in ks.items():
+        if "ssd_kernel" not in name:
+            continue
+        seen += 1
+        assert r["vgpr_count"] <= 128, (name, r)
+        assert r.get("vgpr_spill_count", 0) == 0, (name, r)
+    assert seen == 4, sorted(ks)
