@@ -69,3 +69,18 @@ def test_ssd_kernel_register_budget(tmp_path):
         assert r["vgpr_count"] <= 128, (name, r)
         assert r.get("vgpr_spill_count", 0) == 0, (name, r)
     assert seen == 4, sorted(ks)
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="no hipcc")
+def test_backward_sweep_register_budget(tmp_path):
+    """The reverse sweep runs 8 waves per workgroup, one workgroup per CU (two waves per SIMD,
+    at most 256 VGPRs); no instantiation, for any discretisation, may spill to scratch."""
+    ks = _kernels("scan_bwd.hip", tmp_path)
+    seen = 0
+    for name, r in ks.items():
+        if "scan_bwd_kernel" not in name:
+            continue
+        seen += 1
+        assert r["vgpr_count"] <= 256, (name, r)
+        assert r.get("vgpr_spill_count", 0) == 0, (name, r)
+    assert seen == 12, sorted(ks)
