@@ -320,12 +320,14 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   workspace device memory of ssm_scan_bwd_workspace_bytes(..., checkpoints != NULL)
  *             bytes (partial sums, and without saved checkpoints the checkpoints)
  *
- * Any 1 <= dstate <= 16 (more is SSM_EUNSUPPORTED) and any dim.  dstate == 16 with dim a
- * multiple of 64 runs the native kernels in place; other shapes run them on copies
- * padded (in the workspace) to
- * the next multiple of 64 channels and to 16 states, whose padding carries x = 0 and
- * B = C = 0 and so adds nothing to any gradient; those shapes take no saved
- * checkpoints (SSM_EUNSUPPORTED).  dim == 0 is a no-op; batch == 0 or seqlen == 0 sets
+ * Any 1 <= dstate <= 256 (more is SSM_EUNSUPPORTED) and any dim.  dstate == 16 with dim a
+ * multiple of 64 runs the native kernels in place; dstate < 16 or other dims run them on
+ * copies padded (in the workspace) to the next multiple of 64 channels and to 16 states,
+ * whose padding carries x = 0 and B = C = 0 and so adds nothing to any gradient; dstate >
+ * 16 runs them once per group of 16 states on fp32 copies (the states of one group neither
+ * read nor write another's), with dx, ddelta, dz and ddelta_bias summed over the groups in
+ * fp32 and D's terms taken in the first group only.  Shapes other than dstate == 16 with
+ * dim a multiple of 64 take no saved checkpoints (SSM_EUNSUPPORTED).  dim == 0 is a no-op; batch == 0 or seqlen == 0 sets
  * dA, dD, ddelta_bias to zero (and, with seqlen == 0, dh0 = dh_last or zeros).
  * Deterministic: every reduction runs in a fixed order.
  */

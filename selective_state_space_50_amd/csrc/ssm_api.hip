@@ -549,6 +549,74 @@ hipError_t unpad3(void *dst, const void *src, int64_t n0, int64_t n1, int64_t n2
     return launch_status(s);
 }
 
+// dst [n0][m1][m2] (Eo) from columns c0 .. c0 + m2 - 1 of src [n0][n1][n2] (Ei), converted;
+// rows past n1, columns past n2 and an absent src take fill
+template <typename Eo, typename Ei>
+__global__ void __launch_bounds__(256) gpad3_kernel(Eo *dst, const Ei *src, int64_t n0, int64_t n1, int64_t n2,
+                                                    int64_t c0, int64_t m1, int64_t m2, float fill) {
+    const int64_t total = n0 * m1 * m2;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i2 = i % m2, r = i / m2, i1 = r % m1, i0 = r / m1, c = c0 + i2;
+        put(dst, i, (src && i1 < n1 && c < n2) ? widen(src, (i0 * n1 + i1) * n2 + c) : fill);
+    }
+}
+
+// columns c0 .. c0 + w - 1 of dst [n0][n1][n2] (Eo) from the leading w columns of
+// src [n0][n1][m2] (Ei), converted (w = min(m2, n2 - c0))
+template <typename Eo, typename Ei>
+__global__ void __launch_bounds__(256) gunpad3_kernel(Eo *dst, const Ei *src, int64_t n0, int64_t n1, int64_t n2,
+                                                      int64_t c0, int64_t m1, int64_t m2, int64_t w) {
+    const int64_t total = n0 * n1 * w;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i2 = i % w, r = i / w, i1 = r % n1, i0 = r / n1;
+        put(dst, (i0 * n1 + i1) * n2 + c0 + i2, widen(src, (i0 * m1 + i1) * m2 + i2));
+    }
+}
+
+__global__ void __launch_bounds__(256) add_kernel(float *dst, const float *src, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        dst[i] += src[i];
+}
+
+// es-byte elements in and out (2: bf16, 4: fp32)
+hipError_t gpad3(void *dst, size_t eo, const void *src, size_t ei, int64_t n0, int64_t n1, int64_t n2, int64_t c0,
+                 int64_t m1, int64_t m2, float fill, hipStream_t s) {
+    const dim3 g = grid_for(n0 * m1 * m2);
+    if (eo == 4 && ei == 2)
+        hipLaunchKernelGGL((gpad3_kernel<float, uint16_t>), g, dim3(256), 0, s, static_cast<float *>(dst),
+                           static_cast<const uint16_t *>(src), n0, n1, n2, c0, m1, m2, fill);
+    else if (eo == 4 && ei == 4)
+        hipLaunchKernelGGL((gpad3_kernel<float, float>), g, dim3(256), 0, s, static_cast<float *>(dst),
+                           static_cast<const float *>(src), n0, n1, n2, c0, m1, m2, fill);
+    else
+        return hipErrorInvalidValue;
+    return launch_status(s);
+}
+
+hipError_t gunpad3(void *dst, size_t eo, const void *src, size_t ei, int64_t n0, int64_t n1, int64_t n2, int64_t c0,
+                   int64_t m1, int64_t m2, hipStream_t s) {
+    const int64_t w = m2 < n2 - c0 ? m2 : n2 - c0;
+    if (w <= 0) return hipSuccess;
+    const dim3 g = grid_for(n0 * n1 * w);
+    if (eo == 2 && ei == 4)
+        hipLaunchKernelGGL((gunpad3_kernel<uint16_t, float>), g, dim3(256), 0, s, static_cast<uint16_t *>(dst),
+                           static_cast<const float *>(src), n0, n1, n2, c0, m1, m2, w);
+    else if (eo == 4 && ei == 4)
+        hipLaunchKernelGGL((gunpad3_kernel<float, float>), g, dim3(256), 0, s, static_cast<float *>(dst),
+                           static_cast<const float *>(src), n0, n1, n2, c0, m1, m2, w);
+    else
+        return hipErrorInvalidValue;
+    return launch_status(s);
+}
+
+hipError_t add_f32(float *dst, const float *src, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(add_kernel, grid_for(n), dim3(256), 0, s, dst, src, n);
+    return launch_status(s);
+}
+
 }  // namespace
 }  // namespace ssm
 
@@ -569,7 +637,8 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
     if (st != SSM_OK) return st;
     log_call("scan_bwd B=%lld L=%lld D=%lld N=%lld dtype=%d disc=%d: %s, %lld chunk(s) of %lld, %s, workspace %zu B",
              (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, dtype, discretization,
-             p.pad ? "native kernels on padded copies" : "native kernels", (long long)p.n_chunks,
+             p.pad ? (p.K > 1 ? "native kernels per group of 16 states on fp32 copies" : "native kernels on padded copies")
+                   : "native kernels", (long long)p.n_chunks,
              (long long)p.chunk_len, checkpoints ? "saved checkpoints" : "own checkpoint pass",
              checkpoints ? p.ws_bytes_saved : p.ws_bytes);
     if (dim == 0) return SSM_OK;
@@ -603,6 +672,92 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         return SSM_OK;
     }
     char *ws = static_cast<char *>(workspace);
+    if (p.pad && p.K > 1) {
+        // more than 16 states: the native backward once per group of 16 states, on fp32
+        // copies; the states of one group neither read nor write another's, and the
+        // per-channel gradients are linear in the per-state terms, so they are the groups'
+        // sums (D and its terms in group 0 only)
+        BwdPlan in;
+        st = plan_scan_bwd(batch, seqlen, p.Dp, 16, SSM_DTYPE_F32, &in);
+        if (st != SSM_OK) return st;
+        const size_t es = dtype_size(dtype);
+        const int64_t BL = batch * seqlen, Dp = p.Dp, N = dstate;
+        auto at = [&](int i) { return static_cast<void *>(ws + p.pad_off[i]); };
+        auto atf = [&](int i) { return reinterpret_cast<float *>(ws + p.pad_off[i]); };
+        struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; } toks[] = {
+            {at(kPX), x, BL, 1, dim, 1, Dp, es},
+            {at(kPDelta), delta, BL, 1, dim, 1, Dp, es},
+            {at(kPZ), z, BL, 1, dim, 1, Dp, es},
+            {at(kPDy), dy, BL, 1, dim, 1, Dp, es},
+            {at(kPDskip), Dskip, 1, 1, dim, 1, Dp, 4},
+            {at(kPBias), delta_bias, 1, 1, dim, 1, Dp, 4},
+        };
+        for (const auto &c : toks) {
+            if (!c.src) continue;
+            e = gpad3(c.dst, 4, c.src, c.es, c.n0, c.n1, c.n2, 0, c.m1, c.m2, 0.0f, s);
+            if (e != hipSuccess) return hip_fail("pad launch", e);
+        }
+        for (int64_t g = 0; g < p.K; ++g) {
+            const int64_t c0 = 16 * g;
+            struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; float fill; } ins[] = {
+                {at(kPB), B, BL, 1, N, 1, 16, es, 0.0f},
+                {at(kPC), C, BL, 1, N, 1, 16, es, 0.0f},
+                {at(kPA), A, 1, dim, N, Dp, 16, 4, -1.0f},
+                {at(kPH0), h0, batch, dim, N, Dp, 16, 4, 0.0f},
+                {at(kPDhLast), dh_last, batch, dim, N, Dp, 16, 4, 0.0f},
+            };
+            for (const auto &c : ins) {
+                if (!c.src && c.dst != at(kPA)) continue;
+                e = gpad3(c.dst, 4, c.src, c.es, c.n0, c.n1, c.n2, c0, c.m1, c.m2, c.fill, s);
+                if (e != hipSuccess) return hip_fail("pad launch", e);
+            }
+            // group 0 writes the per-channel gradients straight into their sums
+            const bool g0 = g == 0;
+            float *gdx = g0 ? atf(kSDx) : atf(kPDx), *gdd = g0 ? atf(kSDdelta) : atf(kPDdelta);
+            float *gdz = g0 ? atf(kSDz) : atf(kPDz), *gdb = g0 ? atf(kSDBias) : atf(kPDBias);
+            st = bwd_native(batch, seqlen, Dp, 16, SSM_DTYPE_F32, at(kPX), at(kPDelta), atf(kPA), at(kPB), at(kPC),
+                            (g0 && Dskip) ? atf(kPDskip) : nullptr, z ? at(kPZ) : nullptr,
+                            h0 ? atf(kPH0) : nullptr, at(kPDy), dh_last ? atf(kPDhLast) : nullptr, gdx, gdd,
+                            atf(kPDA), at(kPDB), at(kPDC), (g0 && Dskip) ? atf(kPDD) : nullptr,
+                            z ? static_cast<void *>(gdz) : nullptr, dh0 ? atf(kPDh0) : nullptr, delta_softplus,
+                            discretization, delta_bias ? atf(kPBias) : nullptr, delta_bias ? gdb : nullptr,
+                            nullptr, ws + p.inner_off, in, s);
+            if (st != SSM_OK) return st;
+            if (!g0) {
+                const int64_t nt = BL * Dp;
+                e = add_f32(atf(kSDx), gdx, nt, s);
+                if (e == hipSuccess) e = add_f32(atf(kSDdelta), gdd, nt, s);
+                if (e == hipSuccess && z) e = add_f32(atf(kSDz), gdz, nt, s);
+                if (e == hipSuccess && delta_bias) e = add_f32(atf(kSDBias), gdb, Dp, s);
+                if (e != hipSuccess) return hip_fail("sum launch", e);
+            }
+            // this group's columns of the per-state gradients
+            struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; } outs[] = {
+                {dB, at(kPDB), BL, 1, N, 1, 16, es},
+                {dC, at(kPDC), BL, 1, N, 1, 16, es},
+                {dA, at(kPDA), 1, dim, N, Dp, 16, 4},
+                {dh0, at(kPDh0), batch, dim, N, Dp, 16, 4},
+            };
+            for (const auto &c : outs) {
+                if (!c.dst) continue;
+                e = gunpad3(c.dst, c.es, c.src, 4, c.n0, c.n1, c.n2, c0, c.m1, c.m2, s);
+                if (e != hipSuccess) return hip_fail("unpad launch", e);
+            }
+        }
+        struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; } outs[] = {
+            {dx, at(kSDx), BL, 1, dim, 1, Dp, es},
+            {ddelta, at(kSDdelta), BL, 1, dim, 1, Dp, es},
+            {z ? dz : nullptr, at(kSDz), BL, 1, dim, 1, Dp, es},
+            {Dskip ? dD : nullptr, at(kPDD), 1, 1, dim, 1, Dp, 4},
+            {delta_bias ? ddelta_bias : nullptr, at(kSDBias), 1, 1, dim, 1, Dp, 4},
+        };
+        for (const auto &c : outs) {
+            if (!c.dst) continue;
+            e = gunpad3(c.dst, c.es, c.src, 4, c.n0, c.n1, c.n2, 0, c.m1, c.m2, s);
+            if (e != hipSuccess) return hip_fail("unpad launch", e);
+        }
+        return SSM_OK;
+    }
     if (p.pad) {
         // dstate < 16 or dim not a multiple of 64: the native backward on padded copies
         BwdPlan in;

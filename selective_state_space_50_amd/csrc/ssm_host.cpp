@@ -396,26 +396,30 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
         set_error("ssm_scan_bwd: dim=%lld is too large", (long long)dim);
         return SSM_EUNSUPPORTED;
     }
-    if (dstate > 16) {
-        set_error("ssm_scan_bwd supports dstate <= 16 (got %lld)", (long long)dstate);
+    if (dstate > 256) {
+        set_error("ssm_scan_bwd supports dstate <= 256 (got %lld)", (long long)dstate);
         return SSM_EUNSUPPORTED;
     }
     if (dstate != 16 || dim % 64 != 0) {
-        // run on copies padded to dim Dp and 16 states: the padding channels carry x = 0, the
-        // padding states B = C = 0 (and A = -1), so neither adds to any gradient
+        // run on copies padded to dim Dp and 16 states per group: the padding channels carry
+        // x = 0, the padding states B = C = 0 (and A = -1), so neither adds to any gradient
         BwdPlan p;
         p.pad = true;
         p.Dp = ceil_div(dim, 64) * 64;
+        p.K = ceil_div(dstate, 16);
+        const int gdt = p.K > 1 ? SSM_DTYPE_F32 : dtype;   // the dtype the native kernels run in
         BwdPlan in;
-        st = plan_scan_bwd(batch, seqlen, p.Dp, 16, dtype, &in);
+        st = plan_scan_bwd(batch, seqlen, p.Dp, 16, gdt, &in);
         if (st != SSM_OK) return st;
         const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen);
-        const size_t Dp = static_cast<size_t>(p.Dp), es = dtype_size(dtype);
+        const size_t Dp = static_cast<size_t>(p.Dp), es = dtype_size(gdt);
         const size_t tok = B * L * Dp * es, bc = B * L * 16 * es, st16 = B * Dp * 16 * sizeof(float);
+        const size_t sum = p.K > 1 ? B * L * Dp * sizeof(float) : 0;
         const size_t bytes[kPadBufs] = {tok, tok, tok, tok, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
                                         Dp * sizeof(float), st16, st16,
                                         tok, tok, tok, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
-                                        Dp * sizeof(float), st16};
+                                        Dp * sizeof(float), st16,
+                                        sum, sum, sum, p.K > 1 ? Dp * sizeof(float) : 0};
         size_t ws = 0;
         for (int i = 0; i < kPadBufs; ++i) {
             p.pad_off[i] = ws;

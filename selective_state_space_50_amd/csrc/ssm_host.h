@@ -79,10 +79,12 @@ inline const float *variant_bias(const ssm_variant *v) { return v ? v->delta_bia
 // dA/dD, the adjoint carries, then (last, so that a call given saved checkpoints needs
 // only the part before them) the forward checkpoint pass's own workspace and the state
 // checkpoints.
-// Buffers of the padded backward, in workspace order: inputs, then outputs.
+// Buffers of the padded backward, in workspace order: inputs, then outputs, then (with more
+// than one group of 16 states) the fp32 sums of the per-channel gradients over the groups.
 enum PadBuf {
     kPX, kPDelta, kPZ, kPDy, kPB, kPC, kPA, kPDskip, kPBias, kPH0, kPDhLast,
-    kPDx, kPDdelta, kPDz, kPDB, kPDC, kPDA, kPDD, kPDBias, kPDh0, kPadBufs
+    kPDx, kPDdelta, kPDz, kPDB, kPDC, kPDA, kPDD, kPDBias, kPDh0,
+    kSDx, kSDdelta, kSDz, kSDBias, kPadBufs
 };
 
 struct BwdPlan {
@@ -101,6 +103,11 @@ struct BwdPlan {
     // region comes first, the native plan's workspace (of the padded shape) after it.
     bool pad = false;
     int64_t Dp = 0;
+    // More than 16 states: K = ceil(dstate / 16) groups of 16, each run through the native
+    // kernels on fp32 copies (the token tensors once, B, C, A and the states per group); the
+    // per-channel gradients (dx, ddelta, dz, the bias's) are sums over the groups, D enters
+    // in group 0 only.  K == 1 is the padded path above, on copies of the input dtype.
+    int64_t K = 1;
     size_t pad_off[kPadBufs] = {};
     size_t inner_off = 0;
 };

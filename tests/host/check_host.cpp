@@ -140,7 +140,13 @@ int main() {
         EXPECT(bp.ws_bytes >= bp.inner_off + in.ws_bytes && bp.ws_bytes_saved == bp.ws_bytes);
         EXPECT(ssm_scan_bwd_workspace_bytes(2, 100, 40, 8, SSM_DTYPE_BF16, 0) == bp.ws_bytes);
         EXPECT(plan_scan_bwd(1, 10, 128, 3, SSM_DTYPE_F32, &bp) == SSM_OK && bp.pad && bp.Dp == 128);
-        EXPECT(plan_scan_bwd(1, 10, 128, 17, SSM_DTYPE_F32, &bp) == SSM_EUNSUPPORTED);
+        EXPECT(plan_scan_bwd(1, 10, 128, 257, SSM_DTYPE_F32, &bp) == SSM_EUNSUPPORTED);
+        // more than 16 states: groups of 16 on fp32 copies, with fp32 sums of the per-channel
+        // gradients after the outputs
+        EXPECT(plan_scan_bwd(2, 100, 40, 40, SSM_DTYPE_BF16, &bp) == SSM_OK && bp.pad && bp.K == 3 && bp.Dp == 64);
+        EXPECT(bp.pad_off[kPDx] >= size_t(4) * 2 * 100 * 64 * 4 && bp.pad_off[kSDx] > bp.pad_off[kPDh0]);
+        EXPECT(bp.pad_off[kSDBias] >= bp.pad_off[kSDz] + size_t(2) * 100 * 64 * 4 && bp.inner_off > bp.pad_off[kSDBias]);
+        EXPECT(plan_scan_bwd(2, 100, 40, 8, SSM_DTYPE_BF16, &bp) == SSM_OK && bp.K == 1);
         EXPECT(check_scan_bwd(2, 100, 40, 8, SSM_DTYPE_BF16, x, dl, A, B, C, nullptr, nullptr, nullptr, dl, nullptr,
                               dx, ddl, dA, dB, dC, nullptr, nullptr, nullptr, 0, SSM_DISC_MAMBA, nullptr,
                               nullptr, ck, bws, size_t(1) << 30, &bp) == SSM_EUNSUPPORTED);

@@ -135,6 +135,38 @@ def test_backward_generic_shapes(ssm, Bsz, L, D, N, dt, disc, gate, h0, dhl, sp,
     _check(g, ref, dt, f"generic {Bsz}x{L}x{D} N={N} {dt} {disc} gate={gate} softplus={sp} bias={bias}")
 
 
+MANY_STATES = [
+    # B, L, D, N, dtype, discretisation, gate, h0, dh_last, softplus, bias
+    (2, 60, 64, 32, "f32", "mamba", True, True, True, False, False),
+    (1, 100, 96, 48, "bf16", "zoh", True, True, True, True, True),
+    (2, 33, 40, 17, "f32", "bilinear", False, True, False, False, False),
+    (1, 200, 128, 64, "bf16", "mamba", True, False, True, True, True),
+    (1, 24, 64, 256, "f32", "mamba", True, True, True, False, False),
+    (2, 50, 64, 100, "f32", "zoh", False, False, True, False, True),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,N,dt,disc,gate,h0,dhl,sp,bias", MANY_STATES)
+def test_backward_more_than_16_states(ssm, Bsz, L, D, N, dt, disc, gate, h0, dhl, sp, bias):
+    """17 to 256 states: the native kernels once per group of 16 states (fp32 copies), the
+    per-channel gradients summed over the groups; every output against the oracle."""
+    seed = 500 + L + D + N
+    inp = synth.scan_inputs(Bsz, L, D, N, dt, seed=seed, gate=gate, d_kind="normal", a_kind="random",
+                            softplus_input=sp, h0=h0)
+    inp["discretization"] = disc
+    if bias:
+        b = synth.make_delta_bias(seed, D)
+        inp["delta_bias"] = b if sp else (0.05 * np.abs(b)).astype(np.float32)
+    r = np.random.default_rng(seed + 1000)
+    gy = synth.store(r.standard_normal((Bsz, L, D)).astype(np.float32), dt)
+    gl = r.standard_normal((Bsz, D, N)).astype(np.float32) if dhl else None
+    g = _run(ssm, inp, gy, gl)
+    ref = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    if not gate:
+        ref["dz"] = None
+    _check(g, ref, dt, f"{N} states {Bsz}x{L}x{D} {dt} {disc} gate={gate} softplus={sp} bias={bias}")
+
+
 def test_backward_generic_rejects_saved_checkpoints(ssm):
     """Saved checkpoints exist only for dstate 16 and dim a multiple of 64."""
     import torch
@@ -179,9 +211,9 @@ def test_backward_empty_and_unsupported(ssm):
         assert g[k] is not None and float(g[k].abs().sum()) == 0.0, k
     assert g["dh0"].numel() == 0
     xs = torch.zeros((1, 4, 96), device="cuda")
-    with pytest.raises(ssm.SSMError) as e:   # more than 16 states
-        ssm.scan_bwd(xs, xs, torch.zeros((96, 17), device="cuda"), torch.zeros((1, 4, 17), device="cuda"),
-                     torch.zeros((1, 4, 17), device="cuda"), None, None, None, xs)
+    with pytest.raises(ssm.SSMError) as e:   # more than 256 states
+        ssm.scan_bwd(xs, xs, torch.zeros((96, 257), device="cuda"), torch.zeros((1, 4, 257), device="cuda"),
+                     torch.zeros((1, 4, 257), device="cuda"), None, None, None, xs)
     assert e.value.status == ssm.SSM_EUNSUPPORTED
 
 
