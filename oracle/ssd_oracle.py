@@ -136,3 +136,87 @@ def ssd_storage(inp: dict, batches=None, heads=None):
     bias = None if inp.get("delta_bias") is None else np.asarray(inp["delta_bias"], dtype=np.float64)[hs]
     h0 = None if inp.get("h0") is None else np.asarray(inp["h0"], dtype=np.float64)[bs][:, hs]
     return ssd(x, delta, a, Bm, Cm, D, z, h0, inp.get("delta_softplus", False), bias)
+
+
+def ssd_bwd(x, delta, a, Bm, Cm, D=None, z=None, h0=None, delta_softplus=False, delta_bias=None,
+            gy=None, g_last=None):
+    """Reverse-mode derivative of ``ssd`` (one B/C group: Bm, Cm [B, L, N]) for the loss
+    <gy, y> + <g_last, h_last>, all float64.
+
+    The chain rule through the recurrence above, one step at a time from the last: with
+    lam = dLoss/dH after step t ([B, H, P, N]) and gy0 = gy * silu(z):
+        lam     += gy0 (x) C_t                                  (the readout of step t)
+        dC_t    += sum_{h,p} gy0[h,p] H_t[h,p,:],    dD += sum gy0 x_t,    dx_t = D gy0
+        dx_t    += dt sum_n lam B_t,    dB_t += sum_{h,p} lam dt x_t,
+        d(dt)    = sum_{p,n} lam (a A_bar H_{t-1} + x_t B_t),   da += sum lam dt A_bar H_{t-1}
+        lam      = A_bar lam                                     (to step t - 1)
+    d(dt) is taken back through the softplus and the bias to the raw step size; dh0 is the
+    final lam, and dz = gy y0 silu'(z) with y0 the ungated output.
+    Returns a dict of dx, ddelta, dA, dB, dC, dD, dz, dh0, ddelta_bias (None where the input
+    is absent)."""
+    x = np.asarray(x, dtype=np.float64)
+    Bsz, L, H, P = x.shape
+    Bm = np.asarray(Bm, dtype=np.float64)
+    Cm = np.asarray(Cm, dtype=np.float64)
+    N = Bm.shape[2]
+    a = np.asarray(a, dtype=np.float64)
+    raw = np.asarray(delta, dtype=np.float64)
+    if delta_bias is not None:
+        raw = raw + np.asarray(delta_bias, dtype=np.float64)[None, None, :]
+    dt = _softplus(raw) if delta_softplus else raw
+    Dv = None if D is None else np.asarray(D, dtype=np.float64)
+    zz = None if z is None else np.asarray(z, dtype=np.float64)
+    gy = np.asarray(gy, dtype=np.float64)
+    # forward, keeping every state and the ungated outputs
+    states = np.empty((L + 1, Bsz, H, P, N))
+    states[0] = 0.0 if h0 is None else np.asarray(h0, dtype=np.float64)
+    abar = np.exp(dt * a[None, None, :])                              # [B, L, H]
+    y0 = np.empty((Bsz, L, H, P))
+    for t in range(L):
+        drive = (dt[:, t, :, None] * x[:, t])[:, :, :, None] * Bm[:, t, None, None, :]
+        states[t + 1] = abar[:, t, :, None, None] * states[t] + drive
+        y0[:, t] = np.einsum("bhpn,bn->bhp", states[t + 1], Cm[:, t])
+        if Dv is not None:
+            y0[:, t] += Dv[None, :, None] * x[:, t]
+    if zz is not None:
+        sg = 1.0 / (1.0 + np.exp(-zz))
+        gy0 = gy * zz * sg
+        dz = gy * y0 * sg * (1.0 + zz * (1.0 - sg))
+    else:
+        gy0, dz = gy, None
+    lam = np.zeros((Bsz, H, P, N)) if g_last is None else np.array(g_last, dtype=np.float64, copy=True)
+    dx = np.zeros_like(x)
+    ddt = np.zeros((Bsz, L, H))
+    da = np.zeros(H)
+    dB = np.zeros_like(Bm)
+    dC = np.zeros_like(Cm)
+    dD = None if Dv is None else np.zeros(H)
+    for t in range(L - 1, -1, -1):
+        g = gy0[:, t]                                                 # [B, H, P]
+        lam = lam + g[:, :, :, None] * Cm[:, t, None, None, :]
+        dC[:, t] += np.einsum("bhp,bhpn->bn", g, states[t + 1])
+        if Dv is not None:
+            dD += np.einsum("bhp,bhp->h", g, x[:, t])
+            dx[:, t] += Dv[None, :, None] * g
+        st = dt[:, t]                                                 # [B, H]
+        dx[:, t] += st[:, :, None] * np.einsum("bhpn,bn->bhp", lam, Bm[:, t])
+        dB[:, t] += np.einsum("bhpn,bh,bhp->bn", lam, st, x[:, t])
+        hprev = np.einsum("bhpn,bhpn->bh", lam, states[t])           # sum lam H_{t-1}
+        ab = abar[:, t]
+        ddt[:, t] = a[None, :] * ab * hprev + np.einsum("bhpn,bhp,bn->bh", lam, x[:, t], Bm[:, t])
+        da += np.einsum("bh,bh->h", st * ab, hprev)
+        lam = ab[:, :, None, None] * lam
+    draw = ddt * (1.0 / (1.0 + np.exp(-raw))) if delta_softplus else ddt
+    return {"dx": dx, "ddelta": draw, "dA": da, "dB": dB, "dC": dC, "dD": dD, "dz": dz, "dh0": lam,
+            "ddelta_bias": None if delta_bias is None else draw.sum(axis=(0, 1))}
+
+
+def ssd_bwd_storage(inp: dict, gy, g_last=None):
+    """``ssd_bwd`` on storage-form inputs (``synth.ssd_inputs``, one B/C group), widened
+    exactly; gy in the inputs' storage form, g_last float32 or None."""
+    dt = inp["dtype"]
+    w = lambda k: None if inp.get(k) is None else _widen(inp[k], dt)
+    f = lambda k: None if inp.get(k) is None else np.asarray(inp[k], dtype=np.float64)
+    return ssd_bwd(w("x"), w("delta"), f("A"), w("B"), w("C"), f("Dskip"), w("z"), f("h0"),
+                   inp.get("delta_softplus", False), f("delta_bias"), _widen(gy, dt),
+                   None if g_last is None else np.asarray(g_last, dtype=np.float64))

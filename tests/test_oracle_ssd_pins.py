@@ -240,3 +240,112 @@ def test_planted_group_mistake_is_caught(old, new):
     y, _ = _run(p, fn=ns["ssd"])
     yr, _ = _via_s6(_group_slice(p, 1, 2))
     assert np.max(np.abs(y[:, :, 2:4] - yr)) > 1e-6
+
+
+# ---- the backward (ssd_oracle.ssd_bwd)
+
+def _ssd_loss(p, gy, gl, softplus):
+    y, hl = _run(p, softplus=softplus)
+    return float((y * gy).sum() + (0.0 if gl is None else (hl * gl).sum()))
+
+
+def _ssd_bwd_fd_worst(fn, seed, softplus, gate, h0, bias):
+    """Largest gap between fn's gradients and central finite differences of the forward
+    oracle, element by element over every input (tiny problem)."""
+    p = _problem(seed, Bsz=2, L=6, H=2, P=3, N=4, gate=gate, softplus=softplus, bias=bias, h0=h0)
+    if bias and not softplus:   # a positive step size (a negative one grows the state without bound)
+        p["bias"] = 0.05 * np.abs(p["bias"])
+    rng = np.random.default_rng(seed + 7)
+    gy = rng.standard_normal(p["x"].shape)
+    gl = rng.standard_normal((2, 2, 3, 4))
+    g = fn(p["x"], p["delta"], p["a"], p["Bm"], p["Cm"], p["D"], p["z"], p["h0"], softplus, p["bias"], gy, gl)
+    names = {"x": "dx", "delta": "ddelta", "a": "dA", "Bm": "dB", "Cm": "dC", "D": "dD", "z": "dz", "h0": "dh0",
+             "bias": "ddelta_bias"}
+    worst = 0.0
+    for name, arr in p.items():
+        if arr is None:
+            continue
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            v = arr[idx]
+            eps = 1e-6 * max(1.0, abs(v))
+            arr[idx] = v + eps
+            lp = _ssd_loss(p, gy, gl, softplus)
+            arr[idx] = v - eps
+            lm = _ssd_loss(p, gy, gl, softplus)
+            arr[idx] = v
+            fd = (lp - lm) / (2 * eps)
+            worst = max(worst, abs(fd - g[names[name]][idx]) / max(1.0, abs(fd)))
+    return worst
+
+
+@pytest.mark.parametrize("seed,softplus,gate,h0,bias", [(40, False, True, True, False), (41, True, True, False, True),
+                                                        (42, False, False, True, True), (43, True, False, False, False)])
+def test_ssd_backward_equals_finite_differences(seed, softplus, gate, h0, bias):
+    """Every gradient of the SSD backward oracle against central differences of the SSD
+    forward oracle (pinned above on its own), element by element."""
+    assert _ssd_bwd_fd_worst(ssd_oracle.ssd_bwd, seed, softplus, gate, h0, bias) < 1e-6
+
+
+def test_ssd_backward_is_the_s6_backward_of_the_expansion():
+    """The SSD layer is the S6 scan on the H * P channels with the head's step size, decay and
+    D tied over its channels; so its gradients are the S6 oracle's (numpy, pinned on its own
+    by finite differences) on that expansion, summed over each head's channels."""
+    from oracle.numpy_ref import scan_bwd_np
+    p = _problem(44, Bsz=2, L=9, H=3, P=4, N=5, gate=True, softplus=True, bias=True, h0=True)
+    rng = np.random.default_rng(45)
+    gy = rng.standard_normal(p["x"].shape)
+    gl = rng.standard_normal((2, 3, 4, 5))
+    g = ssd_oracle.ssd_bwd(p["x"], p["delta"], p["a"], p["Bm"], p["Cm"], p["D"], p["z"], p["h0"], True, p["bias"],
+                           gy, gl)
+    Bsz, L, H, P = p["x"].shape
+    N, D = 5, H * P
+    r = scan_bwd_np(p["x"].reshape(Bsz, L, D), np.repeat(p["delta"], P, axis=2),
+                    np.repeat(p["a"], P)[:, None] * np.ones((1, N)), p["Bm"], p["Cm"], np.repeat(p["D"], P),
+                    p["z"].reshape(Bsz, L, D), p["h0"].reshape(Bsz, D, N), True, gy.reshape(Bsz, L, D),
+                    gl.reshape(Bsz, D, N), delta_bias=np.repeat(p["bias"], P))
+    np.testing.assert_allclose(g["dx"], r["dx"].reshape(Bsz, L, H, P), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dz"], r["dz"].reshape(Bsz, L, H, P), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["ddelta"], r["ddelta"].reshape(Bsz, L, H, P).sum(axis=3), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dA"], r["dA"].reshape(H, P * N).sum(axis=1), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dB"], r["dB"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dC"], r["dC"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dD"], r["dD"].reshape(H, P).sum(axis=1), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dh0"], r["dh0"].reshape(Bsz, H, P, N), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["ddelta_bias"], r["ddelta_bias"].reshape(H, P).sum(axis=1), rtol=1e-10, atol=1e-12)
+
+
+# planted mistakes in a copy of ssd_bwd: each must fail the finite-difference pin
+_SSD_BWD_MUTANTS = {
+    "readout_dropped": ("lam = lam + g[:, :, :, None] * Cm[:, t, None, None, :]", "lam = lam"),
+    "decay_term_of_dt_dropped": ("a[None, :] * ab * hprev + np.einsum", "0.0 * hprev + np.einsum"),
+    "dA_without_dt": ("np.einsum(\"bh,bh->h\", st * ab, hprev)", "np.einsum(\"bh,bh->h\", ab, hprev)"),
+    "dC_with_old_state": ("dC[:, t] += np.einsum(\"bhp,bhpn->bn\", g, states[t + 1])",
+                          "dC[:, t] += np.einsum(\"bhp,bhpn->bn\", g, states[t])"),
+    "dh0_not_decayed": ("        lam = ab[:, :, None, None] * lam\n", "        lam = lam\n"),
+    "softplus_chain_dropped": ("draw = ddt * (1.0 / (1.0 + np.exp(-raw))) if delta_softplus else ddt", "draw = ddt"),
+    "silu_prime_dropped": ("dz = gy * y0 * sg * (1.0 + zz * (1.0 - sg))", "dz = gy * y0 * sg"),
+}
+
+
+def _mutated_ssd_bwd(kind):
+    old, new = _SSD_BWD_MUTANTS[kind]
+    src = inspect.getsource(ssd_oracle.ssd_bwd)
+    assert src.count(old) == 1, kind
+    ns = dict(vars(ssd_oracle))
+    exec(src.replace(old, new), ns)
+    return ns["ssd_bwd"]
+
+
+@pytest.mark.parametrize("kind", sorted(_SSD_BWD_MUTANTS))
+def test_planted_ssd_backward_mistake_is_caught(kind):
+    fn = _mutated_ssd_bwd(kind)
+    worst = max(_ssd_bwd_fd_worst(fn, 40, False, True, True, False), _ssd_bwd_fd_worst(fn, 41, True, True, True, True))
+    assert worst > 1e-3, f"mutant {kind} passes the pin"
+
+
+def test_unmutated_ssd_backward_copy_passes():
+    ns = dict(vars(ssd_oracle))
+    exec(inspect.getsource(ssd_oracle.ssd_bwd), ns)
+    assert _ssd_bwd_fd_worst(ns["ssd_bwd"], 41, True, True, True, True) < 1e-6
