@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 #define SSM_MAX_DSTATE 256
 
 typedef enum ssm_dtype {
@@ -437,6 +437,41 @@ int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, 
                 int64_t ngroups, int dtype, const void *x, const void *delta, const float *A, const void *B,
                 const void *C, const float *Dskip, const void *z, const float *delta_bias,
                 const float *h0, float *h_last, void *y, int delta_softplus, void *stream);
+
+/* Bytes of device workspace ssm_ssd_bwd needs for this shape (0 when nothing is
+ * computed or the shape is invalid). */
+size_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                   int64_t dstate, int dtype);
+
+/*
+ * Backward pass of ssm_ssd_fwd for one B/C group: gradients of a loss with respect to
+ * every input, given dy = dLoss/dy and (optionally) dh_last = dLoss/dh_last.  The layer is
+ * the selective scan of ssm_scan_fwd over the nheads * headdim channels (pages: managen.ai
+ * Mamba2Block, brentwoodlivery "Mamba 2 and Hybrid Architectures"), with each head's step
+ * size delta[b, t, h], decay a_h, D_h and bias tied over its headdim channels and B, C
+ * shared by all heads; so the gradients are those of ssm_scan_bwd on the per-channel
+ * expansion, with the tied ones (ddelta, dA, dD, ddelta_bias) summed over each head's
+ * channels.  The call runs exactly that: fp32 copies of the expansion in the workspace,
+ * ssm_scan_bwd on them (up to 256 states: groups of 16), then the per-head sums in a fixed
+ * order (deterministic).
+ *   inputs   x, delta, A, B, C, Dskip, z, delta_bias, h0, delta_softplus: as for ssm_ssd_fwd
+ *            with ngroups == 1 (several groups: SSM_EUNSUPPORTED); dy [B, L, H, P] (dtype),
+ *            dh_last [B, H, P, N] fp32 or NULL
+ *   outputs  dx, dz [B, L, H, P] and ddelta [B, L, H] and dB, dC [B, L, N] in dtype;
+ *            dA, dD, ddelta_bias [H] and dh0 [B, H, P, N] fp32.  dD, dz, ddelta_bias are
+ *            required exactly when Dskip, z, delta_bias are given; dh0 may be NULL.
+ *   workspace device memory of ssm_ssd_bwd_workspace_bytes(...) bytes
+ * Pointers are caller-owned device memory; asynchronous on stream.  batch == 0 or seqlen == 0
+ * writes dA, dD, ddelta_bias as zeros and (seqlen == 0) dh0 = dh_last or zeros.
+ * Not tuned: it costs ceil(N / 16) scan backwards over the H * P channels plus the copies;
+ * a reverse kernel on the matrix cores would be the fast form.
+ */
+int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int64_t ngroups, int dtype, const void *x, const void *delta, const float *A, const void *B,
+                const void *C, const float *Dskip, const void *z, const float *delta_bias,
+                const float *h0, const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
+                void *dB, void *dC, float *dD, void *dz, float *ddelta_bias, float *dh0,
+                int delta_softplus, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ssm.h")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 6     # SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 7     # SSM_ABI_VERSION of include/ssm.h
 
 
 class SSMError(RuntimeError):
@@ -110,6 +110,10 @@ def lib():
     L.ssm_conv1d_fwd.argtypes = [I64, I64, I64, I64, I32, P, P, P, P, P, P, I32, P]
     L.ssm_ssd_fwd.restype = I32
     L.ssm_ssd_fwd.argtypes = [I64, I64, I64, I64, I64, I64, I32] + [P] * 11 + [I32, P]
+    L.ssm_ssd_bwd_workspace_bytes.restype = SZ
+    L.ssm_ssd_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I32]
+    L.ssm_ssd_bwd.restype = I32
+    L.ssm_ssd_bwd.argtypes = [I64, I64, I64, I64, I64, I64, I32] + [P] * 20 + [I32, P, SZ, P]
     L.ssm_conv1d_update.restype = I32
     L.ssm_conv1d_update.argtypes = [I64, I64, I64, I32, P, P, P, P, P, I32, P]
     L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
@@ -659,3 +663,52 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
                            int(bool(delta_softplus)), ctypes.c_void_p(s.cuda_stream))
     _check(st, "ssm_ssd_fwd")
     return (out, h_last) if return_last_state else out
+
+
+def ssd_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, *, delta_softplus=False,
+            delta_bias=None, workspace=None, stream=None):
+    """Gradients of a loss through ssd_fwd (one B/C group: B, C [B, L, N]), given dy =
+    dLoss/dy [B, L, H, P] (x's dtype) and optionally dh_last = dLoss/dh_last [B, H, P, N] fp32.
+
+    Returns a dict: dx, dz (None without z) [B, L, H, P] and ddelta [B, L, H] and dB, dC
+    [B, L, N] in x's dtype; dA, dD (None without D), ddelta_bias (None without a bias) [H] and
+    dh0 [B, H, P, N] in fp32.
+    """
+    import torch
+    if x.dim() != 4 or A.dim() != 1:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim] and A [nheads]")
+    if B.dim() != 3:
+        raise ValueError("ssd_bwd takes one B/C group: B and C [batch, seqlen, dstate]")
+    Bsz, L, H, P = x.shape
+    N = B.shape[-1]
+    dev, dt = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("ssd_bwd runs on the GPU only; tensors must be on a cuda device")
+    if dy is None:
+        raise ValueError("dy is required")
+    for t, name, shape, tdt in ((delta, "delta", (Bsz, L, H), dt), (z, "z", (Bsz, L, H, P), dt),
+                                (B, "B", (Bsz, L, N), dt), (C, "C", (Bsz, L, N), dt), (A, "A", (H,), torch.float32),
+                                (D, "D", (H,), torch.float32), (delta_bias, "delta_bias", (H,), torch.float32),
+                                (h0, "h0", (Bsz, H, P, N), torch.float32), (dy, "dy", (Bsz, L, H, P), dt),
+                                (dh_last, "dh_last", (Bsz, H, P, N), torch.float32)):
+        _need(t, name, shape, tdt, dev)
+    code = _dtype_code(x)
+    f32 = torch.float32
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty((Bsz, L, H), dtype=dt, device=dev),
+           "dz": torch.empty_like(x) if z is not None else None,
+           "dB": torch.empty((Bsz, L, N), dtype=dt, device=dev), "dC": torch.empty((Bsz, L, N), dtype=dt, device=dev),
+           "dA": torch.empty((H,), dtype=f32, device=dev),
+           "dD": torch.empty((H,), dtype=f32, device=dev) if D is not None else None,
+           "ddelta_bias": torch.empty((H,), dtype=f32, device=dev) if delta_bias is not None else None,
+           "dh0": torch.empty((Bsz, H, P, N), dtype=f32, device=dev)}
+    ws_bytes = int(lib().ssm_ssd_bwd_workspace_bytes(Bsz, L, H, P, N, code))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib().ssm_ssd_bwd(Bsz, L, H, P, N, 1, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["dx"]),
+                           _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                           _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), int(bool(delta_softplus)),
+                           _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(s.cuda_stream))
+    _check(st, "ssm_ssd_bwd")
+    return out

@@ -612,6 +612,44 @@ hipError_t gunpad3(void *dst, size_t eo, const void *src, size_t ei, int64_t n0,
     return launch_status(s);
 }
 
+// dst[i] = src[i / R] (converted to fp32), i < n * R
+template <typename Ei>
+__global__ void __launch_bounds__(256) repeat_kernel(float *dst, const Ei *src, int64_t n, int64_t R) {
+    const int64_t total = n * R;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        dst[i] = widen(src, i / R);
+}
+
+// dst[i] = sum of src[i * S .. i * S + S - 1] in that order (converted to Eo), i < n
+template <typename Eo>
+__global__ void __launch_bounds__(256) segsum_kernel(Eo *dst, const float *src, int64_t n, int64_t S) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        float acc = 0.0f;
+        for (int64_t j = 0; j < S; ++j) acc += src[i * S + j];
+        put(dst, i, acc);
+    }
+}
+
+hipError_t repeat_f32(float *dst, const void *src, size_t ei, int64_t n, int64_t R, hipStream_t s) {
+    const dim3 g = grid_for(n * R);
+    if (ei == 2)
+        hipLaunchKernelGGL(repeat_kernel<uint16_t>, g, dim3(256), 0, s, dst, static_cast<const uint16_t *>(src), n, R);
+    else
+        hipLaunchKernelGGL(repeat_kernel<float>, g, dim3(256), 0, s, dst, static_cast<const float *>(src), n, R);
+    return launch_status(s);
+}
+
+hipError_t segsum(void *dst, size_t eo, const float *src, int64_t n, int64_t S, hipStream_t s) {
+    const dim3 g = grid_for(n);
+    if (eo == 2)
+        hipLaunchKernelGGL(segsum_kernel<uint16_t>, g, dim3(256), 0, s, static_cast<uint16_t *>(dst), src, n, S);
+    else
+        hipLaunchKernelGGL(segsum_kernel<float>, g, dim3(256), 0, s, static_cast<float *>(dst), src, n, S);
+    return launch_status(s);
+}
+
 hipError_t add_f32(float *dst, const float *src, int64_t n, hipStream_t s) {
     hipLaunchKernelGGL(add_kernel, grid_for(n), dim3(256), 0, s, dst, src, n);
     return launch_status(s);
@@ -950,4 +988,128 @@ extern "C" int ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     a.softplus = delta_softplus;
     hipError_t e = launch_ssd(a, s);
     return e == hipSuccess ? SSM_OK : hip_fail("ssd launch", e);
+}
+
+namespace ssm {
+namespace {
+// Workspace of ssm_ssd_bwd: fp32 per-channel copies of the inputs (tokens over the H * P
+// channels, each head's step size, decay, D and bias repeated over its channels), the
+// per-channel gradients of the scan backward, then that backward's own workspace.
+enum SsdBwdBuf { kQX, kQDelta, kQZ, kQDy, kQB, kQC, kQA, kQD, kQBias,
+                 kQDx, kQDdelta, kQDz, kQDB, kQDC, kQDA, kQDD, kQDBias, kQInner, kQBufs };
+
+size_t ssd_bwd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                      size_t off[kQBufs]) {
+    const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen);
+    const size_t Dc = static_cast<size_t>(nheads * headdim), N = static_cast<size_t>(dstate), f = sizeof(float);
+    const size_t tok = B * L * Dc * f, bc = B * L * N * f;
+    const size_t bytes[kQInner] = {tok, tok, tok, tok, bc, bc, Dc * N * f, Dc * f, Dc * f,
+                                   tok, tok, tok, bc, bc, Dc * N * f, Dc * f, Dc * f};
+    size_t ws = 0;
+    for (int i = 0; i < kQInner; ++i) {
+        off[i] = ws;
+        ws = (ws + bytes[i] + kWsAlign - 1) / kWsAlign * kWsAlign;
+    }
+    off[kQInner] = ws;
+    return ws + ssm_scan_bwd_workspace_bytes(batch, seqlen, nheads * headdim, dstate, SSM_DTYPE_F32, 0);
+}
+}  // namespace
+}  // namespace ssm
+
+extern "C" size_t ssm_ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                              int64_t dstate, int dtype) {
+    using namespace ssm;
+    if ((dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16) || batch <= 0 || seqlen <= 0 || nheads <= 0 ||
+        headdim < 1 || dstate < 1 || dstate > SSM_MAX_DSTATE)
+        return 0;
+    size_t off[kQBufs];
+    return ssd_bwd_layout(batch, seqlen, nheads, headdim, dstate, off);
+}
+
+extern "C" int ssm_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                           int64_t ngroups, int dtype, const void *x, const void *delta, const float *A, const void *B,
+                           const void *C, const float *Dskip, const void *z, const float *delta_bias,
+                           const float *h0, const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
+                           void *dB, void *dC, float *dD, void *dz, float *ddelta_bias, float *dh0,
+                           int delta_softplus, void *workspace, size_t workspace_bytes, void *stream) {
+    using namespace ssm;
+    clear_error();
+    int st = check_ssd(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, x, delta, A, B, C, Dskip, z,
+                       delta_bias, h0, nullptr, dx, delta_softplus);
+    if (st != SSM_OK) return st;
+    if (ngroups != 1) {
+        set_error("ssm_ssd_bwd takes one B/C group (got ngroups=%lld)", (long long)ngroups);
+        return SSM_EUNSUPPORTED;
+    }
+    const bool any = batch > 0 && seqlen > 0 && nheads > 0;
+    if (any && (!dy || !dx || !ddelta || !dA || !dB || !dC)) {
+        set_error("dy, dx, ddelta, dA, dB and dC are required");
+        return SSM_EINVAL;
+    }
+    if ((Dskip && !dD) || (z && !dz) || (delta_bias && !ddelta_bias)) {
+        set_error("dD, dz and ddelta_bias are required with D, z and delta_bias");
+        return SSM_EINVAL;
+    }
+    if (nheads == 0) return SSM_OK;
+    size_t off[kQBufs];
+    const size_t need = ssd_bwd_layout(batch, seqlen, nheads, headdim, dstate, off);
+    if (any && (!workspace || workspace_bytes < need)) {
+        set_error("workspace of %zu bytes is too small (need %zu)", workspace_bytes, need);
+        return SSM_EWORKSPACE;
+    }
+    log_call("ssd_bwd B=%lld L=%lld H=%lld P=%lld N=%lld dtype=%d: the scan backward on the %lld channels "
+             "(fp32 copies), tied gradients summed per head", (long long)batch, (long long)seqlen,
+             (long long)nheads, (long long)headdim, (long long)dstate, dtype, (long long)(nheads * headdim));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t Dc = nheads * headdim, P = headdim, N = dstate, BL = batch * seqlen;
+    const size_t es = dtype_size(dtype);
+    char *ws = static_cast<char *>(workspace);
+    auto q = [&](int i) { return reinterpret_cast<float *>(ws + off[i]); };
+    hipError_t e = hipSuccess;
+    if (!any) {
+        // no rows or no steps: the per-head gradients are zero, dh0 = dh_last (or zeros)
+        auto fill = [&](float *d, const float *src, int64_t n) {
+            if (!d || n <= 0) return hipSuccess;
+            hipLaunchKernelGGL(fill_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, d,
+                               src, n);
+            return launch_status(s);
+        };
+        e = fill(dA, nullptr, nheads);
+        if (e == hipSuccess && Dskip) e = fill(dD, nullptr, nheads);
+        if (e == hipSuccess && delta_bias) e = fill(ddelta_bias, nullptr, nheads);
+        if (e == hipSuccess && batch > 0) e = fill(dh0, dh_last, batch * Dc * N);
+        return e == hipSuccess ? SSM_OK : hip_fail("fill_state launch", e);
+    }
+    // the per-channel expansion (fp32): tokens converted, each head's values repeated
+    e = gpad3(q(kQX), 4, x, es, BL, 1, Dc, 0, 1, Dc, 0.0f, s);
+    if (e == hipSuccess) e = repeat_f32(q(kQDelta), delta, es, BL * nheads, P, s);
+    if (e == hipSuccess && z) e = gpad3(q(kQZ), 4, z, es, BL, 1, Dc, 0, 1, Dc, 0.0f, s);
+    if (e == hipSuccess) e = gpad3(q(kQDy), 4, dy, es, BL, 1, Dc, 0, 1, Dc, 0.0f, s);
+    if (e == hipSuccess) e = gpad3(q(kQB), 4, B, es, BL, 1, N, 0, 1, N, 0.0f, s);
+    if (e == hipSuccess) e = gpad3(q(kQC), 4, C, es, BL, 1, N, 0, 1, N, 0.0f, s);
+    if (e == hipSuccess) e = repeat_f32(q(kQA), A, 4, nheads, P * N, s);
+    if (e == hipSuccess && Dskip) e = repeat_f32(q(kQD), Dskip, 4, nheads, P, s);
+    if (e == hipSuccess && delta_bias) e = repeat_f32(q(kQBias), delta_bias, 4, nheads, P, s);
+    if (e != hipSuccess) return hip_fail("ssd_bwd expansion launch", e);
+    // the scan backward over the H * P channels (the Mamba discretisation: A_bar = exp(dt a_h),
+    // B_bar = dt B), every input in fp32
+    st = ssm_scan_bwd(batch, seqlen, Dc, N, SSM_DTYPE_F32, q(kQX), q(kQDelta), q(kQA), q(kQB), q(kQC),
+                      Dskip ? q(kQD) : nullptr, z ? q(kQZ) : nullptr, h0, q(kQDy), dh_last, q(kQDx), q(kQDdelta),
+                      q(kQDA), q(kQDB), q(kQDC), Dskip ? q(kQDD) : nullptr, z ? q(kQDz) : nullptr, dh0,
+                      delta_softplus, SSM_DISC_MAMBA, delta_bias ? q(kQBias) : nullptr,
+                      delta_bias ? q(kQDBias) : nullptr, nullptr, ws + off[kQInner], workspace_bytes - off[kQInner],
+                      stream);
+    if (st != SSM_OK) return st;
+    // back to the layer's shapes: per-channel gradients converted, the tied ones summed over
+    // each head's channels (in a fixed order)
+    e = gunpad3(dx, es, q(kQDx), 4, BL, 1, Dc, 0, 1, Dc, s);
+    if (e == hipSuccess && z) e = gunpad3(dz, es, q(kQDz), 4, BL, 1, Dc, 0, 1, Dc, s);
+    if (e == hipSuccess) e = gunpad3(dB, es, q(kQDB), 4, BL, 1, N, 0, 1, N, s);
+    if (e == hipSuccess) e = gunpad3(dC, es, q(kQDC), 4, BL, 1, N, 0, 1, N, s);
+    if (e == hipSuccess) e = segsum(ddelta, es, q(kQDdelta), BL * nheads, P, s);
+    if (e == hipSuccess) e = segsum(dA, 4, q(kQDA), nheads, P * N, s);
+    if (e == hipSuccess && Dskip) e = segsum(dD, 4, q(kQDD), nheads, P, s);
+    if (e == hipSuccess && delta_bias) e = segsum(ddelta_bias, 4, q(kQDBias), nheads, P, s);
+    if (e != hipSuccess) return hip_fail("ssd_bwd reduction launch", e);
+    return SSM_OK;
 }
