@@ -744,7 +744,34 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
           _host(t["C"][:1]), _host(t["D"][:8]), _host(t["z"][:1, :, :8]))
     deferred.append((out["ssd"], lambda a_=a_: ssd_oracle.ssd(*a_), 8 * c["seqlen"] * c["headdim"] * c["dstate"],
                      "state-updates/s", "8 heads of one batch row x 4096 steps, fp64 numpy oracle (one thread)", 1))
-    del t
+    # --- its backward (ssm_ssd_bwd: the scan backward on the per-channel expansion) ---
+    gys = _randn(tuple(t["x"].shape), gen, dev, bf)
+    sws = torch.empty(ssm.ssd_bwd_workspace_bytes(*t["x"].shape, c["dstate"], "bf16"), dtype=torch.uint8, device=dev)
+
+    def ssd_b():
+        ssm.ssd_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, gys, workspace=sws)
+
+    settle_calls(torch, ssd_b)
+    sbt = time_calls(torch, ssd_b, 3)
+    sbms = sbt[len(sbt) // 2]
+    upd = c["batch"] * c["seqlen"] * c["nheads"] * c["headdim"] * c["dstate"]
+    out["ssd_backward"] = {
+        "workload": "Mamba-2 layer SSD scan B4 L4096 H64 P64 N128 bf16 gated, backward (dx, ddelta, dA, dB, dC, dD, dz)",
+        "ms_median": round(sbms, 3), "state_updates_per_s": upd / (sbms * 1e-3),
+        "timing": "median of 3 calls queued back to back, each between two events",
+        "workspace_bytes": sws.numel(),
+        "note": "not tuned: the scan backward over the 4096 channels on fp32 copies, 8 groups of 16 states, "
+                "then the per-head sums",
+    }
+    log(f"ssd backward: {sbms:.2f} ms/call ({upd / (sbms * 1e-3):.3e} state-updates/s)")
+    a_ = tuple(None if v is None else _host(v) for v in (t["x"][:1, :, :2], t["delta"][:1, :, :2], t["A"][:2],
+                                                       t["B"][:1], t["C"][:1], t["D"][:2], t["z"][:1, :, :2]))
+    gy_ = _host(gys[:1, :, :2])
+    deferred.append((out["ssd_backward"],
+                     lambda a_=a_, gy_=gy_: ssd_oracle.ssd_bwd(*a_, None, False, None, gy_, None),
+                     2 * c["seqlen"] * c["headdim"] * c["dstate"], "state-updates/s",
+                     "2 heads of one batch row x 4096 steps, fp64 numpy oracle (one thread)", 1))
+    del t, gys, sws
     torch.cuda.empty_cache()
     # --- causal conv1d + SiLU at the headline shape (HBM-bound) ---
     x, w, bias = _conv_inputs(torch, synth, dev)

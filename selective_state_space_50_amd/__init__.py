@@ -665,6 +665,12 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_softplus=False,
     return (out, h_last) if return_last_state else out
 
 
+def ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, dtype="bf16") -> int:
+    """Device workspace bytes of ssd_bwd for this shape (0: nothing to compute)."""
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    return int(lib().ssm_ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, code))
+
+
 def ssd_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, *, delta_softplus=False,
             delta_bias=None, workspace=None, stream=None):
     """Gradients of a loss through ssd_fwd (one B/C group: B, C [B, L, N]), given dy =
