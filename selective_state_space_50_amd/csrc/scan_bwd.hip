@@ -167,6 +167,13 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
     T pd, px, pg, pz = T{};
     float bcn = 0.0f;                     // next block's B or C element (tid < 256)
     float2 ckn;                           // next block's checkpoint
+    // fp32 outputs with accum set (sums over groups of states): the sums that step w of the
+    // next block adds to, requested with its inputs
+    constexpr bool ACC = std::is_same_v<T, float>;
+    const bool acc = ACC && a.accum;
+    float *const SX = static_cast<float *>(a.dx) + base, *const SD = static_cast<float *>(a.ddelta) + base;
+    float *const SZ = HAS_Z ? static_cast<float *>(a.dz) + base : nullptr;
+    float ox = 0.0f, od = 0.0f, oz = 0.0f;
     auto load2 = [&](int64_t k) __attribute__((always_inline)) {
         ckn = make_float2(ck[k * kN * D], ck[(k * kN + 1) * D]);
         const int64_t r = row(k, w);
@@ -175,6 +182,13 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         pg = GY[r];
         if constexpr (HAS_Z) pz = Z[r];
         if (tid < 256) bcn = bc_elem(k, tid < 128 ? Bm : Cm);
+        if constexpr (ACC) {
+            if (acc) {
+                ox = SX[r];
+                od = SD[r];
+                if constexpr (HAS_Z) oz = SZ[r];
+            }
+        }
     };
     auto block2 = [&](int64_t k, auto full) __attribute__((always_inline)) {
         constexpr bool F = decltype(full)::value;
@@ -189,6 +203,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
         const float xv_w = widen_v(px);
         const float gy_w = widen_v(pg);
         const float zv_w = HAS_Z ? widen_v(pz) : 0.0f;
+        const float ox_w = ox, od_w = od, oz_w = oz;   // the sums this step adds to (acc)
         sP[pb][w][lane] = make_float4(dt_w, dt_w * xv_w, HAS_Z ? gy_w * silu_f(zv_w) : gy_w, xv_w);
         __syncthreads();
         // us: dt x (Mamba) or x; fs: f (zero-order hold) or r (bilinear)
@@ -354,16 +369,16 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(BwdArgs a) {
                 if constexpr (HAS_Z) {
                     const float sg = sigmoid_f(zv);
                     g0 = gy * (zv * sg);
-                    put(static_cast<T *>(a.dz) + b * L * D, t * D + d,
-                        gy * y0 * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f)));
+                    const float vz = gy * y0 * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f));
+                    put(static_cast<T *>(a.dz) + b * L * D, t * D + d, acc ? oz_w + vz : vz);
                 }
                 gDp = __builtin_fmaf(g0, xv, gDp);
                 float gdt = __builtin_fmaf(xv, DISC == kMamba ? S3 : S2, S1);
                 if (a.softplus) gdt *= sigmoid_f(raw);
                 gBp += gdt;
-                put(static_cast<T *>(a.ddelta) + b * L * D, t * D + d, gdt);
-                put(static_cast<T *>(a.dx) + b * L * D, t * D + d,
-                    DISC == kMamba ? __builtin_fmaf(dt, S3, dsk * g0) : __builtin_fmaf(dsk, g0, S3));
+                put(static_cast<T *>(a.ddelta) + b * L * D, t * D + d, acc ? od_w + gdt : gdt);
+                const float vx = DISC == kMamba ? __builtin_fmaf(dt, S3, dsk * g0) : __builtin_fmaf(dsk, g0, S3);
+                put(static_cast<T *>(a.dx) + b * L * D, t * D + d, acc ? ox_w + vx : vx);
             }
         }
     };

@@ -428,7 +428,8 @@ int bwd_native(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int d
                const void *dy, const float *dh_last, void *dx, void *ddelta, float *dA,
                void *dB, void *dC, float *dD, void *dz, float *dh0, int delta_softplus,
                int discretization, const float *delta_bias, float *ddelta_bias,
-               const float *checkpoints, void *workspace, const BwdPlan &p, hipStream_t s) {
+               const float *checkpoints, void *workspace, const BwdPlan &p, hipStream_t s,
+               int accum = 0) {
     hipError_t e;
     char *ws = static_cast<char *>(workspace);
     const bool bf16 = dtype == SSM_DTYPE_BF16;
@@ -489,6 +490,7 @@ int bwd_native(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int d
     a.partDB = reinterpret_cast<float *>(ws + p.partDB_off);
     a.lc_P = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcP_off) : nullptr;
     a.lc_H = p.n_chunks > 1 ? reinterpret_cast<float *>(ws + p.lcH_off) : nullptr;
+    a.accum = accum;
     e = launch_scan_bwd(a, discretization, bf16, z != nullptr, s);
     return e == hipSuccess ? SSM_OK : hip_fail("scan backward launch", e);
 }
@@ -621,14 +623,18 @@ __global__ void __launch_bounds__(256) repeat_kernel(float *dst, const Ei *src, 
         dst[i] = widen(src, i / R);
 }
 
-// dst[i] = sum of src[i * S .. i * S + S - 1] in that order (converted to Eo), i < n
+// dst[i] = sum of src[i * S .. i * S + S - 1] (converted to Eo), i < n: one wavefront per
+// output (i is wave-uniform), lane j adding elements j, j + 64, ... in order, then a fixed
+// butterfly over the lanes, lane 0's result stored (the same order on every call)
 template <typename Eo>
 __global__ void __launch_bounds__(256) segsum_kernel(Eo *dst, const float *src, int64_t n, int64_t S) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); i < n;
+         i += static_cast<int64_t>(gridDim.x) * 4) {
         float acc = 0.0f;
-        for (int64_t j = 0; j < S; ++j) acc += src[i * S + j];
-        put(dst, i, acc);
+        for (int64_t j = lane; j < S; j += 64) acc += src[i * S + j];
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if (lane == 0) put(dst, i, acc);
     }
 }
 
@@ -642,7 +648,7 @@ hipError_t repeat_f32(float *dst, const void *src, size_t ei, int64_t n, int64_t
 }
 
 hipError_t segsum(void *dst, size_t eo, const float *src, int64_t n, int64_t S, hipStream_t s) {
-    const dim3 g = grid_for(n);
+    const dim3 g = grid_for(n * 64);   // four outputs per 256-thread block
     if (eo == 2)
         hipLaunchKernelGGL(segsum_kernel<uint16_t>, g, dim3(256), 0, s, static_cast<uint16_t *>(dst), src, n, S);
     else
@@ -722,11 +728,16 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
         const int64_t BL = batch * seqlen, Dp = p.Dp, N = dstate;
         auto at = [&](int i) { return static_cast<void *>(ws + p.pad_off[i]); };
         auto atf = [&](int i) { return reinterpret_cast<float *>(ws + p.pad_off[i]); };
+        // fp32 tokens that need no padding are read in place, and the per-channel gradients
+        // are summed straight into the caller's outputs (which overlap no input)
+        const bool direct = p.direct;
+        const void *tx = direct ? x : at(kPX), *tdl = direct ? delta : at(kPDelta);
+        const void *tz = direct ? z : at(kPZ), *tdy = direct ? dy : at(kPDy);
         struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; } toks[] = {
-            {at(kPX), x, BL, 1, dim, 1, Dp, es},
-            {at(kPDelta), delta, BL, 1, dim, 1, Dp, es},
-            {at(kPZ), z, BL, 1, dim, 1, Dp, es},
-            {at(kPDy), dy, BL, 1, dim, 1, Dp, es},
+            {at(kPX), direct ? nullptr : x, BL, 1, dim, 1, Dp, es},
+            {at(kPDelta), direct ? nullptr : delta, BL, 1, dim, 1, Dp, es},
+            {at(kPZ), direct ? nullptr : z, BL, 1, dim, 1, Dp, es},
+            {at(kPDy), direct ? nullptr : dy, BL, 1, dim, 1, Dp, es},
             {at(kPDskip), Dskip, 1, 1, dim, 1, Dp, 4},
             {at(kPBias), delta_bias, 1, 1, dim, 1, Dp, 4},
         };
@@ -749,24 +760,24 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
                 e = gpad3(c.dst, 4, c.src, c.es, c.n0, c.n1, c.n2, c0, c.m1, c.m2, c.fill, s);
                 if (e != hipSuccess) return hip_fail("pad launch", e);
             }
-            // group 0 writes the per-channel gradients straight into their sums
+            // the per-channel gradients go straight into their sums: group 0 stores them, the
+            // later groups' kernels add theirs to what the sums hold; the bias's gradient (a
+            // reduction over rows and steps) is added after each later group
             const bool g0 = g == 0;
-            float *gdx = g0 ? atf(kSDx) : atf(kPDx), *gdd = g0 ? atf(kSDdelta) : atf(kPDdelta);
-            float *gdz = g0 ? atf(kSDz) : atf(kPDz), *gdb = g0 ? atf(kSDBias) : atf(kPDBias);
-            st = bwd_native(batch, seqlen, Dp, 16, SSM_DTYPE_F32, at(kPX), at(kPDelta), atf(kPA), at(kPB), at(kPC),
-                            (g0 && Dskip) ? atf(kPDskip) : nullptr, z ? at(kPZ) : nullptr,
-                            h0 ? atf(kPH0) : nullptr, at(kPDy), dh_last ? atf(kPDhLast) : nullptr, gdx, gdd,
+            float *gdx = direct ? static_cast<float *>(dx) : atf(kSDx);
+            float *gdd = direct ? static_cast<float *>(ddelta) : atf(kSDdelta);
+            float *gdz = direct ? static_cast<float *>(dz) : atf(kSDz);
+            float *gdb = g0 ? atf(kSDBias) : atf(kPDBias);
+            st = bwd_native(batch, seqlen, Dp, 16, SSM_DTYPE_F32, tx, tdl, atf(kPA), at(kPB), at(kPC),
+                            (g0 && Dskip) ? atf(kPDskip) : nullptr, z ? tz : nullptr,
+                            h0 ? atf(kPH0) : nullptr, tdy, dh_last ? atf(kPDhLast) : nullptr, gdx, gdd,
                             atf(kPDA), at(kPDB), at(kPDC), (g0 && Dskip) ? atf(kPDD) : nullptr,
                             z ? static_cast<void *>(gdz) : nullptr, dh0 ? atf(kPDh0) : nullptr, delta_softplus,
                             discretization, delta_bias ? atf(kPBias) : nullptr, delta_bias ? gdb : nullptr,
-                            nullptr, ws + p.inner_off, in, s);
+                            nullptr, ws + p.inner_off, in, s, g0 ? 0 : 1);
             if (st != SSM_OK) return st;
-            if (!g0) {
-                const int64_t nt = BL * Dp;
-                e = add_f32(atf(kSDx), gdx, nt, s);
-                if (e == hipSuccess) e = add_f32(atf(kSDdelta), gdd, nt, s);
-                if (e == hipSuccess && z) e = add_f32(atf(kSDz), gdz, nt, s);
-                if (e == hipSuccess && delta_bias) e = add_f32(atf(kSDBias), gdb, Dp, s);
+            if (!g0 && delta_bias) {
+                e = add_f32(atf(kSDBias), gdb, Dp, s);
                 if (e != hipSuccess) return hip_fail("sum launch", e);
             }
             // this group's columns of the per-state gradients
@@ -783,9 +794,9 @@ extern "C" int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t 
             }
         }
         struct { void *dst; const void *src; int64_t n0, n1, n2, m1, m2; size_t es; } outs[] = {
-            {dx, at(kSDx), BL, 1, dim, 1, Dp, es},
-            {ddelta, at(kSDdelta), BL, 1, dim, 1, Dp, es},
-            {z ? dz : nullptr, at(kSDz), BL, 1, dim, 1, Dp, es},
+            {direct ? nullptr : dx, at(kSDx), BL, 1, dim, 1, Dp, es},
+            {direct ? nullptr : ddelta, at(kSDdelta), BL, 1, dim, 1, Dp, es},
+            {(z && !direct) ? dz : nullptr, at(kSDz), BL, 1, dim, 1, Dp, es},
             {Dskip ? dD : nullptr, at(kPDD), 1, 1, dim, 1, Dp, 4},
             {delta_bias ? ddelta_bias : nullptr, at(kSDBias), 1, 1, dim, 1, Dp, 4},
         };

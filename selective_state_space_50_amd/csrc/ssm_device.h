@@ -88,6 +88,7 @@ struct BwdArgs {
     const float *dbias;   // [D] added to delta before the softplus, or null
     float *ddbias;        // [D] gradient of dbias (written when dbias is given)
     float *partDB;        // [n_chunks][B][8][D] per-(chunk, row, wave) shares of ddbias
+    int accum = 0;        // fp32 dx, ddelta, dz: add to what the destination holds
 };
 
 struct SsdArgs {

@@ -414,10 +414,14 @@ int plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
         const size_t B = static_cast<size_t>(batch), L = static_cast<size_t>(seqlen);
         const size_t Dp = static_cast<size_t>(p.Dp), es = dtype_size(gdt);
         const size_t tok = B * L * Dp * es, bc = B * L * 16 * es, st16 = B * Dp * 16 * sizeof(float);
-        const size_t sum = p.K > 1 ? B * L * Dp * sizeof(float) : 0;
-        const size_t bytes[kPadBufs] = {tok, tok, tok, tok, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
+        // with several groups the token gradients go straight into the sums (no per-group copy);
+        // fp32 tokens that need no padding are read in place and summed into the outputs
+        p.direct = p.K > 1 && dtype == SSM_DTYPE_F32 && p.Dp == dim;
+        const size_t tok_in = p.direct ? 0 : tok, tok_out = p.K > 1 ? 0 : tok;
+        const size_t sum = (p.K > 1 && !p.direct) ? B * L * Dp * sizeof(float) : 0;
+        const size_t bytes[kPadBufs] = {tok_in, tok_in, tok_in, tok_in, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
                                         Dp * sizeof(float), st16, st16,
-                                        tok, tok, tok, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
+                                        tok_out, tok_out, tok_out, bc, bc, Dp * 16 * sizeof(float), Dp * sizeof(float),
                                         Dp * sizeof(float), st16,
                                         sum, sum, sum, p.K > 1 ? Dp * sizeof(float) : 0};
         size_t ws = 0;

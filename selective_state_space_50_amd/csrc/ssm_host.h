@@ -108,6 +108,9 @@ struct BwdPlan {
     // per-channel gradients (dx, ddelta, dz, the bias's) are sums over the groups, D enters
     // in group 0 only.  K == 1 is the padded path above, on copies of the input dtype.
     int64_t K = 1;
+    // K > 1 with fp32 tokens of a width that needs no padding: the tokens are read in place and
+    // the per-channel gradients summed straight into the caller's outputs (no token copies)
+    bool direct = false;
     size_t pad_off[kPadBufs] = {};
     size_t inner_off = 0;
 };
