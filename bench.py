@@ -144,6 +144,8 @@ def main():
                     help="only run this many backward calls at the headline shape (for rocprofv3)")
     ap.add_argument("--profile-ssd", type=int, default=0, metavar="CALLS",
                     help="only run this many SSD (Mamba-2 layer) scans (for rocprofv3)")
+    ap.add_argument("--profile-ssd-bwd", type=int, default=0, metavar="CALLS",
+                    help="only run this many SSD backward calls (for rocprofv3)")
     ap.add_argument("--profile-long", type=int, default=0, metavar="CALLS",
                     help="only run this many million-token scans (B1 L1048576 D1024 N16 bf16; for rocprofv3)")
     ap.add_argument("--profile-decode-graph", type=int, default=0, metavar="REPLAYS",
@@ -228,6 +230,18 @@ def main():
             ssm.ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], out=t["y"])
         torch.cuda.synchronize()
         log(f"ssd profile run: {args.profile_ssd} calls")
+        return
+    if args.profile_ssd_bwd:
+        t = _ssd_inputs(torch, dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(6)
+        gys = _randn(tuple(t["x"].shape), gen, dev, torch.bfloat16)
+        sws = torch.empty(ssm.ssd_bwd_workspace_bytes(*t["x"].shape, t["B"].shape[-1], "bf16"), dtype=torch.uint8,
+                          device=dev)
+        for _ in range(args.profile_ssd_bwd):
+            ssm.ssd_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], None, gys, workspace=sws)
+        torch.cuda.synchronize()
+        log(f"ssd backward profile run: {args.profile_ssd_bwd} calls")
         return
     if args.profile_conv:
         x, w, bias = _conv_inputs(torch, synth, dev)
@@ -760,8 +774,8 @@ def secondary(torch, ssm, synth, dev, log, src_hash, sm):
         "ms_median": round(sbms, 3), "state_updates_per_s": upd / (sbms * 1e-3),
         "timing": "median of 3 calls queued back to back, each between two events",
         "workspace_bytes": sws.numel(),
-        "note": "not tuned: the scan backward over the 4096 channels on fp32 copies, 8 groups of 16 states, "
-                "then the per-head sums",
+        "note": "the scan backward over the 4096 channels of the per-channel expansion (fp32), 8 groups of "
+                "16 states summed in the sweep kernel, then the per-head sums",
     }
     log(f"ssd backward: {sbms:.2f} ms/call ({upd / (sbms * 1e-3):.3e} state-updates/s)")
     a_ = tuple(None if v is None else _host(v) for v in (t["x"][:1, :, :2], t["delta"][:1, :, :2], t["A"][:2],
