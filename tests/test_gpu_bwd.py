@@ -167,6 +167,36 @@ def test_backward_more_than_16_states(ssm, Bsz, L, D, N, dt, disc, gate, h0, dhl
     _check(g, ref, dt, f"{N} states {Bsz}x{L}x{D} {dt} {disc} gate={gate} softplus={sp} bias={bias}")
 
 
+MANY_STATES_CHUNKED = [
+    # B, L, D, N, dtype, discretisation, gate, h0, dh_last, softplus, bias: more than 16 states
+    # over few channels, so every group's sweep is cut into chunks as well (fp32 with a width
+    # of 64: tokens read in place and each chunk's blocks adding into the caller's outputs)
+    (2, 3000, 64, 32, "f32", "mamba", True, True, True, False, True),
+    (1, 3300, 96, 24, "bf16", "zoh", True, False, True, True, False),
+]
+
+
+@pytest.mark.parametrize("Bsz,L,D,N,dt,disc,gate,h0,dhl,sp,bias", MANY_STATES_CHUNKED)
+def test_backward_more_than_16_states_chunked(ssm, Bsz, L, D, N, dt, disc, gate, h0, dhl, sp, bias):
+    """Groups of 16 states with chunked sweeps: the later groups' sums over chunk boundaries
+    and partial last blocks; every output against the oracle."""
+    seed = 700 + L + D + N
+    inp = synth.scan_inputs(Bsz, L, D, N, dt, seed=seed, gate=gate, d_kind="normal", a_kind="random",
+                            softplus_input=sp, h0=h0)
+    inp["discretization"] = disc
+    if bias:
+        b = synth.make_delta_bias(seed, D)
+        inp["delta_bias"] = b if sp else (0.05 * np.abs(b)).astype(np.float32)
+    r = np.random.default_rng(seed + 1000)
+    gy = synth.store(r.standard_normal((Bsz, L, D)).astype(np.float32), dt)
+    gl = r.standard_normal((Bsz, D, N)).astype(np.float32) if dhl else None
+    g = _run(ssm, inp, gy, gl)
+    ref = oracle.scan_bwd(inp, synth.to_f64(gy, dt), gl)
+    if not gate:
+        ref["dz"] = None
+    _check(g, ref, dt, f"chunked {N} states {Bsz}x{L}x{D} {dt} {disc} gate={gate} softplus={sp} bias={bias}")
+
+
 def test_backward_generic_rejects_saved_checkpoints(ssm):
     """Saved checkpoints exist only for dstate 16 and dim a multiple of 64."""
     import torch
