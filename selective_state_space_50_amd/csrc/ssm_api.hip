@@ -577,6 +577,15 @@ __global__ void __launch_bounds__(256) gunpad3_kernel(Eo *dst, const Ei *src, in
     }
 }
 
+// dst[i] = src[i] converted, i < n: the copies above when they are flat (no padding, no
+// column offset), without their index arithmetic
+template <typename Eo, typename Ei>
+__global__ void __launch_bounds__(256) convert_kernel(Eo *dst, const Ei *src, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        put(dst, i, widen(src, i));
+}
+
 __global__ void __launch_bounds__(256) add_kernel(float *dst, const float *src, int64_t n) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * 256)
@@ -587,6 +596,17 @@ __global__ void __launch_bounds__(256) add_kernel(float *dst, const float *src, 
 hipError_t gpad3(void *dst, size_t eo, const void *src, size_t ei, int64_t n0, int64_t n1, int64_t n2, int64_t c0,
                  int64_t m1, int64_t m2, float fill, hipStream_t s) {
     const dim3 g = grid_for(n0 * m1 * m2);
+    if (src && n1 == 1 && m1 == 1 && c0 == 0 && m2 == n2 && eo == 4) {
+        if (ei == 2)
+            hipLaunchKernelGGL((convert_kernel<float, uint16_t>), g, dim3(256), 0, s, static_cast<float *>(dst),
+                               static_cast<const uint16_t *>(src), n0 * n2);
+        else if (ei == 4)
+            hipLaunchKernelGGL((convert_kernel<float, float>), g, dim3(256), 0, s, static_cast<float *>(dst),
+                               static_cast<const float *>(src), n0 * n2);
+        else
+            return hipErrorInvalidValue;
+        return launch_status(s);
+    }
     if (eo == 4 && ei == 2)
         hipLaunchKernelGGL((gpad3_kernel<float, uint16_t>), g, dim3(256), 0, s, static_cast<float *>(dst),
                            static_cast<const uint16_t *>(src), n0, n1, n2, c0, m1, m2, fill);
@@ -603,6 +623,17 @@ hipError_t gunpad3(void *dst, size_t eo, const void *src, size_t ei, int64_t n0,
     const int64_t w = m2 < n2 - c0 ? m2 : n2 - c0;
     if (w <= 0) return hipSuccess;
     const dim3 g = grid_for(n0 * n1 * w);
+    if (n1 == 1 && m1 == 1 && c0 == 0 && m2 == n2 && ei == 4) {
+        if (eo == 2)
+            hipLaunchKernelGGL((convert_kernel<uint16_t, float>), g, dim3(256), 0, s, static_cast<uint16_t *>(dst),
+                               static_cast<const float *>(src), n0 * n2);
+        else if (eo == 4)
+            hipLaunchKernelGGL((convert_kernel<float, float>), g, dim3(256), 0, s, static_cast<float *>(dst),
+                               static_cast<const float *>(src), n0 * n2);
+        else
+            return hipErrorInvalidValue;
+        return launch_status(s);
+    }
     if (eo == 2 && ei == 4)
         hipLaunchKernelGGL((gunpad3_kernel<uint16_t, float>), g, dim3(256), 0, s, static_cast<uint16_t *>(dst),
                            static_cast<const float *>(src), n0, n1, n2, c0, m1, m2, w);
@@ -618,6 +649,12 @@ hipError_t gunpad3(void *dst, size_t eo, const void *src, size_t ei, int64_t n0,
 template <typename Ei>
 __global__ void __launch_bounds__(256) repeat_kernel(float *dst, const Ei *src, int64_t n, int64_t R) {
     const int64_t total = n * R;
+    if (total <= 0x7fffffff) {   // 32-bit index arithmetic where it fits
+        const uint32_t t32 = static_cast<uint32_t>(total), r32 = static_cast<uint32_t>(R);
+        for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < t32; i += gridDim.x * 256u)
+            dst[i] = widen(src, i / r32);
+        return;
+    }
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * 256)
         dst[i] = widen(src, i / R);
